@@ -1,0 +1,206 @@
+"""Pins of the oracle's layer arithmetic: dispatch indexing by brute force and
+invariants, the expert FFN against torch's matmul/silu, the identity-expert
+invariant, and every gradient against torch.autograd in fp64 (an independent
+formulation) and central finite differences."""
+import numpy as np
+import pytest
+import torch
+
+import moe_synth as S
+import oracle
+
+
+def _inputs(cfg):
+    w1, w2 = S.all_expert_weights(cfg, threads=1)
+    inp = dict(x=S.x(cfg), wr=S.w_router(cfg), bias=S.router_bias(cfg), w1=w1, w2=w2,
+               dy=S.dy(cfg))
+    if cfg.shared:
+        inp.update(sw1=S.shared_w1(cfg), sw2=S.shared_w2(cfg))
+    return inp
+
+
+# ---------------------------------------------------------------- dispatch
+
+@pytest.mark.parametrize("T,E,k", [(1, 4, 2), (33, 8, 2), (70, 16, 5), (50, 6, 6), (129, 3, 1)])
+def test_dispatch_index_bruteforce(T, E, k):
+    rng = np.random.default_rng(T * E + k)
+    idx = np.stack([rng.permutation(E)[:k] for _ in range(T)]).astype(np.int32)
+    counts, offsets, rmap, ptok = oracle.dispatch_index(idx, E)
+    # brute force: the rows in sorted (expert, token) order
+    entries = sorted((int(idx[t, j]), t, j) for t in range(T) for j in range(k))
+    for r, (e, t, j) in enumerate(entries):
+        assert rmap[t, j] == r and ptok[r] == t
+    # invariants
+    assert counts.sum() == T * k and offsets[E] == T * k and offsets[0] == 0
+    assert np.array_equal(np.diff(offsets), counts)
+    assert np.array_equal(np.sort(rmap.ravel()), np.arange(T * k))
+    assert np.array_equal(np.bincount(ptok, minlength=T), np.full(T, k))
+    for e in range(E):
+        seg = ptok[offsets[e]:offsets[e + 1]]
+        assert np.all(np.diff(seg) > 0)                     # tokens ascend
+        assert np.all((idx[seg] == e).sum(1) == 1)          # each routed to e
+
+
+def test_permute_then_unpermute_is_identity():
+    rng = np.random.default_rng(0)
+    T, E, k, d = 45, 7, 3, 10
+    idx = np.stack([rng.permutation(E)[:k] for _ in range(T)]).astype(np.int32)
+    _, _, rmap, ptok = oracle.dispatch_index(idx, E)
+    x = rng.standard_normal((T, d)).astype(np.float32)
+    xp = oracle.permute(x, rmap)
+    assert np.array_equal(xp, x[ptok])
+    for j in range(k):
+        assert np.array_equal(xp[rmap[:, j]], x)
+    # with k = 1 and gate 1, combine is the inverse permutation
+    idx1 = idx[:, :1]
+    _, _, rmap1, _ = oracle.dispatch_index(idx1, E)
+    y = oracle.combine(oracle.permute(x, rmap1), rmap1, np.ones((T, 1)))
+    assert np.array_equal(y, x.astype(np.float64))
+
+
+# --------------------------------------------------------------------- FFN
+
+def test_ffn_matches_torch_dense_swiglu():
+    g = torch.Generator().manual_seed(7)
+    X = torch.randn(33, 48, generator=g, dtype=torch.float64)
+    W1 = torch.randn(2 * 40, 48, generator=g, dtype=torch.float64) * 0.1
+    W2 = torch.randn(48, 40, generator=g, dtype=torch.float64) * 0.1
+    GU, H, O = oracle.ffn_fwd(X.numpy(), W1.numpy(), W2.numpy())
+    ref = torch.nn.functional.silu(X @ W1[:40].T) * (X @ W1[40:].T)
+    assert np.allclose(H, ref.numpy(), rtol=1e-13, atol=1e-15)
+    assert np.allclose(O, (ref @ W2.T).numpy(), rtol=1e-12, atol=1e-14)
+
+
+def test_identity_experts_return_gate_sum_times_x():
+    for base, shared_add in [(S.CONFIGS[0], 0.0), (S.mini(S.CONFIGS[2], 40, 64, 32, E=32), 1.0),
+                             (S.mini(S.CONFIGS[3], 40, 64, 32, E=16), 0.0)]:
+        inp = _inputs(base)
+        out = oracle.layer(base, inp, identity=True)
+        x = oracle.as_f64(inp["x"])
+        gsum = out["gates"].sum(1, keepdims=True)
+        assert np.allclose(out["y"], (gsum + shared_add) * x, rtol=1e-13, atol=1e-13)
+        if base.renorm:
+            assert np.allclose(gsum, base.gate_scale, atol=1e-13)
+
+
+# --------------------------------------------------------------- gradients
+
+def _torch_layer(cfg, inp, idx, L32):
+    """Independent fp64 torch formulation of the layer with the oracle's
+    selection held fixed; returns leaves and the scalar loss <y, dy>.
+    The gates read the fp32 router logits (their value is L32, their
+    gradient flows as for x W_r^T + b)."""
+    f = cfg.f
+    x = torch.tensor(oracle.as_f64(inp["x"]), requires_grad=True)
+    wr = torch.tensor(oracle.as_f64(inp["wr"]), requires_grad=True)
+    w1 = torch.tensor(oracle.as_f64(inp["w1"]), requires_grad=True)
+    w2 = torch.tensor(oracle.as_f64(inp["w2"]), requires_grad=True)
+    L = x @ wr.T
+    if inp.get("bias") is not None:
+        L = L + torch.tensor(oracle.as_f64(inp["bias"]))
+    L = L + (torch.tensor(L32, dtype=torch.float64) - L.detach())
+    I = torch.tensor(idx, dtype=torch.int64)
+    sel = torch.gather(L, 1, I)
+    if cfg.score == "softmax":
+        g = torch.softmax(sel, 1) if cfg.renorm else torch.gather(torch.softmax(L, 1), 1, I)
+    else:
+        s = torch.sigmoid(sel)
+        g = s / s.sum(1, keepdim=True) if cfg.renorm else s
+    g = g * cfg.gate_scale
+    y = torch.zeros_like(x)
+    for t in range(x.shape[0]):
+        for j in range(cfg.k):
+            e = int(idx[t, j])
+            gu = w1[e] @ x[t]
+            h = torch.nn.functional.silu(gu[:f]) * gu[f:]
+            y[t] = y[t] + g[t, j] * (w2[e] @ h)
+    leaves = dict(x=x, wr=wr, w1=w1, w2=w2)
+    if cfg.shared:
+        sw1 = torch.tensor(oracle.as_f64(inp["sw1"]), requires_grad=True)
+        sw2 = torch.tensor(oracle.as_f64(inp["sw2"]), requires_grad=True)
+        gu = x @ sw1.T
+        y = y + (torch.nn.functional.silu(gu[:, :f]) * gu[:, f:]) @ sw2.T
+        leaves.update(sw1=sw1, sw2=sw2)
+    loss = (y * torch.tensor(oracle.as_f64(inp["dy"]))).sum()
+    return leaves, y, loss
+
+
+@pytest.mark.parametrize("which", [0, 2, 3])
+def test_layer_matches_torch_autograd_fp64(which):
+    cfg = S.CONFIGS[which]
+    if which:
+        cfg = S.mini(cfg, T=24, d=32, f=24, E=16 if which == 2 else 8)
+        if which == 2:
+            cfg = cfg.replace(num_groups=4, topk_groups=2, k=3)
+        else:
+            cfg = cfg.replace(k=3)
+    else:
+        cfg = S.mini(cfg, T=30, d=24, f=20)
+    inp = _inputs(cfg)
+    out = oracle.layer(cfg, inp)
+    leaves, y, loss = _torch_layer(cfg, inp, out["idx"], out["logits"])
+    loss.backward()
+    assert np.allclose(out["y"], y.detach().numpy(), rtol=1e-12, atol=1e-14)
+    assert np.allclose(out["dx"], leaves["x"].grad.numpy(), rtol=1e-10, atol=1e-13)
+    assert np.allclose(out["dw_router"], leaves["wr"].grad.numpy(), rtol=1e-10, atol=1e-13)
+    assert np.allclose(out["dw1"], leaves["w1"].grad.numpy(), rtol=1e-10, atol=1e-13)
+    assert np.allclose(out["dw2"], leaves["w2"].grad.numpy(), rtol=1e-10, atol=1e-13)
+    if cfg.shared:
+        assert np.allclose(out["shared_dw1"], leaves["sw1"].grad.numpy(), rtol=1e-10, atol=1e-13)
+        assert np.allclose(out["shared_dw2"], leaves["sw2"].grad.numpy(), rtol=1e-10, atol=1e-13)
+
+
+def test_layer_gradients_central_differences():
+    """Central differences of <y, dy> in fp64 with routing frozen; the
+    selection margin is checked to exceed the perturbation's effect."""
+    cfg = S.mini(S.CONFIGS[0], T=12, d=16, f=12, E=4)
+    inp = _inputs(cfg)
+    out = oracle.layer(cfg, inp)
+    L = out["logits"].astype(np.float64)
+    srt = np.sort(L, axis=1)
+    margin = np.min(srt[:, -cfg.k] - srt[:, -cfg.k - 1])
+    assert margin > 1e-6
+    dy = oracle.as_f64(inp["dy"])
+    idx = out["idx"]
+
+    def loss(x, wr, w1, w2):
+        Lx = x @ wr.T
+        g = oracle.route_gates(Lx, idx, cfg.score, cfg.renorm, cfg.gate_scale)
+        _, _, rmap, _ = oracle.dispatch_index(idx, cfg.E)
+        Xp = oracle.permute(x, rmap)
+        _, offs, _, _ = oracle.dispatch_index(idx, cfg.E)
+        O = np.zeros((cfg.A, cfg.d))
+        for e in range(cfg.E):
+            r0, r1 = offs[e], offs[e + 1]
+            if r1 > r0:
+                O[r0:r1] = oracle.ffn_fwd(Xp[r0:r1], w1[e], w2[e])[2]
+        return float((oracle.combine(O, rmap, g) * dy).sum())
+
+    base = dict(x=oracle.as_f64(inp["x"]), wr=oracle.as_f64(inp["wr"]),
+                w1=oracle.as_f64(inp["w1"]), w2=oracle.as_f64(inp["w2"]))
+    grads = dict(x=out["dx"], wr=out["dw_router"], w1=out["dw1"], w2=out["dw2"])
+    rng = np.random.default_rng(0)
+    h = 1e-6
+    for name in base:
+        for _ in range(6):
+            pos = tuple(int(rng.integers(0, s)) for s in base[name].shape)
+            p = {kk: v.copy() for kk, v in base.items()}
+            p[name][pos] += h
+            lp = loss(**p)
+            p[name][pos] -= 2 * h
+            lm = loss(**p)
+            fd = (lp - lm) / (2 * h)
+            assert abs(fd - grads[name][pos]) <= 1e-6 * max(1.0, abs(fd)), (name, pos, fd, grads[name][pos])
+
+
+def test_fp8_layer_consistency():
+    """fp8 weights: the oracle's own quantisation of the bf16 masters is used
+    consistently and stays close to the unquantised layer."""
+    cfg = S.mini(S.CONFIGS[4], T=16, d=256, f=256, E=16).replace(num_groups=4, topk_groups=2, k=4)
+    inp = _inputs(cfg)
+    out = oracle.layer(cfg, inp)
+    ref = oracle.layer(cfg.replace(weight="bf16"), inp)
+    assert np.array_equal(out["idx"], ref["idx"])
+    assert oracle.rel_l2(out["y"], ref["y"]) < 0.08
+    q1, s1, q2, s2 = out["w_q"][3]
+    assert s1.shape == (2 * cfg.f // 128, cfg.d // 128) and s2.shape == (cfg.d // 128, cfg.f // 128)
