@@ -1,0 +1,256 @@
+"""Benchmark of the MoE layer token path (forward + backward) on one MI355X.
+
+A step is one forward and backward pass of the whole layer over one batch:
+route -> dispatch -> grouped SwiGLU FFN (+ shared expert) -> combine, then
+combine backward -> grouped FFN backward -> dispatch backward -> route
+backward. Inputs and weights are seeded synthetic tensors already resident in
+HBM when the timed region starts. Prints one JSON line.
+
+The workload is the Mixtral-style layer (T=4096 tokens, d=4096, 8 experts,
+top-2, SwiGLU d_ff=14336, bf16) unless --config names another.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0
+MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "fp8": 5000.0, "f32": 157.3}
+
+
+def stage_work(c):
+    """Algorithmic bytes and flops of every call in a step (what the method
+    must move or compute; intermediate re-reads are not counted)."""
+    T, d, E, k, f, S = c.T, c.d, c.E, c.k, c.f, c.shared
+    A = T * k
+    R = A + S * T
+    bx = 4 if c.act == "f32" else 2
+    bo = ba = bx
+    bw = {"f32": 4, "bf16": 2, "fp8": 1}[c.weight]
+    bg = 4 if c.weight == "f32" else 2
+    bp = (d + 4 * d // 128) if c.weight == "fp8" else d * bx
+    w = {}
+    w["route"] = (T * d * bx + 4 * E * d + 4 * T * E + 8 * T * k + T * E, 2 * T * d * E)
+    w["dispatch"] = (T * d * bx + A * bp + 16 * A, 0)
+    w["grouped_ffn"] = (E * 3 * d * f * bw + A * bp + A * 2 * f * ba + A * d * bo, 6 * d * f * A)
+    if S:
+        w["shared_ffn"] = (3 * d * f * bw + T * bp + T * 2 * f * ba + T * d * bo, 6 * d * f * T)
+    w["combine"] = (A * d * bo + 8 * A + S * T * d * bo + T * d * bo, 2 * A * d)
+    w["combine_bwd"] = (T * d * bo + 2 * A * d * bo + 12 * A, 2 * A * d)
+    w["grouped_ffn_bwd"] = (E * 3 * d * f * (bw + bg) + A * (2 * d * bo + 2 * f * ba + bp),
+                            12 * d * f * A)
+    if S:
+        w["shared_ffn_bwd"] = (3 * d * f * (bw + bg) + T * (2 * d * bo + 2 * f * ba + bp),
+                               12 * d * f * T)
+    w["dispatch_bwd"] = (A * d * bo + T * d * bx + 4 * A + S * T * d * bo, A * d)
+    w["route_bwd"] = (4 * T * E + 12 * T * k + 3 * T * d * bx + 8 * E * d, 4 * T * d * E)
+    return w
+
+
+def make_layer(cfg, device):
+    import torch
+    import moe_synth as S
+    from mixture_experts_layer_gather_amd import MoELayer
+    layer = MoELayer(**cfg.describe(), device=device)
+    w1, w2 = S.all_expert_weights(cfg, device=device, threads=16)
+    bias = S.router_bias(cfg)
+    sw1 = S.shared_w1(cfg).to(device) if cfg.shared else None
+    sw2 = S.shared_w2(cfg).to(device) if cfg.shared else None
+    layer.set_weights(S.w_router(cfg).to(device), w1, w2,
+                      bias=None if bias is None else bias.to(device), sw1=sw1, sw2=sw2)
+    x = S.x(cfg).to(device)
+    dy = S.dy(cfg).to(device)
+    torch.cuda.synchronize()
+    return layer, x, dy
+
+
+def timed_step(layer, x, dy, marks):
+    """One fwd+bwd step with an event after every library call (events are
+    recorded on the stream the library launches on: torch's current one)."""
+    import mixture_experts_layer_gather_amd._lib as L
+    rec = lambda name: marks.append((name, _event()))
+    c = layer.cfg
+    layer.x = x
+    rec("start")
+    L.moe_route(c, x, layer.w_router, layer.bias, layer.logits, layer.topk_idx, layer.topk_gate,
+                layer.routing_map)
+    rec("route")
+    L.moe_dispatch(c, x, layer.topk_idx, layer.counts, layer.offsets, layer.row_id_map,
+                   layer.perm_token, layer.x_perm, layer.x_scale, layer.ws_dispatch)
+    rec("dispatch")
+    L.moe_grouped_ffn(c, layer.x_perm, layer.x_scale, layer.offsets, layer.w1, layer.w1_scale,
+                      layer.w2, layer.w2_scale, layer.act_gu, layer.act_h, layer.h_scale,
+                      layer.out_perm)
+    rec("grouped_ffn")
+    shared_out = None
+    if layer.shared:
+        sx, sxs = x, None
+        if layer.fp8:
+            L.moe_quantize_fp8_blockwise(x, layer.T, layer.d, 1, layer.qb, layer.s_x,
+                                         layer.s_x_scale)
+            sx, sxs = layer.s_x, layer.s_x_scale
+        L.moe_grouped_ffn(layer.scfg, sx, sxs, layer.s_offsets, layer.sw1, layer.sw1_scale,
+                          layer.sw2, layer.sw2_scale, layer.s_gu, layer.s_h, layer.s_h_scale,
+                          layer.s_out)
+        shared_out = layer.s_out
+        rec("shared_ffn")
+    L.moe_combine(c, layer.out_perm, layer.row_id_map, layer.topk_gate, shared_out, layer.y)
+    rec("combine")
+    L.moe_combine_bwd(c, dy, layer.out_perm, layer.row_id_map, layer.topk_gate, layer.d_out_perm,
+                      layer.d_gate)
+    rec("combine_bwd")
+    L.moe_grouped_ffn_bwd(c, layer.x_perm, layer.x_scale, layer.offsets, layer.w1,
+                          layer.w1_scale, layer.w2, layer.w2_scale, layer.act_gu, layer.act_h,
+                          layer.h_scale, layer.d_out_perm, layer.dx_perm, layer.dw1, layer.dw2,
+                          layer.ws_ffn_bwd)
+    rec("grouped_ffn_bwd")
+    dx_add = None
+    if layer.shared:
+        sx, sxs = (layer.s_x, layer.s_x_scale) if layer.fp8 else (x, None)
+        L.moe_grouped_ffn_bwd(layer.scfg, sx, sxs, layer.s_offsets, layer.sw1, layer.sw1_scale,
+                              layer.sw2, layer.sw2_scale, layer.s_gu, layer.s_h, layer.s_h_scale,
+                              dy, layer.s_dx, layer.s_dw1, layer.s_dw2, layer.ws_ffn_bwd)
+        dx_add = layer.s_dx
+        rec("shared_ffn_bwd")
+    L.moe_dispatch_bwd(c, layer.dx_perm, layer.row_id_map, dx_add, layer.dx)
+    rec("dispatch_bwd")
+    L.moe_route_bwd(c, x, layer.w_router, layer.logits, layer.topk_idx, layer.topk_gate,
+                    layer.d_gate, layer.dx, layer.dw_router, layer.ws_route_bwd)
+    rec("route_bwd")
+
+
+def _event():
+    import torch
+    e = torch.cuda.Event(enable_timing=True)
+    e.record()
+    return e
+
+
+def cpu_baseline(cfg, sample_tokens):
+    """The CPU oracle, as it stands, on the first `sample_tokens` tokens of the
+    same workload (all experts' weights, full forward + backward)."""
+    import numpy as np  # noqa: F401
+    import moe_synth as S
+    import oracle
+    sub = cfg.replace(T=sample_tokens)
+    x = S.x(cfg)[:sample_tokens]
+    dy = S.dy(cfg)[:sample_tokens]
+    w1, w2 = S.all_expert_weights(cfg, threads=16)
+    inp = dict(x=x, wr=S.w_router(cfg), bias=S.router_bias(cfg), w1=w1, w2=w2, dy=dy)
+    if cfg.shared:
+        inp.update(sw1=S.shared_w1(cfg), sw2=S.shared_w2(cfg))
+    t0 = time.perf_counter()
+    oracle.layer(sub, inp)
+    dt = time.perf_counter() - t0
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:  # pragma: no cover
+        cores = os.cpu_count()
+    return {"value": sample_tokens / dt, "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"first {sample_tokens} of {cfg.T} tokens of {cfg.name}, full layer fwd+bwd "
+                      f"in fp64 over all {cfg.E} experts' weights; {dt:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--config", default="mixtral_bf16")
+    ap.add_argument("--cpu-sample", type=int, default=384,
+                    help="tokens of the workload timed on the CPU oracle (0: skip)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for {args.gpus}); the path has no "
+              "multi-GPU mode", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import moe_synth as S
+    cfg = S.BY_NAME[args.config]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    layer, x, dy = make_layer(cfg, dev)
+
+    for _ in range(args.warmup):
+        timed_step(layer, x, dy, [])
+    torch.cuda.synchronize()
+
+    steps = []
+    t0 = time.perf_counter()
+    start = _event()
+    for _ in range(args.steps):
+        marks = []
+        timed_step(layer, x, dy, marks)
+        steps.append(marks)
+    stop = _event()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = start.elapsed_time(stop) / args.steps
+
+    per = {}
+    for marks in steps:
+        for (_, a), (name, b) in zip(marks[:-1], marks[1:]):
+            per.setdefault(name, []).append(a.elapsed_time(b))
+    per_ms = {n: sum(v) / len(v) for n, v in per.items()}
+    work = stage_work(cfg)
+    dt = "fp8" if cfg.weight == "fp8" else cfg.act
+    stages = {}
+    for n, t in per_ms.items():
+        b, fl = work[n]
+        stages[n] = {"ms": round(t, 4), "GBps": round(b / t / 1e6, 1),
+                     "TFLOPs": round(fl / t / 1e9, 1) if fl else 0.0}
+    dom = max(per_ms, key=per_ms.get)
+    b, fl = work[dom]
+    if "ffn" in dom:
+        ach = fl / per_ms[dom] / 1e9
+        roof = {"kernel": f"moe_{dom.replace('shared_', 'grouped_')} ({dom})", "bound": "mfma",
+                "achieved": round(ach, 1), "peak": MFMA_PEAK_TFLOPS[dt], "unit": "TFLOP/s",
+                "frac": round(ach / MFMA_PEAK_TFLOPS[dt], 4), "traffic": None}
+    else:
+        ach = b / per_ms[dom] / 1e6
+        roof = {"kernel": dom, "bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBPS,
+                "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBPS, 4), "traffic": None}
+
+    ffn_f = sum(work[n][1] for n in per_ms if "ffn" in n)
+    ffn_t = sum(per_ms[n] for n in per_ms if "ffn" in n)
+    dc_b = work["dispatch"][0] + work["combine"][0]
+    dc_t = per_ms["dispatch"] + per_ms["combine"]
+    out = {
+        "metric": "MoE layer tokens/s; dispatch/combine HBM GB/s; grouped-GEMM MFMA % of peak",
+        "value": round(cfg.T / (ms / 1e3), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": dt,
+        "data": "synthetic (seeded normal inputs and random-init weights of the layer's shape)",
+        "config": {"workload": f"{cfg.name}: MoE layer fwd+bwd, T={cfg.T} d={cfg.d} E={cfg.E}"
+                               f"{'+1 shared' if cfg.shared else ''} top-{cfg.k} {cfg.score}"
+                               f"{' renorm' if cfg.renorm else ''}, SwiGLU d_ff={cfg.f}",
+                   "tokens": cfg.T, "hidden": cfg.d, "experts": cfg.E, "top_k": cfg.k,
+                   "ffn_hidden": cfg.f, "parallelism": "none (one GPU)"},
+        "dispatch_combine_GBps": round(dc_b / dc_t / 1e6, 1),
+        "grouped_gemm_mfma_pct": round(100 * ffn_f / ffn_t / 1e9 / MFMA_PEAK_TFLOPS[dt], 2),
+        "stages": stages,
+        "roofline": roof,
+        "wall_s": round(wall, 3),
+    }
+    if args.cpu_sample > 0:
+        out["cpu_baseline"] = cpu_baseline(cfg, args.cpu_sample)
+    print(json.dumps(out))
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,245 @@
+/*
+ * libmoe: the token path of a Mixture-of-Experts layer on one AMD Instinct
+ * MI355X (gfx950), forward and backward, behind a plain C ABI.
+ *
+ * The path, stage by stage, with the passage of the pages that defines it:
+ *   route        a router scores every expert for every token and keeps a
+ *                few; only those experts run (Megatron Core MoE summary,
+ *                "O essencial" and technical summary section 1; top-k flags
+ *                of the Megatron-Core skill page, "Workflow 2: MoE").
+ *   dispatch     tokens are sent to their experts following the routing map
+ *                (Hybrid-EP article, dispatch operator and routing-map
+ *                paragraphs); on one GPU this is the permutation into
+ *                expert-contiguous rows. Dropless: exactly T*k rows
+ *                (Megatron Core MoE summary, section 2.4).
+ *   grouped_ffn  the experts' GEMMs grouped into one kernel launch
+ *                (Megatron Core MoE summary, section 2.4 "Grouped GEMM").
+ *   combine      tokens come back to their original order with
+ *                high-precision accumulation (Hybrid-EP article, combine
+ *                operator paragraph).
+ * Shapes live in device memory and are never read on the host
+ * (Megatron Core MoE summary, section 2.4, device-initiated kernels), and
+ * every buffer has a size known from the configuration alone (Hybrid-EP
+ * article, buffer pre-allocation paragraph).
+ *
+ * Conventions for every call below.
+ *  - Pointers are device pointers owned by the caller; the library never
+ *    allocates, frees or keeps device memory. Tensors are dense and
+ *    row-major. Every pointer must be 16-byte aligned.
+ *  - `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *    Every call only enqueues work on it: no device synchronisation, no
+ *    device-to-host copy, no host read of counts or offsets.
+ *  - All argument checks run on the host before any launch; on failure a
+ *    negative MOE_ERR_* code is returned and nothing is enqueued.
+ *    num_tokens == 0 is valid and enqueues nothing.
+ *  - Outputs are overwritten unless marked "+=". For the same inputs every
+ *    output is bitwise identical from run to run (no floating-point atomics).
+ *  - The library keeps no global state; calls are thread-safe.
+ *
+ * Notation: T tokens, d hidden, E experts, k top-k, f expert hidden size,
+ * A = T*k dispatched rows. "act" is cfg->act_dtype (f32 or bf16),
+ * "wt" is cfg->weight_dtype (f32, bf16 or fp8 e4m3).
+ */
+#ifndef MOE_H
+#define MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+    MOE_OK = 0,
+    MOE_ERR_INVALID_ARG = -1,       /* bad size, null required pointer, bad enum */
+    MOE_ERR_UNSUPPORTED_DTYPE = -2, /* dtype combination not provided */
+    MOE_ERR_ALIGNMENT = -3,         /* a pointer is not 16-byte aligned */
+    MOE_ERR_WORKSPACE = -4,         /* workspace missing or too small */
+    MOE_ERR_HIP = -5                /* a launch failed (hipGetLastError) */
+};
+
+enum { MOE_DTYPE_F32 = 0, MOE_DTYPE_BF16 = 1, MOE_DTYPE_FP8_E4M3 = 2 };
+enum { MOE_SCORE_SOFTMAX = 0, MOE_SCORE_SIGMOID = 1 };
+enum { MOE_GROUP_TOP2_SUM = 0, MOE_GROUP_MAX = 1 };
+enum { MOE_FFN_SWIGLU = 0, MOE_FFN_IDENTITY = 1 };
+enum {
+    MOE_OP_ROUTE = 0,
+    MOE_OP_DISPATCH = 1,
+    MOE_OP_GROUPED_FFN = 2,
+    MOE_OP_GROUPED_FFN_BWD = 3,
+    MOE_OP_ROUTE_BWD = 4
+};
+
+/* Layer configuration, read on the host only.
+ *  score_fn    MOE_SCORE_SOFTMAX: p = softmax over all experts of the logits;
+ *              MOE_SCORE_SIGMOID: s = 1/(1+exp(-logit)).
+ *  renormalize 1: gates are normalised over the k selected experts.
+ *  gate_scale  multiplies every gate (2.5 for DeepSeek-V3-style routing).
+ *  num_groups, topk_groups  group-limited routing (sigmoid only): experts
+ *              form num_groups contiguous groups; a group's score is the sum
+ *              of its two best sigmoid scores (MOE_GROUP_TOP2_SUM) or its
+ *              best (MOE_GROUP_MAX); top-k is taken inside the topk_groups
+ *              best groups. 1 and 1 turns it off.
+ *  quant_block FP8 block edge (128): activations 1 x block, weights
+ *              block x block, fp32 scales.
+ *  ffn_mode    MOE_FFN_IDENTITY makes every expert the identity (a test mode
+ *              of route, dispatch and combine). */
+typedef struct moe_config {
+    int64_t num_tokens;  /* T */
+    int64_t hidden;      /* d, a multiple of 128 */
+    int64_t num_experts; /* E, 1..1024 */
+    int64_t top_k;       /* k, 1..min(E, 16) */
+    int64_t ffn_hidden;  /* f, a multiple of 128 */
+    int32_t score_fn;
+    int32_t renormalize;
+    float gate_scale;
+    int32_t num_groups;
+    int32_t topk_groups;
+    int32_t group_score;
+    int32_t act_dtype;    /* MOE_DTYPE_F32 or MOE_DTYPE_BF16 */
+    int32_t weight_dtype; /* act_dtype, or MOE_DTYPE_FP8_E4M3 with bf16 act */
+    int32_t quant_block;  /* 128 */
+    int32_t ffn_mode;
+} moe_config;
+
+/* Bytes of workspace the call `op` (MOE_OP_*) needs for this configuration;
+ * 0 if none. Returns 0 as well for an invalid configuration. */
+size_t moe_workspace_size(const moe_config *cfg, int op);
+
+/* Router forward.
+ *   x          [T,d] act
+ *   w_router   [E,d] f32
+ *   expert_bias [E] f32 or NULL: added to every logit before scoring and
+ *              selection (it receives no gradient)
+ * out:
+ *   logits     [T,E] f32. logits[t,e] is the fp32 fused multiply-add
+ *              recurrence acc = fma(x[t,i], w[e,i], acc) over i = 0..d-1
+ *              from +0, then + bias[e]: bit-exact by construction.
+ *   topk_idx   [T,k] i32, slot j = the j-th ranked expert: larger logit
+ *              first, equal logits to the lower index (-0 == +0, NaN last),
+ *              within the group limit when it is on.
+ *   topk_gate  [T,k] f32 gates (see moe_config).
+ *   routing_map [T,E] u8 or NULL: 1 where the expert is selected.
+ * Workspace: none (ws may be NULL). */
+int moe_route(const moe_config *cfg, const void *x, const float *w_router,
+              const float *expert_bias, float *logits, int32_t *topk_idx,
+              float *topk_gate, uint8_t *routing_map, void *ws,
+              size_t ws_bytes, void *stream);
+
+/* Dispatch: histogram, exclusive scan, positions and the gather of tokens
+ * into expert-contiguous rows (Hybrid-EP article, dispatch operator;
+ * Megatron Core MoE summary, sections 2.2 and 2.3 on permutation without
+ * redundant steps or intermediate tensors).
+ *   x          [T,d] act
+ *   topk_idx   [T,k] i32 from moe_route or from the caller (router replay);
+ *              every entry in [0,E), distinct within a token
+ * out (all bit-exact):
+ *   counts     [E] i32 rows per expert
+ *   offsets    [E+1] i32 exclusive prefix sum, offsets[E] = A
+ *   row_id_map [T,k] i32 row of (t, j): offsets[e] + #{t' < t routed to e}
+ *              (rows sorted by expert, then token)
+ *   perm_token [A] i32 source token of each row
+ *   x_perm     [A,d]: act copy of x, or for wt = fp8 the E4M3 codes of x
+ *              quantised per token and 1 x quant_block block
+ *   x_scale    [A, d/quant_block] f32 (fp8 only; NULL otherwise)
+ * Workspace: moe_workspace_size(cfg, MOE_OP_DISPATCH). */
+int moe_dispatch(const moe_config *cfg, const void *x, const int32_t *topk_idx,
+                 int32_t *counts, int32_t *offsets, int32_t *row_id_map,
+                 int32_t *perm_token, void *x_perm, float *x_scale, void *ws,
+                 size_t ws_bytes, void *stream);
+
+/* Grouped SwiGLU expert FFN forward over expert-contiguous rows (Megatron
+ * Core MoE summary, section 2.4: many expert GEMMs in one kernel). For each
+ * expert e and its rows r in [offsets[e], offsets[e+1]):
+ *   GU = X W1_e^T ([gate | up], 2f wide), H = silu(G) * U, O = H W2_e^T.
+ *   x_perm     [A,d] act (wt = fp8: E4M3 codes, with x_scale [A,d/128])
+ *   offsets    [E+1] i32 (device)
+ *   w1         [E,2f,d] wt, rows 0..f-1 gate, f..2f-1 up (fp8: + w1_scale
+ *              [E,2f/128,d/128] f32)
+ *   w2         [E,d,f] wt (fp8: + w2_scale [E,d/128,f/128] f32)
+ * out:
+ *   act_gu     [A,2f] act: G and U (saved for the backward)
+ *   act_h      [A,f]: act, or for wt = fp8 E4M3 codes with h_scale
+ *              [A,f/128] f32 (H is quantised before the second GEMM)
+ *   out_perm   [A,d] act
+ * The shared expert of DeepSeek-style layers is this call with E = 1, k = 1
+ * over the (quantised) unpermuted x and offsets {0, T}.
+ * Workspace: moe_workspace_size(cfg, MOE_OP_GROUPED_FFN). */
+int moe_grouped_ffn(const moe_config *cfg, const void *x_perm,
+                    const float *x_scale, const int32_t *offsets,
+                    const void *w1, const float *w1_scale, const void *w2,
+                    const float *w2_scale, void *act_gu, void *act_h,
+                    float *h_scale, void *out_perm, void *ws, size_t ws_bytes,
+                    void *stream);
+
+/* Combine forward (Hybrid-EP article, combine operator with high-precision
+ * accumulation): y[t] = sum_j gate[t,j] * out_perm[row_id_map[t,j]]
+ * (+ shared_out[t]), accumulated in fp32 in slot order, shared output added
+ * last, one rounding to act.
+ *   out_perm [A,d] act, row_id_map [T,k], topk_gate [T,k] f32,
+ *   shared_out [T,d] act or NULL  ->  y [T,d] act. */
+int moe_combine(const moe_config *cfg, const void *out_perm,
+                const int32_t *row_id_map, const float *topk_gate,
+                const void *shared_out, void *y, void *stream);
+
+/* Combine backward.
+ *   d_out_perm[row_id_map[t,j]] = gate[t,j] * dy[t]   ([A,d] act)
+ *   d_gate[t,j] = <dy[t], out_perm[row_id_map[t,j]]>  ([T,k] f32, fixed-order
+ *                 fp32 reduction). */
+int moe_combine_bwd(const moe_config *cfg, const void *dy, const void *out_perm,
+                    const int32_t *row_id_map, const float *topk_gate,
+                    void *d_out_perm, float *d_gate, void *stream);
+
+/* Grouped SwiGLU expert FFN backward. Per expert e and its rows:
+ *   dH = dO W2_e, dW2_e = dO^T H,
+ *   dG = dH * U * s(G) * (1 + G (1 - s(G))), dU = dH * silu(G),
+ *   dX = [dG dU] W1_e, dW1_e = [dG dU]^T X.
+ * Inputs as in moe_grouped_ffn plus d_out_perm [A,d] act.
+ * out: dx_perm [A,d] act; dw1 [E,2f,d], dw2 [E,d,f] in the parameter dtype
+ * (f32 when wt is f32, else bf16), overwritten; an expert with no rows gets
+ * exact zeros.
+ * Workspace: moe_workspace_size(cfg, MOE_OP_GROUPED_FFN_BWD). */
+int moe_grouped_ffn_bwd(const moe_config *cfg, const void *x_perm,
+                        const float *x_scale, const int32_t *offsets,
+                        const void *w1, const float *w1_scale, const void *w2,
+                        const float *w2_scale, const void *act_gu,
+                        const void *act_h, const float *h_scale,
+                        const void *d_out_perm, void *dx_perm, void *dw1,
+                        void *dw2, void *ws, size_t ws_bytes, void *stream);
+
+/* Dispatch backward: dx[t] = sum_j dx_perm[row_id_map[t,j]] (+ dx_add[t]),
+ * fp32 in slot order, one rounding to act.
+ *   dx_perm [A,d] act, dx_add [T,d] act or NULL -> dx [T,d] act. */
+int moe_dispatch_bwd(const moe_config *cfg, const void *dx_perm,
+                     const int32_t *row_id_map, const void *dx_add, void *dx,
+                     void *stream);
+
+/* Router backward; selection, group choice and the bias are constants.
+ *   dL = d(gates)/d(logits)^T d_gate for the configured score function,
+ *   dw_router = dL^T x   ([E,d] f32, overwritten)
+ *   dx += dL w_router    ([T,d] act, read-modify-write)
+ * Inputs are those of moe_route plus its outputs and d_gate [T,k] f32.
+ * Workspace: moe_workspace_size(cfg, MOE_OP_ROUTE_BWD). */
+int moe_route_bwd(const moe_config *cfg, const void *x, const float *w_router,
+                  const float *logits, const int32_t *topk_idx,
+                  const float *topk_gate, const float *d_gate, void *dx,
+                  float *dw_router, void *ws, size_t ws_bytes, void *stream);
+
+/* FP8 E4M3 block quantisation: src [rows, cols] (src_dtype f32 or bf16) in
+ * blocks of block_r x block_c: amax = max |v|, scale = amax / 448 (1 if
+ * amax is 0), dst = e4m3(v / scale) rounded to nearest even, saturating.
+ * scale is [ceil(rows/block_r), ceil(cols/block_c)] f32. Used for weights
+ * (128 x 128) and for the shared expert's input (1 x 128). */
+int moe_quantize_fp8_blockwise(const void *src, int src_dtype, int64_t rows,
+                               int64_t cols, int64_t block_r, int64_t block_c,
+                               uint8_t *dst, float *scale, void *stream);
+
+/* Static description of a status code. */
+const char *moe_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_H */

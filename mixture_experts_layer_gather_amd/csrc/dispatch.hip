@@ -1,0 +1,360 @@
+// Dispatch and combine kernels (gfx950): the token permutation into
+// expert-contiguous rows and its inverse, forward and backward.
+//
+// Dispatch sends each token to its experts following the routing map and
+// combine returns the expert outputs to token order with high-precision
+// accumulation (Hybrid-EP article, paragraphs on the dispatch/combine
+// operators, the routing map and hierarchical accumulation). On one GPU the
+// transfer becomes a gather into an HBM buffer: each token row is read once
+// and written k times with 16-byte stores; combine is a per-token gather in
+// fp32, in slot order, with no atomics (deterministic).
+//
+// Row order: expert ascending, then token ascending. Ranks inside a chunk of
+// tokens come from per-expert token bitmasks in LDS (popcount of the lower
+// bits), never from the order in which atomics land.
+#include "common.hpp"
+#include "launch.hpp"
+
+namespace moe {
+
+constexpr int kChunkTok = 256;  // tokens per dispatch chunk (one per thread)
+
+int64_t dispatch_chunks(int64_t T) { return (T + kChunkTok - 1) / kChunkTok; }
+
+// --- 1. per-chunk expert histogram --------------------------------------
+__global__ __launch_bounds__(256) void dispatch_count_kernel(const int32_t* __restrict__ idx,
+                                                             int32_t* __restrict__ chunk_cnt,
+                                                             int T, int E, int k) {
+  extern __shared__ int32_t hist[];
+  const int c = blockIdx.x;
+  for (int e = threadIdx.x; e < E; e += 256) hist[e] = 0;
+  __syncthreads();
+  const int t = c * kChunkTok + threadIdx.x;
+  if (t < T)
+    for (int j = 0; j < k; ++j) atomicAdd(&hist[idx[int64_t(t) * k + j]], 1);
+  __syncthreads();
+  for (int e = threadIdx.x; e < E; e += 256) chunk_cnt[int64_t(c) * E + e] = hist[e];
+}
+
+// --- 2. scan over (chunk, expert) -----------------------------------------
+// chunk_cnt[c][e] becomes the first row of expert e's tokens in chunk c.
+__global__ __launch_bounds__(1024) void dispatch_scan_kernel(int32_t* __restrict__ chunk_cnt,
+                                                             int32_t* __restrict__ counts,
+                                                             int32_t* __restrict__ offsets,
+                                                             int nchunks, int E) {
+  __shared__ int32_t s_tot[1024];
+  __shared__ int32_t s_off[1025];
+  const int e = threadIdx.x;
+  int32_t run = 0;
+  if (e < E) {
+    for (int c = 0; c < nchunks; ++c) {
+      const int32_t v = chunk_cnt[int64_t(c) * E + e];
+      chunk_cnt[int64_t(c) * E + e] = run;
+      run += v;
+    }
+    counts[e] = run;
+  }
+  s_tot[e] = (e < E) ? run : 0;
+  __syncthreads();
+  if (e == 0) {  // E <= 1024 values: a short serial exclusive scan
+    int32_t acc = 0;
+    for (int i = 0; i < E; ++i) {
+      s_off[i] = acc;
+      acc += s_tot[i];
+    }
+    s_off[E] = acc;
+  }
+  __syncthreads();
+  if (e < E) {
+    offsets[e] = s_off[e];
+    for (int c = 0; c < nchunks; ++c) chunk_cnt[int64_t(c) * E + e] += s_off[e];
+  }
+  if (e == 0) offsets[E] = s_off[E];
+}
+
+// --- 3. positions: row of every (token, slot) -----------------------------
+__global__ __launch_bounds__(256) void dispatch_pos_kernel(const int32_t* __restrict__ idx,
+                                                           const int32_t* __restrict__ chunk_base,
+                                                           int32_t* __restrict__ row_id_map,
+                                                           int32_t* __restrict__ perm_token,
+                                                           int T, int E, int k) {
+  // bits[e][w]: bit b set when token c*256 + 32w + b of this chunk goes to e
+  extern __shared__ uint32_t bits[];
+  constexpr int W = kChunkTok / 32;
+  const int c = blockIdx.x;
+  for (int i = threadIdx.x; i < E * W; i += 256) bits[i] = 0;
+  __syncthreads();
+  const int tl = threadIdx.x;
+  const int t = c * kChunkTok + tl;
+  int32_t my[16];
+  if (t < T) {
+    _Pragma("unroll") for (int j = 0; j < 16; ++j) if (j < k) {
+      my[j] = idx[int64_t(t) * k + j];
+      atomicOr(&bits[my[j] * W + (tl >> 5)], 1u << (tl & 31));
+    }
+  }
+  __syncthreads();
+  if (t < T) {
+    const int w = tl >> 5;
+    const uint32_t below = (1u << (tl & 31)) - 1u;
+    _Pragma("unroll") for (int j = 0; j < 16; ++j) if (j < k) {
+      const int e = my[j];
+      const uint32_t* be = bits + e * W;
+      int rank = __popc(be[w] & below);
+      for (int i = 0; i < w; ++i) rank += __popc(be[i]);
+      const int32_t row = chunk_base[int64_t(c) * E + e] + rank;
+      row_id_map[int64_t(t) * k + j] = row;
+      perm_token[row] = t;
+    }
+  }
+}
+
+// --- 4. gather: x_perm[row_id_map[t,j]] = x[t] -----------------------------
+// One group of G = d/VEC threads per token, 16 bytes per thread per step.
+template <typename T>
+__global__ __launch_bounds__(256) void dispatch_gather_kernel(const T* __restrict__ x,
+                                                              const int32_t* __restrict__ row_id_map,
+                                                              T* __restrict__ x_perm, int ntok,
+                                                              int d, int k, int tpb) {
+  constexpr int VEC = 16 / sizeof(T);
+  const int chunks = d / VEC;
+  const int per = 256 / tpb;  // threads per token
+  const int sub = threadIdx.x / per;
+  const int t = blockIdx.x * tpb + sub;
+  if (t >= ntok || sub >= tpb) return;
+  int32_t rows[16];
+  _Pragma("unroll") for (int j = 0; j < 16; ++j) if (j < k) rows[j] = row_id_map[int64_t(t) * k + j];
+  const uint4* src = reinterpret_cast<const uint4*>(x + int64_t(t) * d);
+  for (int ch = threadIdx.x % per; ch < chunks; ch += per) {
+    const uint4 v = src[ch];
+    _Pragma("unroll") for (int j = 0; j < 16; ++j) if (j < k)
+      reinterpret_cast<uint4*>(x_perm + int64_t(rows[j]) * d)[ch] = v;
+  }
+}
+
+// FP8 variant: each token is quantised once per 1 x 128 block (scale =
+// amax / 448, fp32 divide; 1 for an all-zero block; E4M3 round to nearest
+// even via v_cvt_pk_fp8_f32) and its codes and scales are written k times.
+// 16 lanes cover one 128-element block (8 bf16 per lane).
+__global__ __launch_bounds__(256) void dispatch_gather_fp8_kernel(
+    const bf16_t* __restrict__ x, const int32_t* __restrict__ row_id_map,
+    uint8_t* __restrict__ xq, float* __restrict__ xs, int ntok, int d, int k) {
+  const int t = blockIdx.x;
+  if (t >= ntok) return;
+  int32_t rows[16];
+  _Pragma("unroll") for (int j = 0; j < 16; ++j) if (j < k) rows[j] = row_id_map[int64_t(t) * k + j];
+  const int nblk = d / 128;
+  const int chunks = d / 8;
+  // all threads of the block iterate the same number of times so that the
+  // 16-lane shuffles always see full groups
+  for (int base = 0; base < chunks; base += 256) {
+    const int ch = base + threadIdx.x;
+    const bool ok = ch < chunks;
+    float v[8];
+    if (ok) Vec16<bf16_t>::load(x + int64_t(t) * d + int64_t(ch) * 8, v);
+    else
+      for (int i = 0; i < 8; ++i) v[i] = 0.0f;
+    float amax = 0.0f;
+    for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(v[i]));
+    for (int o = 8; o >= 1; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o, kWave));
+    const float scale = (amax == 0.0f) ? 1.0f : amax / 448.0f;
+    uint32_t lo = 0, hi = 0;
+    lo = __builtin_amdgcn_cvt_pk_fp8_f32(v[0] / scale, v[1] / scale, lo, false);
+    lo = __builtin_amdgcn_cvt_pk_fp8_f32(v[2] / scale, v[3] / scale, lo, true);
+    hi = __builtin_amdgcn_cvt_pk_fp8_f32(v[4] / scale, v[5] / scale, hi, false);
+    hi = __builtin_amdgcn_cvt_pk_fp8_f32(v[6] / scale, v[7] / scale, hi, true);
+    if (ok) {
+      const int blk = ch / 16;
+      _Pragma("unroll") for (int j = 0; j < 16; ++j) if (j < k) {
+        *reinterpret_cast<uint2*>(xq + int64_t(rows[j]) * d + int64_t(ch) * 8) = make_uint2(lo, hi);
+        if ((ch & 15) == 0) xs[int64_t(rows[j]) * nblk + blk] = scale;
+      }
+    }
+  }
+}
+
+static int tokens_per_block(int64_t d, int vec) {
+  const int64_t per = d / vec;
+  if (per >= 256) return 1;
+  int tpb = 1;
+  while (tpb * 2 * per <= 256) tpb *= 2;
+  return tpb;
+}
+
+void launch_dispatch(const DispatchLaunch& a, hipStream_t st) {
+  const int T = int(a.T), E = int(a.E), k = int(a.k);
+  const int nchunks = int(dispatch_chunks(a.T));
+  dispatch_count_kernel<<<nchunks, 256, sizeof(int32_t) * E, st>>>(a.idx, a.chunk_base, T, E, k);
+  dispatch_scan_kernel<<<1, 1024, 0, st>>>(a.chunk_base, a.counts, a.offsets, nchunks, E);
+  dispatch_pos_kernel<<<nchunks, 256, sizeof(uint32_t) * E * (kChunkTok / 32), st>>>(
+      a.idx, a.chunk_base, a.row_id_map, a.perm_token, T, E, k);
+  if (a.fp8) {
+    dispatch_gather_fp8_kernel<<<T, 256, 0, st>>>(reinterpret_cast<const bf16_t*>(a.x), a.row_id_map,
+                                                  reinterpret_cast<uint8_t*>(a.x_perm), a.x_scale, T,
+                                                  int(a.d), k);
+  } else if (a.act == 1) {
+    const int tpb = tokens_per_block(a.d, 8);
+    dispatch_gather_kernel<bf16_t><<<(T + tpb - 1) / tpb, 256, 0, st>>>(
+        reinterpret_cast<const bf16_t*>(a.x), a.row_id_map, reinterpret_cast<bf16_t*>(a.x_perm), T,
+        int(a.d), k, tpb);
+  } else {
+    const int tpb = tokens_per_block(a.d, 4);
+    dispatch_gather_kernel<float><<<(T + tpb - 1) / tpb, 256, 0, st>>>(
+        reinterpret_cast<const float*>(a.x), a.row_id_map, reinterpret_cast<float*>(a.x_perm), T,
+        int(a.d), k, tpb);
+  }
+}
+
+// --- combine / dispatch backward: per-token ordered gather ----------------
+// dst[t] = sum_j g[t,j] * src[row_id_map[t,j]] (+ add[t]), fp32 in slot
+// order, the added term last, one rounding.
+template <typename T>
+__global__ __launch_bounds__(256) void combine_kernel(const T* __restrict__ src,
+                                                      const int32_t* __restrict__ row_id_map,
+                                                      const float* __restrict__ gate,
+                                                      const T* __restrict__ add, T* __restrict__ dst,
+                                                      int ntok, int d, int k, int tpb) {
+  constexpr int VEC = 16 / sizeof(T);
+  const int chunks = d / VEC;
+  const int per = 256 / tpb;
+  const int sub = threadIdx.x / per;
+  const int t = blockIdx.x * tpb + sub;
+  if (t >= ntok || sub >= tpb) return;
+  int32_t rows[16];
+  float g[16];
+  _Pragma("unroll") for (int j = 0; j < 16; ++j) if (j < k) {
+    rows[j] = row_id_map[int64_t(t) * k + j];
+    g[j] = gate ? gate[int64_t(t) * k + j] : 1.0f;
+  }
+  for (int ch = threadIdx.x % per; ch < chunks; ch += per) {
+    float acc[VEC];
+    for (int i = 0; i < VEC; ++i) acc[i] = 0.0f;
+    _Pragma("unroll") for (int j = 0; j < 16; ++j) if (j < k) {
+      float v[VEC];
+      Vec16<T>::load(src + int64_t(rows[j]) * d + int64_t(ch) * VEC, v);
+      for (int i = 0; i < VEC; ++i) acc[i] = __builtin_fmaf(g[j], v[i], acc[i]);
+    }
+    if (add) {
+      float v[VEC];
+      Vec16<T>::load(add + int64_t(t) * d + int64_t(ch) * VEC, v);
+      for (int i = 0; i < VEC; ++i) acc[i] += v[i];
+    }
+    Vec16<T>::store(dst + int64_t(t) * d + int64_t(ch) * VEC, acc);
+  }
+}
+
+void launch_combine(const CombineLaunch& a, hipStream_t st) {
+  if (a.act == 1) {
+    const int tpb = tokens_per_block(a.d, 8);
+    combine_kernel<bf16_t><<<(a.T + tpb - 1) / tpb, 256, 0, st>>>(
+        reinterpret_cast<const bf16_t*>(a.src), a.row_id_map, a.gate,
+        reinterpret_cast<const bf16_t*>(a.add), reinterpret_cast<bf16_t*>(a.dst), int(a.T),
+        int(a.d), int(a.k), tpb);
+  } else {
+    const int tpb = tokens_per_block(a.d, 4);
+    combine_kernel<float><<<(a.T + tpb - 1) / tpb, 256, 0, st>>>(
+        reinterpret_cast<const float*>(a.src), a.row_id_map, a.gate,
+        reinterpret_cast<const float*>(a.add), reinterpret_cast<float*>(a.dst), int(a.T),
+        int(a.d), int(a.k), tpb);
+  }
+}
+
+// --- combine backward: one block per token --------------------------------
+template <typename T>
+__global__ __launch_bounds__(256) void combine_bwd_kernel(const T* __restrict__ dy,
+                                                          const T* __restrict__ out_perm,
+                                                          const int32_t* __restrict__ row_id_map,
+                                                          const float* __restrict__ gate,
+                                                          T* __restrict__ d_out, float* __restrict__ d_gate,
+                                                          int d, int k) {
+  constexpr int VEC = 16 / sizeof(T);
+  __shared__ float red[4][16];
+  const int t = blockIdx.x;
+  const int chunks = d / VEC;
+  int32_t rows[16];
+  float g[16], part[16];
+  for (int j = 0; j < 16; ++j) part[j] = 0.0f;
+  _Pragma("unroll") for (int j = 0; j < 16; ++j) if (j < k) {
+    rows[j] = row_id_map[int64_t(t) * k + j];
+    g[j] = gate[int64_t(t) * k + j];
+  }
+  for (int ch = threadIdx.x; ch < chunks; ch += 256) {
+    float dv[VEC];
+    Vec16<T>::load(dy + int64_t(t) * d + int64_t(ch) * VEC, dv);
+    _Pragma("unroll") for (int j = 0; j < 16; ++j) if (j < k) {
+      float o[VEC], w[VEC];
+      Vec16<T>::load(out_perm + int64_t(rows[j]) * d + int64_t(ch) * VEC, o);
+      float s = 0.0f;
+      for (int i = 0; i < VEC; ++i) {
+        s = __builtin_fmaf(dv[i], o[i], s);
+        w[i] = g[j] * dv[i];
+      }
+      part[j] += s;
+      Vec16<T>::store(d_out + int64_t(rows[j]) * d + int64_t(ch) * VEC, w);
+    }
+  }
+  const int wave = threadIdx.x / kWave;
+  _Pragma("unroll") for (int j = 0; j < 16; ++j) if (j < k) {
+    const float s = wave_sum(part[j]);
+    if (lane_id() == 0) red[wave][j] = s;
+  }
+  __syncthreads();
+  if (threadIdx.x < k) {
+    const int j = threadIdx.x;
+    d_gate[int64_t(t) * k + j] = ((red[0][j] + red[1][j]) + red[2][j]) + red[3][j];
+  }
+}
+
+void launch_combine_bwd(const CombineBwdLaunch& a, hipStream_t st) {
+  if (a.act == 1)
+    combine_bwd_kernel<bf16_t><<<a.T, 256, 0, st>>>(
+        reinterpret_cast<const bf16_t*>(a.dy), reinterpret_cast<const bf16_t*>(a.out_perm),
+        a.row_id_map, a.gate, reinterpret_cast<bf16_t*>(a.d_out_perm), a.d_gate, int(a.d), int(a.k));
+  else
+    combine_bwd_kernel<float><<<a.T, 256, 0, st>>>(
+        reinterpret_cast<const float*>(a.dy), reinterpret_cast<const float*>(a.out_perm),
+        a.row_id_map, a.gate, reinterpret_cast<float*>(a.d_out_perm), a.d_gate, int(a.d), int(a.k));
+}
+
+// --- FP8 block quantisation (weights 128x128, activations 1x128) ---------
+// One workgroup per block: amax by a fixed-order reduction, then codes.
+template <typename T>
+__global__ __launch_bounds__(256) void quant_blocks_kernel(const T* __restrict__ src, uint8_t* __restrict__ dst,
+                                                           float* __restrict__ scale, int64_t rows,
+                                                           int64_t cols, int br, int bc, int nbc) {
+  __shared__ float red[4];
+  const int64_t I = blockIdx.y, J = blockIdx.x;
+  const int64_t r0 = I * br, c0 = J * bc;
+  const int64_t r1 = min<int64_t>(r0 + br, rows), c1 = min<int64_t>(c0 + bc, cols);
+  const int w = int(c1 - c0);
+  const int n = int(r1 - r0) * w;
+  float amax = 0.0f;
+  for (int i = threadIdx.x; i < n; i += 256) {
+    const int64_t r = r0 + i / w, c = c0 + i % w;
+    amax = fmaxf(amax, fabsf(Elem<T>::load(src + r * cols + c)));
+  }
+  amax = wave_max(amax);
+  if (lane_id() == 0) red[threadIdx.x / kWave] = amax;
+  __syncthreads();
+  amax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  const float s = (amax == 0.0f) ? 1.0f : amax / 448.0f;
+  if (threadIdx.x == 0) scale[I * nbc + J] = s;
+  for (int i = threadIdx.x; i < n; i += 256) {
+    const int64_t r = r0 + i / w, c = c0 + i % w;
+    const float v = Elem<T>::load(src + r * cols + c) / s;
+    dst[r * cols + c] = uint8_t(__builtin_amdgcn_cvt_pk_fp8_f32(v, 0.0f, 0, false) & 0xff);
+  }
+}
+
+void launch_quant_blocks(const QuantLaunch& a, hipStream_t st) {
+  const int nbr = int((a.rows + a.br - 1) / a.br), nbc = int((a.cols + a.bc - 1) / a.bc);
+  const dim3 grid(nbc, nbr);
+  if (a.src_bf16)
+    quant_blocks_kernel<bf16_t><<<grid, 256, 0, st>>>(reinterpret_cast<const bf16_t*>(a.src), a.dst,
+                                                      a.scale, a.rows, a.cols, int(a.br), int(a.bc), nbc);
+  else
+    quant_blocks_kernel<float><<<grid, 256, 0, st>>>(reinterpret_cast<const float*>(a.src), a.dst,
+                                                     a.scale, a.rows, a.cols, int(a.br), int(a.bc), nbc);
+}
+
+}  // namespace moe

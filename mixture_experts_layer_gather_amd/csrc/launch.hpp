@@ -1,0 +1,136 @@
+// Internal launch interface between the C ABI (moe_api.hip) and the kernel
+// files. Arguments are validated by the caller; launchers only enqueue.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+struct RouteLaunch {
+  const void* x;
+  const float* w_router;
+  const float* bias;
+  float* logits;
+  int32_t* idx;
+  float* gate;
+  uint8_t* rmap;
+  int64_t T, d, E, k;
+  int score_fn, renorm;
+  float gate_scale;
+  int num_groups, topk_groups, group_score;
+  bool act_bf16;
+};
+void launch_route_fwd(const RouteLaunch& r, hipStream_t st);
+
+struct RouteBwdLaunch {
+  const void* x;
+  const float* w_router;
+  const float* logits;
+  const int32_t* idx;
+  const float* dgate;
+  void* dx;
+  float* dw_router;
+  float* dL;  // workspace [T,E]
+  int64_t T, d, E, k;
+  int score_fn, renorm;
+  float gate_scale;
+  bool act_bf16;
+};
+void launch_route_bwd(const RouteBwdLaunch& r, hipStream_t st);
+
+// Dispatch: histogram -> scan -> positions -> gather.
+struct DispatchLaunch {
+  const void* x;
+  const int32_t* idx;
+  int32_t* counts;
+  int32_t* offsets;
+  int32_t* row_id_map;
+  int32_t* perm_token;
+  void* x_perm;
+  float* x_scale;        // fp8 only
+  int32_t* chunk_base;   // workspace [nchunks, E]
+  int64_t T, d, E, k;
+  int act;               // 0 f32, 1 bf16
+  bool fp8;
+  int qblock;
+};
+void launch_dispatch(const DispatchLaunch& a, hipStream_t st);
+int64_t dispatch_chunks(int64_t T);
+
+struct CombineLaunch {
+  const void* src;       // out_perm (fwd) / dx_perm (dispatch bwd)
+  const int32_t* row_id_map;
+  const float* gate;     // null: unit gates (dispatch bwd)
+  const void* add;       // shared_out / dx_add, may be null
+  void* dst;
+  int64_t T, d, k;
+  int act;
+};
+void launch_combine(const CombineLaunch& a, hipStream_t st);
+
+struct CombineBwdLaunch {
+  const void* dy;
+  const void* out_perm;
+  const int32_t* row_id_map;
+  const float* gate;
+  void* d_out_perm;
+  float* d_gate;
+  int64_t T, d, k;
+  int act;
+};
+void launch_combine_bwd(const CombineBwdLaunch& a, hipStream_t st);
+
+// Grouped expert FFN.
+struct FfnLaunch {
+  const void* x_perm;
+  const float* x_scale;
+  const int32_t* offsets;
+  const void* w1;
+  const float* w1_scale;
+  const void* w2;
+  const float* w2_scale;
+  void* act_gu;
+  void* act_h;
+  float* h_scale;
+  void* out_perm;
+  int64_t A, d, f, E;
+  int act;   // 0 f32, 1 bf16
+  int wt;    // 0 f32, 1 bf16, 2 fp8
+  bool identity;
+};
+void launch_grouped_ffn(const FfnLaunch& a, hipStream_t st);
+
+struct FfnBwdLaunch {
+  const void* x_perm;
+  const float* x_scale;
+  const int32_t* offsets;
+  const void* w1;
+  const float* w1_scale;
+  const void* w2;
+  const float* w2_scale;
+  const void* act_gu;
+  const void* act_h;
+  const float* h_scale;
+  const void* d_out;
+  void* dx_perm;
+  void* dw1;
+  void* dw2;
+  void* d_gu;            // workspace [A, 2f] act
+  int64_t A, d, f, E;
+  int act;
+  int wt;
+  bool identity;
+};
+void launch_grouped_ffn_bwd(const FfnBwdLaunch& a, hipStream_t st);
+
+struct QuantLaunch {
+  const void* src;
+  int src_bf16;
+  int64_t rows, cols, br, bc;
+  uint8_t* dst;
+  float* scale;
+};
+void launch_quant_blocks(const QuantLaunch& a, hipStream_t st);
+
+}  // namespace moe

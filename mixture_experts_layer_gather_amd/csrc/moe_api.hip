@@ -1,0 +1,298 @@
+// C ABI of libmoe: host-side argument checks, workspace sizing and launches.
+// Every check runs before the first launch; no call reads device memory on
+// the host or synchronises (shapes stay on the device, Megatron Core MoE
+// summary, section 2.4, device-initiated kernels).
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/moe.h"
+#include "launch.hpp"
+
+namespace {
+
+using moe::dispatch_chunks;
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+size_t act_bytes(int dt) { return dt == MOE_DTYPE_F32 ? 4 : 2; }
+
+// Validates the configuration; returns MOE_OK or an error code.
+int check_cfg(const moe_config* c) {
+  if (!c) return MOE_ERR_INVALID_ARG;
+  if (c->num_tokens < 0 || c->num_tokens > (int64_t(1) << 26)) return MOE_ERR_INVALID_ARG;
+  if (c->hidden <= 0 || c->hidden % 128 != 0 || c->hidden > (1 << 20)) return MOE_ERR_INVALID_ARG;
+  if (c->ffn_hidden <= 0 || c->ffn_hidden % 128 != 0 || c->ffn_hidden > (1 << 20))
+    return MOE_ERR_INVALID_ARG;
+  if (c->num_experts < 1 || c->num_experts > 1024) return MOE_ERR_INVALID_ARG;
+  if (c->top_k < 1 || c->top_k > c->num_experts || c->top_k > 16) return MOE_ERR_INVALID_ARG;
+  if (c->num_tokens * c->top_k > (int64_t(1) << 30)) return MOE_ERR_INVALID_ARG;
+  if (c->score_fn != MOE_SCORE_SOFTMAX && c->score_fn != MOE_SCORE_SIGMOID) return MOE_ERR_INVALID_ARG;
+  if (c->renormalize != 0 && c->renormalize != 1) return MOE_ERR_INVALID_ARG;
+  if (!(c->gate_scale == c->gate_scale)) return MOE_ERR_INVALID_ARG;
+  if (c->num_groups < 1 || c->num_groups > 32 || c->num_experts % c->num_groups != 0)
+    return MOE_ERR_INVALID_ARG;
+  if (c->topk_groups < 1 || c->topk_groups > c->num_groups) return MOE_ERR_INVALID_ARG;
+  if (c->group_score != MOE_GROUP_TOP2_SUM && c->group_score != MOE_GROUP_MAX) return MOE_ERR_INVALID_ARG;
+  const bool grouped = c->num_groups > 1 && c->topk_groups < c->num_groups;
+  if (grouped) {
+    if (c->score_fn != MOE_SCORE_SIGMOID) return MOE_ERR_INVALID_ARG;
+    if (int64_t(c->topk_groups) * (c->num_experts / c->num_groups) < c->top_k) return MOE_ERR_INVALID_ARG;
+  }
+  if (c->ffn_mode != MOE_FFN_SWIGLU && c->ffn_mode != MOE_FFN_IDENTITY) return MOE_ERR_INVALID_ARG;
+  if (c->act_dtype != MOE_DTYPE_F32 && c->act_dtype != MOE_DTYPE_BF16) return MOE_ERR_UNSUPPORTED_DTYPE;
+  if (c->weight_dtype == MOE_DTYPE_FP8_E4M3) {
+    if (c->act_dtype != MOE_DTYPE_BF16) return MOE_ERR_UNSUPPORTED_DTYPE;
+    if (c->quant_block != 128) return MOE_ERR_INVALID_ARG;
+  } else if (c->weight_dtype != c->act_dtype) {
+    return MOE_ERR_UNSUPPORTED_DTYPE;
+  }
+  return MOE_OK;
+}
+
+#define MOE_CHECK(expr)          \
+  do {                           \
+    const int _rc = (expr);      \
+    if (_rc != MOE_OK) return _rc; \
+  } while (0)
+
+int need(const void* p) { return p ? MOE_OK : MOE_ERR_INVALID_ARG; }
+int align(const void* p) { return (!p || aligned16(p)) ? MOE_OK : MOE_ERR_ALIGNMENT; }
+
+template <typename... P>
+int align_all(P... ps) {
+  const void* arr[] = {static_cast<const void*>(ps)...};
+  for (const void* p : arr)
+    if (align(p) != MOE_OK) return MOE_ERR_ALIGNMENT;
+  return MOE_OK;
+}
+
+int launched() {
+  const hipError_t e = hipGetLastError();
+  return e == hipSuccess ? MOE_OK : MOE_ERR_HIP;
+}
+
+size_t round_up(size_t v) { return (v + 255) & ~size_t(255); }
+
+}  // namespace
+
+extern "C" {
+
+const char* moe_status_string(int status) {
+  switch (status) {
+    case MOE_OK: return "ok";
+    case MOE_ERR_INVALID_ARG: return "invalid argument";
+    case MOE_ERR_UNSUPPORTED_DTYPE: return "unsupported dtype combination";
+    case MOE_ERR_ALIGNMENT: return "pointer not 16-byte aligned";
+    case MOE_ERR_WORKSPACE: return "workspace missing or too small";
+    case MOE_ERR_HIP: return "HIP launch failed";
+    default: return "unknown status";
+  }
+}
+
+size_t moe_workspace_size(const moe_config* cfg, int op) {
+  if (check_cfg(cfg) != MOE_OK) return 0;
+  const int64_t T = cfg->num_tokens, E = cfg->num_experts, k = cfg->top_k, f = cfg->ffn_hidden;
+  switch (op) {
+    case MOE_OP_DISPATCH: return T ? round_up(size_t(dispatch_chunks(T)) * size_t(E) * 4) : 0;
+    case MOE_OP_GROUPED_FFN_BWD:
+      return round_up(size_t(T) * size_t(k) * size_t(2 * f) * act_bytes(cfg->act_dtype));
+    case MOE_OP_ROUTE_BWD: return round_up(size_t(T) * size_t(E) * 4);
+    default: return 0;
+  }
+}
+
+int moe_route(const moe_config* cfg, const void* x, const float* w_router, const float* expert_bias,
+              float* logits, int32_t* topk_idx, float* topk_gate, uint8_t* routing_map, void* ws,
+              size_t ws_bytes, void* stream) {
+  (void)ws;
+  (void)ws_bytes;
+  MOE_CHECK(check_cfg(cfg));
+  MOE_CHECK(need(x)); MOE_CHECK(need(w_router)); MOE_CHECK(need(logits));
+  MOE_CHECK(need(topk_idx)); MOE_CHECK(need(topk_gate));
+  MOE_CHECK(align(x)); MOE_CHECK(align(w_router)); MOE_CHECK(align(expert_bias));
+  MOE_CHECK(align(logits)); MOE_CHECK(align(topk_idx)); MOE_CHECK(align(topk_gate));
+  MOE_CHECK(align(routing_map));
+  if (cfg->num_tokens == 0) return MOE_OK;
+  moe::RouteLaunch r{};
+  r.x = x; r.w_router = w_router; r.bias = expert_bias; r.logits = logits;
+  r.idx = topk_idx; r.gate = topk_gate; r.rmap = routing_map;
+  r.T = cfg->num_tokens; r.d = cfg->hidden; r.E = cfg->num_experts; r.k = cfg->top_k;
+  r.score_fn = cfg->score_fn; r.renorm = cfg->renormalize; r.gate_scale = cfg->gate_scale;
+  r.num_groups = cfg->num_groups; r.topk_groups = cfg->topk_groups; r.group_score = cfg->group_score;
+  r.act_bf16 = cfg->act_dtype == MOE_DTYPE_BF16;
+  moe::launch_route_fwd(r, static_cast<hipStream_t>(stream));
+  return launched();
+}
+
+int moe_dispatch(const moe_config* cfg, const void* x, const int32_t* topk_idx, int32_t* counts,
+                 int32_t* offsets, int32_t* row_id_map, int32_t* perm_token, void* x_perm,
+                 float* x_scale, void* ws, size_t ws_bytes, void* stream) {
+  MOE_CHECK(check_cfg(cfg));
+  const bool fp8 = cfg->weight_dtype == MOE_DTYPE_FP8_E4M3;
+  MOE_CHECK(need(x)); MOE_CHECK(need(topk_idx)); MOE_CHECK(need(counts)); MOE_CHECK(need(offsets));
+  MOE_CHECK(need(row_id_map)); MOE_CHECK(need(perm_token)); MOE_CHECK(need(x_perm));
+  if (fp8) MOE_CHECK(need(x_scale));
+  MOE_CHECK(align(x)); MOE_CHECK(align(topk_idx)); MOE_CHECK(align(counts)); MOE_CHECK(align(offsets));
+  MOE_CHECK(align(row_id_map)); MOE_CHECK(align(perm_token)); MOE_CHECK(align(x_perm));
+  MOE_CHECK(align(x_scale)); MOE_CHECK(align(ws));
+  if (cfg->num_tokens == 0) return MOE_OK;
+  if (!ws || ws_bytes < moe_workspace_size(cfg, MOE_OP_DISPATCH)) return MOE_ERR_WORKSPACE;
+  moe::DispatchLaunch a{};
+  a.x = x; a.idx = topk_idx; a.counts = counts; a.offsets = offsets; a.row_id_map = row_id_map;
+  a.perm_token = perm_token; a.x_perm = x_perm; a.x_scale = x_scale;
+  a.chunk_base = static_cast<int32_t*>(ws);
+  a.T = cfg->num_tokens; a.d = cfg->hidden; a.E = cfg->num_experts; a.k = cfg->top_k;
+  a.act = cfg->act_dtype == MOE_DTYPE_BF16 ? 1 : 0;
+  a.fp8 = fp8;
+  a.qblock = cfg->quant_block;
+  moe::launch_dispatch(a, static_cast<hipStream_t>(stream));
+  return launched();
+}
+
+int moe_grouped_ffn(const moe_config* cfg, const void* x_perm, const float* x_scale,
+                    const int32_t* offsets, const void* w1, const float* w1_scale, const void* w2,
+                    const float* w2_scale, void* act_gu, void* act_h, float* h_scale, void* out_perm,
+                    void* ws, size_t ws_bytes, void* stream) {
+  (void)ws;
+  (void)ws_bytes;
+  MOE_CHECK(check_cfg(cfg));
+  const bool identity = cfg->ffn_mode == MOE_FFN_IDENTITY;
+  const bool fp8 = cfg->weight_dtype == MOE_DTYPE_FP8_E4M3;
+  MOE_CHECK(need(x_perm)); MOE_CHECK(need(offsets)); MOE_CHECK(need(out_perm));
+  if (!identity) {
+    MOE_CHECK(need(w1)); MOE_CHECK(need(w2)); MOE_CHECK(need(act_gu)); MOE_CHECK(need(act_h));
+    if (fp8) {
+      MOE_CHECK(need(x_scale)); MOE_CHECK(need(w1_scale)); MOE_CHECK(need(w2_scale));
+      MOE_CHECK(need(h_scale));
+    }
+  }
+  MOE_CHECK(align_all(x_perm, x_scale, offsets, w1, w1_scale, w2, w2_scale, act_gu, act_h, h_scale, out_perm));
+  if (fp8 && !identity) return MOE_ERR_UNSUPPORTED_DTYPE;
+  if (cfg->num_tokens == 0) return MOE_OK;
+  moe::FfnLaunch a{};
+  a.x_perm = x_perm; a.x_scale = x_scale; a.offsets = offsets; a.w1 = w1; a.w1_scale = w1_scale;
+  a.w2 = w2; a.w2_scale = w2_scale; a.act_gu = act_gu; a.act_h = act_h; a.h_scale = h_scale;
+  a.out_perm = out_perm;
+  a.A = cfg->num_tokens * cfg->top_k; a.d = cfg->hidden; a.f = cfg->ffn_hidden; a.E = cfg->num_experts;
+  a.act = cfg->act_dtype == MOE_DTYPE_BF16 ? 1 : 0;
+  a.wt = cfg->weight_dtype == MOE_DTYPE_F32 ? 0 : (cfg->weight_dtype == MOE_DTYPE_BF16 ? 1 : 2);
+  a.identity = identity;
+  moe::launch_grouped_ffn(a, static_cast<hipStream_t>(stream));
+  return launched();
+}
+
+int moe_combine(const moe_config* cfg, const void* out_perm, const int32_t* row_id_map,
+                const float* topk_gate, const void* shared_out, void* y, void* stream) {
+  MOE_CHECK(check_cfg(cfg));
+  MOE_CHECK(need(out_perm)); MOE_CHECK(need(row_id_map)); MOE_CHECK(need(topk_gate)); MOE_CHECK(need(y));
+  MOE_CHECK(align_all(out_perm, row_id_map, topk_gate, shared_out, y));
+  if (cfg->num_tokens == 0) return MOE_OK;
+  moe::CombineLaunch a{};
+  a.src = out_perm; a.row_id_map = row_id_map; a.gate = topk_gate; a.add = shared_out; a.dst = y;
+  a.T = cfg->num_tokens; a.d = cfg->hidden; a.k = cfg->top_k;
+  a.act = cfg->act_dtype == MOE_DTYPE_BF16 ? 1 : 0;
+  moe::launch_combine(a, static_cast<hipStream_t>(stream));
+  return launched();
+}
+
+int moe_combine_bwd(const moe_config* cfg, const void* dy, const void* out_perm,
+                    const int32_t* row_id_map, const float* topk_gate, void* d_out_perm, float* d_gate,
+                    void* stream) {
+  MOE_CHECK(check_cfg(cfg));
+  MOE_CHECK(need(dy)); MOE_CHECK(need(out_perm)); MOE_CHECK(need(row_id_map)); MOE_CHECK(need(topk_gate));
+  MOE_CHECK(need(d_out_perm)); MOE_CHECK(need(d_gate));
+  MOE_CHECK(align_all(dy, out_perm, row_id_map, topk_gate, d_out_perm, d_gate));
+  if (cfg->num_tokens == 0) return MOE_OK;
+  moe::CombineBwdLaunch a{};
+  a.dy = dy; a.out_perm = out_perm; a.row_id_map = row_id_map; a.gate = topk_gate;
+  a.d_out_perm = d_out_perm; a.d_gate = d_gate;
+  a.T = cfg->num_tokens; a.d = cfg->hidden; a.k = cfg->top_k;
+  a.act = cfg->act_dtype == MOE_DTYPE_BF16 ? 1 : 0;
+  moe::launch_combine_bwd(a, static_cast<hipStream_t>(stream));
+  return launched();
+}
+
+int moe_grouped_ffn_bwd(const moe_config* cfg, const void* x_perm, const float* x_scale,
+                        const int32_t* offsets, const void* w1, const float* w1_scale, const void* w2,
+                        const float* w2_scale, const void* act_gu, const void* act_h,
+                        const float* h_scale, const void* d_out_perm, void* dx_perm, void* dw1, void* dw2,
+                        void* ws, size_t ws_bytes, void* stream) {
+  MOE_CHECK(check_cfg(cfg));
+  const bool identity = cfg->ffn_mode == MOE_FFN_IDENTITY;
+  const bool fp8 = cfg->weight_dtype == MOE_DTYPE_FP8_E4M3;
+  MOE_CHECK(need(d_out_perm)); MOE_CHECK(need(dx_perm)); MOE_CHECK(need(dw1)); MOE_CHECK(need(dw2));
+  MOE_CHECK(need(offsets));
+  if (!identity) {
+    MOE_CHECK(need(x_perm)); MOE_CHECK(need(w1)); MOE_CHECK(need(w2)); MOE_CHECK(need(act_gu));
+    MOE_CHECK(need(act_h));
+    if (fp8) {
+      MOE_CHECK(need(x_scale)); MOE_CHECK(need(w1_scale)); MOE_CHECK(need(w2_scale));
+      MOE_CHECK(need(h_scale));
+    }
+  }
+  MOE_CHECK(align_all(x_perm, x_scale, offsets, w1, w1_scale, w2, w2_scale, act_gu, act_h, h_scale, d_out_perm, dx_perm, dw1, dw2, ws));
+  if (fp8 && !identity) return MOE_ERR_UNSUPPORTED_DTYPE;
+  if (cfg->num_tokens == 0) return MOE_OK;
+  if (!identity && (!ws || ws_bytes < moe_workspace_size(cfg, MOE_OP_GROUPED_FFN_BWD)))
+    return MOE_ERR_WORKSPACE;
+  moe::FfnBwdLaunch a{};
+  a.x_perm = x_perm; a.x_scale = x_scale; a.offsets = offsets; a.w1 = w1; a.w1_scale = w1_scale;
+  a.w2 = w2; a.w2_scale = w2_scale; a.act_gu = act_gu; a.act_h = act_h; a.h_scale = h_scale;
+  a.d_out = d_out_perm; a.dx_perm = dx_perm; a.dw1 = dw1; a.dw2 = dw2; a.d_gu = ws;
+  a.A = cfg->num_tokens * cfg->top_k; a.d = cfg->hidden; a.f = cfg->ffn_hidden; a.E = cfg->num_experts;
+  a.act = cfg->act_dtype == MOE_DTYPE_BF16 ? 1 : 0;
+  a.wt = cfg->weight_dtype == MOE_DTYPE_F32 ? 0 : (cfg->weight_dtype == MOE_DTYPE_BF16 ? 1 : 2);
+  a.identity = identity;
+  moe::launch_grouped_ffn_bwd(a, static_cast<hipStream_t>(stream));
+  return launched();
+}
+
+int moe_dispatch_bwd(const moe_config* cfg, const void* dx_perm, const int32_t* row_id_map, const void* dx_add,
+                     void* dx, void* stream) {
+  MOE_CHECK(check_cfg(cfg));
+  MOE_CHECK(need(dx_perm)); MOE_CHECK(need(row_id_map)); MOE_CHECK(need(dx));
+  MOE_CHECK(align_all(dx_perm, row_id_map, dx_add, dx));
+  if (cfg->num_tokens == 0) return MOE_OK;
+  moe::CombineLaunch a{};
+  a.src = dx_perm; a.row_id_map = row_id_map; a.gate = nullptr; a.add = dx_add; a.dst = dx;
+  a.T = cfg->num_tokens; a.d = cfg->hidden; a.k = cfg->top_k;
+  a.act = cfg->act_dtype == MOE_DTYPE_BF16 ? 1 : 0;
+  moe::launch_combine(a, static_cast<hipStream_t>(stream));
+  return launched();
+}
+
+int moe_route_bwd(const moe_config* cfg, const void* x, const float* w_router, const float* logits,
+                  const int32_t* topk_idx, const float* topk_gate, const float* d_gate, void* dx,
+                  float* dw_router, void* ws, size_t ws_bytes, void* stream) {
+  MOE_CHECK(check_cfg(cfg));
+  MOE_CHECK(need(x)); MOE_CHECK(need(w_router)); MOE_CHECK(need(logits)); MOE_CHECK(need(topk_idx));
+  MOE_CHECK(need(topk_gate)); MOE_CHECK(need(d_gate)); MOE_CHECK(need(dx)); MOE_CHECK(need(dw_router));
+  MOE_CHECK(align_all(x, w_router, logits, topk_idx, topk_gate, d_gate, dx, dw_router, ws));
+  if (cfg->num_tokens == 0) return MOE_OK;
+  if (!ws || ws_bytes < moe_workspace_size(cfg, MOE_OP_ROUTE_BWD)) return MOE_ERR_WORKSPACE;
+  moe::RouteBwdLaunch r{};
+  r.x = x; r.w_router = w_router; r.logits = logits; r.idx = topk_idx; r.dgate = d_gate;
+  r.dx = dx; r.dw_router = dw_router; r.dL = static_cast<float*>(ws);
+  r.T = cfg->num_tokens; r.d = cfg->hidden; r.E = cfg->num_experts; r.k = cfg->top_k;
+  r.score_fn = cfg->score_fn; r.renorm = cfg->renormalize; r.gate_scale = cfg->gate_scale;
+  r.act_bf16 = cfg->act_dtype == MOE_DTYPE_BF16;
+  moe::launch_route_bwd(r, static_cast<hipStream_t>(stream));
+  return launched();
+}
+
+int moe_quantize_fp8_blockwise(const void* src, int src_dtype, int64_t rows, int64_t cols, int64_t block_r,
+                               int64_t block_c, uint8_t* dst, float* scale, void* stream) {
+  if (src_dtype != MOE_DTYPE_F32 && src_dtype != MOE_DTYPE_BF16) return MOE_ERR_UNSUPPORTED_DTYPE;
+  if (rows < 0 || cols < 0 || block_r < 1 || block_c < 1 || block_r * block_c > (1 << 20))
+    return MOE_ERR_INVALID_ARG;
+  if (rows == 0 || cols == 0) return MOE_OK;
+  MOE_CHECK(need(src)); MOE_CHECK(need(dst)); MOE_CHECK(need(scale));
+  if ((rows + block_r - 1) / block_r > 65535) return MOE_ERR_INVALID_ARG;
+  moe::QuantLaunch q{};
+  q.src = src; q.src_bf16 = src_dtype == MOE_DTYPE_BF16; q.rows = rows; q.cols = cols;
+  q.br = block_r; q.bc = block_c; q.dst = dst; q.scale = scale;
+  moe::launch_quant_blocks(q, static_cast<hipStream_t>(stream));
+  return launched();
+}
+
+}  // extern "C"

@@ -1,0 +1,504 @@
+// Router forward and backward kernels (gfx950).
+//
+// Router scoring, top-k selection and gates: a router chooses a few experts
+// per token (Megatron Core MoE summary, "O essencial" and technical summary
+// section 1); routing is fused with the permutation bookkeeping to cut
+// launches (same page, section 2.4, kernel fusion).
+//
+// The logits use a fixed fp32 order so that selection is reproducible bit for
+// bit: every output is its own fused multiply-add recurrence over the hidden
+// index in ascending order. Work is split over outputs only (no split of the
+// hidden dimension, no cross-lane sum), staged through LDS in chunks.
+//
+// This file is compiled with -ffp-contract=off.
+#include "common.hpp"
+#include "launch.hpp"
+
+namespace moe {
+
+// ---------------------------------------------------------------------------
+// VALU GEMM with a sequential contraction: C[m][n] = sum_k A(m,k) B(k,n),
+// one fused multiply-add per k in ascending order, per output.
+//   A_MK: A(m,k) = A[m*lda + k], else A[k*lda + m]
+//   B_NK: B(k,n) = B[n*ldb + k], else B[k*ldb + n]
+// ---------------------------------------------------------------------------
+enum { VEPI_STORE = 0, VEPI_ADD_ACT = 1 };
+
+struct VArgs {
+  const void* A;
+  int64_t lda;
+  const void* B;
+  int64_t ldb;
+  void* C;
+  int64_t ldc;
+  const float* bias;  // [N] or null, added once after the contraction
+  int M, N, K;
+};
+
+template <typename T>
+__device__ __forceinline__ float ld_elem(const void* p, int64_t i) {
+  return Elem<T>::load(reinterpret_cast<const T*>(p) + i);
+}
+
+template <typename TA, bool A_MK, typename TB, bool B_NK, typename TC, int TM, int TN,
+          int RM, int RN, int KC, int EPI>
+__global__ __launch_bounds__(256) void vgemm_kernel(VArgs a) {
+  static_assert((TM / RM) * (TN / RN) == 256, "256 threads");
+  __shared__ float As[KC][TM + 4];
+  __shared__ float Bs[KC][TN + 4];
+  const int tid = threadIdx.x;
+  const int m0 = blockIdx.y * TM;
+  const int n0 = blockIdx.x * TN;
+  const int tn = tid % (TN / RN);
+  const int tm = tid / (TN / RN);
+  float acc[RM][RN];
+#pragma unroll
+  for (int i = 0; i < RM; ++i)
+#pragma unroll
+    for (int j = 0; j < RN; ++j) acc[i][j] = 0.0f;
+
+  for (int k0 = 0; k0 < a.K; k0 += KC) {
+    // stage A chunk as As[k][m]
+    for (int idx = tid; idx < TM * KC; idx += 256) {
+      int m, kk;
+      if (A_MK) { m = idx / KC; kk = idx % KC; }
+      else { kk = idx / TM; m = idx % TM; }
+      const int gm = m0 + m, gk = k0 + kk;
+      float v = 0.0f;
+      if (gm < a.M && gk < a.K)
+        v = A_MK ? ld_elem<TA>(a.A, int64_t(gm) * a.lda + gk)
+                 : ld_elem<TA>(a.A, int64_t(gk) * a.lda + gm);
+      As[kk][m] = v;
+    }
+    for (int idx = tid; idx < TN * KC; idx += 256) {
+      int n, kk;
+      if (B_NK) { n = idx / KC; kk = idx % KC; }
+      else { kk = idx / TN; n = idx % TN; }
+      const int gn = n0 + n, gk = k0 + kk;
+      float v = 0.0f;
+      if (gn < a.N && gk < a.K)
+        v = B_NK ? ld_elem<TB>(a.B, int64_t(gn) * a.ldb + gk)
+                 : ld_elem<TB>(a.B, int64_t(gk) * a.ldb + gn);
+      Bs[kk][n] = v;
+    }
+    __syncthreads();
+    const int kend = min(KC, a.K - k0);
+    for (int kk = 0; kk < kend; ++kk) {
+      float av[RM], bv[RN];
+#pragma unroll
+      for (int i = 0; i < RM; ++i) av[i] = As[kk][tm * RM + i];
+#pragma unroll
+      for (int j = 0; j < RN; ++j) bv[j] = Bs[kk][tn * RN + j];
+#pragma unroll
+      for (int i = 0; i < RM; ++i)
+#pragma unroll
+        for (int j = 0; j < RN; ++j) acc[i][j] = __builtin_fmaf(av[i], bv[j], acc[i][j]);
+    }
+    __syncthreads();
+  }
+
+#pragma unroll
+  for (int i = 0; i < RM; ++i) {
+    const int gm = m0 + tm * RM + i;
+    if (gm >= a.M) continue;
+#pragma unroll
+    for (int j = 0; j < RN; ++j) {
+      const int gn = n0 + tn * RN + j;
+      if (gn >= a.N) continue;
+      float v = acc[i][j];
+      if (EPI == VEPI_STORE) {
+        if (a.bias) v = v + a.bias[gn];
+        reinterpret_cast<float*>(a.C)[int64_t(gm) * a.ldc + gn] = v;
+      } else {
+        TC* c = reinterpret_cast<TC*>(a.C) + int64_t(gm) * a.ldc + gn;
+        Elem<TC>::store(c, Elem<TC>::load(c) + v);
+      }
+    }
+  }
+}
+
+template <typename TA, bool A_MK, typename TB, bool B_NK, typename TC, int EPI>
+static void launch_vgemm(const VArgs& a, hipStream_t st) {
+  if (a.N <= 16) {
+    constexpr int TM = 16, TN = 16;
+    dim3 grid((a.N + TN - 1) / TN, (a.M + TM - 1) / TM);
+    vgemm_kernel<TA, A_MK, TB, B_NK, TC, TM, TN, 1, 1, 32, EPI><<<grid, 256, 0, st>>>(a);
+  } else {
+    constexpr int TM = 64, TN = 64;
+    dim3 grid((a.N + TN - 1) / TN, (a.M + TM - 1) / TM);
+    vgemm_kernel<TA, A_MK, TB, B_NK, TC, TM, TN, 4, 4, 32, EPI><<<grid, 256, 0, st>>>(a);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Selection: one wave per token. 64-bit keys (ordered logit << 32 | ~expert)
+// make "larger logit first, lower expert on ties" a plain unsigned maximum.
+// -0 is folded into +0; NaN maps below every number; 0 means "not eligible".
+// ---------------------------------------------------------------------------
+constexpr int kMaxK = 16;
+
+__device__ __forceinline__ uint64_t make_key(float L, int e) {
+  uint32_t u = __float_as_uint(L);
+  uint32_t ord;
+  if (L != L) ord = 0u;
+  else {
+    if (u == 0x80000000u) u = 0u;
+    ord = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  }
+  return (uint64_t(ord) << 32) | uint64_t(0xFFFFFFFFu - uint32_t(e));
+}
+
+__device__ __forceinline__ float key_logit(uint64_t key) {
+  const uint32_t ord = uint32_t(key >> 32);
+  const uint32_t u = (ord & 0x80000000u) ? (ord & 0x7FFFFFFFu) : ~ord;
+  return __uint_as_float(u);
+}
+
+__device__ __forceinline__ int key_expert(uint64_t key) {
+  return int(0xFFFFFFFFu - uint32_t(key));
+}
+
+// (Sa, a) strictly above (Sb, b): larger first, NaN last, then lower index.
+__device__ __forceinline__ bool score_above(float Sa, int a, float Sb, int b) {
+  const bool na = Sa != Sa, nb = Sb != Sb;
+  if (na != nb) return nb;
+  if (!na && Sa != Sb) return Sa > Sb;
+  return a < b;
+}
+
+struct SelArgs {
+  const float* logits;
+  int T, E, k;
+  int score_fn, renorm;
+  float gate_scale;
+  int num_groups, topk_groups, group_score;
+  int32_t* idx;
+  float* gate;
+  uint8_t* rmap;
+};
+
+template <int NPL>
+__global__ __launch_bounds__(256) void select_kernel(SelArgs s) {
+  const int wave = threadIdx.x / kWave;
+  const int lane = lane_id();
+  const int t = blockIdx.x * 4 + wave;
+  if (t >= s.T) return;
+  const float* Lrow = s.logits + int64_t(t) * s.E;
+
+  uint64_t key[NPL];
+  float Lv[NPL];
+#pragma unroll
+  for (int p = 0; p < NPL; ++p) {
+    const int e = lane + kWave * p;
+    if (e < s.E) {
+      Lv[p] = Lrow[e];
+      key[p] = make_key(Lv[p], e);
+    } else {
+      Lv[p] = 0.0f;
+      key[p] = 0;
+    }
+  }
+  // global best logit (softmax normaliser), before any group masking
+  uint64_t gbest = 0;
+#pragma unroll
+  for (int p = 0; p < NPL; ++p) gbest = key[p] > gbest ? key[p] : gbest;
+  gbest = wave_max_u64(gbest);
+
+  if (s.num_groups > 1 && s.topk_groups < s.num_groups) {
+    const int gs = s.E / s.num_groups;
+    float my_gscore = 0.0f;  // lane g holds the score of group g
+    for (int g = 0; g < s.num_groups; ++g) {
+      uint64_t m1 = 0;
+#pragma unroll
+      for (int p = 0; p < NPL; ++p) {
+        const int e = lane + kWave * p;
+        if (e < s.E && e / gs == g && key[p] > m1) m1 = key[p];
+      }
+      m1 = wave_max_u64(m1);
+      uint64_t m2 = 0;
+#pragma unroll
+      for (int p = 0; p < NPL; ++p) {
+        const int e = lane + kWave * p;
+        if (e < s.E && e / gs == g && key[p] != m1 && key[p] > m2) m2 = key[p];
+      }
+      m2 = wave_max_u64(m2);
+      float sc = sigmoid_spec(key_logit(m1));
+      if (s.group_score == 0 && gs > 1) sc = sc + sigmoid_spec(key_logit(m2));
+      if (lane == g) my_gscore = sc;
+    }
+    // keep the topk_groups best groups: larger score first, lower group on ties
+    uint32_t kept = 0;
+    for (int r = 0; r < s.topk_groups; ++r) {
+      uint64_t gk = (lane < s.num_groups && !((kept >> lane) & 1u)) ? make_key(my_gscore, lane) : 0;
+      gk = wave_max_u64(gk);
+      kept |= 1u << key_expert(gk);
+    }
+#pragma unroll
+    for (int p = 0; p < NPL; ++p) {
+      const int e = lane + kWave * p;
+      if (e < s.E && !((kept >> (e / gs)) & 1u)) key[p] = 0;
+    }
+  }
+
+  int sel_e[kMaxK];
+  float sel_L[kMaxK];
+  uint32_t mine = 0;  // bit p set: expert lane + 64p was selected
+#pragma unroll
+  for (int j = 0; j < kMaxK; ++j) {
+    if (j < s.k) {
+      uint64_t m = 0;
+#pragma unroll
+      for (int p = 0; p < NPL; ++p) m = key[p] > m ? key[p] : m;
+      m = wave_max_u64(m);
+      sel_e[j] = key_expert(m);
+      sel_L[j] = key_logit(m);
+#pragma unroll
+      for (int p = 0; p < NPL; ++p)
+        if (key[p] == m) {
+          key[p] = 0;
+          mine |= 1u << p;
+        }
+    } else {
+      sel_e[j] = 0;
+      sel_L[j] = 0.0f;
+    }
+  }
+
+  // gates
+  float g[kMaxK];
+  if (s.score_fn == 0) {  // softmax
+    if (s.renorm) {
+      const float m = sel_L[0];
+      float Z = 0.0f;
+#pragma unroll
+      for (int j = 0; j < kMaxK; ++j) {
+        g[j] = (j < s.k) ? exp_spec(sel_L[j] - m) : 0.0f;
+        Z = Z + g[j];
+      }
+#pragma unroll
+      for (int j = 0; j < kMaxK; ++j) g[j] = g[j] / Z * s.gate_scale;
+    } else {
+      const float m = key_logit(gbest);
+      float z = 0.0f;
+#pragma unroll
+      for (int p = 0; p < NPL; ++p)
+        if (lane + kWave * p < s.E) z += exp_spec(Lv[p] - m);
+      const float Z = wave_sum(z);
+#pragma unroll
+      for (int j = 0; j < kMaxK; ++j)
+        g[j] = (j < s.k) ? exp_spec(sel_L[j] - m) / Z * s.gate_scale : 0.0f;
+    }
+  } else {  // sigmoid
+    float Z = 0.0f;
+#pragma unroll
+    for (int j = 0; j < kMaxK; ++j) {
+      g[j] = (j < s.k) ? sigmoid_spec(sel_L[j]) : 0.0f;
+      Z = Z + g[j];
+    }
+#pragma unroll
+    for (int j = 0; j < kMaxK; ++j)
+      g[j] = s.renorm ? g[j] / Z * s.gate_scale : g[j] * s.gate_scale;
+  }
+
+#pragma unroll
+  for (int j = 0; j < kMaxK; ++j)
+    if (j < s.k && lane == j) {
+      s.idx[int64_t(t) * s.k + j] = sel_e[j];
+      s.gate[int64_t(t) * s.k + j] = g[j];
+    }
+  if (s.rmap) {
+#pragma unroll
+    for (int p = 0; p < NPL; ++p) {
+      const int e = lane + kWave * p;
+      if (e < s.E) s.rmap[int64_t(t) * s.E + e] = (mine >> p) & 1u;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Router backward, first step: dL [T,E] from d_gate, one wave per token.
+// ---------------------------------------------------------------------------
+struct DLArgs {
+  const float* logits;
+  const int32_t* idx;
+  const float* dgate;
+  float* dL;
+  int T, E, k;
+  int score_fn, renorm;
+  float gate_scale;
+};
+
+template <int NPL>
+__global__ __launch_bounds__(256) void dlogits_kernel(DLArgs a) {
+  const int wave = threadIdx.x / kWave;
+  const int lane = lane_id();
+  const int t = blockIdx.x * 4 + wave;
+  if (t >= a.T) return;
+  const float* Lrow = a.logits + int64_t(t) * a.E;
+  float dl[NPL];
+#pragma unroll
+  for (int p = 0; p < NPL; ++p) dl[p] = 0.0f;
+  int e_j[kMaxK];
+  float L_j[kMaxK], dg_j[kMaxK];
+#pragma unroll
+  for (int j = 0; j < kMaxK; ++j) {
+    if (j < a.k) {
+      e_j[j] = a.idx[int64_t(t) * a.k + j];
+      L_j[j] = Lrow[e_j[j]];
+      dg_j[j] = a.dgate[int64_t(t) * a.k + j];
+    } else {
+      e_j[j] = -1;
+      L_j[j] = 0.0f;
+      dg_j[j] = 0.0f;
+    }
+  }
+  const float c = a.gate_scale;
+  float sel_grad[kMaxK];  // dL for each selected slot (sparse rules)
+  bool dense = false;
+  if (a.score_fn == 0 && a.renorm) {
+    float m = L_j[0];
+#pragma unroll
+    for (int j = 1; j < kMaxK; ++j)
+      if (j < a.k) m = fmaxf(m, L_j[j]);
+    float q[kMaxK], Z = 0.0f;
+#pragma unroll
+    for (int j = 0; j < kMaxK; ++j) {
+      q[j] = (j < a.k) ? expf(L_j[j] - m) : 0.0f;
+      Z += q[j];
+    }
+    float S = 0.0f;
+#pragma unroll
+    for (int j = 0; j < kMaxK; ++j) {
+      q[j] /= Z;
+      S += q[j] * dg_j[j];
+    }
+#pragma unroll
+    for (int j = 0; j < kMaxK; ++j) sel_grad[j] = c * q[j] * (dg_j[j] - S);
+  } else if (a.score_fn == 0) {
+    dense = true;
+    float Lv[NPL];
+    float m = -__builtin_inff();
+#pragma unroll
+    for (int p = 0; p < NPL; ++p) {
+      const int e = lane + kWave * p;
+      Lv[p] = e < a.E ? Lrow[e] : -__builtin_inff();
+      m = fmaxf(m, Lv[p]);
+    }
+    m = wave_max(m);
+    float z = 0.0f;
+#pragma unroll
+    for (int p = 0; p < NPL; ++p)
+      if (lane + kWave * p < a.E) z += expf(Lv[p] - m);
+    const float Z = wave_sum(z);
+    float S = 0.0f;
+#pragma unroll
+    for (int j = 0; j < kMaxK; ++j)
+      if (j < a.k) S += expf(L_j[j] - m) / Z * dg_j[j];
+#pragma unroll
+    for (int p = 0; p < NPL; ++p) {
+      const int e = lane + kWave * p;
+      if (e >= a.E) continue;
+      float dhat = 0.0f;
+#pragma unroll
+      for (int j = 0; j < kMaxK; ++j)
+        if (j < a.k && e_j[j] == e) dhat = dg_j[j];
+      const float pe = expf(Lv[p] - m) / Z;
+      dl[p] = c * pe * (dhat - S);
+    }
+  } else {
+    float s[kMaxK], Z = 0.0f, S = 0.0f;
+#pragma unroll
+    for (int j = 0; j < kMaxK; ++j) {
+      s[j] = (j < a.k) ? 1.0f / (1.0f + expf(-L_j[j])) : 0.0f;
+      Z += s[j];
+      S += dg_j[j] * s[j];
+    }
+#pragma unroll
+    for (int j = 0; j < kMaxK; ++j) {
+      const float ds = a.renorm ? c * (dg_j[j] / Z - S / (Z * Z)) : c * dg_j[j];
+      sel_grad[j] = ds * s[j] * (1.0f - s[j]);
+    }
+  }
+  if (!dense) {
+#pragma unroll
+    for (int p = 0; p < NPL; ++p) {
+      const int e = lane + kWave * p;
+#pragma unroll
+      for (int j = 0; j < kMaxK; ++j)
+        if (j < a.k && e_j[j] == e) dl[p] = sel_grad[j];
+    }
+  }
+#pragma unroll
+  for (int p = 0; p < NPL; ++p) {
+    const int e = lane + kWave * p;
+    if (e < a.E) a.dL[int64_t(t) * a.E + e] = dl[p];
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Launchers
+// ---------------------------------------------------------------------------
+template <typename TX>
+static void route_fwd_t(const RouteLaunch& r, hipStream_t st) {
+  VArgs v{};
+  v.A = r.x; v.lda = r.d;
+  v.B = r.w_router; v.ldb = r.d;
+  v.C = r.logits; v.ldc = r.E;
+  v.bias = r.bias;
+  v.M = int(r.T); v.N = int(r.E); v.K = int(r.d);
+  launch_vgemm<TX, true, float, true, float, VEPI_STORE>(v, st);
+
+  SelArgs s{};
+  s.logits = r.logits; s.T = int(r.T); s.E = int(r.E); s.k = int(r.k);
+  s.score_fn = r.score_fn; s.renorm = r.renorm; s.gate_scale = r.gate_scale;
+  s.num_groups = r.num_groups; s.topk_groups = r.topk_groups; s.group_score = r.group_score;
+  s.idx = r.idx; s.gate = r.gate; s.rmap = r.rmap;
+  const dim3 grid((r.T + 3) / 4);
+  if (r.E <= 64) select_kernel<1><<<grid, 256, 0, st>>>(s);
+  else if (r.E <= 128) select_kernel<2><<<grid, 256, 0, st>>>(s);
+  else if (r.E <= 256) select_kernel<4><<<grid, 256, 0, st>>>(s);
+  else if (r.E <= 512) select_kernel<8><<<grid, 256, 0, st>>>(s);
+  else select_kernel<16><<<grid, 256, 0, st>>>(s);
+}
+
+void launch_route_fwd(const RouteLaunch& r, hipStream_t st) {
+  if (r.act_bf16) route_fwd_t<bf16_t>(r, st);
+  else route_fwd_t<float>(r, st);
+}
+
+template <typename TX>
+static void route_bwd_t(const RouteBwdLaunch& r, hipStream_t st) {
+  DLArgs d{};
+  d.logits = r.logits; d.idx = r.idx; d.dgate = r.dgate; d.dL = r.dL;
+  d.T = int(r.T); d.E = int(r.E); d.k = int(r.k);
+  d.score_fn = r.score_fn; d.renorm = r.renorm; d.gate_scale = r.gate_scale;
+  const dim3 grid((r.T + 3) / 4);
+  if (r.E <= 64) dlogits_kernel<1><<<grid, 256, 0, st>>>(d);
+  else if (r.E <= 128) dlogits_kernel<2><<<grid, 256, 0, st>>>(d);
+  else if (r.E <= 256) dlogits_kernel<4><<<grid, 256, 0, st>>>(d);
+  else if (r.E <= 512) dlogits_kernel<8><<<grid, 256, 0, st>>>(d);
+  else dlogits_kernel<16><<<grid, 256, 0, st>>>(d);
+
+  // dx[t,:] += sum_e dL[t,e] w[e,:]
+  VArgs v{};
+  v.A = r.dL; v.lda = r.E;
+  v.B = r.w_router; v.ldb = r.d;
+  v.C = r.dx; v.ldc = r.d;
+  v.M = int(r.T); v.N = int(r.d); v.K = int(r.E);
+  launch_vgemm<float, true, float, false, TX, VEPI_ADD_ACT>(v, st);
+
+  // dw[e,:] = sum_t dL[t,e] x[t,:]
+  VArgs w{};
+  w.A = r.dL; w.lda = r.E;
+  w.B = r.x; w.ldb = r.d;
+  w.C = r.dw_router; w.ldc = r.d;
+  w.M = int(r.E); w.N = int(r.d); w.K = int(r.T);
+  launch_vgemm<float, false, TX, false, float, VEPI_STORE>(w, st);
+}
+
+void launch_route_bwd(const RouteBwdLaunch& r, hipStream_t st) {
+  if (r.act_bf16) route_bwd_t<bf16_t>(r, st);
+  else route_bwd_t<float>(r, st);
+}
+
+}  // namespace moe

@@ -103,7 +103,14 @@ def as_f32(a) -> np.ndarray:
 
 
 def as_f64(a) -> np.ndarray:
-    return as_f32(a).astype(np.float64)
+    """Exact widening of stored values to fp64."""
+    try:
+        import torch
+        if isinstance(a, torch.Tensor):
+            return np.ascontiguousarray(a.detach().to("cpu", torch.float64).numpy())
+    except ImportError:  # pragma: no cover
+        pass
+    return np.asarray(a, dtype=np.float64)
 
 
 # ------------------------------------------------------------ fp32 specs
@@ -522,3 +529,33 @@ def rel_l2(a, b) -> float:
     if nb == 0.0:
         return 0.0 if na == 0.0 else float("inf")
     return float(na / nb)
+
+
+def ffn_wgrad_columns(X, W1, W2, dO, cols):
+    """Selected slices of one expert's weight gradients, over all its rows:
+    for each hidden feature n in `cols`, rows n (gate) and f+n (up) of dW1
+    and column n of dW2 — the same formulas as ffn_bwd evaluated only where
+    asked (fp64). Returns (dW1_rows [2*len(cols), d] ordered gate rows then
+    up rows, dW2_cols [d, len(cols)])."""
+    X = np.asarray(X, dtype=np.float64)
+    W1 = np.asarray(W1, dtype=np.float64)
+    W2 = np.asarray(W2, dtype=np.float64)
+    dO = np.asarray(dO, dtype=np.float64)
+    f = W2.shape[1]
+    cols = np.asarray(cols, dtype=np.int64)
+    G = X @ W1[cols].T                     # [M, c]
+    U = X @ W1[f + cols].T
+    dH = dO @ W2[:, cols]                  # [M, c]
+    s = sigmoid64(G)
+    H = G * s * U
+    dG = dH * U * s * (1.0 + G * (1.0 - s))
+    dU = dH * G * s
+    dW1_rows = np.concatenate([dG.T @ X, dU.T @ X], axis=0)
+    dW2_cols = dO.T @ H
+    return dW1_rows, dW2_cols
+
+
+def ffn_dx_rows(X, W1, W2, dO):
+    """dX for the given rows of one expert (fp64), as in ffn_bwd."""
+    GU, H, _ = ffn_fwd(X, W1, W2)
+    return ffn_bwd(X, W1, W2, GU, H, dO)[0]

@@ -1,0 +1,116 @@
+"""Host-side tests of the C ABI (no GPU needed): the library loads, exports
+every function include/moe.h declares, sizes workspaces from the config alone
+and rejects bad arguments before enqueueing anything."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def M():
+    import mixture_experts_layer_gather_amd as m
+    if not os.path.exists(m.LIB_PATH):
+        from mixture_experts_layer_gather_amd import build
+        build.build()
+    return m
+
+
+def _declared():
+    src = open(os.path.join(ROOT, "include", "moe.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_[a-z0-9_]+)\s*\(", src)))
+
+
+def test_exports_every_declared_symbol(M):
+    names = _declared()
+    assert len(names) == 11, names
+    L = M.lib()
+    for n in names:
+        assert hasattr(L, n), n
+    assert sorted(M.EXPORTS) == names
+    # nm view of the dynamic symbol table agrees
+    out = os.popen(f"nm -D --defined-only {M.LIB_PATH}").read()
+    for n in names:
+        assert re.search(rf"\bT {n}\b", out), n
+
+
+def _cfg(M, **kw):
+    base = dict(T=64, d=256, E=8, k=2, f=256, act="bf16", weight="bf16")
+    base.update(kw)
+    return M.make_config(**base)
+
+
+FAKE = 0x10000  # a 16-byte aligned address that is never dereferenced
+
+
+def _route(M, c, x=FAKE, ws=None):
+    L = M.lib()
+    return L.moe_route(ctypes.byref(c), x, FAKE, None, FAKE, FAKE, FAKE, None, ws, 0, None)
+
+
+def test_config_validation(M):
+    L = M.lib()
+    bad = [dict(k=9), dict(k=0), dict(d=200), dict(f=100), dict(E=0), dict(E=2000),
+           dict(T=-1), dict(k=17, E=32), dict(num_groups=3), dict(num_groups=4, topk_groups=5),
+           dict(num_groups=4, topk_groups=2, score="softmax"),
+           dict(E=16, k=5, num_groups=4, topk_groups=1, score="sigmoid")]
+    for kw in bad:
+        assert _route(M, _cfg(M, **kw)) == -1, kw
+    assert _route(M, _cfg(M, act="f32", weight="bf16")) == -2
+    assert _route(M, _cfg(M, act="f32", weight="fp8")) == -2
+    assert _route(M, _cfg(M, weight="fp8", quant_block=64)) == -1
+    assert L.moe_workspace_size(ctypes.byref(_cfg(M, k=9)), 1) == 0
+
+
+def test_empty_batch_enqueues_nothing(M):
+    c = _cfg(M, T=0)
+    L = M.lib()
+    assert _route(M, c) == 0
+    assert L.moe_dispatch(ctypes.byref(c), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, None, 0,
+                          None) == 0
+    assert L.moe_combine(ctypes.byref(c), FAKE, FAKE, FAKE, None, FAKE, None) == 0
+
+
+def test_null_alignment_and_workspace_errors(M):
+    L = M.lib()
+    c = _cfg(M)
+    assert _route(M, c, x=None) == -1
+    assert _route(M, c, x=FAKE + 4) == -3
+    # dispatch with a missing / short workspace
+    assert L.moe_dispatch(ctypes.byref(c), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, None, 0,
+                          None) == -4
+    need = L.moe_workspace_size(ctypes.byref(c), 1)
+    assert need > 0
+    assert L.moe_dispatch(ctypes.byref(c), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE,
+                          need - 1, None) == -4
+    # fp8 dispatch needs the scale output
+    c8 = _cfg(M, weight="fp8")
+    assert L.moe_dispatch(ctypes.byref(c8), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE,
+                          need, None) == -1
+    # route backward workspace
+    assert L.moe_route_bwd(ctypes.byref(c), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, 0,
+                           None) == -4
+    # quantiser arguments
+    assert L.moe_quantize_fp8_blockwise(FAKE, 7, 4, 4, 1, 1, FAKE, FAKE, None) == -2
+    assert L.moe_quantize_fp8_blockwise(FAKE, 1, 4, 4, 0, 1, FAKE, FAKE, None) == -1
+
+
+def test_workspace_sizes_follow_the_config(M):
+    L = M.lib()
+    c = _cfg(M, T=1000, E=16, k=4, f=384, d=512)
+    ws = lambda op: L.moe_workspace_size(ctypes.byref(c), op)
+    assert ws(0) == 0 and ws(2) == 0
+    assert ws(1) >= ((1000 + 255) // 256) * 16 * 4
+    assert ws(3) >= 1000 * 4 * 2 * 384 * 2
+    assert ws(4) >= 1000 * 16 * 4
+    assert all(ws(op) % 256 == 0 for op in range(5))
+
+
+def test_status_strings(M):
+    assert M.moe_status_string(0) == "ok"
+    assert "workspace" in M.moe_status_string(-4)
+    assert M.moe_status_string(-99) == "unknown status"

@@ -1,0 +1,318 @@
+"""GPU parity of the HIP path (through the C ABI) against the CPU oracle.
+
+Integer and index outputs (logits under the fixed fp32 order, top-k indices,
+counts, offsets, row map, token permutation, dispatched rows) are compared bit
+for bit; floating-point outputs by relative L2 error against the fp64 oracle
+with the tolerance of their precision: 1e-5 (fp32), 2e-2 (bf16), 6e-2 (fp8).
+Small layers are compared on every element; full-size layers on every
+routing/dispatch element, the whole forward output, and sampled gradients
+that the oracle evaluates one slice at a time.
+"""
+import os
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import moe_synth as S
+import oracle
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"f32": 1e-5, "bf16": 2e-2, "fp8": 6e-2}
+DEV = "cuda"
+
+
+def _say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def _tol(cfg):
+    return TOL["fp8"] if cfg.weight == "fp8" else TOL[cfg.act]
+
+
+def _np(t):
+    if t.dtype in (torch.int32, torch.int64, torch.uint8):
+        return t.cpu().numpy()
+    return t.float().cpu().numpy()
+
+
+def _inputs(cfg, threads=8):
+    w1, w2 = S.all_expert_weights(cfg, threads=threads)
+    inp = dict(x=S.x(cfg), wr=S.w_router(cfg), bias=S.router_bias(cfg), w1=w1, w2=w2,
+               dy=S.dy(cfg))
+    if cfg.shared:
+        inp.update(sw1=S.shared_w1(cfg), sw2=S.shared_w2(cfg))
+    return inp
+
+
+def _gpu_layer(cfg, inp, identity=False):
+    from mixture_experts_layer_gather_amd import MoELayer
+    layer = MoELayer(**cfg.describe(), identity=identity, device=DEV)
+    cu = lambda t: None if t is None else t.to(DEV)
+    layer.set_weights(cu(inp["wr"]), cu(inp["w1"]), cu(inp["w2"]), bias=cu(inp.get("bias")),
+                      sw1=cu(inp.get("sw1")), sw2=cu(inp.get("sw2")))
+    layer.step(cu(inp["x"]), cu(inp["dy"]))
+    torch.cuda.synchronize()
+    return layer
+
+
+def _check_routing_and_dispatch(cfg, layer, ref):
+    assert np.array_equal(_np(layer.logits), ref["logits"]), "logits not bit-exact"
+    assert np.array_equal(_np(layer.topk_idx), ref["idx"]), "top-k indices differ"
+    for name in ("counts", "offsets", "row_id_map", "perm_token"):
+        assert np.array_equal(_np(getattr(layer, name)), ref[name]), name
+    rm = _np(layer.routing_map)
+    exp = np.zeros((cfg.T, cfg.E), np.uint8)
+    np.put_along_axis(exp, ref["idx"].astype(np.int64), 1, axis=1)
+    assert np.array_equal(rm, exp), "routing map"
+    assert oracle.rel_l2(_np(layer.topk_gate), ref["gates"]) <= 1e-6, "gates"
+
+
+def _compare_small(cfg, identity=False, inp=None):
+    inp = inp or _inputs(cfg)
+    _say(f"[parity] {cfg.name} T={cfg.T} d={cfg.d} E={cfg.E} k={cfg.k} f={cfg.f} id={identity}")
+    layer = _gpu_layer(cfg, inp, identity)
+    ref = oracle.layer(cfg, inp, identity=identity)
+    _check_routing_and_dispatch(cfg, layer, ref)
+    if cfg.weight == "fp8":
+        assert np.array_equal(_np(layer.x_perm), ref["xq_perm"]), "fp8 dispatch codes"
+        assert np.array_equal(_np(layer.x_scale), ref["x_scale_perm"]), "fp8 dispatch scales"
+    else:
+        assert np.array_equal(_np(layer.x_perm), ref["x_perm"]), "x_perm"
+    tol = _tol(cfg)
+    pairs = [("y", layer.y, ref["y"]), ("d_gate", layer.d_gate, ref["d_gate"]),
+             ("dx", layer.dx, ref["dx"])]
+    if identity and cfg.renorm:
+        # every slot then sees the same d_gate, so the exact router gradient
+        # is zero: bound the GPU's against the scale of its factors instead
+        scale = np.linalg.norm(ref["d_gate"]) * np.linalg.norm(oracle.as_f64(inp["x"]))
+        assert np.linalg.norm(_np(layer.dw_router)) <= 1e-5 * scale
+    else:
+        pairs.append(("dw_router", layer.dw_router, ref["dw_router"]))
+    if not identity:
+        pairs += [("out_perm", layer.out_perm, ref["out_perm"]),
+                  ("dw1", layer.dw1, ref["dw1"]), ("dw2", layer.dw2, ref["dw2"])]
+        if cfg.shared:
+            pairs += [("shared_dw1", layer.s_dw1[0], ref["shared_dw1"]),
+                      ("shared_dw2", layer.s_dw2[0], ref["shared_dw2"])]
+    for name, got, want in pairs:
+        err = oracle.rel_l2(_np(got), want)
+        assert err <= tol, f"{name}: rel L2 {err:.3e} > {tol}"
+    if not identity:
+        # experts that received no rows must get exact zero gradients
+        empty = np.nonzero(ref["counts"] == 0)[0]
+        if empty.size:
+            assert not _np(layer.dw1[torch.as_tensor(empty)]).any()
+            assert not _np(layer.dw2[torch.as_tensor(empty)]).any()
+    return layer, ref
+
+
+# ------------------------------------------------------------ small layers
+
+SMALL = {
+    "tiny_fp32": S.CONFIGS[0],
+    "mixtral_mini": S.mini(S.CONFIGS[1], T=1000, d=256, f=384),
+    "mixtral_mini_f32": S.mini(S.CONFIGS[1], T=333, d=128, f=256).replace(act="f32", weight="f32"),
+    "deepseek_mini": S.mini(S.CONFIGS[2], T=300, d=256, f=256, E=32).replace(k=6),
+    "qwen_skew_mini": S.mini(S.CONFIGS[3], T=700, d=256, f=128, E=16).replace(k=4),
+}
+
+
+@pytest.mark.parametrize("name", list(SMALL))
+def test_small_layer_parity(name):
+    _compare_small(SMALL[name])
+
+
+@pytest.mark.parametrize("name", ["tiny_fp32", "deepseek_mini"])
+def test_identity_experts(name):
+    cfg = SMALL[name]
+    layer, ref = _compare_small(cfg, identity=True)
+    x = oracle.as_f64(S.x(cfg))
+    g = ref["gates"].sum(1, keepdims=True) + (1.0 if cfg.shared else 0.0)
+    assert oracle.rel_l2(_np(layer.y), g * x) <= _tol(cfg)
+
+
+def test_edge_shapes():
+    base = S.mini(S.CONFIGS[1], T=1, d=128, f=128, E=8)
+    for cfg in [base,                                    # a single token
+                base.replace(T=37, k=4, E=4, seed_base=40),    # k = E
+                base.replace(T=50, k=1, E=1, seed_base=41),    # one expert
+                base.replace(T=257, seed_base=42),             # chunk tail
+                base.replace(T=64, act="f32", weight="f32", k=3, seed_base=43)]:
+        _compare_small(cfg)
+
+
+def test_all_equal_logits_pick_lowest_indices():
+    cfg = S.mini(S.CONFIGS[1], T=100, d=128, f=128, E=8).replace(k=3)
+    inp = _inputs(cfg)
+    inp["wr"] = torch.zeros_like(inp["wr"])
+    layer, ref = _compare_small(cfg, inp=inp)
+    assert np.array_equal(_np(layer.topk_idx), np.tile(np.arange(3), (100, 1)))
+
+
+def test_deterministic_repeat():
+    cfg = SMALL["qwen_skew_mini"]
+    inp = _inputs(cfg)
+    a = _gpu_layer(cfg, inp)
+    outs = {n: _np(getattr(a, n)).copy() for n in ("y", "dx", "dw1", "dw2", "dw_router", "d_gate")}
+    b = _gpu_layer(cfg, inp)
+    for n, v in outs.items():
+        assert np.array_equal(v, _np(getattr(b, n))), n
+
+
+# ------------------------------------------------------------ fp8 pieces
+
+def test_fp8_block_quantiser_bit_exact():
+    from mixture_experts_layer_gather_amd import moe_quantize_fp8_blockwise
+    g = torch.Generator().manual_seed(11)
+    src = torch.randn(384, 640, generator=g) * torch.exp(torch.randn(384, 1, generator=g) * 3)
+    src[7, :128] = 0.0
+    src[9, 5] = 1e30
+    for br, bc in [(128, 128), (1, 128)]:
+        for dt in (torch.float32, torch.bfloat16):
+            s = src.to(dt)
+            q = torch.empty(384, 640, dtype=torch.uint8, device=DEV)
+            sc = torch.empty(384 // br, 640 // bc, dtype=torch.float32, device=DEV)
+            moe_quantize_fp8_blockwise(s.to(DEV), 384, 640, br, bc, q, sc)
+            torch.cuda.synchronize()
+            rq, rs = oracle.quant_blocks(oracle.as_f32(s), br, bc)
+            assert np.array_equal(_np(sc), rs), (br, bc, dt)
+            assert np.array_equal(_np(q), rq), (br, bc, dt)
+
+
+def test_fp8_encoder_exhaustive_in_range():
+    """Every fp32 value with |v| <= 448 quantised with scale 1 (a 1 x 2^k
+    block holding 448 fixes the scale to exactly 1)."""
+    from mixture_experts_layer_gather_amd import moe_quantize_fp8_blockwise
+    top = int(np.array(448.0, np.float32).view(np.uint32))
+    step = 1 << 24
+    for sign in (0, 1 << 31):
+        for lo in range(0, top + 1, step):
+            hi = min(lo + step, top + 1)
+            bits = (np.arange(lo, hi, dtype=np.uint64) | sign).astype(np.uint32)
+            v = bits.view(np.float32).copy()
+            n = v.size
+            cols = 1 << 20
+            pad = (-n) % cols
+            v = np.concatenate([v, np.zeros(pad, np.float32)]).reshape(-1, cols)
+            v[:, 0] = 448.0 if sign == 0 else -448.0   # pins amax, scale = 1
+            src = torch.from_numpy(v).to(DEV)
+            q = torch.empty(v.shape, dtype=torch.uint8, device=DEV)
+            sc = torch.empty(v.shape[0], 1, dtype=torch.float32, device=DEV)
+            moe_quantize_fp8_blockwise(src, v.shape[0], cols, 1, cols, q, sc)
+            torch.cuda.synchronize()
+            assert np.all(_np(sc) == 1.0)
+            assert np.array_equal(_np(q), oracle.e4m3_encode(v)), hex(lo | sign)
+
+
+def test_fp8_dispatch_bit_exact():
+    from mixture_experts_layer_gather_amd import make_config, moe_dispatch, workspace_size
+    cfg = S.mini(S.CONFIGS[4], T=300, d=512, f=256, E=32).replace(k=4)
+    x = S.x(cfg)
+    L, idx, _ = oracle.route(cfg, x, S.w_router(cfg))
+    counts, offsets, rmap, ptok = oracle.dispatch_index(idx, cfg.E)
+    xq, xs = oracle.quant_blocks(oracle.as_f32(x), 1, 128)
+    c = make_config(**cfg.describe())
+    A = cfg.A
+    out = dict(counts=torch.empty(cfg.E, dtype=torch.int32, device=DEV),
+               offsets=torch.empty(cfg.E + 1, dtype=torch.int32, device=DEV),
+               rmap=torch.empty(cfg.T, cfg.k, dtype=torch.int32, device=DEV),
+               ptok=torch.empty(A, dtype=torch.int32, device=DEV),
+               xq=torch.empty(A, cfg.d, dtype=torch.uint8, device=DEV),
+               xs=torch.empty(A, cfg.d // 128, dtype=torch.float32, device=DEV))
+    ws = torch.empty(workspace_size(c, 1), dtype=torch.uint8, device=DEV)
+    moe_dispatch(c, x.to(DEV), torch.from_numpy(idx).to(DEV), out["counts"], out["offsets"],
+                 out["rmap"], out["ptok"], out["xq"], out["xs"], ws)
+    torch.cuda.synchronize()
+    assert np.array_equal(_np(out["offsets"]), offsets)
+    assert np.array_equal(_np(out["rmap"]), rmap)
+    assert np.array_equal(_np(out["xq"]), oracle.permute(xq, rmap))
+    assert np.array_equal(_np(out["xs"]), oracle.permute(xs, rmap))
+
+
+# ------------------------------------------------------------ full sizes
+
+def _full_size_check(cfg, n_tok=24, n_cols=3):
+    _say(f"[full] {cfg.name}: generating inputs")
+    inp = _inputs(cfg, threads=16)
+    _say(f"[full] {cfg.name}: GPU layer")
+    layer = _gpu_layer(cfg, inp)
+    _say(f"[full] {cfg.name}: oracle routing")
+    L, idx, g = oracle.route(cfg, inp["x"], inp["wr"], inp.get("bias"))
+    counts, offsets, rmap, ptok = oracle.dispatch_index(idx, cfg.E)
+    ref = dict(logits=L, idx=idx, gates=g, counts=counts, offsets=offsets, row_id_map=rmap,
+               perm_token=ptok)
+    _check_routing_and_dispatch(cfg, layer, ref)
+    # dispatched rows: x_perm == x[perm_token], checked on the device
+    x_dev = inp["x"].to(DEV)
+    assert torch.equal(layer.x_perm, x_dev[layer.perm_token.long()]), "x_perm"
+    tol = _tol(cfg)
+    # full forward on the oracle, expert by expert
+    _say(f"[full] {cfg.name}: oracle forward")
+    X = oracle.as_f64(inp["x"])
+    O = np.zeros((cfg.A, cfg.d))
+    for e in range(cfg.E):
+        r0, r1 = offsets[e], offsets[e + 1]
+        if r1 > r0:
+            O[r0:r1] = oracle.ffn_fwd(X[ptok[r0:r1]], oracle.as_f64(inp["w1"][e]),
+                                      oracle.as_f64(inp["w2"][e]))[2]
+    O_sh = None
+    if cfg.shared:
+        O_sh = oracle.ffn_fwd(X, oracle.as_f64(inp["sw1"]), oracle.as_f64(inp["sw2"]))[2]
+    y = oracle.combine(O, rmap, g, O_sh)
+    err = oracle.rel_l2(_np(layer.y), y)
+    _say(f"[full] {cfg.name}: y rel L2 {err:.2e}")
+    assert err <= tol, f"y {err}"
+    # backward: d_gate, router gradients in full; dx on sampled tokens;
+    # weight gradients on sampled experts and features
+    dy = oracle.as_f64(inp["dy"])
+    dO, dgate = oracle.combine_bwd(dy, O, rmap, g)
+    assert oracle.rel_l2(_np(layer.d_gate), dgate) <= tol, "d_gate"
+    dL = oracle.route_bwd_logits(dgate, idx, L, cfg.score, cfg.renorm, cfg.gate_scale)
+    dWr, dx_r = oracle.route_bwd(dL, inp["x"], inp["wr"])
+    err = oracle.rel_l2(_np(layer.dw_router), dWr)
+    _say(f"[full] {cfg.name}: dw_router rel L2 {err:.2e}")
+    assert err <= tol, "dw_router"
+    rng = np.random.default_rng(cfg.seed_base)
+    toks = np.sort(rng.choice(cfg.T, n_tok, replace=False))
+    dx_s = dx_r[toks].copy()
+    by_e = {}
+    for ti, t in enumerate(toks):
+        for j in range(cfg.k):
+            by_e.setdefault(int(idx[t, j]), []).append((ti, int(rmap[t, j])))
+    for e, lst in by_e.items():
+        tis = np.array([a for a, _ in lst])
+        rs = np.array([b for _, b in lst])
+        dxe = oracle.ffn_dx_rows(X[toks[tis]], oracle.as_f64(inp["w1"][e]),
+                                 oracle.as_f64(inp["w2"][e]), dO[rs])
+        np.add.at(dx_s, tis, dxe)
+    if cfg.shared:
+        dx_s += oracle.ffn_dx_rows(X[toks], oracle.as_f64(inp["sw1"]), oracle.as_f64(inp["sw2"]),
+                                   dy[toks])
+    err = oracle.rel_l2(_np(layer.dx[torch.as_tensor(toks)]), dx_s)
+    _say(f"[full] {cfg.name}: dx (sampled) rel L2 {err:.2e}")
+    assert err <= tol, "dx"
+    nonempty = np.nonzero(counts)[0]
+    exps = {int(nonempty[0]), int(np.argmax(counts)), int(rng.choice(nonempty))}
+    for e in sorted(exps):
+        cols = np.sort(rng.choice(cfg.f, n_cols, replace=False))
+        r0, r1 = offsets[e], offsets[e + 1]
+        w1r, w2c = oracle.ffn_wgrad_columns(X[ptok[r0:r1]], oracle.as_f64(inp["w1"][e]),
+                                            oracle.as_f64(inp["w2"][e]), dO[r0:r1], cols)
+        rows = torch.as_tensor(np.concatenate([cols, cfg.f + cols]))
+        got1 = _np(layer.dw1[e][rows])
+        got2 = _np(layer.dw2[e][:, torch.as_tensor(cols)])
+        e1, e2 = oracle.rel_l2(got1, w1r), oracle.rel_l2(got2, w2c)
+        _say(f"[full] {cfg.name}: expert {e} ({counts[e]} rows) dW1 {e1:.2e} dW2 {e2:.2e}")
+        assert e1 <= tol and e2 <= tol
+    empty = np.nonzero(counts == 0)[0]
+    if empty.size:
+        assert not _np(layer.dw1[int(empty[0])]).any() and not _np(layer.dw2[int(empty[0])]).any()
+
+
+@pytest.mark.parametrize("which", [1, 2, 3])
+def test_full_size_layer(which):
+    _full_size_check(S.CONFIGS[which])
