@@ -36,7 +36,7 @@ template <> struct Mfma<bf16_t> {
   static constexpr int MK = 32;  // K per instruction
   typedef bf16x8_t frag;
   static __device__ __forceinline__ frag load(const bf16_t* p) {
-    return __builtin_bit_cast(frag, *reinterpret_cast<const uint4*>(p));
+    return __builtin_bit_cast(frag, *reinterpret_cast<const u32x4*>(p));
   }
   static __device__ __forceinline__ f32x4_t mma(frag a, frag b, f32x4_t c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
@@ -130,23 +130,82 @@ __device__ void find_group(const int32_t* __restrict__ offsets, int G, int tiles
   __syncthreads();
 }
 
+// LDS tiles hold ROWS x BK elements per operand, K-contiguous, without
+// padding. The 16-byte chunks of each row are XOR-swizzled with the row so
+// that both the MFMA fragment reads (16 consecutive rows, one chunk each) and
+// the transposed stores (rows 8 apart) spread over all banks.
+template <typename T, int BK>
+__device__ __forceinline__ int lds_off(int row, int k) {
+  constexpr int VEC = 16 / sizeof(T);
+  constexpr int NCH = BK / VEC;
+  const int sw = (row ^ (row >> 3)) & (NCH - 1);
+  return row * BK + (((k / VEC) ^ sw) * VEC) + (k % VEC);
+}
+
+// 4 K-rows x VEC columns (four 16-byte registers) -> VEC LDS rows of 4
+// K-values each.
+template <typename T, int BK>
+__device__ __forceinline__ void store_transposed(const u32x4* r, T* dst, int c0, int k4) {
+  const uint32_t w[4][4] = {{r[0][0], r[0][1], r[0][2], r[0][3]}, {r[1][0], r[1][1], r[1][2], r[1][3]},
+                            {r[2][0], r[2][1], r[2][2], r[2][3]}, {r[3][0], r[3][1], r[3][2], r[3][3]}};
+  if constexpr (sizeof(T) == 2) {
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      const u32x2 ev = {(w[0][p] & 0xffffu) | (w[1][p] << 16), (w[2][p] & 0xffffu) | (w[3][p] << 16)};
+      const u32x2 od = {(w[0][p] >> 16) | (w[1][p] & 0xffff0000u), (w[2][p] >> 16) | (w[3][p] & 0xffff0000u)};
+      *reinterpret_cast<u32x2*>(dst + lds_off<T, BK>(c0 + 2 * p, k4)) = ev;
+      *reinterpret_cast<u32x2*>(dst + lds_off<T, BK>(c0 + 2 * p + 1, k4)) = od;
+    }
+  } else {
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const u32x4 v = {w[0][c], w[1][c], w[2][c], w[3][c]};
+      *reinterpret_cast<u32x4*>(dst + lds_off<T, BK>(c0 + c, k4)) = v;
+    }
+  }
+}
+
+// Per-thread plan for moving one operand tile (ROWS x BK, stored K-major in
+// LDS) from global memory: the thread's source pointers are fixed for the
+// whole K loop and advance by k0 elements (K-major source) or k0 rows
+// (K-strided source).
+//   K-major source:   N16 chunks of 16 bytes, chunk i = (row r_i, k-chunk c_i)
+//   K-strided source: NT blocks of 4 K-rows x VEC columns
+template <typename T, bool KMAJ, int ROWS, int BK>
+struct OperandPlan {
+  static constexpr int VEC = 16 / sizeof(T);
+  static constexpr int N16 = ROWS * BK / VEC / 256;
+  static constexpr int NT = BK * ROWS / (4 * VEC) / 256;
+  static constexpr int NREG = KMAJ ? N16 : 4 * NT;
+  static constexpr int NPTR = KMAJ ? N16 : NT;
+  static_assert(NPTR >= 1, "tile too small for 256 threads");
+  const T* ptr[NPTR];
+  int lrow[NPTR];  // LDS row (K-major) or first LDS row (K-strided)
+  int lk[NPTR];    // LDS k offset
+  int kr[NPTR];    // K-strided: first K-row of the block (for masking)
+  bool ok[NPTR];   // K-major: row is valid
+};
+
+template <typename T, int BM, int BN, int BK>
+struct Smem {
+  T A[2][BM * BK];
+  T B[2][BN * BK];
+};
+
 template <typename T, typename TC, bool A_KMAJ, bool B_KMAJ, int MODE, int EPI, int BM, int BN,
           int BK, int WM, int WN>
 __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g) {
   using MF = Mfma<T>;
+  using SM = Smem<T, BM, BN, BK>;
   constexpr int VEC = 16 / sizeof(T);
-  constexpr int PAD = VEC;
-  constexpr int LDK = BK + PAD;
   constexpr int WTM = BM / WM, WTN = BN / WN;
   constexpr int FM = WTM / 16, FN = WTN / 16;
-  constexpr int NA = BM * BK / VEC / 256;  // 16-byte chunks per thread
-  constexpr int NB = BN * BK / VEC / 256;
+  using PA = OperandPlan<T, A_KMAJ, BM, BK>;
+  using PB = OperandPlan<T, B_KMAJ, BN, BK>;
   static_assert(WM * WN == 4, "four waves");
-  static_assert(NA >= 1 && NB >= 1, "tile too small");
   static_assert(EPI != EPI_SWIGLU || FN % 2 == 0, "SwiGLU pairs column fragments");
 
-  __shared__ __attribute__((aligned(16))) T As[2][BM][LDK];
-  __shared__ __attribute__((aligned(16))) T Bs[2][BN][LDK];
+  __shared__ __attribute__((aligned(16))) SM sm;
   __shared__ int s_scan[4];
   __shared__ int s_info[3];
 
@@ -157,8 +216,8 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g) {
   const int tile = xcd_remap(blockIdx.x, gridDim.x);
 
   int grp, mt, nt;
-  int row0;          // first A row (ROWS) of the tile
-  int mrows;         // valid rows in the tile (ROWS)
+  int row0;           // first A row (ROWS) of the tile
+  int mrows;          // valid rows in the tile (ROWS)
   int kbase, kcount;  // contraction range
   if (MODE == G_ROWS) {
     find_group<BM>(g.offsets, g.G, g.tiles_n, tile, s_scan, s_info);
@@ -191,77 +250,110 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g) {
   const int m0 = mt * BM;  // KSPLIT: output row block
   const int n0 = nt * BN;
 
-  // global row of B for tile-local row n (SwiGLU: gate and up halves of the
-  // same output columns side by side within each wave's column range)
-  auto brow = [&](int n) -> int {
-    if (EPI == EPI_SWIGLU) {
-      const int w = n / WTN, within = n % WTN;
-      const int half = within / (WTN / 2), j = within % (WTN / 2);
-      return half * g.f + nt * (BN / 2) + w * (WTN / 2) + j;
+  // ---- per-thread load plans
+  PA pa;
+  PB pb;
+  if constexpr (A_KMAJ) {
+#pragma unroll
+    for (int i = 0; i < PA::NPTR; ++i) {
+      const int q = tid + i * 256;
+      const int r = q / (BK / VEC), kc = q % (BK / VEC);
+      pa.lrow[i] = r;
+      pa.lk[i] = kc * VEC;
+      pa.ok[i] = r < mrows;
+      pa.ptr[i] = Ab + int64_t(row0 + (r < mrows ? r : 0)) * g.lda + kc * VEC;
     }
-    return n0 + n;
-  };
+  } else {
+#pragma unroll
+    for (int i = 0; i < PA::NPTR; ++i) {
+      const int q = tid + i * 256;
+      const int kq = q / (BM / VEC), mc = q % (BM / VEC);
+      pa.lrow[i] = mc * VEC;
+      pa.lk[i] = 4 * kq;
+      pa.kr[i] = 4 * kq;
+      pa.ptr[i] = Ab + int64_t(kbase + 4 * kq) * g.lda + m0 + mc * VEC;
+    }
+  }
+  if constexpr (B_KMAJ) {
+#pragma unroll
+    for (int i = 0; i < PB::NPTR; ++i) {
+      const int q = tid + i * 256;
+      const int r = q / (BK / VEC), kc = q % (BK / VEC);
+      int grow = n0 + r;
+      if (EPI == EPI_SWIGLU) {
+        // gate and up rows of the same output columns side by side within
+        // each wave's column range
+        const int w = r / WTN, within = r % WTN;
+        const int half = within / (WTN / 2), j = within % (WTN / 2);
+        grow = half * g.f + nt * (BN / 2) + w * (WTN / 2) + j;
+      }
+      pb.lrow[i] = r;
+      pb.lk[i] = kc * VEC;
+      pb.ok[i] = true;
+      pb.ptr[i] = Bb + int64_t(grow) * g.ldb + kc * VEC;
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < PB::NPTR; ++i) {
+      const int q = tid + i * 256;
+      const int kq = q / (BN / VEC), nc = q % (BN / VEC);
+      pb.lrow[i] = nc * VEC;
+      pb.lk[i] = 4 * kq;
+      pb.kr[i] = 4 * kq;
+      pb.ptr[i] = Bb + int64_t(kbase + 4 * kq) * g.ldb + n0 + nc * VEC;
+    }
+  }
 
-  uint4 ra[NA], rb[NB];
-  auto gload = [&](int k0) {
-#pragma unroll
-    for (int i = 0; i < NA; ++i) {
-      const int q = tid + i * 256;
-      uint4 v = make_uint4(0, 0, 0, 0);
-      if (A_KMAJ) {
-        const int r = q / (BK / VEC), kc = q % (BK / VEC);
-        if (r < mrows)
-          v = *reinterpret_cast<const uint4*>(Ab + int64_t(row0 + r) * g.lda + k0 + kc * VEC);
-      } else {
-        const int kr = q / (BM / VEC), mc = q % (BM / VEC);
-        if (k0 + kr < kcount)
-          v = *reinterpret_cast<const uint4*>(Ab + int64_t(kbase + k0 + kr) * g.lda + m0 + mc * VEC);
-      }
-      ra[i] = v;
-    }
-#pragma unroll
-    for (int i = 0; i < NB; ++i) {
-      const int q = tid + i * 256;
-      uint4 v = make_uint4(0, 0, 0, 0);
-      if (B_KMAJ) {
-        const int r = q / (BK / VEC), kc = q % (BK / VEC);
-        v = *reinterpret_cast<const uint4*>(Bb + int64_t(brow(r)) * g.ldb + k0 + kc * VEC);
-      } else {
-        const int kr = q / (BN / VEC), nc = q % (BN / VEC);
-        if (MODE == G_ROWS || k0 + kr < kcount)
-          v = *reinterpret_cast<const uint4*>(Bb + int64_t(kbase + k0 + kr) * g.ldb + n0 + nc * VEC);
-      }
-      rb[i] = v;
-    }
-  };
-  auto lstore = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < NA; ++i) {
-      const int q = tid + i * 256;
-      if (A_KMAJ) {
-        const int r = q / (BK / VEC), kc = q % (BK / VEC);
-        *reinterpret_cast<uint4*>(&As[buf][r][kc * VEC]) = ra[i];
-      } else {
-        const int kr = q / (BM / VEC), mc = q % (BM / VEC);
-        const T* e = reinterpret_cast<const T*>(&ra[i]);
-#pragma unroll
-        for (int v = 0; v < VEC; ++v) As[buf][mc * VEC + v][kr] = e[v];
-      }
-    }
-#pragma unroll
-    for (int i = 0; i < NB; ++i) {
-      const int q = tid + i * 256;
-      if (B_KMAJ) {
-        const int r = q / (BK / VEC), kc = q % (BK / VEC);
-        *reinterpret_cast<uint4*>(&Bs[buf][r][kc * VEC]) = rb[i];
-      } else {
-        const int kr = q / (BN / VEC), nc = q % (BN / VEC);
-        const T* e = reinterpret_cast<const T*>(&rb[i]);
-#pragma unroll
-        for (int v = 0; v < VEC; ++v) Bs[buf][nc * VEC + v][kr] = e[v];
-      }
-    }
-  };
+  u32x4 ra[PA::NREG], rb[PB::NREG];
+  const u32x4 zero4 = {0u, 0u, 0u, 0u};
+  // global -> registers for the K step starting at k0
+#define MOE_GLOAD(k0)                                                                           \
+  do {                                                                                          \
+    if constexpr (A_KMAJ) {                                                                     \
+      _Pragma("unroll") for (int i = 0; i < PA::NPTR; ++i) {                                    \
+        ra[i] = pa.ok[i] ? *reinterpret_cast<const u32x4*>(pa.ptr[i] + (k0)) : zero4; \
+      }                                                                                         \
+    } else {                                                                                    \
+      _Pragma("unroll") for (int i = 0; i < PA::NPTR; ++i) {                                    \
+        _Pragma("unroll") for (int j = 0; j < 4; ++j) {                                         \
+          const bool v = (k0) + pa.kr[i] + j < kcount;                                          \
+          ra[4 * i + j] = v ? *reinterpret_cast<const u32x4*>(pa.ptr[i] + int64_t((k0) + j) * g.lda) \
+                            : zero4;                                           \
+        }                                                                                       \
+      }                                                                                         \
+    }                                                                                           \
+    if constexpr (B_KMAJ) {                                                                     \
+      _Pragma("unroll") for (int i = 0; i < PB::NPTR; ++i) {                                    \
+        rb[i] = *reinterpret_cast<const u32x4*>(pb.ptr[i] + (k0));                              \
+      }                                                                                         \
+    } else {                                                                                    \
+      _Pragma("unroll") for (int i = 0; i < PB::NPTR; ++i) {                                    \
+        _Pragma("unroll") for (int j = 0; j < 4; ++j) {                                         \
+          const bool v = MODE == G_ROWS || (k0) + pb.kr[i] + j < kcount;                        \
+          rb[4 * i + j] = v ? *reinterpret_cast<const u32x4*>(pb.ptr[i] + int64_t((k0) + j) * g.ldb) \
+                            : zero4;                                           \
+        }                                                                                       \
+      }                                                                                         \
+    }                                                                                           \
+  } while (0)
+  // registers -> LDS buffer `buf`
+#define MOE_LSTORE(buf)                                                                         \
+  do {                                                                                          \
+    if constexpr (A_KMAJ) {                                                                     \
+      _Pragma("unroll") for (int i = 0; i < PA::NPTR; ++i)                                      \
+        *reinterpret_cast<u32x4*>(&sm.A[buf][lds_off<T, BK>(pa.lrow[i], pa.lk[i])]) = ra[i];    \
+    } else {                                                                                    \
+      _Pragma("unroll") for (int i = 0; i < PA::NPTR; ++i)                                      \
+        store_transposed<T, BK>(&ra[4 * i], sm.A[buf], pa.lrow[i], pa.lk[i]);                   \
+    }                                                                                           \
+    if constexpr (B_KMAJ) {                                                                     \
+      _Pragma("unroll") for (int i = 0; i < PB::NPTR; ++i)                                      \
+        *reinterpret_cast<u32x4*>(&sm.B[buf][lds_off<T, BK>(pb.lrow[i], pb.lk[i])]) = rb[i];    \
+    } else {                                                                                    \
+      _Pragma("unroll") for (int i = 0; i < PB::NPTR; ++i)                                      \
+        store_transposed<T, BK>(&rb[4 * i], sm.B[buf], pb.lrow[i], pb.lk[i]);                   \
+    }                                                                                           \
+  } while (0)
 
   f32x4_t acc[FM][FN];
 #pragma unroll
@@ -271,27 +363,29 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g) {
 
   const int nk = (kcount + BK - 1) / BK;
   if (nk > 0) {
-    gload(0);
-    lstore(0);
+    MOE_GLOAD(0);
+    MOE_LSTORE(0);
     __syncthreads();
   }
   for (int s = 0; s < nk; ++s) {
     const int buf = s & 1;
-    if (s + 1 < nk) gload((s + 1) * BK);
+    if (s + 1 < nk) MOE_GLOAD((s + 1) * BK);
 #pragma unroll
     for (int kk = 0; kk < BK / MF::MK; ++kk) {
       const int kofs = kk * MF::MK + (lane / 16) * MF::KP;
       typename MF::frag af[FM], bfr[FN];
 #pragma unroll
-      for (int i = 0; i < FM; ++i) af[i] = MF::load(&As[buf][wm * WTM + i * 16 + (lane % 16)][kofs]);
+      for (int i = 0; i < FM; ++i)
+        af[i] = MF::load(&sm.A[buf][lds_off<T, BK>(wm * WTM + i * 16 + (lane % 16), kofs)]);
 #pragma unroll
-      for (int j = 0; j < FN; ++j) bfr[j] = MF::load(&Bs[buf][wn * WTN + j * 16 + (lane % 16)][kofs]);
+      for (int j = 0; j < FN; ++j)
+        bfr[j] = MF::load(&sm.B[buf][lds_off<T, BK>(wn * WTN + j * 16 + (lane % 16), kofs)]);
 #pragma unroll
       for (int i = 0; i < FM; ++i)
 #pragma unroll
         for (int j = 0; j < FN; ++j) acc[i][j] = MF::mma(af[i], bfr[j], acc[i][j]);
     }
-    if (s + 1 < nk) lstore(buf ^ 1);
+    if (s + 1 < nk) MOE_LSTORE(buf ^ 1);
     __syncthreads();
   }
 
@@ -356,6 +450,9 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g) {
       }
   }
 }
+
+#undef MOE_GLOAD
+#undef MOE_LSTORE
 
 // ---------------------------------------------------------------------------
 template <typename T> struct Tile;

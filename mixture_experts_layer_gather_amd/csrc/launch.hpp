@@ -31,13 +31,15 @@ struct RouteBwdLaunch {
   const float* dgate;
   void* dx;
   float* dw_router;
-  float* dL;  // workspace [T,E]
+  float* dL;       // workspace [T,E]
+  float* dw_part;  // workspace [Z,E,d] (token-chunk partial sums), Z = route_bwd_zsplit
   int64_t T, d, E, k;
   int score_fn, renorm;
   float gate_scale;
   bool act_bf16;
 };
 void launch_route_bwd(const RouteBwdLaunch& r, hipStream_t st);
+int route_bwd_zsplit(int64_t T, int64_t d, int64_t E);
 
 // Dispatch: histogram -> scan -> positions -> gather.
 struct DispatchLaunch {

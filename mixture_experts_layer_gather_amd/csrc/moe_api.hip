@@ -96,7 +96,11 @@ size_t moe_workspace_size(const moe_config* cfg, int op) {
     case MOE_OP_DISPATCH: return T ? round_up(size_t(dispatch_chunks(T)) * size_t(E) * 4) : 0;
     case MOE_OP_GROUPED_FFN_BWD:
       return round_up(size_t(T) * size_t(k) * size_t(2 * f) * act_bytes(cfg->act_dtype));
-    case MOE_OP_ROUTE_BWD: return round_up(size_t(T) * size_t(E) * 4);
+    case MOE_OP_ROUTE_BWD: {
+      const int Z = moe::route_bwd_zsplit(T, cfg->hidden, E);
+      const size_t parts = Z > 1 ? size_t(Z) * size_t(E) * size_t(cfg->hidden) * 4 : 0;
+      return round_up(size_t(T) * size_t(E) * 4) + round_up(parts);
+    }
     default: return 0;
   }
 }
@@ -273,6 +277,8 @@ int moe_route_bwd(const moe_config* cfg, const void* x, const float* w_router, c
   moe::RouteBwdLaunch r{};
   r.x = x; r.w_router = w_router; r.logits = logits; r.idx = topk_idx; r.dgate = d_gate;
   r.dx = dx; r.dw_router = dw_router; r.dL = static_cast<float*>(ws);
+  r.dw_part = reinterpret_cast<float*>(static_cast<char*>(ws) +
+                                       round_up(size_t(cfg->num_tokens) * size_t(cfg->num_experts) * 4));
   r.T = cfg->num_tokens; r.d = cfg->hidden; r.E = cfg->num_experts; r.k = cfg->top_k;
   r.score_fn = cfg->score_fn; r.renorm = cfg->renormalize; r.gate_scale = cfg->gate_scale;
   r.act_bf16 = cfg->act_dtype == MOE_DTYPE_BF16;

@@ -33,6 +33,8 @@ struct VArgs {
   int64_t ldc;
   const float* bias;  // [N] or null, added once after the contraction
   int M, N, K;
+  int kchunk;         // contraction range of blockIdx.z: [z*kchunk, (z+1)*kchunk)
+  int64_t c_zstride;  // elements between the partial outputs of consecutive z
 };
 
 template <typename T>
@@ -44,11 +46,15 @@ template <typename TA, bool A_MK, typename TB, bool B_NK, typename TC, int TM, i
           int RM, int RN, int KC, int EPI>
 __global__ __launch_bounds__(256) void vgemm_kernel(VArgs a) {
   static_assert((TM / RM) * (TN / RN) == 256, "256 threads");
-  __shared__ float As[KC][TM + 4];
-  __shared__ float Bs[KC][TN + 4];
+  static_assert(RM == 4 || RM == 1, "row tile");
+  static_assert(RN == 4 || RN == 1, "column tile");
+  __shared__ __attribute__((aligned(16))) float As[KC][TM + 4];
+  __shared__ __attribute__((aligned(16))) float Bs[KC][TN + 4];
   const int tid = threadIdx.x;
   const int m0 = blockIdx.y * TM;
   const int n0 = blockIdx.x * TN;
+  const int kb = blockIdx.z * a.kchunk;
+  const int ke = min(a.K, kb + a.kchunk);
   const int tn = tid % (TN / RN);
   const int tm = tid / (TN / RN);
   float acc[RM][RN];
@@ -57,7 +63,7 @@ __global__ __launch_bounds__(256) void vgemm_kernel(VArgs a) {
 #pragma unroll
     for (int j = 0; j < RN; ++j) acc[i][j] = 0.0f;
 
-  for (int k0 = 0; k0 < a.K; k0 += KC) {
+  for (int k0 = kb; k0 < ke; k0 += KC) {
     // stage A chunk as As[k][m]
     for (int idx = tid; idx < TM * KC; idx += 256) {
       int m, kk;
@@ -65,7 +71,7 @@ __global__ __launch_bounds__(256) void vgemm_kernel(VArgs a) {
       else { kk = idx / TM; m = idx % TM; }
       const int gm = m0 + m, gk = k0 + kk;
       float v = 0.0f;
-      if (gm < a.M && gk < a.K)
+      if (gm < a.M && gk < ke)
         v = A_MK ? ld_elem<TA>(a.A, int64_t(gm) * a.lda + gk)
                  : ld_elem<TA>(a.A, int64_t(gk) * a.lda + gm);
       As[kk][m] = v;
@@ -76,19 +82,27 @@ __global__ __launch_bounds__(256) void vgemm_kernel(VArgs a) {
       else { kk = idx / TN; n = idx % TN; }
       const int gn = n0 + n, gk = k0 + kk;
       float v = 0.0f;
-      if (gn < a.N && gk < a.K)
+      if (gn < a.N && gk < ke)
         v = B_NK ? ld_elem<TB>(a.B, int64_t(gn) * a.ldb + gk)
                  : ld_elem<TB>(a.B, int64_t(gk) * a.ldb + gn);
       Bs[kk][n] = v;
     }
     __syncthreads();
-    const int kend = min(KC, a.K - k0);
+    const int kend = min(KC, ke - k0);
     for (int kk = 0; kk < kend; ++kk) {
       float av[RM], bv[RN];
-#pragma unroll
-      for (int i = 0; i < RM; ++i) av[i] = As[kk][tm * RM + i];
-#pragma unroll
-      for (int j = 0; j < RN; ++j) bv[j] = Bs[kk][tn * RN + j];
+      if constexpr (RM == 4) {
+        const float4 q = *reinterpret_cast<const float4*>(&As[kk][tm * 4]);
+        av[0] = q.x; av[1] = q.y; av[2] = q.z; av[3] = q.w;
+      } else {
+        av[0] = As[kk][tm];
+      }
+      if constexpr (RN == 4) {
+        const float4 q = *reinterpret_cast<const float4*>(&Bs[kk][tn * 4]);
+        bv[0] = q.x; bv[1] = q.y; bv[2] = q.z; bv[3] = q.w;
+      } else {
+        bv[0] = Bs[kk][tn];
+      }
 #pragma unroll
       for (int i = 0; i < RM; ++i)
 #pragma unroll
@@ -108,7 +122,7 @@ __global__ __launch_bounds__(256) void vgemm_kernel(VArgs a) {
       float v = acc[i][j];
       if (EPI == VEPI_STORE) {
         if (a.bias) v = v + a.bias[gn];
-        reinterpret_cast<float*>(a.C)[int64_t(gm) * a.ldc + gn] = v;
+        reinterpret_cast<float*>(a.C)[blockIdx.z * a.c_zstride + int64_t(gm) * a.ldc + gn] = v;
       } else {
         TC* c = reinterpret_cast<TC*>(a.C) + int64_t(gm) * a.ldc + gn;
         Elem<TC>::store(c, Elem<TC>::load(c) + v);
@@ -117,17 +131,39 @@ __global__ __launch_bounds__(256) void vgemm_kernel(VArgs a) {
   }
 }
 
+// out[i] = sum_z part[z][i] for z = 0..Z-1 in order (deterministic).
+__global__ __launch_bounds__(256) void reduce_parts_kernel(const float* __restrict__ part,
+                                                           float* __restrict__ out, int64_t n, int Z) {
+  for (int64_t i = blockIdx.x * int64_t(256) + threadIdx.x; i < n; i += int64_t(gridDim.x) * 256) {
+    float s = part[i];
+    for (int z = 1; z < Z; ++z) s += part[z * n + i];
+    out[i] = s;
+  }
+}
+
 template <typename TA, bool A_MK, typename TB, bool B_NK, typename TC, int EPI>
-static void launch_vgemm(const VArgs& a, hipStream_t st) {
+static void launch_vgemm(VArgs a, hipStream_t st, int zsplit = 1) {
+  a.kchunk = (a.K + zsplit - 1) / zsplit;
   if (a.N <= 16) {
     constexpr int TM = 16, TN = 16;
-    dim3 grid((a.N + TN - 1) / TN, (a.M + TM - 1) / TM);
+    dim3 grid((a.N + TN - 1) / TN, (a.M + TM - 1) / TM, zsplit);
     vgemm_kernel<TA, A_MK, TB, B_NK, TC, TM, TN, 1, 1, 32, EPI><<<grid, 256, 0, st>>>(a);
   } else {
     constexpr int TM = 64, TN = 64;
-    dim3 grid((a.N + TN - 1) / TN, (a.M + TM - 1) / TM);
+    dim3 grid((a.N + TN - 1) / TN, (a.M + TM - 1) / TM, zsplit);
     vgemm_kernel<TA, A_MK, TB, B_NK, TC, TM, TN, 4, 4, 32, EPI><<<grid, 256, 0, st>>>(a);
   }
+}
+
+// Token-chunk count of the router weight gradient: enough workgroups to
+// fill the chip, chunks of at least 128 tokens.
+int route_bwd_zsplit(int64_t T, int64_t d, int64_t E) {
+  const int64_t base = ((d + 63) / 64) * ((E + 63) / 64);
+  int64_t z = (1024 + base - 1) / base;
+  z = z < 1 ? 1 : z;
+  const int64_t zmax = (T + 127) / 128;
+  if (z > zmax) z = zmax < 1 ? 1 : zmax;
+  return int(z);
 }
 
 // ---------------------------------------------------------------------------
@@ -487,13 +523,21 @@ static void route_bwd_t(const RouteBwdLaunch& r, hipStream_t st) {
   v.M = int(r.T); v.N = int(r.d); v.K = int(r.E);
   launch_vgemm<float, true, float, false, TX, VEPI_ADD_ACT>(v, st);
 
-  // dw[e,:] = sum_t dL[t,e] x[t,:]
+  // dw[e,:] = sum_t dL[t,e] x[t,:], tokens split into Z chunks whose partial
+  // sums are added in chunk order
+  const int Z = route_bwd_zsplit(r.T, r.d, r.E);
   VArgs w{};
   w.A = r.dL; w.lda = r.E;
   w.B = r.x; w.ldb = r.d;
-  w.C = r.dw_router; w.ldc = r.d;
+  w.C = Z > 1 ? r.dw_part : r.dw_router; w.ldc = r.d;
+  w.c_zstride = r.E * r.d;
   w.M = int(r.E); w.N = int(r.d); w.K = int(r.T);
-  launch_vgemm<float, false, TX, false, float, VEPI_STORE>(w, st);
+  launch_vgemm<float, false, TX, false, float, VEPI_STORE>(w, st, Z);
+  if (Z > 1) {
+    const int64_t n = r.E * r.d;
+    reduce_parts_kernel<<<int((n + 255) / 256 < 4096 ? (n + 255) / 256 : 4096), 256, 0, st>>>(
+        r.dw_part, r.dw_router, n, Z);
+  }
 }
 
 void launch_route_bwd(const RouteBwdLaunch& r, hipStream_t st) {
