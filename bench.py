@@ -86,7 +86,7 @@ def timed_step(layer, x, dy, marks):
     rec("dispatch")
     L.moe_grouped_ffn(c, layer.x_perm, layer.x_scale, layer.offsets, layer.w1, layer.w1_scale,
                       layer.w2, layer.w2_scale, layer.act_gu, layer.act_h, layer.h_scale,
-                      layer.out_perm)
+                      layer.out_perm, layer.ws_ffn)
     rec("grouped_ffn")
     shared_out = None
     if layer.shared:
@@ -97,7 +97,7 @@ def timed_step(layer, x, dy, marks):
             sx, sxs = layer.s_x, layer.s_x_scale
         L.moe_grouped_ffn(layer.scfg, sx, sxs, layer.s_offsets, layer.sw1, layer.sw1_scale,
                           layer.sw2, layer.sw2_scale, layer.s_gu, layer.s_h, layer.s_h_scale,
-                          layer.s_out)
+                          layer.s_out, layer.ws_ffn)
         shared_out = layer.s_out
         rec("shared_ffn")
     L.moe_combine(c, layer.out_perm, layer.row_id_map, layer.topk_gate, shared_out, layer.y)

@@ -17,11 +17,19 @@
 //             dX = dGU W1                        A K-major, B N-major
 //   wgrad     dW2 = dO^T H, dW1 = dGU^T X        A [K,M], B [K,N]; K = the
 //                                                expert's rows (ragged)
+// in fp32 (v_mfma_f32_16x16x4f32), bf16 (v_mfma_f32_16x16x32_bf16) and FP8
+// E4M3 (v_mfma_scale_f32_16x16x128_f8f6f4 with unit hardware scales). FP8
+// operands carry fp32 block scales (activations 1 x 128 along K, weights
+// 128 x 128): a K step is exactly one 128-deep block, its MFMA result is
+// multiplied by row scale x column-block scale and added to the fp32
+// accumulator.
+//
 // Tiles are staged through LDS (double buffered, one barrier per K step) in
-// K-contiguous rows so that every MFMA operand is one 16-byte LDS read;
-// operands stored the other way round are transposed on their way into LDS.
-// Workgroup ids are remapped so that each XCD (8 per chip, one L2 each) works
-// through a contiguous range of tiles that share weights and rows.
+// K-contiguous rows so that every MFMA operand is read with 16-byte LDS
+// reads; operands stored the other way round are transposed in registers on
+// their way into LDS. Workgroup ids are remapped so that each XCD (8 per
+// chip, one L2 each) works through a contiguous range of tiles that share
+// weights and rows.
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -30,13 +38,15 @@ namespace moe {
 enum { G_ROWS = 0, G_KSPLIT = 1 };
 enum { EPI_STORE = 0, EPI_SWIGLU = 1, EPI_DSWIGLU = 2 };
 
+typedef uint8_t fp8_t;  // OCP E4M3FN code
+
 template <typename T> struct Mfma;
 template <> struct Mfma<bf16_t> {
   static constexpr int KP = 8;   // elements per lane per instruction
   static constexpr int MK = 32;  // K per instruction
   typedef bf16x8_t frag;
-  static __device__ __forceinline__ frag load(const bf16_t* p) {
-    return __builtin_bit_cast(frag, *reinterpret_cast<const u32x4*>(p));
+  static __device__ __forceinline__ frag load(const bf16_t* p0, const bf16_t*) {
+    return __builtin_bit_cast(frag, *reinterpret_cast<const u32x4*>(p0));
   }
   static __device__ __forceinline__ f32x4_t mma(frag a, frag b, f32x4_t c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
@@ -46,11 +56,31 @@ template <> struct Mfma<float> {
   static constexpr int KP = 1;
   static constexpr int MK = 4;
   typedef float frag;
-  static __device__ __forceinline__ frag load(const float* p) { return *p; }
+  static __device__ __forceinline__ frag load(const float* p0, const float*) { return *p0; }
   static __device__ __forceinline__ f32x4_t mma(frag a, frag b, f32x4_t c) {
     return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
   }
 };
+template <> struct Mfma<fp8_t> {
+  static constexpr int KP = 32;
+  static constexpr int MK = 128;
+  typedef i32x8_t frag;
+  // 32 bytes from two (separately swizzled) 16-byte chunks
+  static __device__ __forceinline__ frag load(const fp8_t* p0, const fp8_t* p1) {
+    const u32x4 lo = *reinterpret_cast<const u32x4*>(p0);
+    const u32x4 hi = *reinterpret_cast<const u32x4*>(p1);
+    return i32x8_t{int(lo[0]), int(lo[1]), int(lo[2]), int(lo[3]),
+                   int(hi[0]), int(hi[1]), int(hi[2]), int(hi[3])};
+  }
+  // A and B formats 0 (E4M3), E8M0 hardware scales 127 (= 1.0)
+  static __device__ __forceinline__ f32x4_t mma(frag a, frag b, f32x4_t c) {
+    return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
+  }
+};
+
+// Activation dtype of the epilogue outputs for operand dtype T.
+template <typename T> struct OutOf { typedef T type; };
+template <> struct OutOf<fp8_t> { typedef bf16_t type; };
 
 struct GemmArgs {
   const void* A;
@@ -69,6 +99,12 @@ struct GemmArgs {
   void* aux1;         // SWIGLU: H out [rows,f]
   int tiles_n;
   int tiles_m;        // KSPLIT
+  // FP8 block scales
+  const float* a_scale;      // [rows, K/128]
+  int a_scale_ld;            // K/128
+  const float* b_scale;      // [G, R/128, C/128] of B's storage [G, R, C]
+  int64_t b_scale_gstride;   // (R/128)*(C/128)
+  int b_scale_ld;            // C/128
 };
 
 // Bijective remap of workgroup ids: consecutive ids are spread over the 8
@@ -133,7 +169,7 @@ __device__ void find_group(const int32_t* __restrict__ offsets, int G, int tiles
 // LDS tiles hold ROWS x BK elements per operand, K-contiguous, without
 // padding. The 16-byte chunks of each row are XOR-swizzled with the row so
 // that both the MFMA fragment reads (16 consecutive rows, one chunk each) and
-// the transposed stores (rows 8 apart) spread over all banks.
+// the transposed stores (rows VEC apart) spread over all banks.
 template <typename T, int BK>
 __device__ __forceinline__ int lds_off(int row, int k) {
   constexpr int VEC = 16 / sizeof(T);
@@ -148,7 +184,24 @@ template <typename T, int BK>
 __device__ __forceinline__ void store_transposed(const u32x4* r, T* dst, int c0, int k4) {
   const uint32_t w[4][4] = {{r[0][0], r[0][1], r[0][2], r[0][3]}, {r[1][0], r[1][1], r[1][2], r[1][3]},
                             {r[2][0], r[2][1], r[2][2], r[2][3]}, {r[3][0], r[3][1], r[3][2], r[3][3]}};
-  if constexpr (sizeof(T) == 2) {
+  if constexpr (sizeof(T) == 1) {
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      // bytes (w0.q, w1.q) and (w2.q, w3.q) interleaved, then merged
+      const uint32_t a01 = __builtin_amdgcn_perm(w[1][p], w[0][p], 0x05010400u);  // q = 0, 1
+      const uint32_t b01 = __builtin_amdgcn_perm(w[1][p], w[0][p], 0x07030602u);  // q = 2, 3
+      const uint32_t a23 = __builtin_amdgcn_perm(w[3][p], w[2][p], 0x05010400u);
+      const uint32_t b23 = __builtin_amdgcn_perm(w[3][p], w[2][p], 0x07030602u);
+      const uint32_t c0v = __builtin_amdgcn_perm(a23, a01, 0x05040100u);
+      const uint32_t c1v = __builtin_amdgcn_perm(a23, a01, 0x07060302u);
+      const uint32_t c2v = __builtin_amdgcn_perm(b23, b01, 0x05040100u);
+      const uint32_t c3v = __builtin_amdgcn_perm(b23, b01, 0x07060302u);
+      *reinterpret_cast<uint32_t*>(dst + lds_off<T, BK>(c0 + 4 * p + 0, k4)) = c0v;
+      *reinterpret_cast<uint32_t*>(dst + lds_off<T, BK>(c0 + 4 * p + 1, k4)) = c1v;
+      *reinterpret_cast<uint32_t*>(dst + lds_off<T, BK>(c0 + 4 * p + 2, k4)) = c2v;
+      *reinterpret_cast<uint32_t*>(dst + lds_off<T, BK>(c0 + 4 * p + 3, k4)) = c3v;
+    }
+  } else if constexpr (sizeof(T) == 2) {
 #pragma unroll
     for (int p = 0; p < 4; ++p) {
       const u32x2 ev = {(w[0][p] & 0xffffu) | (w[1][p] << 16), (w[2][p] & 0xffffu) | (w[3][p] << 16)};
@@ -186,17 +239,20 @@ struct OperandPlan {
   bool ok[NPTR];   // K-major: row is valid
 };
 
-template <typename T, int BM, int BN, int BK>
+template <typename T, int BM, int BN, int BK, bool SCALED>
 struct Smem {
   T A[2][BM * BK];
   T B[2][BN * BK];
+  float SA[SCALED ? 2 : 1][SCALED ? BM : 1];  // FP8 row scales of the A tile
 };
 
 template <typename T, typename TC, bool A_KMAJ, bool B_KMAJ, int MODE, int EPI, int BM, int BN,
           int BK, int WM, int WN>
 __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g) {
   using MF = Mfma<T>;
-  using SM = Smem<T, BM, BN, BK>;
+  using TO = typename OutOf<T>::type;
+  constexpr bool FP8 = sizeof(T) == 1;
+  using SM = Smem<T, BM, BN, BK, FP8>;
   constexpr int VEC = 16 / sizeof(T);
   constexpr int WTM = BM / WM, WTN = BN / WN;
   constexpr int FM = WTM / 16, FN = WTN / 16;
@@ -204,6 +260,8 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g) {
   using PB = OperandPlan<T, B_KMAJ, BN, BK>;
   static_assert(WM * WN == 4, "four waves");
   static_assert(EPI != EPI_SWIGLU || FN % 2 == 0, "SwiGLU pairs column fragments");
+  static_assert(!FP8 || (MODE == G_ROWS && A_KMAJ && BK == 128 && BN <= 128 && BM <= 256),
+                "FP8: row-grouped GEMMs, one 128-deep scale block per K step");
 
   __shared__ __attribute__((aligned(16))) SM sm;
   __shared__ int s_scan[4];
@@ -303,22 +361,41 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g) {
       pb.ptr[i] = Bb + int64_t(kbase + 4 * kq) * g.ldb + n0 + nc * VEC;
     }
   }
+  // FP8: the thread that stages the row scale of A-tile row tid (if any)
+  const float* __restrict__ sa_ptr = nullptr;
+  if constexpr (FP8) {
+    if (tid < BM && tid < mrows) sa_ptr = g.a_scale + int64_t(row0 + tid) * g.a_scale_ld;
+  }
+  // FP8: column-block scale rows of B; SwiGLU tiles span a gate block and an
+  // up block of W1
+  const float* __restrict__ sb_base = nullptr;
+  int sb_blk0 = 0, sb_blk1 = 0;
+  if constexpr (FP8) {
+    sb_base = g.b_scale + int64_t(grp) * g.b_scale_gstride;
+    if (EPI == EPI_SWIGLU) {
+      sb_blk0 = (nt * (BN / 2)) / 128;
+      sb_blk1 = (g.f + nt * (BN / 2)) / 128;
+    } else {
+      sb_blk0 = sb_blk1 = n0 / 128;
+    }
+  }
 
-  u32x4 ra[PA::NREG], rb[PB::NREG];
   const u32x4 zero4 = {0u, 0u, 0u, 0u};
+  u32x4 ra[PA::NREG], rb[PB::NREG];
+  float rs = 0.0f;  // staged FP8 row scale
   // global -> registers for the K step starting at k0
 #define MOE_GLOAD(k0)                                                                           \
   do {                                                                                          \
     if constexpr (A_KMAJ) {                                                                     \
       _Pragma("unroll") for (int i = 0; i < PA::NPTR; ++i) {                                    \
-        ra[i] = pa.ok[i] ? *reinterpret_cast<const u32x4*>(pa.ptr[i] + (k0)) : zero4; \
+        ra[i] = pa.ok[i] ? *reinterpret_cast<const u32x4*>(pa.ptr[i] + (k0)) : zero4;           \
       }                                                                                         \
     } else {                                                                                    \
       _Pragma("unroll") for (int i = 0; i < PA::NPTR; ++i) {                                    \
         _Pragma("unroll") for (int j = 0; j < 4; ++j) {                                         \
           const bool v = (k0) + pa.kr[i] + j < kcount;                                          \
           ra[4 * i + j] = v ? *reinterpret_cast<const u32x4*>(pa.ptr[i] + int64_t((k0) + j) * g.lda) \
-                            : zero4;                                           \
+                            : zero4;                                                            \
         }                                                                                       \
       }                                                                                         \
     }                                                                                           \
@@ -331,10 +408,11 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g) {
         _Pragma("unroll") for (int j = 0; j < 4; ++j) {                                         \
           const bool v = MODE == G_ROWS || (k0) + pb.kr[i] + j < kcount;                        \
           rb[4 * i + j] = v ? *reinterpret_cast<const u32x4*>(pb.ptr[i] + int64_t((k0) + j) * g.ldb) \
-                            : zero4;                                           \
+                            : zero4;                                                            \
         }                                                                                       \
       }                                                                                         \
     }                                                                                           \
+    if constexpr (FP8) rs = sa_ptr ? sa_ptr[(k0) / 128] : 0.0f;                                 \
   } while (0)
   // registers -> LDS buffer `buf`
 #define MOE_LSTORE(buf)                                                                         \
@@ -353,6 +431,9 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g) {
       _Pragma("unroll") for (int i = 0; i < PB::NPTR; ++i)                                      \
         store_transposed<T, BK>(&rb[4 * i], sm.B[buf], pb.lrow[i], pb.lk[i]);                   \
     }                                                                                           \
+    if constexpr (FP8) {                                                                        \
+      if (tid < BM) sm.SA[buf][tid] = rs;                                                       \
+    }                                                                                           \
   } while (0)
 
   f32x4_t acc[FM][FN];
@@ -369,21 +450,51 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g) {
   }
   for (int s = 0; s < nk; ++s) {
     const int buf = s & 1;
+    float sb0 = 0.0f, sb1 = 0.0f;
+    if constexpr (FP8) {
+      const int kb = s;  // BK == 128: one scale block per step
+      if (B_KMAJ) {
+        sb0 = sb_base[int64_t(sb_blk0) * g.b_scale_ld + kb];
+        sb1 = sb_base[int64_t(sb_blk1) * g.b_scale_ld + kb];
+      } else {
+        sb0 = sb1 = sb_base[int64_t(kb) * g.b_scale_ld + sb_blk0];
+      }
+    }
     if (s + 1 < nk) MOE_GLOAD((s + 1) * BK);
 #pragma unroll
     for (int kk = 0; kk < BK / MF::MK; ++kk) {
       const int kofs = kk * MF::MK + (lane / 16) * MF::KP;
       typename MF::frag af[FM], bfr[FN];
 #pragma unroll
-      for (int i = 0; i < FM; ++i)
-        af[i] = MF::load(&sm.A[buf][lds_off<T, BK>(wm * WTM + i * 16 + (lane % 16), kofs)]);
+      for (int i = 0; i < FM; ++i) {
+        const int r = wm * WTM + i * 16 + (lane % 16);
+        af[i] = MF::load(&sm.A[buf][lds_off<T, BK>(r, kofs)], &sm.A[buf][lds_off<T, BK>(r, kofs + 16)]);
+      }
 #pragma unroll
-      for (int j = 0; j < FN; ++j)
-        bfr[j] = MF::load(&sm.B[buf][lds_off<T, BK>(wn * WTN + j * 16 + (lane % 16), kofs)]);
+      for (int j = 0; j < FN; ++j) {
+        const int r = wn * WTN + j * 16 + (lane % 16);
+        bfr[j] = MF::load(&sm.B[buf][lds_off<T, BK>(r, kofs)], &sm.B[buf][lds_off<T, BK>(r, kofs + 16)]);
+      }
+      if constexpr (FP8) {
 #pragma unroll
-      for (int i = 0; i < FM; ++i)
+        for (int i = 0; i < FM; ++i) {
+          const float4 sa4 =
+              *reinterpret_cast<const float4*>(&sm.SA[buf][wm * WTM + i * 16 + 4 * (lane / 16)]);
+          const float sa[4] = {sa4.x, sa4.y, sa4.z, sa4.w};
 #pragma unroll
-        for (int j = 0; j < FN; ++j) acc[i][j] = MF::mma(af[i], bfr[j], acc[i][j]);
+          for (int j = 0; j < FN; ++j) {
+            const float sbj = (EPI == EPI_SWIGLU && j >= FN / 2) ? sb1 : sb0;
+            const f32x4_t d = MF::mma(af[i], bfr[j], f32x4_t{0.0f, 0.0f, 0.0f, 0.0f});
+#pragma unroll
+            for (int r = 0; r < 4; ++r) acc[i][j][r] = __builtin_fmaf(d[r], sa[r] * sbj, acc[i][j][r]);
+          }
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+          for (int j = 0; j < FN; ++j) acc[i][j] = MF::mma(af[i], bfr[j], acc[i][j]);
+      }
     }
     if (s + 1 < nk) MOE_LSTORE(buf ^ 1);
     __syncthreads();
@@ -408,8 +519,8 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g) {
         }
       }
   } else if (EPI == EPI_SWIGLU) {
-    T* GU = reinterpret_cast<T*>(g.aux0);
-    T* H = reinterpret_cast<T*>(g.aux1);
+    TO* GU = reinterpret_cast<TO*>(g.aux0);
+    TO* H = reinterpret_cast<TO*>(g.aux1);
 #pragma unroll
     for (int i = 0; i < FM; ++i)
 #pragma unroll
@@ -422,14 +533,14 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g) {
           const int col = nt * (BN / 2) + wn * (WTN / 2) + j * 16 + lc;
           const float G = acc[i][j][r], U = acc[i][j + FN / 2][r];
           const float Hv = G / (1.0f + expf(-G)) * U;
-          Elem<T>::store(GU + row * (2 * g.f) + col, G);
-          Elem<T>::store(GU + row * (2 * g.f) + g.f + col, U);
-          Elem<T>::store(H + row * g.f + col, Hv);
+          Elem<TO>::store(GU + row * (2 * g.f) + col, G);
+          Elem<TO>::store(GU + row * (2 * g.f) + g.f + col, U);
+          Elem<TO>::store(H + row * g.f + col, Hv);
         }
       }
   } else {  // EPI_DSWIGLU: C = dGU [rows, 2f]
-    const T* GU = reinterpret_cast<const T*>(g.aux0);
-    T* D = reinterpret_cast<T*>(g.C);
+    const TO* GU = reinterpret_cast<const TO*>(g.aux0);
+    TO* D = reinterpret_cast<TO*>(g.C);
 #pragma unroll
     for (int i = 0; i < FM; ++i)
 #pragma unroll
@@ -441,23 +552,92 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g) {
         for (int j = 0; j < FN; ++j) {
           const int col = n0 + wn * WTN + j * 16 + lc;
           const float dH = acc[i][j][r];
-          const float G = Elem<T>::load(GU + row * (2 * g.f) + col);
-          const float U = Elem<T>::load(GU + row * (2 * g.f) + g.f + col);
+          const float G = Elem<TO>::load(GU + row * (2 * g.f) + col);
+          const float U = Elem<TO>::load(GU + row * (2 * g.f) + g.f + col);
           const float sg = 1.0f / (1.0f + expf(-G));
-          Elem<T>::store(D + row * (2 * g.f) + col, dH * U * sg * (1.0f + G * (1.0f - sg)));
-          Elem<T>::store(D + row * (2 * g.f) + g.f + col, dH * G * sg);
+          Elem<TO>::store(D + row * (2 * g.f) + col, dH * U * sg * (1.0f + G * (1.0f - sg)));
+          Elem<TO>::store(D + row * (2 * g.f) + g.f + col, dH * G * sg);
         }
       }
   }
 }
-
 #undef MOE_GLOAD
 #undef MOE_LSTORE
+
+// ---------------------------------------------------------------------------
+// FP8 row quantisation (1 x 128 blocks) and dequantisation, 16 lanes per block
+// ---------------------------------------------------------------------------
+template <typename TS>
+__global__ __launch_bounds__(256) void quant_rows_kernel(const TS* __restrict__ src, fp8_t* __restrict__ q,
+                                                         float* __restrict__ scale, int64_t nchunks) {
+  constexpr int V = 8;  // elements per lane
+  const int64_t ch = blockIdx.x * int64_t(256) + threadIdx.x;  // chunk of 8 elements
+  const bool ok = ch < nchunks;
+  float v[V];
+  if (ok) {
+    if constexpr (sizeof(TS) == 2) {
+      Vec16<bf16_t>::load(reinterpret_cast<const bf16_t*>(src) + ch * V, v);
+    } else {
+      Vec16<float>::load(reinterpret_cast<const float*>(src) + ch * V, v);
+      Vec16<float>::load(reinterpret_cast<const float*>(src) + ch * V + 4, v + 4);
+    }
+  } else {
+    for (int i = 0; i < V; ++i) v[i] = 0.0f;
+  }
+  float amax = 0.0f;
+  for (int i = 0; i < V; ++i) amax = fmaxf(amax, fabsf(v[i]));
+  for (int o = 8; o >= 1; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o, kWave));
+  const float s = (amax == 0.0f) ? 1.0f : amax / 448.0f;
+  uint32_t lo = 0, hi = 0;
+  lo = __builtin_amdgcn_cvt_pk_fp8_f32(v[0] / s, v[1] / s, lo, false);
+  lo = __builtin_amdgcn_cvt_pk_fp8_f32(v[2] / s, v[3] / s, lo, true);
+  hi = __builtin_amdgcn_cvt_pk_fp8_f32(v[4] / s, v[5] / s, hi, false);
+  hi = __builtin_amdgcn_cvt_pk_fp8_f32(v[6] / s, v[7] / s, hi, true);
+  if (ok) {
+    *reinterpret_cast<u32x2*>(q + ch * V) = u32x2{lo, hi};
+    if ((ch & 15) == 0) scale[ch / 16] = s;  // rows are whole 128-blocks
+  }
+}
+
+__global__ __launch_bounds__(256) void dequant_rows_kernel(const fp8_t* __restrict__ q,
+                                                           const float* __restrict__ scale,
+                                                           bf16_t* __restrict__ dst, int64_t nchunks) {
+  const int64_t ch = blockIdx.x * int64_t(256) + threadIdx.x;
+  if (ch >= nchunks) return;
+  const u32x2 c = *reinterpret_cast<const u32x2*>(q + ch * 8);
+  const float s = scale[ch / 16];
+  float v[8] = {__builtin_amdgcn_cvt_f32_fp8(c[0], 0), __builtin_amdgcn_cvt_f32_fp8(c[0], 1),
+                __builtin_amdgcn_cvt_f32_fp8(c[0], 2), __builtin_amdgcn_cvt_f32_fp8(c[0], 3),
+                __builtin_amdgcn_cvt_f32_fp8(c[1], 0), __builtin_amdgcn_cvt_f32_fp8(c[1], 1),
+                __builtin_amdgcn_cvt_f32_fp8(c[1], 2), __builtin_amdgcn_cvt_f32_fp8(c[1], 3)};
+#pragma unroll
+  for (int i = 0; i < 8; ++i) v[i] *= s;
+  Vec16<bf16_t>::store(dst + ch * 8, v);
+}
+
+void launch_quant_rows(const void* src, bool src_bf16, int64_t rows, int64_t cols, uint8_t* q, float* scale,
+                       hipStream_t st) {
+  const int64_t nchunks = rows * cols / 8;
+  const int64_t grid = (nchunks + 255) / 256;
+  if (grid <= 0) return;
+  if (src_bf16)
+    quant_rows_kernel<bf16_t><<<grid, 256, 0, st>>>(reinterpret_cast<const bf16_t*>(src), q, scale, nchunks);
+  else
+    quant_rows_kernel<float><<<grid, 256, 0, st>>>(reinterpret_cast<const float*>(src), q, scale, nchunks);
+}
+
+static void dequant_rows(const uint8_t* q, const float* scale, int64_t rows, int64_t cols, bf16_t* dst,
+                         hipStream_t st) {
+  const int64_t nchunks = rows * cols / 8;
+  const int64_t grid = (nchunks + 255) / 256;
+  if (grid > 0) dequant_rows_kernel<<<grid, 256, 0, st>>>(q, scale, dst, nchunks);
+}
 
 // ---------------------------------------------------------------------------
 template <typename T> struct Tile;
 template <> struct Tile<bf16_t> { static constexpr int BM = 128, BN = 128, BK = 64; };
 template <> struct Tile<float> { static constexpr int BM = 128, BN = 128, BK = 32; };
+template <> struct Tile<fp8_t> { static constexpr int BM = 128, BN = 128, BK = 128; };
 
 static int rows_tile_bound(int64_t A, int64_t G, int BM) {
   return int((A + G * (BM - 1)) / BM);
@@ -492,6 +672,45 @@ static void zero_bytes(void* dst, int64_t bytes, hipStream_t st) {
   if (n > 0) zero_kernel<<<1024, 256, 0, st>>>(reinterpret_cast<uint32_t*>(dst), n);
 }
 
+// Workspace layout of the grouped FFN calls (byte offsets; see ffn_ws_bytes).
+struct FfnWs {
+  size_t h_bf16 = 0;   // fwd fp8: H before quantisation [A, f] bf16
+  size_t d_gu = 0;     // bwd: dGU [A, 2f] act
+  size_t d_out_q = 0;  // bwd fp8: dO codes [A, d] + scales [A, d/128]
+  size_t d_out_s = 0;
+  size_t d_gu_q = 0;   // bwd fp8: dGU codes [A, 2f] + scales [A, 2f/128]
+  size_t d_gu_s = 0;
+  size_t x_deq = 0;    // bwd fp8: dequantised X [A, d] bf16
+  size_t h_deq = 0;    // bwd fp8: dequantised H [A, f] bf16
+  size_t total = 0;
+};
+
+static size_t al(size_t v) { return (v + 255) & ~size_t(255); }
+
+static FfnWs ffn_ws(int64_t A, int64_t d, int64_t f, int act_bytes, bool fp8, bool bwd) {
+  FfnWs w;
+  size_t o = 0;
+  if (!bwd) {
+    if (fp8) { w.h_bf16 = o; o += al(size_t(A) * f * 2); }
+  } else {
+    w.d_gu = o; o += al(size_t(A) * 2 * f * act_bytes);
+    if (fp8) {
+      w.d_out_q = o; o += al(size_t(A) * d);
+      w.d_out_s = o; o += al(size_t(A) * (d / 128) * 4);
+      w.d_gu_q = o; o += al(size_t(A) * 2 * f);
+      w.d_gu_s = o; o += al(size_t(A) * (2 * f / 128) * 4);
+      w.x_deq = o; o += al(size_t(A) * d * 2);
+      w.h_deq = o; o += al(size_t(A) * f * 2);
+    }
+  }
+  w.total = o;
+  return w;
+}
+
+size_t ffn_ws_bytes(int64_t A, int64_t d, int64_t f, int act_bytes, bool fp8, bool bwd) {
+  return ffn_ws(A, d, f, act_bytes, fp8, bwd).total;
+}
+
 template <typename T>
 static void ffn_fwd_t(const FfnLaunch& a, hipStream_t st) {
   constexpr int BM = Tile<T>::BM, BN = Tile<T>::BN;
@@ -516,15 +735,71 @@ static void ffn_fwd_t(const FfnLaunch& a, hipStream_t st) {
   run_gemm<T, T, true, true, G_ROWS, EPI_STORE>(g2, mt_bound * g2.tiles_n, st);
 }
 
+static void ffn_fwd_fp8(const FfnLaunch& a, hipStream_t st) {
+  constexpr int BM = Tile<fp8_t>::BM, BN = Tile<fp8_t>::BN;
+  const FfnWs w = ffn_ws(a.A, a.d, a.f, 2, true, false);
+  bf16_t* h16 = reinterpret_cast<bf16_t*>(static_cast<char*>(a.ws) + w.h_bf16);
+  const int mt_bound = rows_tile_bound(a.A, a.E, BM);
+  GemmArgs g1{};
+  g1.A = a.x_perm; g1.lda = a.d;
+  g1.a_scale = a.x_scale; g1.a_scale_ld = int(a.d / 128);
+  g1.B = a.w1; g1.ldb = a.d; g1.b_gstride = 2 * a.f * a.d;
+  g1.b_scale = a.w1_scale; g1.b_scale_gstride = (2 * a.f / 128) * (a.d / 128); g1.b_scale_ld = int(a.d / 128);
+  g1.offsets = a.offsets; g1.G = int(a.E);
+  g1.N = int(2 * a.f); g1.K = int(a.d); g1.f = int(a.f);
+  g1.aux0 = a.act_gu; g1.aux1 = h16;
+  g1.tiles_n = int(2 * a.f / BN);
+  run_gemm<fp8_t, bf16_t, true, true, G_ROWS, EPI_SWIGLU>(g1, mt_bound * g1.tiles_n, st);
+  // H -> E4M3 per 1 x 128 block (the second GEMM's A operand, saved for bwd)
+  launch_quant_rows(h16, true, a.A, a.f, reinterpret_cast<uint8_t*>(a.act_h), a.h_scale, st);
+  GemmArgs g2{};
+  g2.A = a.act_h; g2.lda = a.f;
+  g2.a_scale = a.h_scale; g2.a_scale_ld = int(a.f / 128);
+  g2.B = a.w2; g2.ldb = a.f; g2.b_gstride = a.d * a.f;
+  g2.b_scale = a.w2_scale; g2.b_scale_gstride = (a.d / 128) * (a.f / 128); g2.b_scale_ld = int(a.f / 128);
+  g2.C = a.out_perm; g2.ldc = a.d;
+  g2.offsets = a.offsets; g2.G = int(a.E);
+  g2.N = int(a.d); g2.K = int(a.f);
+  g2.tiles_n = int(a.d / BN);
+  run_gemm<fp8_t, bf16_t, true, true, G_ROWS, EPI_STORE>(g2, mt_bound * g2.tiles_n, st);
+}
+
+// Weight gradients over the ragged rows of every expert (K split by group).
+template <typename T, typename TW>
+static void wgrad_t(const void* d_out, const void* act_h, const void* d_gu, const void* x, void* dw1,
+                    void* dw2, const int32_t* offsets, int64_t d, int64_t f, int64_t E, hipStream_t st) {
+  constexpr int BM = Tile<T>::BM, BN = Tile<T>::BN;
+  // dW2 = dO^T H   [d, f]
+  GemmArgs g3{};
+  g3.A = d_out; g3.lda = d;
+  g3.B = act_h; g3.ldb = f;
+  g3.C = dw2; g3.ldc = f; g3.c_gstride = d * f;
+  g3.offsets = offsets; g3.G = int(E);
+  g3.M = int(d); g3.N = int(f);
+  g3.tiles_m = int(d / BM); g3.tiles_n = int(f / BN);
+  run_gemm<T, TW, false, false, G_KSPLIT, EPI_STORE>(g3, int(E) * g3.tiles_m * g3.tiles_n, st);
+  // dW1 = dGU^T X   [2f, d]
+  GemmArgs g4{};
+  g4.A = d_gu; g4.lda = 2 * f;
+  g4.B = x; g4.ldb = d;
+  g4.C = dw1; g4.ldc = d; g4.c_gstride = 2 * f * d;
+  g4.offsets = offsets; g4.G = int(E);
+  g4.M = int(2 * f); g4.N = int(d);
+  g4.tiles_m = int(2 * f / BM); g4.tiles_n = int(d / BN);
+  run_gemm<T, TW, false, false, G_KSPLIT, EPI_STORE>(g4, int(E) * g4.tiles_m * g4.tiles_n, st);
+}
+
 template <typename T>
 static void ffn_bwd_t(const FfnBwdLaunch& a, hipStream_t st) {
   constexpr int BM = Tile<T>::BM, BN = Tile<T>::BN;
+  const FfnWs w = ffn_ws(a.A, a.d, a.f, int(sizeof(T)), false, true);
+  void* d_gu = static_cast<char*>(a.ws) + w.d_gu;
   const int mt_bound = rows_tile_bound(a.A, a.E, BM);
   // dH = dO W2, fused SwiGLU backward -> dGU
   GemmArgs g1{};
   g1.A = a.d_out; g1.lda = a.d;
   g1.B = a.w2; g1.ldb = a.f; g1.b_gstride = a.d * a.f;
-  g1.C = a.d_gu; g1.ldc = 2 * a.f;
+  g1.C = d_gu; g1.ldc = 2 * a.f;
   g1.offsets = a.offsets; g1.G = int(a.E);
   g1.N = int(a.f); g1.K = int(a.d); g1.f = int(a.f);
   g1.aux0 = const_cast<void*>(a.act_gu);
@@ -532,31 +807,61 @@ static void ffn_bwd_t(const FfnBwdLaunch& a, hipStream_t st) {
   run_gemm<T, T, true, false, G_ROWS, EPI_DSWIGLU>(g1, mt_bound * g1.tiles_n, st);
   // dX = dGU W1
   GemmArgs g2{};
-  g2.A = a.d_gu; g2.lda = 2 * a.f;
+  g2.A = d_gu; g2.lda = 2 * a.f;
   g2.B = a.w1; g2.ldb = a.d; g2.b_gstride = 2 * a.f * a.d;
   g2.C = a.dx_perm; g2.ldc = a.d;
   g2.offsets = a.offsets; g2.G = int(a.E);
   g2.N = int(a.d); g2.K = int(2 * a.f);
   g2.tiles_n = int(a.d / BN);
   run_gemm<T, T, true, false, G_ROWS, EPI_STORE>(g2, mt_bound * g2.tiles_n, st);
-  // dW2 = dO^T H   [d, f]
-  GemmArgs g3{};
-  g3.A = a.d_out; g3.lda = a.d;
-  g3.B = a.act_h; g3.ldb = a.f;
-  g3.C = a.dw2; g3.ldc = a.f; g3.c_gstride = a.d * a.f;
-  g3.offsets = a.offsets; g3.G = int(a.E);
-  g3.M = int(a.d); g3.N = int(a.f);
-  g3.tiles_m = int(a.d / BM); g3.tiles_n = int(a.f / BN);
-  run_gemm<T, T, false, false, G_KSPLIT, EPI_STORE>(g3, int(a.E) * g3.tiles_m * g3.tiles_n, st);
-  // dW1 = dGU^T X   [2f, d]
-  GemmArgs g4{};
-  g4.A = a.d_gu; g4.lda = 2 * a.f;
-  g4.B = a.x_perm; g4.ldb = a.d;
-  g4.C = a.dw1; g4.ldc = a.d; g4.c_gstride = 2 * a.f * a.d;
-  g4.offsets = a.offsets; g4.G = int(a.E);
-  g4.M = int(2 * a.f); g4.N = int(a.d);
-  g4.tiles_m = int(2 * a.f / BM); g4.tiles_n = int(a.d / BN);
-  run_gemm<T, T, false, false, G_KSPLIT, EPI_STORE>(g4, int(a.E) * g4.tiles_m * g4.tiles_n, st);
+  wgrad_t<T, T>(a.d_out, a.act_h, d_gu, a.x_perm, a.dw1, a.dw2, a.offsets, a.d, a.f, a.E, st);
+}
+
+// FP8 backward: the data-gradient GEMMs run in FP8 with their gradient
+// operand quantised per 1 x 128 block along the contraction dim and the
+// forward's 128 x 128 weight blocks; the weight gradients run in bf16 on the
+// dequantised forward operands (X, H) and the bf16 gradients.
+static void ffn_bwd_fp8(const FfnBwdLaunch& a, hipStream_t st) {
+  constexpr int BM = Tile<fp8_t>::BM, BN = Tile<fp8_t>::BN;
+  const FfnWs w = ffn_ws(a.A, a.d, a.f, 2, true, true);
+  char* ws = static_cast<char*>(a.ws);
+  bf16_t* d_gu = reinterpret_cast<bf16_t*>(ws + w.d_gu);
+  uint8_t* dq = reinterpret_cast<uint8_t*>(ws + w.d_out_q);
+  float* ds = reinterpret_cast<float*>(ws + w.d_out_s);
+  uint8_t* gq = reinterpret_cast<uint8_t*>(ws + w.d_gu_q);
+  float* gs = reinterpret_cast<float*>(ws + w.d_gu_s);
+  bf16_t* xd = reinterpret_cast<bf16_t*>(ws + w.x_deq);
+  bf16_t* hd = reinterpret_cast<bf16_t*>(ws + w.h_deq);
+  const int mt_bound = rows_tile_bound(a.A, a.E, BM);
+  launch_quant_rows(a.d_out, true, a.A, a.d, dq, ds, st);
+  // dH = Q(dO) W2 (+ SwiGLU backward from the saved bf16 GU)
+  GemmArgs g1{};
+  g1.A = dq; g1.lda = a.d;
+  g1.a_scale = ds; g1.a_scale_ld = int(a.d / 128);
+  g1.B = a.w2; g1.ldb = a.f; g1.b_gstride = a.d * a.f;
+  g1.b_scale = a.w2_scale; g1.b_scale_gstride = (a.d / 128) * (a.f / 128); g1.b_scale_ld = int(a.f / 128);
+  g1.C = d_gu; g1.ldc = 2 * a.f;
+  g1.offsets = a.offsets; g1.G = int(a.E);
+  g1.N = int(a.f); g1.K = int(a.d); g1.f = int(a.f);
+  g1.aux0 = const_cast<void*>(a.act_gu);
+  g1.tiles_n = int(a.f / BN);
+  run_gemm<fp8_t, bf16_t, true, false, G_ROWS, EPI_DSWIGLU>(g1, mt_bound * g1.tiles_n, st);
+  // dX = Q(dGU) W1
+  launch_quant_rows(d_gu, true, a.A, 2 * a.f, gq, gs, st);
+  GemmArgs g2{};
+  g2.A = gq; g2.lda = 2 * a.f;
+  g2.a_scale = gs; g2.a_scale_ld = int(2 * a.f / 128);
+  g2.B = a.w1; g2.ldb = a.d; g2.b_gstride = 2 * a.f * a.d;
+  g2.b_scale = a.w1_scale; g2.b_scale_gstride = (2 * a.f / 128) * (a.d / 128); g2.b_scale_ld = int(a.d / 128);
+  g2.C = a.dx_perm; g2.ldc = a.d;
+  g2.offsets = a.offsets; g2.G = int(a.E);
+  g2.N = int(a.d); g2.K = int(2 * a.f);
+  g2.tiles_n = int(a.d / BN);
+  run_gemm<fp8_t, bf16_t, true, false, G_ROWS, EPI_STORE>(g2, mt_bound * g2.tiles_n, st);
+  // weight gradients in bf16 on dequantised X and H
+  dequant_rows(reinterpret_cast<const uint8_t*>(a.x_perm), a.x_scale, a.A, a.d, xd, st);
+  dequant_rows(reinterpret_cast<const uint8_t*>(a.act_h), a.h_scale, a.A, a.f, hd, st);
+  wgrad_t<bf16_t, bf16_t>(a.d_out, hd, d_gu, xd, a.dw1, a.dw2, a.offsets, a.d, a.f, a.E, st);
 }
 
 void launch_grouped_ffn(const FfnLaunch& a, hipStream_t st) {
@@ -564,7 +869,8 @@ void launch_grouped_ffn(const FfnLaunch& a, hipStream_t st) {
     copy_bytes(a.x_perm, a.out_perm, a.A * a.d * (a.act == 1 ? 2 : 4), st);
     return;
   }
-  if (a.wt == 1) ffn_fwd_t<bf16_t>(a, st);
+  if (a.wt == 2) ffn_fwd_fp8(a, st);
+  else if (a.wt == 1) ffn_fwd_t<bf16_t>(a, st);
   else ffn_fwd_t<float>(a, st);
 }
 
@@ -577,7 +883,8 @@ void launch_grouped_ffn_bwd(const FfnBwdLaunch& a, hipStream_t st) {
     zero_bytes(a.dw2, a.E * a.d * a.f * ws, st);
     return;
   }
-  if (a.wt == 1) ffn_bwd_t<bf16_t>(a, st);
+  if (a.wt == 2) ffn_bwd_fp8(a, st);
+  else if (a.wt == 1) ffn_bwd_t<bf16_t>(a, st);
   else ffn_bwd_t<float>(a, st);
 }
 

@@ -96,12 +96,18 @@ struct FfnLaunch {
   void* act_h;
   float* h_scale;
   void* out_perm;
+  void* ws;  // ffn_ws_bytes(..., bwd = false)
   int64_t A, d, f, E;
   int act;   // 0 f32, 1 bf16
   int wt;    // 0 f32, 1 bf16, 2 fp8
   bool identity;
 };
 void launch_grouped_ffn(const FfnLaunch& a, hipStream_t st);
+// Workspace bytes of the grouped FFN forward (bwd = false) or backward.
+size_t ffn_ws_bytes(int64_t A, int64_t d, int64_t f, int act_bytes, bool fp8, bool bwd);
+// FP8 E4M3 quantisation of rows in 1 x 128 blocks (cols a multiple of 128).
+void launch_quant_rows(const void* src, bool src_bf16, int64_t rows, int64_t cols, uint8_t* q,
+                       float* scale, hipStream_t st);
 
 struct FfnBwdLaunch {
   const void* x_perm;
@@ -118,7 +124,7 @@ struct FfnBwdLaunch {
   void* dx_perm;
   void* dw1;
   void* dw2;
-  void* d_gu;            // workspace [A, 2f] act
+  void* ws;              // ffn_ws_bytes(..., bwd = true)
   int64_t A, d, f, E;
   int act;
   int wt;

@@ -94,8 +94,12 @@ size_t moe_workspace_size(const moe_config* cfg, int op) {
   const int64_t T = cfg->num_tokens, E = cfg->num_experts, k = cfg->top_k, f = cfg->ffn_hidden;
   switch (op) {
     case MOE_OP_DISPATCH: return T ? round_up(size_t(dispatch_chunks(T)) * size_t(E) * 4) : 0;
+    case MOE_OP_GROUPED_FFN:
+      return round_up(moe::ffn_ws_bytes(T * k, cfg->hidden, f, int(act_bytes(cfg->act_dtype)),
+                                        cfg->weight_dtype == MOE_DTYPE_FP8_E4M3, false));
     case MOE_OP_GROUPED_FFN_BWD:
-      return round_up(size_t(T) * size_t(k) * size_t(2 * f) * act_bytes(cfg->act_dtype));
+      return round_up(moe::ffn_ws_bytes(T * k, cfg->hidden, f, int(act_bytes(cfg->act_dtype)),
+                                        cfg->weight_dtype == MOE_DTYPE_FP8_E4M3, true));
     case MOE_OP_ROUTE_BWD: {
       const int Z = moe::route_bwd_zsplit(T, cfg->hidden, E);
       const size_t parts = Z > 1 ? size_t(Z) * size_t(E) * size_t(cfg->hidden) * 4 : 0;
@@ -157,8 +161,6 @@ int moe_grouped_ffn(const moe_config* cfg, const void* x_perm, const float* x_sc
                     const int32_t* offsets, const void* w1, const float* w1_scale, const void* w2,
                     const float* w2_scale, void* act_gu, void* act_h, float* h_scale, void* out_perm,
                     void* ws, size_t ws_bytes, void* stream) {
-  (void)ws;
-  (void)ws_bytes;
   MOE_CHECK(check_cfg(cfg));
   const bool identity = cfg->ffn_mode == MOE_FFN_IDENTITY;
   const bool fp8 = cfg->weight_dtype == MOE_DTYPE_FP8_E4M3;
@@ -170,13 +172,15 @@ int moe_grouped_ffn(const moe_config* cfg, const void* x_perm, const float* x_sc
       MOE_CHECK(need(h_scale));
     }
   }
-  MOE_CHECK(align_all(x_perm, x_scale, offsets, w1, w1_scale, w2, w2_scale, act_gu, act_h, h_scale, out_perm));
-  if (fp8 && !identity) return MOE_ERR_UNSUPPORTED_DTYPE;
+  MOE_CHECK(align_all(x_perm, x_scale, offsets, w1, w1_scale, w2, w2_scale, act_gu, act_h, h_scale, out_perm, ws));
+  if (fp8 && identity) return MOE_ERR_UNSUPPORTED_DTYPE;
   if (cfg->num_tokens == 0) return MOE_OK;
+  const size_t need_ws = moe_workspace_size(cfg, MOE_OP_GROUPED_FFN);
+  if (need_ws && (!ws || ws_bytes < need_ws)) return MOE_ERR_WORKSPACE;
   moe::FfnLaunch a{};
   a.x_perm = x_perm; a.x_scale = x_scale; a.offsets = offsets; a.w1 = w1; a.w1_scale = w1_scale;
   a.w2 = w2; a.w2_scale = w2_scale; a.act_gu = act_gu; a.act_h = act_h; a.h_scale = h_scale;
-  a.out_perm = out_perm;
+  a.out_perm = out_perm; a.ws = ws;
   a.A = cfg->num_tokens * cfg->top_k; a.d = cfg->hidden; a.f = cfg->ffn_hidden; a.E = cfg->num_experts;
   a.act = cfg->act_dtype == MOE_DTYPE_BF16 ? 1 : 0;
   a.wt = cfg->weight_dtype == MOE_DTYPE_F32 ? 0 : (cfg->weight_dtype == MOE_DTYPE_BF16 ? 1 : 2);
@@ -235,14 +239,14 @@ int moe_grouped_ffn_bwd(const moe_config* cfg, const void* x_perm, const float* 
     }
   }
   MOE_CHECK(align_all(x_perm, x_scale, offsets, w1, w1_scale, w2, w2_scale, act_gu, act_h, h_scale, d_out_perm, dx_perm, dw1, dw2, ws));
-  if (fp8 && !identity) return MOE_ERR_UNSUPPORTED_DTYPE;
+  if (fp8 && identity) return MOE_ERR_UNSUPPORTED_DTYPE;
   if (cfg->num_tokens == 0) return MOE_OK;
   if (!identity && (!ws || ws_bytes < moe_workspace_size(cfg, MOE_OP_GROUPED_FFN_BWD)))
     return MOE_ERR_WORKSPACE;
   moe::FfnBwdLaunch a{};
   a.x_perm = x_perm; a.x_scale = x_scale; a.offsets = offsets; a.w1 = w1; a.w1_scale = w1_scale;
   a.w2 = w2; a.w2_scale = w2_scale; a.act_gu = act_gu; a.act_h = act_h; a.h_scale = h_scale;
-  a.d_out = d_out_perm; a.dx_perm = dx_perm; a.dw1 = dw1; a.dw2 = dw2; a.d_gu = ws;
+  a.d_out = d_out_perm; a.dx_perm = dx_perm; a.dw1 = dw1; a.dw2 = dw2; a.ws = ws;
   a.A = cfg->num_tokens * cfg->top_k; a.d = cfg->hidden; a.f = cfg->ffn_hidden; a.E = cfg->num_experts;
   a.act = cfg->act_dtype == MOE_DTYPE_BF16 ? 1 : 0;
   a.wt = cfg->weight_dtype == MOE_DTYPE_F32 ? 0 : (cfg->weight_dtype == MOE_DTYPE_BF16 ? 1 : 2);

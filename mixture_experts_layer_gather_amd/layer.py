@@ -75,6 +75,8 @@ class MoELayer:
         # workspaces
         u8 = torch.uint8
         self.ws_dispatch = e(max(1, L.workspace_size(self.cfg, L.OP_DISPATCH)), dt=u8)
+        self.ws_ffn = e(max(1, L.workspace_size(self.cfg, L.OP_GROUPED_FFN),
+                            L.workspace_size(self.scfg, L.OP_GROUPED_FFN)), dt=u8)
         self.ws_ffn_bwd = e(max(1, L.workspace_size(self.cfg, L.OP_GROUPED_FFN_BWD),
                                 L.workspace_size(self.scfg, L.OP_GROUPED_FFN_BWD)), dt=u8)
         self.ws_route_bwd = e(max(1, L.workspace_size(self.cfg, L.OP_ROUTE_BWD)), dt=u8)
@@ -135,7 +137,7 @@ class MoELayer:
                        self.perm_token, self.x_perm, self.x_scale, self.ws_dispatch)
         L.moe_grouped_ffn(c, self.x_perm, self.x_scale, self.offsets, self.w1, self.w1_scale,
                           self.w2, self.w2_scale, self.act_gu, self.act_h, self.h_scale,
-                          self.out_perm)
+                          self.out_perm, self.ws_ffn)
         shared_out = None
         if self.shared:
             sx, sxs = x, None
@@ -144,7 +146,7 @@ class MoELayer:
                 sx, sxs = self.s_x, self.s_x_scale
             L.moe_grouped_ffn(self.scfg, sx, sxs, self.s_offsets, self.sw1, self.sw1_scale,
                               self.sw2, self.sw2_scale, self.s_gu, self.s_h, self.s_h_scale,
-                              self.s_out)
+                              self.s_out, self.ws_ffn)
             shared_out = self.s_out
         L.moe_combine(c, self.out_perm, self.row_id_map, self.topk_gate, shared_out, self.y)
         return self.y

@@ -308,12 +308,17 @@ def ffn_fwd(X, W1, W2, identity: bool = False, h_fp8: bool = False):
     return GU, H, O
 
 
-def ffn_bwd(X, W1, W2, GU, H, dO, identity: bool = False):
+def ffn_bwd(X, W1, W2, GU, H, dO, identity: bool = False, dgrad_fp8: bool = False):
     """Backward of ffn_fwd for one expert's rows (fp64).
       dH  = dO W2                    dW2 = dO^T H
       dG  = dH * U * s(G) * (1 + G (1 - s(G)))   (silu'(G) = s + G s (1 - s))
       dU  = dH * silu(G)
       dX  = [dG dU] W1               dW1 = [dG dU]^T X
+    dgrad_fp8 (FP8 layers): the two data-gradient products take their
+    gradient operand quantised per 1x128 block along its contraction dim
+    (dO along d, [dG dU] along 2f, each from its fp32 rounding); W1, W2, X
+    and H are the dequantised forward values; the weight gradients use the
+    unquantised gradients.
     Returns dX, dW1, dW2, dGU."""
     dO = np.asarray(dO, dtype=np.float64)
     if identity:
@@ -323,13 +328,15 @@ def ffn_bwd(X, W1, W2, GU, H, dO, identity: bool = False):
     W2 = np.asarray(W2, dtype=np.float64)
     f = W2.shape[1]
     G, U = GU[:, :f], GU[:, f:]
-    dH = dO @ W2
+    dOq = fp8_roundtrip_rows(dO.astype(np.float32)) if dgrad_fp8 else dO
+    dH = dOq @ W2
     dW2 = dO.T @ H
     s = sigmoid64(G)
     dG = dH * U * s * (1.0 + G * (1.0 - s))
     dU = dH * G * s
     dGU = np.concatenate([dG, dU], axis=1)
-    dX = dGU @ W1
+    dGUq = fp8_roundtrip_rows(dGU.astype(np.float32)) if dgrad_fp8 else dGU
+    dX = dGUq @ W1
     dW1 = dGU.T @ X
     return dX, dW1, dW2, dGU
 
@@ -503,7 +510,7 @@ def layer(cfg, inp: dict, identity: bool = False) -> dict:
         if r1 > r0:
             W1, W2, _ = W[e]
             dx_e, dw1, dw2, _ = ffn_bwd(Xp[r0:r1], W1, W2, GU[r0:r1], H[r0:r1],
-                                        dO[r0:r1], identity)
+                                        dO[r0:r1], identity, dgrad_fp8=fp8)
             dXp[r0:r1] = dx_e
             if not identity:
                 dW1[e] = dw1
@@ -511,7 +518,7 @@ def layer(cfg, inp: dict, identity: bool = False) -> dict:
     out.update(dx_perm=dXp, dw1=dW1, dw2=dW2)
     dx_sh = None
     if cfg.shared:
-        dx_sh, sdw1, sdw2, _ = ffn_bwd(Xs, SW1, SW2, sgu, sh, dy, identity)
+        dx_sh, sdw1, sdw2, _ = ffn_bwd(Xs, SW1, SW2, sgu, sh, dy, identity, dgrad_fp8=fp8)
         out.update(shared_dx=dx_sh, shared_dw1=sdw1, shared_dw2=sdw2)
     dx = dispatch_bwd(dXp, rmap, dx_sh)
     dL = route_bwd_logits(dgate, idx, L, cfg.score, cfg.renorm, cfg.gate_scale)
@@ -531,7 +538,7 @@ def rel_l2(a, b) -> float:
     return float(na / nb)
 
 
-def ffn_wgrad_columns(X, W1, W2, dO, cols):
+def ffn_wgrad_columns(X, W1, W2, dO, cols, h_fp8: bool = False):
     """Selected slices of one expert's weight gradients, over all its rows:
     for each hidden feature n in `cols`, rows n (gate) and f+n (up) of dW1
     and column n of dW2 — the same formulas as ffn_bwd evaluated only where
@@ -548,6 +555,8 @@ def ffn_wgrad_columns(X, W1, W2, dO, cols):
     dH = dO @ W2[:, cols]                  # [M, c]
     s = sigmoid64(G)
     H = G * s * U
+    if h_fp8:  # the forward's H is quantised per 1x128 block of the full row
+        H = ffn_fwd(X, W1, W2, h_fp8=True)[1][:, cols]
     dG = dH * U * s * (1.0 + G * (1.0 - s))
     dU = dH * G * s
     dW1_rows = np.concatenate([dG.T @ X, dU.T @ X], axis=0)
@@ -555,7 +564,7 @@ def ffn_wgrad_columns(X, W1, W2, dO, cols):
     return dW1_rows, dW2_cols
 
 
-def ffn_dx_rows(X, W1, W2, dO):
+def ffn_dx_rows(X, W1, W2, dO, fp8: bool = False):
     """dX for the given rows of one expert (fp64), as in ffn_bwd."""
-    GU, H, _ = ffn_fwd(X, W1, W2)
-    return ffn_bwd(X, W1, W2, GU, H, dO)[0]
+    GU, H, _ = ffn_fwd(X, W1, W2, h_fp8=fp8)
+    return ffn_bwd(X, W1, W2, GU, H, dO, dgrad_fp8=fp8)[0]

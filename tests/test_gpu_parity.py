@@ -118,6 +118,7 @@ SMALL = {
     "mixtral_mini_f32": S.mini(S.CONFIGS[1], T=333, d=128, f=256).replace(act="f32", weight="f32"),
     "deepseek_mini": S.mini(S.CONFIGS[2], T=300, d=256, f=256, E=32).replace(k=6),
     "qwen_skew_mini": S.mini(S.CONFIGS[3], T=700, d=256, f=128, E=16).replace(k=4),
+    "deepseek_fp8_mini": S.mini(S.CONFIGS[4], T=400, d=384, f=256, E=32).replace(k=6),
 }
 
 
@@ -247,21 +248,38 @@ def _full_size_check(cfg, n_tok=24, n_cols=3):
                perm_token=ptok)
     _check_routing_and_dispatch(cfg, layer, ref)
     # dispatched rows: x_perm == x[perm_token], checked on the device
-    x_dev = inp["x"].to(DEV)
-    assert torch.equal(layer.x_perm, x_dev[layer.perm_token.long()]), "x_perm"
+    if cfg.weight == "fp8":
+        xq, xs = oracle.quant_blocks(oracle.as_f32(inp["x"]), 1, 128)
+        assert np.array_equal(_np(layer.x_perm), xq[ptok]), "fp8 x_perm codes"
+        assert np.array_equal(_np(layer.x_scale), xs[ptok]), "fp8 x_perm scales"
+    else:
+        x_dev = inp["x"].to(DEV)
+        assert torch.equal(layer.x_perm, x_dev[layer.perm_token.long()]), "x_perm"
     tol = _tol(cfg)
-    # full forward on the oracle, expert by expert
+    # full forward on the oracle, expert by expert (FP8 layers: the oracle's
+    # own quantisation of x per 1 x 128 and of the bf16 master weights per
+    # 128 x 128, dequantised exactly)
     _say(f"[full] {cfg.name}: oracle forward")
+    fp8 = cfg.weight == "fp8"
     X = oracle.as_f64(inp["x"])
+    if fp8:
+        X = oracle.fp8_roundtrip_rows(oracle.as_f32(inp["x"]))
+
+    def W(w):
+        if not fp8:
+            return oracle.as_f64(w)
+        q, sc = oracle.quant_blocks(oracle.as_f32(w), 128, 128)
+        return oracle.dequant_blocks(q, sc, 128, 128)
+
     O = np.zeros((cfg.A, cfg.d))
     for e in range(cfg.E):
         r0, r1 = offsets[e], offsets[e + 1]
         if r1 > r0:
-            O[r0:r1] = oracle.ffn_fwd(X[ptok[r0:r1]], oracle.as_f64(inp["w1"][e]),
-                                      oracle.as_f64(inp["w2"][e]))[2]
+            O[r0:r1] = oracle.ffn_fwd(X[ptok[r0:r1]], W(inp["w1"][e]), W(inp["w2"][e]), h_fp8=fp8)[2]
     O_sh = None
     if cfg.shared:
-        O_sh = oracle.ffn_fwd(X, oracle.as_f64(inp["sw1"]), oracle.as_f64(inp["sw2"]))[2]
+        SW1, SW2 = W(inp["sw1"]), W(inp["sw2"])
+        O_sh = oracle.ffn_fwd(X, SW1, SW2, h_fp8=fp8)[2]
     y = oracle.combine(O, rmap, g, O_sh)
     err = oracle.rel_l2(_np(layer.y), y)
     _say(f"[full] {cfg.name}: y rel L2 {err:.2e}")
@@ -286,12 +304,10 @@ def _full_size_check(cfg, n_tok=24, n_cols=3):
     for e, lst in by_e.items():
         tis = np.array([a for a, _ in lst])
         rs = np.array([b for _, b in lst])
-        dxe = oracle.ffn_dx_rows(X[toks[tis]], oracle.as_f64(inp["w1"][e]),
-                                 oracle.as_f64(inp["w2"][e]), dO[rs])
+        dxe = oracle.ffn_dx_rows(X[toks[tis]], W(inp["w1"][e]), W(inp["w2"][e]), dO[rs], fp8=fp8)
         np.add.at(dx_s, tis, dxe)
     if cfg.shared:
-        dx_s += oracle.ffn_dx_rows(X[toks], oracle.as_f64(inp["sw1"]), oracle.as_f64(inp["sw2"]),
-                                   dy[toks])
+        dx_s += oracle.ffn_dx_rows(X[toks], SW1, SW2, dy[toks], fp8=fp8)
     err = oracle.rel_l2(_np(layer.dx[torch.as_tensor(toks)]), dx_s)
     _say(f"[full] {cfg.name}: dx (sampled) rel L2 {err:.2e}")
     assert err <= tol, "dx"
@@ -300,8 +316,8 @@ def _full_size_check(cfg, n_tok=24, n_cols=3):
     for e in sorted(exps):
         cols = np.sort(rng.choice(cfg.f, n_cols, replace=False))
         r0, r1 = offsets[e], offsets[e + 1]
-        w1r, w2c = oracle.ffn_wgrad_columns(X[ptok[r0:r1]], oracle.as_f64(inp["w1"][e]),
-                                            oracle.as_f64(inp["w2"][e]), dO[r0:r1], cols)
+        w1r, w2c = oracle.ffn_wgrad_columns(X[ptok[r0:r1]], W(inp["w1"][e]), W(inp["w2"][e]),
+                                            dO[r0:r1], cols, h_fp8=fp8)
         rows = torch.as_tensor(np.concatenate([cols, cfg.f + cols]))
         got1 = _np(layer.dw1[e][rows])
         got2 = _np(layer.dw2[e][:, torch.as_tensor(cols)])
@@ -313,6 +329,6 @@ def _full_size_check(cfg, n_tok=24, n_cols=3):
         assert not _np(layer.dw1[int(empty[0])]).any() and not _np(layer.dw2[int(empty[0])]).any()
 
 
-@pytest.mark.parametrize("which", [1, 2, 3])
+@pytest.mark.parametrize("which", [1, 2, 3, 4])
 def test_full_size_layer(which):
     _full_size_check(S.CONFIGS[which])
