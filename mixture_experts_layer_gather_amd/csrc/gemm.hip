@@ -107,12 +107,20 @@ struct GemmArgs {
   int b_scale_ld;            // C/128
 };
 
-// Bijective remap of workgroup ids: consecutive ids are spread over the 8
-// XCDs round robin, so give XCD x the x-th contiguous slice of tiles.
-__device__ __forceinline__ int xcd_remap(int bid, int nblocks) {
-  const int q = nblocks / 8, r = nblocks % 8;
+// Workgroup id -> tile. Consecutive ids are dispatched to the 8 XCDs round
+// robin (one L2 each). Tiles are dealt to XCDs in super-blocks of kSuper
+// consecutive tiles: XCD x takes super-blocks x, x+8, x+16, ... so tiles
+// that share operands (same expert, neighbouring row/column blocks) run on
+// one L2, while a hot expert's many super-blocks spread over all XCDs. The
+// grid is a multiple of 8*kSuper, which makes the map a bijection.
+constexpr int kSuper = 64;
+__device__ __forceinline__ int tile_remap(int bid) {
   const int x = bid % 8, i = bid / 8;
-  return x * q + min(x, r) + i;
+  return ((i / kSuper) * 8 + x) * kSuper + (i % kSuper);
+}
+static int padded_grid(int tiles) {
+  const int q = 8 * kSuper;
+  return (tiles + q - 1) / q * q;
 }
 
 // Exclusive scan of per-group row-tile counts; returns the tile's group in
@@ -271,7 +279,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g) {
   const int lane = lane_id();
   const int wave = tid / kWave;
   const int wm = wave / WN, wn = wave % WN;
-  const int tile = xcd_remap(blockIdx.x, gridDim.x);
+  const int tile = tile_remap(blockIdx.x);
 
   int grp, mt, nt;
   int row0;           // first A row (ROWS) of the tile
@@ -292,7 +300,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g) {
   } else {
     const int per = g.tiles_m * g.tiles_n;
     grp = tile / per;
-    if (grp >= g.G) return;
+    if (grp >= g.G) return;  // padding of the grid
     const int rem = tile % per;
     mt = rem / g.tiles_n;
     nt = rem % g.tiles_n;
@@ -647,7 +655,7 @@ template <typename T, typename TC, bool AK, bool BKm, int MODE, int EPI>
 static void run_gemm(GemmArgs g, int grid, hipStream_t st) {
   constexpr int BM = Tile<T>::BM, BN = Tile<T>::BN, BK = Tile<T>::BK;
   if (grid <= 0) return;
-  gemm_kernel<T, TC, AK, BKm, MODE, EPI, BM, BN, BK, 2, 2><<<grid, 256, 0, st>>>(g);
+  gemm_kernel<T, TC, AK, BKm, MODE, EPI, BM, BN, BK, 2, 2><<<padded_grid(grid), 256, 0, st>>>(g);
 }
 
 template <typename T>
