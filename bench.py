@@ -22,6 +22,108 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0
 MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "fp8": 5000.0, "f32": 157.3}
+CSRC = os.path.join(ROOT, "mixture_experts_layer_gather_amd", "csrc")
+PROFILES = os.path.join(ROOT, "profiles")
+
+# Which library call launches a kernel, from its (demangled) name: the GEMM
+# template flags <T, TC, A K-major, B K-major, mode, epilogue, ...> give its
+# role. mode 0 = row-grouped, 1 = K split by group; epilogue 0 = store,
+# 1 = SwiGLU, 2 = SwiGLU backward.
+ROLE_CALL = {"gemm1": "grouped_ffn", "gemm2": "grouped_ffn", "dh": "grouped_ffn_bwd",
+             "dx": "grouped_ffn_bwd", "wgrad": "grouped_ffn_bwd"}
+
+
+def kernel_role(name: str):
+    import re
+    m = re.search(r"gemm_kernel<[^,]+, [^,]+, (true|false), (true|false), (\d), (\d)", name)
+    if not m:
+        return None
+    ak, bk, mode, epi = m.group(1) == "true", m.group(2) == "true", int(m.group(3)), int(m.group(4))
+    if mode == 1:
+        return "wgrad"
+    if epi == 1:
+        return "gemm1"
+    if epi == 2:
+        return "dh"
+    return "gemm2" if bk else "dx"
+
+
+def source_hash() -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for f in sorted(os.listdir(CSRC)):
+        if f.endswith((".hip", ".hpp")):
+            h.update(f.encode())
+            h.update(open(os.path.join(CSRC, f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def summarize_profiles(cfg_name, stats_dir, fetch_dir, write_dir, copy_fetch_dir, copy_write_dir,
+                       command):
+    """Turn rocprofv3 CSV output into profiles/<cfg>_kernels.md and
+    profiles/<cfg>_traffic.json (HBM bytes per launch of each GEMM call,
+    with FETCH_SIZE/WRITE_SIZE scaled by what they read for a 1 GiB copy)."""
+    import csv
+    import collections
+    stats = list(csv.DictReader(open(os.path.join(stats_dir, "run_kernel_stats.csv"))))
+    tot = sum(float(r["TotalDurationNs"]) for r in stats)
+    lines = [f"# Kernel time, {cfg_name}, fwd+bwd steps (rocprofv3 --kernel-trace --stats)", "",
+             "Command (repository root, one MI355X):", "", "```", command["stats"], "```", "",
+             "| avg us | calls | % time | kernel |", "|---:|---:|---:|---|"]
+    for r in stats:
+        lines.append(f"| {float(r['AverageNs']) / 1e3:.1f} | {r['Calls']} | "
+                     f"{100 * float(r['TotalDurationNs']) / tot:.1f} | `{r['Name'][:140]}` |")
+
+    def per_kernel(d):
+        agg = collections.defaultdict(list)
+        for r in csv.DictReader(open(os.path.join(d, "run_counter_collection.csv"))):
+            agg[r["Kernel_Name"]].append(float(r["Counter_Value"]))
+        return {k: sum(v) / len(v) for k, v in agg.items()}
+
+    cf, cw = per_kernel(copy_fetch_dir), per_kernel(copy_write_dir)
+    copy_name = [k for k in cf if "copyBuffer" in k][0]
+    f_fetch = (1 << 30) / (cf[copy_name] * 1024)
+    f_write = (1 << 30) / (cw[copy_name] * 1024)
+    kf, kw = per_kernel(fetch_dir), per_kernel(write_dir)
+    roles = collections.defaultdict(lambda: [0.0, 0.0, 0])
+    for name in kf:
+        role = kernel_role(name)
+        if role:
+            r = roles[role]
+            r[0] += kf[name] * 1024 * f_fetch
+            r[1] += kw.get(name, 0.0) * 1024 * f_write
+            r[2] += 1
+    calls = collections.defaultdict(float)
+    mult = {"wgrad": 2}  # dW1 and dW2 come from the same kernel
+    for role, (fb, wb, _) in roles.items():
+        calls[ROLE_CALL[role]] += (fb + wb) * mult.get(role, 1)
+    out = {"config": cfg_name, "source_hash": source_hash(), "fetch_factor": f_fetch,
+           "write_factor": f_write,
+           "roles_bytes_per_launch": {k: {"fetch": v[0], "write": v[1]} for k, v in roles.items()},
+           "calls_bytes_per_launch": dict(calls), "commands": command}
+    lines += ["", "## HBM traffic per launch (rocprofv3 --pmc FETCH_SIZE, then WRITE_SIZE)", "",
+              f"Scaled by a 1 GiB device copy: FETCH_SIZE x {f_fetch:.3f}, WRITE_SIZE x {f_write:.3f}.",
+              "", "| GEMM role | fetch GB | write GB |", "|---|---:|---:|"]
+    for k, v in roles.items():
+        lines.append(f"| {k} | {v[0] / 1e9:.3f} | {v[1] / 1e9:.3f} |")
+    lines += ["", "Commands:", "", "```"] + [command[k] for k in ("fetch", "write", "copy_fetch",
+                                                                    "copy_write")] + ["```"]
+    os.makedirs(PROFILES, exist_ok=True)
+    open(os.path.join(PROFILES, f"{cfg_name}_kernels.md"), "w").write("\n".join(lines) + "\n")
+    json.dump(out, open(os.path.join(PROFILES, f"{cfg_name}_traffic.json"), "w"), indent=1)
+    print("wrote", os.path.join(PROFILES, f"{cfg_name}_kernels.md"))
+
+
+def measured_traffic(cfg_name, call):
+    """HBM bytes per launch of `call` from the committed counter summary, or
+    None when the kernels changed since the counters were taken."""
+    f = os.path.join(PROFILES, f"{cfg_name}_traffic.json")
+    if not os.path.exists(f):
+        return None
+    d = json.load(open(f))
+    if d.get("source_hash") != source_hash():
+        return None
+    return d["calls_bytes_per_launch"].get(call)
 
 
 def stage_work(c):
@@ -164,9 +266,38 @@ def main():
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--config", default="mixtral_bf16")
-    ap.add_argument("--cpu-sample", type=int, default=384,
+    ap.add_argument("--cpu-sample", type=int, default=4096,
                     help="tokens of the workload timed on the CPU oracle (0: skip)")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="only run a plain 1 GiB device copy (counter calibration)")
+    ap.add_argument("--summarize", nargs=5, metavar="DIR",
+                    help="rocprofv3 output dirs: stats, FETCH_SIZE, WRITE_SIZE, copy FETCH_SIZE, "
+                         "copy WRITE_SIZE; writes profiles/<config>_kernels.md and _traffic.json")
     args = ap.parse_args()
+    if args.summarize:
+        c = args.config
+        cmd = {"stats": f"rocprofv3 --kernel-trace --stats --output-format csv -d <dir> -o run -- "
+                        f"python3 bench.py --steps 3 --warmup 1 --cpu-sample 0 --config {c}",
+               "fetch": f"rocprofv3 --pmc FETCH_SIZE --output-format csv -d <dir> -o run -- "
+                        f"python3 bench.py --steps 2 --warmup 1 --cpu-sample 0 --config {c}",
+               "write": f"rocprofv3 --pmc WRITE_SIZE --output-format csv -d <dir> -o run -- "
+                        f"python3 bench.py --steps 2 --warmup 1 --cpu-sample 0 --config {c}",
+               "copy_fetch": "rocprofv3 --pmc FETCH_SIZE --output-format csv -d <dir> -o run -- "
+                             "python3 bench.py --copy-probe",
+               "copy_write": "rocprofv3 --pmc WRITE_SIZE --output-format csv -d <dir> -o run -- "
+                             "python3 bench.py --copy-probe"}
+        summarize_profiles(c, *args.summarize, command=cmd)
+        return
+    if args.copy_probe:
+        import torch
+        a = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+        b = torch.empty_like(a)
+        a.fill_(1)
+        for _ in range(3):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_probe_bytes": 1 << 30, "launches": 3}))
+        return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for {args.gpus}); the path has no "
               "multi-GPU mode", file=sys.stderr)
@@ -211,9 +342,11 @@ def main():
     b, fl = work[dom]
     if "ffn" in dom:
         ach = fl / per_ms[dom] / 1e9
+        traffic = measured_traffic(cfg.name, dom)
         roof = {"kernel": f"moe_{dom.replace('shared_', 'grouped_')} ({dom})", "bound": "mfma",
                 "achieved": round(ach, 1), "peak": MFMA_PEAK_TFLOPS[dt], "unit": "TFLOP/s",
-                "frac": round(ach / MFMA_PEAK_TFLOPS[dt], 4), "traffic": None}
+                "frac": round(ach / MFMA_PEAK_TFLOPS[dt], 4),
+                "traffic": None if traffic is None else round(traffic)}
     else:
         ach = b / per_ms[dom] / 1e6
         roof = {"kernel": dom, "bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBPS,

@@ -126,11 +126,11 @@ static int padded_grid(int tiles) {
 // Exclusive scan of per-group row-tile counts; returns the tile's group in
 // s_info[0], its row-tile count in s_info[1] and the first tile of the group
 // in s_info[2], or s_info[0] = -1 when the tile is past the end.
-template <int BM>
+template <int BM, int NTH>
 __device__ void find_group(const int32_t* __restrict__ offsets, int G, int tiles_n, int tile,
                            int* s_scan, int* s_info) {
   const int tid = threadIdx.x;
-  constexpr int PER = 4;  // groups per thread (G <= 1024)
+  constexpr int PER = 1024 / NTH;  // groups per thread (G <= 1024)
   int cnt[PER], local = 0;
 #pragma unroll
   for (int i = 0; i < PER; ++i) {
@@ -143,7 +143,7 @@ __device__ void find_group(const int32_t* __restrict__ offsets, int G, int tiles
     cnt[i] = c;
     local += c;
   }
-  // inclusive scan of `local` across the 256 threads
+  // inclusive scan of `local` across the NTH threads
   int v = local;
   const int lane = lane_id();
 #pragma unroll
@@ -232,14 +232,15 @@ __device__ __forceinline__ void store_transposed(const u32x4* r, T* dst, int c0,
 // (K-strided source).
 //   K-major source:   N16 chunks of 16 bytes, chunk i = (row r_i, k-chunk c_i)
 //   K-strided source: NT blocks of 4 K-rows x VEC columns
-template <typename T, bool KMAJ, int ROWS, int BK>
+template <typename T, bool KMAJ, int ROWS, int BK, int NTH>
 struct OperandPlan {
   static constexpr int VEC = 16 / sizeof(T);
-  static constexpr int N16 = ROWS * BK / VEC / 256;
-  static constexpr int NT = BK * ROWS / (4 * VEC) / 256;
+  static constexpr int N16 = ROWS * BK / VEC / NTH;
+  static constexpr int NT = BK * ROWS / (4 * VEC) / NTH;
   static constexpr int NREG = KMAJ ? N16 : 4 * NT;
   static constexpr int NPTR = KMAJ ? N16 : NT;
-  static_assert(NPTR >= 1, "tile too small for 256 threads");
+  static_assert(NPTR >= 1, "tile too small for the workgroup");
+  static_assert(KMAJ ? (N16 * VEC * NTH == ROWS * BK) : (NT * 4 * VEC * NTH == ROWS * BK), "tile/threads");
   const T* ptr[NPTR];
   int lrow[NPTR];  // LDS row (K-major) or first LDS row (K-strided)
   int lk[NPTR];    // LDS k offset
@@ -255,8 +256,9 @@ struct Smem {
 };
 
 template <typename T, typename TC, bool A_KMAJ, bool B_KMAJ, int MODE, int EPI, int BM, int BN,
-          int BK, int WM, int WN>
-__global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g) {
+          int BK, int WM, int WN, int PF>
+__global__ __launch_bounds__(WM * WN * 64) void gemm_kernel(GemmArgs g) {
+  constexpr int NTH = WM * WN * 64;
   using MF = Mfma<T>;
   using TO = typename OutOf<T>::type;
   constexpr bool FP8 = sizeof(T) == 1;
@@ -264,15 +266,15 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g) {
   constexpr int VEC = 16 / sizeof(T);
   constexpr int WTM = BM / WM, WTN = BN / WN;
   constexpr int FM = WTM / 16, FN = WTN / 16;
-  using PA = OperandPlan<T, A_KMAJ, BM, BK>;
-  using PB = OperandPlan<T, B_KMAJ, BN, BK>;
-  static_assert(WM * WN == 4, "four waves");
+  using PA = OperandPlan<T, A_KMAJ, BM, BK, NTH>;
+  using PB = OperandPlan<T, B_KMAJ, BN, BK, NTH>;
+  static_assert(WM * WN == 4 || WM * WN == 8, "four or eight waves");
   static_assert(EPI != EPI_SWIGLU || FN % 2 == 0, "SwiGLU pairs column fragments");
   static_assert(!FP8 || (MODE == G_ROWS && A_KMAJ && BK == 128 && BN <= 128 && BM <= 256),
                 "FP8: row-grouped GEMMs, one 128-deep scale block per K step");
 
   __shared__ __attribute__((aligned(16))) SM sm;
-  __shared__ int s_scan[4];
+  __shared__ int s_scan[8];
   __shared__ int s_info[3];
 
   const int tid = threadIdx.x;
@@ -286,7 +288,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g) {
   int mrows;          // valid rows in the tile (ROWS)
   int kbase, kcount;  // contraction range
   if (MODE == G_ROWS) {
-    find_group<BM>(g.offsets, g.G, g.tiles_n, tile, s_scan, s_info);
+    find_group<BM, NTH>(g.offsets, g.G, g.tiles_n, tile, s_scan, s_info);
     grp = s_info[0];
     if (grp < 0) return;
     const int cnt = s_info[1];
@@ -322,7 +324,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g) {
   if constexpr (A_KMAJ) {
 #pragma unroll
     for (int i = 0; i < PA::NPTR; ++i) {
-      const int q = tid + i * 256;
+      const int q = tid + i * NTH;
       const int r = q / (BK / VEC), kc = q % (BK / VEC);
       pa.lrow[i] = r;
       pa.lk[i] = kc * VEC;
@@ -332,7 +334,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g) {
   } else {
 #pragma unroll
     for (int i = 0; i < PA::NPTR; ++i) {
-      const int q = tid + i * 256;
+      const int q = tid + i * NTH;
       const int kq = q / (BM / VEC), mc = q % (BM / VEC);
       pa.lrow[i] = mc * VEC;
       pa.lk[i] = 4 * kq;
@@ -343,7 +345,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g) {
   if constexpr (B_KMAJ) {
 #pragma unroll
     for (int i = 0; i < PB::NPTR; ++i) {
-      const int q = tid + i * 256;
+      const int q = tid + i * NTH;
       const int r = q / (BK / VEC), kc = q % (BK / VEC);
       int grow = n0 + r;
       if (EPI == EPI_SWIGLU) {
@@ -361,7 +363,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g) {
   } else {
 #pragma unroll
     for (int i = 0; i < PB::NPTR; ++i) {
-      const int q = tid + i * 256;
+      const int q = tid + i * NTH;
       const int kq = q / (BN / VEC), nc = q % (BN / VEC);
       pb.lrow[i] = nc * VEC;
       pb.lk[i] = 4 * kq;
@@ -388,11 +390,13 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g) {
     }
   }
 
+  static_assert(PF == 1 || PF == 2, "prefetch depth");
   const u32x4 zero4 = {0u, 0u, 0u, 0u};
-  u32x4 ra[PA::NREG], rb[PB::NREG];
-  float rs = 0.0f;  // staged FP8 row scale
-  // global -> registers for the K step starting at k0
-#define MOE_GLOAD(k0)                                                                           \
+  // PF register sets of staged operand chunks (and FP8 row scales)
+  u32x4 ra0[PA::NREG], rb0[PB::NREG], ra1[PA::NREG], rb1[PB::NREG];
+  float rs0 = 0.0f, rs1 = 0.0f;
+  // global -> register set (ra, rb, rs) for the K step starting at k0
+#define MOE_GLOAD(k0, ra, rb, rs)                                                               \
   do {                                                                                          \
     if constexpr (A_KMAJ) {                                                                     \
       _Pragma("unroll") for (int i = 0; i < PA::NPTR; ++i) {                                    \
@@ -422,8 +426,8 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g) {
     }                                                                                           \
     if constexpr (FP8) rs = sa_ptr ? sa_ptr[(k0) / 128] : 0.0f;                                 \
   } while (0)
-  // registers -> LDS buffer `buf`
-#define MOE_LSTORE(buf)                                                                         \
+  // register set (ra, rb, rs) -> LDS buffer `buf`
+#define MOE_LSTORE(buf, ra, rb, rs)                                                             \
   do {                                                                                          \
     if constexpr (A_KMAJ) {                                                                     \
       _Pragma("unroll") for (int i = 0; i < PA::NPTR; ++i)                                      \
@@ -450,63 +454,81 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g) {
 #pragma unroll
     for (int j = 0; j < FN; ++j) acc[i][j] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
 
+  // one K step on LDS buffer `buf` (K block s)
+#define MOE_COMPUTE(s, buf)                                                                     \
+  do {                                                                                          \
+    float sb0 = 0.0f, sb1 = 0.0f;                                                               \
+    if constexpr (FP8) {                                                                        \
+      const int kb = (s); /* BK == 128: one scale block per step */                             \
+      if (B_KMAJ) {                                                                             \
+        sb0 = sb_base[int64_t(sb_blk0) * g.b_scale_ld + kb];                                    \
+        sb1 = sb_base[int64_t(sb_blk1) * g.b_scale_ld + kb];                                    \
+      } else {                                                                                  \
+        sb0 = sb1 = sb_base[int64_t(kb) * g.b_scale_ld + sb_blk0];                              \
+      }                                                                                         \
+    }                                                                                           \
+    _Pragma("unroll") for (int kk = 0; kk < BK / MF::MK; ++kk) {                                \
+      const int kofs = kk * MF::MK + (lane / 16) * MF::KP;                                      \
+      typename MF::frag af[FM], bfr[FN];                                                        \
+      _Pragma("unroll") for (int i = 0; i < FM; ++i) {                                          \
+        const int r = wm * WTM + i * 16 + (lane % 16);                                          \
+        af[i] = MF::load(&sm.A[buf][lds_off<T, BK>(r, kofs)], &sm.A[buf][lds_off<T, BK>(r, kofs + 16)]); \
+      }                                                                                         \
+      _Pragma("unroll") for (int j = 0; j < FN; ++j) {                                          \
+        const int r = wn * WTN + j * 16 + (lane % 16);                                          \
+        bfr[j] = MF::load(&sm.B[buf][lds_off<T, BK>(r, kofs)], &sm.B[buf][lds_off<T, BK>(r, kofs + 16)]); \
+      }                                                                                         \
+      if constexpr (FP8) {                                                                      \
+        _Pragma("unroll") for (int i = 0; i < FM; ++i) {                                        \
+          const float4 sa4 =                                                                    \
+              *reinterpret_cast<const float4*>(&sm.SA[buf][wm * WTM + i * 16 + 4 * (lane / 16)]); \
+          const float sa[4] = {sa4.x, sa4.y, sa4.z, sa4.w};                                     \
+          _Pragma("unroll") for (int j = 0; j < FN; ++j) {                                      \
+            const float sbj = (EPI == EPI_SWIGLU && j >= FN / 2) ? sb1 : sb0;                   \
+            const f32x4_t dd = MF::mma(af[i], bfr[j], f32x4_t{0.0f, 0.0f, 0.0f, 0.0f});         \
+            _Pragma("unroll") for (int r = 0; r < 4; ++r)                                       \
+              acc[i][j][r] = __builtin_fmaf(dd[r], sa[r] * sbj, acc[i][j][r]);                  \
+          }                                                                                     \
+        }                                                                                       \
+      } else {                                                                                  \
+        _Pragma("unroll") for (int i = 0; i < FM; ++i)                                          \
+          _Pragma("unroll") for (int j = 0; j < FN; ++j) acc[i][j] = MF::mma(af[i], bfr[j], acc[i][j]); \
+      }                                                                                         \
+    }                                                                                           \
+  } while (0)
+
+  // K loop: LDS double buffer; PF register sets of global loads in flight,
+  // so a load issued at K step s is written to LDS at the end of step
+  // s + PF - 1.
   const int nk = (kcount + BK - 1) / BK;
   if (nk > 0) {
-    MOE_GLOAD(0);
-    MOE_LSTORE(0);
+    MOE_GLOAD(0, ra0, rb0, rs0);
+    if (PF == 2 && nk > 1) MOE_GLOAD(BK, ra1, rb1, rs1);
+    MOE_LSTORE(0, ra0, rb0, rs0);
     __syncthreads();
   }
-  for (int s = 0; s < nk; ++s) {
-    const int buf = s & 1;
-    float sb0 = 0.0f, sb1 = 0.0f;
-    if constexpr (FP8) {
-      const int kb = s;  // BK == 128: one scale block per step
-      if (B_KMAJ) {
-        sb0 = sb_base[int64_t(sb_blk0) * g.b_scale_ld + kb];
-        sb1 = sb_base[int64_t(sb_blk1) * g.b_scale_ld + kb];
-      } else {
-        sb0 = sb1 = sb_base[int64_t(kb) * g.b_scale_ld + sb_blk0];
-      }
+  if constexpr (PF == 1) {
+    for (int s = 0; s < nk; ++s) {
+      const int buf = s & 1;
+      if (s + 1 < nk) MOE_GLOAD((s + 1) * BK, ra0, rb0, rs0);
+      MOE_COMPUTE(s, buf);
+      if (s + 1 < nk) MOE_LSTORE(buf ^ 1, ra0, rb0, rs0);
+      __syncthreads();
     }
-    if (s + 1 < nk) MOE_GLOAD((s + 1) * BK);
-#pragma unroll
-    for (int kk = 0; kk < BK / MF::MK; ++kk) {
-      const int kofs = kk * MF::MK + (lane / 16) * MF::KP;
-      typename MF::frag af[FM], bfr[FN];
-#pragma unroll
-      for (int i = 0; i < FM; ++i) {
-        const int r = wm * WTM + i * 16 + (lane % 16);
-        af[i] = MF::load(&sm.A[buf][lds_off<T, BK>(r, kofs)], &sm.A[buf][lds_off<T, BK>(r, kofs + 16)]);
-      }
-#pragma unroll
-      for (int j = 0; j < FN; ++j) {
-        const int r = wn * WTN + j * 16 + (lane % 16);
-        bfr[j] = MF::load(&sm.B[buf][lds_off<T, BK>(r, kofs)], &sm.B[buf][lds_off<T, BK>(r, kofs + 16)]);
-      }
-      if constexpr (FP8) {
-#pragma unroll
-        for (int i = 0; i < FM; ++i) {
-          const float4 sa4 =
-              *reinterpret_cast<const float4*>(&sm.SA[buf][wm * WTM + i * 16 + 4 * (lane / 16)]);
-          const float sa[4] = {sa4.x, sa4.y, sa4.z, sa4.w};
-#pragma unroll
-          for (int j = 0; j < FN; ++j) {
-            const float sbj = (EPI == EPI_SWIGLU && j >= FN / 2) ? sb1 : sb0;
-            const f32x4_t d = MF::mma(af[i], bfr[j], f32x4_t{0.0f, 0.0f, 0.0f, 0.0f});
-#pragma unroll
-            for (int r = 0; r < 4; ++r) acc[i][j][r] = __builtin_fmaf(d[r], sa[r] * sbj, acc[i][j][r]);
-          }
-        }
-      } else {
-#pragma unroll
-        for (int i = 0; i < FM; ++i)
-#pragma unroll
-          for (int j = 0; j < FN; ++j) acc[i][j] = MF::mma(af[i], bfr[j], acc[i][j]);
-      }
+  } else {
+    for (int s = 0; s < nk; s += 2) {
+      if (s + 2 < nk) MOE_GLOAD((s + 2) * BK, ra0, rb0, rs0);
+      MOE_COMPUTE(s, 0);
+      if (s + 1 < nk) MOE_LSTORE(1, ra1, rb1, rs1);
+      __syncthreads();
+      if (s + 1 >= nk) break;
+      if (s + 3 < nk) MOE_GLOAD((s + 3) * BK, ra1, rb1, rs1);
+      MOE_COMPUTE(s + 1, 1);
+      if (s + 2 < nk) MOE_LSTORE(0, ra0, rb0, rs0);
+      __syncthreads();
     }
-    if (s + 1 < nk) MOE_LSTORE(buf ^ 1);
-    __syncthreads();
   }
+#undef MOE_COMPUTE
 
   // epilogue: lane holds rows 4*(lane/16)+r, column lane%16 of each 16x16
   const int lr = 4 * (lane / 16), lc = lane % 16;
@@ -642,20 +664,36 @@ static void dequant_rows(const uint8_t* q, const float* scale, int64_t rows, int
 }
 
 // ---------------------------------------------------------------------------
-template <typename T> struct Tile;
-template <> struct Tile<bf16_t> { static constexpr int BM = 128, BN = 128, BK = 64; };
-template <> struct Tile<float> { static constexpr int BM = 128, BN = 128, BK = 32; };
-template <> struct Tile<fp8_t> { static constexpr int BM = 128, BN = 128, BK = 128; };
+// Tile configurations: BM x BN output tile, BK deep, WM x WN waves.
+//   Small: 128 x 128, 4 waves of 64 x 64 (every dtype; few rows per expert)
+//   Big:   256 x 256, 8 waves of 128 x 64 (bf16, >= 512 rows per expert):
+//          half the LDS bytes per flop of Small and a quarter of the tiles
+template <typename T, int BM_, int BN_, int BK_, int WM_, int WN_, int PF_>
+struct Cfg {
+  typedef T type;
+  static constexpr int BM = BM_, BN = BN_, BK = BK_, WM = WM_, WN = WN_, PF = PF_;
+};
+template <typename T> struct SmallCfg;
+template <> struct SmallCfg<bf16_t> : Cfg<bf16_t, 128, 128, 64, 2, 2, 1> {};
+template <> struct SmallCfg<float> : Cfg<float, 128, 128, 32, 2, 2, 1> {};
+template <> struct SmallCfg<fp8_t> : Cfg<fp8_t, 128, 128, 128, 2, 2, 1> {};
+typedef Cfg<bf16_t, 256, 256, 64, 2, 4, 1> BigCfg;
 
 static int rows_tile_bound(int64_t A, int64_t G, int BM) {
   return int((A + G * (BM - 1)) / BM);
 }
 
-template <typename T, typename TC, bool AK, bool BKm, int MODE, int EPI>
-static void run_gemm(GemmArgs g, int grid, hipStream_t st) {
-  constexpr int BM = Tile<T>::BM, BN = Tile<T>::BN, BK = Tile<T>::BK;
-  if (grid <= 0) return;
-  gemm_kernel<T, TC, AK, BKm, MODE, EPI, BM, BN, BK, 2, 2><<<padded_grid(grid), 256, 0, st>>>(g);
+template <typename C, typename TC, bool AK, bool BKm, int MODE, int EPI>
+static void run_gemm(GemmArgs g, int tiles, hipStream_t st) {
+  if (tiles <= 0) return;
+  gemm_kernel<typename C::type, TC, AK, BKm, MODE, EPI, C::BM, C::BN, C::BK, C::WM, C::WN, C::PF>
+      <<<padded_grid(tiles), C::WM * C::WN * 64, 0, st>>>(g);
+}
+
+// The big tile pays off when experts hold many rows (it halves LDS traffic
+// per flop); with few rows per expert most of its rows would be padding.
+static bool use_big(int64_t A, int64_t E, int64_t n_dim, int64_t m_dim = 256) {
+  return A >= 512 * E && n_dim % 256 == 0 && m_dim % 256 == 0;
 }
 
 template <typename T>
@@ -719,10 +757,10 @@ size_t ffn_ws_bytes(int64_t A, int64_t d, int64_t f, int act_bytes, bool fp8, bo
   return ffn_ws(A, d, f, act_bytes, fp8, bwd).total;
 }
 
-template <typename T>
+template <typename C>
 static void ffn_fwd_t(const FfnLaunch& a, hipStream_t st) {
-  constexpr int BM = Tile<T>::BM, BN = Tile<T>::BN;
-  const int mt_bound = rows_tile_bound(a.A, a.E, BM);
+  typedef typename C::type T;
+  const int mt_bound = rows_tile_bound(a.A, a.E, C::BM);
   // GEMM1 + SwiGLU
   GemmArgs g1{};
   g1.A = a.x_perm; g1.lda = a.d;
@@ -730,8 +768,8 @@ static void ffn_fwd_t(const FfnLaunch& a, hipStream_t st) {
   g1.offsets = a.offsets; g1.G = int(a.E);
   g1.N = int(2 * a.f); g1.K = int(a.d); g1.f = int(a.f);
   g1.aux0 = a.act_gu; g1.aux1 = a.act_h;
-  g1.tiles_n = int(2 * a.f / BN);
-  run_gemm<T, T, true, true, G_ROWS, EPI_SWIGLU>(g1, mt_bound * g1.tiles_n, st);
+  g1.tiles_n = int(2 * a.f / C::BN);
+  run_gemm<C, T, true, true, G_ROWS, EPI_SWIGLU>(g1, mt_bound * g1.tiles_n, st);
   // GEMM2
   GemmArgs g2{};
   g2.A = a.act_h; g2.lda = a.f;
@@ -739,12 +777,13 @@ static void ffn_fwd_t(const FfnLaunch& a, hipStream_t st) {
   g2.C = a.out_perm; g2.ldc = a.d;
   g2.offsets = a.offsets; g2.G = int(a.E);
   g2.N = int(a.d); g2.K = int(a.f);
-  g2.tiles_n = int(a.d / BN);
-  run_gemm<T, T, true, true, G_ROWS, EPI_STORE>(g2, mt_bound * g2.tiles_n, st);
+  g2.tiles_n = int(a.d / C::BN);
+  run_gemm<C, T, true, true, G_ROWS, EPI_STORE>(g2, mt_bound * g2.tiles_n, st);
 }
 
 static void ffn_fwd_fp8(const FfnLaunch& a, hipStream_t st) {
-  constexpr int BM = Tile<fp8_t>::BM, BN = Tile<fp8_t>::BN;
+  typedef SmallCfg<fp8_t> C;
+  constexpr int BM = C::BM, BN = C::BN;
   const FfnWs w = ffn_ws(a.A, a.d, a.f, 2, true, false);
   bf16_t* h16 = reinterpret_cast<bf16_t*>(static_cast<char*>(a.ws) + w.h_bf16);
   const int mt_bound = rows_tile_bound(a.A, a.E, BM);
@@ -757,7 +796,7 @@ static void ffn_fwd_fp8(const FfnLaunch& a, hipStream_t st) {
   g1.N = int(2 * a.f); g1.K = int(a.d); g1.f = int(a.f);
   g1.aux0 = a.act_gu; g1.aux1 = h16;
   g1.tiles_n = int(2 * a.f / BN);
-  run_gemm<fp8_t, bf16_t, true, true, G_ROWS, EPI_SWIGLU>(g1, mt_bound * g1.tiles_n, st);
+  run_gemm<C, bf16_t, true, true, G_ROWS, EPI_SWIGLU>(g1, mt_bound * g1.tiles_n, st);
   // H -> E4M3 per 1 x 128 block (the second GEMM's A operand, saved for bwd)
   launch_quant_rows(h16, true, a.A, a.f, reinterpret_cast<uint8_t*>(a.act_h), a.h_scale, st);
   GemmArgs g2{};
@@ -769,14 +808,13 @@ static void ffn_fwd_fp8(const FfnLaunch& a, hipStream_t st) {
   g2.offsets = a.offsets; g2.G = int(a.E);
   g2.N = int(a.d); g2.K = int(a.f);
   g2.tiles_n = int(a.d / BN);
-  run_gemm<fp8_t, bf16_t, true, true, G_ROWS, EPI_STORE>(g2, mt_bound * g2.tiles_n, st);
+  run_gemm<C, bf16_t, true, true, G_ROWS, EPI_STORE>(g2, mt_bound * g2.tiles_n, st);
 }
 
 // Weight gradients over the ragged rows of every expert (K split by group).
-template <typename T, typename TW>
+template <typename C, typename TW>
 static void wgrad_t(const void* d_out, const void* act_h, const void* d_gu, const void* x, void* dw1,
                     void* dw2, const int32_t* offsets, int64_t d, int64_t f, int64_t E, hipStream_t st) {
-  constexpr int BM = Tile<T>::BM, BN = Tile<T>::BN;
   // dW2 = dO^T H   [d, f]
   GemmArgs g3{};
   g3.A = d_out; g3.lda = d;
@@ -784,8 +822,8 @@ static void wgrad_t(const void* d_out, const void* act_h, const void* d_gu, cons
   g3.C = dw2; g3.ldc = f; g3.c_gstride = d * f;
   g3.offsets = offsets; g3.G = int(E);
   g3.M = int(d); g3.N = int(f);
-  g3.tiles_m = int(d / BM); g3.tiles_n = int(f / BN);
-  run_gemm<T, TW, false, false, G_KSPLIT, EPI_STORE>(g3, int(E) * g3.tiles_m * g3.tiles_n, st);
+  g3.tiles_m = int(d / C::BM); g3.tiles_n = int(f / C::BN);
+  run_gemm<C, TW, false, false, G_KSPLIT, EPI_STORE>(g3, int(E) * g3.tiles_m * g3.tiles_n, st);
   // dW1 = dGU^T X   [2f, d]
   GemmArgs g4{};
   g4.A = d_gu; g4.lda = 2 * f;
@@ -793,16 +831,24 @@ static void wgrad_t(const void* d_out, const void* act_h, const void* d_gu, cons
   g4.C = dw1; g4.ldc = d; g4.c_gstride = 2 * f * d;
   g4.offsets = offsets; g4.G = int(E);
   g4.M = int(2 * f); g4.N = int(d);
-  g4.tiles_m = int(2 * f / BM); g4.tiles_n = int(d / BN);
-  run_gemm<T, TW, false, false, G_KSPLIT, EPI_STORE>(g4, int(E) * g4.tiles_m * g4.tiles_n, st);
+  g4.tiles_m = int(2 * f / C::BM); g4.tiles_n = int(d / C::BN);
+  run_gemm<C, TW, false, false, G_KSPLIT, EPI_STORE>(g4, int(E) * g4.tiles_m * g4.tiles_n, st);
 }
 
-template <typename T>
-static void ffn_bwd_t(const FfnBwdLaunch& a, hipStream_t st) {
-  constexpr int BM = Tile<T>::BM, BN = Tile<T>::BN;
-  const FfnWs w = ffn_ws(a.A, a.d, a.f, int(sizeof(T)), false, true);
-  void* d_gu = static_cast<char*>(a.ws) + w.d_gu;
-  const int mt_bound = rows_tile_bound(a.A, a.E, BM);
+template <typename TC16>
+static void wgrad_any(const void* d_out, const void* act_h, const void* d_gu, const void* x, void* dw1,
+                      void* dw2, const int32_t* offsets, int64_t A, int64_t d, int64_t f, int64_t E,
+                      hipStream_t st) {
+  if (use_big(A, E, d, f) && use_big(A, E, f, d) && (2 * f) % 256 == 0)
+    wgrad_t<BigCfg, TC16>(d_out, act_h, d_gu, x, dw1, dw2, offsets, d, f, E, st);
+  else
+    wgrad_t<SmallCfg<bf16_t>, TC16>(d_out, act_h, d_gu, x, dw1, dw2, offsets, d, f, E, st);
+}
+
+template <typename C>
+static void dgrad_t(const FfnBwdLaunch& a, void* d_gu, hipStream_t st) {
+  typedef typename C::type T;
+  const int mt_bound = rows_tile_bound(a.A, a.E, C::BM);
   // dH = dO W2, fused SwiGLU backward -> dGU
   GemmArgs g1{};
   g1.A = a.d_out; g1.lda = a.d;
@@ -811,8 +857,8 @@ static void ffn_bwd_t(const FfnBwdLaunch& a, hipStream_t st) {
   g1.offsets = a.offsets; g1.G = int(a.E);
   g1.N = int(a.f); g1.K = int(a.d); g1.f = int(a.f);
   g1.aux0 = const_cast<void*>(a.act_gu);
-  g1.tiles_n = int(a.f / BN);
-  run_gemm<T, T, true, false, G_ROWS, EPI_DSWIGLU>(g1, mt_bound * g1.tiles_n, st);
+  g1.tiles_n = int(a.f / C::BN);
+  run_gemm<C, T, true, false, G_ROWS, EPI_DSWIGLU>(g1, mt_bound * g1.tiles_n, st);
   // dX = dGU W1
   GemmArgs g2{};
   g2.A = d_gu; g2.lda = 2 * a.f;
@@ -820,9 +866,23 @@ static void ffn_bwd_t(const FfnBwdLaunch& a, hipStream_t st) {
   g2.C = a.dx_perm; g2.ldc = a.d;
   g2.offsets = a.offsets; g2.G = int(a.E);
   g2.N = int(a.d); g2.K = int(2 * a.f);
-  g2.tiles_n = int(a.d / BN);
-  run_gemm<T, T, true, false, G_ROWS, EPI_STORE>(g2, mt_bound * g2.tiles_n, st);
-  wgrad_t<T, T>(a.d_out, a.act_h, d_gu, a.x_perm, a.dw1, a.dw2, a.offsets, a.d, a.f, a.E, st);
+  g2.tiles_n = int(a.d / C::BN);
+  run_gemm<C, T, true, false, G_ROWS, EPI_STORE>(g2, mt_bound * g2.tiles_n, st);
+}
+
+template <typename T>
+static void ffn_bwd_t(const FfnBwdLaunch& a, hipStream_t st) {
+  const FfnWs w = ffn_ws(a.A, a.d, a.f, int(sizeof(T)), false, true);
+  void* d_gu = static_cast<char*>(a.ws) + w.d_gu;
+  if constexpr (sizeof(T) == 2) {
+    if (use_big(a.A, a.E, a.f) && use_big(a.A, a.E, a.d)) dgrad_t<BigCfg>(a, d_gu, st);
+    else dgrad_t<SmallCfg<bf16_t>>(a, d_gu, st);
+    wgrad_any<bf16_t>(a.d_out, a.act_h, d_gu, a.x_perm, a.dw1, a.dw2, a.offsets, a.A, a.d, a.f, a.E, st);
+  } else {
+    dgrad_t<SmallCfg<float>>(a, d_gu, st);
+    wgrad_t<SmallCfg<float>, float>(a.d_out, a.act_h, d_gu, a.x_perm, a.dw1, a.dw2, a.offsets, a.d, a.f,
+                                     a.E, st);
+  }
 }
 
 // FP8 backward: the data-gradient GEMMs run in FP8 with their gradient
@@ -830,7 +890,8 @@ static void ffn_bwd_t(const FfnBwdLaunch& a, hipStream_t st) {
 // forward's 128 x 128 weight blocks; the weight gradients run in bf16 on the
 // dequantised forward operands (X, H) and the bf16 gradients.
 static void ffn_bwd_fp8(const FfnBwdLaunch& a, hipStream_t st) {
-  constexpr int BM = Tile<fp8_t>::BM, BN = Tile<fp8_t>::BN;
+  typedef SmallCfg<fp8_t> C;
+  constexpr int BM = C::BM, BN = C::BN;
   const FfnWs w = ffn_ws(a.A, a.d, a.f, 2, true, true);
   char* ws = static_cast<char*>(a.ws);
   bf16_t* d_gu = reinterpret_cast<bf16_t*>(ws + w.d_gu);
@@ -853,7 +914,7 @@ static void ffn_bwd_fp8(const FfnBwdLaunch& a, hipStream_t st) {
   g1.N = int(a.f); g1.K = int(a.d); g1.f = int(a.f);
   g1.aux0 = const_cast<void*>(a.act_gu);
   g1.tiles_n = int(a.f / BN);
-  run_gemm<fp8_t, bf16_t, true, false, G_ROWS, EPI_DSWIGLU>(g1, mt_bound * g1.tiles_n, st);
+  run_gemm<C, bf16_t, true, false, G_ROWS, EPI_DSWIGLU>(g1, mt_bound * g1.tiles_n, st);
   // dX = Q(dGU) W1
   launch_quant_rows(d_gu, true, a.A, 2 * a.f, gq, gs, st);
   GemmArgs g2{};
@@ -865,11 +926,11 @@ static void ffn_bwd_fp8(const FfnBwdLaunch& a, hipStream_t st) {
   g2.offsets = a.offsets; g2.G = int(a.E);
   g2.N = int(a.d); g2.K = int(2 * a.f);
   g2.tiles_n = int(a.d / BN);
-  run_gemm<fp8_t, bf16_t, true, false, G_ROWS, EPI_STORE>(g2, mt_bound * g2.tiles_n, st);
+  run_gemm<C, bf16_t, true, false, G_ROWS, EPI_STORE>(g2, mt_bound * g2.tiles_n, st);
   // weight gradients in bf16 on dequantised X and H
   dequant_rows(reinterpret_cast<const uint8_t*>(a.x_perm), a.x_scale, a.A, a.d, xd, st);
   dequant_rows(reinterpret_cast<const uint8_t*>(a.act_h), a.h_scale, a.A, a.f, hd, st);
-  wgrad_t<bf16_t, bf16_t>(a.d_out, hd, d_gu, xd, a.dw1, a.dw2, a.offsets, a.d, a.f, a.E, st);
+  wgrad_any<bf16_t>(a.d_out, hd, d_gu, xd, a.dw1, a.dw2, a.offsets, a.A, a.d, a.f, a.E, st);
 }
 
 void launch_grouped_ffn(const FfnLaunch& a, hipStream_t st) {
@@ -878,8 +939,12 @@ void launch_grouped_ffn(const FfnLaunch& a, hipStream_t st) {
     return;
   }
   if (a.wt == 2) ffn_fwd_fp8(a, st);
-  else if (a.wt == 1) ffn_fwd_t<bf16_t>(a, st);
-  else ffn_fwd_t<float>(a, st);
+  else if (a.wt == 1) {
+    if (use_big(a.A, a.E, 2 * a.f) && use_big(a.A, a.E, a.d)) ffn_fwd_t<BigCfg>(a, st);
+    else ffn_fwd_t<SmallCfg<bf16_t>>(a, st);
+  } else {
+    ffn_fwd_t<SmallCfg<float>>(a, st);
+  }
 }
 
 void launch_grouped_ffn_bwd(const FfnBwdLaunch& a, hipStream_t st) {

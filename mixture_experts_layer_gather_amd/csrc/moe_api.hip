@@ -298,6 +298,12 @@ int moe_quantize_fp8_blockwise(const void* src, int src_dtype, int64_t rows, int
   if (rows == 0 || cols == 0) return MOE_OK;
   MOE_CHECK(need(src)); MOE_CHECK(need(dst)); MOE_CHECK(need(scale));
   if ((rows + block_r - 1) / block_r > 65535) return MOE_ERR_INVALID_ARG;
+  if (block_r == 1 && block_c == 128 && cols % 128 == 0 && aligned16(src) && aligned16(dst)) {
+    // activation rows: 16 lanes per block, same definition as below
+    moe::launch_quant_rows(src, src_dtype == MOE_DTYPE_BF16, rows, cols, dst, scale,
+                           static_cast<hipStream_t>(stream));
+    return launched();
+  }
   moe::QuantLaunch q{};
   q.src = src; q.src_bf16 = src_dtype == MOE_DTYPE_BF16; q.rows = rows; q.cols = cols;
   q.br = block_r; q.bc = block_c; q.dst = dst; q.scale = scale;

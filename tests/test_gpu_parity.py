@@ -115,6 +115,8 @@ def _compare_small(cfg, identity=False, inp=None):
 SMALL = {
     "tiny_fp32": S.CONFIGS[0],
     "mixtral_mini": S.mini(S.CONFIGS[1], T=1000, d=256, f=384),
+    # >= 512 rows per expert and 256-multiple widths: the 256 x 256 tile path
+    "mixtral_mini_bigtile": S.mini(S.CONFIGS[1], T=2304, d=512, f=512, seed_base=33),
     "mixtral_mini_f32": S.mini(S.CONFIGS[1], T=333, d=128, f=256).replace(act="f32", weight="f32"),
     "deepseek_mini": S.mini(S.CONFIGS[2], T=300, d=256, f=256, E=32).replace(k=6),
     "qwen_skew_mini": S.mini(S.CONFIGS[3], T=700, d=256, f=128, E=16).replace(k=4),
