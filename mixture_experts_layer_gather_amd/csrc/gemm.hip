@@ -757,10 +757,10 @@ size_t ffn_ws_bytes(int64_t A, int64_t d, int64_t f, int act_bytes, bool fp8, bo
   return ffn_ws(A, d, f, act_bytes, fp8, bwd).total;
 }
 
-template <typename C>
+// GEMM1 (+ SwiGLU) with config C1, GEMM2 with C2.
+template <typename C1, typename C2>
 static void ffn_fwd_t(const FfnLaunch& a, hipStream_t st) {
-  typedef typename C::type T;
-  const int mt_bound = rows_tile_bound(a.A, a.E, C::BM);
+  typedef typename C1::type T;
   // GEMM1 + SwiGLU
   GemmArgs g1{};
   g1.A = a.x_perm; g1.lda = a.d;
@@ -768,8 +768,8 @@ static void ffn_fwd_t(const FfnLaunch& a, hipStream_t st) {
   g1.offsets = a.offsets; g1.G = int(a.E);
   g1.N = int(2 * a.f); g1.K = int(a.d); g1.f = int(a.f);
   g1.aux0 = a.act_gu; g1.aux1 = a.act_h;
-  g1.tiles_n = int(2 * a.f / C::BN);
-  run_gemm<C, T, true, true, G_ROWS, EPI_SWIGLU>(g1, mt_bound * g1.tiles_n, st);
+  g1.tiles_n = int(2 * a.f / C1::BN);
+  run_gemm<C1, T, true, true, G_ROWS, EPI_SWIGLU>(g1, rows_tile_bound(a.A, a.E, C1::BM) * g1.tiles_n, st);
   // GEMM2
   GemmArgs g2{};
   g2.A = a.act_h; g2.lda = a.f;
@@ -777,8 +777,8 @@ static void ffn_fwd_t(const FfnLaunch& a, hipStream_t st) {
   g2.C = a.out_perm; g2.ldc = a.d;
   g2.offsets = a.offsets; g2.G = int(a.E);
   g2.N = int(a.d); g2.K = int(a.f);
-  g2.tiles_n = int(a.d / C::BN);
-  run_gemm<C, T, true, true, G_ROWS, EPI_STORE>(g2, mt_bound * g2.tiles_n, st);
+  g2.tiles_n = int(a.d / C2::BN);
+  run_gemm<C2, T, true, true, G_ROWS, EPI_STORE>(g2, rows_tile_bound(a.A, a.E, C2::BM) * g2.tiles_n, st);
 }
 
 static void ffn_fwd_fp8(const FfnLaunch& a, hipStream_t st) {
@@ -845,10 +845,10 @@ static void wgrad_any(const void* d_out, const void* act_h, const void* d_gu, co
     wgrad_t<SmallCfg<bf16_t>, TC16>(d_out, act_h, d_gu, x, dw1, dw2, offsets, d, f, E, st);
 }
 
-template <typename C>
+// dH = dO W2 (+ SwiGLU backward) with config C1, dX = dGU W1 with C2.
+template <typename C1, typename C2>
 static void dgrad_t(const FfnBwdLaunch& a, void* d_gu, hipStream_t st) {
-  typedef typename C::type T;
-  const int mt_bound = rows_tile_bound(a.A, a.E, C::BM);
+  typedef typename C1::type T;
   // dH = dO W2, fused SwiGLU backward -> dGU
   GemmArgs g1{};
   g1.A = a.d_out; g1.lda = a.d;
@@ -857,8 +857,8 @@ static void dgrad_t(const FfnBwdLaunch& a, void* d_gu, hipStream_t st) {
   g1.offsets = a.offsets; g1.G = int(a.E);
   g1.N = int(a.f); g1.K = int(a.d); g1.f = int(a.f);
   g1.aux0 = const_cast<void*>(a.act_gu);
-  g1.tiles_n = int(a.f / C::BN);
-  run_gemm<C, T, true, false, G_ROWS, EPI_DSWIGLU>(g1, mt_bound * g1.tiles_n, st);
+  g1.tiles_n = int(a.f / C1::BN);
+  run_gemm<C1, T, true, false, G_ROWS, EPI_DSWIGLU>(g1, rows_tile_bound(a.A, a.E, C1::BM) * g1.tiles_n, st);
   // dX = dGU W1
   GemmArgs g2{};
   g2.A = d_gu; g2.lda = 2 * a.f;
@@ -866,8 +866,8 @@ static void dgrad_t(const FfnBwdLaunch& a, void* d_gu, hipStream_t st) {
   g2.C = a.dx_perm; g2.ldc = a.d;
   g2.offsets = a.offsets; g2.G = int(a.E);
   g2.N = int(a.d); g2.K = int(2 * a.f);
-  g2.tiles_n = int(a.d / C::BN);
-  run_gemm<C, T, true, false, G_ROWS, EPI_STORE>(g2, mt_bound * g2.tiles_n, st);
+  g2.tiles_n = int(a.d / C2::BN);
+  run_gemm<C2, T, true, false, G_ROWS, EPI_STORE>(g2, rows_tile_bound(a.A, a.E, C2::BM) * g2.tiles_n, st);
 }
 
 template <typename T>
@@ -875,11 +875,13 @@ static void ffn_bwd_t(const FfnBwdLaunch& a, hipStream_t st) {
   const FfnWs w = ffn_ws(a.A, a.d, a.f, int(sizeof(T)), false, true);
   void* d_gu = static_cast<char*>(a.ws) + w.d_gu;
   if constexpr (sizeof(T) == 2) {
-    if (use_big(a.A, a.E, a.f) && use_big(a.A, a.E, a.d)) dgrad_t<BigCfg>(a, d_gu, st);
-    else dgrad_t<SmallCfg<bf16_t>>(a, d_gu, st);
+    // measured on the Mixtral-style layer: the big tile wins for dH, the
+    // small one for dX (its B operand is transposed on the way into LDS)
+    if (use_big(a.A, a.E, a.f)) dgrad_t<BigCfg, SmallCfg<bf16_t>>(a, d_gu, st);
+    else dgrad_t<SmallCfg<bf16_t>, SmallCfg<bf16_t>>(a, d_gu, st);
     wgrad_any<bf16_t>(a.d_out, a.act_h, d_gu, a.x_perm, a.dw1, a.dw2, a.offsets, a.A, a.d, a.f, a.E, st);
   } else {
-    dgrad_t<SmallCfg<float>>(a, d_gu, st);
+    dgrad_t<SmallCfg<float>, SmallCfg<float>>(a, d_gu, st);
     wgrad_t<SmallCfg<float>, float>(a.d_out, a.act_h, d_gu, a.x_perm, a.dw1, a.dw2, a.offsets, a.d, a.f,
                                      a.E, st);
   }
@@ -940,10 +942,11 @@ void launch_grouped_ffn(const FfnLaunch& a, hipStream_t st) {
   }
   if (a.wt == 2) ffn_fwd_fp8(a, st);
   else if (a.wt == 1) {
-    if (use_big(a.A, a.E, 2 * a.f) && use_big(a.A, a.E, a.d)) ffn_fwd_t<BigCfg>(a, st);
-    else ffn_fwd_t<SmallCfg<bf16_t>>(a, st);
+    // measured: the big tile wins for GEMM1 (N = 2f), the small one for GEMM2
+    if (use_big(a.A, a.E, 2 * a.f)) ffn_fwd_t<BigCfg, SmallCfg<bf16_t>>(a, st);
+    else ffn_fwd_t<SmallCfg<bf16_t>, SmallCfg<bf16_t>>(a, st);
   } else {
-    ffn_fwd_t<SmallCfg<float>>(a, st);
+    ffn_fwd_t<SmallCfg<float>, SmallCfg<float>>(a, st);
   }
 }
 
