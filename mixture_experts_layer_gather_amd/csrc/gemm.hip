@@ -30,12 +30,26 @@
 // their way into LDS. Workgroup ids are remapped so that each XCD (8 per
 // chip, one L2 each) works through a contiguous range of tiles that share
 // weights and rows.
+#include <type_traits>
+
 #include "common.hpp"
 #include "launch.hpp"
 
 namespace moe {
 
 enum { G_ROWS = 0, G_KSPLIT = 1 };
+
+// Compile-time loop: f(std::integral_constant<int, I>) for I = 0 .. N-1.
+template <int I, int N> struct StaticFor {
+  template <typename F> __device__ __forceinline__ static void run(F& f) {
+    f(std::integral_constant<int, I>{});
+    StaticFor<I + 1, N>::run(f);
+  }
+};
+template <int N> struct StaticFor<N, N> {
+  template <typename F> __device__ __forceinline__ static void run(F&) {}
+};
+template <int N, typename F> __device__ __forceinline__ void static_for(F&& f) { StaticFor<0, N>::run(f); }
 enum { EPI_STORE = 0, EPI_SWIGLU = 1, EPI_DSWIGLU = 2 };
 
 typedef uint8_t fp8_t;  // OCP E4M3FN code
@@ -45,6 +59,9 @@ template <> struct Mfma<bf16_t> {
   static constexpr int KP = 8;   // elements per lane per instruction
   static constexpr int MK = 32;  // K per instruction
   typedef bf16x8_t frag;
+  // K offset (within the LDS tile) of lane's fragment for sub-step kk
+  static __device__ __forceinline__ int kofs(int lane, int kk) { return kk * MK + (lane / 16) * KP; }
+  static constexpr int K2 = 0;   // offset of the second 16-byte chunk (unused)
   static __device__ __forceinline__ frag load(const bf16_t* p0, const bf16_t*) {
     return __builtin_bit_cast(frag, *reinterpret_cast<const u32x4*>(p0));
   }
@@ -56,6 +73,8 @@ template <> struct Mfma<float> {
   static constexpr int KP = 1;
   static constexpr int MK = 4;
   typedef float frag;
+  static __device__ __forceinline__ int kofs(int lane, int kk) { return kk * MK + lane / 16; }
+  static constexpr int K2 = 0;
   static __device__ __forceinline__ frag load(const float* p0, const float*) { return *p0; }
   static __device__ __forceinline__ f32x4_t mma(frag a, frag b, f32x4_t c) {
     return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
@@ -65,6 +84,12 @@ template <> struct Mfma<fp8_t> {
   static constexpr int KP = 32;
   static constexpr int MK = 128;
   typedef i32x8_t frag;
+  // The 32 K-values a lane feeds are chunks q and q + 4 (q = lane / 16) of the
+  // 128-deep block, not 2q and 2q + 1: A and B use the same order, so every
+  // product is still formed, and the LDS reads then follow the conflict-free
+  // pattern of the bf16 fragments (16 rows x 4 consecutive chunks).
+  static __device__ __forceinline__ int kofs(int lane, int) { return (lane / 16) * 16; }
+  static constexpr int K2 = 64;
   // 32 bytes from two (separately swizzled) 16-byte chunks
   static __device__ __forceinline__ frag load(const fp8_t* p0, const fp8_t* p1) {
     const u32x4 lo = *reinterpret_cast<const u32x4*>(p0);
@@ -174,16 +199,25 @@ __device__ void find_group(const int32_t* __restrict__ offsets, int G, int tiles
   __syncthreads();
 }
 
-// LDS tiles hold ROWS x BK elements per operand, K-contiguous, without
-// padding. The 16-byte chunks of each row are XOR-swizzled with the row so
-// that both the MFMA fragment reads (16 consecutive rows, one chunk each) and
-// the transposed stores (rows VEC apart) spread over all banks.
-template <typename T, int BK>
+// LDS tiles hold ROWS x BK elements per operand (rows of 128 bytes),
+// K-contiguous, without padding; the eight 16-byte chunks of a row are
+// XOR-swizzled with the row. Measured with the LDS bank-conflict counters on
+// gfx950: the MFMA fragment reads (16 consecutive rows x 4 chunks per
+// instruction) are conflict-free when the swizzle takes row bits 0-2 (and
+// not row bit 3); 16-byte row stores are conflict-free for any swizzle; the
+// transposed 8-byte stores of K-strided operands need rows 8 and 16 apart
+// to differ, which row bits 4-6 provide. So K-major operands (filled by DMA)
+// use row bits 0-2 only, which keeps a fragment's address an immediate
+// offset from the first fragment's, and K-strided operands add row bits 4-6.
+template <bool KMAJ>
+__device__ __forceinline__ int lds_swz(int row) {
+  return KMAJ ? (row & 7) : ((row ^ (row >> 4)) & 7);
+}
+template <typename T, int BK, bool KMAJ>
 __device__ __forceinline__ int lds_off(int row, int k) {
   constexpr int VEC = 16 / sizeof(T);
-  constexpr int NCH = BK / VEC;
-  const int sw = (row ^ (row >> 3)) & (NCH - 1);
-  return row * BK + (((k / VEC) ^ sw) * VEC) + (k % VEC);
+  static_assert(BK / VEC == 8, "128-byte LDS rows");
+  return row * BK + (((k / VEC) ^ lds_swz<KMAJ>(row)) * VEC) + (k % VEC);
 }
 
 // 4 K-rows x VEC columns (four 16-byte registers) -> VEC LDS rows of 4
@@ -204,95 +238,137 @@ __device__ __forceinline__ void store_transposed(const u32x4* r, T* dst, int c0,
       const uint32_t c1v = __builtin_amdgcn_perm(a23, a01, 0x07060302u);
       const uint32_t c2v = __builtin_amdgcn_perm(b23, b01, 0x05040100u);
       const uint32_t c3v = __builtin_amdgcn_perm(b23, b01, 0x07060302u);
-      *reinterpret_cast<uint32_t*>(dst + lds_off<T, BK>(c0 + 4 * p + 0, k4)) = c0v;
-      *reinterpret_cast<uint32_t*>(dst + lds_off<T, BK>(c0 + 4 * p + 1, k4)) = c1v;
-      *reinterpret_cast<uint32_t*>(dst + lds_off<T, BK>(c0 + 4 * p + 2, k4)) = c2v;
-      *reinterpret_cast<uint32_t*>(dst + lds_off<T, BK>(c0 + 4 * p + 3, k4)) = c3v;
+      *reinterpret_cast<uint32_t*>(dst + lds_off<T, BK, false>(c0 + 4 * p + 0, k4)) = c0v;
+      *reinterpret_cast<uint32_t*>(dst + lds_off<T, BK, false>(c0 + 4 * p + 1, k4)) = c1v;
+      *reinterpret_cast<uint32_t*>(dst + lds_off<T, BK, false>(c0 + 4 * p + 2, k4)) = c2v;
+      *reinterpret_cast<uint32_t*>(dst + lds_off<T, BK, false>(c0 + 4 * p + 3, k4)) = c3v;
     }
   } else if constexpr (sizeof(T) == 2) {
 #pragma unroll
     for (int p = 0; p < 4; ++p) {
       const u32x2 ev = {(w[0][p] & 0xffffu) | (w[1][p] << 16), (w[2][p] & 0xffffu) | (w[3][p] << 16)};
       const u32x2 od = {(w[0][p] >> 16) | (w[1][p] & 0xffff0000u), (w[2][p] >> 16) | (w[3][p] & 0xffff0000u)};
-      *reinterpret_cast<u32x2*>(dst + lds_off<T, BK>(c0 + 2 * p, k4)) = ev;
-      *reinterpret_cast<u32x2*>(dst + lds_off<T, BK>(c0 + 2 * p + 1, k4)) = od;
+      *reinterpret_cast<u32x2*>(dst + lds_off<T, BK, false>(c0 + 2 * p, k4)) = ev;
+      *reinterpret_cast<u32x2*>(dst + lds_off<T, BK, false>(c0 + 2 * p + 1, k4)) = od;
     }
   } else {
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
       const u32x4 v = {w[0][c], w[1][c], w[2][c], w[3][c]};
-      *reinterpret_cast<u32x4*>(dst + lds_off<T, BK>(c0 + c, k4)) = v;
+      *reinterpret_cast<u32x4*>(dst + lds_off<T, BK, false>(c0 + c, k4)) = v;
     }
   }
 }
 
-// Per-thread plan for moving one operand tile (ROWS x BK, stored K-major in
-// LDS) from global memory: the thread's source pointers are fixed for the
-// whole K loop and advance by k0 elements (K-major source) or k0 rows
-// (K-strided source).
-//   K-major source:   N16 chunks of 16 bytes, chunk i = (row r_i, k-chunk c_i)
-//   K-strided source: NT blocks of 4 K-rows x VEC columns
-template <typename T, bool KMAJ, int ROWS, int BK, int NTH>
+// Raw buffer descriptors (gfx9 family: stride 0, 32-bit untyped data). A
+// load whose byte offset lies at or past `bytes` returns zeros, which masks
+// rows past the end of a group without branches.
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, int64_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0,
+                                           int(uint32_t(bytes > 0 ? bytes : 0)), 0x00020000);
+}
+// One wave instruction of DMA: every lane's 16 bytes at byte offset voff of
+// the buffer go to LDS at dst + 16 * lane (dst is wave-uniform).
+__device__ __forceinline__ void dma16(rsrc_t r, void* dst, uint32_t voff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)dst, 16, voff, 0, 0, 0);
+}
+
+// Operand tiles in LDS, by layout mode:
+//   LM_KDMA  K-major source, DMA straight from global memory into ROWS rows of
+//            BK elements (128 bytes). One wave instruction fills 1 KB of LDS
+//            = 8 rows, lane l the 16 bytes at l * 16; the lane fetches the
+//            logical chunk that the swizzle puts there.
+//   LM_TDMA  K-strided bf16 source, DMA into BK K-rows of ROWS elements (the
+//            source's own orientation); 16-byte chunks are XOR-swizzled with
+//            2 * (K-row & 3). MFMA fragments are read with the LDS transpose
+//            read (ds_read_b64_tr_b16), which hands each lane of a 16-lane
+//            group one column of 4 consecutive K-rows.
+//   LM_REG   other K-strided sources (fp32, FP8): NT blocks of 4 K-rows x VEC
+//            columns per thread, loaded into registers and transposed on
+//            their way into LDS (K-major rows, swizzled as in lds_off).
+enum { LM_KDMA = 0, LM_TDMA = 1, LM_REG = 2 };
+template <typename T, bool KMAJ>
+constexpr int layout_mode() {
+  return KMAJ ? LM_KDMA : (sizeof(T) == 2 ? LM_TDMA : LM_REG);
+}
+
+template <typename T, int LM, int ROWS, int BK, int NTH>
 struct OperandPlan {
   static constexpr int VEC = 16 / sizeof(T);
-  static constexpr int N16 = ROWS * BK / VEC / NTH;
-  static constexpr int NT = BK * ROWS / (4 * VEC) / NTH;
-  static constexpr int NREG = KMAJ ? N16 : 4 * NT;
-  static constexpr int NPTR = KMAJ ? N16 : NT;
-  static_assert(NPTR >= 1, "tile too small for the workgroup");
-  static_assert(KMAJ ? (N16 * VEC * NTH == ROWS * BK) : (NT * 4 * VEC * NTH == ROWS * BK), "tile/threads");
-  const T* ptr[NPTR];
-  int lrow[NPTR];  // LDS row (K-major) or first LDS row (K-strided)
-  int lk[NPTR];    // LDS k offset
-  int kr[NPTR];    // K-strided: first K-row of the block (for masking)
-  bool ok[NPTR];   // K-major: row is valid
+  static constexpr int NW = NTH / 64;
+  static constexpr int NB = ROWS * BK * int(sizeof(T)) / 1024 / NW;  // DMA instructions per wave
+  static constexpr int NT = BK * ROWS / (4 * VEC) / NTH;               // LM_REG blocks per thread
+  static constexpr bool DMA = LM != LM_REG;
+  static constexpr int NREG = DMA ? 1 : 4 * NT;
+  static_assert(!DMA || NB * 1024 * NW == ROWS * BK * int(sizeof(T)), "DMA blocks per wave");
+  static_assert(DMA || (NT >= 1 && NT * 4 * VEC * NTH == ROWS * BK), "tile/threads");
+  static_assert(LM != LM_TDMA || (sizeof(T) == 2 && ROWS * 2 >= 256 && 1024 % (ROWS * 2) == 0),
+                "transposed tiles: bf16 rows of 256 or 512 bytes");
+  uint32_t voff[DMA ? NB : 4 * NT];  // byte offsets from the step's base
+  int lrow[DMA ? 1 : NT];            // LM_REG: first LDS row of the block
+  int lk[DMA ? 1 : NT];              // LM_REG: LDS k offset
 };
 
-template <typename T, int BM, int BN, int BK, bool SCALED>
-struct Smem {
-  T A[2][BM * BK];
-  T B[2][BN * BK];
-  float SA[SCALED ? 2 : 1][SCALED ? BM : 1];  // FP8 row scales of the A tile
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+// LDS transpose read of 16-bit data: in each 16-lane group, slot j of lane i
+// receives element i % 4 of the 8 bytes addressed by lane 4 j + i / 4.
+__device__ __forceinline__ u32x2 lds_read_tr16(const void* p) {
+  return __builtin_bit_cast(
+      u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(void*)p));
+}
+
+// One LDS stage. The two stages are separate objects so that the compiler
+// can tell the DMA into one from the reads of the other.
+template <typename T, int BM, int BN, int BK, int NTH, bool SCALED>
+struct Stage {
+  T A[BM * BK];
+  T B[BN * BK];
+  float SA[SCALED ? (NTH > BM ? NTH : BM) : 1];  // FP8 row scales of the A tile (padded)
 };
 
 template <typename T, typename TC, bool A_KMAJ, bool B_KMAJ, int MODE, int EPI, int BM, int BN,
           int BK, int WM, int WN, int PF>
-__global__ __launch_bounds__(WM * WN * 64) void gemm_kernel(GemmArgs g) {
+__global__ __launch_bounds__(WM * WN * 64) __attribute__((amdgpu_waves_per_eu(2)))
+void gemm_kernel(GemmArgs g) {
   constexpr int NTH = WM * WN * 64;
   using MF = Mfma<T>;
   using TO = typename OutOf<T>::type;
   constexpr bool FP8 = sizeof(T) == 1;
-  using SM = Smem<T, BM, BN, BK, FP8>;
+  using ST = Stage<T, BM, BN, BK, WM * WN * 64, FP8>;
   constexpr int VEC = 16 / sizeof(T);
   constexpr int WTM = BM / WM, WTN = BN / WN;
   constexpr int FM = WTM / 16, FN = WTN / 16;
-  using PA = OperandPlan<T, A_KMAJ, BM, BK, NTH>;
-  using PB = OperandPlan<T, B_KMAJ, BN, BK, NTH>;
+  constexpr int ALM = layout_mode<T, A_KMAJ>(), BLM = layout_mode<T, B_KMAJ>();
+  using PA = OperandPlan<T, ALM, BM, BK, NTH>;
+  using PB = OperandPlan<T, BLM, BN, BK, NTH>;
   static_assert(WM * WN == 4 || WM * WN == 8, "four or eight waves");
   static_assert(EPI != EPI_SWIGLU || FN % 2 == 0, "SwiGLU pairs column fragments");
   static_assert(!FP8 || (MODE == G_ROWS && A_KMAJ && BK == 128 && BN <= 128 && BM <= 256),
                 "FP8: row-grouped GEMMs, one 128-deep scale block per K step");
 
-  __shared__ __attribute__((aligned(16))) SM sm;
+  __shared__ __attribute__((aligned(16))) ST st0;
+  __shared__ __attribute__((aligned(16))) ST st1;
   __shared__ int s_scan[8];
   __shared__ int s_info[3];
 
   const int tid = threadIdx.x;
   const int lane = lane_id();
-  const int wave = tid / kWave;
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
   const int wm = wave / WN, wn = wave % WN;
   const int tile = tile_remap(blockIdx.x);
 
+  // tile -> (group, row tile, column tile); all of it wave-uniform
   int grp, mt, nt;
   int row0;           // first A row (ROWS) of the tile
   int mrows;          // valid rows in the tile (ROWS)
   int kbase, kcount;  // contraction range
   if (MODE == G_ROWS) {
     find_group<BM, NTH>(g.offsets, g.G, g.tiles_n, tile, s_scan, s_info);
-    grp = s_info[0];
+    grp = __builtin_amdgcn_readfirstlane(s_info[0]);
     if (grp < 0) return;
-    const int cnt = s_info[1];
-    const int local = tile - s_info[2];
+    const int cnt = __builtin_amdgcn_readfirstlane(s_info[1]);
+    const int local = tile - __builtin_amdgcn_readfirstlane(s_info[2]);
     nt = local / cnt;
     mt = local % cnt;
     row0 = g.offsets[grp] + mt * BM;
@@ -311,70 +387,109 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_kernel(GemmArgs g) {
     kbase = g.offsets[grp];
     kcount = g.offsets[grp + 1] - kbase;
   }
-
-  const T* __restrict__ Ab = reinterpret_cast<const T*>(g.A);
-  const T* __restrict__ Bb = reinterpret_cast<const T*>(g.B);
-  if (MODE == G_ROWS) Bb += int64_t(grp) * g.b_gstride;
   const int m0 = mt * BM;  // KSPLIT: output row block
   const int n0 = nt * BN;
+  const int nk = (kcount + BK - 1) / BK;  // K steps
+  constexpr int64_t ES = sizeof(T);
 
-  // ---- per-thread load plans
+  // ---- operand sources: byte base at K step 0, byte end of the valid
+  // range, byte advance per K step
+  const char* a_base;
+  int64_t a_end, a_step;
+  if constexpr (A_KMAJ) {  // rows row0 .. row0 + mrows of A [rows, K]
+    a_base = reinterpret_cast<const char*>(g.A) + int64_t(row0) * g.lda * ES;
+    a_end = int64_t(mrows) * g.lda * ES;
+    a_step = BK * ES;
+  } else {  // K-rows kbase .. kbase + kcount of A [K, M]
+    a_base = reinterpret_cast<const char*>(g.A) + int64_t(kbase) * g.lda * ES;
+    a_end = int64_t(kcount) * g.lda * ES;
+    a_step = BK * g.lda * ES;
+  }
+  const char* b_base = reinterpret_cast<const char*>(g.B);
+  if (MODE == G_ROWS) b_base += int64_t(grp) * g.b_gstride * ES;
+  int64_t b_end, b_step;
+  if constexpr (B_KMAJ) {  // rows 0 .. N of B [N, K] (ROWS)
+    b_end = int64_t(g.N) * g.ldb * ES;
+    b_step = BK * ES;
+  } else if constexpr (MODE == G_ROWS) {  // B [K, N]
+    b_end = int64_t(g.K) * g.ldb * ES;
+    b_step = BK * g.ldb * ES;
+  } else {  // K-rows kbase .. kbase + kcount of B [K, N]
+    b_base += int64_t(kbase) * g.ldb * ES;
+    b_end = int64_t(kcount) * g.ldb * ES;
+    b_step = BK * g.ldb * ES;
+  }
+
+  // ---- per-thread load plans (offsets are fixed for the whole K loop)
   PA pa;
   PB pb;
-  if constexpr (A_KMAJ) {
+  // LM_TDMA: K-row kr of the tile holds ROWS elements from column col0; DMA
+  // block b covers K-rows b * RPB .. + RPB
+  auto tdma_voff = [&](int b, int ROWS, int64_t ld, int col0) {
+    const int CPR = ROWS * 2 / 16, RPB = 1024 / (ROWS * 2);
+    const int kr = b * RPB + lane / CPR;
+    const int lc = (lane % CPR) ^ (2 * (kr & 3));
+    return uint32_t((int64_t(kr) * ld + col0 + lc * 8) * ES);
+  };
+  if constexpr (ALM == LM_KDMA) {
 #pragma unroll
-    for (int i = 0; i < PA::NPTR; ++i) {
-      const int q = tid + i * NTH;
-      const int r = q / (BK / VEC), kc = q % (BK / VEC);
-      pa.lrow[i] = r;
-      pa.lk[i] = kc * VEC;
-      pa.ok[i] = r < mrows;
-      pa.ptr[i] = Ab + int64_t(row0 + (r < mrows ? r : 0)) * g.lda + kc * VEC;
+    for (int j = 0; j < PA::NB; ++j) {
+      const int r = (j * PA::NW + wave) * 8 + lane / 8;
+      const int lc = (lane % 8) ^ lds_swz<true>(r);
+      pa.voff[j] = uint32_t(int64_t(r) * g.lda * ES + lc * 16);
     }
+  } else if constexpr (ALM == LM_TDMA) {
+#pragma unroll
+    for (int j = 0; j < PA::NB; ++j) pa.voff[j] = tdma_voff(j * PA::NW + wave, BM, g.lda, m0);
   } else {
 #pragma unroll
-    for (int i = 0; i < PA::NPTR; ++i) {
+    for (int i = 0; i < PA::NT; ++i) {
       const int q = tid + i * NTH;
       const int kq = q / (BM / VEC), mc = q % (BM / VEC);
       pa.lrow[i] = mc * VEC;
       pa.lk[i] = 4 * kq;
-      pa.kr[i] = 4 * kq;
-      pa.ptr[i] = Ab + int64_t(kbase + 4 * kq) * g.lda + m0 + mc * VEC;
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        pa.voff[4 * i + j] = uint32_t((int64_t(4 * kq + j) * g.lda + m0 + mc * VEC) * ES);
     }
   }
-  if constexpr (B_KMAJ) {
+  if constexpr (BLM == LM_KDMA) {
 #pragma unroll
-    for (int i = 0; i < PB::NPTR; ++i) {
-      const int q = tid + i * NTH;
-      const int r = q / (BK / VEC), kc = q % (BK / VEC);
+    for (int j = 0; j < PB::NB; ++j) {
+      const int r = (j * PB::NW + wave) * 8 + lane / 8;
+      const int lc = (lane % 8) ^ lds_swz<true>(r);
       int grow = n0 + r;
       if (EPI == EPI_SWIGLU) {
         // gate and up rows of the same output columns side by side within
         // each wave's column range
         const int w = r / WTN, within = r % WTN;
-        const int half = within / (WTN / 2), j = within % (WTN / 2);
-        grow = half * g.f + nt * (BN / 2) + w * (WTN / 2) + j;
+        const int half = within / (WTN / 2), jj = within % (WTN / 2);
+        grow = half * g.f + nt * (BN / 2) + w * (WTN / 2) + jj;
       }
-      pb.lrow[i] = r;
-      pb.lk[i] = kc * VEC;
-      pb.ok[i] = true;
-      pb.ptr[i] = Bb + int64_t(grow) * g.ldb + kc * VEC;
+      pb.voff[j] = uint32_t(int64_t(grow) * g.ldb * ES + lc * 16);
     }
+  } else if constexpr (BLM == LM_TDMA) {
+#pragma unroll
+    for (int j = 0; j < PB::NB; ++j) pb.voff[j] = tdma_voff(j * PB::NW + wave, BN, g.ldb, n0);
   } else {
 #pragma unroll
-    for (int i = 0; i < PB::NPTR; ++i) {
+    for (int i = 0; i < PB::NT; ++i) {
       const int q = tid + i * NTH;
       const int kq = q / (BN / VEC), nc = q % (BN / VEC);
       pb.lrow[i] = nc * VEC;
       pb.lk[i] = 4 * kq;
-      pb.kr[i] = 4 * kq;
-      pb.ptr[i] = Bb + int64_t(kbase + 4 * kq) * g.ldb + n0 + nc * VEC;
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        pb.voff[4 * i + j] = uint32_t((int64_t(4 * kq + j) * g.ldb + n0 + nc * VEC) * ES);
     }
   }
-  // FP8: the thread that stages the row scale of A-tile row tid (if any)
-  const float* __restrict__ sa_ptr = nullptr;
+  // FP8: thread tid stages the row scale of A-tile row tid; rows past the
+  // group (and threads past the tile) read zeros
+  const char* sa_base = nullptr;
+  int64_t sa_end = 0;
   if constexpr (FP8) {
-    if (tid < BM && tid < mrows) sa_ptr = g.a_scale + int64_t(row0 + tid) * g.a_scale_ld;
+    sa_base = reinterpret_cast<const char*>(g.a_scale + int64_t(row0) * g.a_scale_ld);
+    sa_end = int64_t(mrows) * g.a_scale_ld * 4;
   }
   // FP8: column-block scale rows of B; SwiGLU tiles span a gate block and an
   // up block of W1
@@ -390,63 +505,53 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_kernel(GemmArgs g) {
     }
   }
 
-  static_assert(PF == 1 || PF == 2, "prefetch depth");
-  const u32x4 zero4 = {0u, 0u, 0u, 0u};
-  // PF register sets of staged operand chunks (and FP8 row scales)
-  u32x4 ra0[PA::NREG], rb0[PB::NREG], ra1[PA::NREG], rb1[PB::NREG];
-  float rs0 = 0.0f, rs1 = 0.0f;
-  // global -> register set (ra, rb, rs) for the K step starting at k0
-#define MOE_GLOAD(k0, ra, rb, rs)                                                               \
-  do {                                                                                          \
-    if constexpr (A_KMAJ) {                                                                     \
-      _Pragma("unroll") for (int i = 0; i < PA::NPTR; ++i) {                                    \
-        ra[i] = pa.ok[i] ? *reinterpret_cast<const u32x4*>(pa.ptr[i] + (k0)) : zero4;           \
-      }                                                                                         \
-    } else {                                                                                    \
-      _Pragma("unroll") for (int i = 0; i < PA::NPTR; ++i) {                                    \
-        _Pragma("unroll") for (int j = 0; j < 4; ++j) {                                         \
-          const bool v = (k0) + pa.kr[i] + j < kcount;                                          \
-          ra[4 * i + j] = v ? *reinterpret_cast<const u32x4*>(pa.ptr[i] + int64_t((k0) + j) * g.lda) \
-                            : zero4;                                                            \
-        }                                                                                       \
-      }                                                                                         \
-    }                                                                                           \
-    if constexpr (B_KMAJ) {                                                                     \
-      _Pragma("unroll") for (int i = 0; i < PB::NPTR; ++i) {                                    \
-        rb[i] = *reinterpret_cast<const u32x4*>(pb.ptr[i] + (k0));                              \
-      }                                                                                         \
-    } else {                                                                                    \
-      _Pragma("unroll") for (int i = 0; i < PB::NPTR; ++i) {                                    \
-        _Pragma("unroll") for (int j = 0; j < 4; ++j) {                                         \
-          const bool v = MODE == G_ROWS || (k0) + pb.kr[i] + j < kcount;                        \
-          rb[4 * i + j] = v ? *reinterpret_cast<const u32x4*>(pb.ptr[i] + int64_t((k0) + j) * g.ldb) \
-                            : zero4;                                                            \
-        }                                                                                       \
-      }                                                                                         \
-    }                                                                                           \
-    if constexpr (FP8) rs = sa_ptr ? sa_ptr[(k0) / 128] : 0.0f;                                 \
-  } while (0)
-  // register set (ra, rb, rs) -> LDS buffer `buf`
-#define MOE_LSTORE(buf, ra, rb, rs)                                                             \
-  do {                                                                                          \
-    if constexpr (A_KMAJ) {                                                                     \
-      _Pragma("unroll") for (int i = 0; i < PA::NPTR; ++i)                                      \
-        *reinterpret_cast<u32x4*>(&sm.A[buf][lds_off<T, BK>(pa.lrow[i], pa.lk[i])]) = ra[i];    \
-    } else {                                                                                    \
-      _Pragma("unroll") for (int i = 0; i < PA::NPTR; ++i)                                      \
-        store_transposed<T, BK>(&ra[4 * i], sm.A[buf], pa.lrow[i], pa.lk[i]);                   \
-    }                                                                                           \
-    if constexpr (B_KMAJ) {                                                                     \
-      _Pragma("unroll") for (int i = 0; i < PB::NPTR; ++i)                                      \
-        *reinterpret_cast<u32x4*>(&sm.B[buf][lds_off<T, BK>(pb.lrow[i], pb.lk[i])]) = rb[i];    \
-    } else {                                                                                    \
-      _Pragma("unroll") for (int i = 0; i < PB::NPTR; ++i)                                      \
-        store_transposed<T, BK>(&rb[4 * i], sm.B[buf], pb.lrow[i], pb.lk[i]);                   \
-    }                                                                                           \
-    if constexpr (FP8) {                                                                        \
-      if (tid < BM) sm.SA[buf][tid] = rs;                                                       \
-    }                                                                                           \
-  } while (0)
+  // register-staged operand chunks (K-strided sources) and FP8 row scale
+  u32x4 ra[PA::NREG], rb[PB::NREG];
+  float rs = 0.0f;
+
+  // issue the loads of K step s into stage st: DMA for K-major operands,
+  // registers for K-strided ones
+  auto issue = [&](ST& st, int s) {
+    // steps at or past the end (padding, last prefetch) get empty ranges:
+    // for a K-major operand the advanced base would otherwise reach into
+    // the next row
+    const bool live = s < nk;
+    const rsrc_t ar = make_rsrc(a_base + int64_t(s) * a_step, live ? a_end - int64_t(s) * a_step : 0);
+    const rsrc_t br = make_rsrc(b_base + int64_t(s) * b_step, live ? b_end - int64_t(s) * b_step : 0);
+    if constexpr (PA::DMA) {
+#pragma unroll
+      for (int j = 0; j < PA::NB; ++j)
+        dma16(ar, &st.A[(j * PA::NW + wave) * (1024 / ES)], pa.voff[j]);
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4 * PA::NT; ++i) ra[i] = __builtin_amdgcn_raw_buffer_load_b128(ar, pa.voff[i], 0, 0);
+    }
+    if constexpr (PB::DMA) {
+#pragma unroll
+      for (int j = 0; j < PB::NB; ++j)
+        dma16(br, &st.B[(j * PB::NW + wave) * (1024 / ES)], pb.voff[j]);
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4 * PB::NT; ++i) rb[i] = __builtin_amdgcn_raw_buffer_load_b128(br, pb.voff[i], 0, 0);
+    }
+    if constexpr (FP8) {
+      const rsrc_t sr = make_rsrc(sa_base, live ? sa_end : 0);
+      rs = __builtin_bit_cast(
+          float, __builtin_amdgcn_raw_buffer_load_b32(sr, uint32_t((tid * g.a_scale_ld + s * (BK / 128)) * 4), 0, 0));
+    }
+  };
+  // write the register-staged parts of a step into stage st
+  auto commit = [&](ST& st) {
+    if constexpr (!PA::DMA) {
+#pragma unroll
+      for (int i = 0; i < PA::NT; ++i) store_transposed<T, BK>(&ra[4 * i], st.A, pa.lrow[i], pa.lk[i]);
+    }
+    if constexpr (!PB::DMA) {
+#pragma unroll
+      for (int i = 0; i < PB::NT; ++i) store_transposed<T, BK>(&rb[4 * i], st.B, pb.lrow[i], pb.lk[i]);
+    }
+    if constexpr (FP8) st.SA[tid] = rs;
+  };
 
   f32x4_t acc[FM][FN];
 #pragma unroll
@@ -454,81 +559,138 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_kernel(GemmArgs g) {
 #pragma unroll
     for (int j = 0; j < FN; ++j) acc[i][j] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
 
-  // one K step on LDS buffer `buf` (K block s)
-#define MOE_COMPUTE(s, buf)                                                                     \
-  do {                                                                                          \
-    float sb0 = 0.0f, sb1 = 0.0f;                                                               \
-    if constexpr (FP8) {                                                                        \
-      const int kb = (s); /* BK == 128: one scale block per step */                             \
-      if (B_KMAJ) {                                                                             \
-        sb0 = sb_base[int64_t(sb_blk0) * g.b_scale_ld + kb];                                    \
-        sb1 = sb_base[int64_t(sb_blk1) * g.b_scale_ld + kb];                                    \
-      } else {                                                                                  \
-        sb0 = sb1 = sb_base[int64_t(kb) * g.b_scale_ld + sb_blk0];                              \
-      }                                                                                         \
-    }                                                                                           \
-    _Pragma("unroll") for (int kk = 0; kk < BK / MF::MK; ++kk) {                                \
-      const int kofs = kk * MF::MK + (lane / 16) * MF::KP;                                      \
-      typename MF::frag af[FM], bfr[FN];                                                        \
-      _Pragma("unroll") for (int i = 0; i < FM; ++i) {                                          \
-        const int r = wm * WTM + i * 16 + (lane % 16);                                          \
-        af[i] = MF::load(&sm.A[buf][lds_off<T, BK>(r, kofs)], &sm.A[buf][lds_off<T, BK>(r, kofs + 16)]); \
-      }                                                                                         \
-      _Pragma("unroll") for (int j = 0; j < FN; ++j) {                                          \
-        const int r = wn * WTN + j * 16 + (lane % 16);                                          \
-        bfr[j] = MF::load(&sm.B[buf][lds_off<T, BK>(r, kofs)], &sm.B[buf][lds_off<T, BK>(r, kofs + 16)]); \
-      }                                                                                         \
-      if constexpr (FP8) {                                                                      \
-        _Pragma("unroll") for (int i = 0; i < FM; ++i) {                                        \
-          const float4 sa4 =                                                                    \
-              *reinterpret_cast<const float4*>(&sm.SA[buf][wm * WTM + i * 16 + 4 * (lane / 16)]); \
-          const float sa[4] = {sa4.x, sa4.y, sa4.z, sa4.w};                                     \
-          _Pragma("unroll") for (int j = 0; j < FN; ++j) {                                      \
-            const float sbj = (EPI == EPI_SWIGLU && j >= FN / 2) ? sb1 : sb0;                   \
-            const f32x4_t dd = MF::mma(af[i], bfr[j], f32x4_t{0.0f, 0.0f, 0.0f, 0.0f});         \
-            _Pragma("unroll") for (int r = 0; r < 4; ++r)                                       \
-              acc[i][j][r] = __builtin_fmaf(dd[r], sa[r] * sbj, acc[i][j][r]);                  \
-          }                                                                                     \
-        }                                                                                       \
-      } else {                                                                                  \
-        _Pragma("unroll") for (int i = 0; i < FM; ++i)                                          \
-          _Pragma("unroll") for (int j = 0; j < FN; ++j) acc[i][j] = MF::mma(af[i], bfr[j], acc[i][j]); \
-      }                                                                                         \
-    }                                                                                           \
-  } while (0)
+  // LM_TDMA fragment: tile columns c0 .. c0 + 16 (one per lane of a 16-lane
+  // group), K-rows 32 kk + 8 (lane / 16) .. + 8 from two transpose reads
+  auto load_tr = [&](const T* tile, int ROWS, int c0, int kk) {
+    typename MF::frag f{};
+    if constexpr (sizeof(T) == 2) {
+      const int s16 = lane % 16, t = s16 / 4, q = s16 % 4;
+      const int kr = kk * 32 + 8 * (lane / 16) + t;
+      const int col = c0 + 4 * q;
+      const char* p =
+          reinterpret_cast<const char*>(tile) + kr * (ROWS * 2) + (((col / 8) ^ (2 * t)) * 16) + (col % 8) * 2;
+      const u32x2 lo = lds_read_tr16(p), hi = lds_read_tr16(p + 4 * ROWS * 2);
+      f = __builtin_bit_cast(typename MF::frag, u32x4{lo[0], lo[1], hi[0], hi[1]});
+    }
+    return f;
+  };
+  // fragment i (rows i*16 .. +16 of the wave's A rows) / j (B rows), sub-step kk
+  auto load_a = [&](const ST& st, int i, int kk) {
+    if constexpr (ALM == LM_TDMA) {
+      return load_tr(st.A, BM, wm * WTM + i * 16, kk);
+    } else {
+      const int r = wm * WTM + i * 16 + (lane % 16), kofs = MF::kofs(lane, kk);
+      return MF::load(&st.A[lds_off<T, BK, A_KMAJ>(r, kofs)], &st.A[lds_off<T, BK, A_KMAJ>(r, kofs + MF::K2)]);
+    }
+  };
+  auto load_b = [&](const ST& st, int j, int kk) {
+    if constexpr (BLM == LM_TDMA) {
+      return load_tr(st.B, BN, wn * WTN + j * 16, kk);
+    } else {
+      const int r = wn * WTN + j * 16 + (lane % 16), kofs = MF::kofs(lane, kk);
+      return MF::load(&st.B[lds_off<T, BK, B_KMAJ>(r, kofs)], &st.B[lds_off<T, BK, B_KMAJ>(r, kofs + MF::K2)]);
+    }
+  };
 
-  // K loop: LDS double buffer; PF register sets of global loads in flight,
-  // so a load issued at K step s is written to LDS at the end of step
-  // s + PF - 1.
-  const int nk = (kcount + BK - 1) / BK;
+  // one K step (K block s) on stage st
+  auto compute = [&](const ST& st, int s) {
+    float sb0 = 0.0f, sb1 = 0.0f;
+    if constexpr (FP8) {
+      const int kb = min(s, nk - 1);  // BK == 128: one scale block per step
+      if (B_KMAJ) {
+        sb0 = sb_base[int64_t(sb_blk0) * g.b_scale_ld + kb];
+        sb1 = sb_base[int64_t(sb_blk1) * g.b_scale_ld + kb];
+      } else {
+        sb0 = sb1 = sb_base[int64_t(kb) * g.b_scale_ld + sb_blk0];
+      }
+    }
+    if constexpr (FP8) {
+      // one 128-deep block per step: B fragments first, then one A fragment
+      // ahead of the FN MFMAs (into temporaries) and their scaled adds
+      static_assert(BK == MF::MK, "one MFMA K block per step");
+      typename MF::frag bfr[FN], acur, anxt;
+#pragma unroll
+      for (int j = 0; j < FN; ++j) bfr[j] = load_b(st, j, 0);
+      acur = load_a(st, 0, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, FN + 1, 0);
+      static_for<FM>([&](auto ic) {
+        constexpr int i = decltype(ic)::value;
+        if constexpr (i + 1 < FM) anxt = load_a(st, i + 1, 0);
+        const float4 sa4 = *reinterpret_cast<const float4*>(&st.SA[wm * WTM + i * 16 + 4 * (lane / 16)]);
+        const float sa[4] = {sa4.x, sa4.y, sa4.z, sa4.w};
+        f32x4_t dd[FN];
+#pragma unroll
+        for (int j = 0; j < FN; ++j) dd[j] = MF::mma(acur, bfr[j], f32x4_t{0.0f, 0.0f, 0.0f, 0.0f});
+#pragma unroll
+        for (int j = 0; j < FN; ++j) {
+          const float sbj = (EPI == EPI_SWIGLU && j >= FN / 2) ? sb1 : sb0;
+#pragma unroll
+          for (int r = 0; r < 4; ++r) acc[i][j][r] = __builtin_fmaf(dd[j][r], sa[r] * sbj, acc[i][j][r]);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x100, (i + 1 < FM) ? 2 : 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, FN, 0);
+        if constexpr (i + 1 < FM) acur = anxt;
+      });
+    } else {
+      // Software-pipelined fragment reads: the B fragments of sub-step kk and
+      // one A fragment are read ahead of the MFMAs that use them; the order
+      // is pinned (one DS read, then FN MFMAs) so that the scheduler does not
+      // hoist every read of the next sub-step and run out of registers.
+      constexpr int KK = BK / MF::MK;
+      typename MF::frag bcur[FN], bnxt[FN], acur, anxt;
+#pragma unroll
+      for (int j = 0; j < FN; ++j) bcur[j] = load_b(st, j, 0);
+      acur = load_a(st, 0, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, FN + 1, 0);
+      static_for<KK * FM>([&](auto tc) {
+        constexpr int t = decltype(tc)::value;
+        constexpr int kk = t / FM, i = t % FM;
+        constexpr bool more_a = t + 1 < KK * FM;
+        constexpr bool more_b = i == FM - 1 && kk + 1 < KK;
+        if constexpr (more_a) anxt = load_a(st, (t + 1) % FM, (t + 1) / FM);
+        if constexpr (more_b) {
+#pragma unroll
+          for (int j = 0; j < FN; ++j) bnxt[j] = load_b(st, j, kk + 1);
+        }
+#pragma unroll
+        for (int j = 0; j < FN; ++j) acc[i][j] = MF::mma(acur, bcur[j], acc[i][j]);
+        constexpr int nreads = (more_a ? 1 : 0) + (more_b ? FN : 0);
+        if constexpr (nreads > 0) __builtin_amdgcn_sched_group_barrier(0x100, nreads, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, FN, 0);
+        acur = anxt;
+        if constexpr (more_b) {
+#pragma unroll
+          for (int j = 0; j < FN; ++j) bcur[j] = bnxt[j];
+        }
+      });
+    }
+  };
+
+  // K loop over two LDS stages: the loads of step s + 1 are issued before
+  // the MFMAs of step s and land (DMA, or registers written to LDS) before
+  // the barrier that ends step s. Unrolled by two so that every access names
+  // its stage statically, over an even number of steps so that the loop has
+  // one exit: the step past the end (odd step counts) and the prefetch past
+  // the last step read outside their descriptors' ranges, i.e. zeros, and
+  // touch no memory.
   if (nk > 0) {
-    MOE_GLOAD(0, ra0, rb0, rs0);
-    if (PF == 2 && nk > 1) MOE_GLOAD(BK, ra1, rb1, rs1);
-    MOE_LSTORE(0, ra0, rb0, rs0);
+    const int nk2 = (nk + 1) & ~1;
+    issue(st0, 0);
+    commit(st0);
     __syncthreads();
-  }
-  if constexpr (PF == 1) {
-    for (int s = 0; s < nk; ++s) {
-      const int buf = s & 1;
-      if (s + 1 < nk) MOE_GLOAD((s + 1) * BK, ra0, rb0, rs0);
-      MOE_COMPUTE(s, buf);
-      if (s + 1 < nk) MOE_LSTORE(buf ^ 1, ra0, rb0, rs0);
+    for (int s = 0; s < nk2; s += 2) {
+      issue(st1, s + 1);
+      __builtin_amdgcn_sched_barrier(0);
+      compute(st0, s);
+      commit(st1);
       __syncthreads();
-    }
-  } else {
-    for (int s = 0; s < nk; s += 2) {
-      if (s + 2 < nk) MOE_GLOAD((s + 2) * BK, ra0, rb0, rs0);
-      MOE_COMPUTE(s, 0);
-      if (s + 1 < nk) MOE_LSTORE(1, ra1, rb1, rs1);
-      __syncthreads();
-      if (s + 1 >= nk) break;
-      if (s + 3 < nk) MOE_GLOAD((s + 3) * BK, ra1, rb1, rs1);
-      MOE_COMPUTE(s + 1, 1);
-      if (s + 2 < nk) MOE_LSTORE(0, ra0, rb0, rs0);
+      issue(st0, s + 2);
+      __builtin_amdgcn_sched_barrier(0);
+      compute(st1, s + 1);
+      commit(st0);
       __syncthreads();
     }
   }
-#undef MOE_COMPUTE
 
   // epilogue: lane holds rows 4*(lane/16)+r, column lane%16 of each 16x16
   const int lr = 4 * (lane / 16), lc = lane % 16;
@@ -591,8 +753,6 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_kernel(GemmArgs g) {
       }
   }
 }
-#undef MOE_GLOAD
-#undef MOE_LSTORE
 
 // ---------------------------------------------------------------------------
 // FP8 row quantisation (1 x 128 blocks) and dequantisation, 16 lanes per block
