@@ -281,9 +281,12 @@ __device__ __forceinline__ void dma16(rsrc_t r, void* dst, uint32_t voff) {
 //            logical chunk that the swizzle puts there.
 //   LM_TDMA  K-strided bf16 source, DMA into BK K-rows of ROWS elements (the
 //            source's own orientation); 16-byte chunks are XOR-swizzled with
-//            2 * (K-row & 3). MFMA fragments are read with the LDS transpose
+//            tr_swz(K-row). MFMA fragments are read with the LDS transpose
 //            read (ds_read_b64_tr_b16), which hands each lane of a 16-lane
-//            group one column of 4 consecutive K-rows.
+//            group one column of 4 consecutive K-rows. Measured on gfx950,
+//            the transpose read serves 32 lanes (two groups, K-rows 8 apart)
+//            at a time: the swizzle separates the 4 K-rows of a group (bits
+//            1-2) and the two groups (bit 3), which makes it conflict-free.
 //   LM_REG   other K-strided sources (fp32, FP8): NT blocks of 4 K-rows x VEC
 //            columns per thread, loaded into registers and transposed on
 //            their way into LDS (K-major rows, swizzled as in lds_off).
@@ -304,11 +307,35 @@ struct OperandPlan {
   static_assert(!DMA || NB * 1024 * NW == ROWS * BK * int(sizeof(T)), "DMA blocks per wave");
   static_assert(DMA || (NT >= 1 && NT * 4 * VEC * NTH == ROWS * BK), "tile/threads");
   static_assert(LM != LM_TDMA || (sizeof(T) == 2 && ROWS * 2 >= 256 && 1024 % (ROWS * 2) == 0),
-                "transposed tiles: bf16 rows of 256 or 512 bytes");
+                "transposed tiles: bf16 rows of 256 or 512 bytes (at least 16 chunks for the swizzle)");
   uint32_t voff[DMA ? NB : 4 * NT];  // byte offsets from the step's base
   int lrow[DMA ? 1 : NT];            // LM_REG: first LDS row of the block
   int lk[DMA ? 1 : NT];              // LM_REG: LDS k offset
 };
+
+__device__ __forceinline__ int tr_swz(int kr) { return (2 * (kr & 3)) ^ (8 * ((kr >> 3) & 1)); }
+
+// 8 consecutive values: fp32 from LDS; bf16 / fp32 to and from global memory
+__device__ __forceinline__ void lds_read8(const float* p, float* v) {
+  const float4 a = *reinterpret_cast<const float4*>(p), b = *reinterpret_cast<const float4*>(p + 4);
+  v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w; v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+}
+template <typename T> __device__ __forceinline__ void store8(T* p, const float* v) {
+  if constexpr (sizeof(T) == 2) {
+    Vec16<bf16_t>::store(p, v);
+  } else {
+    Vec16<float>::store(p, v);
+    Vec16<float>::store(p + 4, v + 4);
+  }
+}
+template <typename T> __device__ __forceinline__ void load8(const T* p, float* v) {
+  if constexpr (sizeof(T) == 2) {
+    Vec16<bf16_t>::load(p, v);
+  } else {
+    Vec16<float>::load(p, v);
+    Vec16<float>::load(p + 4, v + 4);
+  }
+}
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 // LDS transpose read of 16-bit data: in each 16-lane group, slot j of lane i
@@ -428,7 +455,7 @@ void gemm_kernel(GemmArgs g) {
   auto tdma_voff = [&](int b, int ROWS, int64_t ld, int col0) {
     const int CPR = ROWS * 2 / 16, RPB = 1024 / (ROWS * 2);
     const int kr = b * RPB + lane / CPR;
-    const int lc = (lane % CPR) ^ (2 * (kr & 3));
+    const int lc = (lane % CPR) ^ tr_swz(kr);
     return uint32_t((int64_t(kr) * ld + col0 + lc * 8) * ES);
   };
   if constexpr (ALM == LM_KDMA) {
@@ -568,7 +595,7 @@ void gemm_kernel(GemmArgs g) {
       const int kr = kk * 32 + 8 * (lane / 16) + t;
       const int col = c0 + 4 * q;
       const char* p =
-          reinterpret_cast<const char*>(tile) + kr * (ROWS * 2) + (((col / 8) ^ (2 * t)) * 16) + (col % 8) * 2;
+          reinterpret_cast<const char*>(tile) + kr * (ROWS * 2) + (((col / 8) ^ tr_swz(kr)) * 16) + (col % 8) * 2;
       const u32x2 lo = lds_read_tr16(p), hi = lds_read_tr16(p + 4 * ROWS * 2);
       f = __builtin_bit_cast(typename MF::frag, u32x4{lo[0], lo[1], hi[0], hi[1]});
     }
@@ -692,65 +719,78 @@ void gemm_kernel(GemmArgs g) {
     }
   }
 
-  // epilogue: lane holds rows 4*(lane/16)+r, column lane%16 of each 16x16
-  const int lr = 4 * (lane / 16), lc = lane % 16;
-  if (EPI == EPI_STORE) {
-    TC* Cb = reinterpret_cast<TC*>(g.C);
-    if (MODE == G_KSPLIT) Cb += int64_t(grp) * g.c_gstride;
+  // Epilogue through LDS (all stages are free after the K loop's last
+  // barrier). A lane holds rows 4 (lane / 16) + r, column lane % 16 of each
+  // 16 x 16 accumulator block; every wave writes one 16-row block of its
+  // tile at a time to a private LDS region and reads it back as 8
+  // consecutive columns per lane, so that global loads and stores are 16
+  // bytes wide. A wave's LDS accesses complete in order, so no barrier is
+  // needed between its writes and reads.
+  constexpr int EP = WTN + 4;          // floats per staged row (pad: no bank conflicts)
+  constexpr int UPR = WTN / 8;         // 8-column units per staged row
+  static_assert(int(sizeof(ST)) >= NTH / 64 * 16 * EP * 4, "staging fits in one LDS stage");
+  float* stg = reinterpret_cast<float*>(&st0) + wave * 16 * EP;
+  TC* Cb = reinterpret_cast<TC*>(g.C);
+  if (MODE == G_KSPLIT) Cb += int64_t(grp) * g.c_gstride;
 #pragma unroll
-    for (int i = 0; i < FM; ++i)
+  for (int i = 0; i < FM; ++i) {
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int rl = wm * WTM + i * 16 + lr + r;
-        if (MODE == G_ROWS && rl >= mrows) continue;
-        const int64_t row = (MODE == G_ROWS) ? int64_t(row0 + rl) : int64_t(m0 + rl);
+    for (int j = 0; j < FN; ++j)
 #pragma unroll
-        for (int j = 0; j < FN; ++j) {
-          const int col = n0 + wn * WTN + j * 16 + lc;
-          Elem<TC>::store(Cb + row * g.ldc + col, acc[i][j][r]);
+      for (int r = 0; r < 4; ++r) stg[(4 * (lane / 16) + r) * EP + j * 16 + lane % 16] = acc[i][j][r];
+    const int rbase = wm * WTM + i * 16;  // tile row of the block's first row
+    if constexpr (EPI == EPI_SWIGLU) {
+      // staged columns [0, WTN/2) are gate values, [WTN/2, WTN) up values
+      // of the same output columns
+      TO* GU = reinterpret_cast<TO*>(g.aux0);
+      TO* H = reinterpret_cast<TO*>(g.aux1);
+#pragma unroll
+      for (int u = lane; u < 16 * UPR / 2; u += 64) {
+        const int rr = u / (UPR / 2), c8 = u % (UPR / 2);
+        const int rl = rbase + rr;
+        if (rl < mrows) {
+          const int64_t row = row0 + rl;
+          const int col = nt * (BN / 2) + wn * (WTN / 2) + c8 * 8;
+          float G[8], U[8], Hv[8];
+          lds_read8(&stg[rr * EP + c8 * 8], G);
+          lds_read8(&stg[rr * EP + WTN / 2 + c8 * 8], U);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) Hv[e] = G[e] / (1.0f + expf(-G[e])) * U[e];
+          store8<TO>(GU + row * (2 * g.f) + col, G);
+          store8<TO>(GU + row * (2 * g.f) + g.f + col, U);
+          store8<TO>(H + row * g.f + col, Hv);
         }
       }
-  } else if (EPI == EPI_SWIGLU) {
-    TO* GU = reinterpret_cast<TO*>(g.aux0);
-    TO* H = reinterpret_cast<TO*>(g.aux1);
+    } else {
 #pragma unroll
-    for (int i = 0; i < FM; ++i)
+      for (int u = lane; u < 16 * UPR; u += 64) {
+        const int rr = u / UPR, c8 = u % UPR;
+        const int rl = rbase + rr;
+        if (MODE == G_KSPLIT || rl < mrows) {
+          const int64_t row = (MODE == G_ROWS) ? int64_t(row0 + rl) : int64_t(m0 + rl);
+          const int col = n0 + wn * WTN + c8 * 8;
+          float v[8];
+          lds_read8(&stg[rr * EP + c8 * 8], v);
+          if constexpr (EPI == EPI_STORE) {
+            store8<TC>(Cb + row * g.ldc + col, v);
+          } else {  // EPI_DSWIGLU: v = dH; C = dGU [rows, 2f]
+            const TO* GU = reinterpret_cast<const TO*>(g.aux0);
+            TO* D = reinterpret_cast<TO*>(g.C);
+            float G[8], U[8], dG[8], dU[8];
+            load8<TO>(GU + row * (2 * g.f) + col, G);
+            load8<TO>(GU + row * (2 * g.f) + g.f + col, U);
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int rl = wm * WTM + i * 16 + lr + r;
-        if (rl >= mrows) continue;
-        const int64_t row = row0 + rl;
-#pragma unroll
-        for (int j = 0; j < FN / 2; ++j) {
-          const int col = nt * (BN / 2) + wn * (WTN / 2) + j * 16 + lc;
-          const float G = acc[i][j][r], U = acc[i][j + FN / 2][r];
-          const float Hv = G / (1.0f + expf(-G)) * U;
-          Elem<TO>::store(GU + row * (2 * g.f) + col, G);
-          Elem<TO>::store(GU + row * (2 * g.f) + g.f + col, U);
-          Elem<TO>::store(H + row * g.f + col, Hv);
+            for (int e = 0; e < 8; ++e) {
+              const float sg = 1.0f / (1.0f + expf(-G[e]));
+              dG[e] = v[e] * U[e] * sg * (1.0f + G[e] * (1.0f - sg));
+              dU[e] = v[e] * G[e] * sg;
+            }
+            store8<TO>(D + row * (2 * g.f) + col, dG);
+            store8<TO>(D + row * (2 * g.f) + g.f + col, dU);
+          }
         }
       }
-  } else {  // EPI_DSWIGLU: C = dGU [rows, 2f]
-    const TO* GU = reinterpret_cast<const TO*>(g.aux0);
-    TO* D = reinterpret_cast<TO*>(g.C);
-#pragma unroll
-    for (int i = 0; i < FM; ++i)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int rl = wm * WTM + i * 16 + lr + r;
-        if (rl >= mrows) continue;
-        const int64_t row = row0 + rl;
-#pragma unroll
-        for (int j = 0; j < FN; ++j) {
-          const int col = n0 + wn * WTN + j * 16 + lc;
-          const float dH = acc[i][j][r];
-          const float G = Elem<TO>::load(GU + row * (2 * g.f) + col);
-          const float U = Elem<TO>::load(GU + row * (2 * g.f) + g.f + col);
-          const float sg = 1.0f / (1.0f + expf(-G));
-          Elem<TO>::store(D + row * (2 * g.f) + col, dH * U * sg * (1.0f + G * (1.0f - sg)));
-          Elem<TO>::store(D + row * (2 * g.f) + g.f + col, dH * G * sg);
-        }
-      }
+    }
   }
 }
 
