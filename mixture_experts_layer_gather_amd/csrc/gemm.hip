@@ -269,10 +269,25 @@ __device__ __forceinline__ rsrc_t make_rsrc(const void* base, int64_t bytes) {
                                            int(uint32_t(bytes > 0 ? bytes : 0)), 0x00020000);
 }
 // One wave instruction of DMA: every lane's 16 bytes at byte offset voff of
-// the buffer go to LDS at dst + 16 * lane (dst is wave-uniform).
-__device__ __forceinline__ void dma16(rsrc_t r, void* dst, uint32_t voff) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)dst, 16, voff, 0, 0, 0);
+// the buffer described by rsrc go to LDS at dst + 16 * lane (dst is
+// wave-uniform). Issued as inline assembly on purpose: the compiler then does
+// not track it as an LDS write and inserts no wait for it before LDS reads
+// (it cannot tell the transpose-read intrinsic apart from the stage being
+// filled, and would wait for the prefetch of the next K step there). The K
+// loop therefore waits for its DMA explicitly (vmcnt) before each barrier.
+__device__ __forceinline__ u32x4 rsrc_words(const void* base, int64_t bytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  return u32x4{uint32_t(a), uint32_t(a >> 32) & 0xffffu, uint32_t(bytes > 0 ? bytes : 0), 0x00020000u};
 }
+__device__ __forceinline__ void dma16(u32x4 rsrc, void* dst, uint32_t voff) {
+  const uint32_t lds = uint32_t(reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) char*)dst));
+  asm volatile("s_mov_b32 m0, %1\n\tbuffer_load_dwordx4 %0, %2, 0 offen lds"
+               :
+               : "v"(voff), "s"(lds), "s"(rsrc)
+               : "memory", "m0");
+}
+// s_waitcnt vmcnt(0) (expcnt and lgkmcnt left at their maxima)
+__device__ __forceinline__ void wait_vm0() { __builtin_amdgcn_s_waitcnt(0x0f70); }
 
 // Operand tiles in LDS, by layout mode:
 //   LM_KDMA  K-major source, DMA straight from global memory into ROWS rows of
@@ -543,21 +558,27 @@ void gemm_kernel(GemmArgs g) {
     // for a K-major operand the advanced base would otherwise reach into
     // the next row
     const bool live = s < nk;
-    const rsrc_t ar = make_rsrc(a_base + int64_t(s) * a_step, live ? a_end - int64_t(s) * a_step : 0);
-    const rsrc_t br = make_rsrc(b_base + int64_t(s) * b_step, live ? b_end - int64_t(s) * b_step : 0);
+    const char* ab = a_base + int64_t(s) * a_step;
+    const char* bb = b_base + int64_t(s) * b_step;
+    const int64_t an = live ? a_end - int64_t(s) * a_step : 0;
+    const int64_t bn = live ? b_end - int64_t(s) * b_step : 0;
     if constexpr (PA::DMA) {
+      const u32x4 ar = rsrc_words(ab, an);
 #pragma unroll
       for (int j = 0; j < PA::NB; ++j)
         dma16(ar, &st.A[(j * PA::NW + wave) * (1024 / ES)], pa.voff[j]);
     } else {
+      const rsrc_t ar = make_rsrc(ab, an);
 #pragma unroll
       for (int i = 0; i < 4 * PA::NT; ++i) ra[i] = __builtin_amdgcn_raw_buffer_load_b128(ar, pa.voff[i], 0, 0);
     }
     if constexpr (PB::DMA) {
+      const u32x4 br = rsrc_words(bb, bn);
 #pragma unroll
       for (int j = 0; j < PB::NB; ++j)
         dma16(br, &st.B[(j * PB::NW + wave) * (1024 / ES)], pb.voff[j]);
     } else {
+      const rsrc_t br = make_rsrc(bb, bn);
 #pragma unroll
       for (int i = 0; i < 4 * PB::NT; ++i) rb[i] = __builtin_amdgcn_raw_buffer_load_b128(br, pb.voff[i], 0, 0);
     }
@@ -704,17 +725,20 @@ void gemm_kernel(GemmArgs g) {
     const int nk2 = (nk + 1) & ~1;
     issue(st0, 0);
     commit(st0);
+    wait_vm0();
     __syncthreads();
     for (int s = 0; s < nk2; s += 2) {
       issue(st1, s + 1);
       __builtin_amdgcn_sched_barrier(0);
       compute(st0, s);
       commit(st1);
+      wait_vm0();
       __syncthreads();
       issue(st0, s + 2);
       __builtin_amdgcn_sched_barrier(0);
       compute(st1, s + 1);
       commit(st0);
+      wait_vm0();
       __syncthreads();
     }
   }
