@@ -63,6 +63,7 @@ enum { MOE_DTYPE_F32 = 0, MOE_DTYPE_BF16 = 1, MOE_DTYPE_FP8_E4M3 = 2 };
 enum { MOE_SCORE_SOFTMAX = 0, MOE_SCORE_SIGMOID = 1 };
 enum { MOE_GROUP_TOP2_SUM = 0, MOE_GROUP_MAX = 1 };
 enum { MOE_FFN_SWIGLU = 0, MOE_FFN_IDENTITY = 1 };
+enum { MOE_TILE_AUTO = 0, MOE_TILE_SMALL = 1, MOE_TILE_BIG = 2 };
 enum {
     MOE_OP_ROUTE = 0,
     MOE_OP_DISPATCH = 1,
@@ -84,7 +85,13 @@ enum {
  *  quant_block FP8 block edge (128): activations 1 x block, weights
  *              block x block, fp32 scales.
  *  ffn_mode    MOE_FFN_IDENTITY makes every expert the identity (a test mode
- *              of route, dispatch and combine). */
+ *              of route, dispatch and combine).
+ *  gemm_tile   output tile of the bf16 expert GEMMs: MOE_TILE_AUTO picks per
+ *              GEMM from the shapes (see DESIGN notes in gemm.hip);
+ *              MOE_TILE_SMALL forces 128 x 128; MOE_TILE_BIG forces
+ *              256 x 256 wherever the dimensions are multiples of 256.
+ *              Results do not depend on it beyond rounding order: it exists
+ *              for tuning and to test every kernel variant. */
 typedef struct moe_config {
     int64_t num_tokens;  /* T */
     int64_t hidden;      /* d, a multiple of 128 */
@@ -101,6 +108,7 @@ typedef struct moe_config {
     int32_t weight_dtype; /* act_dtype, or MOE_DTYPE_FP8_E4M3 with bf16 act */
     int32_t quant_block;  /* 128 */
     int32_t ffn_mode;
+    int32_t gemm_tile;   /* MOE_TILE_*, 0 by default */
 } moe_config;
 
 /* Bytes of workspace the call `op` (MOE_OP_*) needs for this configuration;

@@ -51,15 +51,18 @@ class MoeConfig(ctypes.Structure):
         ("weight_dtype", ctypes.c_int32),
         ("quant_block", ctypes.c_int32),
         ("ffn_mode", ctypes.c_int32),
+        ("gemm_tile", ctypes.c_int32),
     ]
+
+TILE = {"auto": 0, "small": 1, "big": 2}
 
 
 def make_config(T, d, E, k, f, score="softmax", renorm=True, gate_scale=1.0, num_groups=1,
                 topk_groups=1, group_score="top2_sum", act="bf16", weight="bf16",
-                quant_block=128, identity=False, **_ignored) -> MoeConfig:
+                quant_block=128, identity=False, gemm_tile="auto", **_ignored) -> MoeConfig:
     return MoeConfig(T, d, E, k, f, SCORE[score], int(bool(renorm)), float(gate_scale),
                      num_groups, topk_groups, GROUP_SCORE[group_score], DTYPE[act], DTYPE[weight],
-                     quant_block, 1 if identity else 0)
+                     quant_block, 1 if identity else 0, TILE[gemm_tile])
 
 
 _lib = None

@@ -907,6 +907,7 @@ static int rows_tile_bound(int64_t A, int64_t G, int BM) {
   return int((A + G * (BM - 1)) / BM);
 }
 
+
 template <typename C, typename TC, bool AK, bool BKm, int MODE, int EPI>
 static void run_gemm(GemmArgs g, int tiles, hipStream_t st) {
   if (tiles <= 0) return;
@@ -914,11 +915,22 @@ static void run_gemm(GemmArgs g, int tiles, hipStream_t st) {
       <<<padded_grid(tiles), C::WM * C::WN * 64, 0, st>>>(g);
 }
 
-// The big tile pays off when experts hold many rows (it halves LDS traffic
-// per flop); with few rows per expert most of its rows would be padding.
-static bool use_big(int64_t A, int64_t E, int64_t n_dim, int64_t m_dim = 256) {
-  return A >= 512 * E && n_dim % 256 == 0 && m_dim % 256 == 0;
+// Tile choice for the row-grouped GEMMs. The big tile halves operand traffic
+// per flop but pads each expert's rows to a multiple of 256 and makes a
+// quarter as many tiles: it is used when experts hold many rows (padding at
+// most about half the rows) and the grid still has at least four rounds of
+// tiles for the 256 CUs (measured: with two rounds of long-K tiles the
+// ragged last round costs more than the big tile saves).
+static int rows_tile_bound(int64_t A, int64_t G, int BM);
+// `tile` (MOE_TILE_*: 0 auto, 1 small, 2 big) overrides the choice.
+static bool big_rows(int tile, int64_t A, int64_t E, int64_t n_dim) {
+  if (n_dim % 256 != 0 || tile == 1) return false;
+  if (tile == 2) return true;
+  return A >= 512 * E && int64_t(rows_tile_bound(A, E, 256)) * (n_dim / 256) >= 4 * 256;
 }
+// Weight gradients tile the (M, N) = weight shape of every expert, whatever
+// its rows: the big tile whenever the weight shape allows.
+static bool big_wgrad(int tile, int64_t d, int64_t f) { return tile != 1 && d % 256 == 0 && f % 256 == 0; }
 
 template <typename T>
 __global__ void copy_kernel(const T* __restrict__ src, T* __restrict__ dst, int64_t n) {
@@ -981,28 +993,31 @@ size_t ffn_ws_bytes(int64_t A, int64_t d, int64_t f, int act_bytes, bool fp8, bo
   return ffn_ws(A, d, f, act_bytes, fp8, bwd).total;
 }
 
-// GEMM1 (+ SwiGLU) with config C1, GEMM2 with C2.
-template <typename C1, typename C2>
-static void ffn_fwd_t(const FfnLaunch& a, hipStream_t st) {
-  typedef typename C1::type T;
-  // GEMM1 + SwiGLU
+// GEMM1 (+ SwiGLU): GU = X W1^T, H = silu(G) * U
+template <typename C>
+static void gemm1_fwd(const FfnLaunch& a, hipStream_t st) {
+  typedef typename C::type T;
   GemmArgs g1{};
   g1.A = a.x_perm; g1.lda = a.d;
   g1.B = a.w1; g1.ldb = a.d; g1.b_gstride = 2 * a.f * a.d;
   g1.offsets = a.offsets; g1.G = int(a.E);
   g1.N = int(2 * a.f); g1.K = int(a.d); g1.f = int(a.f);
   g1.aux0 = a.act_gu; g1.aux1 = a.act_h;
-  g1.tiles_n = int(2 * a.f / C1::BN);
-  run_gemm<C1, T, true, true, G_ROWS, EPI_SWIGLU>(g1, rows_tile_bound(a.A, a.E, C1::BM) * g1.tiles_n, st);
-  // GEMM2
+  g1.tiles_n = int(2 * a.f / C::BN);
+  run_gemm<C, T, true, true, G_ROWS, EPI_SWIGLU>(g1, rows_tile_bound(a.A, a.E, C::BM) * g1.tiles_n, st);
+}
+// GEMM2: O = H W2^T
+template <typename C>
+static void gemm2_fwd(const FfnLaunch& a, hipStream_t st) {
+  typedef typename C::type T;
   GemmArgs g2{};
   g2.A = a.act_h; g2.lda = a.f;
   g2.B = a.w2; g2.ldb = a.f; g2.b_gstride = a.d * a.f;
   g2.C = a.out_perm; g2.ldc = a.d;
   g2.offsets = a.offsets; g2.G = int(a.E);
   g2.N = int(a.d); g2.K = int(a.f);
-  g2.tiles_n = int(a.d / C2::BN);
-  run_gemm<C2, T, true, true, G_ROWS, EPI_STORE>(g2, rows_tile_bound(a.A, a.E, C2::BM) * g2.tiles_n, st);
+  g2.tiles_n = int(a.d / C::BN);
+  run_gemm<C, T, true, true, G_ROWS, EPI_STORE>(g2, rows_tile_bound(a.A, a.E, C::BM) * g2.tiles_n, st);
 }
 
 static void ffn_fwd_fp8(const FfnLaunch& a, hipStream_t st) {
@@ -1060,20 +1075,18 @@ static void wgrad_t(const void* d_out, const void* act_h, const void* d_gu, cons
 }
 
 template <typename TC16>
-static void wgrad_any(const void* d_out, const void* act_h, const void* d_gu, const void* x, void* dw1,
-                      void* dw2, const int32_t* offsets, int64_t A, int64_t d, int64_t f, int64_t E,
-                      hipStream_t st) {
-  if (use_big(A, E, d, f) && use_big(A, E, f, d) && (2 * f) % 256 == 0)
+static void wgrad_any(int tile, const void* d_out, const void* act_h, const void* d_gu, const void* x, void* dw1,
+                      void* dw2, const int32_t* offsets, int64_t d, int64_t f, int64_t E, hipStream_t st) {
+  if (big_wgrad(tile, d, f))
     wgrad_t<BigCfg, TC16>(d_out, act_h, d_gu, x, dw1, dw2, offsets, d, f, E, st);
   else
     wgrad_t<SmallCfg<bf16_t>, TC16>(d_out, act_h, d_gu, x, dw1, dw2, offsets, d, f, E, st);
 }
 
-// dH = dO W2 (+ SwiGLU backward) with config C1, dX = dGU W1 with C2.
-template <typename C1, typename C2>
-static void dgrad_t(const FfnBwdLaunch& a, void* d_gu, hipStream_t st) {
-  typedef typename C1::type T;
-  // dH = dO W2, fused SwiGLU backward -> dGU
+// dH = dO W2, fused SwiGLU backward -> dGU
+template <typename C>
+static void dh_bwd(const FfnBwdLaunch& a, void* d_gu, hipStream_t st) {
+  typedef typename C::type T;
   GemmArgs g1{};
   g1.A = a.d_out; g1.lda = a.d;
   g1.B = a.w2; g1.ldb = a.f; g1.b_gstride = a.d * a.f;
@@ -1081,17 +1094,21 @@ static void dgrad_t(const FfnBwdLaunch& a, void* d_gu, hipStream_t st) {
   g1.offsets = a.offsets; g1.G = int(a.E);
   g1.N = int(a.f); g1.K = int(a.d); g1.f = int(a.f);
   g1.aux0 = const_cast<void*>(a.act_gu);
-  g1.tiles_n = int(a.f / C1::BN);
-  run_gemm<C1, T, true, false, G_ROWS, EPI_DSWIGLU>(g1, rows_tile_bound(a.A, a.E, C1::BM) * g1.tiles_n, st);
-  // dX = dGU W1
+  g1.tiles_n = int(a.f / C::BN);
+  run_gemm<C, T, true, false, G_ROWS, EPI_DSWIGLU>(g1, rows_tile_bound(a.A, a.E, C::BM) * g1.tiles_n, st);
+}
+// dX = dGU W1
+template <typename C>
+static void dx_bwd(const FfnBwdLaunch& a, const void* d_gu, hipStream_t st) {
+  typedef typename C::type T;
   GemmArgs g2{};
   g2.A = d_gu; g2.lda = 2 * a.f;
   g2.B = a.w1; g2.ldb = a.d; g2.b_gstride = 2 * a.f * a.d;
   g2.C = a.dx_perm; g2.ldc = a.d;
   g2.offsets = a.offsets; g2.G = int(a.E);
   g2.N = int(a.d); g2.K = int(2 * a.f);
-  g2.tiles_n = int(a.d / C2::BN);
-  run_gemm<C2, T, true, false, G_ROWS, EPI_STORE>(g2, rows_tile_bound(a.A, a.E, C2::BM) * g2.tiles_n, st);
+  g2.tiles_n = int(a.d / C::BN);
+  run_gemm<C, T, true, false, G_ROWS, EPI_STORE>(g2, rows_tile_bound(a.A, a.E, C::BM) * g2.tiles_n, st);
 }
 
 template <typename T>
@@ -1099,13 +1116,14 @@ static void ffn_bwd_t(const FfnBwdLaunch& a, hipStream_t st) {
   const FfnWs w = ffn_ws(a.A, a.d, a.f, int(sizeof(T)), false, true);
   void* d_gu = static_cast<char*>(a.ws) + w.d_gu;
   if constexpr (sizeof(T) == 2) {
-    // measured on the Mixtral-style layer: the big tile wins for dH, the
-    // small one for dX (its B operand is transposed on the way into LDS)
-    if (use_big(a.A, a.E, a.f)) dgrad_t<BigCfg, SmallCfg<bf16_t>>(a, d_gu, st);
-    else dgrad_t<SmallCfg<bf16_t>, SmallCfg<bf16_t>>(a, d_gu, st);
-    wgrad_any<bf16_t>(a.d_out, a.act_h, d_gu, a.x_perm, a.dw1, a.dw2, a.offsets, a.A, a.d, a.f, a.E, st);
+    if (big_rows(a.tile, a.A, a.E, a.f)) dh_bwd<BigCfg>(a, d_gu, st);
+    else dh_bwd<SmallCfg<bf16_t>>(a, d_gu, st);
+    if (big_rows(a.tile, a.A, a.E, a.d)) dx_bwd<BigCfg>(a, d_gu, st);
+    else dx_bwd<SmallCfg<bf16_t>>(a, d_gu, st);
+    wgrad_any<bf16_t>(a.tile, a.d_out, a.act_h, d_gu, a.x_perm, a.dw1, a.dw2, a.offsets, a.d, a.f, a.E, st);
   } else {
-    dgrad_t<SmallCfg<float>, SmallCfg<float>>(a, d_gu, st);
+    dh_bwd<SmallCfg<float>>(a, d_gu, st);
+    dx_bwd<SmallCfg<float>>(a, d_gu, st);
     wgrad_t<SmallCfg<float>, float>(a.d_out, a.act_h, d_gu, a.x_perm, a.dw1, a.dw2, a.offsets, a.d, a.f,
                                      a.E, st);
   }
@@ -1156,7 +1174,7 @@ static void ffn_bwd_fp8(const FfnBwdLaunch& a, hipStream_t st) {
   // weight gradients in bf16 on dequantised X and H
   dequant_rows(reinterpret_cast<const uint8_t*>(a.x_perm), a.x_scale, a.A, a.d, xd, st);
   dequant_rows(reinterpret_cast<const uint8_t*>(a.act_h), a.h_scale, a.A, a.f, hd, st);
-  wgrad_any<bf16_t>(a.d_out, hd, d_gu, xd, a.dw1, a.dw2, a.offsets, a.A, a.d, a.f, a.E, st);
+  wgrad_any<bf16_t>(a.tile, a.d_out, hd, d_gu, xd, a.dw1, a.dw2, a.offsets, a.d, a.f, a.E, st);
 }
 
 void launch_grouped_ffn(const FfnLaunch& a, hipStream_t st) {
@@ -1166,11 +1184,13 @@ void launch_grouped_ffn(const FfnLaunch& a, hipStream_t st) {
   }
   if (a.wt == 2) ffn_fwd_fp8(a, st);
   else if (a.wt == 1) {
-    // measured: the big tile wins for GEMM1 (N = 2f), the small one for GEMM2
-    if (use_big(a.A, a.E, 2 * a.f)) ffn_fwd_t<BigCfg, SmallCfg<bf16_t>>(a, st);
-    else ffn_fwd_t<SmallCfg<bf16_t>, SmallCfg<bf16_t>>(a, st);
+    if (big_rows(a.tile, a.A, a.E, 2 * a.f)) gemm1_fwd<BigCfg>(a, st);
+    else gemm1_fwd<SmallCfg<bf16_t>>(a, st);
+    if (big_rows(a.tile, a.A, a.E, a.d)) gemm2_fwd<BigCfg>(a, st);
+    else gemm2_fwd<SmallCfg<bf16_t>>(a, st);
   } else {
-    ffn_fwd_t<SmallCfg<float>, SmallCfg<float>>(a, st);
+    gemm1_fwd<SmallCfg<float>>(a, st);
+    gemm2_fwd<SmallCfg<float>>(a, st);
   }
 }
 

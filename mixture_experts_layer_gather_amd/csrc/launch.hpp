@@ -101,6 +101,7 @@ struct FfnLaunch {
   int act;   // 0 f32, 1 bf16
   int wt;    // 0 f32, 1 bf16, 2 fp8
   bool identity;
+  int tile;  // MOE_TILE_*
 };
 void launch_grouped_ffn(const FfnLaunch& a, hipStream_t st);
 // Workspace bytes of the grouped FFN forward (bwd = false) or backward.
@@ -129,6 +130,7 @@ struct FfnBwdLaunch {
   int act;
   int wt;
   bool identity;
+  int tile;  // MOE_TILE_*
 };
 void launch_grouped_ffn_bwd(const FfnBwdLaunch& a, hipStream_t st);
 

@@ -39,6 +39,7 @@ int check_cfg(const moe_config* c) {
     if (int64_t(c->topk_groups) * (c->num_experts / c->num_groups) < c->top_k) return MOE_ERR_INVALID_ARG;
   }
   if (c->ffn_mode != MOE_FFN_SWIGLU && c->ffn_mode != MOE_FFN_IDENTITY) return MOE_ERR_INVALID_ARG;
+  if (c->gemm_tile < MOE_TILE_AUTO || c->gemm_tile > MOE_TILE_BIG) return MOE_ERR_INVALID_ARG;
   if (c->act_dtype != MOE_DTYPE_F32 && c->act_dtype != MOE_DTYPE_BF16) return MOE_ERR_UNSUPPORTED_DTYPE;
   if (c->weight_dtype == MOE_DTYPE_FP8_E4M3) {
     if (c->act_dtype != MOE_DTYPE_BF16) return MOE_ERR_UNSUPPORTED_DTYPE;
@@ -185,6 +186,7 @@ int moe_grouped_ffn(const moe_config* cfg, const void* x_perm, const float* x_sc
   a.act = cfg->act_dtype == MOE_DTYPE_BF16 ? 1 : 0;
   a.wt = cfg->weight_dtype == MOE_DTYPE_F32 ? 0 : (cfg->weight_dtype == MOE_DTYPE_BF16 ? 1 : 2);
   a.identity = identity;
+  a.tile = cfg->gemm_tile;
   moe::launch_grouped_ffn(a, static_cast<hipStream_t>(stream));
   return launched();
 }
@@ -251,6 +253,7 @@ int moe_grouped_ffn_bwd(const moe_config* cfg, const void* x_perm, const float* 
   a.act = cfg->act_dtype == MOE_DTYPE_BF16 ? 1 : 0;
   a.wt = cfg->weight_dtype == MOE_DTYPE_F32 ? 0 : (cfg->weight_dtype == MOE_DTYPE_BF16 ? 1 : 2);
   a.identity = identity;
+  a.tile = cfg->gemm_tile;
   moe::launch_grouped_ffn_bwd(a, static_cast<hipStream_t>(stream));
   return launched();
 }

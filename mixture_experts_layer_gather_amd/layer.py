@@ -21,7 +21,7 @@ _TORCH = {"f32": torch.float32, "bf16": torch.bfloat16}
 class MoELayer:
     def __init__(self, T, d, E, k, f, shared=0, score="softmax", renorm=True, gate_scale=1.0,
                  num_groups=1, topk_groups=1, group_score="top2_sum", act="bf16", weight="bf16",
-                 quant_block=128, identity=False, device="cuda", **_ignored):
+                 quant_block=128, identity=False, gemm_tile="auto", device="cuda", **_ignored):
         self.T, self.d, self.E, self.k, self.f = T, d, E, k, f
         self.A = T * k
         self.shared = int(shared)
@@ -30,10 +30,10 @@ class MoELayer:
         self.qb = quant_block
         kw = dict(score=score, renorm=renorm, gate_scale=gate_scale, num_groups=num_groups,
                   topk_groups=topk_groups, group_score=group_score, act=act, weight=weight,
-                  quant_block=quant_block, identity=identity)
+                  quant_block=quant_block, identity=identity, gemm_tile=gemm_tile)
         self.cfg = L.make_config(T, d, E, k, f, **kw)
         self.scfg = L.make_config(T, d, 1, 1, f, act=act, weight=weight, quant_block=quant_block,
-                                  identity=identity)
+                                  identity=identity, gemm_tile=gemm_tile)
         dev = torch.device(device)
         at = _TORCH[act]
         pt = torch.float32 if weight == "f32" else torch.bfloat16   # parameter dtype

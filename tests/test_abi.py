@@ -63,6 +63,10 @@ def test_config_validation(M):
     assert _route(M, _cfg(M, act="f32", weight="bf16")) == -2
     assert _route(M, _cfg(M, act="f32", weight="fp8")) == -2
     assert _route(M, _cfg(M, weight="fp8", quant_block=64)) == -1
+    for tile in (-1, 3):  # MOE_TILE_* is 0, 1 or 2
+        c = _cfg(M)
+        c.gemm_tile = tile
+        assert _route(M, c) == -1, tile
     assert L.moe_workspace_size(ctypes.byref(_cfg(M, k=9)), 1) == 0
 
 

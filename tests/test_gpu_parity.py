@@ -48,9 +48,9 @@ def _inputs(cfg, threads=8):
     return inp
 
 
-def _gpu_layer(cfg, inp, identity=False):
+def _gpu_layer(cfg, inp, identity=False, gemm_tile="auto"):
     from mixture_experts_layer_gather_amd import MoELayer
-    layer = MoELayer(**cfg.describe(), identity=identity, device=DEV)
+    layer = MoELayer(**cfg.describe(), identity=identity, gemm_tile=gemm_tile, device=DEV)
     cu = lambda t: None if t is None else t.to(DEV)
     layer.set_weights(cu(inp["wr"]), cu(inp["w1"]), cu(inp["w2"]), bias=cu(inp.get("bias")),
                       sw1=cu(inp.get("sw1")), sw2=cu(inp.get("sw2")))
@@ -71,10 +71,11 @@ def _check_routing_and_dispatch(cfg, layer, ref):
     assert oracle.rel_l2(_np(layer.topk_gate), ref["gates"]) <= 1e-6, "gates"
 
 
-def _compare_small(cfg, identity=False, inp=None):
+def _compare_small(cfg, identity=False, inp=None, gemm_tile="auto"):
     inp = inp or _inputs(cfg)
-    _say(f"[parity] {cfg.name} T={cfg.T} d={cfg.d} E={cfg.E} k={cfg.k} f={cfg.f} id={identity}")
-    layer = _gpu_layer(cfg, inp, identity)
+    _say(f"[parity] {cfg.name} T={cfg.T} d={cfg.d} E={cfg.E} k={cfg.k} f={cfg.f} id={identity} "
+         f"tile={gemm_tile}")
+    layer = _gpu_layer(cfg, inp, identity, gemm_tile)
     ref = oracle.layer(cfg, inp, identity=identity)
     _check_routing_and_dispatch(cfg, layer, ref)
     if cfg.weight == "fp8":
@@ -115,18 +116,31 @@ def _compare_small(cfg, identity=False, inp=None):
 SMALL = {
     "tiny_fp32": S.CONFIGS[0],
     "mixtral_mini": S.mini(S.CONFIGS[1], T=1000, d=256, f=384),
-    # >= 512 rows per expert and 256-multiple widths: the 256 x 256 tile path
+    # >= 512 rows per expert and 256-multiple widths, run with the 256 x 256
+    # tile forced on every GEMM (too few tiles for the shape-based choice)
     "mixtral_mini_bigtile": S.mini(S.CONFIGS[1], T=2304, d=512, f=512, seed_base=33),
     "mixtral_mini_f32": S.mini(S.CONFIGS[1], T=333, d=128, f=256).replace(act="f32", weight="f32"),
     "deepseek_mini": S.mini(S.CONFIGS[2], T=300, d=256, f=256, E=32).replace(k=6),
     "qwen_skew_mini": S.mini(S.CONFIGS[3], T=700, d=256, f=128, E=16).replace(k=4),
+    # 256 x 256 tiles forced where the widths allow (GEMM1, GEMM2 and dX; f =
+    # 128 keeps dH and the weight gradients on 128 x 128): mixed tile sizes
+    # and ragged groups smaller than a tile
+    "qwen_skew_mini_big": S.mini(S.CONFIGS[3], T=700, d=256, f=128, E=16).replace(k=4, seed_base=34),
     "deepseek_fp8_mini": S.mini(S.CONFIGS[4], T=400, d=384, f=256, E=32).replace(k=6),
 }
 
 
+FORCED_TILE = {"mixtral_mini_bigtile": "big", "qwen_skew_mini_big": "big"}
+
+
 @pytest.mark.parametrize("name", list(SMALL))
 def test_small_layer_parity(name):
-    _compare_small(SMALL[name])
+    _compare_small(SMALL[name], gemm_tile=FORCED_TILE.get(name, "auto"))
+
+
+def test_forced_small_tiles():
+    # the 128 x 128 tile on shapes that would take the 256 x 256 one
+    _compare_small(SMALL["mixtral_mini_bigtile"], gemm_tile="small")
 
 
 @pytest.mark.parametrize("name", ["tiny_fp32", "deepseek_mini"])
