@@ -199,25 +199,28 @@ __device__ void find_group(const int32_t* __restrict__ offsets, int G, int tiles
   __syncthreads();
 }
 
-// LDS tiles hold ROWS x BK elements per operand (rows of 128 bytes),
-// K-contiguous, without padding; the eight 16-byte chunks of a row are
-// XOR-swizzled with the row. Measured with the LDS bank-conflict counters on
-// gfx950: the MFMA fragment reads (16 consecutive rows x 4 chunks per
-// instruction) are conflict-free when the swizzle takes row bits 0-2 (and
-// not row bit 3); 16-byte row stores are conflict-free for any swizzle; the
-// transposed 8-byte stores of K-strided operands need rows 8 and 16 apart
-// to differ, which row bits 4-6 provide. So K-major operands (filled by DMA)
-// use row bits 0-2 only, which keeps a fragment's address an immediate
-// offset from the first fragment's, and K-strided operands add row bits 4-6.
-template <bool KMAJ>
+// LDS tiles hold ROWS x BK elements per operand (rows of 128 or 64 bytes),
+// K-contiguous, without padding; the 16-byte chunks of a row are XOR-swizzled
+// with the row. Measured with the LDS bank-conflict counters on gfx950: the
+// MFMA fragment reads (16 consecutive rows x 4 chunks per instruction) of
+// 128-byte rows are conflict-free when the swizzle takes row bits 0-2 (and
+// not row bit 3); for 64-byte rows, row bits 1-2; 16-byte row stores are
+// conflict-free for any swizzle; the transposed 8-byte stores of K-strided
+// operands (128-byte rows only) need rows 8 and 16 apart to differ, which
+// row bits 4-6 provide. So K-major operands (filled by DMA) use the low row
+// bits only, which keeps a fragment's address an immediate offset from the
+// first fragment's, and K-strided operands add row bits 4-6.
+template <bool KMAJ, int NCH>
 __device__ __forceinline__ int lds_swz(int row) {
+  static_assert(NCH == 8 || (NCH == 4 && KMAJ), "128-byte rows, or 64-byte K-major rows");
+  if constexpr (NCH == 4) return (row >> 1) & 3;
   return KMAJ ? (row & 7) : ((row ^ (row >> 4)) & 7);
 }
 template <typename T, int BK, bool KMAJ>
 __device__ __forceinline__ int lds_off(int row, int k) {
   constexpr int VEC = 16 / sizeof(T);
-  static_assert(BK / VEC == 8, "128-byte LDS rows");
-  return row * BK + (((k / VEC) ^ lds_swz<KMAJ>(row)) * VEC) + (k % VEC);
+  constexpr int NCH = BK / VEC;
+  return row * BK + (((k / VEC) ^ lds_swz<KMAJ, NCH>(row)) * VEC) + (k % VEC);
 }
 
 // 4 K-rows x VEC columns (four 16-byte registers) -> VEC LDS rows of 4
@@ -360,17 +363,16 @@ __device__ __forceinline__ u32x2 lds_read_tr16(const void* p) {
       u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(void*)p));
 }
 
-// One LDS stage. The two stages are separate objects so that the compiler
-// can tell the DMA into one from the reads of the other.
+// One LDS stage (operand tiles and FP8 row scales).
 template <typename T, int BM, int BN, int BK, int NTH, bool SCALED>
-struct Stage {
+struct alignas(16) Stage {  // 16-byte multiple: stages sit back to back in one array
   T A[BM * BK];
   T B[BN * BK];
   float SA[SCALED ? (NTH > BM ? NTH : BM) : 1];  // FP8 row scales of the A tile (padded)
 };
 
 template <typename T, typename TC, bool A_KMAJ, bool B_KMAJ, int MODE, int EPI, int BM, int BN,
-          int BK, int WM, int WN, int PF>
+          int BK, int WM, int WN, int NS>
 __global__ __launch_bounds__(WM * WN * 64) __attribute__((amdgpu_waves_per_eu(2)))
 void gemm_kernel(GemmArgs g) {
   constexpr int NTH = WM * WN * 64;
@@ -389,8 +391,11 @@ void gemm_kernel(GemmArgs g) {
   static_assert(!FP8 || (MODE == G_ROWS && A_KMAJ && BK == 128 && BN <= 128 && BM <= 256),
                 "FP8: row-grouped GEMMs, one 128-deep scale block per K step");
 
-  __shared__ __attribute__((aligned(16))) ST st0;
-  __shared__ __attribute__((aligned(16))) ST st1;
+  static_assert(NS >= 2 && NS <= 4, "LDS stages");
+  static_assert(sizeof(ST) % 16 == 0, "stage alignment");
+  __shared__ __attribute__((aligned(16))) ST stv[NS];
+  ST& st0 = stv[0];
+  ST& st1 = stv[1];
   __shared__ int s_scan[8];
   __shared__ int s_info[3];
 
@@ -463,6 +468,8 @@ void gemm_kernel(GemmArgs g) {
   }
 
   // ---- per-thread load plans (offsets are fixed for the whole K loop)
+  constexpr int RB = BK * int(ES);   // bytes per K-major LDS row
+  constexpr int NCH = RB / 16;       // 16-byte chunks per K-major LDS row
   PA pa;
   PB pb;
   // LM_TDMA: K-row kr of the tile holds ROWS elements from column col0; DMA
@@ -476,8 +483,8 @@ void gemm_kernel(GemmArgs g) {
   if constexpr (ALM == LM_KDMA) {
 #pragma unroll
     for (int j = 0; j < PA::NB; ++j) {
-      const int r = (j * PA::NW + wave) * 8 + lane / 8;
-      const int lc = (lane % 8) ^ lds_swz<true>(r);
+      const int r = (j * PA::NW + wave) * (1024 / RB) + lane / NCH;
+      const int lc = (lane % NCH) ^ lds_swz<true, NCH>(r);
       pa.voff[j] = uint32_t(int64_t(r) * g.lda * ES + lc * 16);
     }
   } else if constexpr (ALM == LM_TDMA) {
@@ -498,8 +505,8 @@ void gemm_kernel(GemmArgs g) {
   if constexpr (BLM == LM_KDMA) {
 #pragma unroll
     for (int j = 0; j < PB::NB; ++j) {
-      const int r = (j * PB::NW + wave) * 8 + lane / 8;
-      const int lc = (lane % 8) ^ lds_swz<true>(r);
+      const int r = (j * PB::NW + wave) * (1024 / RB) + lane / NCH;
+      const int lc = (lane % NCH) ^ lds_swz<true, NCH>(r);
       int grow = n0 + r;
       if (EPI == EPI_SWIGLU) {
         // gate and up rows of the same output columns side by side within
@@ -714,30 +721,57 @@ void gemm_kernel(GemmArgs g) {
     }
   };
 
-  // K loop over two LDS stages: the loads of step s + 1 are issued before
-  // the MFMAs of step s and land (DMA, or registers written to LDS) before
-  // the barrier that ends step s. Unrolled by two so that every access names
-  // its stage statically, over an even number of steps so that the loop has
-  // one exit: the step past the end (odd step counts) and the prefetch past
-  // the last step read outside their descriptors' ranges, i.e. zeros, and
-  // touch no memory.
-  if (nk > 0) {
-    const int nk2 = (nk + 1) & ~1;
-    issue(st0, 0);
-    commit(st0);
-    wait_vm0();
-    __syncthreads();
-    for (int s = 0; s < nk2; s += 2) {
-      issue(st1, s + 1);
-      __builtin_amdgcn_sched_barrier(0);
-      compute(st0, s);
-      commit(st1);
+  // K loop. Two stages: the loads of step s + 1 are issued before the MFMAs
+  // of step s and land (DMA, or registers written to LDS) before the barrier
+  // that ends step s; unrolled by two over an even number of steps so that
+  // the loop has one exit and no conditional loads (the step past the end
+  // of odd step counts and the prefetch past the last step read outside
+  // their descriptors' ranges, i.e. zeros, and touch no memory).
+  // NS > 2 stages (DMA operands only): the loads of step s + NS - 1 are
+  // issued at step s, and the barrier that ends step s waits only for step
+  // s + 1 to land, so NS - 1 steps of loads are in flight.
+  if constexpr (NS == 2) {
+    if (nk > 0) {
+      const int nk2 = (nk + 1) & ~1;
+      issue(st0, 0);
+      commit(st0);
       wait_vm0();
       __syncthreads();
-      issue(st0, s + 2);
-      __builtin_amdgcn_sched_barrier(0);
-      compute(st1, s + 1);
-      commit(st0);
+      for (int s = 0; s < nk2; s += 2) {
+        issue(st1, s + 1);
+        __builtin_amdgcn_sched_barrier(0);
+        compute(st0, s);
+        commit(st1);
+        wait_vm0();
+        __syncthreads();
+        issue(st0, s + 2);
+        __builtin_amdgcn_sched_barrier(0);
+        compute(st1, s + 1);
+        commit(st0);
+        wait_vm0();
+        __syncthreads();
+      }
+    }
+  } else {
+    static_assert(PA::DMA && PB::DMA && !FP8, "deep pipelines take DMA operands only");
+    constexpr int NDMA = PA::NB + PB::NB;  // DMA instructions per wave and step
+    constexpr int LEFT = NDMA * (NS - 2);  // may stay in flight at a step's end
+    static_assert(LEFT < 64, "vmcnt range");
+    constexpr int WAIT = (LEFT & 15) | ((LEFT >> 4) << 14) | (7 << 4) | (15 << 8);
+    if (nk > 0) {
+#pragma unroll
+      for (int p = 0; p < NS - 1; ++p) issue(stv[p], p);
+      __builtin_amdgcn_s_waitcnt(WAIT);
+      __syncthreads();
+      for (int s = 0; s < nk; ++s) {
+        issue(stv[(s + NS - 1) % NS], s + NS - 1);
+        __builtin_amdgcn_sched_barrier(0);
+        compute(stv[s % NS], s);
+        __builtin_amdgcn_s_waitcnt(WAIT);
+        __syncthreads();
+      }
+      // the last prefetches (zeros) may still be landing: the epilogue
+      // reuses their LDS
       wait_vm0();
       __syncthreads();
     }
@@ -752,8 +786,8 @@ void gemm_kernel(GemmArgs g) {
   // needed between its writes and reads.
   constexpr int EP = WTN + 4;          // floats per staged row (pad: no bank conflicts)
   constexpr int UPR = WTN / 8;         // 8-column units per staged row
-  static_assert(int(sizeof(ST)) >= NTH / 64 * 16 * EP * 4, "staging fits in one LDS stage");
-  float* stg = reinterpret_cast<float*>(&st0) + wave * 16 * EP;
+  static_assert(int(sizeof(ST)) * NS >= NTH / 64 * 16 * EP * 4, "staging fits in the LDS stages");
+  float* stg = reinterpret_cast<float*>(stv) + wave * 16 * EP;
   TC* Cb = reinterpret_cast<TC*>(g.C);
   if (MODE == G_KSPLIT) Cb += int64_t(grp) * g.c_gstride;
 #pragma unroll
@@ -888,20 +922,27 @@ static void dequant_rows(const uint8_t* q, const float* scale, int64_t rows, int
 }
 
 // ---------------------------------------------------------------------------
-// Tile configurations: BM x BN output tile, BK deep, WM x WN waves.
-//   Small: 128 x 128, 4 waves of 64 x 64 (every dtype; few rows per expert)
-//   Big:   256 x 256, 8 waves of 128 x 64 (bf16, >= 512 rows per expert):
-//          half the LDS bytes per flop of Small and a quarter of the tiles
-template <typename T, int BM_, int BN_, int BK_, int WM_, int WN_, int PF_>
+// Tile configurations: BM x BN output tile, BK deep, WM x WN waves, NS LDS
+// stages.
+//   Small: 128 x 128, 4 waves of 64 x 64, 2 stages of 32 KB (every dtype;
+//          two workgroups per CU hide each other's load latency)
+//   Big:   256 x 256, 8 waves of 128 x 64, 2 stages of 64 KB: half the
+//          operand bytes per flop of Small and a quarter of the tiles
+//   Wgrad: Big's tile with 4 stages of 32 KB (BK = 32) for the weight
+//          gradients, whose K (an expert's rows) is often short: three K
+//          steps of loads in flight and a shorter prologue (measured: 2
+//          stages are faster for the long-K row-grouped GEMMs)
+template <typename T, int BM_, int BN_, int BK_, int WM_, int WN_, int NS_>
 struct Cfg {
   typedef T type;
-  static constexpr int BM = BM_, BN = BN_, BK = BK_, WM = WM_, WN = WN_, PF = PF_;
+  static constexpr int BM = BM_, BN = BN_, BK = BK_, WM = WM_, WN = WN_, NS = NS_;
 };
 template <typename T> struct SmallCfg;
-template <> struct SmallCfg<bf16_t> : Cfg<bf16_t, 128, 128, 64, 2, 2, 1> {};
-template <> struct SmallCfg<float> : Cfg<float, 128, 128, 32, 2, 2, 1> {};
-template <> struct SmallCfg<fp8_t> : Cfg<fp8_t, 128, 128, 128, 2, 2, 1> {};
-typedef Cfg<bf16_t, 256, 256, 64, 2, 4, 1> BigCfg;
+template <> struct SmallCfg<bf16_t> : Cfg<bf16_t, 128, 128, 64, 2, 2, 2> {};
+template <> struct SmallCfg<float> : Cfg<float, 128, 128, 32, 2, 2, 2> {};
+template <> struct SmallCfg<fp8_t> : Cfg<fp8_t, 128, 128, 128, 2, 2, 2> {};
+typedef Cfg<bf16_t, 256, 256, 64, 2, 4, 2> BigCfg;
+typedef Cfg<bf16_t, 256, 256, 32, 2, 4, 4> WgradCfg;
 
 static int rows_tile_bound(int64_t A, int64_t G, int BM) {
   return int((A + G * (BM - 1)) / BM);
@@ -911,7 +952,7 @@ static int rows_tile_bound(int64_t A, int64_t G, int BM) {
 template <typename C, typename TC, bool AK, bool BKm, int MODE, int EPI>
 static void run_gemm(GemmArgs g, int tiles, hipStream_t st) {
   if (tiles <= 0) return;
-  gemm_kernel<typename C::type, TC, AK, BKm, MODE, EPI, C::BM, C::BN, C::BK, C::WM, C::WN, C::PF>
+  gemm_kernel<typename C::type, TC, AK, BKm, MODE, EPI, C::BM, C::BN, C::BK, C::WM, C::WN, C::NS>
       <<<padded_grid(tiles), C::WM * C::WN * 64, 0, st>>>(g);
 }
 
@@ -1078,7 +1119,7 @@ template <typename TC16>
 static void wgrad_any(int tile, const void* d_out, const void* act_h, const void* d_gu, const void* x, void* dw1,
                       void* dw2, const int32_t* offsets, int64_t d, int64_t f, int64_t E, hipStream_t st) {
   if (big_wgrad(tile, d, f))
-    wgrad_t<BigCfg, TC16>(d_out, act_h, d_gu, x, dw1, dw2, offsets, d, f, E, st);
+    wgrad_t<WgradCfg, TC16>(d_out, act_h, d_gu, x, dw1, dw2, offsets, d, f, E, st);
   else
     wgrad_t<SmallCfg<bf16_t>, TC16>(d_out, act_h, d_gu, x, dw1, dw2, offsets, d, f, E, st);
 }
