@@ -74,6 +74,28 @@ def summarize_profiles(cfg_name, stats_dir, fetch_dir, write_dir, copy_fetch_dir
         lines.append(f"| {float(r['AverageNs']) / 1e3:.1f} | {r['Calls']} | "
                      f"{100 * float(r['TotalDurationNs']) / tot:.1f} | `{r['Name'][:140]}` |")
 
+    # library calls: GEMM kernels by role, per step (steps = GEMM1 launches)
+    role_ns = collections.defaultdict(float)
+    role_calls = collections.defaultdict(int)
+    for r in stats:
+        role = kernel_role(r["Name"])
+        if role:
+            role_ns[role] += float(r["TotalDurationNs"])
+            role_calls[role] += int(r["Calls"])
+    steps = max(1, role_calls.get("gemm1", 1))
+    lines += ["", "## Library calls per step (sum of their GEMM kernels)", "",
+              f"Steps in the trace: {steps} (warm-up included).", "",
+              "| call | ms per step | kernels (avg us x launches per step) |", "|---|---:|---|"]
+    by_call = collections.defaultdict(list)
+    for role in ("gemm1", "gemm2", "dh", "dx", "wgrad"):
+        if role in role_ns:
+            by_call[ROLE_CALL[role]].append(role)
+    for call, rs in by_call.items():
+        ms = sum(role_ns[x] for x in rs) / steps / 1e6
+        parts = ", ".join(f"{x} {role_ns[x] / role_calls[x] / 1e3:.0f} x {role_calls[x] / steps:g}"
+                          for x in rs)
+        lines.append(f"| {call} | {ms:.3f} | {parts} |")
+
     def per_kernel(d):
         agg = collections.defaultdict(list)
         for r in csv.DictReader(open(os.path.join(d, "run_counter_collection.csv"))):

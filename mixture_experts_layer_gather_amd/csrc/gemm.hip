@@ -426,9 +426,14 @@ void gemm_kernel(GemmArgs g) {
     const int per = g.tiles_m * g.tiles_n;
     grp = tile / per;
     if (grp >= g.G) return;  // padding of the grid
+    // bands of 8 row tiles, row tile fastest: 64 consecutive tiles (one
+    // XCD's share) cover 8 x 8 tiles and share each A and B panel 8 times
     const int rem = tile % per;
-    mt = rem / g.tiles_n;
-    nt = rem % g.tiles_n;
+    const int band = rem / (8 * g.tiles_n);
+    const int in_band = min(8, g.tiles_m - band * 8);
+    const int idx = rem - band * 8 * g.tiles_n;
+    mt = band * 8 + idx % in_band;
+    nt = idx / in_band;
     row0 = 0;
     mrows = BM;
     kbase = g.offsets[grp];
