@@ -155,6 +155,128 @@ static void launch_vgemm(VArgs a, hipStream_t st, int zsplit = 1) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// Router logits L[t][e] = (sum_i x[t][i] w[e][i]) + bias[e], each output its
+// own fp32 FMA recurrence over i = 0 .. d-1 in ascending order (the same
+// order as vgemm_kernel, so results are bit-identical), built for latency
+// hiding at low occupancy: a block holds 64 tokens x 64 experts, a thread
+// 4 x 4 independent recurrences; LDS rows are K-contiguous (pitch 36 floats)
+// and read 4 hidden values at a time; the next 32-wide hidden chunk is
+// fetched with 16-byte global loads into registers while the current one is
+// consumed, and LDS is double-buffered. Expert rows are interleaved by 16
+// across lanes (thread tn owns experts tn + 16 j), which makes the float4
+// reads of the weight tile conflict-free; token rows are shared by 16 lanes
+// (broadcast). d must be a multiple of 32.
+// ---------------------------------------------------------------------------
+constexpr int kLgTM = 64, kLgTN = 64, kLgKC = 32, kLgP = kLgKC + 4;
+
+template <typename TX>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void logits_kernel(const TX* __restrict__ x, const float* __restrict__ w,
+                                                     const float* __restrict__ bias, float* __restrict__ out,
+                                                     int T, int E, int d) {
+  __shared__ __attribute__((aligned(16))) float As[2][kLgTM * kLgP];
+  __shared__ __attribute__((aligned(16))) float Bs[2][kLgTN * kLgP];
+  const int tid = threadIdx.x;
+  const int t0 = blockIdx.y * kLgTM, e0 = blockIdx.x * kLgTN;
+  const int tm = tid / 16, tn = tid % 16;
+  // global -> register plan. x chunk: 64 rows x 32 values; w chunk: 64 rows x 32 floats
+  constexpr int XV = 16 / sizeof(TX);              // x values per 16-byte load
+  constexpr int XL = kLgTM * kLgKC / XV / 256;     // x loads per thread (1 bf16, 2 f32)
+  int xrow[XL], xk[XL];
+#pragma unroll
+  for (int q = 0; q < XL; ++q) {
+    const int idx = tid + 256 * q;
+    xrow[q] = idx / (kLgKC / XV);
+    xk[q] = (idx % (kLgKC / XV)) * XV;
+  }
+  int wrow[2], wk[2];
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+    const int idx = tid + 256 * q;
+    wrow[q] = idx / (kLgKC / 4);
+    wk[q] = (idx % (kLgKC / 4)) * 4;
+  }
+  const int nch = d / kLgKC;
+  float xv[XL][XV];
+  float4 wv[2];
+  auto gload = [&](int c) {
+    const int k0 = c * kLgKC;
+#pragma unroll
+    for (int q = 0; q < XL; ++q) {
+      const int t = t0 + xrow[q];
+      if (t < T) {
+        Vec16<TX>::load(x + int64_t(t) * d + k0 + xk[q], xv[q]);
+      } else {
+#pragma unroll
+        for (int v = 0; v < XV; ++v) xv[q][v] = 0.0f;
+      }
+    }
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      const int e = e0 + wrow[q];
+      wv[q] = e < E ? *reinterpret_cast<const float4*>(w + int64_t(e) * d + k0 + wk[q])
+                    : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+    }
+  };
+  auto lstore = [&](int buf) {
+#pragma unroll
+    for (int q = 0; q < XL; ++q)
+#pragma unroll
+      for (int v = 0; v < XV; v += 4)
+        *reinterpret_cast<float4*>(&As[buf][xrow[q] * kLgP + xk[q] + v]) =
+            make_float4(xv[q][v], xv[q][v + 1], xv[q][v + 2], xv[q][v + 3]);
+#pragma unroll
+    for (int q = 0; q < 2; ++q) *reinterpret_cast<float4*>(&Bs[buf][wrow[q] * kLgP + wk[q]]) = wv[q];
+  };
+  float acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = 0.0f;
+  auto compute = [&](int buf) {
+#pragma unroll 2
+    for (int k = 0; k < kLgKC; k += 4) {
+      float4 a[4], b[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) a[i] = *reinterpret_cast<const float4*>(&As[buf][(tm + 16 * i) * kLgP + k]);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) b[j] = *reinterpret_cast<const float4*>(&Bs[buf][(tn + 16 * j) * kLgP + k]);
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          acc[i][j] = __builtin_fmaf(a[i].x, b[j].x, acc[i][j]);
+          acc[i][j] = __builtin_fmaf(a[i].y, b[j].y, acc[i][j]);
+          acc[i][j] = __builtin_fmaf(a[i].z, b[j].z, acc[i][j]);
+          acc[i][j] = __builtin_fmaf(a[i].w, b[j].w, acc[i][j]);
+        }
+    }
+  };
+  gload(0);
+  lstore(0);
+  __syncthreads();
+  for (int c = 0; c + 1 < nch; ++c) {
+    gload(c + 1);
+    compute(c & 1);
+    lstore((c + 1) & 1);
+    __syncthreads();
+  }
+  compute((nch - 1) & 1);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int t = t0 + tm + 16 * i;
+    if (t >= T) continue;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int e = e0 + tn + 16 * j;
+      if (e >= E) continue;
+      float v = acc[i][j];
+      if (bias) v = v + bias[e];
+      out[int64_t(t) * E + e] = v;
+    }
+  }
+}
+
 // Token-chunk count of the router weight gradient: enough workgroups to
 // fill the chip, chunks of at least 128 tokens.
 int route_bwd_zsplit(int64_t T, int64_t d, int64_t E) {
@@ -476,13 +598,19 @@ __global__ __launch_bounds__(256) void dlogits_kernel(DLArgs a) {
 // ---------------------------------------------------------------------------
 template <typename TX>
 static void route_fwd_t(const RouteLaunch& r, hipStream_t st) {
-  VArgs v{};
-  v.A = r.x; v.lda = r.d;
-  v.B = r.w_router; v.ldb = r.d;
-  v.C = r.logits; v.ldc = r.E;
-  v.bias = r.bias;
-  v.M = int(r.T); v.N = int(r.E); v.K = int(r.d);
-  launch_vgemm<TX, true, float, true, float, VEPI_STORE>(v, st);
+  if (r.E >= 32) {
+    const dim3 grid(unsigned((r.E + kLgTN - 1) / kLgTN), unsigned((r.T + kLgTM - 1) / kLgTM));
+    logits_kernel<TX><<<grid, 256, 0, st>>>(reinterpret_cast<const TX*>(r.x), r.w_router, r.bias, r.logits,
+                                            int(r.T), int(r.E), int(r.d));
+  } else {
+    VArgs v{};
+    v.A = r.x; v.lda = r.d;
+    v.B = r.w_router; v.ldb = r.d;
+    v.C = r.logits; v.ldc = r.E;
+    v.bias = r.bias;
+    v.M = int(r.T); v.N = int(r.E); v.K = int(r.d);
+    launch_vgemm<TX, true, float, true, float, VEPI_STORE>(v, st);
+  }
 
   SelArgs s{};
   s.logits = r.logits; s.T = int(r.T); s.E = int(r.E); s.k = int(r.k);
