@@ -38,38 +38,55 @@ __global__ __launch_bounds__(256) void dispatch_count_kernel(const int32_t* __re
 
 // --- 2. scan over (chunk, expert) -----------------------------------------
 // chunk_cnt[c][e] becomes the first row of expert e's tokens in chunk c.
+// Thread e owns expert e: its column is read twice with 16 loads in flight
+// (totals, then running bases); the exclusive scan of the totals over the
+// experts runs on wave shuffles. Integer sums: the order does not matter.
 __global__ __launch_bounds__(1024) void dispatch_scan_kernel(int32_t* __restrict__ chunk_cnt,
                                                              int32_t* __restrict__ counts,
                                                              int32_t* __restrict__ offsets,
                                                              int nchunks, int E) {
-  __shared__ int32_t s_tot[1024];
-  __shared__ int32_t s_off[1025];
+  constexpr int B = 16;
+  __shared__ int32_t s_wave[16];
   const int e = threadIdx.x;
-  int32_t run = 0;
+  const int lane = lane_id(), wave = e / kWave;
+  int32_t total = 0;
   if (e < E) {
-    for (int c = 0; c < nchunks; ++c) {
-      const int32_t v = chunk_cnt[int64_t(c) * E + e];
-      chunk_cnt[int64_t(c) * E + e] = run;
-      run += v;
+    for (int c0 = 0; c0 < nchunks; c0 += B) {
+      int32_t v[B];
+#pragma unroll
+      for (int j = 0; j < B; ++j) v[j] = (c0 + j < nchunks) ? chunk_cnt[int64_t(c0 + j) * E + e] : 0;
+#pragma unroll
+      for (int j = 0; j < B; ++j) total += v[j];
     }
-    counts[e] = run;
   }
-  s_tot[e] = (e < E) ? run : 0;
-  __syncthreads();
-  if (e == 0) {  // E <= 1024 values: a short serial exclusive scan
-    int32_t acc = 0;
-    for (int i = 0; i < E; ++i) {
-      s_off[i] = acc;
-      acc += s_tot[i];
-    }
-    s_off[E] = acc;
+  // inclusive scan of the totals within each wave, then across waves
+  int32_t inc = total;
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) {
+    const int32_t u = __shfl_up(inc, o, kWave);
+    if (lane >= o) inc += u;
   }
+  if (lane == kWave - 1) s_wave[wave] = inc;
   __syncthreads();
+  int32_t before = 0;
+  for (int w = 0; w < wave; ++w) before += s_wave[w];
+  const int32_t base = before + inc - total;  // exclusive prefix over experts
   if (e < E) {
-    offsets[e] = s_off[e];
-    for (int c = 0; c < nchunks; ++c) chunk_cnt[int64_t(c) * E + e] += s_off[e];
+    int32_t run = base;
+    for (int c0 = 0; c0 < nchunks; c0 += B) {
+      int32_t v[B];
+#pragma unroll
+      for (int j = 0; j < B; ++j) v[j] = (c0 + j < nchunks) ? chunk_cnt[int64_t(c0 + j) * E + e] : 0;
+#pragma unroll
+      for (int j = 0; j < B; ++j) {
+        if (c0 + j < nchunks) chunk_cnt[int64_t(c0 + j) * E + e] = run;
+        run += v[j];
+      }
+    }
+    counts[e] = total;
+    offsets[e] = base;
+    if (e == E - 1) offsets[E] = base + total;
   }
-  if (e == 0) offsets[E] = s_off[E];
 }
 
 // --- 3. positions: row of every (token, slot) -----------------------------

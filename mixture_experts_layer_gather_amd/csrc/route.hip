@@ -277,6 +277,110 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void l
   }
 }
 
+// Router logits for few experts (E <= 32): one thread per (token, expert)
+// recurrence, same ascending order. A block holds 256 / EP tokens x EP
+// experts (EP = E rounded up to a power of two); the 256-wide hidden chunk
+// of the block's tokens and of all experts' weights is staged in LDS
+// (16-byte global loads, prefetched into registers, double-buffered LDS) and
+// read 4 hidden values at a time; token rows are shared by the EP lanes of a
+// token and weight rows by the tokens of a wave (broadcast reads). A chunk is
+// long enough (256 dependent FMAs per lane) to cover the next chunk's load
+// latency. d must be a multiple of 4; the last chunk may be partial.
+constexpr int kSeKC = 256, kSeP = kSeKC + 4;
+
+template <typename TX, int EP>
+__global__ __launch_bounds__(256) void logits_small_e_kernel(const TX* __restrict__ x, const float* __restrict__ w,
+                                                             const float* __restrict__ bias, float* __restrict__ out,
+                                                             int T, int E, int d) {
+  constexpr int TPB = 256 / EP;  // tokens per block
+  __shared__ __attribute__((aligned(16))) float Xs[2][TPB * kSeP];
+  __shared__ __attribute__((aligned(16))) float Ws[2][EP * kSeP];
+  const int tid = threadIdx.x;
+  const int e = tid % EP, tl = tid / EP;
+  const int t0 = blockIdx.x * TPB;
+  // x chunk: TPB rows x 64 values; w chunk: EP rows x 64 floats
+  constexpr int XV = 16 / sizeof(TX);
+  constexpr int XU = TPB * kSeKC / XV;   // 16-byte units of the x chunk
+  constexpr int WU = EP * kSeKC / 4;     // 16-byte units of the w chunk
+  constexpr int XL = (XU + 255) / 256, WL = (WU + 255) / 256;
+  const int nch = (d + kSeKC - 1) / kSeKC;
+  float xv[XL][XV];
+  float4 wv[WL];
+  auto gload = [&](int c) {
+    const int k0 = c * kSeKC;
+#pragma unroll
+    for (int q = 0; q < XL; ++q) {
+      const int u = tid + 256 * q, r = u / (kSeKC / XV), kk = (u % (kSeKC / XV)) * XV;
+      if (u < XU && t0 + r < T && k0 + kk < d) {
+        Vec16<TX>::load(x + int64_t(t0 + r) * d + k0 + kk, xv[q]);
+      } else {
+#pragma unroll
+        for (int v = 0; v < XV; ++v) xv[q][v] = 0.0f;
+      }
+    }
+#pragma unroll
+    for (int q = 0; q < WL; ++q) {
+      const int u = tid + 256 * q, r = u / (kSeKC / 4), kk = (u % (kSeKC / 4)) * 4;
+      wv[q] = (u < WU && r < E && k0 + kk < d) ? *reinterpret_cast<const float4*>(w + int64_t(r) * d + k0 + kk)
+                                               : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+    }
+  };
+  auto lstore = [&](int buf) {
+#pragma unroll
+    for (int q = 0; q < XL; ++q) {
+      const int u = tid + 256 * q, r = u / (kSeKC / XV), kk = (u % (kSeKC / XV)) * XV;
+      if (u < XU)
+#pragma unroll
+        for (int v = 0; v < XV; v += 4)
+          *reinterpret_cast<float4*>(&Xs[buf][r * kSeP + kk + v]) =
+              make_float4(xv[q][v], xv[q][v + 1], xv[q][v + 2], xv[q][v + 3]);
+    }
+#pragma unroll
+    for (int q = 0; q < WL; ++q) {
+      const int u = tid + 256 * q, r = u / (kSeKC / 4), kk = (u % (kSeKC / 4)) * 4;
+      if (u < WU) *reinterpret_cast<float4*>(&Ws[buf][r * kSeP + kk]) = wv[q];
+    }
+  };
+  float acc = 0.0f;
+  auto compute = [&](int buf, int kend) {
+#pragma unroll 4
+    for (int k = 0; k < kend; k += 4) {
+      const float4 a = *reinterpret_cast<const float4*>(&Xs[buf][tl * kSeP + k]);
+      const float4 b = *reinterpret_cast<const float4*>(&Ws[buf][e * kSeP + k]);
+      acc = __builtin_fmaf(a.x, b.x, acc);
+      acc = __builtin_fmaf(a.y, b.y, acc);
+      acc = __builtin_fmaf(a.z, b.z, acc);
+      acc = __builtin_fmaf(a.w, b.w, acc);
+    }
+  };
+  gload(0);
+  lstore(0);
+  __syncthreads();
+  for (int c = 0; c + 1 < nch; ++c) {
+    gload(c + 1);
+    compute(c & 1, kSeKC);
+    lstore((c + 1) & 1);
+    __syncthreads();
+  }
+  compute((nch - 1) & 1, d - (nch - 1) * kSeKC);
+  const int t = t0 + tl;
+  if (t < T && e < E) {
+    float v = acc;
+    if (bias) v = v + bias[e];
+    out[int64_t(t) * E + e] = v;
+  }
+}
+
+template <typename TX>
+static void launch_logits_small_e(const RouteLaunch& r, hipStream_t st) {
+  const TX* x = reinterpret_cast<const TX*>(r.x);
+  const int T = int(r.T), E = int(r.E), d = int(r.d);
+  auto grid = [&](int ep) { return dim3(unsigned((T + 256 / ep - 1) / (256 / ep))); };
+  if (E <= 8) logits_small_e_kernel<TX, 8><<<grid(8), 256, 0, st>>>(x, r.w_router, r.bias, r.logits, T, E, d);
+  else if (E <= 16) logits_small_e_kernel<TX, 16><<<grid(16), 256, 0, st>>>(x, r.w_router, r.bias, r.logits, T, E, d);
+  else logits_small_e_kernel<TX, 32><<<grid(32), 256, 0, st>>>(x, r.w_router, r.bias, r.logits, T, E, d);
+}
+
 // Token-chunk count of the router weight gradient: enough workgroups to
 // fill the chip, chunks of at least 128 tokens.
 int route_bwd_zsplit(int64_t T, int64_t d, int64_t E) {
@@ -603,13 +707,7 @@ static void route_fwd_t(const RouteLaunch& r, hipStream_t st) {
     logits_kernel<TX><<<grid, 256, 0, st>>>(reinterpret_cast<const TX*>(r.x), r.w_router, r.bias, r.logits,
                                             int(r.T), int(r.E), int(r.d));
   } else {
-    VArgs v{};
-    v.A = r.x; v.lda = r.d;
-    v.B = r.w_router; v.ldb = r.d;
-    v.C = r.logits; v.ldc = r.E;
-    v.bias = r.bias;
-    v.M = int(r.T); v.N = int(r.E); v.K = int(r.d);
-    launch_vgemm<TX, true, float, true, float, VEPI_STORE>(v, st);
+    launch_logits_small_e<TX>(r, st);
   }
 
   SelArgs s{};
