@@ -225,55 +225,75 @@ void launch_dispatch(const DispatchLaunch& a, hipStream_t st) {
 // --- combine / dispatch backward: per-token ordered gather ----------------
 // dst[t] = sum_j g[t,j] * src[row_id_map[t,j]] (+ add[t]), fp32 in slot
 // order, the added term last, one rounding.
-template <typename T>
+template <typename T, int KMAX>
 __global__ __launch_bounds__(256) void combine_kernel(const T* __restrict__ src,
                                                       const int32_t* __restrict__ row_id_map,
                                                       const float* __restrict__ gate,
                                                       const T* __restrict__ add, T* __restrict__ dst,
                                                       int ntok, int d, int k, int tpb) {
   constexpr int VEC = 16 / sizeof(T);
+  // chunks per pass: every load of a pass is issued before any arithmetic,
+  // so a thread keeps NC (k + 1) 16-byte loads in flight
+  constexpr int NC = KMAX <= 4 ? 2 : 1;
   const int chunks = d / VEC;
   const int per = 256 / tpb;
   const int sub = threadIdx.x / per;
   const int t = blockIdx.x * tpb + sub;
   if (t >= ntok || sub >= tpb) return;
-  int32_t rows[16];
-  float g[16];
-  _Pragma("unroll") for (int j = 0; j < 16; ++j) if (j < k) {
+  int32_t rows[KMAX];
+  float g[KMAX];
+  _Pragma("unroll") for (int j = 0; j < KMAX; ++j) if (j < k) {
     rows[j] = row_id_map[int64_t(t) * k + j];
     g[j] = gate ? gate[int64_t(t) * k + j] : 1.0f;
   }
-  for (int ch = threadIdx.x % per; ch < chunks; ch += per) {
-    float acc[VEC];
-    for (int i = 0; i < VEC; ++i) acc[i] = 0.0f;
-    _Pragma("unroll") for (int j = 0; j < 16; ++j) if (j < k) {
-      float v[VEC];
-      Vec16<T>::load(src + int64_t(rows[j]) * d + int64_t(ch) * VEC, v);
-      for (int i = 0; i < VEC; ++i) acc[i] = __builtin_fmaf(g[j], v[i], acc[i]);
+  for (int ch0 = threadIdx.x % per; ch0 < chunks; ch0 += NC * per) {
+    uint4 raw[NC][KMAX + 1];
+    _Pragma("unroll") for (int h = 0; h < NC; ++h) {
+      const int ch = ch0 + h * per;
+      if (ch < chunks) {
+        _Pragma("unroll") for (int j = 0; j < KMAX; ++j) if (j < k)
+          raw[h][j] = *reinterpret_cast<const uint4*>(src + int64_t(rows[j]) * d + int64_t(ch) * VEC);
+        if (add) raw[h][KMAX] = *reinterpret_cast<const uint4*>(add + int64_t(t) * d + int64_t(ch) * VEC);
+      }
     }
-    if (add) {
-      float v[VEC];
-      Vec16<T>::load(add + int64_t(t) * d + int64_t(ch) * VEC, v);
-      for (int i = 0; i < VEC; ++i) acc[i] += v[i];
+    _Pragma("unroll") for (int h = 0; h < NC; ++h) {
+      const int ch = ch0 + h * per;
+      if (ch >= chunks) break;
+      float acc[VEC];
+      for (int i = 0; i < VEC; ++i) acc[i] = 0.0f;
+      _Pragma("unroll") for (int j = 0; j < KMAX; ++j) if (j < k) {
+        float v[VEC];
+        Vec16<T>::load(reinterpret_cast<const T*>(&raw[h][j]), v);
+        for (int i = 0; i < VEC; ++i) acc[i] = __builtin_fmaf(g[j], v[i], acc[i]);
+      }
+      if (add) {
+        float v[VEC];
+        Vec16<T>::load(reinterpret_cast<const T*>(&raw[h][KMAX]), v);
+        for (int i = 0; i < VEC; ++i) acc[i] += v[i];
+      }
+      Vec16<T>::store(dst + int64_t(t) * d + int64_t(ch) * VEC, acc);
     }
-    Vec16<T>::store(dst + int64_t(t) * d + int64_t(ch) * VEC, acc);
   }
 }
 
+template <typename T, int KMAX>
+static void combine_t(const CombineLaunch& a, int tpb, hipStream_t st) {
+  combine_kernel<T, KMAX><<<(a.T + tpb - 1) / tpb, 256, 0, st>>>(
+      reinterpret_cast<const T*>(a.src), a.row_id_map, a.gate, reinterpret_cast<const T*>(a.add),
+      reinterpret_cast<T*>(a.dst), int(a.T), int(a.d), int(a.k), tpb);
+}
+template <typename T>
+static void combine_k(const CombineLaunch& a, hipStream_t st) {
+  const int tpb = tokens_per_block(a.d, 16 / int(sizeof(T)));
+  if (a.k <= 2) combine_t<T, 2>(a, tpb, st);
+  else if (a.k <= 4) combine_t<T, 4>(a, tpb, st);
+  else if (a.k <= 8) combine_t<T, 8>(a, tpb, st);
+  else combine_t<T, 16>(a, tpb, st);
+}
+
 void launch_combine(const CombineLaunch& a, hipStream_t st) {
-  if (a.act == 1) {
-    const int tpb = tokens_per_block(a.d, 8);
-    combine_kernel<bf16_t><<<(a.T + tpb - 1) / tpb, 256, 0, st>>>(
-        reinterpret_cast<const bf16_t*>(a.src), a.row_id_map, a.gate,
-        reinterpret_cast<const bf16_t*>(a.add), reinterpret_cast<bf16_t*>(a.dst), int(a.T),
-        int(a.d), int(a.k), tpb);
-  } else {
-    const int tpb = tokens_per_block(a.d, 4);
-    combine_kernel<float><<<(a.T + tpb - 1) / tpb, 256, 0, st>>>(
-        reinterpret_cast<const float*>(a.src), a.row_id_map, a.gate,
-        reinterpret_cast<const float*>(a.add), reinterpret_cast<float*>(a.dst), int(a.T),
-        int(a.d), int(a.k), tpb);
-  }
+  if (a.act == 1) combine_k<bf16_t>(a, st);
+  else combine_k<float>(a, st);
 }
 
 // --- combine backward: one block per token --------------------------------
