@@ -36,6 +36,20 @@ template <> struct Elem<bf16_t> {
   static __device__ __forceinline__ void store(bf16_t* p, float v) { *p = f32_to_bf16(v); }
 };
 
+// Streaming 16-byte load/store (nontemporal hint). For tensors touched once
+// per kernel: the lines do not displace the cache contents of the GEMMs, and
+// when the caches hold dirty lines of an earlier kernel these accesses do not
+// wait for their write-back (measured on a 100 MB gather-and-sum: 21 us
+// instead of 29 us after a 1 GB copy; equal when the caches are clean).
+__device__ __forceinline__ uint4 ld_stream(const void* p) {
+  const u32x4 q = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+  return make_uint4(q.x, q.y, q.z, q.w);
+}
+__device__ __forceinline__ void st_stream(void* p, uint4 v) {
+  const u32x4 q = {v.x, v.y, v.z, v.w};
+  __builtin_nontemporal_store(q, reinterpret_cast<u32x4*>(p));
+}
+
 // 16-byte vector of elements: 4 f32 or 8 bf16, unpacked to f32.
 template <typename T> struct Vec16;
 template <> struct Vec16<float> {
@@ -46,6 +60,14 @@ template <> struct Vec16<float> {
   }
   static __device__ __forceinline__ void store(float* p, const float* v) {
     *reinterpret_cast<float4*>(p) = make_float4(v[0], v[1], v[2], v[3]);
+  }
+  static __device__ __forceinline__ void unpack(uint4 q, float* v) {
+    v[0] = __uint_as_float(q.x); v[1] = __uint_as_float(q.y);
+    v[2] = __uint_as_float(q.z); v[3] = __uint_as_float(q.w);
+  }
+  static __device__ __forceinline__ uint4 pack(const float* v) {
+    return make_uint4(__float_as_uint(v[0]), __float_as_uint(v[1]), __float_as_uint(v[2]),
+                      __float_as_uint(v[3]));
   }
 };
 template <> struct Vec16<bf16_t> {
@@ -66,6 +88,22 @@ template <> struct Vec16<bf16_t> {
       w[i] = static_cast<uint32_t>(f32_to_bf16(v[2 * i])) |
              (static_cast<uint32_t>(f32_to_bf16(v[2 * i + 1])) << 16);
     *reinterpret_cast<uint4*>(p) = make_uint4(w[0], w[1], w[2], w[3]);
+  }
+  static __device__ __forceinline__ void unpack(uint4 q, float* v) {
+    const uint32_t w[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      v[2 * i] = __uint_as_float(w[i] << 16);
+      v[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+    }
+  }
+  static __device__ __forceinline__ uint4 pack(const float* v) {
+    uint32_t w[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      w[i] = static_cast<uint32_t>(f32_to_bf16(v[2 * i])) |
+             (static_cast<uint32_t>(f32_to_bf16(v[2 * i + 1])) << 16);
+    return make_uint4(w[0], w[1], w[2], w[3]);
   }
 };
 

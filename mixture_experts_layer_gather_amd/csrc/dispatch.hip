@@ -252,8 +252,8 @@ __global__ __launch_bounds__(256) void combine_kernel(const T* __restrict__ src,
       const int ch = ch0 + h * per;
       if (ch < chunks) {
         _Pragma("unroll") for (int j = 0; j < KMAX; ++j) if (j < k)
-          raw[h][j] = *reinterpret_cast<const uint4*>(src + int64_t(rows[j]) * d + int64_t(ch) * VEC);
-        if (add) raw[h][KMAX] = *reinterpret_cast<const uint4*>(add + int64_t(t) * d + int64_t(ch) * VEC);
+          raw[h][j] = ld_stream(src + int64_t(rows[j]) * d + int64_t(ch) * VEC);
+        if (add) raw[h][KMAX] = ld_stream(add + int64_t(t) * d + int64_t(ch) * VEC);
       }
     }
     _Pragma("unroll") for (int h = 0; h < NC; ++h) {
@@ -263,15 +263,15 @@ __global__ __launch_bounds__(256) void combine_kernel(const T* __restrict__ src,
       for (int i = 0; i < VEC; ++i) acc[i] = 0.0f;
       _Pragma("unroll") for (int j = 0; j < KMAX; ++j) if (j < k) {
         float v[VEC];
-        Vec16<T>::load(reinterpret_cast<const T*>(&raw[h][j]), v);
+        Vec16<T>::unpack(raw[h][j], v);
         for (int i = 0; i < VEC; ++i) acc[i] = __builtin_fmaf(g[j], v[i], acc[i]);
       }
       if (add) {
         float v[VEC];
-        Vec16<T>::load(reinterpret_cast<const T*>(&raw[h][KMAX]), v);
+        Vec16<T>::unpack(raw[h][KMAX], v);
         for (int i = 0; i < VEC; ++i) acc[i] += v[i];
       }
-      Vec16<T>::store(dst + int64_t(t) * d + int64_t(ch) * VEC, acc);
+      st_stream(dst + int64_t(t) * d + int64_t(ch) * VEC, Vec16<T>::pack(acc));
     }
   }
 }
@@ -297,7 +297,7 @@ void launch_combine(const CombineLaunch& a, hipStream_t st) {
 }
 
 // --- combine backward: one block per token --------------------------------
-template <typename T>
+template <typename T, int KMAX>
 __global__ __launch_bounds__(256) void combine_bwd_kernel(const T* __restrict__ dy,
                                                           const T* __restrict__ out_perm,
                                                           const int32_t* __restrict__ row_id_map,
@@ -308,30 +308,33 @@ __global__ __launch_bounds__(256) void combine_bwd_kernel(const T* __restrict__ 
   __shared__ float red[4][16];
   const int t = blockIdx.x;
   const int chunks = d / VEC;
-  int32_t rows[16];
-  float g[16], part[16];
-  for (int j = 0; j < 16; ++j) part[j] = 0.0f;
-  _Pragma("unroll") for (int j = 0; j < 16; ++j) if (j < k) {
+  int32_t rows[KMAX];
+  float g[KMAX], part[KMAX];
+  for (int j = 0; j < KMAX; ++j) part[j] = 0.0f;
+  _Pragma("unroll") for (int j = 0; j < KMAX; ++j) if (j < k) {
     rows[j] = row_id_map[int64_t(t) * k + j];
     g[j] = gate[int64_t(t) * k + j];
   }
   for (int ch = threadIdx.x; ch < chunks; ch += 256) {
     float dv[VEC];
-    Vec16<T>::load(dy + int64_t(t) * d + int64_t(ch) * VEC, dv);
-    _Pragma("unroll") for (int j = 0; j < 16; ++j) if (j < k) {
+    Vec16<T>::unpack(ld_stream(dy + int64_t(t) * d + int64_t(ch) * VEC), dv);
+    uint4 raw[KMAX];
+    _Pragma("unroll") for (int j = 0; j < KMAX; ++j) if (j < k)
+      raw[j] = ld_stream(out_perm + int64_t(rows[j]) * d + int64_t(ch) * VEC);
+    _Pragma("unroll") for (int j = 0; j < KMAX; ++j) if (j < k) {
       float o[VEC], w[VEC];
-      Vec16<T>::load(out_perm + int64_t(rows[j]) * d + int64_t(ch) * VEC, o);
+      Vec16<T>::unpack(raw[j], o);
       float s = 0.0f;
       for (int i = 0; i < VEC; ++i) {
         s = __builtin_fmaf(dv[i], o[i], s);
         w[i] = g[j] * dv[i];
       }
       part[j] += s;
-      Vec16<T>::store(d_out + int64_t(rows[j]) * d + int64_t(ch) * VEC, w);
+      st_stream(d_out + int64_t(rows[j]) * d + int64_t(ch) * VEC, Vec16<T>::pack(w));
     }
   }
   const int wave = threadIdx.x / kWave;
-  _Pragma("unroll") for (int j = 0; j < 16; ++j) if (j < k) {
+  _Pragma("unroll") for (int j = 0; j < KMAX; ++j) if (j < k) {
     const float s = wave_sum(part[j]);
     if (lane_id() == 0) red[wave][j] = s;
   }
@@ -342,15 +345,23 @@ __global__ __launch_bounds__(256) void combine_bwd_kernel(const T* __restrict__ 
   }
 }
 
+template <typename T, int KMAX>
+static void combine_bwd_t(const CombineBwdLaunch& a, hipStream_t st) {
+  combine_bwd_kernel<T, KMAX><<<a.T, 256, 0, st>>>(
+      reinterpret_cast<const T*>(a.dy), reinterpret_cast<const T*>(a.out_perm), a.row_id_map, a.gate,
+      reinterpret_cast<T*>(a.d_out_perm), a.d_gate, int(a.d), int(a.k));
+}
+template <typename T>
+static void combine_bwd_k(const CombineBwdLaunch& a, hipStream_t st) {
+  if (a.k <= 2) combine_bwd_t<T, 2>(a, st);
+  else if (a.k <= 4) combine_bwd_t<T, 4>(a, st);
+  else if (a.k <= 8) combine_bwd_t<T, 8>(a, st);
+  else combine_bwd_t<T, 16>(a, st);
+}
+
 void launch_combine_bwd(const CombineBwdLaunch& a, hipStream_t st) {
-  if (a.act == 1)
-    combine_bwd_kernel<bf16_t><<<a.T, 256, 0, st>>>(
-        reinterpret_cast<const bf16_t*>(a.dy), reinterpret_cast<const bf16_t*>(a.out_perm),
-        a.row_id_map, a.gate, reinterpret_cast<bf16_t*>(a.d_out_perm), a.d_gate, int(a.d), int(a.k));
-  else
-    combine_bwd_kernel<float><<<a.T, 256, 0, st>>>(
-        reinterpret_cast<const float*>(a.dy), reinterpret_cast<const float*>(a.out_perm),
-        a.row_id_map, a.gate, reinterpret_cast<float*>(a.d_out_perm), a.d_gate, int(a.d), int(a.k));
+  if (a.act == 1) combine_bwd_k<bf16_t>(a, st);
+  else combine_bwd_k<float>(a, st);
 }
 
 // --- FP8 block quantisation (weights 128x128, activations 1x128) ---------
