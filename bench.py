@@ -282,6 +282,53 @@ def cpu_baseline(cfg, sample_tokens):
                       f"in fp64 over all {cfg.E} experts' weights; {dt:.1f} s"}
 
 
+def vendor_gemm(name):
+    """Context for the grouped GEMM's roofline: the vendor library's dense
+    GEMM (torch.matmul, hipBLASLt) on the same per-expert shapes, one call per
+    expert with the mean rows per expert, bf16 in and out, no epilogue work;
+    and a large square GEMM as the library's best case on this GPU."""
+    import torch
+    import moe_synth as S
+    cfg = S.BY_NAME[name]
+    dev = torch.device("cuda:0")
+    bf = torch.bfloat16
+    E, d, f = cfg.E, cfg.d, cfg.f
+    R = cfg.T * cfg.k // E
+    g = torch.Generator(device=dev).manual_seed(0)
+    def rnd(*shape):
+        return torch.randn(*shape, dtype=bf, device=dev, generator=g)
+    x, dy = rnd(E * R, d), rnd(E * R, d)
+    h, gu = rnd(E * R, f), rnd(E * R, 2 * f)
+    w1, w2 = rnd(E, 2 * f, d), rnd(E, d, f)
+    rows = lambda t, e: t[e * R:(e + 1) * R]
+    f1, f2 = 2.0 * E * R * d * 2 * f, 2.0 * E * R * f * d
+    cases = [("gemm1", "X_e @ W1_e^T", lambda: [rows(x, e) @ w1[e].t() for e in range(E)], f1),
+             ("gemm2", "H_e @ W2_e^T", lambda: [rows(h, e) @ w2[e].t() for e in range(E)], f2),
+             ("dh", "dY_e @ W2_e", lambda: [rows(dy, e) @ w2[e] for e in range(E)], f2),
+             ("dx", "dGU_e @ W1_e", lambda: [rows(gu, e) @ w1[e] for e in range(E)], f1),
+             ("wgrad dW1", "X_e^T @ dGU_e", lambda: [rows(x, e).t() @ rows(gu, e) for e in range(E)], f1),
+             ("wgrad dW2", "H_e^T @ dY_e", lambda: [rows(h, e).t() @ rows(dy, e) for e in range(E)], f2)]
+    sq = rnd(8192, 8192)
+    cases.append(("square", "8192 x 8192 x 8192", lambda: sq @ sq, 2.0 * 8192 ** 3))
+    print(f"# torch.matmul (hipBLASLt) on the GEMM shapes of {name}\n")
+    print(f"{E} experts x {R} rows (mean rows per expert), d={d}, f={f}; bf16; "
+          f"one call per expert; peak 2500 TFLOP/s.\n")
+    print("| role | product | ms | TFLOP/s | % of peak |\n|---|---|---:|---:|---:|")
+    for role, what, fn, flops in cases:
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(10):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / 10
+        print(f"| {role} | {what} | {ms:.3f} | {flops / ms / 1e9:.0f} | {flops / ms / 1e9 / 25:.1f} |",
+              flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -292,6 +339,8 @@ def main():
                     help="tokens of the workload timed on the CPU oracle (0: skip)")
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run a plain 1 GiB device copy (counter calibration)")
+    ap.add_argument("--vendor-gemm", action="store_true",
+                    help="only time torch.matmul (hipBLASLt) on the config's per-expert GEMM shapes")
     ap.add_argument("--summarize", nargs=5, metavar="DIR",
                     help="rocprofv3 output dirs: stats, FETCH_SIZE, WRITE_SIZE, copy FETCH_SIZE, "
                          "copy WRITE_SIZE; writes profiles/<config>_kernels.md and _traffic.json")
@@ -310,15 +359,24 @@ def main():
                              "python3 bench.py --copy-probe"}
         summarize_profiles(c, *args.summarize, command=cmd)
         return
+    if args.vendor_gemm:
+        vendor_gemm(args.config)
+        return
     if args.copy_probe:
         import torch
         a = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
         b = torch.empty_like(a)
         a.fill_(1)
-        for _ in range(3):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        b.copy_(a)
+        e0.record()
+        for _ in range(2):
             b.copy_(a)
+        e1.record()
         torch.cuda.synchronize()
-        print(json.dumps({"copy_probe_bytes": 1 << 30, "launches": 3}))
+        ms = e0.elapsed_time(e1) / 2
+        print(json.dumps({"copy_probe_bytes": 1 << 30, "launches": 3,
+                          "copy_GBps": round(2 * (1 << 30) / ms / 1e6, 1)}))
         return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for {args.gpus}); the path has no "
