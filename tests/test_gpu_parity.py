@@ -250,6 +250,48 @@ def test_fp8_dispatch_bit_exact():
     assert np.array_equal(_np(out["xs"]), oracle.permute(xs, rmap))
 
 
+def _random_routing(T, E, k, seed, skew):
+    """k distinct experts per token; skew > 0 draws experts with Zipf-like
+    weights (hot experts, some empty ones)."""
+    rng = np.random.default_rng(seed)
+    w = 1.0 / np.arange(1, E + 1) ** skew
+    keys = np.log(rng.random((T, E))) / w  # Efraimidis-Spirakis: top-k = weighted draw without replacement
+    return np.argsort(-keys, axis=1, kind="stable")[:, :k].astype(np.int32)
+
+
+# (T, E, k, skew): ragged last chunks, E up to the 1024 limit, k = E, hot and
+# empty experts
+DISPATCH_INDEX_CASES = [(3000, 24, 3, 0.0), (1024, 1024, 8, 1.1), (4096, 8, 8, 0.0),
+                        (12000, 16, 4, 1.2), (2000, 600, 2, 0.0), (257, 5, 5, 0.0)]
+
+
+@pytest.mark.parametrize("T,E,k,skew", DISPATCH_INDEX_CASES)
+def test_dispatch_index_paths(T, E, k, skew):
+    from mixture_experts_layer_gather_amd import make_config, moe_dispatch, workspace_size
+    d = 128
+    _say(f"[dispatch index] T={T} E={E} k={k} skew={skew}")
+    idx = _random_routing(T, E, k, seed=T * 7 + E, skew=skew)
+    counts, offsets, rmap, ptok = oracle.dispatch_index(idx, E)
+    x = torch.arange(T * d, dtype=torch.float32).reshape(T, d).to(torch.bfloat16)
+    c = make_config(T=T, d=d, E=E, k=k, f=128)
+    A = T * k
+    out = dict(counts=torch.empty(E, dtype=torch.int32, device=DEV),
+               offsets=torch.empty(E + 1, dtype=torch.int32, device=DEV),
+               rmap=torch.empty(T, k, dtype=torch.int32, device=DEV),
+               ptok=torch.empty(A, dtype=torch.int32, device=DEV),
+               xp=torch.empty(A, d, dtype=torch.bfloat16, device=DEV))
+    ws = torch.empty(workspace_size(c, 1), dtype=torch.uint8, device=DEV)
+    moe_dispatch(c, x.to(DEV), torch.from_numpy(idx).to(DEV), out["counts"], out["offsets"],
+                 out["rmap"], out["ptok"], out["xp"], None, ws)
+    torch.cuda.synchronize()
+    assert np.array_equal(_np(out["counts"]), counts)
+    assert np.array_equal(_np(out["offsets"]), offsets)
+    assert np.array_equal(_np(out["rmap"]), rmap)
+    assert np.array_equal(_np(out["ptok"]), ptok)
+    got = out["xp"].view(torch.int16).cpu().numpy()
+    assert np.array_equal(got, oracle.permute(x.view(torch.int16).numpy(), rmap))
+
+
 # ------------------------------------------------------------ full sizes
 
 def _full_size_check(cfg, n_tok=24, n_cols=3):
