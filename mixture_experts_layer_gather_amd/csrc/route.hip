@@ -17,10 +17,17 @@
 namespace moe {
 
 // ---------------------------------------------------------------------------
-// VALU GEMM with a sequential contraction: C[m][n] = sum_k A(m,k) B(k,n),
-// one fused multiply-add per k in ascending order, per output.
-//   A_MK: A(m,k) = A[m*lda + k], else A[k*lda + m]
-//   B_NK: B(k,n) = B[n*ldb + k], else B[k*ldb + n]
+// Router backward products on the fp32 matrix cores (v_mfma_f32_16x16x4f32):
+//   C(m, n) (op)= sum_k A(m, k) B(k, n) over the block's contraction range
+//   A fp32:  A_MK: A(m,k) = A[m*lda + k], else A[k*lda + m]
+//   B (f32 or bf16, widened exactly): B(k,n) = B[k*ldb + n]
+//   EPI store: fp32 C[z*c_zstride + m*ldc + n]; EPI add: C (act dtype) += v,
+//   one rounding.
+// The backward has no bit-exactness requirement (unlike the logits); the
+// summation order is fixed by the tiling, so results are deterministic.
+// Tile 64 x 128 (4 waves of 32 x 64), contraction chunks of 32 staged in
+// LDS; the next chunk is loaded into registers while the current one is
+// multiplied.
 // ---------------------------------------------------------------------------
 enum { VEPI_STORE = 0, VEPI_ADD_ACT = 1 };
 
@@ -31,7 +38,6 @@ struct VArgs {
   int64_t ldb;
   void* C;
   int64_t ldc;
-  const float* bias;  // [N] or null, added once after the contraction
   int M, N, K;
   int kchunk;         // contraction range of blockIdx.z: [z*kchunk, (z+1)*kchunk)
   int64_t c_zstride;  // elements between the partial outputs of consecutive z
@@ -42,90 +48,158 @@ __device__ __forceinline__ float ld_elem(const void* p, int64_t i) {
   return Elem<T>::load(reinterpret_cast<const T*>(p) + i);
 }
 
-template <typename TA, bool A_MK, typename TB, bool B_NK, typename TC, int TM, int TN,
-          int RM, int RN, int KC, int EPI>
-__global__ __launch_bounds__(256) void vgemm_kernel(VArgs a) {
-  static_assert((TM / RM) * (TN / RN) == 256, "256 threads");
-  static_assert(RM == 4 || RM == 1, "row tile");
-  static_assert(RN == 4 || RN == 1, "column tile");
-  __shared__ __attribute__((aligned(16))) float As[KC][TM + 4];
-  __shared__ __attribute__((aligned(16))) float Bs[KC][TN + 4];
-  const int tid = threadIdx.x;
-  const int m0 = blockIdx.y * TM;
-  const int n0 = blockIdx.x * TN;
+constexpr int kRgBM = 64, kRgBN = 128, kRgBK = 32;
+
+template <typename TB, bool A_MK, typename TC, int EPI>
+__global__ __launch_bounds__(256) void rgemm_kernel(VArgs a) {
+  constexpr int BM = kRgBM, BN = kRgBN, BK = kRgBK;
+  constexpr int PA = BM + 4, PB = BN + 4;   // LDS pitches (floats; rows stay 16-byte aligned)
+  constexpr int VB = 16 / int(sizeof(TB));  // B elements per 16-byte load
+  constexpr int NA = BM * BK / 4 / 256;     // 4-float groups of A per thread
+  constexpr int NB = BN * BK / VB / 256;    // 16-byte groups of B per thread
+  __shared__ __attribute__((aligned(16))) float As[BK * PA];  // [k][m]
+  __shared__ __attribute__((aligned(16))) float Bs[BK * PB];  // [k][n]
+  // epilogue staging of the read-modify-write (add) variant
+  __shared__ __attribute__((aligned(16))) float Cs[EPI == VEPI_ADD_ACT ? 4 * 16 * (64 + 4) : 4];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int m0 = blockIdx.y * BM, n0 = blockIdx.x * BN;
   const int kb = blockIdx.z * a.kchunk;
   const int ke = min(a.K, kb + a.kchunk);
-  const int tn = tid % (TN / RN);
-  const int tm = tid / (TN / RN);
-  float acc[RM][RN];
+  const float* A = reinterpret_cast<const float*>(a.A);
+  const bool a_vec = (a.lda & 3) == 0;  // 16-byte loads along A's contiguous index
+  // A group i: 4 values along A's contiguous index (k when A_MK, else m)
+  auto a_pos = [&](int i, int& m, int& kk) {
+    const int q = (tid + 256 * i) * 4;
+    if (A_MK) { m = q / BK; kk = q % BK; } else { kk = q / BM; m = q % BM; }
+  };
+  float ra[NA][4], rb[NB][VB];
+  auto gload = [&](int k0) {
 #pragma unroll
-  for (int i = 0; i < RM; ++i)
-#pragma unroll
-    for (int j = 0; j < RN; ++j) acc[i][j] = 0.0f;
-
-  for (int k0 = kb; k0 < ke; k0 += KC) {
-    // stage A chunk as As[k][m]
-    for (int idx = tid; idx < TM * KC; idx += 256) {
+    for (int i = 0; i < NA; ++i) {
       int m, kk;
-      if (A_MK) { m = idx / KC; kk = idx % KC; }
-      else { kk = idx / TM; m = idx % TM; }
+      a_pos(i, m, kk);
       const int gm = m0 + m, gk = k0 + kk;
-      float v = 0.0f;
-      if (gm < a.M && gk < ke)
-        v = A_MK ? ld_elem<TA>(a.A, int64_t(gm) * a.lda + gk)
-                 : ld_elem<TA>(a.A, int64_t(gk) * a.lda + gm);
-      As[kk][m] = v;
+      const bool full = A_MK ? (gm < a.M && gk + 4 <= ke) : (gk < ke && gm + 4 <= a.M);
+      if (full && a_vec) {
+        const float4 v = *reinterpret_cast<const float4*>(A_MK ? A + int64_t(gm) * a.lda + gk
+                                                                : A + int64_t(gk) * a.lda + gm);
+        ra[i][0] = v.x; ra[i][1] = v.y; ra[i][2] = v.z; ra[i][3] = v.w;
+      } else {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int mm = A_MK ? gm : gm + j, kq = A_MK ? gk + j : gk;
+          ra[i][j] = (mm < a.M && kq < ke) ? (A_MK ? A[int64_t(mm) * a.lda + kq] : A[int64_t(kq) * a.lda + mm]) : 0.0f;
+        }
+      }
     }
-    for (int idx = tid; idx < TN * KC; idx += 256) {
-      int n, kk;
-      if (B_NK) { n = idx / KC; kk = idx % KC; }
-      else { kk = idx / TN; n = idx % TN; }
+#pragma unroll
+    for (int i = 0; i < NB; ++i) {
+      const int q = (tid + 256 * i) * VB;
+      const int n = q % BN, kk = q / BN;
       const int gn = n0 + n, gk = k0 + kk;
-      float v = 0.0f;
-      if (gn < a.N && gk < ke)
-        v = B_NK ? ld_elem<TB>(a.B, int64_t(gn) * a.ldb + gk)
-                 : ld_elem<TB>(a.B, int64_t(gk) * a.ldb + gn);
-      Bs[kk][n] = v;
+      const TB* p = reinterpret_cast<const TB*>(a.B) + int64_t(gk) * a.ldb + gn;
+      if (gk < ke && gn + VB <= a.N) {
+        Vec16<TB>::load(p, rb[i]);
+      } else {
+#pragma unroll
+        for (int j = 0; j < VB; ++j) rb[i][j] = (gk < ke && gn + j < a.N) ? Elem<TB>::load(p + j) : 0.0f;
+      }
+    }
+  };
+  f32x4_t acc[2][4];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+  if (kb < ke) gload(kb);
+  for (int k0 = kb; k0 < ke; k0 += BK) {
+    __syncthreads();  // the previous chunk's reads are done
+#pragma unroll
+    for (int i = 0; i < NA; ++i) {
+      int m, kk;
+      a_pos(i, m, kk);
+      if (A_MK) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) As[(kk + j) * PA + m] = ra[i][j];
+      } else {
+        *reinterpret_cast<float4*>(&As[kk * PA + m]) = make_float4(ra[i][0], ra[i][1], ra[i][2], ra[i][3]);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < NB; ++i) {
+      const int q = (tid + 256 * i) * VB;
+      float* d = &Bs[(q / BN) * PB + q % BN];
+#pragma unroll
+      for (int j = 0; j < VB; j += 4) *reinterpret_cast<float4*>(d + j) = make_float4(rb[i][j], rb[i][j + 1], rb[i][j + 2], rb[i][j + 3]);
     }
     __syncthreads();
-    const int kend = min(KC, ke - k0);
-    for (int kk = 0; kk < kend; ++kk) {
-      float av[RM], bv[RN];
-      if constexpr (RM == 4) {
-        const float4 q = *reinterpret_cast<const float4*>(&As[kk][tm * 4]);
-        av[0] = q.x; av[1] = q.y; av[2] = q.z; av[3] = q.w;
-      } else {
-        av[0] = As[kk][tm];
-      }
-      if constexpr (RN == 4) {
-        const float4 q = *reinterpret_cast<const float4*>(&Bs[kk][tn * 4]);
-        bv[0] = q.x; bv[1] = q.y; bv[2] = q.z; bv[3] = q.w;
-      } else {
-        bv[0] = Bs[kk][tn];
-      }
+    if (k0 + BK < ke) gload(k0 + BK);
+    // A fragment: lane holds A(m = l % 16, k = l / 16); B: B(k = l / 16, n = l % 16)
 #pragma unroll
-      for (int i = 0; i < RM; ++i)
+    for (int k4 = 0; k4 < BK / 4; ++k4) {
+      const int kr = 4 * k4 + lane / 16;
+      float af[2], bf[4];
 #pragma unroll
-        for (int j = 0; j < RN; ++j) acc[i][j] = __builtin_fmaf(av[i], bv[j], acc[i][j]);
+      for (int i = 0; i < 2; ++i) af[i] = As[kr * PA + wm * 32 + i * 16 + lane % 16];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) bf[j] = Bs[kr * PB + wn * 64 + j * 16 + lane % 16];
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(af[i], bf[j], acc[i][j], 0, 0, 0);
     }
-    __syncthreads();
   }
-
+  if constexpr (EPI == VEPI_STORE) {
+    // fp32 partial sums: a lane holds rows 4 (l / 16) + r, column l % 16 of
+    // each 16 x 16 block; 16 lanes store 64 contiguous bytes
 #pragma unroll
-  for (int i = 0; i < RM; ++i) {
-    const int gm = m0 + tm * RM + i;
-    if (gm >= a.M) continue;
+    for (int i = 0; i < 2; ++i)
 #pragma unroll
-    for (int j = 0; j < RN; ++j) {
-      const int gn = n0 + tn * RN + j;
-      if (gn >= a.N) continue;
-      float v = acc[i][j];
-      if (EPI == VEPI_STORE) {
-        if (a.bias) v = v + a.bias[gn];
-        reinterpret_cast<float*>(a.C)[blockIdx.z * a.c_zstride + int64_t(gm) * a.ldc + gn] = v;
+      for (int j = 0; j < 4; ++j) {
+        const int gn = n0 + wn * 64 + j * 16 + lane % 16;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int gm = m0 + wm * 32 + i * 16 + 4 * (lane / 16) + r;
+          if (gm < a.M && gn < a.N)
+            reinterpret_cast<float*>(a.C)[blockIdx.z * a.c_zstride + int64_t(gm) * a.ldc + gn] = acc[i][j][r];
+        }
+      }
+    return;
+  }
+  // Add into the activation gradient through LDS: each wave stages 16 rows x
+  // 64 columns at a time and reads them back as 8 consecutive columns per
+  // lane, for 16-byte read-modify-write accesses.
+  constexpr int EP = 64 + 4;
+  float* stg = Cs + wave * 16 * EP;
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) stg[(4 * (lane / 16) + r) * EP + j * 16 + lane % 16] = acc[i][j][r];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int u = lane + 64 * h, rr = u / 8, c8 = (u % 8) * 8;
+      const int gm = m0 + wm * 32 + i * 16 + rr, gn = n0 + wn * 64 + c8;
+      if (gm >= a.M) continue;
+      float v[8];
+      const float4 lo = *reinterpret_cast<const float4*>(&stg[rr * EP + c8]);
+      const float4 hi = *reinterpret_cast<const float4*>(&stg[rr * EP + c8 + 4]);
+      v[0] = lo.x; v[1] = lo.y; v[2] = lo.z; v[3] = lo.w; v[4] = hi.x; v[5] = hi.y; v[6] = hi.z; v[7] = hi.w;
+      TC* c = reinterpret_cast<TC*>(a.C) + int64_t(gm) * a.ldc + gn;
+      if (gn + 8 <= a.N) {
+        constexpr int VC = 16 / int(sizeof(TC));
+        float o[8];
+#pragma unroll
+        for (int e = 0; e < 8; e += VC) Vec16<TC>::load(c + e, o + e);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) o[e] = o[e] + v[e];
+#pragma unroll
+        for (int e = 0; e < 8; e += VC) Vec16<TC>::store(c + e, o + e);
       } else {
-        TC* c = reinterpret_cast<TC*>(a.C) + int64_t(gm) * a.ldc + gn;
-        Elem<TC>::store(c, Elem<TC>::load(c) + v);
+        for (int e = 0; e < 8; ++e)
+          if (gn + e < a.N) Elem<TC>::store(c + e, Elem<TC>::load(c + e) + v[e]);
       }
     }
   }
@@ -141,24 +215,17 @@ __global__ __launch_bounds__(256) void reduce_parts_kernel(const float* __restri
   }
 }
 
-template <typename TA, bool A_MK, typename TB, bool B_NK, typename TC, int EPI>
-static void launch_vgemm(VArgs a, hipStream_t st, int zsplit = 1) {
+template <typename TB, bool A_MK, typename TC, int EPI>
+static void launch_rgemm(VArgs a, hipStream_t st, int zsplit = 1) {
   a.kchunk = (a.K + zsplit - 1) / zsplit;
-  if (a.N <= 16) {
-    constexpr int TM = 16, TN = 16;
-    dim3 grid((a.N + TN - 1) / TN, (a.M + TM - 1) / TM, zsplit);
-    vgemm_kernel<TA, A_MK, TB, B_NK, TC, TM, TN, 1, 1, 32, EPI><<<grid, 256, 0, st>>>(a);
-  } else {
-    constexpr int TM = 64, TN = 64;
-    dim3 grid((a.N + TN - 1) / TN, (a.M + TM - 1) / TM, zsplit);
-    vgemm_kernel<TA, A_MK, TB, B_NK, TC, TM, TN, 4, 4, 32, EPI><<<grid, 256, 0, st>>>(a);
-  }
+  dim3 grid((a.N + kRgBN - 1) / kRgBN, (a.M + kRgBM - 1) / kRgBM, zsplit);
+  rgemm_kernel<TB, A_MK, TC, EPI><<<grid, 256, 0, st>>>(a);
 }
 
 // ---------------------------------------------------------------------------
 // Router logits L[t][e] = (sum_i x[t][i] w[e][i]) + bias[e], each output its
 // own fp32 FMA recurrence over i = 0 .. d-1 in ascending order (the same
-// order as vgemm_kernel, so results are bit-identical), built for latency
+// order everywhere, so results are bit-identical), built for latency
 // hiding at low occupancy: a block holds 64 tokens x 64 experts, a thread
 // 4 x 4 independent recurrences; LDS rows are K-contiguous (pitch 36 floats)
 // and read 4 hidden values at a time; the next 32-wide hidden chunk is
@@ -384,10 +451,10 @@ static void launch_logits_small_e(const RouteLaunch& r, hipStream_t st) {
 // Token-chunk count of the router weight gradient: enough workgroups to
 // fill the chip, chunks of at least 128 tokens.
 int route_bwd_zsplit(int64_t T, int64_t d, int64_t E) {
-  const int64_t base = ((d + 63) / 64) * ((E + 63) / 64);
+  const int64_t base = ((d + kRgBN - 1) / kRgBN) * ((E + kRgBM - 1) / kRgBM);
   int64_t z = (1024 + base - 1) / base;
   z = z < 1 ? 1 : z;
-  const int64_t zmax = (T + 127) / 128;
+  const int64_t zmax = (T + 255) / 256;
   if (z > zmax) z = zmax < 1 ? 1 : zmax;
   return int(z);
 }
@@ -747,7 +814,7 @@ static void route_bwd_t(const RouteBwdLaunch& r, hipStream_t st) {
   v.B = r.w_router; v.ldb = r.d;
   v.C = r.dx; v.ldc = r.d;
   v.M = int(r.T); v.N = int(r.d); v.K = int(r.E);
-  launch_vgemm<float, true, float, false, TX, VEPI_ADD_ACT>(v, st);
+  launch_rgemm<float, true, TX, VEPI_ADD_ACT>(v, st);
 
   // dw[e,:] = sum_t dL[t,e] x[t,:], tokens split into Z chunks whose partial
   // sums are added in chunk order
@@ -758,7 +825,7 @@ static void route_bwd_t(const RouteBwdLaunch& r, hipStream_t st) {
   w.C = Z > 1 ? r.dw_part : r.dw_router; w.ldc = r.d;
   w.c_zstride = r.E * r.d;
   w.M = int(r.E); w.N = int(r.d); w.K = int(r.T);
-  launch_vgemm<float, false, TX, false, float, VEPI_STORE>(w, st, Z);
+  launch_rgemm<TX, false, float, VEPI_STORE>(w, st, Z);
   if (Z > 1) {
     const int64_t n = r.E * r.d;
     reduce_parts_kernel<<<int((n + 255) / 256 < 4096 ? (n + 255) / 256 : 4096), 256, 0, st>>>(
