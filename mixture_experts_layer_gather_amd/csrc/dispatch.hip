@@ -394,10 +394,63 @@ __global__ __launch_bounds__(256) void quant_blocks_kernel(const T* __restrict__
   }
 }
 
+// Whole 128 x 128 blocks (the weight layout): the block stays in registers
+// between the amax and the codes, so the source is read once. Thread t holds
+// columns 8 (t % 16) .. + 8 of rows t / 16 + 16 i (i < 8): 16-byte loads, a
+// group of 16 threads covers one 256- (bf16) or 512-byte (fp32) row segment;
+// the codes leave as 8-byte stores. Same scale and per-element arithmetic as
+// quant_blocks_kernel.
+template <typename T>
+__global__ __launch_bounds__(256) void quant_tiles128_kernel(const T* __restrict__ src, uint8_t* __restrict__ dst,
+                                                             float* __restrict__ scale, int64_t cols, int nbc) {
+  __shared__ float red[4];
+  const int64_t I = blockIdx.y, J = blockIdx.x;
+  const int c = int(threadIdx.x % 16) * 8, rw = int(threadIdx.x / 16);
+  const int64_t base = (I * 128 + rw) * cols + J * 128 + c;
+  float v[8][8];
+  float amax = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const T* p = src + base + int64_t(16 * i) * cols;
+    if constexpr (sizeof(T) == 2) {
+      Vec16<bf16_t>::load(p, v[i]);
+    } else {
+      Vec16<float>::load(p, v[i]);
+      Vec16<float>::load(p + 4, v[i] + 4);
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf(v[i][e]));
+  }
+  amax = wave_max(amax);
+  if (lane_id() == 0) red[threadIdx.x / kWave] = amax;
+  __syncthreads();
+  amax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  const float s = (amax == 0.0f) ? 1.0f : amax / 448.0f;
+  if (threadIdx.x == 0) scale[I * nbc + J] = s;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    uint32_t lo = 0, hi = 0;
+    lo = __builtin_amdgcn_cvt_pk_fp8_f32(v[i][0] / s, v[i][1] / s, lo, false);
+    lo = __builtin_amdgcn_cvt_pk_fp8_f32(v[i][2] / s, v[i][3] / s, lo, true);
+    hi = __builtin_amdgcn_cvt_pk_fp8_f32(v[i][4] / s, v[i][5] / s, hi, false);
+    hi = __builtin_amdgcn_cvt_pk_fp8_f32(v[i][6] / s, v[i][7] / s, hi, true);
+    *reinterpret_cast<uint2*>(dst + base + int64_t(16 * i) * cols) = make_uint2(lo, hi);
+  }
+}
+
 void launch_quant_blocks(const QuantLaunch& a, hipStream_t st) {
   const int nbr = int((a.rows + a.br - 1) / a.br), nbc = int((a.cols + a.bc - 1) / a.bc);
   const dim3 grid(nbc, nbr);
-  if (a.src_bf16)
+  const bool tiles = a.br == 128 && a.bc == 128 && a.rows % 128 == 0 && a.cols % 128 == 0 &&
+                     (reinterpret_cast<uintptr_t>(a.src) & 15) == 0 && (reinterpret_cast<uintptr_t>(a.dst) & 15) == 0;
+  if (tiles) {
+    if (a.src_bf16)
+      quant_tiles128_kernel<bf16_t><<<grid, 256, 0, st>>>(reinterpret_cast<const bf16_t*>(a.src), a.dst, a.scale,
+                                                          a.cols, nbc);
+    else
+      quant_tiles128_kernel<float><<<grid, 256, 0, st>>>(reinterpret_cast<const float*>(a.src), a.dst, a.scale,
+                                                         a.cols, nbc);
+  } else if (a.src_bf16)
     quant_blocks_kernel<bf16_t><<<grid, 256, 0, st>>>(reinterpret_cast<const bf16_t*>(a.src), a.dst,
                                                       a.scale, a.rows, a.cols, int(a.br), int(a.bc), nbc);
   else

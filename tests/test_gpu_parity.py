@@ -185,19 +185,22 @@ def test_deterministic_repeat():
 def test_fp8_block_quantiser_bit_exact():
     from mixture_experts_layer_gather_amd import moe_quantize_fp8_blockwise
     g = torch.Generator().manual_seed(11)
-    src = torch.randn(384, 640, generator=g) * torch.exp(torch.randn(384, 1, generator=g) * 3)
-    src[7, :128] = 0.0
-    src[9, 5] = 1e30
-    for br, bc in [(128, 128), (1, 128)]:
-        for dt in (torch.float32, torch.bfloat16):
-            s = src.to(dt)
-            q = torch.empty(384, 640, dtype=torch.uint8, device=DEV)
-            sc = torch.empty(384 // br, 640 // bc, dtype=torch.float32, device=DEV)
-            moe_quantize_fp8_blockwise(s.to(DEV), 384, 640, br, bc, q, sc)
-            torch.cuda.synchronize()
-            rq, rs = oracle.quant_blocks(oracle.as_f32(s), br, bc)
-            assert np.array_equal(_np(sc), rs), (br, bc, dt)
-            assert np.array_equal(_np(q), rq), (br, bc, dt)
+    # whole 128 x 128 blocks (register path) and ragged edges (general path)
+    for R, C in [(384, 640), (300, 520)]:
+        src = torch.randn(R, C, generator=g) * torch.exp(torch.randn(R, 1, generator=g) * 3)
+        src[7, :128] = 0.0
+        src[9, 5] = 1e30
+        src[200:256, 128:256] = 0.0  # an all-zero 128 x 128 block: scale 1, codes 0
+        for br, bc in [(128, 128), (1, 128)]:
+            for dt in (torch.float32, torch.bfloat16):
+                s = src.to(dt)
+                q = torch.empty(R, C, dtype=torch.uint8, device=DEV)
+                sc = torch.empty(-(-R // br), -(-C // bc), dtype=torch.float32, device=DEV)
+                moe_quantize_fp8_blockwise(s.to(DEV), R, C, br, bc, q, sc)
+                torch.cuda.synchronize()
+                rq, rs = oracle.quant_blocks(oracle.as_f32(s), br, bc)
+                assert np.array_equal(_np(sc), rs), (R, C, br, bc, dt)
+                assert np.array_equal(_np(q), rq), (R, C, br, bc, dt)
 
 
 def test_fp8_encoder_exhaustive_in_range():
