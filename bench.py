@@ -48,13 +48,16 @@ def kernel_role(name: str):
     return "gemm2" if bk else "dx"
 
 
+# the sources the grouped GEMM kernels (whose traffic is stored) are built from
+GEMM_SOURCES = ("common.hpp", "gemm.hip", "launch.hpp")
+
+
 def source_hash() -> str:
     import hashlib
     h = hashlib.sha256()
-    for f in sorted(os.listdir(CSRC)):
-        if f.endswith((".hip", ".hpp")):
-            h.update(f.encode())
-            h.update(open(os.path.join(CSRC, f), "rb").read())
+    for f in GEMM_SOURCES:
+        h.update(f.encode())
+        h.update(open(os.path.join(CSRC, f), "rb").read())
     return h.hexdigest()[:16]
 
 
