@@ -50,6 +50,65 @@ __device__ __forceinline__ float ld_elem(const void* p, int64_t i) {
 
 constexpr int kRgBM = 64, kRgBN = 128, kRgBK = 32;
 
+// Epilogue of the router-backward products (acc: a lane holds rows
+// 4 (l / 16) + r, column l % 16 of each 16 x 16 block of its 32 x 64 part).
+template <typename TC, int EPI>
+__device__ __forceinline__ void rgemm_epilogue(const VArgs& a, const f32x4_t (&acc)[2][4], float* Cs, int m0, int n0,
+                                               int wm, int wn, int wave, int lane) {
+  if constexpr (EPI == VEPI_STORE) {
+    // fp32 partial sums: 16 lanes store 64 contiguous bytes
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int gn = n0 + wn * 64 + j * 16 + lane % 16;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int gm = m0 + wm * 32 + i * 16 + 4 * (lane / 16) + r;
+          if (gm < a.M && gn < a.N)
+            reinterpret_cast<float*>(a.C)[blockIdx.z * a.c_zstride + int64_t(gm) * a.ldc + gn] = acc[i][j][r];
+        }
+      }
+    return;
+  }
+  // Add into the activation gradient through LDS: each wave stages 16 rows x
+  // 64 columns at a time and reads them back as 8 consecutive columns per
+  // lane, for 16-byte read-modify-write accesses.
+  constexpr int EP = 64 + 4;
+  float* stg = Cs + wave * 16 * EP;
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) stg[(4 * (lane / 16) + r) * EP + j * 16 + lane % 16] = acc[i][j][r];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int u = lane + 64 * h, rr = u / 8, c8 = (u % 8) * 8;
+      const int gm = m0 + wm * 32 + i * 16 + rr, gn = n0 + wn * 64 + c8;
+      if (gm >= a.M) continue;
+      float v[8];
+      const float4 lo = *reinterpret_cast<const float4*>(&stg[rr * EP + c8]);
+      const float4 hi = *reinterpret_cast<const float4*>(&stg[rr * EP + c8 + 4]);
+      v[0] = lo.x; v[1] = lo.y; v[2] = lo.z; v[3] = lo.w; v[4] = hi.x; v[5] = hi.y; v[6] = hi.z; v[7] = hi.w;
+      TC* c = reinterpret_cast<TC*>(a.C) + int64_t(gm) * a.ldc + gn;
+      if (gn + 8 <= a.N) {
+        constexpr int VC = 16 / int(sizeof(TC));
+        float o[8];
+#pragma unroll
+        for (int e = 0; e < 8; e += VC) Vec16<TC>::load(c + e, o + e);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) o[e] = o[e] + v[e];
+#pragma unroll
+        for (int e = 0; e < 8; e += VC) Vec16<TC>::store(c + e, o + e);
+      } else {
+        for (int e = 0; e < 8; ++e)
+          if (gn + e < a.N) Elem<TC>::store(c + e, Elem<TC>::load(c + e) + v[e]);
+      }
+    }
+  }
+}
+
 template <typename TB, bool A_MK, typename TC, int EPI>
 __global__ __launch_bounds__(256) void rgemm_kernel(VArgs a) {
   constexpr int BM = kRgBM, BN = kRgBN, BK = kRgBK;
@@ -150,59 +209,115 @@ __global__ __launch_bounds__(256) void rgemm_kernel(VArgs a) {
         for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(af[i], bf[j], acc[i][j], 0, 0, 0);
     }
   }
-  if constexpr (EPI == VEPI_STORE) {
-    // fp32 partial sums: a lane holds rows 4 (l / 16) + r, column l % 16 of
-    // each 16 x 16 block; 16 lanes store 64 contiguous bytes
+  rgemm_epilogue<TC, EPI>(a, acc, Cs, m0, n0, wm, wn, wave, lane);
+}
+
+// bf16-activation variant on the bf16 matrix cores (v_mfma_f32_16x16x32_bf16):
+// both operands are rounded to bf16 once (round to nearest even; x already
+// is bf16), the products are accumulated in fp32. Same tiling, chunking,
+// index maps and epilogues as rgemm_kernel; the LDS tiles are K-contiguous
+// ([m][k], [n][k]) so that a lane reads its 8 K values as 16 bytes.
+template <typename TB, bool A_MK, typename TC, int EPI>
+__global__ __launch_bounds__(256) void rgemm_bf16_kernel(VArgs a) {
+  constexpr int BM = kRgBM, BN = kRgBN, BK = kRgBK;
+  constexpr int PK = BK + 8;                // LDS row pitch (bf16): 80 bytes, 16-byte aligned
+  constexpr int VB = 16 / int(sizeof(TB));  // B elements per 16-byte load
+  constexpr int NA = BM * BK / 4 / 256;
+  constexpr int NB = BN * BK / VB / 256;
+  __shared__ __attribute__((aligned(16))) bf16_t As[BM * PK];  // [m][k]
+  __shared__ __attribute__((aligned(16))) bf16_t Bs[BN * PK];  // [n][k]
+  __shared__ __attribute__((aligned(16))) float Cs[EPI == VEPI_ADD_ACT ? 4 * 16 * (64 + 4) : 4];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int m0 = blockIdx.y * BM, n0 = blockIdx.x * BN;
+  const int kb = blockIdx.z * a.kchunk;
+  const int ke = min(a.K, kb + a.kchunk);
+  const float* A = reinterpret_cast<const float*>(a.A);
+  const bool a_vec = (a.lda & 3) == 0;
+  auto a_pos = [&](int i, int& m, int& kk) {
+    const int q = (tid + 256 * i) * 4;
+    if (A_MK) { m = q / BK; kk = q % BK; } else { kk = q / BM; m = q % BM; }
+  };
+  float ra[NA][4], rb[NB][VB];
+  auto gload = [&](int k0) {
+#pragma unroll
+    for (int i = 0; i < NA; ++i) {
+      int m, kk;
+      a_pos(i, m, kk);
+      const int gm = m0 + m, gk = k0 + kk;
+      const bool full = A_MK ? (gm < a.M && gk + 4 <= ke) : (gk < ke && gm + 4 <= a.M);
+      if (full && a_vec) {
+        const float4 v = *reinterpret_cast<const float4*>(A_MK ? A + int64_t(gm) * a.lda + gk
+                                                                : A + int64_t(gk) * a.lda + gm);
+        ra[i][0] = v.x; ra[i][1] = v.y; ra[i][2] = v.z; ra[i][3] = v.w;
+      } else {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int mm = A_MK ? gm : gm + j, kq = A_MK ? gk + j : gk;
+          ra[i][j] = (mm < a.M && kq < ke) ? (A_MK ? A[int64_t(mm) * a.lda + kq] : A[int64_t(kq) * a.lda + mm]) : 0.0f;
+        }
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < NB; ++i) {
+      const int q = (tid + 256 * i) * VB;
+      const int n = q % BN, kk = q / BN;
+      const int gn = n0 + n, gk = k0 + kk;
+      const TB* p = reinterpret_cast<const TB*>(a.B) + int64_t(gk) * a.ldb + gn;
+      if (gk < ke && gn + VB <= a.N) {
+        Vec16<TB>::load(p, rb[i]);
+      } else {
+#pragma unroll
+        for (int j = 0; j < VB; ++j) rb[i][j] = (gk < ke && gn + j < a.N) ? Elem<TB>::load(p + j) : 0.0f;
+      }
+    }
+  };
+  f32x4_t acc[2][4];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+  if (kb < ke) gload(kb);
+  for (int k0 = kb; k0 < ke; k0 += BK) {
+    __syncthreads();  // the previous chunk's reads are done
+#pragma unroll
+    for (int i = 0; i < NA; ++i) {
+      int m, kk;
+      a_pos(i, m, kk);
+      if (A_MK) {
+        const uint32_t lo = uint32_t(f32_to_bf16(ra[i][0])) | (uint32_t(f32_to_bf16(ra[i][1])) << 16);
+        const uint32_t hi = uint32_t(f32_to_bf16(ra[i][2])) | (uint32_t(f32_to_bf16(ra[i][3])) << 16);
+        *reinterpret_cast<uint2*>(&As[m * PK + kk]) = make_uint2(lo, hi);
+      } else {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) As[(m + j) * PK + kk] = f32_to_bf16(ra[i][j]);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < NB; ++i) {
+      const int q = (tid + 256 * i) * VB;
+      const int n = q % BN, kk = q / BN;
+#pragma unroll
+      for (int j = 0; j < VB; ++j) Bs[(n + j) * PK + kk] = f32_to_bf16(rb[i][j]);
+    }
+    __syncthreads();
+    if (k0 + BK < ke) gload(k0 + BK);
+    // fragments: lane holds A(m = l % 16, k = 8 (l / 16) .. + 8), B likewise in n
+    bf16x8_t af[2], bf[4];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+      af[i] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4*>(
+                                               &As[(wm * 32 + i * 16 + lane % 16) * PK + 8 * (lane / 16)]));
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      bf[j] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4*>(
+                                               &Bs[(wn * 64 + j * 16 + lane % 16) * PK + 8 * (lane / 16)]));
 #pragma unroll
     for (int i = 0; i < 2; ++i)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int gn = n0 + wn * 64 + j * 16 + lane % 16;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int gm = m0 + wm * 32 + i * 16 + 4 * (lane / 16) + r;
-          if (gm < a.M && gn < a.N)
-            reinterpret_cast<float*>(a.C)[blockIdx.z * a.c_zstride + int64_t(gm) * a.ldc + gn] = acc[i][j][r];
-        }
-      }
-    return;
+      for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bf[j], acc[i][j], 0, 0, 0);
   }
-  // Add into the activation gradient through LDS: each wave stages 16 rows x
-  // 64 columns at a time and reads them back as 8 consecutive columns per
-  // lane, for 16-byte read-modify-write accesses.
-  constexpr int EP = 64 + 4;
-  float* stg = Cs + wave * 16 * EP;
-#pragma unroll
-  for (int i = 0; i < 2; ++i) {
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) stg[(4 * (lane / 16) + r) * EP + j * 16 + lane % 16] = acc[i][j][r];
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const int u = lane + 64 * h, rr = u / 8, c8 = (u % 8) * 8;
-      const int gm = m0 + wm * 32 + i * 16 + rr, gn = n0 + wn * 64 + c8;
-      if (gm >= a.M) continue;
-      float v[8];
-      const float4 lo = *reinterpret_cast<const float4*>(&stg[rr * EP + c8]);
-      const float4 hi = *reinterpret_cast<const float4*>(&stg[rr * EP + c8 + 4]);
-      v[0] = lo.x; v[1] = lo.y; v[2] = lo.z; v[3] = lo.w; v[4] = hi.x; v[5] = hi.y; v[6] = hi.z; v[7] = hi.w;
-      TC* c = reinterpret_cast<TC*>(a.C) + int64_t(gm) * a.ldc + gn;
-      if (gn + 8 <= a.N) {
-        constexpr int VC = 16 / int(sizeof(TC));
-        float o[8];
-#pragma unroll
-        for (int e = 0; e < 8; e += VC) Vec16<TC>::load(c + e, o + e);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) o[e] = o[e] + v[e];
-#pragma unroll
-        for (int e = 0; e < 8; e += VC) Vec16<TC>::store(c + e, o + e);
-      } else {
-        for (int e = 0; e < 8; ++e)
-          if (gn + e < a.N) Elem<TC>::store(c + e, Elem<TC>::load(c + e) + v[e]);
-      }
-    }
-  }
+  rgemm_epilogue<TC, EPI>(a, acc, Cs, m0, n0, wm, wn, wave, lane);
 }
 
 // out[i] = sum_z part[z][i] for z = 0..Z-1 in order (deterministic).
@@ -215,11 +330,15 @@ __global__ __launch_bounds__(256) void reduce_parts_kernel(const float* __restri
   }
 }
 
-template <typename TB, bool A_MK, typename TC, int EPI>
+// BF16: bf16 matrix cores (bf16 activations), else fp32 matrix cores
+template <bool BF16, typename TB, bool A_MK, typename TC, int EPI>
 static void launch_rgemm(VArgs a, hipStream_t st, int zsplit = 1) {
   a.kchunk = (a.K + zsplit - 1) / zsplit;
   dim3 grid((a.N + kRgBN - 1) / kRgBN, (a.M + kRgBM - 1) / kRgBM, zsplit);
-  rgemm_kernel<TB, A_MK, TC, EPI><<<grid, 256, 0, st>>>(a);
+  if constexpr (BF16)
+    rgemm_bf16_kernel<TB, A_MK, TC, EPI><<<grid, 256, 0, st>>>(a);
+  else
+    rgemm_kernel<TB, A_MK, TC, EPI><<<grid, 256, 0, st>>>(a);
 }
 
 // ---------------------------------------------------------------------------
@@ -814,7 +933,8 @@ static void route_bwd_t(const RouteBwdLaunch& r, hipStream_t st) {
   v.B = r.w_router; v.ldb = r.d;
   v.C = r.dx; v.ldc = r.d;
   v.M = int(r.T); v.N = int(r.d); v.K = int(r.E);
-  launch_rgemm<float, true, TX, VEPI_ADD_ACT>(v, st);
+  constexpr bool BF16 = sizeof(TX) == 2;
+  launch_rgemm<BF16, float, true, TX, VEPI_ADD_ACT>(v, st);
 
   // dw[e,:] = sum_t dL[t,e] x[t,:], tokens split into Z chunks whose partial
   // sums are added in chunk order
@@ -825,7 +945,7 @@ static void route_bwd_t(const RouteBwdLaunch& r, hipStream_t st) {
   w.C = Z > 1 ? r.dw_part : r.dw_router; w.ldc = r.d;
   w.c_zstride = r.E * r.d;
   w.M = int(r.E); w.N = int(r.d); w.K = int(r.T);
-  launch_rgemm<TX, false, float, VEPI_STORE>(w, st, Z);
+  launch_rgemm<BF16, TX, false, float, VEPI_STORE>(w, st, Z);
   if (Z > 1) {
     const int64_t n = r.E * r.d;
     reduce_parts_kernel<<<int((n + 255) / 256 < 4096 ? (n + 255) / 256 : 4096), 256, 0, st>>>(
