@@ -354,16 +354,20 @@ static void launch_rgemm(VArgs a, hipStream_t st, int zsplit = 1) {
 // reads of the weight tile conflict-free; token rows are shared by 16 lanes
 // (broadcast). d must be a multiple of 32.
 // ---------------------------------------------------------------------------
-constexpr int kLgTM = 64, kLgTN = 64, kLgKC = 32, kLgP = kLgKC + 4;
+constexpr int kLgTM = 64, kLgKC = 32, kLgP = kLgKC + 4;
 
-template <typename TX>
+// TN = 64 experts per block, or 32 when 64 would leave fewer than two blocks
+// per CU (then a thread holds 4 x 2 recurrences)
+template <typename TX, int TN>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void logits_kernel(const TX* __restrict__ x, const float* __restrict__ w,
                                                      const float* __restrict__ bias, float* __restrict__ out,
                                                      int T, int E, int d) {
+  constexpr int FN = TN / 16;                  // expert columns per thread
+  constexpr int WL = TN * kLgKC / 4 / 256;     // w loads per thread
   __shared__ __attribute__((aligned(16))) float As[2][kLgTM * kLgP];
-  __shared__ __attribute__((aligned(16))) float Bs[2][kLgTN * kLgP];
+  __shared__ __attribute__((aligned(16))) float Bs[2][TN * kLgP];
   const int tid = threadIdx.x;
-  const int t0 = blockIdx.y * kLgTM, e0 = blockIdx.x * kLgTN;
+  const int t0 = blockIdx.y * kLgTM, e0 = blockIdx.x * TN;
   const int tm = tid / 16, tn = tid % 16;
   // global -> register plan. x chunk: 64 rows x 32 values; w chunk: 64 rows x 32 floats
   constexpr int XV = 16 / sizeof(TX);              // x values per 16-byte load
@@ -375,16 +379,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void l
     xrow[q] = idx / (kLgKC / XV);
     xk[q] = (idx % (kLgKC / XV)) * XV;
   }
-  int wrow[2], wk[2];
+  int wrow[WL], wk[WL];
 #pragma unroll
-  for (int q = 0; q < 2; ++q) {
+  for (int q = 0; q < WL; ++q) {
     const int idx = tid + 256 * q;
     wrow[q] = idx / (kLgKC / 4);
     wk[q] = (idx % (kLgKC / 4)) * 4;
   }
   const int nch = d / kLgKC;
   float xv[XL][XV];
-  float4 wv[2];
+  float4 wv[WL];
   auto gload = [&](int c) {
     const int k0 = c * kLgKC;
 #pragma unroll
@@ -398,7 +402,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void l
       }
     }
 #pragma unroll
-    for (int q = 0; q < 2; ++q) {
+    for (int q = 0; q < WL; ++q) {
       const int e = e0 + wrow[q];
       wv[q] = e < E ? *reinterpret_cast<const float4*>(w + int64_t(e) * d + k0 + wk[q])
                     : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
@@ -412,25 +416,25 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void l
         *reinterpret_cast<float4*>(&As[buf][xrow[q] * kLgP + xk[q] + v]) =
             make_float4(xv[q][v], xv[q][v + 1], xv[q][v + 2], xv[q][v + 3]);
 #pragma unroll
-    for (int q = 0; q < 2; ++q) *reinterpret_cast<float4*>(&Bs[buf][wrow[q] * kLgP + wk[q]]) = wv[q];
+    for (int q = 0; q < WL; ++q) *reinterpret_cast<float4*>(&Bs[buf][wrow[q] * kLgP + wk[q]]) = wv[q];
   };
-  float acc[4][4];
+  float acc[4][FN];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = 0.0f;
+    for (int j = 0; j < FN; ++j) acc[i][j] = 0.0f;
   auto compute = [&](int buf) {
 #pragma unroll 2
     for (int k = 0; k < kLgKC; k += 4) {
-      float4 a[4], b[4];
+      float4 a[4], b[FN];
 #pragma unroll
       for (int i = 0; i < 4; ++i) a[i] = *reinterpret_cast<const float4*>(&As[buf][(tm + 16 * i) * kLgP + k]);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) b[j] = *reinterpret_cast<const float4*>(&Bs[buf][(tn + 16 * j) * kLgP + k]);
+      for (int j = 0; j < FN; ++j) b[j] = *reinterpret_cast<const float4*>(&Bs[buf][(tn + 16 * j) * kLgP + k]);
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
+        for (int j = 0; j < FN; ++j) {
           acc[i][j] = __builtin_fmaf(a[i].x, b[j].x, acc[i][j]);
           acc[i][j] = __builtin_fmaf(a[i].y, b[j].y, acc[i][j]);
           acc[i][j] = __builtin_fmaf(a[i].z, b[j].z, acc[i][j]);
@@ -453,7 +457,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void l
     const int t = t0 + tm + 16 * i;
     if (t >= T) continue;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
+    for (int j = 0; j < FN; ++j) {
       const int e = e0 + tn + 16 * j;
       if (e >= E) continue;
       float v = acc[i][j];
@@ -889,9 +893,14 @@ __global__ __launch_bounds__(256) void dlogits_kernel(DLArgs a) {
 template <typename TX>
 static void route_fwd_t(const RouteLaunch& r, hipStream_t st) {
   if (r.E >= 32) {
-    const dim3 grid(unsigned((r.E + kLgTN - 1) / kLgTN), unsigned((r.T + kLgTM - 1) / kLgTM));
-    logits_kernel<TX><<<grid, 256, 0, st>>>(reinterpret_cast<const TX*>(r.x), r.w_router, r.bias, r.logits,
-                                            int(r.T), int(r.E), int(r.d));
+    const unsigned gy = unsigned((r.T + kLgTM - 1) / kLgTM);
+    const int64_t blocks64 = int64_t((r.E + 63) / 64) * gy;
+    if (blocks64 >= 512)
+      logits_kernel<TX, 64><<<dim3(unsigned((r.E + 63) / 64), gy), 256, 0, st>>>(
+          reinterpret_cast<const TX*>(r.x), r.w_router, r.bias, r.logits, int(r.T), int(r.E), int(r.d));
+    else
+      logits_kernel<TX, 32><<<dim3(unsigned((r.E + 31) / 32), gy), 256, 0, st>>>(
+          reinterpret_cast<const TX*>(r.x), r.w_router, r.bias, r.logits, int(r.T), int(r.E), int(r.d));
   } else {
     launch_logits_small_e<TX>(r, st);
   }

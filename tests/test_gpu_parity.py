@@ -253,6 +253,30 @@ def test_fp8_dispatch_bit_exact():
     assert np.array_equal(_np(out["xs"]), oracle.permute(xs, rmap))
 
 
+# (T, E): 64 experts per workgroup (>= 512 workgroups) and 32 per workgroup,
+# with ragged token and expert tiles
+ROUTE_TILE_CASES = [(16384, 128), (300, 64), (1000, 96), (8192, 72)]
+
+
+@pytest.mark.parametrize("T,E", ROUTE_TILE_CASES)
+def test_route_logits_tilings(T, E):
+    from mixture_experts_layer_gather_amd import make_config, moe_route, workspace_size
+    cfg = S.mini(S.CONFIGS[3], T=T, d=256, f=128, E=E).replace(k=4)
+    _say(f"[route tiles] T={T} E={E}")
+    x, wr = S.x(cfg), S.w_router(cfg)
+    bias = S.router_bias(cfg)
+    L = oracle.router_logits(x, wr, None if bias is None else bias)
+    c = make_config(**cfg.describe())
+    logits = torch.empty(T, E, dtype=torch.float32, device=DEV)
+    idx = torch.empty(T, cfg.k, dtype=torch.int32, device=DEV)
+    gate = torch.empty(T, cfg.k, dtype=torch.float32, device=DEV)
+    ws = torch.empty(max(1, workspace_size(c, 0)), dtype=torch.uint8, device=DEV)
+    moe_route(c, x.to(DEV), wr.to(DEV), None if bias is None else bias.to(DEV), logits, idx, gate, ws=ws)
+    torch.cuda.synchronize()
+    assert np.array_equal(_np(logits), L)
+    assert np.array_equal(_np(idx), oracle.route_select(L, cfg.k))
+
+
 def _random_routing(T, E, k, seed, skew):
     """k distinct experts per token; skew > 0 draws experts with Zipf-like
     weights (hot experts, some empty ones)."""
