@@ -77,60 +77,89 @@ def summarize_profiles(cfg_name, stats_dir, fetch_dir, write_dir, copy_fetch_dir
         lines.append(f"| {float(r['AverageNs']) / 1e3:.1f} | {r['Calls']} | "
                      f"{100 * float(r['TotalDurationNs']) / tot:.1f} | `{r['Name'][:140]}` |")
 
-    # library calls: GEMM kernels by role, per step (steps = GEMM1 launches)
-    role_ns = collections.defaultdict(float)
-    role_calls = collections.defaultdict(int)
-    for r in stats:
-        role = kernel_role(r["Name"])
-        if role:
-            role_ns[role] += float(r["TotalDurationNs"])
-            role_calls[role] += int(r["Calls"])
-    steps = max(1, role_calls.get("gemm1", 1))
+    # library calls: GEMM launches by role, per step. Steps = router selection
+    # launches (one per step). Within a step the routed experts' call comes
+    # before the shared expert's, so a role's first launch(es) of each step
+    # (two for wgrad: dW2, dW1) are the routed call's, the rest the shared's.
+    def by_step(rows, value):
+        rows = sorted(rows, key=lambda r: int(r["Dispatch_Id"]))
+        steps = sum(1 for r in rows if "select_kernel" in r["Kernel_Name"])
+        seq = collections.defaultdict(list)
+        for r in rows:
+            role = kernel_role(r["Kernel_Name"])
+            if role:
+                seq[role].append(value(r))
+        split = {}
+        for role, vals in seq.items():
+            n = len(vals) // max(1, steps)
+            if steps == 0 or n * steps != len(vals):
+                raise ValueError(f"{role}: {len(vals)} launches in {steps} steps")
+            nr = 2 if role == "wgrad" else 1
+            routed = [v for i, v in enumerate(vals) if i % n < nr]
+            shared = [v for i, v in enumerate(vals) if i % n >= nr]
+            split[role] = (routed, shared, nr, n - nr)
+        return steps, split
+
+    trace = list(csv.DictReader(open(os.path.join(stats_dir, "run_kernel_trace.csv"))))
+    steps, tsplit = by_step(trace, lambda r: int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
     lines += ["", "## Library calls per step (sum of their GEMM kernels)", "",
-              f"Steps in the trace: {steps} (warm-up included).", "",
+              f"Steps in the trace: {steps} (warm-up included); launches of the routed experts' "
+              "calls, then of the shared expert's where there is one.", "",
               "| call | ms per step | kernels (avg us x launches per step) |", "|---|---:|---|"]
-    by_call = collections.defaultdict(list)
-    for role in ("gemm1", "gemm2", "dh", "dx", "wgrad"):
-        if role in role_ns:
-            by_call[ROLE_CALL[role]].append(role)
-    for call, rs in by_call.items():
-        ms = sum(role_ns[x] for x in rs) / steps / 1e6
-        parts = ", ".join(f"{x} {role_ns[x] / role_calls[x] / 1e3:.0f} x {role_calls[x] / steps:g}"
-                          for x in rs)
-        lines.append(f"| {call} | {ms:.3f} | {parts} |")
+    roles_order = ("gemm1", "gemm2", "dh", "dx", "wgrad")
+    for which, prefix in ((0, "grouped"), (1, "shared")):
+        for fb in ("ffn", "ffn_bwd"):
+            call = f"{prefix}_{fb}"
+            rs = [x for x in roles_order if x in tsplit and ROLE_CALL[x] == f"grouped_{fb}"
+                  and tsplit[x][which]]
+            if not rs:
+                continue
+            ms = sum(sum(tsplit[x][which]) for x in rs) / steps / 1e6
+            parts = ", ".join(f"{x} {sum(tsplit[x][which]) / len(tsplit[x][which]) / 1e3:.0f} x "
+                              f"{tsplit[x][2 + which]}" for x in rs)
+            lines.append(f"| {call} | {ms:.3f} | {parts} |")
 
-    def per_kernel(d):
-        agg = collections.defaultdict(list)
-        for r in csv.DictReader(open(os.path.join(d, "run_counter_collection.csv"))):
-            agg[r["Kernel_Name"]].append(float(r["Counter_Value"]))
-        return {k: sum(v) / len(v) for k, v in agg.items()}
+    def counters(d):
+        return list(csv.DictReader(open(os.path.join(d, "run_counter_collection.csv"))))
 
-    cf, cw = per_kernel(copy_fetch_dir), per_kernel(copy_write_dir)
-    copy_name = [k for k in cf if "copyBuffer" in k][0]
-    f_fetch = (1 << 30) / (cf[copy_name] * 1024)
-    f_write = (1 << 30) / (cw[copy_name] * 1024)
-    kf, kw = per_kernel(fetch_dir), per_kernel(write_dir)
-    roles = collections.defaultdict(lambda: [0.0, 0.0, 0])
-    for name in kf:
-        role = kernel_role(name)
-        if role:
-            r = roles[role]
-            r[0] += kf[name] * 1024 * f_fetch
-            r[1] += kw.get(name, 0.0) * 1024 * f_write
-            r[2] += 1
+    def copy_kib(d):
+        v = [float(r["Counter_Value"]) for r in counters(d) if "copyBuffer" in r["Kernel_Name"]]
+        return sum(v) / len(v)
+
+    f_fetch = (1 << 30) / (copy_kib(copy_fetch_dir) * 1024)
+    f_write = (1 << 30) / (copy_kib(copy_write_dir) * 1024)
+    _, fsplit = by_step(counters(fetch_dir), lambda r: float(r["Counter_Value"]) * 1024 * f_fetch)
+    _, wsplit = by_step(counters(write_dir), lambda r: float(r["Counter_Value"]) * 1024 * f_write)
+
+    def per_launch(split, role, which):
+        vals = split[role][which]
+        nper = split[role][2 + which]
+        return sum(vals) / len(vals) * nper if vals else 0.0  # bytes per step of the role
+
+    roles = {}
+    for role in roles_order:
+        if role in fsplit:
+            n = fsplit[role][2]
+            roles[role] = [per_launch(fsplit, role, 0) / n, per_launch(wsplit, role, 0) / n]
     calls = collections.defaultdict(float)
-    mult = {"wgrad": 2}  # dW1 and dW2 come from the same kernel
-    for role, (fb, wb, _) in roles.items():
-        calls[ROLE_CALL[role]] += (fb + wb) * mult.get(role, 1)
+    for which, prefix in ((0, "grouped"), (1, "shared")):
+        for role in roles_order:
+            if role in fsplit and fsplit[role][which]:
+                calls[f"{prefix}_{ROLE_CALL[role][len('grouped_'):]}"] += (
+                    per_launch(fsplit, role, which) + per_launch(wsplit, role, which))
     out = {"config": cfg_name, "source_hash": source_hash(), "fetch_factor": f_fetch,
            "write_factor": f_write,
            "roles_bytes_per_launch": {k: {"fetch": v[0], "write": v[1]} for k, v in roles.items()},
            "calls_bytes_per_launch": dict(calls), "commands": command}
     lines += ["", "## HBM traffic per launch (rocprofv3 --pmc FETCH_SIZE, then WRITE_SIZE)", "",
-              f"Scaled by a 1 GiB device copy: FETCH_SIZE x {f_fetch:.3f}, WRITE_SIZE x {f_write:.3f}.",
+              f"Scaled by a 1 GiB device copy: FETCH_SIZE x {f_fetch:.3f}, WRITE_SIZE x {f_write:.3f}. "
+              "Launches of the routed experts' calls (wgrad: the mean of dW2 and dW1).",
               "", "| GEMM role | fetch GB | write GB |", "|---|---:|---:|"]
     for k, v in roles.items():
         lines.append(f"| {k} | {v[0] / 1e9:.3f} | {v[1] / 1e9:.3f} |")
+    lines += ["", "| call | HBM GB per launch (fetch + write) |", "|---|---:|"]
+    for k, v in calls.items():
+        lines.append(f"| {k} | {v / 1e9:.3f} |")
     lines += ["", "Commands:", "", "```"] + [command[k] for k in ("fetch", "write", "copy_fetch",
                                                                     "copy_write")] + ["```"]
     os.makedirs(PROFILES, exist_ok=True)
