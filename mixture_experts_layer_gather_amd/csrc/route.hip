@@ -126,7 +126,8 @@ __global__ __launch_bounds__(256) void rgemm_kernel(VArgs a) {
   const int kb = blockIdx.z * a.kchunk;
   const int ke = min(a.K, kb + a.kchunk);
   const float* A = reinterpret_cast<const float*>(a.A);
-  const bool a_vec = (a.lda & 3) == 0;  // 16-byte loads along A's contiguous index
+  // 16-byte loads along A's contiguous index (A_MK: chunk starts stay 4-aligned)
+  const bool a_vec = (a.lda & 3) == 0 && (!A_MK || (a.kchunk & 3) == 0);
   // A group i: 4 values along A's contiguous index (k when A_MK, else m)
   auto a_pos = [&](int i, int& m, int& kk) {
     const int q = (tid + 256 * i) * 4;
@@ -233,7 +234,7 @@ __global__ __launch_bounds__(256) void rgemm_bf16_kernel(VArgs a) {
   const int kb = blockIdx.z * a.kchunk;
   const int ke = min(a.K, kb + a.kchunk);
   const float* A = reinterpret_cast<const float*>(a.A);
-  const bool a_vec = (a.lda & 3) == 0;
+  const bool a_vec = (a.lda & 3) == 0 && (!A_MK || (a.kchunk & 3) == 0);
   auto a_pos = [&](int i, int& m, int& kk) {
     const int q = (tid + 256 * i) * 4;
     if (A_MK) { m = q / BK; kk = q % BK; } else { kk = q / BM; m = q % BM; }
