@@ -216,17 +216,38 @@ __global__ __launch_bounds__(256) void rgemm_kernel(VArgs a) {
 // bf16-activation variant on the bf16 matrix cores (v_mfma_f32_16x16x32_bf16):
 // both operands are rounded to bf16 once (round to nearest even; x already
 // is bf16), the products are accumulated in fp32. Same tiling, chunking,
-// index maps and epilogues as rgemm_kernel; the LDS tiles are K-contiguous
-// ([m][k], [n][k]) so that a lane reads its 8 K values as 16 bytes.
+// index maps and epilogues as rgemm_kernel. A fragment holds 8 consecutive
+// K values of one row (A) or column (B): a K-contiguous tile ([m][k], A when
+// A_MK) is read as 16 bytes per lane; tiles kept in their source orientation
+// ([k][m], [k][n]) are read with the LDS transpose read ds_read_b64_tr_b16,
+// which gives lane i of a 16-lane group, slot j, element i % 4 of the 8 bytes
+// addressed by lane 4 j + i / 4 (so every tile store is 8 or 16 bytes wide).
+typedef short rg_s16x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ u32x2 rg_read_tr16(const bf16_t* p) {
+  return __builtin_bit_cast(
+      u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) rg_s16x4*)(void*)p));
+}
+// fragment of columns c0 .. c0 + 16 of a [k][col] tile with pitch P (elements)
+__device__ __forceinline__ bf16x8_t rg_frag_tr(const bf16_t* tile, int P, int c0, int lane) {
+  const int s16 = lane % 16;
+  const bf16_t* p = tile + (8 * (lane / 16) + s16 / 4) * P + c0 + 4 * (s16 % 4);
+  const u32x2 lo = rg_read_tr16(p), hi = rg_read_tr16(p + 4 * P);
+  return __builtin_bit_cast(bf16x8_t, u32x4{lo[0], lo[1], hi[0], hi[1]});
+}
+__device__ __forceinline__ uint32_t rg_pack2(float a, float b) {
+  return uint32_t(f32_to_bf16(a)) | (uint32_t(f32_to_bf16(b)) << 16);
+}
+
 template <typename TB, bool A_MK, typename TC, int EPI>
 __global__ __launch_bounds__(256) void rgemm_bf16_kernel(VArgs a) {
   constexpr int BM = kRgBM, BN = kRgBN, BK = kRgBK;
-  constexpr int PK = BK + 8;                // LDS row pitch (bf16): 80 bytes, 16-byte aligned
+  constexpr int PK = BK + 8;                // [m][k] pitch (bf16): 80 bytes
+  constexpr int PM = BM + 8, PN = BN + 8;   // [k][m], [k][n] pitches: 144, 272 bytes
   constexpr int VB = 16 / int(sizeof(TB));  // B elements per 16-byte load
   constexpr int NA = BM * BK / 4 / 256;
   constexpr int NB = BN * BK / VB / 256;
-  __shared__ __attribute__((aligned(16))) bf16_t As[BM * PK];  // [m][k]
-  __shared__ __attribute__((aligned(16))) bf16_t Bs[BN * PK];  // [n][k]
+  __shared__ __attribute__((aligned(16))) bf16_t As[A_MK ? BM * PK : BK * PM];
+  __shared__ __attribute__((aligned(16))) bf16_t Bs[BK * PN];  // [k][n]
   __shared__ __attribute__((aligned(16))) float Cs[EPI == VEPI_ADD_ACT ? 4 * 16 * (64 + 4) : 4];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
@@ -285,34 +306,35 @@ __global__ __launch_bounds__(256) void rgemm_bf16_kernel(VArgs a) {
     for (int i = 0; i < NA; ++i) {
       int m, kk;
       a_pos(i, m, kk);
-      if (A_MK) {
-        const uint32_t lo = uint32_t(f32_to_bf16(ra[i][0])) | (uint32_t(f32_to_bf16(ra[i][1])) << 16);
-        const uint32_t hi = uint32_t(f32_to_bf16(ra[i][2])) | (uint32_t(f32_to_bf16(ra[i][3])) << 16);
-        *reinterpret_cast<uint2*>(&As[m * PK + kk]) = make_uint2(lo, hi);
-      } else {
-#pragma unroll
-        for (int j = 0; j < 4; ++j) As[(m + j) * PK + kk] = f32_to_bf16(ra[i][j]);
-      }
+      // 4 values along A's contiguous index: k ([m][k] tile) or m ([k][m] tile)
+      const uint2 v = make_uint2(rg_pack2(ra[i][0], ra[i][1]), rg_pack2(ra[i][2], ra[i][3]));
+      *reinterpret_cast<uint2*>(&As[A_MK ? m * PK + kk : kk * PM + m]) = v;
     }
 #pragma unroll
     for (int i = 0; i < NB; ++i) {
       const int q = (tid + 256 * i) * VB;
-      const int n = q % BN, kk = q / BN;
-#pragma unroll
-      for (int j = 0; j < VB; ++j) Bs[(n + j) * PK + kk] = f32_to_bf16(rb[i][j]);
+      bf16_t* d = &Bs[(q / BN) * PN + q % BN];
+      if constexpr (VB == 8) {
+        *reinterpret_cast<uint4*>(d) = make_uint4(rg_pack2(rb[i][0], rb[i][1]), rg_pack2(rb[i][2], rb[i][3]),
+                                                  rg_pack2(rb[i][4], rb[i][5]), rg_pack2(rb[i][6], rb[i][7]));
+      } else {
+        *reinterpret_cast<uint2*>(d) = make_uint2(rg_pack2(rb[i][0], rb[i][1]), rg_pack2(rb[i][2], rb[i][3]));
+      }
     }
     __syncthreads();
     if (k0 + BK < ke) gload(k0 + BK);
-    // fragments: lane holds A(m = l % 16, k = 8 (l / 16) .. + 8), B likewise in n
+    // fragments: lane holds row / column l % 16, K values 8 (l / 16) .. + 8
     bf16x8_t af[2], bf[4];
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
-      af[i] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4*>(
-                                               &As[(wm * 32 + i * 16 + lane % 16) * PK + 8 * (lane / 16)]));
+    for (int i = 0; i < 2; ++i) {
+      if constexpr (A_MK)
+        af[i] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4*>(
+                                                 &As[(wm * 32 + i * 16 + lane % 16) * PK + 8 * (lane / 16)]));
+      else
+        af[i] = rg_frag_tr(As, PM, wm * 32 + i * 16, lane);
+    }
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
-      bf[j] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4*>(
-                                               &Bs[(wn * 64 + j * 16 + lane % 16) * PK + 8 * (lane / 16)]));
+    for (int j = 0; j < 4; ++j) bf[j] = rg_frag_tr(Bs, PN, wn * 64 + j * 16, lane);
 #pragma unroll
     for (int i = 0; i < 2; ++i)
 #pragma unroll
