@@ -305,13 +305,21 @@ __device__ __forceinline__ void wait_vm0() { __builtin_amdgcn_s_waitcnt(0x0f70);
 //            the transpose read serves 32 lanes (two groups, K-rows 8 apart)
 //            at a time: the swizzle separates the 4 K-rows of a group (bits
 //            1-2) and the two groups (bit 3), which makes it conflict-free.
-//   LM_REG   other K-strided sources (fp32, FP8): NT blocks of 4 K-rows x VEC
+//            FP8 (128-byte K-rows, 8 chunks): chunks are XOR-swizzled with
+//            tr8_swz(K-row) and fragments are read with ds_read_b64_tr_b8,
+//            which gives lane i of a 16-lane group, byte j, element i % 8 of
+//            the 8 bytes addressed by lane 2 j + i / 8 (measured on gfx950):
+//            lanes 2 j and 2 j + 1 address the two 8-column halves of K-row
+//            j, so a lane receives its column of 8 consecutive K-rows. The
+//            swizzle gives the 16 K-rows that two groups read together 16
+//            distinct bank windows.
+//   LM_REG   other K-strided sources (fp32): NT blocks of 4 K-rows x VEC
 //            columns per thread, loaded into registers and transposed on
 //            their way into LDS (K-major rows, swizzled as in lds_off).
 enum { LM_KDMA = 0, LM_TDMA = 1, LM_REG = 2 };
 template <typename T, bool KMAJ>
 constexpr int layout_mode() {
-  return KMAJ ? LM_KDMA : (sizeof(T) == 2 ? LM_TDMA : LM_REG);
+  return KMAJ ? LM_KDMA : (sizeof(T) <= 2 ? LM_TDMA : LM_REG);
 }
 
 template <typename T, int LM, int ROWS, int BK, int NTH>
@@ -324,14 +332,19 @@ struct OperandPlan {
   static constexpr int NREG = DMA ? 1 : 4 * NT;
   static_assert(!DMA || NB * 1024 * NW == ROWS * BK * int(sizeof(T)), "DMA blocks per wave");
   static_assert(DMA || (NT >= 1 && NT * 4 * VEC * NTH == ROWS * BK), "tile/threads");
-  static_assert(LM != LM_TDMA || (sizeof(T) == 2 && ROWS * 2 >= 256 && 1024 % (ROWS * 2) == 0),
-                "transposed tiles: bf16 rows of 256 or 512 bytes (at least 16 chunks for the swizzle)");
+  static_assert(LM != LM_TDMA || (sizeof(T) == 2 && ROWS * 2 >= 256 && 1024 % (ROWS * 2) == 0) ||
+                    (sizeof(T) == 1 && ROWS == 128),
+                "transposed tiles: bf16 rows of 256 or 512 bytes (at least 16 chunks for the swizzle), "
+                "FP8 rows of 128 bytes");
   uint32_t voff[DMA ? NB : 4 * NT];  // byte offsets from the step's base
   int lrow[DMA ? 1 : NT];            // LM_REG: first LDS row of the block
   int lk[DMA ? 1 : NT];              // LM_REG: LDS k offset
 };
 
 __device__ __forceinline__ int tr_swz(int kr) { return (2 * (kr & 3)) ^ (8 * ((kr >> 3) & 1)); }
+// FP8 K-rows of 8 chunks: K-rows 0, 2, 4, 6, 16, 18, 20, 22 (and the odd ones,
+// which sit in the other half of the banks) get chunk masks 0 .. 7
+__device__ __forceinline__ int tr8_swz(int kr) { return ((kr >> 1) & 3) | ((kr >> 2) & 4); }
 
 // 8 consecutive values: fp32 from LDS; bf16 / fp32 to and from global memory
 __device__ __forceinline__ void lds_read8(const float* p, float* v) {
@@ -480,10 +493,11 @@ void gemm_kernel(GemmArgs g) {
   // LM_TDMA: K-row kr of the tile holds ROWS elements from column col0; DMA
   // block b covers K-rows b * RPB .. + RPB
   auto tdma_voff = [&](int b, int ROWS, int64_t ld, int col0) {
-    const int CPR = ROWS * 2 / 16, RPB = 1024 / (ROWS * 2);
+    constexpr int EPC = 16 / int(ES);  // elements per 16-byte chunk
+    const int CPR = ROWS / EPC, RPB = 1024 / (ROWS * int(ES));
     const int kr = b * RPB + lane / CPR;
-    const int lc = (lane % CPR) ^ tr_swz(kr);
-    return uint32_t((int64_t(kr) * ld + col0 + lc * 8) * ES);
+    const int lc = (lane % CPR) ^ (ES == 1 ? tr8_swz(kr) : tr_swz(kr));
+    return uint32_t((int64_t(kr) * ld + col0 + lc * EPC) * ES);
   };
   if constexpr (ALM == LM_KDMA) {
 #pragma unroll
@@ -631,6 +645,22 @@ void gemm_kernel(GemmArgs g) {
           reinterpret_cast<const char*>(tile) + kr * (ROWS * 2) + (((col / 8) ^ tr_swz(kr)) * 16) + (col % 8) * 2;
       const u32x2 lo = lds_read_tr16(p), hi = lds_read_tr16(p + 4 * ROWS * 2);
       f = __builtin_bit_cast(typename MF::frag, u32x4{lo[0], lo[1], hi[0], hi[1]});
+    } else if constexpr (sizeof(T) == 1) {
+      // K chunks q and q + 4 of the 128-deep block (q = lane / 16), 8 K-rows
+      // per transpose read: K-rows 16 q, 16 q + 8, 64 + 16 q, 72 + 16 q
+      const int s16 = lane % 16, j = s16 / 2, h = s16 % 2;
+      const int col = c0 + 8 * h;
+      int w[8];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int kr = 16 * (lane / 16) + 8 * (r & 1) + 64 * (r >> 1) + j;
+        const char* p = reinterpret_cast<const char*>(tile) + kr * ROWS + (((col / 16) ^ tr8_swz(kr)) * 16) + col % 16;
+        const i32x2 v = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+            (__attribute__((address_space(3))) i32x2*)(void*)p);
+        w[2 * r] = v[0];
+        w[2 * r + 1] = v[1];
+      }
+      f = i32x8_t{w[0], w[1], w[2], w[3], w[4], w[5], w[6], w[7]};
     }
     return f;
   };
