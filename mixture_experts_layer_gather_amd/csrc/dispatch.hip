@@ -90,16 +90,86 @@ __global__ __launch_bounds__(1024) void dispatch_scan_kernel(int32_t* __restrict
 }
 
 // --- 3. positions: row of every (token, slot) -----------------------------
+// SCAN = false: chunk_base holds the scanned bases (kernel 2).
+// SCAN = true (few chunks): chunk_base holds the raw per-chunk counts of
+// kernel 1, and every block derives its own chunk's bases from them (expert
+// totals, their exclusive scan, plus the earlier chunks' counts; integer sums
+// in any order); block 0 also writes counts and offsets. One launch fewer.
+// SCAN = true up to this many chunks (measured: 16 chunks x 8 experts 8.9 ->
+// 6.1 us for scan + positions; 64 chunks x 128 experts 14.0 -> 14.9 us)
+constexpr int kScanInPosChunks = 32;
+template <bool SCAN>
 __global__ __launch_bounds__(256) void dispatch_pos_kernel(const int32_t* __restrict__ idx,
                                                            const int32_t* __restrict__ chunk_base,
+                                                           int32_t* __restrict__ counts,
+                                                           int32_t* __restrict__ offsets,
                                                            int32_t* __restrict__ row_id_map,
                                                            int32_t* __restrict__ perm_token,
                                                            int T, int E, int k) {
-  // bits[e][w]: bit b set when token c*256 + 32w + b of this chunk goes to e
+  // bits[e][w]: bit b set when token c*256 + 32w + b of this chunk goes to e;
+  // SCAN: s_base[e] = first row of expert e's tokens in this chunk
   extern __shared__ uint32_t bits[];
   constexpr int W = kChunkTok / 32;
   const int c = blockIdx.x;
+  int32_t* s_base = reinterpret_cast<int32_t*>(bits + E * W);
   for (int i = threadIdx.x; i < E * W; i += 256) bits[i] = 0;
+  if constexpr (SCAN) {
+    __shared__ int32_t s_wave[4];
+    const int nchunks = (T + kChunkTok - 1) / kChunkTok;
+    // thread t owns experts 4t .. 4t + 3 (E <= 1024)
+    int32_t tot[4] = {0, 0, 0, 0}, pre[4] = {0, 0, 0, 0};
+    const int e0 = 4 * threadIdx.x;
+    if (e0 < E) {
+      // 8 chunks' loads in flight at a time; 16-byte loads when rows allow
+      const bool vec = (E & 3) == 0;
+      for (int c0 = 0; c0 < nchunks; c0 += 8) {
+        int4 v[8];
+#pragma unroll
+        for (int b = 0; b < 8; ++b) {
+          const int cc = c0 + b;
+          const int32_t* p = chunk_base + int64_t(cc) * E + e0;
+          if (cc >= nchunks) v[b] = make_int4(0, 0, 0, 0);
+          else if (vec) v[b] = *reinterpret_cast<const int4*>(p);
+          else v[b] = make_int4(p[0], e0 + 1 < E ? p[1] : 0, e0 + 2 < E ? p[2] : 0, e0 + 3 < E ? p[3] : 0);
+        }
+#pragma unroll
+        for (int b = 0; b < 8; ++b) {
+          const int32_t w4[4] = {v[b].x, v[b].y, v[b].z, v[b].w};
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            tot[u] += w4[u];
+            if (c0 + b < c) pre[u] += w4[u];
+          }
+        }
+      }
+    }
+    const int32_t mine = tot[0] + tot[1] + tot[2] + tot[3];
+    const int lane = lane_id(), wave = threadIdx.x / kWave;
+    int32_t inc = mine;
+#pragma unroll
+    for (int o = 1; o < kWave; o <<= 1) {
+      const int32_t u = __shfl_up(inc, o, kWave);
+      if (lane >= o) inc += u;
+    }
+    if (lane == kWave - 1) s_wave[wave] = inc;
+    __syncthreads();
+    int32_t before = 0;
+    for (int w = 0; w < wave; ++w) before += s_wave[w];
+    int32_t run = before + inc - mine;  // exclusive prefix over experts < e0
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int e = e0 + u;
+      if (e < E) {
+        s_base[e] = run + pre[u];
+        if (c == 0) {
+          counts[e] = tot[u];
+          offsets[e] = run;
+          if (e == E - 1) offsets[E] = run + tot[u];
+        }
+      }
+      run += tot[u];
+    }
+  }
   __syncthreads();
   const int tl = threadIdx.x;
   const int t = c * kChunkTok + tl;
@@ -119,7 +189,7 @@ __global__ __launch_bounds__(256) void dispatch_pos_kernel(const int32_t* __rest
       const uint32_t* be = bits + e * W;
       int rank = __popc(be[w] & below);
       for (int i = 0; i < w; ++i) rank += __popc(be[i]);
-      const int32_t row = chunk_base[int64_t(c) * E + e] + rank;
+      const int32_t row = (SCAN ? s_base[e] : chunk_base[int64_t(c) * E + e]) + rank;
       row_id_map[int64_t(t) * k + j] = row;
       perm_token[row] = t;
     }
@@ -202,9 +272,15 @@ void launch_dispatch(const DispatchLaunch& a, hipStream_t st) {
   const int T = int(a.T), E = int(a.E), k = int(a.k);
   const int nchunks = int(dispatch_chunks(a.T));
   dispatch_count_kernel<<<nchunks, 256, sizeof(int32_t) * E, st>>>(a.idx, a.chunk_base, T, E, k);
-  dispatch_scan_kernel<<<1, 1024, 0, st>>>(a.chunk_base, a.counts, a.offsets, nchunks, E);
-  dispatch_pos_kernel<<<nchunks, 256, sizeof(uint32_t) * E * (kChunkTok / 32), st>>>(
-      a.idx, a.chunk_base, a.row_id_map, a.perm_token, T, E, k);
+  const size_t bits_lds = sizeof(uint32_t) * E * (kChunkTok / 32);
+  if (nchunks <= kScanInPosChunks) {
+    dispatch_pos_kernel<true><<<nchunks, 256, bits_lds + sizeof(int32_t) * E, st>>>(
+        a.idx, a.chunk_base, a.counts, a.offsets, a.row_id_map, a.perm_token, T, E, k);
+  } else {
+    dispatch_scan_kernel<<<1, 1024, 0, st>>>(a.chunk_base, a.counts, a.offsets, nchunks, E);
+    dispatch_pos_kernel<false><<<nchunks, 256, bits_lds, st>>>(a.idx, a.chunk_base, a.counts, a.offsets,
+                                                               a.row_id_map, a.perm_token, T, E, k);
+  }
   if (a.fp8) {
     dispatch_gather_fp8_kernel<<<T, 256, 0, st>>>(reinterpret_cast<const bf16_t*>(a.x), a.row_id_map,
                                                   reinterpret_cast<uint8_t*>(a.x_perm), a.x_scale, T,

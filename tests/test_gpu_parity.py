@@ -287,9 +287,11 @@ def _random_routing(T, E, k, seed, skew):
 
 
 # (T, E, k, skew): ragged last chunks, E up to the 1024 limit, k = E, hot and
-# empty experts
+# empty experts; up to 32 chunks of 256 tokens the positions kernel derives
+# its bases itself, beyond that a separate scan runs
 DISPATCH_INDEX_CASES = [(3000, 24, 3, 0.0), (1024, 1024, 8, 1.1), (4096, 8, 8, 0.0),
-                        (12000, 16, 4, 1.2), (2000, 600, 2, 0.0), (257, 5, 5, 0.0)]
+                        (12000, 16, 4, 1.2), (2000, 600, 2, 0.0), (257, 5, 5, 0.0),
+                        (8192, 6, 2, 0.3), (8193, 16, 2, 0.5), (70000, 16, 2, 0.5)]
 
 
 @pytest.mark.parametrize("T,E,k,skew", DISPATCH_INDEX_CASES)
