@@ -227,6 +227,9 @@ int moe_dispatch_bwd(const moe_config *cfg, const void *dx_perm,
  *   dL = d(gates)/d(logits)^T d_gate for the configured score function,
  *   dw_router = dL^T x   ([E,d] f32, overwritten)
  *   dx += dL w_router    ([T,d] act, read-modify-write)
+ * Both products accumulate in fp32; with bf16 activations their operands
+ * (dL, x, w_router) are rounded to bf16 first, with fp32 activations they
+ * stay fp32. Results are deterministic (fixed summation order).
  * Inputs are those of moe_route plus its outputs and d_gate [T,k] f32.
  * Workspace: moe_workspace_size(cfg, MOE_OP_ROUTE_BWD). */
 int moe_route_bwd(const moe_config *cfg, const void *x, const float *w_router,
