@@ -130,23 +130,33 @@ struct GemmArgs {
   const float* b_scale;      // [G, R/128, C/128] of B's storage [G, R, C]
   int64_t b_scale_gstride;   // (R/128)*(C/128)
   int b_scale_ld;            // C/128
+  int ksuper;                // tiles per XCD super-block (set by run_gemm)
 };
 
 // Workgroup id -> tile. Consecutive ids are dispatched to the 8 XCDs round
-// robin (one L2 each). Tiles are dealt to XCDs in super-blocks of kSuper
+// robin (one L2 each). Tiles are dealt to XCDs in super-blocks of ks
 // consecutive tiles: XCD x takes super-blocks x, x+8, x+16, ... so tiles
 // that share operands (same expert, neighbouring row/column blocks) run on
 // one L2, while a hot expert's many super-blocks spread over all XCDs. The
-// grid is a multiple of 8*kSuper, which makes the map a bijection.
-constexpr int kSuper = 64;
-__device__ __forceinline__ int tile_remap(int bid) {
+// grid is a multiple of 8*ks, which makes the map a bijection.
+__device__ __forceinline__ int tile_remap(int bid, int ks) {
   const int x = bid % 8, i = bid / 8;
-  return ((i / kSuper) * 8 + x) * kSuper + (i % kSuper);
+  return ((i / ks) * 8 + x) * ks + (i % ks);
 }
-static int padded_grid(int tiles) {
-  const int q = 8 * kSuper;
+static int padded_grid(int tiles, int ks) {
+  const int q = 8 * ks;
   return (tiles + q - 1) / q * q;
 }
+// Super-block sizes, measured (per-launch times on the Mixtral-, Qwen3- and
+// DeepSeek-style layers against 64 everywhere):
+//   row-grouped GEMMs on the 128 x 128 tile: 32 (Mixtral dX 2.41 -> 2.29 ms,
+//     DeepSeek GEMM1 3.89 -> 3.81 ms, the others within noise);
+//   on the 256 x 256 tile: 64;
+//   weight gradients: 16 when an expert has fewer than 256 tiles (so that a
+//     super-block stays inside one expert; Qwen3-style 0.91 -> 0.78 ms), else
+//     64 (16 costs the DeepSeek-style layer 4 %).
+constexpr int kSuperRowsSmall = 32, kSuperRowsBig = 64;
+static int super_wgrad(int tiles_per_group) { return tiles_per_group < 256 ? 16 : 64; }
 
 // Exclusive scan of per-group row-tile counts; returns the tile's group in
 // s_info[0], its row-tile count in s_info[1] and the first tile of the group
@@ -416,7 +426,7 @@ void gemm_kernel(GemmArgs g) {
   const int lane = lane_id();
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
   const int wm = wave / WN, wn = wave % WN;
-  const int tile = tile_remap(blockIdx.x);
+  const int tile = tile_remap(blockIdx.x, g.ksuper);
 
   // tile -> (group, row tile, column tile); all of it wave-uniform
   int grp, mt, nt;
@@ -439,8 +449,9 @@ void gemm_kernel(GemmArgs g) {
     const int per = g.tiles_m * g.tiles_n;
     grp = tile / per;
     if (grp >= g.G) return;  // padding of the grid
-    // bands of 8 row tiles, row tile fastest: 64 consecutive tiles (one
-    // XCD's share) cover 8 x 8 tiles and share each A and B panel 8 times
+    // bands of 8 row tiles, row tile fastest: a super-block of ks
+    // consecutive tiles covers 8 x (ks / 8) tiles, sharing each A panel
+    // ks / 8 times and each B panel 8 times
     const int rem = tile % per;
     const int band = rem / (8 * g.tiles_n);
     const int in_band = min(8, g.tiles_m - band * 8);
@@ -989,8 +1000,10 @@ static int rows_tile_bound(int64_t A, int64_t G, int BM) {
 template <typename C, typename TC, bool AK, bool BKm, int MODE, int EPI>
 static void run_gemm(GemmArgs g, int tiles, hipStream_t st) {
   if (tiles <= 0) return;
+  if (MODE == G_KSPLIT) g.ksuper = super_wgrad(g.tiles_m * g.tiles_n);
+  else g.ksuper = C::BM == 128 ? kSuperRowsSmall : kSuperRowsBig;
   gemm_kernel<typename C::type, TC, AK, BKm, MODE, EPI, C::BM, C::BN, C::BK, C::WM, C::WN, C::NS>
-      <<<padded_grid(tiles), C::WM * C::WN * 64, 0, st>>>(g);
+      <<<padded_grid(tiles, g.ksuper), C::WM * C::WN * 64, 0, st>>>(g);
 }
 
 // Tile choice for the row-grouped GEMMs. The big tile halves operand traffic
