@@ -24,12 +24,13 @@
 // multiplied by row scale x column-block scale and added to the fp32
 // accumulator.
 //
-// Tiles are staged through LDS (double buffered, one barrier per K step) in
-// K-contiguous rows so that every MFMA operand is read with 16-byte LDS
-// reads; operands stored the other way round are transposed in registers on
-// their way into LDS. Workgroup ids are remapped so that each XCD (8 per
-// chip, one L2 each) works through a contiguous range of tiles that share
-// weights and rows.
+// Tiles go global -> LDS by DMA (2 or 3 stages, one barrier per K step).
+// K-major operands land in K-contiguous rows and are read with 16-byte LDS
+// reads; K-strided bf16 and FP8 operands land in their source orientation
+// and are read with the LDS transpose reads; only K-strided fp32 operands are
+// transposed in registers on their way into LDS. Workgroup ids are remapped
+// so that each XCD (8 per chip, one L2 each) works through a contiguous range
+// of tiles that share weights and rows.
 #include <type_traits>
 
 #include "common.hpp"
@@ -238,43 +239,16 @@ __device__ __forceinline__ int lds_off(int row, int k) {
   return row * BK + (((k / VEC) ^ lds_swz<KMAJ, NCH>(row)) * VEC) + (k % VEC);
 }
 
-// 4 K-rows x VEC columns (four 16-byte registers) -> VEC LDS rows of 4
-// K-values each.
+// fp32: 4 K-rows x 4 columns (four 16-byte registers) -> 4 LDS rows of 4
+// K-values each (the only register-transposed operands: K-strided bf16 and
+// FP8 tiles are read with the LDS transpose reads instead).
 template <typename T, int BK>
 __device__ __forceinline__ void store_transposed(const u32x4* r, T* dst, int c0, int k4) {
-  const uint32_t w[4][4] = {{r[0][0], r[0][1], r[0][2], r[0][3]}, {r[1][0], r[1][1], r[1][2], r[1][3]},
-                            {r[2][0], r[2][1], r[2][2], r[2][3]}, {r[3][0], r[3][1], r[3][2], r[3][3]}};
-  if constexpr (sizeof(T) == 1) {
+  static_assert(sizeof(T) == 4, "register transposes serve fp32 operands only");
 #pragma unroll
-    for (int p = 0; p < 4; ++p) {
-      // bytes (w0.q, w1.q) and (w2.q, w3.q) interleaved, then merged
-      const uint32_t a01 = __builtin_amdgcn_perm(w[1][p], w[0][p], 0x05010400u);  // q = 0, 1
-      const uint32_t b01 = __builtin_amdgcn_perm(w[1][p], w[0][p], 0x07030602u);  // q = 2, 3
-      const uint32_t a23 = __builtin_amdgcn_perm(w[3][p], w[2][p], 0x05010400u);
-      const uint32_t b23 = __builtin_amdgcn_perm(w[3][p], w[2][p], 0x07030602u);
-      const uint32_t c0v = __builtin_amdgcn_perm(a23, a01, 0x05040100u);
-      const uint32_t c1v = __builtin_amdgcn_perm(a23, a01, 0x07060302u);
-      const uint32_t c2v = __builtin_amdgcn_perm(b23, b01, 0x05040100u);
-      const uint32_t c3v = __builtin_amdgcn_perm(b23, b01, 0x07060302u);
-      *reinterpret_cast<uint32_t*>(dst + lds_off<T, BK, false>(c0 + 4 * p + 0, k4)) = c0v;
-      *reinterpret_cast<uint32_t*>(dst + lds_off<T, BK, false>(c0 + 4 * p + 1, k4)) = c1v;
-      *reinterpret_cast<uint32_t*>(dst + lds_off<T, BK, false>(c0 + 4 * p + 2, k4)) = c2v;
-      *reinterpret_cast<uint32_t*>(dst + lds_off<T, BK, false>(c0 + 4 * p + 3, k4)) = c3v;
-    }
-  } else if constexpr (sizeof(T) == 2) {
-#pragma unroll
-    for (int p = 0; p < 4; ++p) {
-      const u32x2 ev = {(w[0][p] & 0xffffu) | (w[1][p] << 16), (w[2][p] & 0xffffu) | (w[3][p] << 16)};
-      const u32x2 od = {(w[0][p] >> 16) | (w[1][p] & 0xffff0000u), (w[2][p] >> 16) | (w[3][p] & 0xffff0000u)};
-      *reinterpret_cast<u32x2*>(dst + lds_off<T, BK, false>(c0 + 2 * p, k4)) = ev;
-      *reinterpret_cast<u32x2*>(dst + lds_off<T, BK, false>(c0 + 2 * p + 1, k4)) = od;
-    }
-  } else {
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      const u32x4 v = {w[0][c], w[1][c], w[2][c], w[3][c]};
-      *reinterpret_cast<u32x4*>(dst + lds_off<T, BK, false>(c0 + c, k4)) = v;
-    }
+  for (int c = 0; c < 4; ++c) {
+    const u32x4 v = {r[0][c], r[1][c], r[2][c], r[3][c]};
+    *reinterpret_cast<u32x4*>(dst + lds_off<T, BK, false>(c0 + c, k4)) = v;
   }
 }
 
