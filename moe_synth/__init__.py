@@ -57,6 +57,7 @@ class LayerConfig:
     std: float = 0.02      # std of router and expert weights
     bias: str = "none"     # "none" | "zipf": per-expert router logit bias
     quant_block: int = 128
+    aux_coeff: float = 0.0  # load-balancing auxiliary loss coefficient (0: off)
 
     @property
     def A(self) -> int:

@@ -432,6 +432,38 @@ def route_bwd(dL, x, wr):
     return dL.T @ X, dL @ W
 
 
+# ------------------------------------------ load-balancing auxiliary loss
+
+def aux_loss(logits, idx, E: int, coeff: float) -> float:
+    """Load-balancing auxiliary loss, Switch-Transformer form (the pages name
+    the loss and its 0.01 coefficient, skill page workflow "Fluxo 2"; they give
+    no formula, and routing fuses it, Megatron Core MoE summary section 2.4):
+      f_e  = #{(t, j): idx[t,j] = e} / (T k)      share of the routing slots
+      P_e  = (1/T) sum_t softmax(L[t,:])_e       mean router probability
+      loss = coeff * E * sum_e f_e P_e
+    The probabilities are the softmax over all experts whatever the gate's
+    score function; f is a constant of the routing (no gradient). fp64."""
+    L = np.asarray(logits, dtype=np.float64)
+    T = L.shape[0]
+    k = np.asarray(idx).shape[1]
+    p = np.exp(L - L.max(axis=1, keepdims=True))
+    p /= p.sum(axis=1, keepdims=True)
+    f = np.bincount(np.asarray(idx, dtype=np.int64).reshape(-1), minlength=E) / float(T * k)
+    return float(coeff * E * np.dot(f, p.mean(axis=0)))
+
+
+def aux_loss_dlogits(logits, idx, E: int, coeff: float, d_aux: float = 1.0) -> np.ndarray:
+    """d(aux_loss)/dL [T,E] times the upstream gradient d_aux (fp64):
+    coeff * E / T * d_aux * p[t,e] * (f_e - sum_j f_j p[t,j])."""
+    L = np.asarray(logits, dtype=np.float64)
+    T = L.shape[0]
+    k = np.asarray(idx).shape[1]
+    p = np.exp(L - L.max(axis=1, keepdims=True))
+    p /= p.sum(axis=1, keepdims=True)
+    f = np.bincount(np.asarray(idx, dtype=np.int64).reshape(-1), minlength=E) / float(T * k)
+    return coeff * E / T * d_aux * p * (f[None, :] - (p @ f)[:, None])
+
+
 # -------------------------------------------------------- the whole layer
 
 def layer(cfg, inp: dict, identity: bool = False) -> dict:
@@ -522,6 +554,10 @@ def layer(cfg, inp: dict, identity: bool = False) -> dict:
         out.update(shared_dx=dx_sh, shared_dw1=sdw1, shared_dw2=sdw2)
     dx = dispatch_bwd(dXp, rmap, dx_sh)
     dL = route_bwd_logits(dgate, idx, L, cfg.score, cfg.renorm, cfg.gate_scale)
+    if cfg.aux_coeff:
+        # the auxiliary loss enters the step's total loss with weight 1
+        out["aux_loss"] = aux_loss(L, idx, E, cfg.aux_coeff)
+        dL = dL + aux_loss_dlogits(L, idx, E, cfg.aux_coeff, 1.0)
     dWr, dx_r = route_bwd(dL, inp["x"], inp["wr"])
     out.update(d_logits=dL, dw_router=dWr, dx=dx + dx_r, dx_router=dx_r)
     return out

@@ -204,3 +204,52 @@ def test_fp8_layer_consistency():
     assert oracle.rel_l2(out["y"], ref["y"]) < 0.08
     q1, s1, q2, s2 = out["w_q"][3]
     assert s1.shape == (2 * cfg.f // 128, cfg.d // 128) and s2.shape == (cfg.d // 128, cfg.f // 128)
+
+
+# ------------------------------------------ load-balancing auxiliary loss
+
+def test_aux_loss_balanced_routing_equals_coefficient():
+    # equal logits (p = 1/E) and every expert holding T k / E slots (f = 1/E):
+    # coeff * E * sum_e (1/E)(1/E) = coeff exactly
+    E, T, k = 8, 16, 2
+    L = np.zeros((T, E), dtype=np.float32)
+    idx = np.array([[(2 * t) % E, (2 * t + 1) % E] for t in range(T)], dtype=np.int32)
+    assert oracle.aux_loss(L, idx, E, 0.01) == pytest.approx(0.01, rel=1e-15)
+
+
+def test_aux_loss_two_experts_closed_form():
+    # one token, two experts, slot on expert 0: loss = 2 c sigma(a - b),
+    # dloss/da = -dloss/db = 2 c p0 p1
+    a, b, c = 0.7, -0.4, 0.03
+    L = np.array([[a, b]], dtype=np.float64)
+    idx = np.array([[0]], dtype=np.int32)
+    p0 = 1.0 / (1.0 + np.exp(-(a - b)))
+    assert oracle.aux_loss(L, idx, 2, c) == pytest.approx(2 * c * p0, rel=1e-14)
+    g = oracle.aux_loss_dlogits(L, idx, 2, c)
+    assert g[0, 0] == pytest.approx(2 * c * p0 * (1 - p0), rel=1e-12)
+    assert g[0, 1] == pytest.approx(-2 * c * p0 * (1 - p0), rel=1e-12)
+
+
+def test_aux_loss_gradient_matches_autograd_and_differences():
+    rng = np.random.default_rng(5)
+    T, E, k, c, d_aux = 40, 12, 3, 0.01, 1.7
+    L = rng.normal(size=(T, E)) * 2.0
+    idx = np.argsort(-L, axis=1)[:, :k].astype(np.int32)
+    g = oracle.aux_loss_dlogits(L, idx, E, c, d_aux)
+    # torch autograd on an independent formulation (f constant)
+    f = torch.bincount(torch.from_numpy(idx.astype(np.int64)).reshape(-1), minlength=E).double() / (T * k)
+    Lt = torch.from_numpy(L).requires_grad_(True)
+    loss = c * E * (f * torch.softmax(Lt, dim=1).mean(dim=0)).sum()
+    (d_aux * loss).backward()
+    assert np.allclose(g, Lt.grad.numpy(), rtol=1e-12, atol=1e-15)
+    assert oracle.aux_loss(L, idx, E, c) == pytest.approx(float(loss), rel=1e-13)
+    # central differences of the oracle's own loss (selection held fixed)
+    h = 1e-6
+    for t, e in [(0, 0), (7, 5), (39, 11)]:
+        Lp, Lm = L.copy(), L.copy()
+        Lp[t, e] += h
+        Lm[t, e] -= h
+        fd = (oracle.aux_loss(Lp, idx, E, c) - oracle.aux_loss(Lm, idx, E, c)) / (2 * h)
+        assert d_aux * fd == pytest.approx(g[t, e], rel=1e-5, abs=1e-11)
+    # softmax is shift invariant: every row of the gradient sums to zero
+    assert np.allclose(g.sum(axis=1), 0.0, atol=1e-15)
