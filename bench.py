@@ -206,6 +206,8 @@ def stage_work(c):
                                12 * d * f * T)
     w["dispatch_bwd"] = (A * d * bo + T * d * bx + 4 * A + S * T * d * bo, A * d)
     w["route_bwd"] = (4 * T * E + 12 * T * k + 3 * T * d * bx + 8 * E * d, 4 * T * d * E)
+    if c.aux_coeff:
+        w["aux_loss"] = (4 * T * E + 4 * T * k, 0)   # logits and indices, read once
     return w
 
 
@@ -237,6 +239,9 @@ def timed_step(layer, x, dy, marks):
     L.moe_route(c, x, layer.w_router, layer.bias, layer.logits, layer.topk_idx, layer.topk_gate,
                 layer.routing_map)
     rec("route")
+    if layer.aux:
+        L.moe_route_aux_loss(c, layer.logits, layer.topk_idx, layer.aux_loss, layer.ws_aux)
+        rec("aux_loss")
     L.moe_dispatch(c, x, layer.topk_idx, layer.counts, layer.offsets, layer.row_id_map,
                    layer.perm_token, layer.x_perm, layer.x_scale, layer.ws_dispatch)
     rec("dispatch")
@@ -277,7 +282,8 @@ def timed_step(layer, x, dy, marks):
     L.moe_dispatch_bwd(c, layer.dx_perm, layer.row_id_map, dx_add, layer.dx)
     rec("dispatch_bwd")
     L.moe_route_bwd(c, x, layer.w_router, layer.logits, layer.topk_idx, layer.topk_gate,
-                    layer.d_gate, layer.dx, layer.dw_router, layer.ws_route_bwd)
+                    layer.d_gate, layer.dx, layer.dw_router, layer.ws_route_bwd,
+                    d_aux=layer.d_aux if layer.aux else None)
     rec("route_bwd")
 
 
@@ -367,6 +373,9 @@ def main():
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--config", default="mixtral_bf16")
+    ap.add_argument("--aux-coeff", type=float, default=0.0,
+                    help="load-balancing auxiliary loss coefficient (0.01 in the Megatron recipe; "
+                         "0: off, as in the workloads' definitions)")
     ap.add_argument("--cpu-sample", type=int, default=4096,
                     help="tokens of the workload timed on the CPU oracle (0: skip)")
     ap.add_argument("--copy-probe", action="store_true",
@@ -418,6 +427,8 @@ def main():
     import torch
     import moe_synth as S
     cfg = S.BY_NAME[args.config]
+    if args.aux_coeff:
+        cfg = cfg.replace(aux_coeff=args.aux_coeff)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     layer, x, dy = make_layer(cfg, dev)
@@ -483,7 +494,8 @@ def main():
         "data": "synthetic (seeded normal inputs and random-init weights of the layer's shape)",
         "config": {"workload": f"{cfg.name}: MoE layer fwd+bwd, T={cfg.T} d={cfg.d} E={cfg.E}"
                                f"{'+1 shared' if cfg.shared else ''} top-{cfg.k} {cfg.score}"
-                               f"{' renorm' if cfg.renorm else ''}, SwiGLU d_ff={cfg.f}",
+                               f"{' renorm' if cfg.renorm else ''}, SwiGLU d_ff={cfg.f}"
+                               f"{f', aux loss {cfg.aux_coeff:g}' if cfg.aux_coeff else ''}",
                    "tokens": cfg.T, "hidden": cfg.d, "experts": cfg.E, "top_k": cfg.k,
                    "ffn_hidden": cfg.f, "parallelism": "none (one GPU)"},
         "dispatch_combine_GBps": round(dc_b / dc_t / 1e6, 1),

@@ -69,7 +69,8 @@ enum {
     MOE_OP_DISPATCH = 1,
     MOE_OP_GROUPED_FFN = 2,
     MOE_OP_GROUPED_FFN_BWD = 3,
-    MOE_OP_ROUTE_BWD = 4
+    MOE_OP_ROUTE_BWD = 4,
+    MOE_OP_AUX_LOSS = 5
 };
 
 /* Layer configuration, read on the host only.
@@ -91,7 +92,10 @@ enum {
  *              MOE_TILE_SMALL forces 128 x 128; MOE_TILE_BIG forces
  *              256 x 256 wherever the dimensions are multiples of 256.
  *              Results do not depend on it beyond rounding order: it exists
- *              for tuning and to test every kernel variant. */
+ *              for tuning and to test every kernel variant.
+ *  aux_coeff   weight of the load-balancing auxiliary loss (0.01 in the
+ *              MoE workflow of the Megatron Core page); 0 turns the loss
+ *              and its gradient off. */
 typedef struct moe_config {
     int64_t num_tokens;  /* T */
     int64_t hidden;      /* d, a multiple of 128 */
@@ -109,6 +113,7 @@ typedef struct moe_config {
     int32_t quant_block;  /* 128 */
     int32_t ffn_mode;
     int32_t gemm_tile;   /* MOE_TILE_*, 0 by default */
+    float aux_coeff;     /* finite, >= 0 */
 } moe_config;
 
 /* Bytes of workspace the call `op` (MOE_OP_*) needs for this configuration;
@@ -223,19 +228,46 @@ int moe_dispatch_bwd(const moe_config *cfg, const void *dx_perm,
                      const int32_t *row_id_map, const void *dx_add, void *dx,
                      void *stream);
 
+/* Load-balancing auxiliary loss of the routing ("Distributed Training
+ * Megatron Core" page, MoE workflow "Fluxo 2": the aux_loss balancing type
+ * with coefficient 0.01; Megatron Core MoE summary, section 2.4: fused with
+ * routing). The pages name the loss
+ * but not its formula; this is the Switch-Transformer form:
+ *   f_e = #{(t,j): topk_idx[t,j] = e} / (T k)   share of the routing slots
+ *   P_e = (1/T) sum_t softmax(logits[t,:])_e    mean router probability
+ *   aux_loss = aux_coeff * E * sum_e f_e P_e
+ * The probabilities are the softmax over all E experts whatever score_fn is
+ * (the logits include the expert bias when moe_route added one); f is a
+ * constant of the selection. fp32 throughout, fixed summation order
+ * (deterministic). Entries of topk_idx outside [0,E) are not counted.
+ *   logits [T,E] f32, topk_idx [T,k] i32 (from moe_route)
+ * out: aux_loss [1] f32 (device). T = 0 writes nothing.
+ * Requires aux_coeff != 0 (else MOE_ERR_INVALID_ARG).
+ * Workspace: moe_workspace_size(cfg, MOE_OP_AUX_LOSS). */
+int moe_route_aux_loss(const moe_config *cfg, const float *logits,
+                       const int32_t *topk_idx, float *aux_loss, void *ws,
+                       size_t ws_bytes, void *stream);
+
 /* Router backward; selection, group choice and the bias are constants.
  *   dL = d(gates)/d(logits)^T d_gate for the configured score function,
+ *        plus, when aux_coeff != 0 and d_aux is not NULL, the gradient of
+ *        the auxiliary loss times d_aux[0]:
+ *        aux_coeff * E / T * d_aux * p[t,e] * (f_e - sum_j f_j p[t,j])
+ *        (p the softmax over all experts, f as in moe_route_aux_loss),
  *   dw_router = dL^T x   ([E,d] f32, overwritten)
  *   dx += dL w_router    ([T,d] act, read-modify-write)
  * Both products accumulate in fp32; with bf16 activations their operands
  * (dL, x, w_router) are rounded to bf16 first, with fp32 activations they
  * stay fp32. Results are deterministic (fixed summation order).
- * Inputs are those of moe_route plus its outputs and d_gate [T,k] f32.
- * Workspace: moe_workspace_size(cfg, MOE_OP_ROUTE_BWD). */
+ * Inputs are those of moe_route plus its outputs, d_gate [T,k] f32 and
+ * d_aux [1] f32 (device) or NULL.
+ * Workspace: moe_workspace_size(cfg, MOE_OP_ROUTE_BWD) (larger when
+ * aux_coeff != 0). */
 int moe_route_bwd(const moe_config *cfg, const void *x, const float *w_router,
                   const float *logits, const int32_t *topk_idx,
-                  const float *topk_gate, const float *d_gate, void *dx,
-                  float *dw_router, void *ws, size_t ws_bytes, void *stream);
+                  const float *topk_gate, const float *d_gate,
+                  const float *d_aux, void *dx, float *dw_router, void *ws,
+                  size_t ws_bytes, void *stream);
 
 /* FP8 E4M3 block quantisation: src [rows, cols] (src_dtype f32 or bf16) in
  * blocks of block_r x block_c: amax = max |v|, scale = amax / 448 (1 if

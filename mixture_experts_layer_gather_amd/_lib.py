@@ -21,10 +21,11 @@ STATUS = {0: "MOE_OK", -1: "MOE_ERR_INVALID_ARG", -2: "MOE_ERR_UNSUPPORTED_DTYPE
 DTYPE = {"f32": 0, "bf16": 1, "fp8": 2}
 SCORE = {"softmax": 0, "sigmoid": 1}
 GROUP_SCORE = {"top2_sum": 0, "max": 1}
-OP_ROUTE, OP_DISPATCH, OP_GROUPED_FFN, OP_GROUPED_FFN_BWD, OP_ROUTE_BWD = range(5)
+OP_ROUTE, OP_DISPATCH, OP_GROUPED_FFN, OP_GROUPED_FFN_BWD, OP_ROUTE_BWD, OP_AUX_LOSS = range(6)
 
 EXPORTS = ["moe_workspace_size", "moe_route", "moe_dispatch", "moe_grouped_ffn", "moe_combine",
            "moe_combine_bwd", "moe_grouped_ffn_bwd", "moe_dispatch_bwd", "moe_route_bwd",
+           "moe_route_aux_loss",
            "moe_quantize_fp8_blockwise", "moe_status_string"]
 
 
@@ -52,6 +53,7 @@ class MoeConfig(ctypes.Structure):
         ("quant_block", ctypes.c_int32),
         ("ffn_mode", ctypes.c_int32),
         ("gemm_tile", ctypes.c_int32),
+        ("aux_coeff", ctypes.c_float),
     ]
 
 TILE = {"auto": 0, "small": 1, "big": 2}
@@ -59,10 +61,11 @@ TILE = {"auto": 0, "small": 1, "big": 2}
 
 def make_config(T, d, E, k, f, score="softmax", renorm=True, gate_scale=1.0, num_groups=1,
                 topk_groups=1, group_score="top2_sum", act="bf16", weight="bf16",
-                quant_block=128, identity=False, gemm_tile="auto", **_ignored) -> MoeConfig:
+                quant_block=128, identity=False, gemm_tile="auto", aux_coeff=0.0,
+                **_ignored) -> MoeConfig:
     return MoeConfig(T, d, E, k, f, SCORE[score], int(bool(renorm)), float(gate_scale),
                      num_groups, topk_groups, GROUP_SCORE[group_score], DTYPE[act], DTYPE[weight],
-                     quant_block, 1 if identity else 0, TILE[gemm_tile])
+                     quant_block, 1 if identity else 0, TILE[gemm_tile], float(aux_coeff))
 
 
 _lib = None
@@ -88,7 +91,8 @@ def lib():
             "moe_combine_bwd": (ctypes.c_int, [C, P, P, P, P, P, P, P]),
             "moe_grouped_ffn_bwd": (ctypes.c_int, [C] + [P] * 15 + [sz, P]),
             "moe_dispatch_bwd": (ctypes.c_int, [C, P, P, P, P, P]),
-            "moe_route_bwd": (ctypes.c_int, [C, P, P, P, P, P, P, P, P, P, sz, P]),
+            "moe_route_bwd": (ctypes.c_int, [C] + [P] * 10 + [sz, P]),
+            "moe_route_aux_loss": (ctypes.c_int, [C, P, P, P, P, sz, P]),
             "moe_quantize_fp8_blockwise": (ctypes.c_int, [P, ctypes.c_int, i64, i64, i64, i64, P, P, P]),
             "moe_status_string": (ctypes.c_char_p, [ctypes.c_int]),
         }
@@ -176,11 +180,17 @@ def moe_dispatch_bwd(cfg, dx_perm, row_id_map, dx_add, dx, stream=None):
                                                       _stream(stream)))
 
 
+def moe_route_aux_loss(cfg, logits, topk_idx, aux_loss, ws=None, stream=None):
+    _check("moe_route_aux_loss", lib().moe_route_aux_loss(ctypes.byref(cfg), _p(logits),
+                                                          _p(topk_idx), _p(aux_loss), _p(ws),
+                                                          _nbytes(ws), _stream(stream)))
+
+
 def moe_route_bwd(cfg, x, w_router, logits, topk_idx, topk_gate, d_gate, dx, dw_router, ws=None,
-                  stream=None):
+                  stream=None, d_aux=None):
     _check("moe_route_bwd", lib().moe_route_bwd(ctypes.byref(cfg), _p(x), _p(w_router), _p(logits),
-                                                _p(topk_idx), _p(topk_gate), _p(d_gate), _p(dx),
-                                                _p(dw_router), _p(ws), _nbytes(ws),
+                                                _p(topk_idx), _p(topk_gate), _p(d_gate), _p(d_aux),
+                                                _p(dx), _p(dw_router), _p(ws), _nbytes(ws),
                                                 _stream(stream)))
 
 

@@ -33,6 +33,12 @@ struct RouteBwdLaunch {
   float* dw_router;
   float* dL;       // workspace [T,E]
   float* dw_part;  // workspace [Z,E,d] (token-chunk partial sums), Z = route_bwd_zsplit
+  // auxiliary-loss gradient, on when d_aux is set: counts [aux_blocks(T),E]
+  // i32 and f [E] f32 in workspace
+  const float* d_aux;
+  int32_t* aux_counts;
+  float* aux_f;
+  float aux_coeff;
   int64_t T, d, E, k;
   int score_fn, renorm;
   float gate_scale;
@@ -40,6 +46,20 @@ struct RouteBwdLaunch {
 };
 void launch_route_bwd(const RouteBwdLaunch& r, hipStream_t st);
 int route_bwd_zsplit(int64_t T, int64_t d, int64_t E);
+
+// Load-balancing auxiliary loss: per-block partial probability sums and
+// expert counts (workspace, [aux_blocks(T), E] each), then the loss.
+struct AuxLaunch {
+  const float* logits;
+  const int32_t* idx;
+  float* p_part;
+  int32_t* c_part;
+  float* loss;
+  int64_t T, E, k;
+  float coeff;
+};
+void launch_route_aux_loss(const AuxLaunch& a, hipStream_t st);
+int aux_blocks(int64_t T);
 
 // Dispatch: histogram -> scan -> positions -> gather.
 struct DispatchLaunch {

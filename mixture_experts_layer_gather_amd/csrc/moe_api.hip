@@ -40,6 +40,7 @@ int check_cfg(const moe_config* c) {
   }
   if (c->ffn_mode != MOE_FFN_SWIGLU && c->ffn_mode != MOE_FFN_IDENTITY) return MOE_ERR_INVALID_ARG;
   if (c->gemm_tile < MOE_TILE_AUTO || c->gemm_tile > MOE_TILE_BIG) return MOE_ERR_INVALID_ARG;
+  if (!(c->aux_coeff >= 0.0f && c->aux_coeff < __builtin_inff())) return MOE_ERR_INVALID_ARG;
   if (c->act_dtype != MOE_DTYPE_F32 && c->act_dtype != MOE_DTYPE_BF16) return MOE_ERR_UNSUPPORTED_DTYPE;
   if (c->weight_dtype == MOE_DTYPE_FP8_E4M3) {
     if (c->act_dtype != MOE_DTYPE_BF16) return MOE_ERR_UNSUPPORTED_DTYPE;
@@ -74,6 +75,16 @@ int launched() {
 
 size_t round_up(size_t v) { return (v + 255) & ~size_t(255); }
 
+// One [aux_blocks(T), E] array of 4-byte partials (counts or probability sums).
+size_t aux_part_bytes(const moe_config* c) {
+  return round_up(size_t(moe::aux_blocks(c->num_tokens)) * size_t(c->num_experts) * 4);
+}
+
+// Router backward's extra workspace for the auxiliary loss: counts + f [E].
+size_t aux_bwd_bytes(const moe_config* c) {
+  return c->aux_coeff != 0.0f ? aux_part_bytes(c) + round_up(size_t(c->num_experts) * 4) : 0;
+}
+
 }  // namespace
 
 extern "C" {
@@ -104,8 +115,9 @@ size_t moe_workspace_size(const moe_config* cfg, int op) {
     case MOE_OP_ROUTE_BWD: {
       const int Z = moe::route_bwd_zsplit(T, cfg->hidden, E);
       const size_t parts = Z > 1 ? size_t(Z) * size_t(E) * size_t(cfg->hidden) * 4 : 0;
-      return round_up(size_t(T) * size_t(E) * 4) + round_up(parts);
+      return round_up(size_t(T) * size_t(E) * 4) + round_up(parts) + aux_bwd_bytes(cfg);
     }
+    case MOE_OP_AUX_LOSS: return 2 * aux_part_bytes(cfg);
     default: return 0;
   }
 }
@@ -272,20 +284,48 @@ int moe_dispatch_bwd(const moe_config* cfg, const void* dx_perm, const int32_t* 
   return launched();
 }
 
+int moe_route_aux_loss(const moe_config* cfg, const float* logits, const int32_t* topk_idx,
+                       float* aux_loss, void* ws, size_t ws_bytes, void* stream) {
+  MOE_CHECK(check_cfg(cfg));
+  if (cfg->aux_coeff == 0.0f) return MOE_ERR_INVALID_ARG;
+  MOE_CHECK(need(logits)); MOE_CHECK(need(topk_idx)); MOE_CHECK(need(aux_loss));
+  MOE_CHECK(align_all(logits, topk_idx, ws));
+  if (cfg->num_tokens == 0) return MOE_OK;
+  if (!ws || ws_bytes < moe_workspace_size(cfg, MOE_OP_AUX_LOSS)) return MOE_ERR_WORKSPACE;
+  moe::AuxLaunch a{};
+  a.logits = logits; a.idx = topk_idx; a.loss = aux_loss;
+  a.c_part = static_cast<int32_t*>(ws);
+  a.p_part = reinterpret_cast<float*>(static_cast<char*>(ws) + aux_part_bytes(cfg));
+  a.T = cfg->num_tokens; a.E = cfg->num_experts; a.k = cfg->top_k; a.coeff = cfg->aux_coeff;
+  moe::launch_route_aux_loss(a, static_cast<hipStream_t>(stream));
+  return launched();
+}
+
 int moe_route_bwd(const moe_config* cfg, const void* x, const float* w_router, const float* logits,
-                  const int32_t* topk_idx, const float* topk_gate, const float* d_gate, void* dx,
-                  float* dw_router, void* ws, size_t ws_bytes, void* stream) {
+                  const int32_t* topk_idx, const float* topk_gate, const float* d_gate,
+                  const float* d_aux, void* dx, float* dw_router, void* ws, size_t ws_bytes,
+                  void* stream) {
   MOE_CHECK(check_cfg(cfg));
   MOE_CHECK(need(x)); MOE_CHECK(need(w_router)); MOE_CHECK(need(logits)); MOE_CHECK(need(topk_idx));
   MOE_CHECK(need(topk_gate)); MOE_CHECK(need(d_gate)); MOE_CHECK(need(dx)); MOE_CHECK(need(dw_router));
   MOE_CHECK(align_all(x, w_router, logits, topk_idx, topk_gate, d_gate, dx, dw_router, ws));
   if (cfg->num_tokens == 0) return MOE_OK;
   if (!ws || ws_bytes < moe_workspace_size(cfg, MOE_OP_ROUTE_BWD)) return MOE_ERR_WORKSPACE;
+  const int Z = moe::route_bwd_zsplit(cfg->num_tokens, cfg->hidden, cfg->num_experts);
+  const size_t dl_bytes = round_up(size_t(cfg->num_tokens) * size_t(cfg->num_experts) * 4);
+  const size_t part_bytes =
+      round_up(Z > 1 ? size_t(Z) * size_t(cfg->num_experts) * size_t(cfg->hidden) * 4 : 0);
+  char* w = static_cast<char*>(ws);
   moe::RouteBwdLaunch r{};
   r.x = x; r.w_router = w_router; r.logits = logits; r.idx = topk_idx; r.dgate = d_gate;
-  r.dx = dx; r.dw_router = dw_router; r.dL = static_cast<float*>(ws);
-  r.dw_part = reinterpret_cast<float*>(static_cast<char*>(ws) +
-                                       round_up(size_t(cfg->num_tokens) * size_t(cfg->num_experts) * 4));
+  r.dx = dx; r.dw_router = dw_router; r.dL = reinterpret_cast<float*>(w);
+  r.dw_part = reinterpret_cast<float*>(w + dl_bytes);
+  if (cfg->aux_coeff != 0.0f && d_aux) {
+    r.d_aux = d_aux;
+    r.aux_counts = reinterpret_cast<int32_t*>(w + dl_bytes + part_bytes);
+    r.aux_f = reinterpret_cast<float*>(w + dl_bytes + part_bytes + aux_part_bytes(cfg));
+    r.aux_coeff = cfg->aux_coeff;
+  }
   r.T = cfg->num_tokens; r.d = cfg->hidden; r.E = cfg->num_experts; r.k = cfg->top_k;
   r.score_fn = cfg->score_fn; r.renorm = cfg->renormalize; r.gate_scale = cfg->gate_scale;
   r.act_bf16 = cfg->act_dtype == MOE_DTYPE_BF16;

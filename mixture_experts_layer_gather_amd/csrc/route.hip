@@ -801,6 +801,11 @@ struct DLArgs {
   int T, E, k;
   int score_fn, renorm;
   float gate_scale;
+  // auxiliary loss (aux_f NULL: off): f [E] and the upstream gradient d_aux
+  // [1]; aux_scale = coeff * E / T
+  const float* aux_f;
+  const float* d_aux;
+  float aux_scale;
 };
 
 template <int NPL>
@@ -903,11 +908,186 @@ __global__ __launch_bounds__(256) void dlogits_kernel(DLArgs a) {
         if (j < a.k && e_j[j] == e) dl[p] = sel_grad[j];
     }
   }
+  if (a.aux_f) {
+    // + aux_scale * d_aux * p_e * (f_e - sum_j f_j p_j), p the softmax over
+    // all experts
+    float Lv[NPL], fv[NPL];
+    float m = -__builtin_inff();
+#pragma unroll
+    for (int p = 0; p < NPL; ++p) {
+      const int e = lane + kWave * p;
+      Lv[p] = e < a.E ? Lrow[e] : -__builtin_inff();
+      fv[p] = e < a.E ? a.aux_f[e] : 0.0f;
+      m = fmaxf(m, Lv[p]);
+    }
+    m = wave_max(m);
+    float q[NPL], z = 0.0f;
+#pragma unroll
+    for (int p = 0; p < NPL; ++p) {
+      q[p] = lane + kWave * p < a.E ? expf(Lv[p] - m) : 0.0f;
+      z += q[p];
+    }
+    const float Z = wave_sum(z);
+    float dot = 0.0f;
+#pragma unroll
+    for (int p = 0; p < NPL; ++p) {
+      q[p] /= Z;
+      dot += fv[p] * q[p];
+    }
+    dot = wave_sum(dot);
+    const float sc = a.aux_scale * a.d_aux[0];
+#pragma unroll
+    for (int p = 0; p < NPL; ++p) dl[p] += sc * q[p] * (fv[p] - dot);
+  }
 #pragma unroll
   for (int p = 0; p < NPL; ++p) {
     const int e = lane + kWave * p;
     if (e < a.E) a.dL[int64_t(t) * a.E + e] = dl[p];
   }
+}
+
+// ---------------------------------------------------------------------------
+// Load-balancing auxiliary loss (Switch form, see moe_route_aux_loss):
+//   aux_partials_kernel  one block per chunk of tokens: the chunk's expert
+//                        counts (LDS integer histogram) and, with WITH_P, its
+//                        sum of softmax probabilities (one wave per token,
+//                        waves added in wave order);
+//   aux_final_kernel     one block: adds the chunk partials in chunk order,
+//                        writes f_e = count_e / (T k) and/or the loss.
+// Integer counts are exact; the float sums have a fixed order, so the result
+// is deterministic. HBM traffic: logits once (T E 4 bytes) plus idx.
+// ---------------------------------------------------------------------------
+constexpr int kAuxMaxBlocks = 256;  // chunks: enough blocks for small T, few partials for large T
+
+static int64_t aux_tokens_per_block(int64_t T) {
+  const int64_t per = (T + kAuxMaxBlocks - 1) / kAuxMaxBlocks;
+  return per < 64 ? 64 : (per + 63) / 64 * 64;
+}
+
+int aux_blocks(int64_t T) {
+  return T <= 0 ? 0 : int((T + aux_tokens_per_block(T) - 1) / aux_tokens_per_block(T));
+}
+
+template <int NPL, bool WITH_P>
+__global__ __launch_bounds__(256) void aux_partials_kernel(const float* __restrict__ logits,
+                                                           const int32_t* __restrict__ idx,
+                                                           float* __restrict__ p_part,
+                                                           int32_t* __restrict__ c_part, int T,
+                                                           int E, int k, int tpb) {
+  __shared__ float ps[WITH_P ? 4 : 1][kWave * NPL];
+  __shared__ int cnt[kWave * NPL];
+  const int wave = threadIdx.x / kWave;
+  const int lane = lane_id();
+  const int t0 = blockIdx.x * tpb;
+  const int nt = min(tpb, T - t0);
+  for (int e = threadIdx.x; e < E; e += blockDim.x) cnt[e] = 0;
+  __syncthreads();
+  const int32_t* ib = idx + int64_t(t0) * k;
+  for (int i = threadIdx.x; i < nt * k; i += blockDim.x) {
+    const int e = ib[i];
+    if (unsigned(e) < unsigned(E)) atomicAdd(&cnt[e], 1);
+  }
+  if constexpr (WITH_P) {
+    float acc[NPL];
+#pragma unroll
+    for (int p = 0; p < NPL; ++p) acc[p] = 0.0f;
+    for (int tt = wave; tt < nt; tt += 4) {
+      const float* Lrow = logits + int64_t(t0 + tt) * E;
+      float Lv[NPL];
+      float m = -__builtin_inff();
+#pragma unroll
+      for (int p = 0; p < NPL; ++p) {
+        const int e = lane + kWave * p;
+        Lv[p] = e < E ? Lrow[e] : -__builtin_inff();
+        m = fmaxf(m, Lv[p]);
+      }
+      m = wave_max(m);
+      float q[NPL], z = 0.0f;
+#pragma unroll
+      for (int p = 0; p < NPL; ++p) {
+        q[p] = lane + kWave * p < E ? expf(Lv[p] - m) : 0.0f;
+        z += q[p];
+      }
+      const float Z = wave_sum(z);
+#pragma unroll
+      for (int p = 0; p < NPL; ++p) acc[p] += q[p] / Z;
+    }
+#pragma unroll
+    for (int p = 0; p < NPL; ++p) ps[wave][lane + kWave * p] = acc[p];
+  }
+  __syncthreads();
+  for (int e = threadIdx.x; e < E; e += blockDim.x) {
+    c_part[int64_t(blockIdx.x) * E + e] = cnt[e];
+    if constexpr (WITH_P)
+      p_part[int64_t(blockIdx.x) * E + e] = ((ps[0][e] + ps[1][e]) + ps[2][e]) + ps[3][e];
+  }
+}
+
+// 1024 threads: expert e gets S = 1024 / E threads, split s adds chunks
+// s, s+S, s+2S, ... in order; the S split sums are then added in split order.
+__global__ __launch_bounds__(1024) void aux_final_kernel(const float* __restrict__ p_part,
+                                                         const int32_t* __restrict__ c_part,
+                                                         int nblk, int E, float tk,
+                                                         float loss_scale, float* __restrict__ f_out,
+                                                         float* __restrict__ loss) {
+  __shared__ float sp[1024];
+  __shared__ int sc[1024];
+  __shared__ float red[1024];
+  const int tid = threadIdx.x;
+  const int S = 1024 / E;
+  if (tid < S * E) {
+    const int e = tid % E, s = tid / E;
+    int c = 0;
+    float P = 0.0f;
+#pragma unroll 8
+    for (int b = s; b < nblk; b += S) {
+      c += c_part[int64_t(b) * E + e];
+      if (p_part) P += p_part[int64_t(b) * E + e];
+    }
+    sp[tid] = P;
+    sc[tid] = c;
+  }
+  __syncthreads();
+  float term = 0.0f;
+  if (tid < E) {
+    int c = 0;
+    float P = 0.0f;
+    for (int s = 0; s < S; ++s) {
+      c += sc[s * E + tid];
+      P += sp[s * E + tid];
+    }
+    const float fe = float(c) / tk;
+    if (f_out) f_out[tid] = fe;
+    term = fe * P;
+  }
+  if (!loss) return;
+  red[tid] = term;
+  __syncthreads();
+  for (int o = 512; o > 0; o >>= 1) {
+    if (tid < o) red[tid] += red[tid + o];
+    __syncthreads();
+  }
+  if (tid == 0) loss[0] = loss_scale * red[0];
+}
+
+template <bool WITH_P>
+static void launch_aux_partials(const float* logits, const int32_t* idx, float* p_part,
+                                int32_t* c_part, int64_t T, int64_t E, int64_t k, hipStream_t st) {
+  const int nb = aux_blocks(T);
+  const int tpb = int(aux_tokens_per_block(T));
+  const int t = int(T), e = int(E), kk = int(k);
+  if (E <= 64) aux_partials_kernel<1, WITH_P><<<nb, 256, 0, st>>>(logits, idx, p_part, c_part, t, e, kk, tpb);
+  else if (E <= 128) aux_partials_kernel<2, WITH_P><<<nb, 256, 0, st>>>(logits, idx, p_part, c_part, t, e, kk, tpb);
+  else if (E <= 256) aux_partials_kernel<4, WITH_P><<<nb, 256, 0, st>>>(logits, idx, p_part, c_part, t, e, kk, tpb);
+  else if (E <= 512) aux_partials_kernel<8, WITH_P><<<nb, 256, 0, st>>>(logits, idx, p_part, c_part, t, e, kk, tpb);
+  else aux_partials_kernel<16, WITH_P><<<nb, 256, 0, st>>>(logits, idx, p_part, c_part, t, e, kk, tpb);
+}
+
+void launch_route_aux_loss(const AuxLaunch& a, hipStream_t st) {
+  launch_aux_partials<true>(a.logits, a.idx, a.p_part, a.c_part, a.T, a.E, a.k, st);
+  aux_final_kernel<<<1, 1024, 0, st>>>(a.p_part, a.c_part, aux_blocks(a.T), int(a.E),
+                                       float(a.T * a.k), a.coeff * float(a.E) / float(a.T), nullptr,
+                                       a.loss);
 }
 
 // ---------------------------------------------------------------------------
@@ -952,6 +1132,15 @@ static void route_bwd_t(const RouteBwdLaunch& r, hipStream_t st) {
   d.logits = r.logits; d.idx = r.idx; d.dgate = r.dgate; d.dL = r.dL;
   d.T = int(r.T); d.E = int(r.E); d.k = int(r.k);
   d.score_fn = r.score_fn; d.renorm = r.renorm; d.gate_scale = r.gate_scale;
+  if (r.d_aux) {
+    // f_e from the selection, then the aux term inside dlogits_kernel
+    launch_aux_partials<false>(nullptr, r.idx, nullptr, r.aux_counts, r.T, r.E, r.k, st);
+    aux_final_kernel<<<1, 1024, 0, st>>>(nullptr, r.aux_counts, aux_blocks(r.T), int(r.E),
+                                         float(r.T * r.k), 0.0f, r.aux_f, nullptr);
+    d.aux_f = r.aux_f;
+    d.d_aux = r.d_aux;
+    d.aux_scale = r.aux_coeff * float(r.E) / float(r.T);
+  }
   const dim3 grid((r.T + 3) / 4);
   if (r.E <= 64) dlogits_kernel<1><<<grid, 256, 0, st>>>(d);
   else if (r.E <= 128) dlogits_kernel<2><<<grid, 256, 0, st>>>(d);

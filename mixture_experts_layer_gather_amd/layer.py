@@ -21,7 +21,8 @@ _TORCH = {"f32": torch.float32, "bf16": torch.bfloat16}
 class MoELayer:
     def __init__(self, T, d, E, k, f, shared=0, score="softmax", renorm=True, gate_scale=1.0,
                  num_groups=1, topk_groups=1, group_score="top2_sum", act="bf16", weight="bf16",
-                 quant_block=128, identity=False, gemm_tile="auto", device="cuda", **_ignored):
+                 quant_block=128, identity=False, gemm_tile="auto", aux_coeff=0.0, device="cuda",
+                 **_ignored):
         self.T, self.d, self.E, self.k, self.f = T, d, E, k, f
         self.A = T * k
         self.shared = int(shared)
@@ -30,8 +31,10 @@ class MoELayer:
         self.qb = quant_block
         kw = dict(score=score, renorm=renorm, gate_scale=gate_scale, num_groups=num_groups,
                   topk_groups=topk_groups, group_score=group_score, act=act, weight=weight,
-                  quant_block=quant_block, identity=identity, gemm_tile=gemm_tile)
+                  quant_block=quant_block, identity=identity, gemm_tile=gemm_tile,
+                  aux_coeff=aux_coeff)
         self.cfg = L.make_config(T, d, E, k, f, **kw)
+        self.aux = aux_coeff != 0.0
         self.scfg = L.make_config(T, d, 1, 1, f, act=act, weight=weight, quant_block=quant_block,
                                   identity=identity, gemm_tile=gemm_tile)
         dev = torch.device(device)
@@ -46,6 +49,10 @@ class MoELayer:
         self.topk_idx = e(T, k, dt=i32)
         self.topk_gate = e(T, k, dt=torch.float32)
         self.routing_map = e(T, E, dt=torch.uint8)
+        # auxiliary loss: its value, and its weight in the step's total loss
+        # (1, the upstream gradient of the backward)
+        self.aux_loss = e(1, dt=torch.float32)
+        self.d_aux = torch.ones(1, dtype=torch.float32, device=dev)
         # dispatch
         self.counts = e(E, dt=i32)
         self.offsets = e(E + 1, dt=i32)
@@ -80,6 +87,7 @@ class MoELayer:
         self.ws_ffn_bwd = e(max(1, L.workspace_size(self.cfg, L.OP_GROUPED_FFN_BWD),
                                 L.workspace_size(self.scfg, L.OP_GROUPED_FFN_BWD)), dt=u8)
         self.ws_route_bwd = e(max(1, L.workspace_size(self.cfg, L.OP_ROUTE_BWD)), dt=u8)
+        self.ws_aux = e(max(1, L.workspace_size(self.cfg, L.OP_AUX_LOSS)), dt=u8)
         if self.shared:
             self.s_offsets = torch.tensor([0, T], dtype=i32, device=dev)
             if self.fp8:
@@ -133,6 +141,8 @@ class MoELayer:
         c = self.cfg
         L.moe_route(c, x, self.w_router, self.bias, self.logits, self.topk_idx, self.topk_gate,
                     self.routing_map)
+        if self.aux:
+            L.moe_route_aux_loss(c, self.logits, self.topk_idx, self.aux_loss, self.ws_aux)
         L.moe_dispatch(c, x, self.topk_idx, self.counts, self.offsets, self.row_id_map,
                        self.perm_token, self.x_perm, self.x_scale, self.ws_dispatch)
         L.moe_grouped_ffn(c, self.x_perm, self.x_scale, self.offsets, self.w1, self.w1_scale,
@@ -167,7 +177,8 @@ class MoELayer:
             dx_add = self.s_dx
         L.moe_dispatch_bwd(c, self.dx_perm, self.row_id_map, dx_add, self.dx)
         L.moe_route_bwd(c, self.x, self.w_router, self.logits, self.topk_idx, self.topk_gate,
-                        self.d_gate, self.dx, self.dw_router, self.ws_route_bwd)
+                        self.d_gate, self.dx, self.dw_router, self.ws_route_bwd,
+                        d_aux=self.d_aux if self.aux else None)
         return self.dx
 
     def step(self, x, dy):

@@ -27,7 +27,7 @@ def _declared():
 
 def test_exports_every_declared_symbol(M):
     names = _declared()
-    assert len(names) == 11, names
+    assert len(names) == 12, names
     L = M.lib()
     for n in names:
         assert hasattr(L, n), n
@@ -67,6 +67,8 @@ def test_config_validation(M):
         c = _cfg(M)
         c.gemm_tile = tile
         assert _route(M, c) == -1, tile
+    for coeff in (-0.01, float("nan"), float("inf")):
+        assert _route(M, _cfg(M, aux_coeff=coeff)) == -1, coeff
     assert L.moe_workspace_size(ctypes.byref(_cfg(M, k=9)), 1) == 0
 
 
@@ -96,8 +98,16 @@ def test_null_alignment_and_workspace_errors(M):
     assert L.moe_dispatch(ctypes.byref(c8), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE,
                           need, None) == -1
     # route backward workspace
-    assert L.moe_route_bwd(ctypes.byref(c), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, 0,
-                           None) == -4
+    assert L.moe_route_bwd(ctypes.byref(c), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, FAKE,
+                           None, 0, None) == -4
+    # auxiliary loss: needs a nonzero coefficient, an output and a workspace
+    assert L.moe_route_aux_loss(ctypes.byref(c), FAKE, FAKE, FAKE, FAKE, 1 << 20, None) == -1
+    ca = _cfg(M, aux_coeff=0.01)
+    assert L.moe_route_aux_loss(ctypes.byref(ca), FAKE, FAKE, None, FAKE, 1 << 20, None) == -1
+    assert L.moe_route_aux_loss(ctypes.byref(ca), FAKE, FAKE, FAKE, None, 0, None) == -4
+    need = L.moe_workspace_size(ctypes.byref(ca), 5)
+    assert L.moe_route_aux_loss(ctypes.byref(ca), FAKE, FAKE, FAKE, FAKE, need - 1, None) == -4
+    assert L.moe_route_aux_loss(ctypes.byref(ca), FAKE + 4, FAKE, FAKE, FAKE, need, None) == -3
     # quantiser arguments
     assert L.moe_quantize_fp8_blockwise(FAKE, 7, 4, 4, 1, 1, FAKE, FAKE, None) == -2
     assert L.moe_quantize_fp8_blockwise(FAKE, 1, 4, 4, 0, 1, FAKE, FAKE, None) == -1
@@ -111,7 +121,16 @@ def test_workspace_sizes_follow_the_config(M):
     assert ws(1) >= ((1000 + 255) // 256) * 16 * 4
     assert ws(3) >= 1000 * 4 * 2 * 384 * 2
     assert ws(4) >= 1000 * 16 * 4
-    assert all(ws(op) % 256 == 0 for op in range(5))
+    assert all(ws(op) % 256 == 0 for op in range(6))
+    # the auxiliary loss: two [chunks, E] partial arrays; the router backward
+    # grows by the counts and f [E] only when the loss is on
+    ca = _cfg(M, T=1000, E=16, k=4, f=384, d=512, aux_coeff=0.01)
+    wa = lambda op: L.moe_workspace_size(ctypes.byref(ca), op)
+    assert wa(5) >= 2 * 16 * 4 and wa(5) == ws(5)
+    assert wa(4) >= ws(4) + 16 * 4 + 16 * 4
+    # 1 << 22 tokens: at most 256 chunks of partials
+    cb = _cfg(M, T=1 << 22, E=1024, k=2, aux_coeff=0.01)
+    assert L.moe_workspace_size(ctypes.byref(cb), 5) == 2 * 256 * 1024 * 4
 
 
 def test_status_strings(M):

@@ -84,6 +84,9 @@ def _compare_small(cfg, identity=False, inp=None, gemm_tile="auto"):
     else:
         assert np.array_equal(_np(layer.x_perm), ref["x_perm"]), "x_perm"
     tol = _tol(cfg)
+    if cfg.aux_coeff:
+        err = abs(float(layer.aux_loss.item()) - ref["aux_loss"]) / ref["aux_loss"]
+        assert err <= 1e-5, f"aux_loss rel {err:.2e}"
     pairs = [("y", layer.y, ref["y"]), ("d_gate", layer.d_gate, ref["d_gate"]),
              ("dx", layer.dx, ref["dx"])]
     if identity and cfg.renorm:
@@ -127,6 +130,12 @@ SMALL = {
     # and ragged groups smaller than a tile
     "qwen_skew_mini_big": S.mini(S.CONFIGS[3], T=700, d=256, f=128, E=16).replace(k=4, seed_base=34),
     "deepseek_fp8_mini": S.mini(S.CONFIGS[4], T=400, d=384, f=256, E=32).replace(k=6),
+    # the load-balancing auxiliary loss on (coefficient 0.01): its value and
+    # its share of the router gradient
+    "mixtral_mini_aux": S.mini(S.CONFIGS[1], T=1000, d=256, f=384).replace(aux_coeff=0.01),
+    "tiny_fp32_aux": S.CONFIGS[0].replace(aux_coeff=0.01),
+    "deepseek_mini_aux": S.mini(S.CONFIGS[2], T=300, d=256, f=256, E=32).replace(
+        k=6, aux_coeff=0.01),
 }
 
 
@@ -419,3 +428,63 @@ def _full_size_check(cfg, n_tok=24, n_cols=3):
 @pytest.mark.parametrize("which", [1, 2, 3, 4])
 def test_full_size_layer(which):
     _full_size_check(S.CONFIGS[which])
+
+
+# ------------------------------------------------ load-balancing aux loss
+
+AUX_CASES = [
+    # (T, d, E, k, act, score): ragged last chunk, several experts per lane,
+    # chunks of more than 64 tokens (T > 16384), E = 1000 (one split per expert)
+    (777, 128, 64, 4, "f32", "softmax"),
+    (513, 256, 300, 8, "bf16", "sigmoid"),
+    (70000, 128, 16, 2, "f32", "softmax"),
+    (300, 128, 1000, 16, "f32", "softmax"),
+    (1, 128, 8, 2, "f32", "softmax"),
+]
+
+
+@pytest.mark.parametrize("T,d,E,k,act,score", AUX_CASES)
+def test_aux_loss_and_gradient(T, d, E, k, act, score):
+    """The auxiliary loss alone: moe_route_aux_loss against the oracle, then
+    moe_route_bwd with d_gate = 0, so that dL is only the auxiliary term
+    times d_aux, seen through dw_router = dL^T x and dx = dL w_router."""
+    from mixture_experts_layer_gather_amd import _lib as L
+    coeff, d_aux = 0.01, 2.5
+    cfg = S.LayerConfig("aux", 90 + E % 7, T=T, d=d, E=E, k=k, f=128, act=act, weight=act,
+                        score=score, renorm=True, std=0.05, aux_coeff=coeff)
+    _say(f"[aux] T={T} d={d} E={E} k={k} {act} {score}")
+    x, wr = S.x(cfg), S.w_router(cfg)
+    Lo, idx, _ = oracle.route(cfg, x, wr)
+    c = L.make_config(**cfg.describe())
+    at = torch.float32 if act == "f32" else torch.bfloat16
+    xd, wd = x.to(DEV), wr.to(DEV)
+    logits = torch.empty(T, E, dtype=torch.float32, device=DEV)
+    tidx = torch.empty(T, k, dtype=torch.int32, device=DEV)
+    gate = torch.empty(T, k, dtype=torch.float32, device=DEV)
+    L.moe_route(c, xd, wd, None, logits, tidx, gate)
+    ws = torch.empty(max(1, L.workspace_size(c, L.OP_AUX_LOSS)), dtype=torch.uint8, device=DEV)
+    loss = torch.full((1,), float("nan"), device=DEV)
+    L.moe_route_aux_loss(c, logits, tidx, loss, ws)
+    torch.cuda.synchronize()
+    assert np.array_equal(_np(logits), Lo) and np.array_equal(_np(tidx), idx)
+    want = oracle.aux_loss(Lo, idx, E, coeff)
+    err = abs(loss.item() - want) / want
+    _say(f"[aux] loss {loss.item():.8f} oracle {want:.8f} rel {err:.2e}")
+    assert err <= 1e-5
+    dx = torch.zeros(T, d, dtype=at, device=DEV)
+    dwr = torch.empty(E, d, dtype=torch.float32, device=DEV)
+    wsb = torch.empty(L.workspace_size(c, L.OP_ROUTE_BWD), dtype=torch.uint8, device=DEV)
+    L.moe_route_bwd(c, xd, wd, logits, tidx, gate, torch.zeros(T, k, device=DEV), dx, dwr, wsb,
+                    d_aux=torch.full((1,), d_aux, device=DEV))
+    torch.cuda.synchronize()
+    dL = oracle.aux_loss_dlogits(Lo, idx, E, coeff, d_aux)
+    dWr, dx_r = oracle.route_bwd(dL, x, wr)
+    tol = TOL[act]
+    e1, e2 = oracle.rel_l2(_np(dwr), dWr), oracle.rel_l2(_np(dx), dx_r)
+    _say(f"[aux] dw_router rel L2 {e1:.2e} dx rel L2 {e2:.2e}")
+    assert e1 <= tol and e2 <= tol
+    # d_aux = NULL leaves the auxiliary term out: d_gate = 0 then gives zeros
+    dx.zero_()
+    L.moe_route_bwd(c, xd, wd, logits, tidx, gate, torch.zeros(T, k, device=DEV), dx, dwr, wsb)
+    torch.cuda.synchronize()
+    assert not dwr.any() and not dx.any()
