@@ -951,6 +951,7 @@ __global__ __launch_bounds__(256) void dlogits_kernel(DLArgs a) {
 //   aux_partials_kernel  one block per chunk of tokens: the chunk's expert
 //                        counts (LDS integer histogram) and, with WITH_P, its
 //                        sum of softmax probabilities (one wave per token,
+//                        each wave loading several rows before reducing any,
 //                        waves added in wave order);
 //   aux_final_kernel     one block: adds the chunk partials in chunk order,
 //                        writes f_e = count_e / (T k) and/or the loss.
@@ -958,10 +959,12 @@ __global__ __launch_bounds__(256) void dlogits_kernel(DLArgs a) {
 // is deterministic. HBM traffic: logits once (T E 4 bytes) plus idx.
 // ---------------------------------------------------------------------------
 constexpr int kAuxMaxBlocks = 256;  // chunks: enough blocks for small T, few partials for large T
+constexpr int kAuxWaves = 8;        // waves per block of aux_partials_kernel
+constexpr int kAuxRows = 4;         // logit rows a wave loads before reducing them
 
 static int64_t aux_tokens_per_block(int64_t T) {
   const int64_t per = (T + kAuxMaxBlocks - 1) / kAuxMaxBlocks;
-  return per < 64 ? 64 : (per + 63) / 64 * 64;
+  return per < 32 ? 32 : (per + 31) / 32 * 32;
 }
 
 int aux_blocks(int64_t T) {
@@ -969,12 +972,10 @@ int aux_blocks(int64_t T) {
 }
 
 template <int NPL, bool WITH_P>
-__global__ __launch_bounds__(256) void aux_partials_kernel(const float* __restrict__ logits,
-                                                           const int32_t* __restrict__ idx,
-                                                           float* __restrict__ p_part,
-                                                           int32_t* __restrict__ c_part, int T,
-                                                           int E, int k, int tpb) {
-  __shared__ float ps[WITH_P ? 4 : 1][kWave * NPL];
+__global__ __launch_bounds__(kAuxWaves * kWave) void aux_partials_kernel(
+    const float* __restrict__ logits, const int32_t* __restrict__ idx, float* __restrict__ p_part,
+    int32_t* __restrict__ c_part, int T, int E, int k, int tpb) {
+  __shared__ float ps[WITH_P ? kAuxWaves : 1][kWave * NPL];
   __shared__ int cnt[kWave * NPL];
   const int wave = threadIdx.x / kWave;
   const int lane = lane_id();
@@ -991,26 +992,36 @@ __global__ __launch_bounds__(256) void aux_partials_kernel(const float* __restri
     float acc[NPL];
 #pragma unroll
     for (int p = 0; p < NPL; ++p) acc[p] = 0.0f;
-    for (int tt = wave; tt < nt; tt += 4) {
-      const float* Lrow = logits + int64_t(t0 + tt) * E;
-      float Lv[NPL];
-      float m = -__builtin_inff();
+    // wave w takes tokens w, w + 8, w + 16, ...: kAuxRows rows loaded at once
+    for (int tt = wave; tt < nt; tt += kAuxWaves * kAuxRows) {
+      float Lv[kAuxRows][NPL];
 #pragma unroll
-      for (int p = 0; p < NPL; ++p) {
-        const int e = lane + kWave * p;
-        Lv[p] = e < E ? Lrow[e] : -__builtin_inff();
-        m = fmaxf(m, Lv[p]);
+      for (int r = 0; r < kAuxRows; ++r) {
+        const int t = tt + r * kAuxWaves;
+        const float* Lrow = logits + int64_t(t0 + t) * E;
+#pragma unroll
+        for (int p = 0; p < NPL; ++p) {
+          const int e = lane + kWave * p;
+          Lv[r][p] = (t < nt && e < E) ? Lrow[e] : -__builtin_inff();
+        }
       }
-      m = wave_max(m);
-      float q[NPL], z = 0.0f;
 #pragma unroll
-      for (int p = 0; p < NPL; ++p) {
-        q[p] = lane + kWave * p < E ? expf(Lv[p] - m) : 0.0f;
-        z += q[p];
+      for (int r = 0; r < kAuxRows; ++r) {
+        if (tt + r * kAuxWaves >= nt) break;
+        float m = Lv[r][0];
+#pragma unroll
+        for (int p = 1; p < NPL; ++p) m = fmaxf(m, Lv[r][p]);
+        m = wave_max(m);
+        float q[NPL], z = 0.0f;
+#pragma unroll
+        for (int p = 0; p < NPL; ++p) {
+          q[p] = lane + kWave * p < E ? expf(Lv[r][p] - m) : 0.0f;
+          z += q[p];
+        }
+        const float Z = wave_sum(z);
+#pragma unroll
+        for (int p = 0; p < NPL; ++p) acc[p] += q[p] / Z;
       }
-      const float Z = wave_sum(z);
-#pragma unroll
-      for (int p = 0; p < NPL; ++p) acc[p] += q[p] / Z;
     }
 #pragma unroll
     for (int p = 0; p < NPL; ++p) ps[wave][lane + kWave * p] = acc[p];
@@ -1018,33 +1029,39 @@ __global__ __launch_bounds__(256) void aux_partials_kernel(const float* __restri
   __syncthreads();
   for (int e = threadIdx.x; e < E; e += blockDim.x) {
     c_part[int64_t(blockIdx.x) * E + e] = cnt[e];
-    if constexpr (WITH_P)
-      p_part[int64_t(blockIdx.x) * E + e] = ((ps[0][e] + ps[1][e]) + ps[2][e]) + ps[3][e];
+    if constexpr (WITH_P) {
+      float v = ps[0][e];
+#pragma unroll
+      for (int w = 1; w < kAuxWaves; ++w) v += ps[w][e];
+      p_part[int64_t(blockIdx.x) * E + e] = v;
+    }
   }
 }
 
 // 1024 threads: expert e gets S = 1024 / E threads, split s adds chunks
 // s, s+S, s+2S, ... in order; the S split sums are then added in split order.
+// WITH_P: probability sums present (the loss); without, only f_e.
+template <bool WITH_P>
 __global__ __launch_bounds__(1024) void aux_final_kernel(const float* __restrict__ p_part,
                                                          const int32_t* __restrict__ c_part,
                                                          int nblk, int E, float tk,
                                                          float loss_scale, float* __restrict__ f_out,
                                                          float* __restrict__ loss) {
-  __shared__ float sp[1024];
+  __shared__ float sp[WITH_P ? 1024 : 1];
   __shared__ int sc[1024];
-  __shared__ float red[1024];
+  __shared__ float red[WITH_P ? 1024 : 1];
   const int tid = threadIdx.x;
   const int S = 1024 / E;
   if (tid < S * E) {
     const int e = tid % E, s = tid / E;
     int c = 0;
     float P = 0.0f;
-#pragma unroll 8
+#pragma unroll 16
     for (int b = s; b < nblk; b += S) {
       c += c_part[int64_t(b) * E + e];
-      if (p_part) P += p_part[int64_t(b) * E + e];
+      if constexpr (WITH_P) P += p_part[int64_t(b) * E + e];
     }
-    sp[tid] = P;
+    if constexpr (WITH_P) sp[tid] = P;
     sc[tid] = c;
   }
   __syncthreads();
@@ -1054,20 +1071,21 @@ __global__ __launch_bounds__(1024) void aux_final_kernel(const float* __restrict
     float P = 0.0f;
     for (int s = 0; s < S; ++s) {
       c += sc[s * E + tid];
-      P += sp[s * E + tid];
+      if constexpr (WITH_P) P += sp[s * E + tid];
     }
     const float fe = float(c) / tk;
     if (f_out) f_out[tid] = fe;
     term = fe * P;
   }
-  if (!loss) return;
-  red[tid] = term;
-  __syncthreads();
-  for (int o = 512; o > 0; o >>= 1) {
-    if (tid < o) red[tid] += red[tid + o];
+  if constexpr (WITH_P) {
+    red[tid] = term;
     __syncthreads();
+    for (int o = 512; o > 0; o >>= 1) {
+      if (tid < o) red[tid] += red[tid + o];
+      __syncthreads();
+    }
+    if (tid == 0) loss[0] = loss_scale * red[0];
   }
-  if (tid == 0) loss[0] = loss_scale * red[0];
 }
 
 template <bool WITH_P>
@@ -1076,18 +1094,19 @@ static void launch_aux_partials(const float* logits, const int32_t* idx, float* 
   const int nb = aux_blocks(T);
   const int tpb = int(aux_tokens_per_block(T));
   const int t = int(T), e = int(E), kk = int(k);
-  if (E <= 64) aux_partials_kernel<1, WITH_P><<<nb, 256, 0, st>>>(logits, idx, p_part, c_part, t, e, kk, tpb);
-  else if (E <= 128) aux_partials_kernel<2, WITH_P><<<nb, 256, 0, st>>>(logits, idx, p_part, c_part, t, e, kk, tpb);
-  else if (E <= 256) aux_partials_kernel<4, WITH_P><<<nb, 256, 0, st>>>(logits, idx, p_part, c_part, t, e, kk, tpb);
-  else if (E <= 512) aux_partials_kernel<8, WITH_P><<<nb, 256, 0, st>>>(logits, idx, p_part, c_part, t, e, kk, tpb);
-  else aux_partials_kernel<16, WITH_P><<<nb, 256, 0, st>>>(logits, idx, p_part, c_part, t, e, kk, tpb);
+  constexpr int B = kAuxWaves * kWave;
+  if (E <= 64) aux_partials_kernel<1, WITH_P><<<nb, B, 0, st>>>(logits, idx, p_part, c_part, t, e, kk, tpb);
+  else if (E <= 128) aux_partials_kernel<2, WITH_P><<<nb, B, 0, st>>>(logits, idx, p_part, c_part, t, e, kk, tpb);
+  else if (E <= 256) aux_partials_kernel<4, WITH_P><<<nb, B, 0, st>>>(logits, idx, p_part, c_part, t, e, kk, tpb);
+  else if (E <= 512) aux_partials_kernel<8, WITH_P><<<nb, B, 0, st>>>(logits, idx, p_part, c_part, t, e, kk, tpb);
+  else aux_partials_kernel<16, WITH_P><<<nb, B, 0, st>>>(logits, idx, p_part, c_part, t, e, kk, tpb);
 }
 
 void launch_route_aux_loss(const AuxLaunch& a, hipStream_t st) {
   launch_aux_partials<true>(a.logits, a.idx, a.p_part, a.c_part, a.T, a.E, a.k, st);
-  aux_final_kernel<<<1, 1024, 0, st>>>(a.p_part, a.c_part, aux_blocks(a.T), int(a.E),
-                                       float(a.T * a.k), a.coeff * float(a.E) / float(a.T), nullptr,
-                                       a.loss);
+  aux_final_kernel<true><<<1, 1024, 0, st>>>(a.p_part, a.c_part, aux_blocks(a.T), int(a.E),
+                                             float(a.T * a.k), a.coeff * float(a.E) / float(a.T),
+                                             nullptr, a.loss);
 }
 
 // ---------------------------------------------------------------------------
@@ -1135,8 +1154,8 @@ static void route_bwd_t(const RouteBwdLaunch& r, hipStream_t st) {
   if (r.d_aux) {
     // f_e from the selection, then the aux term inside dlogits_kernel
     launch_aux_partials<false>(nullptr, r.idx, nullptr, r.aux_counts, r.T, r.E, r.k, st);
-    aux_final_kernel<<<1, 1024, 0, st>>>(nullptr, r.aux_counts, aux_blocks(r.T), int(r.E),
-                                         float(r.T * r.k), 0.0f, r.aux_f, nullptr);
+    aux_final_kernel<false><<<1, 1024, 0, st>>>(nullptr, r.aux_counts, aux_blocks(r.T), int(r.E),
+                                                float(r.T * r.k), 0.0f, r.aux_f, nullptr);
     d.aux_f = r.aux_f;
     d.d_aux = r.d_aux;
     d.aux_scale = r.aux_coeff * float(r.E) / float(r.T);
