@@ -18,10 +18,12 @@ The pages print no dataset; seeded normal inputs stand in for real token
 activations and trained weights.
 
 Seeding: every tensor is drawn with its own CPU ``torch.Generator`` seeded
-with ``(seed_base << 40) | (tensor_id << 24) | expert_id``, as fp32
+with ``(seed_base << 16) | (tensor_id << 11) | expert_id``, as fp32
 ``normal_()``, multiplied by ``std`` in fp32, then cast round-to-nearest-even
-to the stored dtype. Expert weights are drawn per expert so that one expert
-can be regenerated alone.
+to the stored dtype. The CPU generator (a Mersenne twister) keeps only the
+low 32 bits of its seed, so the three fields are packed into 32 bits.
+Expert weights are drawn per expert so that one expert can be regenerated
+alone.
 """
 from __future__ import annotations
 
@@ -110,8 +112,10 @@ def master_dtype(cfg: LayerConfig) -> torch.dtype:
 
 def draw(seed_base: int, tensor_id: int, expert_id: int, shape, std: float,
          dtype: torch.dtype, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    if not (0 <= seed_base < 1 << 16 and 0 <= tensor_id < 1 << 5 and 0 <= expert_id < 1 << 11):
+        raise ValueError(f"seed fields out of range: {seed_base}, {tensor_id}, {expert_id}")
     g = torch.Generator("cpu")
-    g.manual_seed((seed_base << 40) | (tensor_id << 24) | expert_id)
+    g.manual_seed((seed_base << 16) | (tensor_id << 11) | expert_id)
     t = torch.empty(shape, dtype=torch.float32)
     t.normal_(generator=g)
     if std != 1.0:
