@@ -211,11 +211,11 @@ def stage_work(c):
     return w
 
 
-def make_layer(cfg, device):
+def make_layer(cfg, device, recompute="none"):
     import torch
     import moe_synth as S
     from mixture_experts_layer_gather_amd import MoELayer
-    layer = MoELayer(**cfg.describe(), device=device)
+    layer = MoELayer(**cfg.describe(), recompute=recompute, device=device)
     w1, w2 = S.all_expert_weights(cfg, device=device, threads=16)
     bias = S.router_bias(cfg)
     sw1 = S.shared_w1(cfg).to(device) if cfg.shared else None
@@ -285,6 +285,26 @@ def timed_step(layer, x, dy, marks):
                     layer.d_gate, layer.dx, layer.dw_router, layer.ws_route_bwd,
                     d_aux=layer.d_aux if layer.aux else None)
     rec("route_bwd")
+
+
+def graph_replay(layer, x, dy, warmup, steps, T):
+    """The whole step captured once into a HIP graph (every library call
+    only enqueues and reads its shapes from device memory), then replayed."""
+    import torch
+    g = torch.cuda.CUDAGraph()
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g):
+        layer.step(x, dy)
+    for _ in range(warmup):
+        g.replay()
+    torch.cuda.synchronize()
+    start = _event()
+    for _ in range(steps):
+        g.replay()
+    stop = _event()
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(stop) / steps
+    return {"ms_per_step": round(ms, 4), "tokens_per_s": round(T / (ms / 1e3), 1)}
 
 
 def _event():
@@ -376,6 +396,11 @@ def main():
     ap.add_argument("--aux-coeff", type=float, default=0.0,
                     help="load-balancing auxiliary loss coefficient (0.01 in the Megatron recipe; "
                          "0: off, as in the workloads' definitions)")
+    ap.add_argument("--recompute", choices=["none", "act", "full"], default="none",
+                    help="activations the expert FFN keeps for the backward: GU and H (none), "
+                         "GU only (act), nothing (full)")
+    ap.add_argument("--graph", action="store_true",
+                    help="also capture the step into one HIP graph and time its replays")
     ap.add_argument("--cpu-sample", type=int, default=4096,
                     help="tokens of the workload timed on the CPU oracle (0: skip)")
     ap.add_argument("--copy-probe", action="store_true",
@@ -431,7 +456,7 @@ def main():
         cfg = cfg.replace(aux_coeff=args.aux_coeff)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    layer, x, dy = make_layer(cfg, dev)
+    layer, x, dy = make_layer(cfg, dev, args.recompute)
 
     for _ in range(args.warmup):
         timed_step(layer, x, dy, [])
@@ -504,6 +529,10 @@ def main():
         "roofline": roof,
         "wall_s": round(wall, 3),
     }
+    if args.recompute != "none":
+        out["config"]["recompute"] = args.recompute
+    if args.graph:
+        out["graph"] = graph_replay(layer, x, dy, args.warmup, args.steps, cfg.T)
     if args.cpu_sample > 0:
         out["cpu_baseline"] = cpu_baseline(cfg, args.cpu_sample)
     print(json.dumps(out))

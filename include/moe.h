@@ -64,6 +64,7 @@ enum { MOE_SCORE_SOFTMAX = 0, MOE_SCORE_SIGMOID = 1 };
 enum { MOE_GROUP_TOP2_SUM = 0, MOE_GROUP_MAX = 1 };
 enum { MOE_FFN_SWIGLU = 0, MOE_FFN_IDENTITY = 1 };
 enum { MOE_TILE_AUTO = 0, MOE_TILE_SMALL = 1, MOE_TILE_BIG = 2 };
+enum { MOE_RECOMPUTE_NONE = 0, MOE_RECOMPUTE_ACT = 1, MOE_RECOMPUTE_FULL = 2 };
 enum {
     MOE_OP_ROUTE = 0,
     MOE_OP_DISPATCH = 1,
@@ -95,7 +96,14 @@ enum {
  *              for tuning and to test every kernel variant.
  *  aux_coeff   weight of the load-balancing auxiliary loss (0.01 in the
  *              MoE workflow of the Megatron Core page); 0 turns the loss
- *              and its gradient off. */
+ *              and its gradient off.
+ *  recompute   what the grouped FFN keeps between its forward and backward
+ *              calls: MOE_RECOMPUTE_NONE saves GU and H; MOE_RECOMPUTE_ACT
+ *              saves GU only (act_h, h_scale may be NULL) and the backward
+ *              rebuilds the SwiGLU output H from it; MOE_RECOMPUTE_FULL
+ *              saves nothing (act_gu may be NULL too) and the backward
+ *              reruns the first expert GEMM. Outputs are bitwise the same
+ *              in all three modes. */
 typedef struct moe_config {
     int64_t num_tokens;  /* T */
     int64_t hidden;      /* d, a multiple of 128 */
@@ -114,6 +122,7 @@ typedef struct moe_config {
     int32_t ffn_mode;
     int32_t gemm_tile;   /* MOE_TILE_*, 0 by default */
     float aux_coeff;     /* finite, >= 0 */
+    int32_t recompute;   /* MOE_RECOMPUTE_*, 0 by default */
 } moe_config;
 
 /* Bytes of workspace the call `op` (MOE_OP_*) needs for this configuration;
@@ -176,6 +185,11 @@ int moe_dispatch(const moe_config *cfg, const void *x, const int32_t *topk_idx,
  *   act_h      [A,f]: act, or for wt = fp8 E4M3 codes with h_scale
  *              [A,f/128] f32 (H is quantised before the second GEMM)
  *   out_perm   [A,d] act
+ * With cfg->recompute = MOE_RECOMPUTE_ACT, act_h and h_scale may be NULL and
+ * are not written (H lives in the workspace only); with MOE_RECOMPUTE_FULL,
+ * act_gu is not written either.
+ * H is computed from G and U as stored in act_gu (rounded to act), so that
+ * the backward can rebuild it bit for bit.
  * The shared expert of DeepSeek-style layers is this call with E = 1, k = 1
  * over the (quantised) unpermuted x and offsets {0, T}.
  * Workspace: moe_workspace_size(cfg, MOE_OP_GROUPED_FFN). */
@@ -212,6 +226,17 @@ int moe_combine_bwd(const moe_config *cfg, const void *dy, const void *out_perm,
  * out: dx_perm [A,d] act; dw1 [E,2f,d], dw2 [E,d,f] in the parameter dtype
  * (f32 when wt is f32, else bf16), overwritten; an expert with no rows gets
  * exact zeros.
+ * Recompute (Megatron Core MoE summary, section 2.2: activations that take
+ * memory but are cheap to compute are recomputed in the backward instead of
+ * stored):
+ *   MOE_RECOMPUTE_ACT: act_h and h_scale are ignored (may be NULL); the dH
+ *     GEMM's epilogue, which reads G and U anyway, also writes H =
+ *     silu(G) * U into the workspace ([A,f] act; fp8: [A,f] bf16, then
+ *     its E4M3 codes and scales as in the forward).
+ *   MOE_RECOMPUTE_FULL: act_gu is ignored too; GU and H are recomputed from
+ *     x_perm and w1 by the forward's first GEMM into the workspace, which
+ *     grows by [A,3f] act (fp8: + the bf16 H, codes and scales).
+ * The results are bitwise those of MOE_RECOMPUTE_NONE.
  * Workspace: moe_workspace_size(cfg, MOE_OP_GROUPED_FFN_BWD). */
 int moe_grouped_ffn_bwd(const moe_config *cfg, const void *x_perm,
                         const float *x_scale, const int32_t *offsets,

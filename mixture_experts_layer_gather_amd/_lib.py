@@ -54,18 +54,21 @@ class MoeConfig(ctypes.Structure):
         ("ffn_mode", ctypes.c_int32),
         ("gemm_tile", ctypes.c_int32),
         ("aux_coeff", ctypes.c_float),
+        ("recompute", ctypes.c_int32),
     ]
 
 TILE = {"auto": 0, "small": 1, "big": 2}
+RECOMPUTE = {"none": 0, "act": 1, "full": 2}
 
 
 def make_config(T, d, E, k, f, score="softmax", renorm=True, gate_scale=1.0, num_groups=1,
                 topk_groups=1, group_score="top2_sum", act="bf16", weight="bf16",
                 quant_block=128, identity=False, gemm_tile="auto", aux_coeff=0.0,
-                **_ignored) -> MoeConfig:
+                recompute="none", **_ignored) -> MoeConfig:
     return MoeConfig(T, d, E, k, f, SCORE[score], int(bool(renorm)), float(gate_scale),
                      num_groups, topk_groups, GROUP_SCORE[group_score], DTYPE[act], DTYPE[weight],
-                     quant_block, 1 if identity else 0, TILE[gemm_tile], float(aux_coeff))
+                     quant_block, 1 if identity else 0, TILE[gemm_tile], float(aux_coeff),
+                     RECOMPUTE[recompute])
 
 
 _lib = None

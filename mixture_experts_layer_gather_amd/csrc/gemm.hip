@@ -121,8 +121,8 @@ struct GemmArgs {
   int G;
   int M, N, K;        // ROWS: N, K used; KSPLIT: M, N used
   int f;              // SwiGLU half width
-  void* aux0;         // SWIGLU: GU out [rows,2f]; DSWIGLU: GU in
-  void* aux1;         // SWIGLU: H out [rows,f]
+  void* aux0;         // SWIGLU: GU out [rows,2f] or null (not kept); DSWIGLU: GU in
+  void* aux1;         // SWIGLU: H out [rows,f]; DSWIGLU: H recomputed out, or null
   int tiles_n;
   int tiles_m;        // KSPLIT
   // FP8 block scales
@@ -348,6 +348,16 @@ template <typename T> __device__ __forceinline__ void store8(T* p, const float* 
     Vec16<float>::store(p + 4, v + 4);
   }
 }
+// Rounds 8 values to the storage type T and back (the values as saved).
+template <typename T> __device__ __forceinline__ void round8(float* v) {
+  if constexpr (sizeof(T) == 2) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v[e] = bf16_to_f32(f32_to_bf16(v[e]));
+  }
+}
+// SwiGLU output from the gate and up values as saved; the forward and the
+// backward's recompute share this expression, so both give the same bits.
+__device__ __forceinline__ float swiglu_h(float g, float u) { return g / (1.0f + expf(-g)) * u; }
 template <typename T> __device__ __forceinline__ void load8(const T* p, float* v) {
   if constexpr (sizeof(T) == 2) {
     Vec16<bf16_t>::load(p, v);
@@ -837,10 +847,14 @@ void gemm_kernel(GemmArgs g) {
           float G[8], U[8], Hv[8];
           lds_read8(&stg[rr * EP + c8 * 8], G);
           lds_read8(&stg[rr * EP + WTN / 2 + c8 * 8], U);
+          round8<TO>(G);
+          round8<TO>(U);
 #pragma unroll
-          for (int e = 0; e < 8; ++e) Hv[e] = G[e] / (1.0f + expf(-G[e])) * U[e];
-          store8<TO>(GU + row * (2 * g.f) + col, G);
-          store8<TO>(GU + row * (2 * g.f) + g.f + col, U);
+          for (int e = 0; e < 8; ++e) Hv[e] = swiglu_h(G[e], U[e]);
+          if (GU) {
+            store8<TO>(GU + row * (2 * g.f) + col, G);
+            store8<TO>(GU + row * (2 * g.f) + g.f + col, U);
+          }
           store8<TO>(H + row * g.f + col, Hv);
         }
       }
@@ -870,6 +884,12 @@ void gemm_kernel(GemmArgs g) {
             }
             store8<TO>(D + row * (2 * g.f) + col, dG);
             store8<TO>(D + row * (2 * g.f) + g.f + col, dU);
+            if (g.aux1) {  // activation recompute: H for the weight gradient
+              float Hv[8];
+#pragma unroll
+              for (int e = 0; e < 8; ++e) Hv[e] = swiglu_h(G[e], U[e]);
+              store8<TO>(reinterpret_cast<TO*>(g.aux1) + row * g.f + col, Hv);
+            }
           }
         }
       }
@@ -1026,7 +1046,10 @@ static void zero_bytes(void* dst, int64_t bytes, hipStream_t st) {
 
 // Workspace layout of the grouped FFN calls (byte offsets; see ffn_ws_bytes).
 struct FfnWs {
-  size_t h_bf16 = 0;   // fwd fp8: H before quantisation [A, f] bf16
+  size_t h_bf16 = 0;   // fp8: H before quantisation [A, f] bf16 (fwd; bwd with recompute)
+  size_t r_gu = 0;     // recompute 2, bwd: GU [A, 2f] act
+  size_t r_h = 0;      // recompute: H [A, f] (act; fp8: E4M3 codes)
+  size_t r_hs = 0;     // recompute, fp8: H scales [A, f/128]
   size_t d_gu = 0;     // bwd: dGU [A, 2f] act
   size_t d_out_q = 0;  // bwd fp8: dO codes [A, d] + scales [A, d/128]
   size_t d_out_s = 0;
@@ -1039,12 +1062,18 @@ struct FfnWs {
 
 static size_t al(size_t v) { return (v + 255) & ~size_t(255); }
 
-static FfnWs ffn_ws(int64_t A, int64_t d, int64_t f, int act_bytes, bool fp8, bool bwd) {
+static FfnWs ffn_ws(int64_t A, int64_t d, int64_t f, int act_bytes, bool fp8, bool bwd, int rc) {
   FfnWs w;
   size_t o = 0;
-  if (!bwd) {
-    if (fp8) { w.h_bf16 = o; o += al(size_t(A) * f * 2); }
-  } else {
+  // H, when it is not kept between the calls, lives in the workspace: the
+  // forward's GEMM2 operand, or the backward's rebuilt copy
+  if (fp8 && (!bwd || rc)) { w.h_bf16 = o; o += al(size_t(A) * f * 2); }
+  if (bwd && rc == 2) { w.r_gu = o; o += al(size_t(A) * 2 * f * act_bytes); }
+  if (rc) {
+    w.r_h = o; o += al(size_t(A) * f * (fp8 ? 1 : act_bytes));
+    if (fp8) { w.r_hs = o; o += al(size_t(A) * (f / 128) * 4); }
+  }
+  if (bwd) {
     w.d_gu = o; o += al(size_t(A) * 2 * f * act_bytes);
     if (fp8) {
       w.d_out_q = o; o += al(size_t(A) * d);
@@ -1059,29 +1088,31 @@ static FfnWs ffn_ws(int64_t A, int64_t d, int64_t f, int act_bytes, bool fp8, bo
   return w;
 }
 
-size_t ffn_ws_bytes(int64_t A, int64_t d, int64_t f, int act_bytes, bool fp8, bool bwd) {
-  return ffn_ws(A, d, f, act_bytes, fp8, bwd).total;
+size_t ffn_ws_bytes(int64_t A, int64_t d, int64_t f, int act_bytes, bool fp8, bool bwd, int recompute) {
+  return ffn_ws(A, d, f, act_bytes, fp8, bwd, recompute).total;
 }
 
-// GEMM1 (+ SwiGLU): GU = X W1^T, H = silu(G) * U
+static char* at(void* base, size_t off) { return static_cast<char*>(base) + off; }
+
+// GEMM1 (+ SwiGLU): GU = X W1^T (stored unless gu is null), H = silu(G) * U
 template <typename C>
-static void gemm1_fwd(const FfnLaunch& a, hipStream_t st) {
+static void gemm1_fwd(const FfnLaunch& a, void* gu, void* h, hipStream_t st) {
   typedef typename C::type T;
   GemmArgs g1{};
   g1.A = a.x_perm; g1.lda = a.d;
   g1.B = a.w1; g1.ldb = a.d; g1.b_gstride = 2 * a.f * a.d;
   g1.offsets = a.offsets; g1.G = int(a.E);
   g1.N = int(2 * a.f); g1.K = int(a.d); g1.f = int(a.f);
-  g1.aux0 = a.act_gu; g1.aux1 = a.act_h;
+  g1.aux0 = gu; g1.aux1 = h;
   g1.tiles_n = int(2 * a.f / C::BN);
   run_gemm<C, T, true, true, G_ROWS, EPI_SWIGLU>(g1, rows_tile_bound(a.A, a.E, C::BM) * g1.tiles_n, st);
 }
 // GEMM2: O = H W2^T
 template <typename C>
-static void gemm2_fwd(const FfnLaunch& a, hipStream_t st) {
+static void gemm2_fwd(const FfnLaunch& a, const void* h, hipStream_t st) {
   typedef typename C::type T;
   GemmArgs g2{};
-  g2.A = a.act_h; g2.lda = a.f;
+  g2.A = h; g2.lda = a.f;
   g2.B = a.w2; g2.ldb = a.f; g2.b_gstride = a.d * a.f;
   g2.C = a.out_perm; g2.ldc = a.d;
   g2.offsets = a.offsets; g2.G = int(a.E);
@@ -1090,12 +1121,11 @@ static void gemm2_fwd(const FfnLaunch& a, hipStream_t st) {
   run_gemm<C, T, true, true, G_ROWS, EPI_STORE>(g2, rows_tile_bound(a.A, a.E, C::BM) * g2.tiles_n, st);
 }
 
-static void ffn_fwd_fp8(const FfnLaunch& a, hipStream_t st) {
+// FP8 GEMM1 (+ SwiGLU) into h16 (bf16), then H -> E4M3 per 1 x 128 block
+// (the second GEMM's A operand, and the weight gradient's after dequantising)
+static void gemm1_fwd_fp8(const FfnLaunch& a, void* gu, bf16_t* h16, uint8_t* hq, float* hs,
+                          hipStream_t st) {
   typedef SmallCfg<fp8_t> C;
-  constexpr int BM = C::BM, BN = C::BN;
-  const FfnWs w = ffn_ws(a.A, a.d, a.f, 2, true, false);
-  bf16_t* h16 = reinterpret_cast<bf16_t*>(static_cast<char*>(a.ws) + w.h_bf16);
-  const int mt_bound = rows_tile_bound(a.A, a.E, BM);
   GemmArgs g1{};
   g1.A = a.x_perm; g1.lda = a.d;
   g1.a_scale = a.x_scale; g1.a_scale_ld = int(a.d / 128);
@@ -1103,21 +1133,36 @@ static void ffn_fwd_fp8(const FfnLaunch& a, hipStream_t st) {
   g1.b_scale = a.w1_scale; g1.b_scale_gstride = (2 * a.f / 128) * (a.d / 128); g1.b_scale_ld = int(a.d / 128);
   g1.offsets = a.offsets; g1.G = int(a.E);
   g1.N = int(2 * a.f); g1.K = int(a.d); g1.f = int(a.f);
-  g1.aux0 = a.act_gu; g1.aux1 = h16;
-  g1.tiles_n = int(2 * a.f / BN);
-  run_gemm<C, bf16_t, true, true, G_ROWS, EPI_SWIGLU>(g1, mt_bound * g1.tiles_n, st);
-  // H -> E4M3 per 1 x 128 block (the second GEMM's A operand, saved for bwd)
-  launch_quant_rows(h16, true, a.A, a.f, reinterpret_cast<uint8_t*>(a.act_h), a.h_scale, st);
+  g1.aux0 = gu; g1.aux1 = h16;
+  g1.tiles_n = int(2 * a.f / C::BN);
+  run_gemm<C, bf16_t, true, true, G_ROWS, EPI_SWIGLU>(g1, rows_tile_bound(a.A, a.E, C::BM) * g1.tiles_n, st);
+  launch_quant_rows(h16, true, a.A, a.f, hq, hs, st);
+}
+
+static void gemm2_fwd_fp8(const FfnLaunch& a, const uint8_t* hq, const float* hs, hipStream_t st) {
+  typedef SmallCfg<fp8_t> C;
   GemmArgs g2{};
-  g2.A = a.act_h; g2.lda = a.f;
-  g2.a_scale = a.h_scale; g2.a_scale_ld = int(a.f / 128);
+  g2.A = hq; g2.lda = a.f;
+  g2.a_scale = hs; g2.a_scale_ld = int(a.f / 128);
   g2.B = a.w2; g2.ldb = a.f; g2.b_gstride = a.d * a.f;
   g2.b_scale = a.w2_scale; g2.b_scale_gstride = (a.d / 128) * (a.f / 128); g2.b_scale_ld = int(a.f / 128);
   g2.C = a.out_perm; g2.ldc = a.d;
   g2.offsets = a.offsets; g2.G = int(a.E);
   g2.N = int(a.d); g2.K = int(a.f);
-  g2.tiles_n = int(a.d / BN);
-  run_gemm<C, bf16_t, true, true, G_ROWS, EPI_STORE>(g2, mt_bound * g2.tiles_n, st);
+  g2.tiles_n = int(a.d / C::BN);
+  run_gemm<C, bf16_t, true, true, G_ROWS, EPI_STORE>(g2, rows_tile_bound(a.A, a.E, C::BM) * g2.tiles_n, st);
+}
+
+// The first half of the forward: GU (into gu unless null) and H (+ scales).
+static void ffn_fwd_gu_h(const FfnLaunch& a, void* gu, void* h, float* hs, bf16_t* h16, hipStream_t st) {
+  if (a.wt == 2) {
+    gemm1_fwd_fp8(a, gu, h16, static_cast<uint8_t*>(h), hs, st);
+  } else if (a.wt == 1) {
+    if (big_rows(a.tile, a.A, a.E, 2 * a.f)) gemm1_fwd<BigCfg>(a, gu, h, st);
+    else gemm1_fwd<SmallCfg<bf16_t>>(a, gu, h, st);
+  } else {
+    gemm1_fwd<SmallCfg<float>>(a, gu, h, st);
+  }
 }
 
 // Weight gradients over the ragged rows of every expert (K split by group).
@@ -1153,9 +1198,9 @@ static void wgrad_any(int tile, const void* d_out, const void* act_h, const void
     wgrad_t<SmallCfg<bf16_t>, TC16>(d_out, act_h, d_gu, x, dw1, dw2, offsets, d, f, E, st);
 }
 
-// dH = dO W2, fused SwiGLU backward -> dGU
+// dH = dO W2, fused SwiGLU backward -> dGU (and H rebuilt into h_out unless null)
 template <typename C>
-static void dh_bwd(const FfnBwdLaunch& a, void* d_gu, hipStream_t st) {
+static void dh_bwd(const FfnBwdLaunch& a, void* d_gu, void* h_out, hipStream_t st) {
   typedef typename C::type T;
   GemmArgs g1{};
   g1.A = a.d_out; g1.lda = a.d;
@@ -1163,7 +1208,7 @@ static void dh_bwd(const FfnBwdLaunch& a, void* d_gu, hipStream_t st) {
   g1.C = d_gu; g1.ldc = 2 * a.f;
   g1.offsets = a.offsets; g1.G = int(a.E);
   g1.N = int(a.f); g1.K = int(a.d); g1.f = int(a.f);
-  g1.aux0 = const_cast<void*>(a.act_gu);
+  g1.aux0 = const_cast<void*>(a.act_gu); g1.aux1 = h_out;
   g1.tiles_n = int(a.f / C::BN);
   run_gemm<C, T, true, false, G_ROWS, EPI_DSWIGLU>(g1, rows_tile_bound(a.A, a.E, C::BM) * g1.tiles_n, st);
 }
@@ -1181,18 +1226,20 @@ static void dx_bwd(const FfnBwdLaunch& a, const void* d_gu, hipStream_t st) {
   run_gemm<C, T, true, false, G_ROWS, EPI_STORE>(g2, rows_tile_bound(a.A, a.E, C::BM) * g2.tiles_n, st);
 }
 
+// a.act_h is the saved H, or, with h_out set (activation recompute), the
+// buffer the dH GEMM's epilogue rebuilds H into from the saved GU.
 template <typename T>
-static void ffn_bwd_t(const FfnBwdLaunch& a, hipStream_t st) {
-  const FfnWs w = ffn_ws(a.A, a.d, a.f, int(sizeof(T)), false, true);
-  void* d_gu = static_cast<char*>(a.ws) + w.d_gu;
+static void ffn_bwd_t(const FfnBwdLaunch& a, void* h_out, hipStream_t st) {
+  const FfnWs w = ffn_ws(a.A, a.d, a.f, int(sizeof(T)), false, true, a.recompute);
+  void* d_gu = at(a.ws, w.d_gu);
   if constexpr (sizeof(T) == 2) {
-    if (big_rows(a.tile, a.A, a.E, a.f)) dh_bwd<BigCfg>(a, d_gu, st);
-    else dh_bwd<SmallCfg<bf16_t>>(a, d_gu, st);
+    if (big_rows(a.tile, a.A, a.E, a.f)) dh_bwd<BigCfg>(a, d_gu, h_out, st);
+    else dh_bwd<SmallCfg<bf16_t>>(a, d_gu, h_out, st);
     if (big_rows(a.tile, a.A, a.E, a.d)) dx_bwd<BigCfg>(a, d_gu, st);
     else dx_bwd<SmallCfg<bf16_t>>(a, d_gu, st);
     wgrad_any<bf16_t>(a.tile, a.d_out, a.act_h, d_gu, a.x_perm, a.dw1, a.dw2, a.offsets, a.d, a.f, a.E, st);
   } else {
-    dh_bwd<SmallCfg<float>>(a, d_gu, st);
+    dh_bwd<SmallCfg<float>>(a, d_gu, h_out, st);
     dx_bwd<SmallCfg<float>>(a, d_gu, st);
     wgrad_t<SmallCfg<float>, float>(a.d_out, a.act_h, d_gu, a.x_perm, a.dw1, a.dw2, a.offsets, a.d, a.f,
                                      a.E, st);
@@ -1202,20 +1249,20 @@ static void ffn_bwd_t(const FfnBwdLaunch& a, hipStream_t st) {
 // FP8 backward: the data-gradient GEMMs run in FP8 with their gradient
 // operand quantised per 1 x 128 block along the contraction dim and the
 // forward's 128 x 128 weight blocks; the weight gradients run in bf16 on the
-// dequantised forward operands (X, H) and the bf16 gradients.
-static void ffn_bwd_fp8(const FfnBwdLaunch& a, hipStream_t st) {
+// dequantised forward operands (X, H) and the bf16 gradients. With h16 set
+// (activation recompute) the dH epilogue rebuilds H in bf16 from the saved
+// GU and it is quantised as in the forward into a.act_h / a.h_scale.
+static void ffn_bwd_fp8(const FfnBwdLaunch& a, bf16_t* h16, hipStream_t st) {
   typedef SmallCfg<fp8_t> C;
-  constexpr int BM = C::BM, BN = C::BN;
-  const FfnWs w = ffn_ws(a.A, a.d, a.f, 2, true, true);
-  char* ws = static_cast<char*>(a.ws);
-  bf16_t* d_gu = reinterpret_cast<bf16_t*>(ws + w.d_gu);
-  uint8_t* dq = reinterpret_cast<uint8_t*>(ws + w.d_out_q);
-  float* ds = reinterpret_cast<float*>(ws + w.d_out_s);
-  uint8_t* gq = reinterpret_cast<uint8_t*>(ws + w.d_gu_q);
-  float* gs = reinterpret_cast<float*>(ws + w.d_gu_s);
-  bf16_t* xd = reinterpret_cast<bf16_t*>(ws + w.x_deq);
-  bf16_t* hd = reinterpret_cast<bf16_t*>(ws + w.h_deq);
-  const int mt_bound = rows_tile_bound(a.A, a.E, BM);
+  const FfnWs w = ffn_ws(a.A, a.d, a.f, 2, true, true, a.recompute);
+  bf16_t* d_gu = reinterpret_cast<bf16_t*>(at(a.ws, w.d_gu));
+  uint8_t* dq = reinterpret_cast<uint8_t*>(at(a.ws, w.d_out_q));
+  float* ds = reinterpret_cast<float*>(at(a.ws, w.d_out_s));
+  uint8_t* gq = reinterpret_cast<uint8_t*>(at(a.ws, w.d_gu_q));
+  float* gs = reinterpret_cast<float*>(at(a.ws, w.d_gu_s));
+  bf16_t* xd = reinterpret_cast<bf16_t*>(at(a.ws, w.x_deq));
+  bf16_t* hd = reinterpret_cast<bf16_t*>(at(a.ws, w.h_deq));
+  const int mt_bound = rows_tile_bound(a.A, a.E, C::BM);
   launch_quant_rows(a.d_out, true, a.A, a.d, dq, ds, st);
   // dH = Q(dO) W2 (+ SwiGLU backward from the saved bf16 GU)
   GemmArgs g1{};
@@ -1226,9 +1273,12 @@ static void ffn_bwd_fp8(const FfnBwdLaunch& a, hipStream_t st) {
   g1.C = d_gu; g1.ldc = 2 * a.f;
   g1.offsets = a.offsets; g1.G = int(a.E);
   g1.N = int(a.f); g1.K = int(a.d); g1.f = int(a.f);
-  g1.aux0 = const_cast<void*>(a.act_gu);
-  g1.tiles_n = int(a.f / BN);
+  g1.aux0 = const_cast<void*>(a.act_gu); g1.aux1 = h16;
+  g1.tiles_n = int(a.f / C::BN);
   run_gemm<C, bf16_t, true, false, G_ROWS, EPI_DSWIGLU>(g1, mt_bound * g1.tiles_n, st);
+  if (h16)
+    launch_quant_rows(h16, true, a.A, a.f, static_cast<uint8_t*>(const_cast<void*>(a.act_h)),
+                      const_cast<float*>(a.h_scale), st);
   // dX = Q(dGU) W1
   launch_quant_rows(d_gu, true, a.A, 2 * a.f, gq, gs, st);
   GemmArgs g2{};
@@ -1239,7 +1289,7 @@ static void ffn_bwd_fp8(const FfnBwdLaunch& a, hipStream_t st) {
   g2.C = a.dx_perm; g2.ldc = a.d;
   g2.offsets = a.offsets; g2.G = int(a.E);
   g2.N = int(a.d); g2.K = int(2 * a.f);
-  g2.tiles_n = int(a.d / BN);
+  g2.tiles_n = int(a.d / C::BN);
   run_gemm<C, bf16_t, true, false, G_ROWS, EPI_STORE>(g2, mt_bound * g2.tiles_n, st);
   // weight gradients in bf16 on dequantised X and H
   dequant_rows(reinterpret_cast<const uint8_t*>(a.x_perm), a.x_scale, a.A, a.d, xd, st);
@@ -1252,15 +1302,21 @@ void launch_grouped_ffn(const FfnLaunch& a, hipStream_t st) {
     copy_bytes(a.x_perm, a.out_perm, a.A * a.d * (a.act == 1 ? 2 : 4), st);
     return;
   }
-  if (a.wt == 2) ffn_fwd_fp8(a, st);
-  else if (a.wt == 1) {
-    if (big_rows(a.tile, a.A, a.E, 2 * a.f)) gemm1_fwd<BigCfg>(a, st);
-    else gemm1_fwd<SmallCfg<bf16_t>>(a, st);
-    if (big_rows(a.tile, a.A, a.E, a.d)) gemm2_fwd<BigCfg>(a, st);
-    else gemm2_fwd<SmallCfg<bf16_t>>(a, st);
+  const FfnWs w = ffn_ws(a.A, a.d, a.f, a.act == 1 ? 2 : 4, a.wt == 2, false, a.recompute);
+  // what the backward will not find saved goes to the workspace (H) or is
+  // not stored at all (GU)
+  void* gu = a.recompute == 2 ? nullptr : a.act_gu;
+  void* h = a.recompute ? at(a.ws, w.r_h) : a.act_h;
+  float* hs = a.recompute ? reinterpret_cast<float*>(at(a.ws, w.r_hs)) : a.h_scale;
+  bf16_t* h16 = reinterpret_cast<bf16_t*>(at(a.ws, w.h_bf16));
+  ffn_fwd_gu_h(a, gu, h, hs, h16, st);
+  if (a.wt == 2) {
+    gemm2_fwd_fp8(a, static_cast<const uint8_t*>(h), hs, st);
+  } else if (a.wt == 1) {
+    if (big_rows(a.tile, a.A, a.E, a.d)) gemm2_fwd<BigCfg>(a, h, st);
+    else gemm2_fwd<SmallCfg<bf16_t>>(a, h, st);
   } else {
-    gemm1_fwd<SmallCfg<float>>(a, st);
-    gemm2_fwd<SmallCfg<float>>(a, st);
+    gemm2_fwd<SmallCfg<float>>(a, h, st);
   }
 }
 
@@ -1273,9 +1329,30 @@ void launch_grouped_ffn_bwd(const FfnBwdLaunch& a, hipStream_t st) {
     zero_bytes(a.dw2, a.E * a.d * a.f * ws, st);
     return;
   }
-  if (a.wt == 2) ffn_bwd_fp8(a, st);
-  else if (a.wt == 1) ffn_bwd_t<bf16_t>(a, st);
-  else ffn_bwd_t<float>(a, st);
+  const bool fp8 = a.wt == 2;
+  const FfnWs w = ffn_ws(a.A, a.d, a.f, es, fp8, true, a.recompute);
+  FfnBwdLaunch b = a;
+  void* h_out = nullptr;  // activation recompute: H rebuilt by the dH epilogue
+  if (a.recompute) {
+    b.act_h = at(a.ws, w.r_h);
+    b.h_scale = reinterpret_cast<const float*>(at(a.ws, w.r_hs));
+    bf16_t* h16 = reinterpret_cast<bf16_t*>(at(a.ws, w.h_bf16));
+    if (a.recompute == 2) {
+      // rerun the forward's first GEMM: GU and H exactly as the forward made them
+      FfnLaunch f{};
+      f.x_perm = a.x_perm; f.x_scale = a.x_scale; f.offsets = a.offsets;
+      f.w1 = a.w1; f.w1_scale = a.w1_scale;
+      f.A = a.A; f.d = a.d; f.f = a.f; f.E = a.E; f.act = a.act; f.wt = a.wt; f.tile = a.tile;
+      b.act_gu = at(a.ws, w.r_gu);
+      ffn_fwd_gu_h(f, const_cast<void*>(b.act_gu), const_cast<void*>(b.act_h),
+                   const_cast<float*>(b.h_scale), h16, st);
+    } else {
+      h_out = fp8 ? static_cast<void*>(h16) : const_cast<void*>(b.act_h);
+    }
+  }
+  if (fp8) ffn_bwd_fp8(b, static_cast<bf16_t*>(h_out), st);
+  else if (a.wt == 1) ffn_bwd_t<bf16_t>(b, h_out, st);
+  else ffn_bwd_t<float>(b, h_out, st);
 }
 
 }  // namespace moe

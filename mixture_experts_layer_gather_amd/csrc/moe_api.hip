@@ -41,6 +41,7 @@ int check_cfg(const moe_config* c) {
   if (c->ffn_mode != MOE_FFN_SWIGLU && c->ffn_mode != MOE_FFN_IDENTITY) return MOE_ERR_INVALID_ARG;
   if (c->gemm_tile < MOE_TILE_AUTO || c->gemm_tile > MOE_TILE_BIG) return MOE_ERR_INVALID_ARG;
   if (!(c->aux_coeff >= 0.0f && c->aux_coeff < __builtin_inff())) return MOE_ERR_INVALID_ARG;
+  if (c->recompute < MOE_RECOMPUTE_NONE || c->recompute > MOE_RECOMPUTE_FULL) return MOE_ERR_INVALID_ARG;
   if (c->act_dtype != MOE_DTYPE_F32 && c->act_dtype != MOE_DTYPE_BF16) return MOE_ERR_UNSUPPORTED_DTYPE;
   if (c->weight_dtype == MOE_DTYPE_FP8_E4M3) {
     if (c->act_dtype != MOE_DTYPE_BF16) return MOE_ERR_UNSUPPORTED_DTYPE;
@@ -108,10 +109,10 @@ size_t moe_workspace_size(const moe_config* cfg, int op) {
     case MOE_OP_DISPATCH: return T ? round_up(size_t(dispatch_chunks(T)) * size_t(E) * 4) : 0;
     case MOE_OP_GROUPED_FFN:
       return round_up(moe::ffn_ws_bytes(T * k, cfg->hidden, f, int(act_bytes(cfg->act_dtype)),
-                                        cfg->weight_dtype == MOE_DTYPE_FP8_E4M3, false));
+                                        cfg->weight_dtype == MOE_DTYPE_FP8_E4M3, false, cfg->recompute));
     case MOE_OP_GROUPED_FFN_BWD:
       return round_up(moe::ffn_ws_bytes(T * k, cfg->hidden, f, int(act_bytes(cfg->act_dtype)),
-                                        cfg->weight_dtype == MOE_DTYPE_FP8_E4M3, true));
+                                        cfg->weight_dtype == MOE_DTYPE_FP8_E4M3, true, cfg->recompute));
     case MOE_OP_ROUTE_BWD: {
       const int Z = moe::route_bwd_zsplit(T, cfg->hidden, E);
       const size_t parts = Z > 1 ? size_t(Z) * size_t(E) * size_t(cfg->hidden) * 4 : 0;
@@ -179,10 +180,12 @@ int moe_grouped_ffn(const moe_config* cfg, const void* x_perm, const float* x_sc
   const bool fp8 = cfg->weight_dtype == MOE_DTYPE_FP8_E4M3;
   MOE_CHECK(need(x_perm)); MOE_CHECK(need(offsets)); MOE_CHECK(need(out_perm));
   if (!identity) {
-    MOE_CHECK(need(w1)); MOE_CHECK(need(w2)); MOE_CHECK(need(act_gu)); MOE_CHECK(need(act_h));
+    MOE_CHECK(need(w1)); MOE_CHECK(need(w2));
+    if (cfg->recompute < MOE_RECOMPUTE_FULL) MOE_CHECK(need(act_gu));
+    if (cfg->recompute == MOE_RECOMPUTE_NONE) MOE_CHECK(need(act_h));
     if (fp8) {
       MOE_CHECK(need(x_scale)); MOE_CHECK(need(w1_scale)); MOE_CHECK(need(w2_scale));
-      MOE_CHECK(need(h_scale));
+      if (cfg->recompute == MOE_RECOMPUTE_NONE) MOE_CHECK(need(h_scale));
     }
   }
   MOE_CHECK(align_all(x_perm, x_scale, offsets, w1, w1_scale, w2, w2_scale, act_gu, act_h, h_scale, out_perm, ws));
@@ -199,6 +202,7 @@ int moe_grouped_ffn(const moe_config* cfg, const void* x_perm, const float* x_sc
   a.wt = cfg->weight_dtype == MOE_DTYPE_F32 ? 0 : (cfg->weight_dtype == MOE_DTYPE_BF16 ? 1 : 2);
   a.identity = identity;
   a.tile = cfg->gemm_tile;
+  a.recompute = cfg->recompute;
   moe::launch_grouped_ffn(a, static_cast<hipStream_t>(stream));
   return launched();
 }
@@ -245,11 +249,12 @@ int moe_grouped_ffn_bwd(const moe_config* cfg, const void* x_perm, const float* 
   MOE_CHECK(need(d_out_perm)); MOE_CHECK(need(dx_perm)); MOE_CHECK(need(dw1)); MOE_CHECK(need(dw2));
   MOE_CHECK(need(offsets));
   if (!identity) {
-    MOE_CHECK(need(x_perm)); MOE_CHECK(need(w1)); MOE_CHECK(need(w2)); MOE_CHECK(need(act_gu));
-    MOE_CHECK(need(act_h));
+    MOE_CHECK(need(x_perm)); MOE_CHECK(need(w1)); MOE_CHECK(need(w2));
+    if (cfg->recompute < MOE_RECOMPUTE_FULL) MOE_CHECK(need(act_gu));
+    if (cfg->recompute == MOE_RECOMPUTE_NONE) MOE_CHECK(need(act_h));
     if (fp8) {
       MOE_CHECK(need(x_scale)); MOE_CHECK(need(w1_scale)); MOE_CHECK(need(w2_scale));
-      MOE_CHECK(need(h_scale));
+      if (cfg->recompute == MOE_RECOMPUTE_NONE) MOE_CHECK(need(h_scale));
     }
   }
   MOE_CHECK(align_all(x_perm, x_scale, offsets, w1, w1_scale, w2, w2_scale, act_gu, act_h, h_scale, d_out_perm, dx_perm, dw1, dw2, ws));
@@ -266,6 +271,7 @@ int moe_grouped_ffn_bwd(const moe_config* cfg, const void* x_perm, const float* 
   a.wt = cfg->weight_dtype == MOE_DTYPE_F32 ? 0 : (cfg->weight_dtype == MOE_DTYPE_BF16 ? 1 : 2);
   a.identity = identity;
   a.tile = cfg->gemm_tile;
+  a.recompute = cfg->recompute;
   moe::launch_grouped_ffn_bwd(a, static_cast<hipStream_t>(stream));
   return launched();
 }

@@ -21,8 +21,8 @@ _TORCH = {"f32": torch.float32, "bf16": torch.bfloat16}
 class MoELayer:
     def __init__(self, T, d, E, k, f, shared=0, score="softmax", renorm=True, gate_scale=1.0,
                  num_groups=1, topk_groups=1, group_score="top2_sum", act="bf16", weight="bf16",
-                 quant_block=128, identity=False, gemm_tile="auto", aux_coeff=0.0, device="cuda",
-                 **_ignored):
+                 quant_block=128, identity=False, gemm_tile="auto", aux_coeff=0.0, recompute="none",
+                 device="cuda", **_ignored):
         self.T, self.d, self.E, self.k, self.f = T, d, E, k, f
         self.A = T * k
         self.shared = int(shared)
@@ -32,11 +32,15 @@ class MoELayer:
         kw = dict(score=score, renorm=renorm, gate_scale=gate_scale, num_groups=num_groups,
                   topk_groups=topk_groups, group_score=group_score, act=act, weight=weight,
                   quant_block=quant_block, identity=identity, gemm_tile=gemm_tile,
-                  aux_coeff=aux_coeff)
+                  aux_coeff=aux_coeff, recompute=recompute)
         self.cfg = L.make_config(T, d, E, k, f, **kw)
         self.aux = aux_coeff != 0.0
         self.scfg = L.make_config(T, d, 1, 1, f, act=act, weight=weight, quant_block=quant_block,
-                                  identity=identity, gemm_tile=gemm_tile)
+                                  identity=identity, gemm_tile=gemm_tile, recompute=recompute)
+        # activations the expert FFN keeps from forward to backward: GU and H,
+        # GU only ("act": H is rebuilt from it), or nothing ("full")
+        keep_gu = recompute != "full"
+        keep_h = recompute == "none"
         dev = torch.device(device)
         at = _TORCH[act]
         pt = torch.float32 if weight == "f32" else torch.bfloat16   # parameter dtype
@@ -58,17 +62,19 @@ class MoELayer:
         self.offsets = e(E + 1, dt=i32)
         self.row_id_map = e(T, k, dt=i32)
         self.perm_token = e(A, dt=i32)
+        self.act_h = self.h_scale = None
         if self.fp8:
             self.x_perm = e(A, d, dt=torch.uint8)
             self.x_scale = e(A, d // quant_block, dt=torch.float32)
-            self.act_h = e(A, f, dt=torch.uint8)
-            self.h_scale = e(A, f // quant_block, dt=torch.float32)
+            if keep_h:
+                self.act_h = e(A, f, dt=torch.uint8)
+                self.h_scale = e(A, f // quant_block, dt=torch.float32)
         else:
             self.x_perm = e(A, d)
             self.x_scale = None
-            self.act_h = e(A, f)
-            self.h_scale = None
-        self.act_gu = e(A, 2 * f)
+            if keep_h:
+                self.act_h = e(A, f)
+        self.act_gu = e(A, 2 * f) if keep_gu else None
         self.out_perm = e(A, d)
         self.y = e(T, d)
         # backward
@@ -90,15 +96,16 @@ class MoELayer:
         self.ws_aux = e(max(1, L.workspace_size(self.cfg, L.OP_AUX_LOSS)), dt=u8)
         if self.shared:
             self.s_offsets = torch.tensor([0, T], dtype=i32, device=dev)
+            self.s_h = self.s_h_scale = None
             if self.fp8:
                 self.s_x = e(T, d, dt=torch.uint8)
                 self.s_x_scale = e(T, d // quant_block, dt=torch.float32)
-                self.s_h = e(T, f, dt=torch.uint8)
-                self.s_h_scale = e(T, f // quant_block, dt=torch.float32)
-            else:
+                if keep_h:
+                    self.s_h = e(T, f, dt=torch.uint8)
+                    self.s_h_scale = e(T, f // quant_block, dt=torch.float32)
+            elif keep_h:
                 self.s_h = e(T, f)
-                self.s_h_scale = None
-            self.s_gu = e(T, 2 * f)
+            self.s_gu = e(T, 2 * f) if keep_gu else None
             self.s_out = e(T, d)
             self.s_dx = e(T, d)
             self.s_dw1 = e(1, 2 * f, d, dt=pt)

@@ -137,3 +137,49 @@ def test_status_strings(M):
     assert M.moe_status_string(0) == "ok"
     assert "workspace" in M.moe_status_string(-4)
     assert M.moe_status_string(-99) == "unknown status"
+
+
+def test_recompute_modes(M):
+    """MOE_RECOMPUTE_*: 0, 1, 2 only; which saved activations may be NULL;
+    the workspace grows by what is no longer saved."""
+    L = M.lib()
+    for bad in (-1, 3):
+        c = _cfg(M)
+        c.recompute = bad
+        assert _route(M, c) == -1, bad
+    A, d, f = 1000 * 4, 512, 384
+    sizes = {}
+    for mode, rc in M.RECOMPUTE.items():
+        c = _cfg(M, T=1000, E=16, k=4, f=f, d=d, recompute=mode)
+        sizes[mode] = (L.moe_workspace_size(ctypes.byref(c), 2), L.moe_workspace_size(ctypes.byref(c), 3))
+    # forward: H moves to the workspace; backward: + H, and + GU for "full"
+    assert sizes["none"][0] == 0
+    assert sizes["act"][0] >= A * f * 2 and sizes["full"][0] == sizes["act"][0]
+    assert sizes["act"][1] >= sizes["none"][1] + A * f * 2
+    assert sizes["full"][1] >= sizes["act"][1] + A * 2 * f * 2
+    c8 = _cfg(M, T=1000, E=16, k=4, f=f, d=d, weight="fp8", recompute="act")
+    c8n = _cfg(M, T=1000, E=16, k=4, f=f, d=d, weight="fp8")
+    assert (L.moe_workspace_size(ctypes.byref(c8), 3)
+            >= L.moe_workspace_size(ctypes.byref(c8n), 3) + A * f * 3 + A * (f // 128) * 4)
+
+    def ffn(c, gu, h, hs, ws, n):
+        return L.moe_grouped_ffn(ctypes.byref(c), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, gu, h, hs,
+                                 FAKE, ws, n, None)
+
+    def ffn_bwd(c, gu, h, hs, ws, n):
+        return L.moe_grouped_ffn_bwd(ctypes.byref(c), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, gu, h,
+                                     hs, FAKE, FAKE, FAKE, FAKE, ws, n, None)
+
+    # T = 0 returns after the argument checks: no launch, no device access
+    for mode, need_gu, need_h in (("none", True, True), ("act", True, False), ("full", False, False)):
+        c = _cfg(M, T=0, weight="fp8", recompute=mode)
+        for call in (ffn, ffn_bwd):
+            assert call(c, FAKE, FAKE, FAKE, None, 0) == 0, (mode, call)
+            assert (call(c, None, FAKE, FAKE, None, 0) == -1) == need_gu, (mode, call)
+            assert (call(c, FAKE, None, FAKE, None, 0) == -1) == need_h, (mode, call)
+            assert (call(c, FAKE, FAKE, None, None, 0) == -1) == need_h, (mode, call)
+        # with tokens, a recompute workspace is required
+        c1 = _cfg(M, T=64, recompute=mode)
+        if mode != "none":
+            assert ffn(c1, FAKE, None, None, None, 0) == -4
+            assert ffn_bwd(c1, FAKE, None, None, None, 0) == -4
