@@ -55,7 +55,7 @@ class LayerConfig:
     topk_groups: int = 1
     group_score: str = "top2_sum"  # "top2_sum" | "max"
     act: str = "bf16"      # "f32" | "bf16": dtype of x, y, activations
-    weight: str = "bf16"   # "f32" | "bf16" | "fp8"
+    weight: str = "bf16"   # "f32" | "bf16" | "fp8" | "mxfp8"
     std: float = 0.02      # std of router and expert weights
     bias: str = "none"     # "none" | "zipf": per-expert router logit bias
     quant_block: int = 128
@@ -88,7 +88,15 @@ CONFIGS = [
                 shared=1, score="sigmoid", renorm=True, gate_scale=2.5,
                 num_groups=8, topk_groups=4, weight="fp8", std=0.006),
 ]
-BY_NAME = {c.name: c for c in CONFIGS}
+# The MXFP8 variant of the FP8 workload: 1 x 32 blocks with power-of-two
+# (E8M0) scales instead of 1 x 128 / 128 x 128 blocks with fp32 scales
+# (Hybrid-EP article, results in MXFP8).
+EXTRA_CONFIGS = [
+    LayerConfig("deepseek_v3_mxfp8", 6, T=8192, d=7168, E=256, k=8, f=2048,
+                shared=1, score="sigmoid", renorm=True, gate_scale=2.5,
+                num_groups=8, topk_groups=4, weight="mxfp8", quant_block=32, std=0.006),
+]
+BY_NAME = {c.name: c for c in CONFIGS + EXTRA_CONFIGS}
 
 
 def mini(cfg: LayerConfig, T: int, d: int, f: int, E: Optional[int] = None,

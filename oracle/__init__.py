@@ -9,8 +9,9 @@ Everything floating-point is computed in float64 on the values as stored
 (bf16/fp32 inputs widened exactly), except the two pieces that must be
 reproduced bit for bit and are therefore specified in fp32 and implemented
 in plain C (``spec.c``): the router logits and the selection that reads them
-(including the sigmoid group score and its exponential ``exp_spec``), and the
-FP8 E4M3 block quantiser.
+(including the sigmoid group score and its exponential ``exp_spec``), the
+FP8 E4M3 block quantiser with fp32 scales, and the MXFP8 quantiser (E4M3
+codes in blocks of 32 with power-of-two E8M0 scales).
 
 Sources. The pages name the stages and their meaning, not their formulas:
   * router -> a few experts per token, the rest idle
@@ -83,6 +84,9 @@ def lib():
         L.orc_e4m3_encode_array.argtypes = [P, P, i64]
         L.orc_e4m3_decode_array.argtypes = [P, P, i64]
         L.orc_quant_blocks.argtypes = [i64, i64, P, i64, i64, P, P]
+        L.orc_mx_scale_exp.restype = ctypes.c_int
+        L.orc_mx_scale_exp.argtypes = [ctypes.c_float]
+        L.orc_quant_mx_rows.argtypes = [i64, i64, P, P, P]
         _lib = L
     return _lib
 
@@ -276,6 +280,52 @@ def fp8_roundtrip_rows(a, block: int = 128) -> np.ndarray:
     return dequant_blocks(q, s, 1, block)
 
 
+# ------------------------------------------------------------ MXFP8
+
+MX_BLOCK = 32
+
+
+def quant_mx_rows(src):
+    """MXFP8 quantisation of the rows of src [R,C] (C a multiple of 32) in
+    1 x 32 blocks: returns (q uint8 [R,C] E4M3 codes, e8m0 uint8 [R,C/32]).
+    The rule (OCP MX v1.0) is in spec.c: orc_quant_mx_rows."""
+    s = as_f32(src)
+    R, C = s.shape
+    if C % MX_BLOCK:
+        raise ValueError("MXFP8 rows need a multiple of 32 columns")
+    q = np.empty((R, C), dtype=np.uint8)
+    e = np.empty((R, C // MX_BLOCK), dtype=np.uint8)
+    lib().orc_quant_mx_rows(R, C, _ptr(s), _ptr(q), _ptr(e))
+    return q, e
+
+
+def quant_mx_cols(src):
+    """MXFP8 in 32 x 1 blocks (32 consecutive rows of one column), for an
+    operand contracted over its rows: (q uint8 [R,C], e8m0 uint8 [R/32, C])."""
+    qt, et = quant_mx_rows(np.ascontiguousarray(as_f32(src).T))
+    return np.ascontiguousarray(qt.T), np.ascontiguousarray(et.T)
+
+
+def mx_scale(e8m0) -> np.ndarray:
+    """E8M0 byte -> 2^(byte - 127) in fp64 (255, NaN, is never produced)."""
+    return np.ldexp(1.0, np.asarray(e8m0, dtype=np.int64) - 127)
+
+
+def dequant_mx_rows(q, e8m0) -> np.ndarray:
+    v = e4m3_decode(q).astype(np.float64)
+    return v * np.repeat(mx_scale(e8m0), MX_BLOCK, axis=1)
+
+
+def dequant_mx_cols(q, e8m0) -> np.ndarray:
+    v = e4m3_decode(q).astype(np.float64)
+    return v * np.repeat(mx_scale(e8m0), MX_BLOCK, axis=0)
+
+
+def mx_roundtrip_rows(a) -> np.ndarray:
+    """Quantise rows in 1 x 32 MX blocks (from fp32) and dequantise (fp64)."""
+    return dequant_mx_rows(*quant_mx_rows(np.asarray(a, dtype=np.float32)))
+
+
 # ------------------------------------------------------------ expert FFN
 
 def silu(z):
@@ -288,11 +338,13 @@ def sigmoid64(z):
         return 1.0 / (1.0 + np.exp(-z))
 
 
-def ffn_fwd(X, W1, W2, identity: bool = False, h_fp8: bool = False):
+def ffn_fwd(X, W1, W2, identity: bool = False, h_fp8: bool = False, h_quant=None):
     """SwiGLU expert on rows X [M,d] (fp64): W1 [2f,d] = [gate rows; up rows],
     W2 [d,f].  G = X W1[:f]^T, U = X W1[f:]^T, H = silu(G) * U, O = H W2^T.
     With h_fp8, H is quantised per 1x128 block along f (from its fp32
-    rounding) before the second product, and the dequantised H is returned.
+    rounding) before the second product, and the dequantised H is returned;
+    h_quant, when given, is the quantise-dequantise function used instead
+    (MXFP8: 1 x 32 blocks).
     identity: O = X (a test mode of route/dispatch/combine)."""
     X = np.asarray(X, dtype=np.float64)
     if identity:
@@ -302,13 +354,16 @@ def ffn_fwd(X, W1, W2, identity: bool = False, h_fp8: bool = False):
     f = W2.shape[1]
     GU = X @ W1.T
     H = silu(GU[:, :f]) * GU[:, f:]
-    if h_fp8:
-        H = fp8_roundtrip_rows(H.astype(np.float32))
+    if h_fp8 and h_quant is None:
+        h_quant = fp8_roundtrip_rows
+    if h_quant is not None:
+        H = h_quant(H.astype(np.float32))
     O = H @ W2.T
     return GU, H, O
 
 
-def ffn_bwd(X, W1, W2, GU, H, dO, identity: bool = False, dgrad_fp8: bool = False):
+def ffn_bwd(X, W1, W2, GU, H, dO, identity: bool = False, dgrad_fp8: bool = False,
+            dgrad_quant=None, W1d=None, W2d=None):
     """Backward of ffn_fwd for one expert's rows (fp64).
       dH  = dO W2                    dW2 = dO^T H
       dG  = dH * U * s(G) * (1 + G (1 - s(G)))   (silu'(G) = s + G s (1 - s))
@@ -318,7 +373,10 @@ def ffn_bwd(X, W1, W2, GU, H, dO, identity: bool = False, dgrad_fp8: bool = Fals
     gradient operand quantised per 1x128 block along its contraction dim
     (dO along d, [dG dU] along 2f, each from its fp32 rounding); W1, W2, X
     and H are the dequantised forward values; the weight gradients use the
-    unquantised gradients.
+    unquantised gradients. dgrad_quant, when given, replaces the 1x128
+    quantise-dequantise of the gradient operands (MXFP8: 1 x 32 blocks), and
+    W1d / W2d replace W1 / W2 in the two data-gradient products (MXFP8
+    weights quantised in 32 x 1 blocks along those products' contraction).
     Returns dX, dW1, dW2, dGU."""
     dO = np.asarray(dO, dtype=np.float64)
     if identity:
@@ -328,15 +386,19 @@ def ffn_bwd(X, W1, W2, GU, H, dO, identity: bool = False, dgrad_fp8: bool = Fals
     W2 = np.asarray(W2, dtype=np.float64)
     f = W2.shape[1]
     G, U = GU[:, :f], GU[:, f:]
-    dOq = fp8_roundtrip_rows(dO.astype(np.float32)) if dgrad_fp8 else dO
-    dH = dOq @ W2
+    if dgrad_fp8 and dgrad_quant is None:
+        dgrad_quant = fp8_roundtrip_rows
+    W1d = W1 if W1d is None else np.asarray(W1d, dtype=np.float64)
+    W2d = W2 if W2d is None else np.asarray(W2d, dtype=np.float64)
+    dOq = dgrad_quant(dO.astype(np.float32)) if dgrad_quant else dO
+    dH = dOq @ W2d
     dW2 = dO.T @ H
     s = sigmoid64(G)
     dG = dH * U * s * (1.0 + G * (1.0 - s))
     dU = dH * G * s
     dGU = np.concatenate([dG, dU], axis=1)
-    dGUq = fp8_roundtrip_rows(dGU.astype(np.float32)) if dgrad_fp8 else dGU
-    dX = dGUq @ W1
+    dGUq = dgrad_quant(dGU.astype(np.float32)) if dgrad_quant else dGU
+    dX = dGUq @ W1d
     dW1 = dGU.T @ X
     return dX, dW1, dW2, dGU
 
@@ -472,18 +534,31 @@ def layer(cfg, inp: dict, identity: bool = False) -> dict:
     inp: x [T,d], wr [E,d], bias [E] or None, w1 [E,2f,d], w2 [E,d,f],
     sw1/sw2 (shared expert, when cfg.shared), dy [T,d]; torch or numpy.
     For fp8 weights the oracle quantises the bf16 masters itself in
-    128 x 128 blocks and the dispatched rows per 1 x 128 block.
+    128 x 128 blocks and the dispatched rows per 1 x 128 block. For mxfp8
+    every operand of the six expert products is quantised in blocks of 32
+    along that product's contraction dimension with E8M0 scales: x, H, dO
+    and [dG dU] in 1 x 32 row blocks; W1 and W2 in row blocks for the
+    forward and in 32 x 1 column blocks for the data gradients; the weight
+    gradients take the dequantised x and H and the unquantised gradients.
     """
     E, k, f = cfg.E, cfg.k, cfg.f
+    mx = cfg.weight == "mxfp8"
     fp8 = cfg.weight == "fp8"
     qb = cfg.quant_block
+    h_quant = mx_roundtrip_rows if mx else (fp8_roundtrip_rows if fp8 else None)
     out = {}
     L, idx, g = route(cfg, inp["x"], inp["wr"], inp.get("bias"))
     out.update(logits=L, idx=idx, gates=g)
     counts, offsets, rmap, ptok = dispatch_index(idx, E)
     out.update(counts=counts, offsets=offsets, row_id_map=rmap, perm_token=ptok)
     x32 = as_f32(inp["x"])
-    if fp8:
+    if mx:
+        xq, xs = quant_mx_rows(x32)
+        out.update(xq=xq, x_scale=xs)
+        Xdq = dequant_mx_rows(xq, xs)
+        Xp = permute(Xdq, rmap)
+        out.update(xq_perm=permute(xq, rmap), x_scale_perm=permute(xs, rmap))
+    elif fp8:
         xq, xs = quant_blocks(x32, 1, qb)
         out.update(xq=xq, x_scale=xs)
         Xp = permute(dequant_blocks(xq, xs, 1, qb), rmap)
@@ -495,6 +570,12 @@ def layer(cfg, inp: dict, identity: bool = False) -> dict:
     def expert_weights(w1, w2):
         w1 = as_f32(w1)
         w2 = as_f32(w2)
+        if mx:
+            r1, r2 = quant_mx_rows(w1), quant_mx_rows(w2)
+            c1, c2 = quant_mx_cols(w1), quant_mx_cols(w2)
+            return (dequant_mx_rows(*r1), dequant_mx_rows(*r2),
+                    dict(w1_rows=r1, w2_rows=r2, w1_cols=c1, w2_cols=c2,
+                         W1d=dequant_mx_cols(*c1), W2d=dequant_mx_cols(*c2)))
         if not fp8:
             return w1.astype(np.float64), w2.astype(np.float64), None
         q1, s1 = quant_blocks(w1, qb, qb)
@@ -513,19 +594,19 @@ def layer(cfg, inp: dict, identity: bool = False) -> dict:
         W.append((W1, W2, q))
         r0, r1 = offsets[e], offsets[e + 1]
         if r1 > r0:
-            gu, h, o = ffn_fwd(Xp[r0:r1], W1, W2, identity, h_fp8=fp8)
+            gu, h, o = ffn_fwd(Xp[r0:r1], W1, W2, identity, h_quant=h_quant)
             O[r0:r1] = o
             if not identity:
                 GU[r0:r1] = gu
                 H[r0:r1] = h
     out.update(out_perm=O, act_gu=GU, act_h=H)
-    if fp8:
+    if fp8 or mx:
         out["w_q"] = [w[2] for w in W]
     O_sh = None
     if cfg.shared:
         SW1, SW2, sq = expert_weights(inp["sw1"], inp["sw2"])
-        Xs = dequant_blocks(xq, xs, 1, qb) if fp8 else x32.astype(np.float64)
-        sgu, sh, O_sh = ffn_fwd(Xs, SW1, SW2, identity, h_fp8=fp8)
+        Xs = Xdq if mx else (dequant_blocks(xq, xs, 1, qb) if fp8 else x32.astype(np.float64))
+        sgu, sh, O_sh = ffn_fwd(Xs, SW1, SW2, identity, h_quant=h_quant)
         out.update(shared_out=O_sh, shared_gu=sgu, shared_h=sh)
     y = combine(O, rmap, g, O_sh)
     out["y"] = y
@@ -540,9 +621,11 @@ def layer(cfg, inp: dict, identity: bool = False) -> dict:
     for e in range(E):
         r0, r1 = offsets[e], offsets[e + 1]
         if r1 > r0:
-            W1, W2, _ = W[e]
+            W1, W2, wq = W[e]
             dx_e, dw1, dw2, _ = ffn_bwd(Xp[r0:r1], W1, W2, GU[r0:r1], H[r0:r1],
-                                        dO[r0:r1], identity, dgrad_fp8=fp8)
+                                        dO[r0:r1], identity, dgrad_quant=h_quant,
+                                        W1d=wq["W1d"] if mx else None,
+                                        W2d=wq["W2d"] if mx else None)
             dXp[r0:r1] = dx_e
             if not identity:
                 dW1[e] = dw1
@@ -550,7 +633,9 @@ def layer(cfg, inp: dict, identity: bool = False) -> dict:
     out.update(dx_perm=dXp, dw1=dW1, dw2=dW2)
     dx_sh = None
     if cfg.shared:
-        dx_sh, sdw1, sdw2, _ = ffn_bwd(Xs, SW1, SW2, sgu, sh, dy, identity, dgrad_fp8=fp8)
+        dx_sh, sdw1, sdw2, _ = ffn_bwd(Xs, SW1, SW2, sgu, sh, dy, identity, dgrad_quant=h_quant,
+                                       W1d=sq["W1d"] if mx else None,
+                                       W2d=sq["W2d"] if mx else None)
         out.update(shared_dx=dx_sh, shared_dw1=sdw1, shared_dw2=sdw2)
     dx = dispatch_bwd(dXp, rmap, dx_sh)
     dL = route_bwd_logits(dgate, idx, L, cfg.score, cfg.renorm, cfg.gate_scale)

@@ -313,3 +313,44 @@ void orc_quant_blocks(int64_t R, int64_t C, const float *src, int64_t br,
         }
     }
 }
+
+/* MXFP8 (OCP Microscaling Formats v1.0, the MXFP8 E4M3 format the Hybrid-EP
+ * article's results use): one power-of-two scale X = 2^x per block of 32
+ * consecutive elements of a row, stored as an E8M0 byte x + 127. The MX
+ * definition fixes the format, not how x is chosen. Here x is the smallest
+ * integer with amax * 2^-x <= 448 (the largest E4M3 magnitude), so that no
+ * element saturates; x = 0 when amax = 0, and x >= -127 (E8M0's range).
+ * With amax = m * 2^e, m in [0.5, 1): amax * 2^-x = m * 2^(e-x), which is
+ * <= 448 = 0.875 * 2^9 exactly when e - x <= 9 (m <= 0.875) or e - x <= 8
+ * (m > 0.875). Elements are v * 2^-x (a power-of-two rescaling) encoded to
+ * E4M3 with round-to-nearest-even (orc_e4m3_encode). */
+int orc_mx_scale_exp(float amax)
+{
+    if (amax == 0.0f) return 0;
+    int e;
+    float m = frexpf(amax, &e);
+    int x = (m > 0.875f) ? e - 8 : e - 9;
+    if (x < -127) x = -127;
+    if (x > 127) x = 127;
+    return x;
+}
+
+/* src [R,C] fp32, C a multiple of 32: q [R,C] E4M3 codes, e8m0 [R, C/32]. */
+void orc_quant_mx_rows(int64_t R, int64_t C, const float *src, uint8_t *q, uint8_t *e8m0)
+{
+    int64_t nb = C / 32;
+#pragma omp parallel for collapse(2) schedule(static)
+    for (int64_t r = 0; r < R; ++r) {
+        for (int64_t b = 0; b < nb; ++b) {
+            const float *v = src + r * C + b * 32;
+            float amax = 0.0f;
+            for (int i = 0; i < 32; ++i) {
+                float a = fabsf(v[i]);
+                if (a > amax) amax = a;
+            }
+            int x = orc_mx_scale_exp(amax);
+            e8m0[r * nb + b] = (uint8_t)(x + 127);
+            for (int i = 0; i < 32; ++i) q[r * C + b * 32 + i] = orc_e4m3_encode(ldexpf(v[i], -x));
+        }
+    }
+}

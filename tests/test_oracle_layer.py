@@ -253,3 +253,66 @@ def test_aux_loss_gradient_matches_autograd_and_differences():
         assert d_aux * fd == pytest.approx(g[t, e], rel=1e-5, abs=1e-11)
     # softmax is shift invariant: every row of the gradient sums to zero
     assert np.allclose(g.sum(axis=1), 0.0, atol=1e-15)
+
+
+def _mx_mini():
+    return S.mini(S.BY_NAME["deepseek_v3_mxfp8"], T=16, d=256, f=256, E=16).replace(
+        num_groups=4, topk_groups=2, k=4)
+
+
+def test_mxfp8_layer_plumbing_reduces_to_unquantised(monkeypatch):
+    """With every MX quantise-dequantise replaced by the identity, the mxfp8
+    layer must equal the unquantised one up to the fp32 rounding that H, dO
+    and [dG dU] take before quantisation (relative 1e-7): each product then
+    takes the operands it would take without quantisation (no transposed or
+    swapped weights, no gradient quantised where it should not be), which
+    any plumbing mistake would break at order 1."""
+    cfg = _mx_mini()
+    inp = _inputs(cfg)
+    ref = oracle.layer(cfg.replace(weight="bf16", quant_block=128), inp)
+    ident = lambda a: (np.asarray(a, dtype=np.float32), None)
+    monkeypatch.setattr(oracle, "quant_mx_rows", ident)
+    monkeypatch.setattr(oracle, "quant_mx_cols", ident)
+    monkeypatch.setattr(oracle, "dequant_mx_rows", lambda q, e: q.astype(np.float64))
+    monkeypatch.setattr(oracle, "dequant_mx_cols", lambda q, e: q.astype(np.float64))
+    monkeypatch.setattr(oracle, "mx_roundtrip_rows", lambda a: np.asarray(a, np.float32).astype(np.float64))
+    out = oracle.layer(cfg, inp)
+    for n in ("y", "dx", "dw1", "dw2", "dw_router", "d_gate", "shared_dw1", "shared_dw2"):
+        assert oracle.rel_l2(out[n], ref[n]) < 1e-6, n
+
+
+def test_mxfp8_layer_close_to_unquantised():
+    cfg = _mx_mini()
+    inp = _inputs(cfg)
+    out = oracle.layer(cfg, inp)
+    ref = oracle.layer(cfg.replace(weight="bf16", quant_block=128), inp)
+    assert np.array_equal(out["idx"], ref["idx"])
+    for n in ("y", "dx", "dw1", "dw2", "shared_dw1", "shared_dw2"):
+        assert oracle.rel_l2(out[n], ref[n]) < 0.1, n
+    wq = out["w_q"][3]
+    f, d = cfg.f, cfg.d
+    assert wq["w1_rows"][1].shape == (2 * f, d // 32) and wq["w2_rows"][1].shape == (d, f // 32)
+    assert wq["w1_cols"][1].shape == (2 * f // 32, d) and wq["w2_cols"][1].shape == (d // 32, f)
+    assert out["x_scale"].dtype == np.uint8 and out["x_scale"].shape == (cfg.T, d // 32)
+
+
+def test_mxfp8_column_blocks_feed_only_the_data_gradients(monkeypatch):
+    """Marking the column-quantised weights (dequantised x2, exact) must
+    double dH and so dW1, quadruple dX through both data-gradient products,
+    and leave y and dW2 unchanged: the 32 x 1 weight blocks serve exactly
+    the two data-gradient products."""
+    cfg = _mx_mini()
+    inp = _inputs(cfg)
+    ident = lambda a: (np.asarray(a, dtype=np.float32), None)
+    monkeypatch.setattr(oracle, "quant_mx_rows", ident)
+    monkeypatch.setattr(oracle, "quant_mx_cols", ident)
+    monkeypatch.setattr(oracle, "dequant_mx_rows", lambda q, e: q.astype(np.float64))
+    monkeypatch.setattr(oracle, "mx_roundtrip_rows", lambda a: np.asarray(a, np.float32).astype(np.float64))
+    monkeypatch.setattr(oracle, "dequant_mx_cols", lambda q, e: q.astype(np.float64))
+    base = oracle.layer(cfg, inp)
+    monkeypatch.setattr(oracle, "dequant_mx_cols", lambda q, e: 2.0 * q.astype(np.float64))
+    out = oracle.layer(cfg, inp)
+    assert np.array_equal(out["y"], base["y"]) and np.array_equal(out["dw2"], base["dw2"])
+    assert oracle.rel_l2(out["dw1"], 2 * base["dw1"]) < 1e-6
+    assert oracle.rel_l2(out["dx_perm"], 4 * base["dx_perm"]) < 1e-6
+    assert oracle.rel_l2(out["shared_dx"], 4 * base["shared_dx"]) < 1e-6

@@ -268,3 +268,102 @@ def test_quant_blocks_properties():
         deq = oracle.dequant_blocks(q, s, br, bc)
         err = np.abs(deq - src.astype(np.float64))
         assert np.all(err <= np.maximum(np.abs(src) * 2.0 ** -4, S * 2.0 ** -10) * (1 + 1e-7))
+
+
+# ---------------------------------------------------------------- MXFP8
+
+def _e4m3_values_by_definition():
+    """All 256 E4M3FN code values from the format's definition (1 sign, 4
+    exponent bits with bias 7, 3 mantissa bits; exponent 0 is subnormal; only
+    S.1111.111 is NaN): an enumeration independent of the oracle's tables."""
+    vals = np.empty(256)
+    for c in range(256):
+        s, e, m = c >> 7, (c >> 3) & 15, c & 7
+        if e == 15 and m == 7:
+            vals[c] = np.nan
+        elif e == 0:
+            vals[c] = (-1) ** s * m / 8 * 2.0 ** -6
+        else:
+            vals[c] = (-1) ** s * (1 + m / 8) * 2.0 ** (e - 7)
+    return vals
+
+
+def _mx_exp_brute(amax):
+    """Smallest integer x in [-127, 127] with amax * 2^-x <= 448, by search."""
+    if amax == 0:
+        return 0
+    for x in range(-127, 128):
+        if float(amax) * 2.0 ** -x <= 448.0:
+            return x
+    raise AssertionError
+
+
+def test_mx_scale_exponent_bruteforce():
+    rng = np.random.default_rng(21)
+    cases = [0.0, 448.0, 449.0, 447.99997, 1.0, 0.875, 0.875 * 2 ** 9, 0.87500006 * 2 ** 9, 1.75, 3.5,
+             2.0 ** -126, 2.0 ** -140, 1e-45, 3.0e38, 2.0 ** 120 * 1.7]
+    cases += list((np.exp(rng.uniform(-90, 88, 3000))).astype(F32))
+    cases += list(F32(448) * F32(2.0) ** rng.integers(-130, 120, 500).astype(F32))  # power-of-two multiples
+    for a in cases:
+        a = F32(a)
+        assert oracle.lib().orc_mx_scale_exp(a) == _mx_exp_brute(a), a
+
+
+def test_mx_rows_nearest_code_bruteforce():
+    """Every code is the E4M3 value nearest to v * 2^-x (ties to an even
+    mantissa), found by scanning all 256 codes; the E8M0 byte is x + 127."""
+    vals = _e4m3_values_by_definition()
+    finite = ~np.isnan(vals)
+    rng = np.random.default_rng(22)
+    R, C = 24, 128
+    src = (rng.standard_normal((R, C)) * np.exp(rng.uniform(-30, 30, (R, 1)))).astype(F32)
+    src[3, 32:64] = 0.0                      # an all-zero block
+    src[4, :32] = 0.0
+    src[4, 7] = -3.0e-41                     # a lone fp32 subnormal
+    src[5, 64:96] = 1e-3
+    src[5, 70] = 1e3                         # one large element among small ones
+    src[6, :32] = np.linspace(-448, 448, 32)  # exact E4M3 range
+    q, e = oracle.quant_mx_rows(src)
+    assert q.shape == (R, C) and e.shape == (R, C // 32)
+    for r in range(R):
+        for b in range(C // 32):
+            blk = src[r, 32 * b:32 * b + 32]
+            x = _mx_exp_brute(np.max(np.abs(blk)))
+            assert e[r, b] == x + 127
+            for i, v in enumerate(blk):
+                t = float(v) * 2.0 ** -x
+                assert abs(t) <= 448.0
+                dist = np.where(finite, np.abs(vals - t), np.inf)
+                best = np.nonzero(dist == dist.min())[0]
+                code = q[r, 32 * b + i]
+                if t == 0.0:
+                    assert vals[code] == 0.0 and (code >> 7) == (np.signbit(v))
+                    continue
+                best = [c for c in best if (c >> 7) == (t < 0) or vals[c] == 0]
+                if len(best) > 1:  # a tie: the even mantissa
+                    best = [c for c in best if c & 1 == 0]
+                assert code in best, (r, b, i, v, t, code, best)
+
+
+def test_mx_properties_and_roundtrip():
+    rng = np.random.default_rng(23)
+    src = (rng.standard_normal((64, 256)) * np.exp(rng.standard_normal((64, 1)) * 4)).astype(F32)
+    q, e = oracle.quant_mx_rows(src)
+    deq = oracle.dequant_mx_rows(q, e)
+    X = np.repeat(oracle.mx_scale(e), 32, axis=1)
+    # every block's largest element lands in [224, 448] after scaling: one
+    # more halving of the scale would push it past 448
+    amax_code = np.abs(oracle.e4m3_decode(q)).reshape(64, 8, 32).max(axis=2)
+    assert np.all((amax_code >= 224) & (amax_code <= 448))
+    # error of round-to-nearest: half a step, relative 2^-4 in the normal
+    # range, absolute 2^-10 X in the subnormal one
+    err = np.abs(deq - src.astype(np.float64))
+    assert np.all(err <= np.maximum(np.abs(src) * 2.0 ** -4, X * 2.0 ** -10) * (1 + 1e-12))
+    # exact values survive: small integers times a power of two
+    ex = (rng.integers(-15, 16, (8, 64)) * 2.0 ** rng.integers(-20, 20, (8, 1))).astype(F32)
+    assert np.array_equal(oracle.mx_roundtrip_rows(ex), ex.astype(np.float64))
+    # column blocks are the row blocks of the transpose
+    qc, ec = oracle.quant_mx_cols(src[:, :64].T.copy())
+    assert np.array_equal(qc, q[:, :64].T) and np.array_equal(ec, e[:, :2].T)
+    with pytest.raises(ValueError):
+        oracle.quant_mx_rows(np.zeros((2, 48), F32))
