@@ -188,9 +188,10 @@ def stage_work(c):
     R = A + S * T
     bx = 4 if c.act == "f32" else 2
     bo = ba = bx
-    bw = {"f32": 4, "bf16": 2, "fp8": 1}[c.weight]
+    bw = {"f32": 4, "bf16": 2, "fp8": 1, "mxfp8": 1}[c.weight]
     bg = 4 if c.weight == "f32" else 2
-    bp = (d + 4 * d // 128) if c.weight == "fp8" else d * bx
+    # dispatched row: codes + scales (fp32 per 128, or one E8M0 byte per 32)
+    bp = {"fp8": d + 4 * d // 128, "mxfp8": d + d // 32}.get(c.weight, d * bx)
     w = {}
     w["route"] = (T * d * bx + 4 * E * d + 4 * T * E + 8 * T * k + T * E, 2 * T * d * E)
     w["dispatch"] = (T * d * bx + A * bp + 16 * A, 0)
@@ -253,8 +254,7 @@ def timed_step(layer, x, dy, marks):
     if layer.shared:
         sx, sxs = x, None
         if layer.fp8:
-            L.moe_quantize_fp8_blockwise(x, layer.T, layer.d, 1, layer.qb, layer.s_x,
-                                         layer.s_x_scale)
+            layer.quantize_shared_input(x)
             sx, sxs = layer.s_x, layer.s_x_scale
         L.moe_grouped_ffn(layer.scfg, sx, sxs, layer.s_offsets, layer.sw1, layer.sw1_scale,
                           layer.sw2, layer.sw2_scale, layer.s_gu, layer.s_h, layer.s_h_scale,
@@ -266,16 +266,16 @@ def timed_step(layer, x, dy, marks):
     L.moe_combine_bwd(c, dy, layer.out_perm, layer.row_id_map, layer.topk_gate, layer.d_out_perm,
                       layer.d_gate)
     rec("combine_bwd")
-    L.moe_grouped_ffn_bwd(c, layer.x_perm, layer.x_scale, layer.offsets, layer.w1,
-                          layer.w1_scale, layer.w2, layer.w2_scale, layer.act_gu, layer.act_h,
+    L.moe_grouped_ffn_bwd(c, layer.x_perm, layer.x_scale, layer.offsets, layer.w1b,
+                          layer.w1b_scale, layer.w2b, layer.w2b_scale, layer.act_gu, layer.act_h,
                           layer.h_scale, layer.d_out_perm, layer.dx_perm, layer.dw1, layer.dw2,
                           layer.ws_ffn_bwd)
     rec("grouped_ffn_bwd")
     dx_add = None
     if layer.shared:
         sx, sxs = (layer.s_x, layer.s_x_scale) if layer.fp8 else (x, None)
-        L.moe_grouped_ffn_bwd(layer.scfg, sx, sxs, layer.s_offsets, layer.sw1, layer.sw1_scale,
-                              layer.sw2, layer.sw2_scale, layer.s_gu, layer.s_h, layer.s_h_scale,
+        L.moe_grouped_ffn_bwd(layer.scfg, sx, sxs, layer.s_offsets, layer.sw1b, layer.sw1b_scale,
+                              layer.sw2b, layer.sw2b_scale, layer.s_gu, layer.s_h, layer.s_h_scale,
                               dy, layer.s_dx, layer.s_dw1, layer.s_dw2, layer.ws_ffn_bwd)
         dx_add = layer.s_dx
         rec("shared_ffn_bwd")
@@ -480,7 +480,7 @@ def main():
             per.setdefault(name, []).append(a.elapsed_time(b))
     per_ms = {n: sum(v) / len(v) for n, v in per.items()}
     work = stage_work(cfg)
-    dt = "fp8" if cfg.weight == "fp8" else cfg.act
+    dt = "fp8" if cfg.weight in ("fp8", "mxfp8") else cfg.act
     stages = {}
     for n, t in per_ms.items():
         b, fl = work[n]

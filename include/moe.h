@@ -59,7 +59,7 @@ enum {
     MOE_ERR_HIP = -5                /* a launch failed (hipGetLastError) */
 };
 
-enum { MOE_DTYPE_F32 = 0, MOE_DTYPE_BF16 = 1, MOE_DTYPE_FP8_E4M3 = 2 };
+enum { MOE_DTYPE_F32 = 0, MOE_DTYPE_BF16 = 1, MOE_DTYPE_FP8_E4M3 = 2, MOE_DTYPE_MXFP8 = 3 };
 enum { MOE_SCORE_SOFTMAX = 0, MOE_SCORE_SIGMOID = 1 };
 enum { MOE_GROUP_TOP2_SUM = 0, MOE_GROUP_MAX = 1 };
 enum { MOE_FFN_SWIGLU = 0, MOE_FFN_IDENTITY = 1 };
@@ -117,8 +117,8 @@ typedef struct moe_config {
     int32_t topk_groups;
     int32_t group_score;
     int32_t act_dtype;    /* MOE_DTYPE_F32 or MOE_DTYPE_BF16 */
-    int32_t weight_dtype; /* act_dtype, or MOE_DTYPE_FP8_E4M3 with bf16 act */
-    int32_t quant_block;  /* 128 */
+    int32_t weight_dtype; /* act_dtype, or MOE_DTYPE_FP8_E4M3 / MOE_DTYPE_MXFP8 with bf16 act */
+    int32_t quant_block;  /* 128 (FP8_E4M3) or 32 (MXFP8) */
     int32_t ffn_mode;
     int32_t gemm_tile;   /* MOE_TILE_*, 0 by default */
     float aux_coeff;     /* finite, >= 0 */
@@ -168,7 +168,7 @@ int moe_route(const moe_config *cfg, const void *x, const float *w_router,
  * Workspace: moe_workspace_size(cfg, MOE_OP_DISPATCH). */
 int moe_dispatch(const moe_config *cfg, const void *x, const int32_t *topk_idx,
                  int32_t *counts, int32_t *offsets, int32_t *row_id_map,
-                 int32_t *perm_token, void *x_perm, float *x_scale, void *ws,
+                 int32_t *perm_token, void *x_perm, void *x_scale, void *ws,
                  size_t ws_bytes, void *stream);
 
 /* Grouped SwiGLU expert FFN forward over expert-contiguous rows (Megatron
@@ -194,10 +194,10 @@ int moe_dispatch(const moe_config *cfg, const void *x, const int32_t *topk_idx,
  * over the (quantised) unpermuted x and offsets {0, T}.
  * Workspace: moe_workspace_size(cfg, MOE_OP_GROUPED_FFN). */
 int moe_grouped_ffn(const moe_config *cfg, const void *x_perm,
-                    const float *x_scale, const int32_t *offsets,
-                    const void *w1, const float *w1_scale, const void *w2,
-                    const float *w2_scale, void *act_gu, void *act_h,
-                    float *h_scale, void *out_perm, void *ws, size_t ws_bytes,
+                    const void *x_scale, const int32_t *offsets,
+                    const void *w1, const void *w1_scale, const void *w2,
+                    const void *w2_scale, void *act_gu, void *act_h,
+                    void *h_scale, void *out_perm, void *ws, size_t ws_bytes,
                     void *stream);
 
 /* Combine forward (Hybrid-EP article, combine operator with high-precision
@@ -239,10 +239,10 @@ int moe_combine_bwd(const moe_config *cfg, const void *dy, const void *out_perm,
  * The results are bitwise those of MOE_RECOMPUTE_NONE.
  * Workspace: moe_workspace_size(cfg, MOE_OP_GROUPED_FFN_BWD). */
 int moe_grouped_ffn_bwd(const moe_config *cfg, const void *x_perm,
-                        const float *x_scale, const int32_t *offsets,
-                        const void *w1, const float *w1_scale, const void *w2,
-                        const float *w2_scale, const void *act_gu,
-                        const void *act_h, const float *h_scale,
+                        const void *x_scale, const int32_t *offsets,
+                        const void *w1, const void *w1_scale, const void *w2,
+                        const void *w2_scale, const void *act_gu,
+                        const void *act_h, const void *h_scale,
                         const void *d_out_perm, void *dx_perm, void *dw1,
                         void *dw2, void *ws, size_t ws_bytes, void *stream);
 
@@ -302,6 +302,21 @@ int moe_route_bwd(const moe_config *cfg, const void *x, const float *w_router,
 int moe_quantize_fp8_blockwise(const void *src, int src_dtype, int64_t rows,
                                int64_t cols, int64_t block_r, int64_t block_c,
                                uint8_t *dst, float *scale, void *stream);
+
+/* MXFP8 quantisation (OCP Microscaling v1.0 MXFP8 E4M3, the format of the
+ * Hybrid-EP article's FP8 results): src [rows, cols] (src_dtype f32 or bf16)
+ * in blocks of 32 consecutive elements, along rows (colwise = 0: blocks
+ * 1 x 32, cols % 32 == 0, e8m0 [rows, cols/32]) or along columns
+ * (colwise = 1: blocks 32 x 1, rows % 32 == 0, e8m0 [rows/32, cols]).
+ * Per block: x = the smallest integer in [-127, 127] with amax * 2^-x <=
+ * 448 (0 for an all-zero block), e8m0 = x + 127, dst = e4m3(v * 2^-x)
+ * rounded to nearest even (no element saturates). Weights are quantised
+ * both ways: rows for the forward products, columns for the data-gradient
+ * products, whose contraction runs along the weights' other dimension.
+ * Errors: MOE_ERR_INVALID_ARG (sizes, NULL), MOE_ERR_UNSUPPORTED_DTYPE,
+ * MOE_ERR_ALIGNMENT (colwise = 0 needs 16-byte aligned src and dst). */
+int moe_quantize_mxfp8(const void *src, int src_dtype, int64_t rows, int64_t cols,
+                       int colwise, uint8_t *dst, uint8_t *e8m0, void *stream);
 
 /* Static description of a status code. */
 const char *moe_status_string(int status);

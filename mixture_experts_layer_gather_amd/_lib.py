@@ -18,7 +18,7 @@ LIB_PATH = os.path.join(HERE, "libmoe.so")
 MOE_OK = 0
 STATUS = {0: "MOE_OK", -1: "MOE_ERR_INVALID_ARG", -2: "MOE_ERR_UNSUPPORTED_DTYPE",
           -3: "MOE_ERR_ALIGNMENT", -4: "MOE_ERR_WORKSPACE", -5: "MOE_ERR_HIP"}
-DTYPE = {"f32": 0, "bf16": 1, "fp8": 2}
+DTYPE = {"f32": 0, "bf16": 1, "fp8": 2, "mxfp8": 3}
 SCORE = {"softmax": 0, "sigmoid": 1}
 GROUP_SCORE = {"top2_sum": 0, "max": 1}
 OP_ROUTE, OP_DISPATCH, OP_GROUPED_FFN, OP_GROUPED_FFN_BWD, OP_ROUTE_BWD, OP_AUX_LOSS = range(6)
@@ -26,7 +26,7 @@ OP_ROUTE, OP_DISPATCH, OP_GROUPED_FFN, OP_GROUPED_FFN_BWD, OP_ROUTE_BWD, OP_AUX_
 EXPORTS = ["moe_workspace_size", "moe_route", "moe_dispatch", "moe_grouped_ffn", "moe_combine",
            "moe_combine_bwd", "moe_grouped_ffn_bwd", "moe_dispatch_bwd", "moe_route_bwd",
            "moe_route_aux_loss",
-           "moe_quantize_fp8_blockwise", "moe_status_string"]
+           "moe_quantize_fp8_blockwise", "moe_quantize_mxfp8", "moe_status_string"]
 
 
 class MoeError(RuntimeError):
@@ -97,6 +97,7 @@ def lib():
             "moe_route_bwd": (ctypes.c_int, [C] + [P] * 10 + [sz, P]),
             "moe_route_aux_loss": (ctypes.c_int, [C, P, P, P, P, sz, P]),
             "moe_quantize_fp8_blockwise": (ctypes.c_int, [P, ctypes.c_int, i64, i64, i64, i64, P, P, P]),
+            "moe_quantize_mxfp8": (ctypes.c_int, [P, ctypes.c_int, i64, i64, ctypes.c_int, P, P, P]),
             "moe_status_string": (ctypes.c_char_p, [ctypes.c_int]),
         }
         for name, (res, args) in sig.items():
@@ -202,6 +203,13 @@ def moe_quantize_fp8_blockwise(src, rows, cols, block_r, block_c, dst, scale, st
     sdt = {torch.float32: 0, torch.bfloat16: 1}[src.dtype]
     _check("moe_quantize_fp8_blockwise", lib().moe_quantize_fp8_blockwise(
         _p(src), sdt, rows, cols, block_r, block_c, _p(dst), _p(scale), _stream(stream)))
+
+
+def moe_quantize_mxfp8(src, rows, cols, colwise, dst, e8m0, stream=None):
+    import torch
+    sdt = {torch.float32: 0, torch.bfloat16: 1}[src.dtype]
+    _check("moe_quantize_mxfp8", lib().moe_quantize_mxfp8(
+        _p(src), sdt, rows, cols, int(bool(colwise)), _p(dst), _p(e8m0), _stream(stream)))
 
 
 def moe_status_string(rc: int) -> str:

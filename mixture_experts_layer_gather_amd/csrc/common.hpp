@@ -26,6 +26,30 @@ __device__ __forceinline__ bf16_t f32_to_bf16(float f) {
   return __builtin_bit_cast(bf16_t, b);
 }
 
+// MXFP8 shared exponent of a block of 32 elements with largest magnitude
+// amax (>= 0): the smallest x in [-127, 127] with amax * 2^-x <= 448, 0 for
+// amax = 0. With amax = 1.m * 2^(E-127): x = E - 134 when the mantissa
+// exceeds 0.75 (amax's fraction m/2 above 0.875), else E - 135; an fp32
+// subnormal amax gives x below -127, i.e. -127.
+__device__ __forceinline__ int mx_scale_exp(float amax) {
+  const uint32_t b = __float_as_uint(amax);
+  if (b == 0) return 0;
+  const int E = int(b >> 23);
+  if (E == 0) return -127;
+  const int x = E - 134 - ((b & 0x7fffffu) <= 0x600000u ? 1 : 0);
+  return x < -127 ? -127 : (x > 127 ? 127 : x);
+}
+
+// E4M3 codes of 8 values scaled by 2^-x (exact), round to nearest even.
+__device__ __forceinline__ u32x2 mx_codes8(const float* v, int x) {
+  uint32_t lo = 0, hi = 0;
+  lo = __builtin_amdgcn_cvt_pk_fp8_f32(ldexpf(v[0], -x), ldexpf(v[1], -x), lo, false);
+  lo = __builtin_amdgcn_cvt_pk_fp8_f32(ldexpf(v[2], -x), ldexpf(v[3], -x), lo, true);
+  hi = __builtin_amdgcn_cvt_pk_fp8_f32(ldexpf(v[4], -x), ldexpf(v[5], -x), hi, false);
+  hi = __builtin_amdgcn_cvt_pk_fp8_f32(ldexpf(v[6], -x), ldexpf(v[7], -x), hi, true);
+  return u32x2{lo, hi};
+}
+
 // Load/store one element of an activation tensor stored as f32 or bf16.
 template <typename T> struct Elem;
 template <> struct Elem<float> {

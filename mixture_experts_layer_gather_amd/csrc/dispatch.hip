@@ -260,6 +260,39 @@ __global__ __launch_bounds__(256) void dispatch_gather_fp8_kernel(
   }
 }
 
+// MXFP8 variant: 1 x 32 blocks, 4 lanes per block; codes of x * 2^-e with
+// the E8M0 byte e + 127 per block (e from mx_scale_exp, as in the MXFP8
+// quantiser of the expert GEMMs), written k times.
+__global__ __launch_bounds__(256) void dispatch_gather_mx_kernel(
+    const bf16_t* __restrict__ x, const int32_t* __restrict__ row_id_map,
+    uint8_t* __restrict__ xq, uint8_t* __restrict__ xs, int ntok, int d, int k) {
+  const int t = blockIdx.x;
+  if (t >= ntok) return;
+  int32_t rows[16];
+  _Pragma("unroll") for (int j = 0; j < 16; ++j) if (j < k) rows[j] = row_id_map[int64_t(t) * k + j];
+  const int nblk = d / 32;
+  const int chunks = d / 8;
+  for (int base = 0; base < chunks; base += 256) {
+    const int ch = base + threadIdx.x;
+    const bool ok = ch < chunks;
+    float v[8];
+    if (ok) Vec16<bf16_t>::load(x + int64_t(t) * d + int64_t(ch) * 8, v);
+    else
+      for (int i = 0; i < 8; ++i) v[i] = 0.0f;
+    float amax = 0.0f;
+    for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(v[i]));
+    for (int o = 2; o >= 1; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o, kWave));
+    const int e = mx_scale_exp(amax);
+    const u32x2 c = mx_codes8(v, e);
+    if (ok) {
+      _Pragma("unroll") for (int j = 0; j < 16; ++j) if (j < k) {
+        *reinterpret_cast<uint2*>(xq + int64_t(rows[j]) * d + int64_t(ch) * 8) = make_uint2(c[0], c[1]);
+        if ((ch & 3) == 0) xs[int64_t(rows[j]) * nblk + ch / 4] = uint8_t(e + 127);
+      }
+    }
+  }
+}
+
 static int tokens_per_block(int64_t d, int vec) {
   const int64_t per = d / vec;
   if (per >= 256) return 1;
@@ -281,7 +314,11 @@ void launch_dispatch(const DispatchLaunch& a, hipStream_t st) {
     dispatch_pos_kernel<false><<<nchunks, 256, bits_lds, st>>>(a.idx, a.chunk_base, a.counts, a.offsets,
                                                                a.row_id_map, a.perm_token, T, E, k);
   }
-  if (a.fp8) {
+  if (a.mx) {
+    dispatch_gather_mx_kernel<<<T, 256, 0, st>>>(reinterpret_cast<const bf16_t*>(a.x), a.row_id_map,
+                                                 reinterpret_cast<uint8_t*>(a.x_perm),
+                                                 reinterpret_cast<uint8_t*>(a.x_scale), T, int(a.d), k);
+  } else if (a.fp8) {
     dispatch_gather_fp8_kernel<<<T, 256, 0, st>>>(reinterpret_cast<const bf16_t*>(a.x), a.row_id_map,
                                                   reinterpret_cast<uint8_t*>(a.x_perm), a.x_scale, T,
                                                   int(a.d), k);

@@ -54,6 +54,9 @@ template <int N, typename F> __device__ __forceinline__ void static_for(F&& f) {
 enum { EPI_STORE = 0, EPI_SWIGLU = 1, EPI_DSWIGLU = 2 };
 
 typedef uint8_t fp8_t;  // OCP E4M3FN code
+// MXFP8 operand: E4M3 codes whose scales are E8M0 bytes per 32 K-values,
+// applied by the matrix core itself (a distinct type selects that path)
+enum class mx8_t : uint8_t {};
 
 template <typename T> struct Mfma;
 template <> struct Mfma<bf16_t> {
@@ -104,9 +107,27 @@ template <> struct Mfma<fp8_t> {
   }
 };
 
+// MXFP8: the same fragments. In the matrix core's K order a lane of group
+// q = l / 16 feeds K-values 16q .. 16q + 15 and 64 + 16q .. 64 + 16q + 15 of
+// the 128-deep block, and the scale byte of lane l (row or column l % 16)
+// applies to K block q, i.e. K-values 32q .. 32q + 31, held by groups 2q % 4
+// and (2q + 1) % 4 (measured on gfx950 with one wave and marked scales). The
+// operands' K order in LDS is the source order, so block q of a row is MXFP8
+// block 4 s + q of step s.
+template <> struct Mfma<mx8_t> : Mfma<fp8_t> {
+  static __device__ __forceinline__ frag load(const mx8_t* p0, const mx8_t* p1) {
+    return Mfma<fp8_t>::load(reinterpret_cast<const fp8_t*>(p0), reinterpret_cast<const fp8_t*>(p1));
+  }
+  static __device__ __forceinline__ f32x4_t mma_scaled(frag a, frag b, f32x4_t c, int sa, int sb) {
+    return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, sa, 0, sb);
+  }
+};
+
 // Activation dtype of the epilogue outputs for operand dtype T.
 template <typename T> struct OutOf { typedef T type; };
 template <> struct OutOf<fp8_t> { typedef bf16_t type; };
+template <> struct OutOf<mx8_t> { typedef bf16_t type; };
+
 
 struct GemmArgs {
   const void* A;
@@ -382,6 +403,15 @@ struct alignas(16) Stage {  // 16-byte multiple: stages sit back to back in one 
   T B[BN * BK];
   float SA[SCALED ? (NTH > BM ? NTH : BM) : 1];  // FP8 row scales of the A tile (padded)
 };
+// MXFP8 stage: per A row and per B column, the E8M0 bytes of the step's four
+// 32-deep K blocks in one word (byte q = block q)
+template <int BM, int BN, int BK, int NTH>
+struct alignas(16) StageMx {
+  mx8_t A[BM * BK];
+  mx8_t B[BN * BK];
+  uint32_t SA[NTH > BM ? NTH : BM];
+  uint32_t SB[BN];
+};
 
 template <typename T, typename TC, bool A_KMAJ, bool B_KMAJ, int MODE, int EPI, int BM, int BN,
           int BK, int WM, int WN, int NS>
@@ -391,7 +421,8 @@ void gemm_kernel(GemmArgs g) {
   using MF = Mfma<T>;
   using TO = typename OutOf<T>::type;
   constexpr bool FP8 = sizeof(T) == 1;
-  using ST = Stage<T, BM, BN, BK, WM * WN * 64, FP8>;
+  constexpr bool MX = std::is_same<T, mx8_t>::value;
+  using ST = std::conditional_t<MX, StageMx<BM, BN, BK, WM * WN * 64>, Stage<T, BM, BN, BK, WM * WN * 64, FP8>>;
   constexpr int VEC = 16 / sizeof(T);
   constexpr int WTM = BM / WM, WTN = BN / WN;
   constexpr int FM = WTM / 16, FN = WTN / 16;
@@ -552,7 +583,8 @@ void gemm_kernel(GemmArgs g) {
     }
   }
   // FP8: thread tid stages the row scale of A-tile row tid; rows past the
-  // group (and threads past the tile) read zeros
+  // group (and threads past the tile) read zeros. MXFP8: the same word holds
+  // the row's four E8M0 bytes of the step (a_scale_ld = K / 128 words).
   const char* sa_base = nullptr;
   int64_t sa_end = 0;
   if constexpr (FP8) {
@@ -563,7 +595,7 @@ void gemm_kernel(GemmArgs g) {
   // up block of W1
   const float* __restrict__ sb_base = nullptr;
   int sb_blk0 = 0, sb_blk1 = 0;
-  if constexpr (FP8) {
+  if constexpr (FP8 && !MX) {
     sb_base = g.b_scale + int64_t(grp) * g.b_scale_gstride;
     if (EPI == EPI_SWIGLU) {
       sb_blk0 = (nt * (BN / 2)) / 128;
@@ -573,9 +605,31 @@ void gemm_kernel(GemmArgs g) {
     }
   }
 
+  // MXFP8: E8M0 bytes of B (b_scale bytes; group stride b_scale_gstride
+  // bytes). K-major B [N, K]: row n's bytes at n * b_scale_ld (= K / 32), so
+  // thread tid < BN reads one word per step for tile column tid; K-strided B
+  // [K, N]: scale row kb (K block) at kb * b_scale_ld (= N), four bytes per
+  // step and column.
+  const char* mb_base = nullptr;
+  int64_t mb_end = 0;
+  int mb_row = 0;  // K-major: byte offset of column tid's scale row
+  if constexpr (MX) {
+    mb_base = reinterpret_cast<const char*>(g.b_scale) + int64_t(grp) * g.b_scale_gstride;
+    mb_end = B_KMAJ ? int64_t(g.N) * g.b_scale_ld : int64_t(g.K / 32) * g.b_scale_ld;
+    if constexpr (B_KMAJ) {
+      int grow = n0 + tid;
+      if (EPI == EPI_SWIGLU) {  // the B rows' order of the DMA plan above
+        const int w = tid / WTN, within = tid % WTN;
+        grow = (within / (WTN / 2)) * g.f + nt * (BN / 2) + w * (WTN / 2) + within % (WTN / 2);
+      }
+      mb_row = grow * g.b_scale_ld;
+    }
+  }
+
   // register-staged operand chunks (K-strided sources) and FP8 row scale
   u32x4 ra[PA::NREG], rb[PB::NREG];
   float rs = 0.0f;
+  uint32_t rsb = 0;
 
   // issue the loads of K step s into stage st: DMA for K-major operands,
   // registers for K-strided ones
@@ -613,6 +667,22 @@ void gemm_kernel(GemmArgs g) {
       rs = __builtin_bit_cast(
           float, __builtin_amdgcn_raw_buffer_load_b32(sr, uint32_t((tid * g.a_scale_ld + s * (BK / 128)) * 4), 0, 0));
     }
+    if constexpr (MX) {
+      if (tid < BN) {
+        const rsrc_t sr = make_rsrc(mb_base, live ? mb_end : 0);
+        if constexpr (B_KMAJ) {
+          rsb = __builtin_amdgcn_raw_buffer_load_b32(sr, uint32_t(mb_row + 4 * s), 0, 0);
+        } else {
+          uint32_t w = 0;
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+            w |= uint32_t(__builtin_amdgcn_raw_buffer_load_b8(
+                     sr, uint32_t((4 * s + q) * g.b_scale_ld + n0 + tid), 0, 0))
+                 << (8 * q);
+          rsb = w;
+        }
+      }
+    }
   };
   // write the register-staged parts of a step into stage st
   auto commit = [&](ST& st) {
@@ -624,7 +694,12 @@ void gemm_kernel(GemmArgs g) {
 #pragma unroll
       for (int i = 0; i < PB::NT; ++i) store_transposed<T, BK>(&rb[4 * i], st.B, pb.lrow[i], pb.lk[i]);
     }
-    if constexpr (FP8) st.SA[tid] = rs;
+    if constexpr (MX) {
+      st.SA[tid] = __builtin_bit_cast(uint32_t, rs);
+      if (tid < BN) st.SB[tid] = rsb;
+    } else if constexpr (FP8) {
+      st.SA[tid] = rs;
+    }
   };
 
   f32x4_t acc[FM][FN];
@@ -685,7 +760,7 @@ void gemm_kernel(GemmArgs g) {
   // one K step (K block s) on stage st
   auto compute = [&](const ST& st, int s) {
     float sb0 = 0.0f, sb1 = 0.0f;
-    if constexpr (FP8) {
+    if constexpr (FP8 && !MX) {
       const int kb = min(s, nk - 1);  // BK == 128: one scale block per step
       if (B_KMAJ) {
         sb0 = sb_base[int64_t(sb_blk0) * g.b_scale_ld + kb];
@@ -694,7 +769,29 @@ void gemm_kernel(GemmArgs g) {
         sb0 = sb1 = sb_base[int64_t(kb) * g.b_scale_ld + sb_blk0];
       }
     }
-    if constexpr (FP8) {
+    if constexpr (MX) {
+      // one 128-deep block per step; the matrix core applies the E8M0 byte
+      // of K block q = lane / 16 (byte q of the row's or column's word) and
+      // accumulates in place
+      static_assert(BK == MF::MK, "one MFMA K block per step");
+      const int sh = 8 * (lane / 16);
+      typename MF::frag bfr[FN], acur, anxt;
+      int sbj[FN];
+#pragma unroll
+      for (int j = 0; j < FN; ++j) {
+        bfr[j] = load_b(st, j, 0);
+        sbj[j] = int((st.SB[wn * WTN + j * 16 + lane % 16] >> sh) & 0xffu);
+      }
+      acur = load_a(st, 0, 0);
+      static_for<FM>([&](auto ic) {
+        constexpr int i = decltype(ic)::value;
+        if constexpr (i + 1 < FM) anxt = load_a(st, i + 1, 0);
+        const int sai = int((st.SA[wm * WTM + i * 16 + lane % 16] >> sh) & 0xffu);
+#pragma unroll
+        for (int j = 0; j < FN; ++j) acc[i][j] = MF::mma_scaled(acur, bfr[j], acc[i][j], sai, sbj[j]);
+        if constexpr (i + 1 < FM) acur = anxt;
+      });
+    } else if constexpr (FP8) {
       // one 128-deep block per step: B fragments first, then one A fragment
       // ahead of the FN MFMAs (into temporaries) and their scaled adds
       static_assert(BK == MF::MK, "one MFMA K block per step");
@@ -967,6 +1064,115 @@ static void dequant_rows(const uint8_t* q, const float* scale, int64_t rows, int
 }
 
 // ---------------------------------------------------------------------------
+// MXFP8 quantisation: E4M3 codes of v * 2^-x with one E8M0 byte x + 127 per
+// block of 32 (x = mx_scale_exp of the block's largest magnitude, so that no
+// scaled value exceeds 448; ldexp is an exact rescaling, then round to
+// nearest even by v_cvt_pk_fp8_f32). Row blocks (1 x 32): 4 lanes per block;
+// column blocks (32 x 1): one thread per block, 32 rows apart.
+// ---------------------------------------------------------------------------
+template <typename TS>
+__device__ __forceinline__ void load8_src(const TS* src, int64_t i, float* v) {
+  if constexpr (sizeof(TS) == 2) {
+    Vec16<bf16_t>::load(reinterpret_cast<const bf16_t*>(src) + i, v);
+  } else {
+    Vec16<float>::load(reinterpret_cast<const float*>(src) + i, v);
+    Vec16<float>::load(reinterpret_cast<const float*>(src) + i + 4, v + 4);
+  }
+}
+
+
+template <typename TS>
+__global__ __launch_bounds__(256) void quant_mx_rows_kernel(const TS* __restrict__ src, uint8_t* __restrict__ q,
+                                                            uint8_t* __restrict__ e8m0, int64_t nchunks) {
+  const int64_t ch = blockIdx.x * int64_t(256) + threadIdx.x;  // chunk of 8 elements
+  const bool ok = ch < nchunks;
+  float v[8];
+  if (ok) load8_src(src, ch * 8, v);
+  else
+    for (int i = 0; i < 8; ++i) v[i] = 0.0f;
+  float amax = 0.0f;
+  for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(v[i]));
+  for (int o = 2; o >= 1; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o, kWave));
+  const int x = mx_scale_exp(amax);
+  const u32x2 c = mx_codes8(v, x);
+  if (ok) {
+    *reinterpret_cast<u32x2*>(q + ch * 8) = c;
+    if ((ch & 3) == 0) e8m0[ch / 4] = uint8_t(x + 127);  // rows are whole 32-blocks
+  }
+}
+
+template <typename TS>
+__global__ __launch_bounds__(256) void quant_mx_cols_kernel(const TS* __restrict__ src, uint8_t* __restrict__ q,
+                                                            uint8_t* __restrict__ e8m0, int64_t C,
+                                                            int64_t col_blocks) {
+  const int64_t br = blockIdx.x / col_blocks;  // block row: rows 32 br .. + 32
+  const int64_t c = (blockIdx.x % col_blocks) * 256 + threadIdx.x;
+  if (c >= C) return;
+  const TS* p = src + br * 32 * C + c;
+  float v[32];
+  float amax = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 32; ++i) {
+    if constexpr (sizeof(TS) == 2) v[i] = bf16_to_f32(reinterpret_cast<const bf16_t*>(p)[int64_t(i) * C]);
+    else v[i] = reinterpret_cast<const float*>(p)[int64_t(i) * C];
+    amax = fmaxf(amax, fabsf(v[i]));
+  }
+  const int x = mx_scale_exp(amax);
+#pragma unroll
+  for (int i = 0; i < 32; i += 8) {
+    const u32x2 w = mx_codes8(v + i, x);
+#pragma unroll
+    for (int b = 0; b < 8; ++b) q[(br * 32 + i + b) * C + c] = uint8_t(w[b / 4] >> (8 * (b % 4)));
+  }
+  e8m0[br * C + c] = uint8_t(x + 127);
+}
+
+__global__ __launch_bounds__(256) void dequant_mx_rows_kernel(const fp8_t* __restrict__ q,
+                                                              const uint8_t* __restrict__ e8m0,
+                                                              bf16_t* __restrict__ dst, int64_t nchunks) {
+  const int64_t ch = blockIdx.x * int64_t(256) + threadIdx.x;
+  if (ch >= nchunks) return;
+  const u32x2 c = *reinterpret_cast<const u32x2*>(q + ch * 8);
+  const int x = int(e8m0[ch / 4]) - 127;
+  float v[8] = {__builtin_amdgcn_cvt_f32_fp8(c[0], 0), __builtin_amdgcn_cvt_f32_fp8(c[0], 1),
+                __builtin_amdgcn_cvt_f32_fp8(c[0], 2), __builtin_amdgcn_cvt_f32_fp8(c[0], 3),
+                __builtin_amdgcn_cvt_f32_fp8(c[1], 0), __builtin_amdgcn_cvt_f32_fp8(c[1], 1),
+                __builtin_amdgcn_cvt_f32_fp8(c[1], 2), __builtin_amdgcn_cvt_f32_fp8(c[1], 3)};
+#pragma unroll
+  for (int i = 0; i < 8; ++i) v[i] = ldexpf(v[i], x);
+  Vec16<bf16_t>::store(dst + ch * 8, v);
+}
+
+void launch_quant_mx_rows(const void* src, bool src_bf16, int64_t rows, int64_t cols, uint8_t* q,
+                          uint8_t* e8m0, hipStream_t st) {
+  const int64_t nchunks = rows * cols / 8;
+  const int64_t grid = (nchunks + 255) / 256;
+  if (grid <= 0) return;
+  if (src_bf16)
+    quant_mx_rows_kernel<bf16_t><<<grid, 256, 0, st>>>(reinterpret_cast<const bf16_t*>(src), q, e8m0, nchunks);
+  else
+    quant_mx_rows_kernel<float><<<grid, 256, 0, st>>>(reinterpret_cast<const float*>(src), q, e8m0, nchunks);
+}
+
+void launch_quant_mx_cols(const void* src, bool src_bf16, int64_t rows, int64_t cols, uint8_t* q,
+                          uint8_t* e8m0, hipStream_t st) {
+  const int64_t cb = (cols + 255) / 256;
+  const int64_t grid = (rows / 32) * cb;
+  if (grid <= 0) return;
+  if (src_bf16)
+    quant_mx_cols_kernel<bf16_t><<<grid, 256, 0, st>>>(reinterpret_cast<const bf16_t*>(src), q, e8m0, cols, cb);
+  else
+    quant_mx_cols_kernel<float><<<grid, 256, 0, st>>>(reinterpret_cast<const float*>(src), q, e8m0, cols, cb);
+}
+
+static void dequant_mx_rows(const uint8_t* q, const uint8_t* e8m0, int64_t rows, int64_t cols, bf16_t* dst,
+                            hipStream_t st) {
+  const int64_t nchunks = rows * cols / 8;
+  const int64_t grid = (nchunks + 255) / 256;
+  if (grid > 0) dequant_mx_rows_kernel<<<grid, 256, 0, st>>>(q, e8m0, dst, nchunks);
+}
+
+// ---------------------------------------------------------------------------
 // Tile configurations: BM x BN output tile, BK deep, WM x WN waves, NS LDS
 // stages.
 //   Small: 128 x 128, 4 waves of 64 x 64, 2 stages of 32 KB (every dtype;
@@ -988,6 +1194,7 @@ template <typename T> struct SmallCfg;
 template <> struct SmallCfg<bf16_t> : Cfg<bf16_t, 128, 128, 64, 2, 2, 2> {};
 template <> struct SmallCfg<float> : Cfg<float, 128, 128, 32, 2, 2, 2> {};
 template <> struct SmallCfg<fp8_t> : Cfg<fp8_t, 128, 128, 128, 2, 2, 2> {};
+template <> struct SmallCfg<mx8_t> : Cfg<mx8_t, 128, 128, 128, 2, 2, 2> {};
 typedef Cfg<bf16_t, 256, 256, 64, 2, 4, 2> BigCfg;
 typedef Cfg<bf16_t, 128, 256, 32, 2, 2, 3> WgradCfg;
 
@@ -1153,9 +1360,44 @@ static void gemm2_fwd_fp8(const FfnLaunch& a, const uint8_t* hq, const float* hs
   run_gemm<C, bf16_t, true, true, G_ROWS, EPI_STORE>(g2, rows_tile_bound(a.A, a.E, C::BM) * g2.tiles_n, st);
 }
 
+// MXFP8 GEMMs: scale words of 4 E8M0 bytes per A row (a_scale_ld = K / 128
+// words); B scales in bytes: rows of K / 32 for K-major weights (the forward's
+// row-quantised W1, W2), rows of N per 32-deep K block for K-strided weights
+// (the data gradients' column-quantised W2, W1).
+static void gemm1_fwd_mx(const FfnLaunch& a, void* gu, bf16_t* h16, uint8_t* hq, uint8_t* hs, hipStream_t st) {
+  typedef SmallCfg<mx8_t> C;
+  GemmArgs g1{};
+  g1.A = a.x_perm; g1.lda = a.d;
+  g1.a_scale = a.x_scale; g1.a_scale_ld = int(a.d / 128);
+  g1.B = a.w1; g1.ldb = a.d; g1.b_gstride = 2 * a.f * a.d;
+  g1.b_scale = a.w1_scale; g1.b_scale_gstride = 2 * a.f * (a.d / 32); g1.b_scale_ld = int(a.d / 32);
+  g1.offsets = a.offsets; g1.G = int(a.E);
+  g1.N = int(2 * a.f); g1.K = int(a.d); g1.f = int(a.f);
+  g1.aux0 = gu; g1.aux1 = h16;
+  g1.tiles_n = int(2 * a.f / C::BN);
+  run_gemm<C, bf16_t, true, true, G_ROWS, EPI_SWIGLU>(g1, rows_tile_bound(a.A, a.E, C::BM) * g1.tiles_n, st);
+  launch_quant_mx_rows(h16, true, a.A, a.f, hq, hs, st);
+}
+
+static void gemm2_fwd_mx(const FfnLaunch& a, const uint8_t* hq, const uint8_t* hs, hipStream_t st) {
+  typedef SmallCfg<mx8_t> C;
+  GemmArgs g2{};
+  g2.A = hq; g2.lda = a.f;
+  g2.a_scale = reinterpret_cast<const float*>(hs); g2.a_scale_ld = int(a.f / 128);
+  g2.B = a.w2; g2.ldb = a.f; g2.b_gstride = a.d * a.f;
+  g2.b_scale = a.w2_scale; g2.b_scale_gstride = a.d * (a.f / 32); g2.b_scale_ld = int(a.f / 32);
+  g2.C = a.out_perm; g2.ldc = a.d;
+  g2.offsets = a.offsets; g2.G = int(a.E);
+  g2.N = int(a.d); g2.K = int(a.f);
+  g2.tiles_n = int(a.d / C::BN);
+  run_gemm<C, bf16_t, true, true, G_ROWS, EPI_STORE>(g2, rows_tile_bound(a.A, a.E, C::BM) * g2.tiles_n, st);
+}
+
 // The first half of the forward: GU (into gu unless null) and H (+ scales).
 static void ffn_fwd_gu_h(const FfnLaunch& a, void* gu, void* h, float* hs, bf16_t* h16, hipStream_t st) {
-  if (a.wt == 2) {
+  if (a.wt == 3) {
+    gemm1_fwd_mx(a, gu, h16, static_cast<uint8_t*>(h), reinterpret_cast<uint8_t*>(hs), st);
+  } else if (a.wt == 2) {
     gemm1_fwd_fp8(a, gu, h16, static_cast<uint8_t*>(h), hs, st);
   } else if (a.wt == 1) {
     if (big_rows(a.tile, a.A, a.E, 2 * a.f)) gemm1_fwd<BigCfg>(a, gu, h, st);
@@ -1252,8 +1494,22 @@ static void ffn_bwd_t(const FfnBwdLaunch& a, void* h_out, hipStream_t st) {
 // dequantised forward operands (X, H) and the bf16 gradients. With h16 set
 // (activation recompute) the dH epilogue rebuilds H in bf16 from the saved
 // GU and it is quantised as in the forward into a.act_h / a.h_scale.
+// MXFP8 (MXF): the same structure with 1 x 32 E8M0 blocks for the gradient
+// operands and, for the weights, the column-quantised copies (32 x 1 blocks
+// along these products' contraction dims) that the caller passes as w1, w2.
+template <bool MXF>
 static void ffn_bwd_fp8(const FfnBwdLaunch& a, bf16_t* h16, hipStream_t st) {
-  typedef SmallCfg<fp8_t> C;
+  typedef SmallCfg<std::conditional_t<MXF, mx8_t, fp8_t>> C;
+  auto quant = [&](const void* src, int64_t rows, int64_t cols, uint8_t* q, float* sc) {
+    if constexpr (MXF) launch_quant_mx_rows(src, true, rows, cols, q, reinterpret_cast<uint8_t*>(sc), st);
+    else launch_quant_rows(src, true, rows, cols, q, sc, st);
+  };
+  auto dequant = [&](const void* q, const float* sc, int64_t rows, int64_t cols, bf16_t* dst) {
+    if constexpr (MXF)
+      dequant_mx_rows(static_cast<const uint8_t*>(q), reinterpret_cast<const uint8_t*>(sc), rows, cols, dst, st);
+    else
+      dequant_rows(static_cast<const uint8_t*>(q), sc, rows, cols, dst, st);
+  };
   const FfnWs w = ffn_ws(a.A, a.d, a.f, 2, true, true, a.recompute);
   bf16_t* d_gu = reinterpret_cast<bf16_t*>(at(a.ws, w.d_gu));
   uint8_t* dq = reinterpret_cast<uint8_t*>(at(a.ws, w.d_out_q));
@@ -1263,37 +1519,39 @@ static void ffn_bwd_fp8(const FfnBwdLaunch& a, bf16_t* h16, hipStream_t st) {
   bf16_t* xd = reinterpret_cast<bf16_t*>(at(a.ws, w.x_deq));
   bf16_t* hd = reinterpret_cast<bf16_t*>(at(a.ws, w.h_deq));
   const int mt_bound = rows_tile_bound(a.A, a.E, C::BM);
-  launch_quant_rows(a.d_out, true, a.A, a.d, dq, ds, st);
+  quant(a.d_out, a.A, a.d, dq, ds);
   // dH = Q(dO) W2 (+ SwiGLU backward from the saved bf16 GU)
   GemmArgs g1{};
   g1.A = dq; g1.lda = a.d;
   g1.a_scale = ds; g1.a_scale_ld = int(a.d / 128);
   g1.B = a.w2; g1.ldb = a.f; g1.b_gstride = a.d * a.f;
-  g1.b_scale = a.w2_scale; g1.b_scale_gstride = (a.d / 128) * (a.f / 128); g1.b_scale_ld = int(a.f / 128);
+  g1.b_scale = a.w2_scale;
+  if constexpr (MXF) { g1.b_scale_gstride = (a.d / 32) * a.f; g1.b_scale_ld = int(a.f); }
+  else { g1.b_scale_gstride = (a.d / 128) * (a.f / 128); g1.b_scale_ld = int(a.f / 128); }
   g1.C = d_gu; g1.ldc = 2 * a.f;
   g1.offsets = a.offsets; g1.G = int(a.E);
   g1.N = int(a.f); g1.K = int(a.d); g1.f = int(a.f);
   g1.aux0 = const_cast<void*>(a.act_gu); g1.aux1 = h16;
   g1.tiles_n = int(a.f / C::BN);
   run_gemm<C, bf16_t, true, false, G_ROWS, EPI_DSWIGLU>(g1, mt_bound * g1.tiles_n, st);
-  if (h16)
-    launch_quant_rows(h16, true, a.A, a.f, static_cast<uint8_t*>(const_cast<void*>(a.act_h)),
-                      const_cast<float*>(a.h_scale), st);
+  if (h16) quant(h16, a.A, a.f, static_cast<uint8_t*>(const_cast<void*>(a.act_h)), const_cast<float*>(a.h_scale));
   // dX = Q(dGU) W1
-  launch_quant_rows(d_gu, true, a.A, 2 * a.f, gq, gs, st);
+  quant(d_gu, a.A, 2 * a.f, gq, gs);
   GemmArgs g2{};
   g2.A = gq; g2.lda = 2 * a.f;
   g2.a_scale = gs; g2.a_scale_ld = int(2 * a.f / 128);
   g2.B = a.w1; g2.ldb = a.d; g2.b_gstride = 2 * a.f * a.d;
-  g2.b_scale = a.w1_scale; g2.b_scale_gstride = (2 * a.f / 128) * (a.d / 128); g2.b_scale_ld = int(a.d / 128);
+  g2.b_scale = a.w1_scale;
+  if constexpr (MXF) { g2.b_scale_gstride = (2 * a.f / 32) * a.d; g2.b_scale_ld = int(a.d); }
+  else { g2.b_scale_gstride = (2 * a.f / 128) * (a.d / 128); g2.b_scale_ld = int(a.d / 128); }
   g2.C = a.dx_perm; g2.ldc = a.d;
   g2.offsets = a.offsets; g2.G = int(a.E);
   g2.N = int(a.d); g2.K = int(2 * a.f);
   g2.tiles_n = int(a.d / C::BN);
   run_gemm<C, bf16_t, true, false, G_ROWS, EPI_STORE>(g2, mt_bound * g2.tiles_n, st);
   // weight gradients in bf16 on dequantised X and H
-  dequant_rows(reinterpret_cast<const uint8_t*>(a.x_perm), a.x_scale, a.A, a.d, xd, st);
-  dequant_rows(reinterpret_cast<const uint8_t*>(a.act_h), a.h_scale, a.A, a.f, hd, st);
+  dequant(a.x_perm, a.x_scale, a.A, a.d, xd);
+  dequant(a.act_h, a.h_scale, a.A, a.f, hd);
   wgrad_any<bf16_t>(a.tile, a.d_out, hd, d_gu, xd, a.dw1, a.dw2, a.offsets, a.d, a.f, a.E, st);
 }
 
@@ -1302,7 +1560,7 @@ void launch_grouped_ffn(const FfnLaunch& a, hipStream_t st) {
     copy_bytes(a.x_perm, a.out_perm, a.A * a.d * (a.act == 1 ? 2 : 4), st);
     return;
   }
-  const FfnWs w = ffn_ws(a.A, a.d, a.f, a.act == 1 ? 2 : 4, a.wt == 2, false, a.recompute);
+  const FfnWs w = ffn_ws(a.A, a.d, a.f, a.act == 1 ? 2 : 4, a.wt >= 2, false, a.recompute);
   // what the backward will not find saved goes to the workspace (H) or is
   // not stored at all (GU)
   void* gu = a.recompute == 2 ? nullptr : a.act_gu;
@@ -1310,7 +1568,9 @@ void launch_grouped_ffn(const FfnLaunch& a, hipStream_t st) {
   float* hs = a.recompute ? reinterpret_cast<float*>(at(a.ws, w.r_hs)) : a.h_scale;
   bf16_t* h16 = reinterpret_cast<bf16_t*>(at(a.ws, w.h_bf16));
   ffn_fwd_gu_h(a, gu, h, hs, h16, st);
-  if (a.wt == 2) {
+  if (a.wt == 3) {
+    gemm2_fwd_mx(a, static_cast<const uint8_t*>(h), reinterpret_cast<const uint8_t*>(hs), st);
+  } else if (a.wt == 2) {
     gemm2_fwd_fp8(a, static_cast<const uint8_t*>(h), hs, st);
   } else if (a.wt == 1) {
     if (big_rows(a.tile, a.A, a.E, a.d)) gemm2_fwd<BigCfg>(a, h, st);
@@ -1329,7 +1589,7 @@ void launch_grouped_ffn_bwd(const FfnBwdLaunch& a, hipStream_t st) {
     zero_bytes(a.dw2, a.E * a.d * a.f * ws, st);
     return;
   }
-  const bool fp8 = a.wt == 2;
+  const bool fp8 = a.wt >= 2;
   const FfnWs w = ffn_ws(a.A, a.d, a.f, es, fp8, true, a.recompute);
   FfnBwdLaunch b = a;
   void* h_out = nullptr;  // activation recompute: H rebuilt by the dH epilogue
@@ -1350,7 +1610,8 @@ void launch_grouped_ffn_bwd(const FfnBwdLaunch& a, hipStream_t st) {
       h_out = fp8 ? static_cast<void*>(h16) : const_cast<void*>(b.act_h);
     }
   }
-  if (fp8) ffn_bwd_fp8(b, static_cast<bf16_t*>(h_out), st);
+  if (a.wt == 3) ffn_bwd_fp8<true>(b, static_cast<bf16_t*>(h_out), st);
+  else if (fp8) ffn_bwd_fp8<false>(b, static_cast<bf16_t*>(h_out), st);
   else if (a.wt == 1) ffn_bwd_t<bf16_t>(b, h_out, st);
   else ffn_bwd_t<float>(b, h_out, st);
 }

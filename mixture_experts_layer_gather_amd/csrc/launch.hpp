@@ -70,11 +70,12 @@ struct DispatchLaunch {
   int32_t* row_id_map;
   int32_t* perm_token;
   void* x_perm;
-  float* x_scale;        // fp8 only
+  float* x_scale;        // fp8 only (mx: E8M0 bytes [T*k, d/32])
   int32_t* chunk_base;   // workspace [nchunks, E]
   int64_t T, d, E, k;
   int act;               // 0 f32, 1 bf16
   bool fp8;
+  bool mx;               // MXFP8: 1 x 32 blocks, E8M0 scales
   int qblock;
 };
 void launch_dispatch(const DispatchLaunch& a, hipStream_t st);
@@ -119,7 +120,7 @@ struct FfnLaunch {
   void* ws;  // ffn_ws_bytes(..., bwd = false)
   int64_t A, d, f, E;
   int act;   // 0 f32, 1 bf16
-  int wt;    // 0 f32, 1 bf16, 2 fp8
+  int wt;    // 0 f32, 1 bf16, 2 fp8, 3 mxfp8 (scale pointers then hold E8M0 bytes)
   bool identity;
   int tile;       // MOE_TILE_*
   int recompute;  // 0 keep GU and H, 1 keep GU only, 2 keep neither
@@ -130,6 +131,12 @@ size_t ffn_ws_bytes(int64_t A, int64_t d, int64_t f, int act_bytes, bool fp8, bo
 // FP8 E4M3 quantisation of rows in 1 x 128 blocks (cols a multiple of 128).
 void launch_quant_rows(const void* src, bool src_bf16, int64_t rows, int64_t cols, uint8_t* q,
                        float* scale, hipStream_t st);
+// MXFP8: rows in 1 x 32 blocks (cols % 32 == 0), E8M0 [rows, cols/32]; or
+// columns in 32 x 1 blocks (rows % 32 == 0), E8M0 [rows/32, cols].
+void launch_quant_mx_rows(const void* src, bool src_bf16, int64_t rows, int64_t cols, uint8_t* q,
+                          uint8_t* e8m0, hipStream_t st);
+void launch_quant_mx_cols(const void* src, bool src_bf16, int64_t rows, int64_t cols, uint8_t* q,
+                          uint8_t* e8m0, hipStream_t st);
 
 struct FfnBwdLaunch {
   const void* x_perm;

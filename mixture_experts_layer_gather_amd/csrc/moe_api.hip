@@ -16,6 +16,19 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 
 size_t act_bytes(int dt) { return dt == MOE_DTYPE_F32 ? 4 : 2; }
 
+// FP8 E4M3 codes with either scale kind (fp32 block scales or MXFP8 E8M0)
+bool is_fp8(const moe_config* c) {
+  return c->weight_dtype == MOE_DTYPE_FP8_E4M3 || c->weight_dtype == MOE_DTYPE_MXFP8;
+}
+int weight_kind(const moe_config* c) {
+  switch (c->weight_dtype) {
+    case MOE_DTYPE_F32: return 0;
+    case MOE_DTYPE_BF16: return 1;
+    case MOE_DTYPE_FP8_E4M3: return 2;
+    default: return 3;
+  }
+}
+
 // Validates the configuration; returns MOE_OK or an error code.
 int check_cfg(const moe_config* c) {
   if (!c) return MOE_ERR_INVALID_ARG;
@@ -46,6 +59,11 @@ int check_cfg(const moe_config* c) {
   if (c->weight_dtype == MOE_DTYPE_FP8_E4M3) {
     if (c->act_dtype != MOE_DTYPE_BF16) return MOE_ERR_UNSUPPORTED_DTYPE;
     if (c->quant_block != 128) return MOE_ERR_INVALID_ARG;
+  } else if (c->weight_dtype == MOE_DTYPE_MXFP8) {
+    if (c->act_dtype != MOE_DTYPE_BF16) return MOE_ERR_UNSUPPORTED_DTYPE;
+    if (c->quant_block != 32) return MOE_ERR_INVALID_ARG;
+    // the backward holds the column-quantised weights only: it cannot rerun GEMM1
+    if (c->recompute == MOE_RECOMPUTE_FULL) return MOE_ERR_UNSUPPORTED_DTYPE;
   } else if (c->weight_dtype != c->act_dtype) {
     return MOE_ERR_UNSUPPORTED_DTYPE;
   }
@@ -109,10 +127,10 @@ size_t moe_workspace_size(const moe_config* cfg, int op) {
     case MOE_OP_DISPATCH: return T ? round_up(size_t(dispatch_chunks(T)) * size_t(E) * 4) : 0;
     case MOE_OP_GROUPED_FFN:
       return round_up(moe::ffn_ws_bytes(T * k, cfg->hidden, f, int(act_bytes(cfg->act_dtype)),
-                                        cfg->weight_dtype == MOE_DTYPE_FP8_E4M3, false, cfg->recompute));
+                                        is_fp8(cfg), false, cfg->recompute));
     case MOE_OP_GROUPED_FFN_BWD:
       return round_up(moe::ffn_ws_bytes(T * k, cfg->hidden, f, int(act_bytes(cfg->act_dtype)),
-                                        cfg->weight_dtype == MOE_DTYPE_FP8_E4M3, true, cfg->recompute));
+                                        is_fp8(cfg), true, cfg->recompute));
     case MOE_OP_ROUTE_BWD: {
       const int Z = moe::route_bwd_zsplit(T, cfg->hidden, E);
       const size_t parts = Z > 1 ? size_t(Z) * size_t(E) * size_t(cfg->hidden) * 4 : 0;
@@ -148,9 +166,9 @@ int moe_route(const moe_config* cfg, const void* x, const float* w_router, const
 
 int moe_dispatch(const moe_config* cfg, const void* x, const int32_t* topk_idx, int32_t* counts,
                  int32_t* offsets, int32_t* row_id_map, int32_t* perm_token, void* x_perm,
-                 float* x_scale, void* ws, size_t ws_bytes, void* stream) {
+                 void* x_scale, void* ws, size_t ws_bytes, void* stream) {
   MOE_CHECK(check_cfg(cfg));
-  const bool fp8 = cfg->weight_dtype == MOE_DTYPE_FP8_E4M3;
+  const bool fp8 = is_fp8(cfg);
   MOE_CHECK(need(x)); MOE_CHECK(need(topk_idx)); MOE_CHECK(need(counts)); MOE_CHECK(need(offsets));
   MOE_CHECK(need(row_id_map)); MOE_CHECK(need(perm_token)); MOE_CHECK(need(x_perm));
   if (fp8) MOE_CHECK(need(x_scale));
@@ -161,23 +179,24 @@ int moe_dispatch(const moe_config* cfg, const void* x, const int32_t* topk_idx, 
   if (!ws || ws_bytes < moe_workspace_size(cfg, MOE_OP_DISPATCH)) return MOE_ERR_WORKSPACE;
   moe::DispatchLaunch a{};
   a.x = x; a.idx = topk_idx; a.counts = counts; a.offsets = offsets; a.row_id_map = row_id_map;
-  a.perm_token = perm_token; a.x_perm = x_perm; a.x_scale = x_scale;
+  a.perm_token = perm_token; a.x_perm = x_perm; a.x_scale = static_cast<float*>(x_scale);
   a.chunk_base = static_cast<int32_t*>(ws);
   a.T = cfg->num_tokens; a.d = cfg->hidden; a.E = cfg->num_experts; a.k = cfg->top_k;
   a.act = cfg->act_dtype == MOE_DTYPE_BF16 ? 1 : 0;
   a.fp8 = fp8;
+  a.mx = cfg->weight_dtype == MOE_DTYPE_MXFP8;
   a.qblock = cfg->quant_block;
   moe::launch_dispatch(a, static_cast<hipStream_t>(stream));
   return launched();
 }
 
-int moe_grouped_ffn(const moe_config* cfg, const void* x_perm, const float* x_scale,
-                    const int32_t* offsets, const void* w1, const float* w1_scale, const void* w2,
-                    const float* w2_scale, void* act_gu, void* act_h, float* h_scale, void* out_perm,
+int moe_grouped_ffn(const moe_config* cfg, const void* x_perm, const void* x_scale,
+                    const int32_t* offsets, const void* w1, const void* w1_scale, const void* w2,
+                    const void* w2_scale, void* act_gu, void* act_h, void* h_scale, void* out_perm,
                     void* ws, size_t ws_bytes, void* stream) {
   MOE_CHECK(check_cfg(cfg));
   const bool identity = cfg->ffn_mode == MOE_FFN_IDENTITY;
-  const bool fp8 = cfg->weight_dtype == MOE_DTYPE_FP8_E4M3;
+  const bool fp8 = is_fp8(cfg);
   MOE_CHECK(need(x_perm)); MOE_CHECK(need(offsets)); MOE_CHECK(need(out_perm));
   if (!identity) {
     MOE_CHECK(need(w1)); MOE_CHECK(need(w2));
@@ -194,12 +213,13 @@ int moe_grouped_ffn(const moe_config* cfg, const void* x_perm, const float* x_sc
   const size_t need_ws = moe_workspace_size(cfg, MOE_OP_GROUPED_FFN);
   if (need_ws && (!ws || ws_bytes < need_ws)) return MOE_ERR_WORKSPACE;
   moe::FfnLaunch a{};
-  a.x_perm = x_perm; a.x_scale = x_scale; a.offsets = offsets; a.w1 = w1; a.w1_scale = w1_scale;
-  a.w2 = w2; a.w2_scale = w2_scale; a.act_gu = act_gu; a.act_h = act_h; a.h_scale = h_scale;
+  a.x_perm = x_perm; a.x_scale = static_cast<const float*>(x_scale); a.offsets = offsets; a.w1 = w1;
+  a.w1_scale = static_cast<const float*>(w1_scale); a.w2 = w2; a.w2_scale = static_cast<const float*>(w2_scale);
+  a.act_gu = act_gu; a.act_h = act_h; a.h_scale = static_cast<float*>(h_scale);
   a.out_perm = out_perm; a.ws = ws;
   a.A = cfg->num_tokens * cfg->top_k; a.d = cfg->hidden; a.f = cfg->ffn_hidden; a.E = cfg->num_experts;
   a.act = cfg->act_dtype == MOE_DTYPE_BF16 ? 1 : 0;
-  a.wt = cfg->weight_dtype == MOE_DTYPE_F32 ? 0 : (cfg->weight_dtype == MOE_DTYPE_BF16 ? 1 : 2);
+  a.wt = weight_kind(cfg);
   a.identity = identity;
   a.tile = cfg->gemm_tile;
   a.recompute = cfg->recompute;
@@ -238,14 +258,14 @@ int moe_combine_bwd(const moe_config* cfg, const void* dy, const void* out_perm,
   return launched();
 }
 
-int moe_grouped_ffn_bwd(const moe_config* cfg, const void* x_perm, const float* x_scale,
-                        const int32_t* offsets, const void* w1, const float* w1_scale, const void* w2,
-                        const float* w2_scale, const void* act_gu, const void* act_h,
-                        const float* h_scale, const void* d_out_perm, void* dx_perm, void* dw1, void* dw2,
+int moe_grouped_ffn_bwd(const moe_config* cfg, const void* x_perm, const void* x_scale,
+                        const int32_t* offsets, const void* w1, const void* w1_scale, const void* w2,
+                        const void* w2_scale, const void* act_gu, const void* act_h,
+                        const void* h_scale, const void* d_out_perm, void* dx_perm, void* dw1, void* dw2,
                         void* ws, size_t ws_bytes, void* stream) {
   MOE_CHECK(check_cfg(cfg));
   const bool identity = cfg->ffn_mode == MOE_FFN_IDENTITY;
-  const bool fp8 = cfg->weight_dtype == MOE_DTYPE_FP8_E4M3;
+  const bool fp8 = is_fp8(cfg);
   MOE_CHECK(need(d_out_perm)); MOE_CHECK(need(dx_perm)); MOE_CHECK(need(dw1)); MOE_CHECK(need(dw2));
   MOE_CHECK(need(offsets));
   if (!identity) {
@@ -263,12 +283,13 @@ int moe_grouped_ffn_bwd(const moe_config* cfg, const void* x_perm, const float* 
   if (!identity && (!ws || ws_bytes < moe_workspace_size(cfg, MOE_OP_GROUPED_FFN_BWD)))
     return MOE_ERR_WORKSPACE;
   moe::FfnBwdLaunch a{};
-  a.x_perm = x_perm; a.x_scale = x_scale; a.offsets = offsets; a.w1 = w1; a.w1_scale = w1_scale;
-  a.w2 = w2; a.w2_scale = w2_scale; a.act_gu = act_gu; a.act_h = act_h; a.h_scale = h_scale;
+  a.x_perm = x_perm; a.x_scale = static_cast<const float*>(x_scale); a.offsets = offsets; a.w1 = w1;
+  a.w1_scale = static_cast<const float*>(w1_scale); a.w2 = w2; a.w2_scale = static_cast<const float*>(w2_scale);
+  a.act_gu = act_gu; a.act_h = act_h; a.h_scale = static_cast<const float*>(h_scale);
   a.d_out = d_out_perm; a.dx_perm = dx_perm; a.dw1 = dw1; a.dw2 = dw2; a.ws = ws;
   a.A = cfg->num_tokens * cfg->top_k; a.d = cfg->hidden; a.f = cfg->ffn_hidden; a.E = cfg->num_experts;
   a.act = cfg->act_dtype == MOE_DTYPE_BF16 ? 1 : 0;
-  a.wt = cfg->weight_dtype == MOE_DTYPE_F32 ? 0 : (cfg->weight_dtype == MOE_DTYPE_BF16 ? 1 : 2);
+  a.wt = weight_kind(cfg);
   a.identity = identity;
   a.tile = cfg->gemm_tile;
   a.recompute = cfg->recompute;
@@ -357,6 +378,21 @@ int moe_quantize_fp8_blockwise(const void* src, int src_dtype, int64_t rows, int
   q.src = src; q.src_bf16 = src_dtype == MOE_DTYPE_BF16; q.rows = rows; q.cols = cols;
   q.br = block_r; q.bc = block_c; q.dst = dst; q.scale = scale;
   moe::launch_quant_blocks(q, static_cast<hipStream_t>(stream));
+  return launched();
+}
+
+int moe_quantize_mxfp8(const void* src, int src_dtype, int64_t rows, int64_t cols, int colwise, uint8_t* dst,
+                       uint8_t* e8m0, void* stream) {
+  if (src_dtype != MOE_DTYPE_F32 && src_dtype != MOE_DTYPE_BF16) return MOE_ERR_UNSUPPORTED_DTYPE;
+  if (rows < 0 || cols < 0 || (colwise != 0 && colwise != 1)) return MOE_ERR_INVALID_ARG;
+  if (colwise ? rows % 32 != 0 : cols % 32 != 0) return MOE_ERR_INVALID_ARG;
+  if (rows * cols > (int64_t(1) << 40)) return MOE_ERR_INVALID_ARG;
+  if (rows == 0 || cols == 0) return MOE_OK;
+  MOE_CHECK(need(src)); MOE_CHECK(need(dst)); MOE_CHECK(need(e8m0));
+  if (!colwise && (!aligned16(src) || !aligned16(dst))) return MOE_ERR_ALIGNMENT;
+  const bool bf16 = src_dtype == MOE_DTYPE_BF16;
+  if (colwise) moe::launch_quant_mx_cols(src, bf16, rows, cols, dst, e8m0, static_cast<hipStream_t>(stream));
+  else moe::launch_quant_mx_rows(src, bf16, rows, cols, dst, e8m0, static_cast<hipStream_t>(stream));
   return launched();
 }
 

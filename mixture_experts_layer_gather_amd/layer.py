@@ -27,8 +27,11 @@ class MoELayer:
         self.A = T * k
         self.shared = int(shared)
         self.act, self.weight = act, weight
-        self.fp8 = weight == "fp8"
+        self.mx = weight == "mxfp8"
+        self.fp8 = weight in ("fp8", "mxfp8")   # E4M3 codes, with either scale kind
         self.qb = quant_block
+        # scales: fp32 per 1 x 128 / 128 x 128 block, or E8M0 bytes per 32
+        sdt = torch.uint8 if self.mx else torch.float32
         kw = dict(score=score, renorm=renorm, gate_scale=gate_scale, num_groups=num_groups,
                   topk_groups=topk_groups, group_score=group_score, act=act, weight=weight,
                   quant_block=quant_block, identity=identity, gemm_tile=gemm_tile,
@@ -65,10 +68,10 @@ class MoELayer:
         self.act_h = self.h_scale = None
         if self.fp8:
             self.x_perm = e(A, d, dt=torch.uint8)
-            self.x_scale = e(A, d // quant_block, dt=torch.float32)
+            self.x_scale = e(A, d // quant_block, dt=sdt)
             if keep_h:
                 self.act_h = e(A, f, dt=torch.uint8)
-                self.h_scale = e(A, f // quant_block, dt=torch.float32)
+                self.h_scale = e(A, f // quant_block, dt=sdt)
         else:
             self.x_perm = e(A, d)
             self.x_scale = None
@@ -99,10 +102,10 @@ class MoELayer:
             self.s_h = self.s_h_scale = None
             if self.fp8:
                 self.s_x = e(T, d, dt=torch.uint8)
-                self.s_x_scale = e(T, d // quant_block, dt=torch.float32)
+                self.s_x_scale = e(T, d // quant_block, dt=sdt)
                 if keep_h:
                     self.s_h = e(T, f, dt=torch.uint8)
-                    self.s_h_scale = e(T, f // quant_block, dt=torch.float32)
+                    self.s_h_scale = e(T, f // quant_block, dt=sdt)
             elif keep_h:
                 self.s_h = e(T, f)
             self.s_gu = e(T, 2 * f) if keep_gu else None
@@ -122,25 +125,62 @@ class MoELayer:
         L.moe_quantize_fp8_blockwise(w, G * R, C, qb, qb, q, s)
         return q, s
 
+    def _quant_weight_mx(self, w, colwise):
+        """MXFP8 of an expert weight stack [G, R, C] (setup step): 1 x 32
+        blocks along C (rows) for the forward products, 32 x 1 blocks along
+        R (columns) for the data-gradient products; R is a multiple of 32,
+        so no block spans two experts."""
+        G, R, C = w.shape
+        q = torch.empty(G, R, C, dtype=torch.uint8, device=w.device)
+        s = torch.empty(G, R // 32, C, dtype=torch.uint8, device=w.device) if colwise else \
+            torch.empty(G, R, C // 32, dtype=torch.uint8, device=w.device)
+        L.moe_quantize_mxfp8(w, G * R, C, colwise, q, s)
+        return q, s
+
     def set_weights(self, w_router, w1, w2, bias=None, sw1=None, sw2=None):
         self.w_router = w_router
         self.bias = bias
         self.w1_master, self.w2_master = w1, w2
-        if self.fp8:
+        # the weights the backward's data-gradient products read (MXFP8:
+        # column-quantised copies; otherwise the forward's)
+        if self.mx:
+            self.w1, self.w1_scale = self._quant_weight_mx(w1, False)
+            self.w2, self.w2_scale = self._quant_weight_mx(w2, False)
+            self.w1b, self.w1b_scale = self._quant_weight_mx(w1, True)
+            self.w2b, self.w2b_scale = self._quant_weight_mx(w2, True)
+        elif self.fp8:
             self.w1, self.w1_scale = self._quant_weight(w1)
             self.w2, self.w2_scale = self._quant_weight(w2)
         else:
             self.w1, self.w2 = w1, w2
             self.w1_scale = self.w2_scale = None
+        if not self.mx:
+            self.w1b, self.w1b_scale, self.w2b, self.w2b_scale = self.w1, self.w1_scale, self.w2, self.w2_scale
         if self.shared:
             sw1 = sw1.reshape(1, *sw1.shape[-2:])
             sw2 = sw2.reshape(1, *sw2.shape[-2:])
-            if self.fp8:
+            if self.mx:
+                self.sw1, self.sw1_scale = self._quant_weight_mx(sw1, False)
+                self.sw2, self.sw2_scale = self._quant_weight_mx(sw2, False)
+                self.sw1b, self.sw1b_scale = self._quant_weight_mx(sw1, True)
+                self.sw2b, self.sw2b_scale = self._quant_weight_mx(sw2, True)
+            elif self.fp8:
                 self.sw1, self.sw1_scale = self._quant_weight(sw1)
                 self.sw2, self.sw2_scale = self._quant_weight(sw2)
             else:
                 self.sw1, self.sw2 = sw1, sw2
                 self.sw1_scale = self.sw2_scale = None
+            if not self.mx:
+                self.sw1b, self.sw1b_scale = self.sw1, self.sw1_scale
+                self.sw2b, self.sw2b_scale = self.sw2, self.sw2_scale
+
+    def quantize_shared_input(self, x):
+        """The shared expert's input in the layer's FP8 format (its rows are
+        the unpermuted tokens)."""
+        if self.mx:
+            L.moe_quantize_mxfp8(x, self.T, self.d, False, self.s_x, self.s_x_scale)
+        else:
+            L.moe_quantize_fp8_blockwise(x, self.T, self.d, 1, self.qb, self.s_x, self.s_x_scale)
 
     # ------------------------------------------------------------ passes
     def forward(self, x: torch.Tensor) -> torch.Tensor:
@@ -159,7 +199,7 @@ class MoELayer:
         if self.shared:
             sx, sxs = x, None
             if self.fp8:
-                L.moe_quantize_fp8_blockwise(x, self.T, self.d, 1, self.qb, self.s_x, self.s_x_scale)
+                self.quantize_shared_input(x)
                 sx, sxs = self.s_x, self.s_x_scale
             L.moe_grouped_ffn(self.scfg, sx, sxs, self.s_offsets, self.sw1, self.sw1_scale,
                               self.sw2, self.sw2_scale, self.s_gu, self.s_h, self.s_h_scale,
@@ -172,14 +212,14 @@ class MoELayer:
         c = self.cfg
         L.moe_combine_bwd(c, dy, self.out_perm, self.row_id_map, self.topk_gate, self.d_out_perm,
                           self.d_gate)
-        L.moe_grouped_ffn_bwd(c, self.x_perm, self.x_scale, self.offsets, self.w1, self.w1_scale,
-                              self.w2, self.w2_scale, self.act_gu, self.act_h, self.h_scale,
+        L.moe_grouped_ffn_bwd(c, self.x_perm, self.x_scale, self.offsets, self.w1b, self.w1b_scale,
+                              self.w2b, self.w2b_scale, self.act_gu, self.act_h, self.h_scale,
                               self.d_out_perm, self.dx_perm, self.dw1, self.dw2, self.ws_ffn_bwd)
         dx_add = None
         if self.shared:
             sx, sxs = (self.s_x, self.s_x_scale) if self.fp8 else (self.x, None)
-            L.moe_grouped_ffn_bwd(self.scfg, sx, sxs, self.s_offsets, self.sw1, self.sw1_scale,
-                                  self.sw2, self.sw2_scale, self.s_gu, self.s_h, self.s_h_scale,
+            L.moe_grouped_ffn_bwd(self.scfg, sx, sxs, self.s_offsets, self.sw1b, self.sw1b_scale,
+                                  self.sw2b, self.sw2b_scale, self.s_gu, self.s_h, self.s_h_scale,
                                   dy, self.s_dx, self.s_dw1, self.s_dw2, self.ws_ffn_bwd)
             dx_add = self.s_dx
         L.moe_dispatch_bwd(c, self.dx_perm, self.row_id_map, dx_add, self.dx)

@@ -659,25 +659,32 @@ def rel_l2(a, b) -> float:
     return float(na / nb)
 
 
-def ffn_wgrad_columns(X, W1, W2, dO, cols, h_fp8: bool = False):
+def ffn_wgrad_columns(X, W1, W2, dO, cols, h_fp8: bool = False, quant=None, W2d=None):
     """Selected slices of one expert's weight gradients, over all its rows:
     for each hidden feature n in `cols`, rows n (gate) and f+n (up) of dW1
     and column n of dW2 — the same formulas as ffn_bwd evaluated only where
-    asked (fp64). Returns (dW1_rows [2*len(cols), d] ordered gate rows then
-    up rows, dW2_cols [d, len(cols)])."""
+    asked (fp64). FP8 layers (h_fp8: 1 x 128 blocks; or quant, the
+    quantise-dequantise of the layer's format) quantise H in the forward and
+    dO before the dH product, which reads W2d (the weights of the data
+    gradients; W2 by default), as ffn_fwd and ffn_bwd do. Returns (dW1_rows
+    [2*len(cols), d] ordered gate rows then up rows, dW2_cols [d, len(cols)])."""
     X = np.asarray(X, dtype=np.float64)
     W1 = np.asarray(W1, dtype=np.float64)
     W2 = np.asarray(W2, dtype=np.float64)
+    W2d = W2 if W2d is None else np.asarray(W2d, dtype=np.float64)
     dO = np.asarray(dO, dtype=np.float64)
+    if h_fp8 and quant is None:
+        quant = fp8_roundtrip_rows
     f = W2.shape[1]
     cols = np.asarray(cols, dtype=np.int64)
     G = X @ W1[cols].T                     # [M, c]
     U = X @ W1[f + cols].T
-    dH = dO @ W2[:, cols]                  # [M, c]
+    dOq = quant(dO.astype(np.float32)) if quant else dO
+    dH = dOq @ W2d[:, cols]                # [M, c]
     s = sigmoid64(G)
     H = G * s * U
-    if h_fp8:  # the forward's H is quantised per 1x128 block of the full row
-        H = ffn_fwd(X, W1, W2, h_fp8=True)[1][:, cols]
+    if quant:  # the forward's H is quantised in blocks of the full row
+        H = ffn_fwd(X, W1, W2, h_quant=quant)[1][:, cols]
     dG = dH * U * s * (1.0 + G * (1.0 - s))
     dU = dH * G * s
     dW1_rows = np.concatenate([dG.T @ X, dU.T @ X], axis=0)
@@ -685,7 +692,10 @@ def ffn_wgrad_columns(X, W1, W2, dO, cols, h_fp8: bool = False):
     return dW1_rows, dW2_cols
 
 
-def ffn_dx_rows(X, W1, W2, dO, fp8: bool = False):
-    """dX for the given rows of one expert (fp64), as in ffn_bwd."""
-    GU, H, _ = ffn_fwd(X, W1, W2, h_fp8=fp8)
-    return ffn_bwd(X, W1, W2, GU, H, dO, dgrad_fp8=fp8)[0]
+def ffn_dx_rows(X, W1, W2, dO, fp8: bool = False, quant=None, W1d=None, W2d=None):
+    """dX for the given rows of one expert (fp64), as in ffn_bwd (FP8: fp8
+    for 1 x 128 blocks, or quant and the data-gradient weights W1d, W2d)."""
+    if fp8 and quant is None:
+        quant = fp8_roundtrip_rows
+    GU, H, _ = ffn_fwd(X, W1, W2, h_quant=quant)
+    return ffn_bwd(X, W1, W2, GU, H, dO, dgrad_quant=quant, W1d=W1d, W2d=W2d)[0]

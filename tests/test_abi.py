@@ -27,7 +27,7 @@ def _declared():
 
 def test_exports_every_declared_symbol(M):
     names = _declared()
-    assert len(names) == 12, names
+    assert len(names) == 13, names
     L = M.lib()
     for n in names:
         assert hasattr(L, n), n
@@ -183,3 +183,27 @@ def test_recompute_modes(M):
         if mode != "none":
             assert ffn(c1, FAKE, None, None, None, 0) == -4
             assert ffn_bwd(c1, FAKE, None, None, None, 0) == -4
+
+
+def test_mxfp8_config_and_quantiser_arguments(M):
+    L = M.lib()
+    c = _cfg(M, weight="mxfp8", quant_block=32, T=0)
+    assert _route(M, c) == 0
+    assert _route(M, _cfg(M, weight="mxfp8", quant_block=128)) == -1
+    assert _route(M, _cfg(M, act="f32", weight="mxfp8", quant_block=32)) == -2
+    # the backward holds the column-quantised weights only: no GEMM1 rerun
+    assert _route(M, _cfg(M, weight="mxfp8", quant_block=32, recompute="full")) == -2
+    assert _route(M, _cfg(M, weight="mxfp8", quant_block=32, recompute="act", T=0)) == 0
+    # E8M0 scales take as many bytes as the fp32 1 x 128 scales: same workspace
+    cm = _cfg(M, T=1000, E=16, k=4, f=384, d=512, weight="mxfp8", quant_block=32)
+    cf = _cfg(M, T=1000, E=16, k=4, f=384, d=512, weight="fp8")
+    for op in (1, 2, 3):
+        assert L.moe_workspace_size(ctypes.byref(cm), op) == L.moe_workspace_size(ctypes.byref(cf), op)
+    q = L.moe_quantize_mxfp8
+    assert q(FAKE, 7, 32, 32, 0, FAKE, FAKE, None) == -2          # dtype
+    assert q(FAKE, 1, 32, 48, 0, FAKE, FAKE, None) == -1          # cols % 32 (rows mode)
+    assert q(FAKE, 1, 48, 32, 1, FAKE, FAKE, None) == -1          # rows % 32 (column mode)
+    assert q(FAKE, 1, 32, 32, 2, FAKE, FAKE, None) == -1          # colwise flag
+    assert q(None, 1, 32, 32, 0, FAKE, FAKE, None) == -1          # NULL
+    assert q(FAKE + 4, 1, 32, 32, 0, FAKE, FAKE, None) == -3      # alignment (rows mode)
+    assert q(FAKE, 1, 0, 32, 0, None, None, None) == 0            # empty: nothing to do

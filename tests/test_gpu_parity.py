@@ -30,7 +30,7 @@ def _say(msg):
 
 
 def _tol(cfg):
-    return TOL["fp8"] if cfg.weight == "fp8" else TOL[cfg.act]
+    return TOL["fp8"] if cfg.weight in ("fp8", "mxfp8") else TOL[cfg.act]
 
 
 def _np(t):
@@ -78,7 +78,7 @@ def _compare_small(cfg, identity=False, inp=None, gemm_tile="auto"):
     layer = _gpu_layer(cfg, inp, identity, gemm_tile)
     ref = oracle.layer(cfg, inp, identity=identity)
     _check_routing_and_dispatch(cfg, layer, ref)
-    if cfg.weight == "fp8":
+    if cfg.weight in ("fp8", "mxfp8"):
         assert np.array_equal(_np(layer.x_perm), ref["xq_perm"]), "fp8 dispatch codes"
         assert np.array_equal(_np(layer.x_scale), ref["x_scale_perm"]), "fp8 dispatch scales"
     else:
@@ -130,6 +130,8 @@ SMALL = {
     # and ragged groups smaller than a tile
     "qwen_skew_mini_big": S.mini(S.CONFIGS[3], T=700, d=256, f=128, E=16).replace(k=4, seed_base=34),
     "deepseek_fp8_mini": S.mini(S.CONFIGS[4], T=400, d=384, f=256, E=32).replace(k=6),
+    # MXFP8: 1 x 32 / 32 x 1 blocks with E8M0 scales on the matrix cores
+    "deepseek_mxfp8_mini": S.mini(S.BY_NAME["deepseek_v3_mxfp8"], T=400, d=384, f=256, E=32).replace(k=6),
     # the load-balancing auxiliary loss on (coefficient 0.01): its value and
     # its share of the router gradient
     "mixtral_mini_aux": S.mini(S.CONFIGS[1], T=1000, d=256, f=384).replace(aux_coeff=0.01),
@@ -235,6 +237,34 @@ def test_fp8_encoder_exhaustive_in_range():
             torch.cuda.synchronize()
             assert np.all(_np(sc) == 1.0)
             assert np.array_equal(_np(q), oracle.e4m3_encode(v)), hex(lo | sign)
+
+
+def test_mxfp8_quantiser_bit_exact():
+    """moe_quantize_mxfp8 in both block orientations against the oracle:
+    codes and E8M0 bytes bit for bit, over blocks whose magnitudes span the
+    fp32 range (zero blocks, lone subnormals, values at powers of two)."""
+    from mixture_experts_layer_gather_amd import moe_quantize_mxfp8
+    g = torch.Generator().manual_seed(12)
+    R, C = 256, 640
+    src = torch.randn(R, C, generator=g) * torch.exp(torch.randn(R, 1, generator=g) * 12)
+    src[:, 5] *= torch.exp(torch.randn(R, generator=g) * 20)     # one outlier column
+    src[3, :32] = 0.0
+    src[:32, 100] = 0.0
+    src[4, 32:64] = 0.0
+    src[4, 40] = -2.0e-40                                        # an fp32 subnormal alone
+    src[5, :32] = torch.tensor([2.0 ** i for i in range(-16, 16)])
+    src[6, :] = 448.0 * 2.0 ** 30
+    for dt in (torch.float32, torch.bfloat16):
+        s = src.to(dt)
+        s32 = s.float().numpy()
+        for colwise in (False, True):
+            q = torch.empty(R, C, dtype=torch.uint8, device=DEV)
+            e = torch.empty((R // 32, C) if colwise else (R, C // 32), dtype=torch.uint8, device=DEV)
+            moe_quantize_mxfp8(s.to(DEV), R, C, colwise, q, e)
+            torch.cuda.synchronize()
+            rq, re = (oracle.quant_mx_cols if colwise else oracle.quant_mx_rows)(s32)
+            assert np.array_equal(_np(e), re), (dt, colwise, "scales")
+            assert np.array_equal(_np(q), rq), (dt, colwise, "codes")
 
 
 def test_fp8_dispatch_bit_exact():
@@ -344,8 +374,10 @@ def _full_size_check(cfg, n_tok=24, n_cols=3):
                perm_token=ptok)
     _check_routing_and_dispatch(cfg, layer, ref)
     # dispatched rows: x_perm == x[perm_token], checked on the device
-    if cfg.weight == "fp8":
-        xq, xs = oracle.quant_blocks(oracle.as_f32(inp["x"]), 1, 128)
+    mx = cfg.weight == "mxfp8"
+    if cfg.weight in ("fp8", "mxfp8"):
+        xq, xs = (oracle.quant_mx_rows if mx else lambda a: oracle.quant_blocks(a, 1, 128))(
+            oracle.as_f32(inp["x"]))
         assert np.array_equal(_np(layer.x_perm), xq[ptok]), "fp8 x_perm codes"
         assert np.array_equal(_np(layer.x_scale), xs[ptok]), "fp8 x_perm scales"
     else:
@@ -357,25 +389,33 @@ def _full_size_check(cfg, n_tok=24, n_cols=3):
     # 128 x 128, dequantised exactly)
     _say(f"[full] {cfg.name}: oracle forward")
     fp8 = cfg.weight == "fp8"
+    quant = oracle.mx_roundtrip_rows if mx else (oracle.fp8_roundtrip_rows if fp8 else None)
     X = oracle.as_f64(inp["x"])
-    if fp8:
-        X = oracle.fp8_roundtrip_rows(oracle.as_f32(inp["x"]))
+    if quant:
+        X = quant(oracle.as_f32(inp["x"]))
 
     def W(w):
+        if mx:
+            return oracle.dequant_mx_rows(*oracle.quant_mx_rows(oracle.as_f32(w)))
         if not fp8:
             return oracle.as_f64(w)
         q, sc = oracle.quant_blocks(oracle.as_f32(w), 128, 128)
         return oracle.dequant_blocks(q, sc, 128, 128)
 
+    def Wd(w):  # the data-gradient products' weights (MXFP8: 32 x 1 blocks)
+        return oracle.dequant_mx_cols(*oracle.quant_mx_cols(oracle.as_f32(w))) if mx else None
+
     O = np.zeros((cfg.A, cfg.d))
     for e in range(cfg.E):
         r0, r1 = offsets[e], offsets[e + 1]
         if r1 > r0:
-            O[r0:r1] = oracle.ffn_fwd(X[ptok[r0:r1]], W(inp["w1"][e]), W(inp["w2"][e]), h_fp8=fp8)[2]
+            O[r0:r1] = oracle.ffn_fwd(X[ptok[r0:r1]], W(inp["w1"][e]), W(inp["w2"][e]), h_quant=quant)[2]
+        if e % 32 == 31:
+            _say(f"[full] {cfg.name}: oracle forward, {e + 1} experts done")
     O_sh = None
     if cfg.shared:
         SW1, SW2 = W(inp["sw1"]), W(inp["sw2"])
-        O_sh = oracle.ffn_fwd(X, SW1, SW2, h_fp8=fp8)[2]
+        O_sh = oracle.ffn_fwd(X, SW1, SW2, h_quant=quant)[2]
     y = oracle.combine(O, rmap, g, O_sh)
     err = oracle.rel_l2(_np(layer.y), y)
     _say(f"[full] {cfg.name}: y rel L2 {err:.2e}")
@@ -397,13 +437,17 @@ def _full_size_check(cfg, n_tok=24, n_cols=3):
     for ti, t in enumerate(toks):
         for j in range(cfg.k):
             by_e.setdefault(int(idx[t, j]), []).append((ti, int(rmap[t, j])))
-    for e, lst in by_e.items():
+    for n_e, (e, lst) in enumerate(by_e.items()):
+        if n_e % 32 == 31:
+            _say(f"[full] {cfg.name}: oracle dx, {n_e + 1} of {len(by_e)} experts")
         tis = np.array([a for a, _ in lst])
         rs = np.array([b for _, b in lst])
-        dxe = oracle.ffn_dx_rows(X[toks[tis]], W(inp["w1"][e]), W(inp["w2"][e]), dO[rs], fp8=fp8)
+        dxe = oracle.ffn_dx_rows(X[toks[tis]], W(inp["w1"][e]), W(inp["w2"][e]), dO[rs], quant=quant,
+                                 W1d=Wd(inp["w1"][e]), W2d=Wd(inp["w2"][e]))
         np.add.at(dx_s, tis, dxe)
     if cfg.shared:
-        dx_s += oracle.ffn_dx_rows(X[toks], SW1, SW2, dy[toks], fp8=fp8)
+        dx_s += oracle.ffn_dx_rows(X[toks], SW1, SW2, dy[toks], quant=quant, W1d=Wd(inp["sw1"]),
+                                   W2d=Wd(inp["sw2"]))
     err = oracle.rel_l2(_np(layer.dx[torch.as_tensor(toks)]), dx_s)
     _say(f"[full] {cfg.name}: dx (sampled) rel L2 {err:.2e}")
     assert err <= tol, "dx"
@@ -413,7 +457,7 @@ def _full_size_check(cfg, n_tok=24, n_cols=3):
         cols = np.sort(rng.choice(cfg.f, n_cols, replace=False))
         r0, r1 = offsets[e], offsets[e + 1]
         w1r, w2c = oracle.ffn_wgrad_columns(X[ptok[r0:r1]], W(inp["w1"][e]), W(inp["w2"][e]),
-                                            dO[r0:r1], cols, h_fp8=fp8)
+                                            dO[r0:r1], cols, quant=quant, W2d=Wd(inp["w2"][e]))
         rows = torch.as_tensor(np.concatenate([cols, cfg.f + cols]))
         got1 = _np(layer.dw1[e][rows])
         got2 = _np(layer.dw2[e][:, torch.as_tensor(cols)])
@@ -425,9 +469,12 @@ def _full_size_check(cfg, n_tok=24, n_cols=3):
         assert not _np(layer.dw1[int(empty[0])]).any() and not _np(layer.dw2[int(empty[0])]).any()
 
 
-@pytest.mark.parametrize("which", [1, 2, 3, 4])
+@pytest.mark.parametrize("which", [1, 2, 3, 4, "deepseek_v3_mxfp8"])
 def test_full_size_layer(which):
-    _full_size_check(S.CONFIGS[which])
+    if isinstance(which, int):
+        _full_size_check(S.CONFIGS[which])
+    else:  # MXFP8: the oracle also quantises each sampled expert's weights in columns
+        _full_size_check(S.BY_NAME[which], n_tok=8)
 
 
 # ------------------------------------------------ load-balancing aux loss

@@ -58,7 +58,8 @@ RECOMPUTE_CASES = [("tiny_fp32", "act"), ("tiny_fp32", "full"),
                    ("mixtral_mini", "act"), ("mixtral_mini", "full"),
                    ("qwen_skew_mini_big", "act"), ("qwen_skew_mini_big", "full"),
                    ("deepseek_mini", "act"), ("deepseek_mini", "full"),
-                   ("deepseek_fp8_mini", "act"), ("deepseek_fp8_mini", "full")]
+                   ("deepseek_fp8_mini", "act"), ("deepseek_fp8_mini", "full"),
+                   ("deepseek_mxfp8_mini", "act")]
 
 
 @pytest.mark.parametrize("name,mode", RECOMPUTE_CASES)
@@ -77,12 +78,12 @@ def test_recompute_matches_saved_activations(name, mode):
     _same(_outputs(base), _outputs(rc), f"{name} recompute={mode}")
 
 
-@pytest.mark.parametrize("name", ["tiny_fp32", "mixtral_mini", "deepseek_fp8_mini"])
+@pytest.mark.parametrize("name", ["tiny_fp32", "mixtral_mini", "deepseek_fp8_mini", "deepseek_mxfp8_mini"])
 def test_recompute_against_oracle(name):
     cfg = SMALL[name]
     inp = _inputs(cfg)
     _say(f"[recompute-oracle] {name}")
-    layer = _layer(cfg, inp, "full")
+    layer = _layer(cfg, inp, "act" if cfg.weight == "mxfp8" else "full")
     layer.step(inp["x"].to(DEV), inp["dy"].to(DEV))
     torch.cuda.synchronize()
     ref = oracle.layer(cfg, inp)
@@ -107,7 +108,7 @@ def _scribble(layer, outs):
 
 GRAPH_CASES = [("mixtral_mini", "none"), ("qwen_skew_mini", "none"), ("tiny_fp32_aux", "none"),
                ("deepseek_fp8_mini", "none"), ("deepseek_mini_aux", "full"),
-               ("mixtral_mini", "act")]
+               ("mixtral_mini", "act"), ("deepseek_mxfp8_mini", "none")]
 
 
 @pytest.mark.parametrize("name,mode", GRAPH_CASES)

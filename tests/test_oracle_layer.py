@@ -316,3 +316,40 @@ def test_mxfp8_column_blocks_feed_only_the_data_gradients(monkeypatch):
     assert oracle.rel_l2(out["dw1"], 2 * base["dw1"]) < 1e-6
     assert oracle.rel_l2(out["dx_perm"], 4 * base["dx_perm"]) < 1e-6
     assert oracle.rel_l2(out["shared_dx"], 4 * base["shared_dx"]) < 1e-6
+
+
+@pytest.mark.parametrize("which", ["bf16", "fp8", "mxfp8"])
+def test_sampled_gradient_helpers_match_the_full_layer(which):
+    """The slice-by-slice helpers the full-size GPU tests use (dX rows, dW1
+    rows and dW2 columns of one expert) equal the full oracle's tensors."""
+    base = S.mini(S.CONFIGS[4], T=24, d=256, f=256, E=4).replace(num_groups=2, topk_groups=1, k=2)
+    cfg = {"bf16": base.replace(weight="bf16"), "fp8": base,
+           "mxfp8": base.replace(weight="mxfp8", quant_block=32)}[which]
+    inp = _inputs(cfg)
+    out = oracle.layer(cfg, inp)
+    fp8, mx = which == "fp8", which == "mxfp8"
+    x32 = oracle.as_f32(inp["x"])
+    X = (oracle.mx_roundtrip_rows(x32) if mx else
+         oracle.fp8_roundtrip_rows(x32) if fp8 else x32.astype(np.float64))
+    quant = oracle.mx_roundtrip_rows if mx else (oracle.fp8_roundtrip_rows if fp8 else None)
+    ptok, offs = out["perm_token"], out["offsets"]
+    e = int(np.argmax(out["counts"]))
+    r0, r1 = offs[e], offs[e + 1]
+    if mx:
+        w1, w2 = oracle.as_f32(inp["w1"][e]), oracle.as_f32(inp["w2"][e])
+        W1, W2 = oracle.dequant_mx_rows(*oracle.quant_mx_rows(w1)), oracle.dequant_mx_rows(*oracle.quant_mx_rows(w2))
+        W1d, W2d = oracle.dequant_mx_cols(*oracle.quant_mx_cols(w1)), oracle.dequant_mx_cols(*oracle.quant_mx_cols(w2))
+    elif fp8:
+        W1 = oracle.dequant_blocks(*oracle.quant_blocks(oracle.as_f32(inp["w1"][e]), 128, 128), 128, 128)
+        W2 = oracle.dequant_blocks(*oracle.quant_blocks(oracle.as_f32(inp["w2"][e]), 128, 128), 128, 128)
+        W1d, W2d = None, None
+    else:
+        W1, W2, W1d, W2d = oracle.as_f64(inp["w1"][e]), oracle.as_f64(inp["w2"][e]), None, None
+    dO = out["d_out_perm"][r0:r1]
+    dx = oracle.ffn_dx_rows(X[ptok[r0:r1]], W1, W2, dO, quant=quant, W1d=W1d, W2d=W2d)
+    assert np.allclose(dx, out["dx_perm"][r0:r1], rtol=1e-10, atol=1e-14)
+    cols = np.array([0, 5, 77, 255])
+    w1r, w2c = oracle.ffn_wgrad_columns(X[ptok[r0:r1]], W1, W2, dO, cols, quant=quant, W2d=W2d)
+    f = cfg.f
+    assert np.allclose(w1r, out["dw1"][e][np.concatenate([cols, f + cols])], rtol=1e-10, atol=1e-14)
+    assert np.allclose(w2c, out["dw2"][e][:, cols], rtol=1e-10, atol=1e-14)
