@@ -130,6 +130,12 @@ SMALL = {
     # and ragged groups smaller than a tile
     "qwen_skew_mini_big": S.mini(S.CONFIGS[3], T=700, d=256, f=128, E=16).replace(k=4, seed_base=34),
     "deepseek_fp8_mini": S.mini(S.CONFIGS[4], T=400, d=384, f=256, E=32).replace(k=6),
+    # the other group rule (a group's best score instead of its best two)
+    # and sigmoid gates without renormalisation
+    "deepseek_mini_gmax": S.mini(S.CONFIGS[2], T=300, d=256, f=256, E=32).replace(
+        k=6, group_score="max", seed_base=61),
+    "deepseek_mini_norenorm": S.mini(S.CONFIGS[2], T=300, d=256, f=256, E=32).replace(
+        k=6, renorm=False, gate_scale=1.0, seed_base=62),
     # MXFP8: 1 x 32 / 32 x 1 blocks with E8M0 scales on the matrix cores
     "deepseek_mxfp8_mini": S.mini(S.BY_NAME["deepseek_v3_mxfp8"], T=400, d=384, f=256, E=32).replace(k=6),
     # the load-balancing auxiliary loss on (coefficient 0.01): its value and
