@@ -230,61 +230,12 @@ def make_layer(cfg, device, recompute="none"):
 
 
 def timed_step(layer, x, dy, marks):
-    """One fwd+bwd step with an event after every library call (events are
-    recorded on the stream the library launches on: torch's current one)."""
-    import mixture_experts_layer_gather_amd._lib as L
+    """One fwd+bwd step with an event after every library call, on torch's
+    current stream (where the library launches)."""
     rec = lambda name: marks.append((name, _event()))
-    c = layer.cfg
-    layer.x = x
     rec("start")
-    L.moe_route(c, x, layer.w_router, layer.bias, layer.logits, layer.topk_idx, layer.topk_gate,
-                layer.routing_map)
-    rec("route")
-    if layer.aux:
-        L.moe_route_aux_loss(c, layer.logits, layer.topk_idx, layer.aux_loss, layer.ws_aux)
-        rec("aux_loss")
-    L.moe_dispatch(c, x, layer.topk_idx, layer.counts, layer.offsets, layer.row_id_map,
-                   layer.perm_token, layer.x_perm, layer.x_scale, layer.ws_dispatch)
-    rec("dispatch")
-    L.moe_grouped_ffn(c, layer.x_perm, layer.x_scale, layer.offsets, layer.w1, layer.w1_scale,
-                      layer.w2, layer.w2_scale, layer.act_gu, layer.act_h, layer.h_scale,
-                      layer.out_perm, layer.ws_ffn)
-    rec("grouped_ffn")
-    shared_out = None
-    if layer.shared:
-        sx, sxs = x, None
-        if layer.fp8:
-            layer.quantize_shared_input(x)
-            sx, sxs = layer.s_x, layer.s_x_scale
-        L.moe_grouped_ffn(layer.scfg, sx, sxs, layer.s_offsets, layer.sw1, layer.sw1_scale,
-                          layer.sw2, layer.sw2_scale, layer.s_gu, layer.s_h, layer.s_h_scale,
-                          layer.s_out, layer.ws_ffn)
-        shared_out = layer.s_out
-        rec("shared_ffn")
-    L.moe_combine(c, layer.out_perm, layer.row_id_map, layer.topk_gate, shared_out, layer.y)
-    rec("combine")
-    L.moe_combine_bwd(c, dy, layer.out_perm, layer.row_id_map, layer.topk_gate, layer.d_out_perm,
-                      layer.d_gate)
-    rec("combine_bwd")
-    L.moe_grouped_ffn_bwd(c, layer.x_perm, layer.x_scale, layer.offsets, layer.w1b,
-                          layer.w1b_scale, layer.w2b, layer.w2b_scale, layer.act_gu, layer.act_h,
-                          layer.h_scale, layer.d_out_perm, layer.dx_perm, layer.dw1, layer.dw2,
-                          layer.ws_ffn_bwd)
-    rec("grouped_ffn_bwd")
-    dx_add = None
-    if layer.shared:
-        sx, sxs = (layer.s_x, layer.s_x_scale) if layer.fp8 else (x, None)
-        L.moe_grouped_ffn_bwd(layer.scfg, sx, sxs, layer.s_offsets, layer.sw1b, layer.sw1b_scale,
-                              layer.sw2b, layer.sw2b_scale, layer.s_gu, layer.s_h, layer.s_h_scale,
-                              dy, layer.s_dx, layer.s_dw1, layer.s_dw2, layer.ws_ffn_bwd)
-        dx_add = layer.s_dx
-        rec("shared_ffn_bwd")
-    L.moe_dispatch_bwd(c, layer.dx_perm, layer.row_id_map, dx_add, layer.dx)
-    rec("dispatch_bwd")
-    L.moe_route_bwd(c, x, layer.w_router, layer.logits, layer.topk_idx, layer.topk_gate,
-                    layer.d_gate, layer.dx, layer.dw_router, layer.ws_route_bwd,
-                    d_aux=layer.d_aux if layer.aux else None)
-    rec("route_bwd")
+    layer.forward(x, mark=rec)
+    layer.backward(dy, mark=rec)
 
 
 def graph_replay(layer, x, dy, warmup, steps, T):

@@ -183,49 +183,70 @@ class MoELayer:
             L.moe_quantize_fp8_blockwise(x, self.T, self.d, 1, self.qb, self.s_x, self.s_x_scale)
 
     # ------------------------------------------------------------ passes
-    def forward(self, x: torch.Tensor) -> torch.Tensor:
+    def _shared_fwd(self, x):
+        sx, sxs = x, None
+        if self.fp8:
+            self.quantize_shared_input(x)
+            sx, sxs = self.s_x, self.s_x_scale
+        L.moe_grouped_ffn(self.scfg, sx, sxs, self.s_offsets, self.sw1, self.sw1_scale,
+                          self.sw2, self.sw2_scale, self.s_gu, self.s_h, self.s_h_scale,
+                          self.s_out, self.ws_ffn)
+
+    def _shared_bwd(self, dy):
+        sx, sxs = (self.s_x, self.s_x_scale) if self.fp8 else (self.x, None)
+        L.moe_grouped_ffn_bwd(self.scfg, sx, sxs, self.s_offsets, self.sw1b, self.sw1b_scale,
+                              self.sw2b, self.sw2b_scale, self.s_gu, self.s_h, self.s_h_scale,
+                              dy, self.s_dx, self.s_dw1, self.s_dw2, self.ws_ffn_bwd)
+
+    def forward(self, x: torch.Tensor, mark=None) -> torch.Tensor:
+        """mark(name), when given, is called after each library call (the
+        benchmark records an event on the current stream there)."""
+        mark = mark or (lambda name: None)
         self.x = x
         c = self.cfg
         L.moe_route(c, x, self.w_router, self.bias, self.logits, self.topk_idx, self.topk_gate,
                     self.routing_map)
+        mark("route")
         if self.aux:
             L.moe_route_aux_loss(c, self.logits, self.topk_idx, self.aux_loss, self.ws_aux)
+            mark("aux_loss")
         L.moe_dispatch(c, x, self.topk_idx, self.counts, self.offsets, self.row_id_map,
                        self.perm_token, self.x_perm, self.x_scale, self.ws_dispatch)
+        mark("dispatch")
         L.moe_grouped_ffn(c, self.x_perm, self.x_scale, self.offsets, self.w1, self.w1_scale,
                           self.w2, self.w2_scale, self.act_gu, self.act_h, self.h_scale,
                           self.out_perm, self.ws_ffn)
+        mark("grouped_ffn")
         shared_out = None
         if self.shared:
-            sx, sxs = x, None
-            if self.fp8:
-                self.quantize_shared_input(x)
-                sx, sxs = self.s_x, self.s_x_scale
-            L.moe_grouped_ffn(self.scfg, sx, sxs, self.s_offsets, self.sw1, self.sw1_scale,
-                              self.sw2, self.sw2_scale, self.s_gu, self.s_h, self.s_h_scale,
-                              self.s_out, self.ws_ffn)
+            self._shared_fwd(x)
+            mark("shared_ffn")
             shared_out = self.s_out
         L.moe_combine(c, self.out_perm, self.row_id_map, self.topk_gate, shared_out, self.y)
+        mark("combine")
         return self.y
 
-    def backward(self, dy: torch.Tensor) -> torch.Tensor:
+    def backward(self, dy: torch.Tensor, mark=None) -> torch.Tensor:
+        mark = mark or (lambda name: None)
         c = self.cfg
         L.moe_combine_bwd(c, dy, self.out_perm, self.row_id_map, self.topk_gate, self.d_out_perm,
                           self.d_gate)
+        mark("combine_bwd")
         L.moe_grouped_ffn_bwd(c, self.x_perm, self.x_scale, self.offsets, self.w1b, self.w1b_scale,
                               self.w2b, self.w2b_scale, self.act_gu, self.act_h, self.h_scale,
                               self.d_out_perm, self.dx_perm, self.dw1, self.dw2, self.ws_ffn_bwd)
+        mark("grouped_ffn_bwd")
         dx_add = None
         if self.shared:
-            sx, sxs = (self.s_x, self.s_x_scale) if self.fp8 else (self.x, None)
-            L.moe_grouped_ffn_bwd(self.scfg, sx, sxs, self.s_offsets, self.sw1b, self.sw1b_scale,
-                                  self.sw2b, self.sw2b_scale, self.s_gu, self.s_h, self.s_h_scale,
-                                  dy, self.s_dx, self.s_dw1, self.s_dw2, self.ws_ffn_bwd)
+            self._shared_bwd(dy)
+            mark("shared_ffn_bwd")
             dx_add = self.s_dx
         L.moe_dispatch_bwd(c, self.dx_perm, self.row_id_map, dx_add, self.dx)
+        mark("dispatch_bwd")
         L.moe_route_bwd(c, self.x, self.w_router, self.logits, self.topk_idx, self.topk_gate,
                         self.d_gate, self.dx, self.dw_router, self.ws_route_bwd,
                         d_aux=self.d_aux if self.aux else None)
+        mark("route_bwd")
         return self.dx
 
     def step(self, x, dy):
