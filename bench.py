@@ -468,17 +468,26 @@ def main():
                      "TFLOPs": round(fl / t / 1e9, 1) if fl else 0.0}
     dom = max(per_ms, key=per_ms.get)
     b, fl = work[dom]
+    # the binding roofline of the dominant call: its flops at the matrix
+    # cores' peak or its algorithmic bytes at the HBM peak, whichever takes
+    # longer (the expert FFN of 256-expert layers streams more weight bytes
+    # than it has flops to hide them behind)
+    mfma_bound = fl and fl / (MFMA_PEAK_TFLOPS[dt] * 1e12) >= b / (HBM_PEAK_GBPS * 1e9)
     if "ffn" in dom:
-        ach = fl / per_ms[dom] / 1e9
         traffic = measured_traffic(cfg.name, dom)
-        roof = {"kernel": f"moe_{dom.replace('shared_', 'grouped_')} ({dom})", "bound": "mfma",
-                "achieved": round(ach, 1), "peak": MFMA_PEAK_TFLOPS[dt], "unit": "TFLOP/s",
-                "frac": round(ach / MFMA_PEAK_TFLOPS[dt], 4),
-                "traffic": None if traffic is None else round(traffic)}
+        traffic = None if traffic is None else round(traffic)
+        kname = f"moe_{dom.replace('shared_', 'grouped_')} ({dom})"
+    else:
+        traffic, kname = None, dom
+    if mfma_bound:
+        ach = fl / per_ms[dom] / 1e9
+        roof = {"kernel": kname, "bound": "mfma", "achieved": round(ach, 1), "peak": MFMA_PEAK_TFLOPS[dt],
+                "unit": "TFLOP/s", "frac": round(ach / MFMA_PEAK_TFLOPS[dt], 4), "traffic": traffic}
     else:
         ach = b / per_ms[dom] / 1e6
-        roof = {"kernel": dom, "bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBPS,
-                "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBPS, 4), "traffic": None}
+        roof = {"kernel": kname, "bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBPS,
+                "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBPS, 4), "traffic": traffic,
+                "algorithmic_bytes": round(b)}
 
     ffn_f = sum(work[n][1] for n in per_ms if "ffn" in n)
     ffn_t = sum(per_ms[n] for n in per_ms if "ffn" in n)
