@@ -31,7 +31,11 @@
  *    device-to-host copy, no host read of counts or offsets.
  *  - All argument checks run on the host before any launch; on failure a
  *    negative MOE_ERR_* code is returned and nothing is enqueued.
- *    num_tokens == 0 is valid and enqueues nothing.
+ *  - num_tokens == 0 is valid. Buffers with T or A rows may then be NULL
+ *    and are not touched; outputs whose size does not depend on T get their
+ *    exact values, by a fill kernel: zero counts and offsets (moe_dispatch),
+ *    zero weight gradients (moe_grouped_ffn_bwd, moe_route_bwd), a zero
+ *    auxiliary loss. Every other call enqueues nothing.
  *  - Outputs are overwritten unless marked "+=". For the same inputs every
  *    output is bitwise identical from run to run (no floating-point atomics).
  *  - The library keeps no global state; calls are thread-safe.
@@ -266,7 +270,7 @@ int moe_dispatch_bwd(const moe_config *cfg, const void *dx_perm,
  * constant of the selection. fp32 throughout, fixed summation order
  * (deterministic). Entries of topk_idx outside [0,E) are not counted.
  *   logits [T,E] f32, topk_idx [T,k] i32 (from moe_route)
- * out: aux_loss [1] f32 (device). T = 0 writes nothing.
+ * out: aux_loss [1] f32 (device). T = 0 writes 0 (no tokens, no imbalance).
  * Requires aux_coeff != 0 (else MOE_ERR_INVALID_ARG).
  * Workspace: moe_workspace_size(cfg, MOE_OP_AUX_LOSS). */
 int moe_route_aux_loss(const moe_config *cfg, const float *logits,

@@ -1251,6 +1251,8 @@ static void zero_bytes(void* dst, int64_t bytes, hipStream_t st) {
   if (n > 0) zero_kernel<<<1024, 256, 0, st>>>(reinterpret_cast<uint32_t*>(dst), n);
 }
 
+void launch_zero(void* dst, int64_t bytes, hipStream_t st) { zero_bytes(dst, bytes, st); }
+
 // Workspace layout of the grouped FFN calls (byte offsets; see ffn_ws_bytes).
 struct FfnWs {
   size_t h_bf16 = 0;   // fp8: H before quantisation [A, f] bf16 (fwd; bwd with recompute)

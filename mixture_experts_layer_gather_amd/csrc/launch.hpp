@@ -163,6 +163,10 @@ struct FfnBwdLaunch {
 };
 void launch_grouped_ffn_bwd(const FfnBwdLaunch& a, hipStream_t st);
 
+// Fills bytes (a multiple of 4) of device memory with zeros (a kernel, not
+// a memset, so that the call can be captured into a graph).
+void launch_zero(void* dst, int64_t bytes, hipStream_t st);
+
 struct QuantLaunch {
   const void* src;
   int src_bf16;

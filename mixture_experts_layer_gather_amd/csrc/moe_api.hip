@@ -147,12 +147,12 @@ int moe_route(const moe_config* cfg, const void* x, const float* w_router, const
   (void)ws;
   (void)ws_bytes;
   MOE_CHECK(check_cfg(cfg));
+  if (cfg->num_tokens == 0) return MOE_OK;  // every output is empty
   MOE_CHECK(need(x)); MOE_CHECK(need(w_router)); MOE_CHECK(need(logits));
   MOE_CHECK(need(topk_idx)); MOE_CHECK(need(topk_gate));
   MOE_CHECK(align(x)); MOE_CHECK(align(w_router)); MOE_CHECK(align(expert_bias));
   MOE_CHECK(align(logits)); MOE_CHECK(align(topk_idx)); MOE_CHECK(align(topk_gate));
   MOE_CHECK(align(routing_map));
-  if (cfg->num_tokens == 0) return MOE_OK;
   moe::RouteLaunch r{};
   r.x = x; r.w_router = w_router; r.bias = expert_bias; r.logits = logits;
   r.idx = topk_idx; r.gate = topk_gate; r.rmap = routing_map;
@@ -169,13 +169,19 @@ int moe_dispatch(const moe_config* cfg, const void* x, const int32_t* topk_idx, 
                  void* x_scale, void* ws, size_t ws_bytes, void* stream) {
   MOE_CHECK(check_cfg(cfg));
   const bool fp8 = is_fp8(cfg);
+  if (cfg->num_tokens == 0) {  // an empty batch: every expert has no rows
+    MOE_CHECK(need(counts)); MOE_CHECK(need(offsets)); MOE_CHECK(align_all(counts, offsets));
+    const hipStream_t st = static_cast<hipStream_t>(stream);
+    moe::launch_zero(counts, cfg->num_experts * 4, st);
+    moe::launch_zero(offsets, (cfg->num_experts + 1) * 4, st);
+    return launched();
+  }
   MOE_CHECK(need(x)); MOE_CHECK(need(topk_idx)); MOE_CHECK(need(counts)); MOE_CHECK(need(offsets));
   MOE_CHECK(need(row_id_map)); MOE_CHECK(need(perm_token)); MOE_CHECK(need(x_perm));
   if (fp8) MOE_CHECK(need(x_scale));
   MOE_CHECK(align(x)); MOE_CHECK(align(topk_idx)); MOE_CHECK(align(counts)); MOE_CHECK(align(offsets));
   MOE_CHECK(align(row_id_map)); MOE_CHECK(align(perm_token)); MOE_CHECK(align(x_perm));
   MOE_CHECK(align(x_scale)); MOE_CHECK(align(ws));
-  if (cfg->num_tokens == 0) return MOE_OK;
   if (!ws || ws_bytes < moe_workspace_size(cfg, MOE_OP_DISPATCH)) return MOE_ERR_WORKSPACE;
   moe::DispatchLaunch a{};
   a.x = x; a.idx = topk_idx; a.counts = counts; a.offsets = offsets; a.row_id_map = row_id_map;
@@ -197,6 +203,8 @@ int moe_grouped_ffn(const moe_config* cfg, const void* x_perm, const void* x_sca
   MOE_CHECK(check_cfg(cfg));
   const bool identity = cfg->ffn_mode == MOE_FFN_IDENTITY;
   const bool fp8 = is_fp8(cfg);
+  if (fp8 && identity) return MOE_ERR_UNSUPPORTED_DTYPE;
+  if (cfg->num_tokens == 0) return MOE_OK;  // every output is empty
   MOE_CHECK(need(x_perm)); MOE_CHECK(need(offsets)); MOE_CHECK(need(out_perm));
   if (!identity) {
     MOE_CHECK(need(w1)); MOE_CHECK(need(w2));
@@ -208,8 +216,6 @@ int moe_grouped_ffn(const moe_config* cfg, const void* x_perm, const void* x_sca
     }
   }
   MOE_CHECK(align_all(x_perm, x_scale, offsets, w1, w1_scale, w2, w2_scale, act_gu, act_h, h_scale, out_perm, ws));
-  if (fp8 && identity) return MOE_ERR_UNSUPPORTED_DTYPE;
-  if (cfg->num_tokens == 0) return MOE_OK;
   const size_t need_ws = moe_workspace_size(cfg, MOE_OP_GROUPED_FFN);
   if (need_ws && (!ws || ws_bytes < need_ws)) return MOE_ERR_WORKSPACE;
   moe::FfnLaunch a{};
@@ -230,9 +236,9 @@ int moe_grouped_ffn(const moe_config* cfg, const void* x_perm, const void* x_sca
 int moe_combine(const moe_config* cfg, const void* out_perm, const int32_t* row_id_map,
                 const float* topk_gate, const void* shared_out, void* y, void* stream) {
   MOE_CHECK(check_cfg(cfg));
+  if (cfg->num_tokens == 0) return MOE_OK;
   MOE_CHECK(need(out_perm)); MOE_CHECK(need(row_id_map)); MOE_CHECK(need(topk_gate)); MOE_CHECK(need(y));
   MOE_CHECK(align_all(out_perm, row_id_map, topk_gate, shared_out, y));
-  if (cfg->num_tokens == 0) return MOE_OK;
   moe::CombineLaunch a{};
   a.src = out_perm; a.row_id_map = row_id_map; a.gate = topk_gate; a.add = shared_out; a.dst = y;
   a.T = cfg->num_tokens; a.d = cfg->hidden; a.k = cfg->top_k;
@@ -245,10 +251,10 @@ int moe_combine_bwd(const moe_config* cfg, const void* dy, const void* out_perm,
                     const int32_t* row_id_map, const float* topk_gate, void* d_out_perm, float* d_gate,
                     void* stream) {
   MOE_CHECK(check_cfg(cfg));
+  if (cfg->num_tokens == 0) return MOE_OK;
   MOE_CHECK(need(dy)); MOE_CHECK(need(out_perm)); MOE_CHECK(need(row_id_map)); MOE_CHECK(need(topk_gate));
   MOE_CHECK(need(d_out_perm)); MOE_CHECK(need(d_gate));
   MOE_CHECK(align_all(dy, out_perm, row_id_map, topk_gate, d_out_perm, d_gate));
-  if (cfg->num_tokens == 0) return MOE_OK;
   moe::CombineBwdLaunch a{};
   a.dy = dy; a.out_perm = out_perm; a.row_id_map = row_id_map; a.gate = topk_gate;
   a.d_out_perm = d_out_perm; a.d_gate = d_gate;
@@ -266,6 +272,16 @@ int moe_grouped_ffn_bwd(const moe_config* cfg, const void* x_perm, const void* x
   MOE_CHECK(check_cfg(cfg));
   const bool identity = cfg->ffn_mode == MOE_FFN_IDENTITY;
   const bool fp8 = is_fp8(cfg);
+  if (fp8 && identity) return MOE_ERR_UNSUPPORTED_DTYPE;
+  if (cfg->num_tokens == 0) {  // no rows: the weight gradients are exact zeros
+    MOE_CHECK(need(dw1)); MOE_CHECK(need(dw2)); MOE_CHECK(align_all(dw1, dw2));
+    const int64_t pb = cfg->weight_dtype == MOE_DTYPE_F32 ? 4 : 2;
+    const int64_t E = cfg->num_experts, d = cfg->hidden, f = cfg->ffn_hidden;
+    const hipStream_t st = static_cast<hipStream_t>(stream);
+    moe::launch_zero(dw1, E * 2 * f * d * pb, st);
+    moe::launch_zero(dw2, E * d * f * pb, st);
+    return launched();
+  }
   MOE_CHECK(need(d_out_perm)); MOE_CHECK(need(dx_perm)); MOE_CHECK(need(dw1)); MOE_CHECK(need(dw2));
   MOE_CHECK(need(offsets));
   if (!identity) {
@@ -278,8 +294,6 @@ int moe_grouped_ffn_bwd(const moe_config* cfg, const void* x_perm, const void* x
     }
   }
   MOE_CHECK(align_all(x_perm, x_scale, offsets, w1, w1_scale, w2, w2_scale, act_gu, act_h, h_scale, d_out_perm, dx_perm, dw1, dw2, ws));
-  if (fp8 && identity) return MOE_ERR_UNSUPPORTED_DTYPE;
-  if (cfg->num_tokens == 0) return MOE_OK;
   if (!identity && (!ws || ws_bytes < moe_workspace_size(cfg, MOE_OP_GROUPED_FFN_BWD)))
     return MOE_ERR_WORKSPACE;
   moe::FfnBwdLaunch a{};
@@ -300,9 +314,9 @@ int moe_grouped_ffn_bwd(const moe_config* cfg, const void* x_perm, const void* x
 int moe_dispatch_bwd(const moe_config* cfg, const void* dx_perm, const int32_t* row_id_map, const void* dx_add,
                      void* dx, void* stream) {
   MOE_CHECK(check_cfg(cfg));
+  if (cfg->num_tokens == 0) return MOE_OK;
   MOE_CHECK(need(dx_perm)); MOE_CHECK(need(row_id_map)); MOE_CHECK(need(dx));
   MOE_CHECK(align_all(dx_perm, row_id_map, dx_add, dx));
-  if (cfg->num_tokens == 0) return MOE_OK;
   moe::CombineLaunch a{};
   a.src = dx_perm; a.row_id_map = row_id_map; a.gate = nullptr; a.add = dx_add; a.dst = dx;
   a.T = cfg->num_tokens; a.d = cfg->hidden; a.k = cfg->top_k;
@@ -315,9 +329,13 @@ int moe_route_aux_loss(const moe_config* cfg, const float* logits, const int32_t
                        float* aux_loss, void* ws, size_t ws_bytes, void* stream) {
   MOE_CHECK(check_cfg(cfg));
   if (cfg->aux_coeff == 0.0f) return MOE_ERR_INVALID_ARG;
-  MOE_CHECK(need(logits)); MOE_CHECK(need(topk_idx)); MOE_CHECK(need(aux_loss));
+  MOE_CHECK(need(aux_loss));
+  if (cfg->num_tokens == 0) {  // no tokens, no imbalance: the loss is 0
+    moe::launch_zero(aux_loss, 4, static_cast<hipStream_t>(stream));
+    return launched();
+  }
+  MOE_CHECK(need(logits)); MOE_CHECK(need(topk_idx));
   MOE_CHECK(align_all(logits, topk_idx, ws));
-  if (cfg->num_tokens == 0) return MOE_OK;
   if (!ws || ws_bytes < moe_workspace_size(cfg, MOE_OP_AUX_LOSS)) return MOE_ERR_WORKSPACE;
   moe::AuxLaunch a{};
   a.logits = logits; a.idx = topk_idx; a.loss = aux_loss;
@@ -333,10 +351,14 @@ int moe_route_bwd(const moe_config* cfg, const void* x, const float* w_router, c
                   const float* d_aux, void* dx, float* dw_router, void* ws, size_t ws_bytes,
                   void* stream) {
   MOE_CHECK(check_cfg(cfg));
+  if (cfg->num_tokens == 0) {  // a sum over no tokens: dw_router = 0
+    MOE_CHECK(need(dw_router)); MOE_CHECK(align(dw_router));
+    moe::launch_zero(dw_router, cfg->num_experts * cfg->hidden * 4, static_cast<hipStream_t>(stream));
+    return launched();
+  }
   MOE_CHECK(need(x)); MOE_CHECK(need(w_router)); MOE_CHECK(need(logits)); MOE_CHECK(need(topk_idx));
   MOE_CHECK(need(topk_gate)); MOE_CHECK(need(d_gate)); MOE_CHECK(need(dx)); MOE_CHECK(need(dw_router));
   MOE_CHECK(align_all(x, w_router, logits, topk_idx, topk_gate, d_gate, dx, dw_router, ws));
-  if (cfg->num_tokens == 0) return MOE_OK;
   if (!ws || ws_bytes < moe_workspace_size(cfg, MOE_OP_ROUTE_BWD)) return MOE_ERR_WORKSPACE;
   const int Z = moe::route_bwd_zsplit(cfg->num_tokens, cfg->hidden, cfg->num_experts);
   const size_t dl_bytes = round_up(size_t(cfg->num_tokens) * size_t(cfg->num_experts) * 4);

@@ -73,12 +73,27 @@ def test_config_validation(M):
 
 
 def test_empty_batch_enqueues_nothing(M):
+    """T = 0: the calls whose outputs all have T rows return at once and
+    accept NULL buffers (an empty tensor has no storage). The calls that
+    must still write exact zeros (counts and offsets, expert and router
+    weight gradients, the auxiliary loss) require those outputs; this CPU
+    test only checks the refusals, which come before any launch."""
     c = _cfg(M, T=0)
     L = M.lib()
-    assert _route(M, c) == 0
-    assert L.moe_dispatch(ctypes.byref(c), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, None, 0,
-                          None) == 0
-    assert L.moe_combine(ctypes.byref(c), FAKE, FAKE, FAKE, None, FAKE, None) == 0
+    N = None
+    assert _route(M, c, x=None) == 0
+    assert L.moe_combine(ctypes.byref(c), N, N, N, N, N, N) == 0
+    assert L.moe_combine_bwd(ctypes.byref(c), N, N, N, N, N, N, N) == 0
+    assert L.moe_dispatch_bwd(ctypes.byref(c), N, N, N, N, N) == 0
+    assert L.moe_grouped_ffn(ctypes.byref(c), *([N] * 12), 0, N) == 0
+    # zeros to write: the output may not be NULL
+    assert L.moe_dispatch(ctypes.byref(c), N, N, N, FAKE, N, N, N, N, N, 0, N) == -1    # counts
+    assert L.moe_dispatch(ctypes.byref(c), N, N, FAKE, N, N, N, N, N, N, 0, N) == -1    # offsets
+    assert L.moe_grouped_ffn_bwd(ctypes.byref(c), *([N] * 12), N, FAKE, N, 0, N) == -1  # dw1
+    assert L.moe_grouped_ffn_bwd(ctypes.byref(c), *([N] * 12), FAKE, N, N, 0, N) == -1  # dw2
+    assert L.moe_route_bwd(ctypes.byref(c), *([N] * 9), N, 0, N) == -1                  # dw_router
+    ca = _cfg(M, T=0, aux_coeff=0.01)
+    assert L.moe_route_aux_loss(ctypes.byref(ca), N, N, N, N, 0, N) == -1
 
 
 def test_null_alignment_and_workspace_errors(M):
@@ -170,14 +185,16 @@ def test_recompute_modes(M):
         return L.moe_grouped_ffn_bwd(ctypes.byref(c), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, gu, h,
                                      hs, FAKE, FAKE, FAKE, FAKE, ws, n, None)
 
-    # T = 0 returns after the argument checks: no launch, no device access
+    # FP8: both calls need a workspace, so with none given every case below
+    # returns an error (NULL: -1, else the missing workspace: -4) before any
+    # launch or device access
     for mode, need_gu, need_h in (("none", True, True), ("act", True, False), ("full", False, False)):
-        c = _cfg(M, T=0, weight="fp8", recompute=mode)
+        c = _cfg(M, T=64, weight="fp8", recompute=mode)
         for call in (ffn, ffn_bwd):
-            assert call(c, FAKE, FAKE, FAKE, None, 0) == 0, (mode, call)
-            assert (call(c, None, FAKE, FAKE, None, 0) == -1) == need_gu, (mode, call)
-            assert (call(c, FAKE, None, FAKE, None, 0) == -1) == need_h, (mode, call)
-            assert (call(c, FAKE, FAKE, None, None, 0) == -1) == need_h, (mode, call)
+            assert call(c, FAKE, FAKE, FAKE, None, 0) == -4, (mode, call)
+            assert call(c, None, FAKE, FAKE, None, 0) == (-1 if need_gu else -4), (mode, call)
+            assert call(c, FAKE, None, FAKE, None, 0) == (-1 if need_h else -4), (mode, call)
+            assert call(c, FAKE, FAKE, None, None, 0) == (-1 if need_h else -4), (mode, call)
         # with tokens, a recompute workspace is required
         c1 = _cfg(M, T=64, recompute=mode)
         if mode != "none":

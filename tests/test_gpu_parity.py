@@ -179,6 +179,32 @@ def test_edge_shapes():
         _compare_small(cfg)
 
 
+@pytest.mark.parametrize("name", ["tiny_fp32", "mixtral_mini", "deepseek_fp8_mini", "deepseek_mxfp8_mini"])
+def test_empty_batch(name):
+    """T = 0: no rows for any expert, so counts, offsets and every weight
+    gradient are exact zeros (and the auxiliary loss is 0); the T-row
+    outputs are empty. The outputs are filled with garbage first."""
+    from mixture_experts_layer_gather_amd import MoELayer
+    cfg = SMALL[name].replace(T=0, aux_coeff=0.01)
+    _say(f"[empty] {name}")
+    inp = _inputs(cfg)
+    layer = MoELayer(**cfg.describe(), device=DEV)
+    cu = lambda t: None if t is None else t.to(DEV)
+    layer.set_weights(cu(inp["wr"]), cu(inp["w1"]), cu(inp["w2"]), bias=cu(inp.get("bias")),
+                      sw1=cu(inp.get("sw1")), sw2=cu(inp.get("sw2")))
+    outs = ["counts", "offsets", "dw1", "dw2", "dw_router", "aux_loss"]
+    if cfg.shared:
+        outs += ["s_dw1", "s_dw2"]
+    for n in outs:
+        t = getattr(layer, n)
+        t.fill_(float("nan") if t.dtype.is_floating_point else -7)
+    layer.step(cu(inp["x"]), cu(inp["dy"]))
+    torch.cuda.synchronize()
+    for n in outs:
+        assert not _np(getattr(layer, n)).any(), n
+    assert layer.y.shape == (0, cfg.d) and layer.dx.shape == (0, cfg.d)
+
+
 def test_all_equal_logits_pick_lowest_indices():
     cfg = S.mini(S.CONFIGS[1], T=100, d=128, f=128, E=8).replace(k=3)
     inp = _inputs(cfg)
