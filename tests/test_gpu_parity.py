@@ -136,6 +136,9 @@ SMALL = {
         k=6, group_score="max", seed_base=61),
     "deepseek_mini_norenorm": S.mini(S.CONFIGS[2], T=300, d=256, f=256, E=32).replace(
         k=6, renorm=False, gate_scale=1.0, seed_base=62),
+    # the largest expert count and top-k the library takes (E = 1024,
+    # k = 16): most experts get 0 to 3 rows
+    "max_experts_topk": S.mini(S.CONFIGS[1], T=200, d=128, f=128, E=1024).replace(k=16, seed_base=63),
     # MXFP8: 1 x 32 / 32 x 1 blocks with E8M0 scales on the matrix cores
     "deepseek_mxfp8_mini": S.mini(S.BY_NAME["deepseek_v3_mxfp8"], T=400, d=384, f=256, E=32).replace(k=6),
     # the load-balancing auxiliary loss on (coefficient 0.01): its value and
