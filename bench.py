@@ -197,6 +197,48 @@ def summarize_profiles(cfg_name, stats_dir, fetch_dir, write_dir, copy_fetch_dir
     print("wrote", os.path.join(PROFILES, f"{cfg_name}_kernels.md"))
 
 
+def summarize_mfma(cfg_name, pmc_dir):
+    """profiles/<cfg>_mfma.md from a `rocprofv3 --pmc MfmaUtil MfmaFlopsBF16`
+    run: per GEMM role, the matrix cores' busy share while the kernel runs
+    and the MFMA work they did against the algorithmic flops (the excess is
+    the zero rows that pad ragged expert tiles)."""
+    import csv
+    import collections
+    import moe_synth as S
+    cfg = S.BY_NAME[cfg_name]
+    A, d, f = cfg.T * cfg.k, cfg.d, cfg.f
+    alg = {"gemm1": 4 * A * d * f, "gemm2": 2 * A * f * d, "dh": 2 * A * d * f, "dx": 4 * A * f * d,
+           "wgrad": 3 * A * d * f}  # wgrad: the mean of dW2 (2 A d f) and dW1 (4 A d f)
+    acc = collections.defaultdict(lambda: collections.defaultdict(list))
+    for r in csv.DictReader(open(os.path.join(pmc_dir, "run_counter_collection.csv"))):
+        role = kernel_role(r["Kernel_Name"])
+        if role:
+            acc[role][r["Counter_Name"]].append(float(r["Counter_Value"]))
+    cmd = (f"rocprofv3 --pmc MfmaUtil MfmaFlopsBF16 --output-format csv -d <dir> -o run -- "
+           f"python3 bench.py --steps 2 --warmup 1 --cpu-sample 0 --config {cfg_name}")
+    lines = [f"# Matrix-core utilisation, {cfg_name} (rocprofv3 derived counters)", "",
+             "Command (repository root, one MI355X):", "", "```", cmd, "```", "",
+             "MfmaUtil = SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE x SIMDs): the share of the "
+             "kernel's active cycles in which the matrix cores are busy, at the clock the GPU runs "
+             "at under load. MfmaFlopsBF16 = SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512: the MFMA work done, "
+             "compared with the algorithmic flops of the launch (routed experts and, for a layer "
+             "with one, the shared expert averaged in). Means over all launches of the role.", "",
+             "| GEMM role | launches | MFMA busy % | MFMA TFLOP per launch | algorithmic TFLOP | ratio |",
+             "|---|---:|---:|---:|---:|---:|"]
+    for role in ("gemm1", "gemm2", "dh", "dx", "wgrad"):
+        v = acc.get(role)
+        if not v:
+            continue
+        u = sum(v["MfmaUtil"]) / len(v["MfmaUtil"])
+        fl = sum(v["MfmaFlopsBF16"]) / len(v["MfmaFlopsBF16"])
+        lines.append(f"| {role} | {len(v['MfmaUtil'])} | {u:.1f} | {fl / 1e12:.3f} | "
+                     f"{alg[role] / 1e12:.3f} | {fl / alg[role]:.3f} |")
+    os.makedirs(PROFILES, exist_ok=True)
+    out = os.path.join(PROFILES, f"{cfg_name}_mfma.md")
+    open(out, "w").write("\n".join(lines) + "\n")
+    print("wrote", out)
+
+
 def measured_traffic(cfg_name, call):
     """HBM bytes per launch of `call` from the committed counter summary, or
     None when the kernels changed since the counters were taken."""
@@ -387,10 +429,15 @@ def main():
                     help="only run a plain 1 GiB device copy (counter calibration)")
     ap.add_argument("--vendor-gemm", action="store_true",
                     help="only time torch.matmul (hipBLASLt) on the config's per-expert GEMM shapes")
+    ap.add_argument("--summarize-mfma", metavar="DIR",
+                    help="rocprofv3 --pmc MfmaUtil MfmaFlopsBF16 output dir; writes profiles/<config>_mfma.md")
     ap.add_argument("--summarize", nargs=5, metavar="DIR",
                     help="rocprofv3 output dirs: stats, FETCH_SIZE, WRITE_SIZE, copy FETCH_SIZE, "
                          "copy WRITE_SIZE; writes profiles/<config>_kernels.md and _traffic.json")
     args = ap.parse_args()
+    if args.summarize_mfma:
+        summarize_mfma(args.config, args.summarize_mfma)
+        return
     if args.summarize:
         c = args.config
         cmd = {"stats": f"rocprofv3 --kernel-trace --stats --output-format csv -d <dir> -o run -- "
