@@ -166,9 +166,10 @@ int moe_route(const moe_config *cfg, const void *x, const float *w_router,
  *   row_id_map [T,k] i32 row of (t, j): offsets[e] + #{t' < t routed to e}
  *              (rows sorted by expert, then token)
  *   perm_token [A] i32 source token of each row
- *   x_perm     [A,d]: act copy of x, or for wt = fp8 the E4M3 codes of x
- *              quantised per token and 1 x quant_block block
- *   x_scale    [A, d/quant_block] f32 (fp8 only; NULL otherwise)
+ *   x_perm     [A,d]: act copy of x, or for wt = fp8 / mxfp8 the E4M3 codes
+ *              of x quantised per token and 1 x quant_block block
+ *   x_scale    [A, d/quant_block]: f32 scales (fp8), E8M0 bytes (mxfp8,
+ *              see moe_quantize_mxfp8); NULL otherwise
  * Workspace: moe_workspace_size(cfg, MOE_OP_DISPATCH). */
 int moe_dispatch(const moe_config *cfg, const void *x, const int32_t *topk_idx,
                  int32_t *counts, int32_t *offsets, int32_t *row_id_map,
@@ -179,15 +180,19 @@ int moe_dispatch(const moe_config *cfg, const void *x, const int32_t *topk_idx,
  * Core MoE summary, section 2.4: many expert GEMMs in one kernel). For each
  * expert e and its rows r in [offsets[e], offsets[e+1]):
  *   GU = X W1_e^T ([gate | up], 2f wide), H = silu(G) * U, O = H W2_e^T.
- *   x_perm     [A,d] act (wt = fp8: E4M3 codes, with x_scale [A,d/128])
+ *   x_perm     [A,d] act (wt = fp8: E4M3 codes, with x_scale [A,d/128] f32;
+ *              mxfp8: with x_scale [A,d/32] E8M0 bytes)
  *   offsets    [E+1] i32 (device)
  *   w1         [E,2f,d] wt, rows 0..f-1 gate, f..2f-1 up (fp8: + w1_scale
- *              [E,2f/128,d/128] f32)
- *   w2         [E,d,f] wt (fp8: + w2_scale [E,d/128,f/128] f32)
+ *              [E,2f/128,d/128] f32; mxfp8: quantised along d, + w1_scale
+ *              [E,2f,d/32] E8M0)
+ *   w2         [E,d,f] wt (fp8: + w2_scale [E,d/128,f/128] f32; mxfp8:
+ *              quantised along f, + w2_scale [E,d,f/32] E8M0)
  * out:
  *   act_gu     [A,2f] act: G and U (saved for the backward)
- *   act_h      [A,f]: act, or for wt = fp8 E4M3 codes with h_scale
- *              [A,f/128] f32 (H is quantised before the second GEMM)
+ *   act_h      [A,f]: act, or for wt = fp8 / mxfp8 E4M3 codes with h_scale
+ *              [A,f/128] f32 / [A,f/32] E8M0 (H is quantised before the
+ *              second GEMM)
  *   out_perm   [A,d] act
  * With cfg->recompute = MOE_RECOMPUTE_ACT, act_h and h_scale may be NULL and
  * are not written (H lives in the workspace only); with MOE_RECOMPUTE_FULL,
@@ -226,7 +231,11 @@ int moe_combine_bwd(const moe_config *cfg, const void *dy, const void *out_perm,
  *   dH = dO W2_e, dW2_e = dO^T H,
  *   dG = dH * U * s(G) * (1 + G (1 - s(G))), dU = dH * silu(G),
  *   dX = [dG dU] W1_e, dW1_e = [dG dU]^T X.
- * Inputs as in moe_grouped_ffn plus d_out_perm [A,d] act.
+ * Inputs as in moe_grouped_ffn plus d_out_perm [A,d] act, except that for
+ * mxfp8 w1 and w2 are the copies quantised along their other dimension
+ * (32 x 1 blocks: w1_scale [E,2f/32,d], w2_scale [E,d/32,f] E8M0), the
+ * contraction of the two data-gradient products; mxfp8 takes no
+ * MOE_RECOMPUTE_FULL (it would need the forward's w1 as well).
  * out: dx_perm [A,d] act; dw1 [E,2f,d], dw2 [E,d,f] in the parameter dtype
  * (f32 when wt is f32, else bf16), overwritten; an expert with no rows gets
  * exact zeros.
