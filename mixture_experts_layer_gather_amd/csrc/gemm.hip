@@ -173,7 +173,9 @@ static int padded_grid(int tiles, int ks) {
 // DeepSeek-style layers against 64 everywhere):
 //   row-grouped GEMMs on the 128 x 128 tile: 32 (Mixtral dX 2.41 -> 2.29 ms,
 //     DeepSeek GEMM1 3.89 -> 3.81 ms, the others within noise);
-//   on the 256 x 256 tile: 64;
+//   on the 256 x 256 tile: 64, and 32 when experts average at least 128
+//     tiles (Mixtral-style GEMM1 and dH: step 9.41 -> 9.34 ms; the
+//     Qwen3-style GEMM1, about 30 tiles per expert, loses 3 % with 32);
 //   weight gradients: 16 when an expert has fewer than 256 tiles (so that a
 //     super-block stays inside one expert; Qwen3-style 0.91 -> 0.78 ms), else
 //     64 (16 costs the DeepSeek-style layer 4 %).
@@ -182,7 +184,9 @@ static int padded_grid(int tiles, int ks) {
 constexpr int kSuperRowsSmall = 32, kSuperRowsBig = 64;
 static int super_wgrad(int tiles_per_group) { return tiles_per_group < 256 ? 16 : 64; }
 static int super_rows(int tiles_per_group, int bm) {
-  return tiles_per_group < 16 ? 16 : (bm == 128 ? kSuperRowsSmall : kSuperRowsBig);
+  if (tiles_per_group < 16) return 16;
+  if (bm == 128) return kSuperRowsSmall;
+  return tiles_per_group >= 128 ? 32 : kSuperRowsBig;
 }
 
 // Exclusive scan of per-group row-tile counts; returns the tile's group in
