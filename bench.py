@@ -501,6 +501,8 @@ def main():
     wall = time.perf_counter() - t0
     ms = start.elapsed_time(stop) / args.steps
 
+    # each step from its first to its last event: median and minimum
+    step_ms = sorted(m[0][1].elapsed_time(m[-1][1]) for m in steps)
     per = {}
     for marks in steps:
         for (_, a), (name, b) in zip(marks[:-1], marks[1:]):
@@ -548,6 +550,8 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms, 4),
+        "ms_per_step_median": round(step_ms[len(step_ms) // 2], 4),
+        "ms_per_step_min": round(step_ms[0], 4),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
