@@ -53,11 +53,17 @@ GEMM_SOURCES = ("common.hpp", "gemm.hip", "launch.hpp")
 
 
 def source_hash() -> str:
+    """Hash of the GEMM sources' code, comments and blank space removed (a
+    comment edit does not change the kernels the counters measured)."""
     import hashlib
+    import re
     h = hashlib.sha256()
     for f in GEMM_SOURCES:
+        code = open(os.path.join(CSRC, f)).read()
+        code = re.sub(r"/\*.*?\*/", " ", code, flags=re.S)
+        code = re.sub(r"//[^\n]*", " ", code)
         h.update(f.encode())
-        h.update(open(os.path.join(CSRC, f), "rb").read())
+        h.update(" ".join(code.split()).encode())
     return h.hexdigest()[:16]
 
 

@@ -22,7 +22,10 @@
 // operands carry fp32 block scales (activations 1 x 128 along K, weights
 // 128 x 128): a K step is exactly one 128-deep block, its MFMA result is
 // multiplied by row scale x column-block scale and added to the fp32
-// accumulator.
+// accumulator. MXFP8 operands (mx8_t) carry one E8M0 byte per 32 K-values,
+// which the same instruction applies itself (hardware scales per lane).
+// The SwiGLU epilogues can skip saving GU and rebuild H in the backward
+// (activation recompute).
 //
 // Tiles go global -> LDS by DMA (2 or 3 stages, one barrier per K step).
 // K-major operands land in K-contiguous rows and are read with 16-byte LDS
