@@ -4,10 +4,16 @@ A step is one forward and backward pass of the whole layer over one batch:
 route -> dispatch -> grouped SwiGLU FFN (+ shared expert) -> combine, then
 combine backward -> grouped FFN backward -> dispatch backward -> route
 backward. Inputs and weights are seeded synthetic tensors already resident in
-HBM when the timed region starts. Prints one JSON line.
+HBM when the timed region starts. Before every timed step a 1 GiB scratch
+buffer is written and another 1 GiB read, outside the timed events, so that
+no step finds its working set in the 256 MB memory-side cache (MALL) or the
+L2s. Prints one JSON line.
 
-The workload is the Mixtral-style layer (T=4096 tokens, d=4096, 8 experts,
-top-2, SwiGLU d_ff=14336, bf16) unless --config names another.
+By default every workload runs: the headline is the largest one that fits one
+GPU, the DeepSeek-V3-style FP8 layer (T=8192, d=7168, 256 routed experts +
+1 shared, top-8, d_ff=2048, E4M3 with 1x128 / 128x128 fp32 block scales); the
+tiny fp32, Mixtral-style, DeepSeek-V3-style bf16 and Qwen3-style skewed
+layers follow in the same line under "configs". --config names one workload.
 """
 from __future__ import annotations
 
@@ -23,6 +29,13 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBPS = 8000.0
 MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "fp8": 5000.0, "f32": 157.3}
 CSRC = os.path.join(ROOT, "mixture_experts_layer_gather_amd", "csrc")
+# The headline workload: the largest of the five that one GPU holds. The
+# others are reported in the same line for context.
+HEADLINE = "deepseek_v3_fp8"
+CONTEXT_CONFIGS = ("tiny_fp32", "mixtral_bf16", "deepseek_v3_bf16", "qwen3_skew_bf16",
+                   "deepseek_v3_mxfp8")
+# tokens of the headline workload the CPU oracle runs (a bounded sample)
+CPU_SAMPLE_TOKENS = 256
 PROFILES = os.path.join(ROOT, "profiles")
 
 # Which library call launches a kernel, from its (demangled) name: the GEMM
@@ -67,13 +80,76 @@ def source_hash() -> str:
     return h.hexdigest()[:16]
 
 
+def step_calls(cfg):
+    """The library calls of one step, in launch order."""
+    calls = ["route"] + (["aux_loss"] if cfg.aux_coeff else []) + ["dispatch", "grouped_ffn"]
+    calls += (["shared_ffn"] if cfg.shared else []) + ["combine", "combine_bwd", "grouped_ffn_bwd"]
+    calls += (["shared_ffn_bwd"] if cfg.shared else []) + ["dispatch_bwd", "route_bwd"]
+    return calls
+
+
+def _is_step_start(name):
+    import re
+    return re.search(r"moe::logits(_small_e)?_kernel<", name) is not None
+
+
+def _call_ends(call, name, wgrads_seen):
+    """Whether the kernel `name` is the last one the library call `call`
+    launches (route_bwd, the step's last call, ends at the next step)."""
+    if call == "route":
+        return "moe::select_kernel<" in name
+    if call == "aux_loss":
+        return "moe::aux_final_kernel<true>" in name
+    if call == "dispatch":
+        return "moe::dispatch_gather" in name
+    if call in ("grouped_ffn", "shared_ffn"):
+        return kernel_role(name) == "gemm2"
+    if call in ("combine", "dispatch_bwd"):
+        return "moe::combine_kernel<" in name
+    if call == "combine_bwd":
+        return "moe::combine_bwd_kernel<" in name
+    if call in ("grouped_ffn_bwd", "shared_ffn_bwd"):
+        return kernel_role(name) == "wgrad" and wgrads_seen == 2
+    return False
+
+
+def attribute_calls(rows, calls, name_key="Kernel_Name"):
+    """Library kernels of a rocprofv3 trace or counter CSV, assigned to
+    (step, call). Kernels outside the library (torch's fills, the cache
+    flush) and those before the first step (weight quantisation at set-up)
+    are left out. Returns a list of (step, call, row) in dispatch order."""
+    rows = sorted(rows, key=lambda r: int(r["Dispatch_Id"]))
+    out = []
+    step, ci, wg = -1, 0, 0
+    for r in rows:
+        n = r[name_key]
+        if "moe::" not in n:
+            continue
+        if _is_step_start(n) and (step < 0 or ci > 0):
+            step, ci, wg = step + 1, 0, 0
+        if step < 0:
+            continue
+        if ci >= len(calls):
+            raise ValueError(f"kernel {n} past the step's last call")
+        if kernel_role(n) == "wgrad":
+            wg += 1
+        out.append((step, calls[ci], r))
+        if _call_ends(calls[ci], n, wg):
+            ci, wg = ci + 1, 0
+    return out
+
+
 def summarize_profiles(cfg_name, stats_dir, fetch_dir, write_dir, copy_fetch_dir, copy_write_dir,
                        command):
     """Turn rocprofv3 CSV output into profiles/<cfg>_kernels.md and
-    profiles/<cfg>_traffic.json (HBM bytes per launch of each GEMM call,
-    with FETCH_SIZE/WRITE_SIZE scaled by what they read for a 1 GiB copy)."""
+    profiles/<cfg>_traffic.json: kernel time per library call and step (every
+    kernel a call launches), and HBM bytes per call and per GEMM role, with
+    FETCH_SIZE/WRITE_SIZE scaled by what they read for a 1 GiB copy."""
     import csv
     import collections
+    import moe_synth as S
+    cfg = S.BY_NAME[cfg_name]
+    calls = step_calls(cfg)
     stats = list(csv.DictReader(open(os.path.join(stats_dir, "run_kernel_stats.csv"))))
     tot = sum(float(r["TotalDurationNs"]) for r in stats)
     lines = [f"# Kernel time, {cfg_name}, fwd+bwd steps (rocprofv3 --kernel-trace --stats)", "",
@@ -83,47 +159,27 @@ def summarize_profiles(cfg_name, stats_dir, fetch_dir, write_dir, copy_fetch_dir
         lines.append(f"| {float(r['AverageNs']) / 1e3:.1f} | {r['Calls']} | "
                      f"{100 * float(r['TotalDurationNs']) / tot:.1f} | `{r['Name'][:140]}` |")
 
-    # library calls: GEMM launches by role, per step. Steps = router selection
-    # launches (one per step). Within a step the routed experts' call comes
-    # before the shared expert's, so a role's first launch(es) of each step
-    # (two for wgrad: dW2, dW1) are the routed call's, the rest the shared's.
-    def by_step(rows, value):
-        rows = sorted(rows, key=lambda r: int(r["Dispatch_Id"]))
-        steps = sum(1 for r in rows if "select_kernel" in r["Kernel_Name"])
-        seq = collections.defaultdict(list)
-        for r in rows:
-            role = kernel_role(r["Kernel_Name"])
-            if role:
-                seq[role].append(value(r))
-        split = {}
-        for role, vals in seq.items():
-            n = len(vals) // max(1, steps)
-            if steps == 0 or n * steps != len(vals):
-                raise ValueError(f"{role}: {len(vals)} launches in {steps} steps")
-            nr = 2 if role == "wgrad" else 1
-            routed = [v for i, v in enumerate(vals) if i % n < nr]
-            shared = [v for i, v in enumerate(vals) if i % n >= nr]
-            split[role] = (routed, shared, nr, n - nr)
-        return steps, split
-
     trace = list(csv.DictReader(open(os.path.join(stats_dir, "run_kernel_trace.csv"))))
-    steps, tsplit = by_step(trace, lambda r: int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
-    lines += ["", "## Library calls per step (sum of their GEMM kernels)", "",
-              f"Steps in the trace: {steps} (warm-up included); launches of the routed experts' "
-              "calls, then of the shared expert's where there is one.", "",
+    att = attribute_calls(trace, calls)
+    steps = 1 + max(s for s, _, _ in att)
+    dur = lambda r: int(r["End_Timestamp"]) - int(r["Start_Timestamp"])
+    call_ns = collections.defaultdict(float)
+    call_kern = collections.defaultdict(lambda: collections.defaultdict(list))
+    for _, c, r in att:
+        call_ns[c] += dur(r)
+        role = kernel_role(r["Kernel_Name"]) or r["Kernel_Name"].split("(")[0].replace("void ", "")
+        call_kern[c][role].append(dur(r))
+    lines += ["", "## Library calls per step (every kernel each call launches)", "",
+              f"Steps in the trace: {steps} (warm-up included). Kernels are assigned to calls by "
+              "their order in the step; a call's time is the sum of its kernels' durations "
+              "(gaps between them not counted).", "",
               "| call | ms per step | kernels (avg us x launches per step) |", "|---|---:|---|"]
-    roles_order = ("gemm1", "gemm2", "dh", "dx", "wgrad")
-    for which, prefix in ((0, "grouped"), (1, "shared")):
-        for fb in ("ffn", "ffn_bwd"):
-            call = f"{prefix}_{fb}"
-            rs = [x for x in roles_order if x in tsplit and ROLE_CALL[x] == f"grouped_{fb}"
-                  and tsplit[x][which]]
-            if not rs:
-                continue
-            ms = sum(sum(tsplit[x][which]) for x in rs) / steps / 1e6
-            parts = ", ".join(f"{x} {sum(tsplit[x][which]) / len(tsplit[x][which]) / 1e3:.0f} x "
-                              f"{tsplit[x][2 + which]}" for x in rs)
-            lines.append(f"| {call} | {ms:.3f} | {parts} |")
+    for c in calls:
+        if c not in call_ns:
+            continue
+        parts = ", ".join(f"{k} {sum(v) / len(v) / 1e3:.1f} x {len(v) / steps:g}"
+                          for k, v in call_kern[c].items())
+        lines.append(f"| {c} | {call_ns[c] / steps / 1e6:.3f} | {parts} |")
 
     def counters(d):
         return list(csv.DictReader(open(os.path.join(d, "run_counter_collection.csv"))))
@@ -134,67 +190,66 @@ def summarize_profiles(cfg_name, stats_dir, fetch_dir, write_dir, copy_fetch_dir
 
     f_fetch = (1 << 30) / (copy_kib(copy_fetch_dir) * 1024)
     f_write = (1 << 30) / (copy_kib(copy_write_dir) * 1024)
-    _, fsplit = by_step(counters(fetch_dir), lambda r: float(r["Counter_Value"]) * 1024 * f_fetch)
-    _, wsplit = by_step(counters(write_dir), lambda r: float(r["Counter_Value"]) * 1024 * f_write)
 
-    def per_launch(split, role, which):
-        vals = split[role][which]
-        nper = split[role][2 + which]
-        return sum(vals) / len(vals) * nper if vals else 0.0  # bytes per step of the role
+    def per_step(d, factor):
+        rows = counters(d)
+        a = attribute_calls(rows, calls)
+        n = 1 + max(s for s, _, _ in a)
+        by_call = collections.defaultdict(float)
+        by_role = collections.defaultdict(lambda: collections.defaultdict(list))
+        by_kernel = collections.defaultdict(list)
+        for _, c, r in a:
+            v = float(r["Counter_Value"]) * 1024 * factor
+            by_call[c] += v / n
+            role = kernel_role(r["Kernel_Name"])
+            if role:
+                by_role[c][role].append(v)
+            else:
+                by_kernel[r["Kernel_Name"]].append(v)
+        return by_call, by_role, by_kernel
 
+    fc, fr, fk = per_step(fetch_dir, f_fetch)
+    wc, wr, wk = per_step(write_dir, f_write)
     roles = {}
-    for role in roles_order:
-        if role in fsplit:
-            n = fsplit[role][2]
-            roles[role] = [per_launch(fsplit, role, 0) / n, per_launch(wsplit, role, 0) / n]
-    calls = collections.defaultdict(float)
-    for which, prefix in ((0, "grouped"), (1, "shared")):
-        for role in roles_order:
-            if role in fsplit and fsplit[role][which]:
-                calls[f"{prefix}_{ROLE_CALL[role][len('grouped_'):]}"] += (
-                    per_launch(fsplit, role, which) + per_launch(wsplit, role, which))
+    for c in ("grouped_ffn", "grouped_ffn_bwd"):
+        for role, v in fr.get(c, {}).items():
+            w = wr[c][role]
+            roles[role] = [sum(v) / len(v), sum(w) / len(w)]
     out = {"config": cfg_name, "source_hash": source_hash(), "fetch_factor": f_fetch,
            "write_factor": f_write,
            "roles_bytes_per_launch": {k: {"fetch": v[0], "write": v[1]} for k, v in roles.items()},
-           "calls_bytes_per_launch": dict(calls), "commands": command}
-    lines += ["", "## HBM traffic per launch (rocprofv3 --pmc FETCH_SIZE, then WRITE_SIZE)", "",
+           "calls_bytes_per_launch": {c: fc[c] + wc.get(c, 0.0) for c in calls if c in fc},
+           "calls_ms_per_step": {c: call_ns[c] / steps / 1e6 for c in calls if c in call_ns},
+           "commands": command}
+    lines += ["", "## HBM traffic (rocprofv3 --pmc FETCH_SIZE, then WRITE_SIZE)", "",
               f"Scaled by a 1 GiB device copy: FETCH_SIZE x {f_fetch:.3f}, WRITE_SIZE x {f_write:.3f}. "
-              "Launches of the routed experts' calls (wgrad: the mean of dW2 and dW1).",
+              "Per GEMM role: the routed experts' launches (wgrad: the mean of dW2 and dW1).",
               "", "| GEMM role | fetch GB | write GB |", "|---|---:|---:|"]
     for k, v in roles.items():
         lines.append(f"| {k} | {v[0] / 1e9:.3f} | {v[1] / 1e9:.3f} |")
-    lines += ["", "| call | HBM GB per launch (fetch + write) |", "|---|---:|"]
-    for k, v in calls.items():
-        lines.append(f"| {k} | {v / 1e9:.3f} |")
-    # the other library kernels (route, dispatch, combine, quantisers):
-    # measured HBM bytes per launch and the bandwidth they imply at the
-    # stats run's mean duration (means over all launches of a kernel in the
-    # traces, set-up launches included)
+    lines += ["", "| call | HBM GB per step (fetch + write, every kernel of the call) | GB/s at the "
+              "call's kernel time |", "|---|---:|---:|"]
+    for c in calls:
+        if c in fc:
+            b = fc[c] + wc.get(c, 0.0)
+            t = call_ns.get(c, 0.0) / steps
+            lines.append(f"| {c} | {b / 1e9:.3f} | {b / t:.0f} |" if t else f"| {c} | {b / 1e9:.3f} | |")
+    # the other library kernels: measured bytes per launch and the bandwidth
+    # they imply at the stats run's mean duration
     avg_ns = {r["Name"]: float(r["AverageNs"]) for r in stats}
-
-    def per_kernel(d, factor):
-        acc = collections.defaultdict(list)
-        for r in counters(d):
-            n = r["Kernel_Name"]
-            if n.startswith(("moe::", "void moe::")) and "gemm_kernel" not in n:
-                acc[n].append(float(r["Counter_Value"]) * 1024 * factor)
-        return {n: sum(v) / len(v) for n, v in acc.items()}, {n: len(v) for n, v in acc.items()}
-
-    kf, kn = per_kernel(fetch_dir, f_fetch)
-    kw, _ = per_kernel(write_dir, f_write)
     lines += ["", "## Other library kernels: HBM traffic per launch and bandwidth", "",
               "FETCH_SIZE and WRITE_SIZE per launch (scaled as above), divided by the kernel's mean "
-              "duration in the stats run; means over every launch in the traces (set-up launches "
-              "of the quantisers included). 8 TB/s is the vendor peak; a 1 GiB copy reaches "
-              "4.5-5.3 TB/s on this GPU.", "",
+              "duration in the stats run; means over every launch inside the steps. 8 TB/s is the "
+              "vendor peak; the measured copy peak is in the benchmark line.", "",
               "| kernel | launches | fetch MB | write MB | mean us | GB/s |", "|---|---:|---:|---:|---:|---:|"]
-    for n in sorted(kf, key=lambda n: -(kf[n] + kw.get(n, 0.0))):
+    for n in sorted(fk, key=lambda n: -(sum(fk[n]) / len(fk[n]))):
         if n not in avg_ns:
             continue
-        b = kf[n] + kw.get(n, 0.0)
+        f_ = sum(fk[n]) / len(fk[n])
+        w_ = sum(wk.get(n, [0.0])) / max(1, len(wk.get(n, [])))
         us = avg_ns[n] / 1e3
-        lines.append(f"| `{n[:110]}` | {kn[n]} | {kf[n] / 1e6:.1f} | {kw.get(n, 0.0) / 1e6:.1f} | "
-                     f"{us:.1f} | {b / (us * 1e3):.0f} |")
+        lines.append(f"| `{n[:110]}` | {len(fk[n])} | {f_ / 1e6:.1f} | {w_ / 1e6:.1f} | "
+                     f"{us:.1f} | {(f_ + w_) / (us * 1e3):.0f} |")
     lines += ["", "Commands:", "", "```"] + [command[k] for k in ("fetch", "write", "copy_fetch",
                                                                     "copy_write")] + ["```"]
     os.makedirs(PROFILES, exist_ok=True)
@@ -315,9 +370,44 @@ def timed_step(layer, x, dy, marks):
     layer.backward(dy, mark=rec)
 
 
-def graph_replay(layer, x, dy, warmup, steps, T):
+class CacheFlush:
+    """Writes 1 GiB, then reads another 1 GiB, so that the next step finds
+    neither its own data nor dirty lines in the L2s or the 256 MB MALL."""
+
+    def __init__(self, device):
+        import torch
+        self.w = torch.empty(1 << 30, dtype=torch.uint8, device=device)
+        self.r = torch.ones(1 << 28, dtype=torch.int32, device=device)
+        self.n = 0
+
+    def __call__(self):
+        self.n += 1
+        self.w.fill_(self.n & 0xFF)
+        self.r.sum()
+
+
+def copy_peak(device, flush):
+    """A plain 1 GiB device-to-device copy (torch), after a flush: read +
+    written bytes over its event time, best of three."""
+    import torch
+    a = torch.ones(1 << 30, dtype=torch.uint8, device=device)
+    b = torch.empty_like(a)
+    best = 0.0
+    for _ in range(3):
+        flush()
+        e0, e1 = _event(), None
+        b.copy_(a)
+        e1 = _event()
+        torch.cuda.synchronize()
+        best = max(best, 2 * (1 << 30) / e0.elapsed_time(e1) / 1e6)
+    del a, b
+    return best
+
+
+def graph_replay(layer, x, dy, warmup, steps, T, flush):
     """The whole step captured once into a HIP graph (every library call
-    only enqueues and reads its shapes from device memory), then replayed."""
+    only enqueues and reads its shapes from device memory), then replayed,
+    each replay after a cache flush."""
     import torch
     g = torch.cuda.CUDAGraph()
     torch.cuda.synchronize()
@@ -326,12 +416,14 @@ def graph_replay(layer, x, dy, warmup, steps, T):
     for _ in range(warmup):
         g.replay()
     torch.cuda.synchronize()
-    start = _event()
+    ts = []
     for _ in range(steps):
+        flush()
+        a = _event()
         g.replay()
-    stop = _event()
+        ts.append((a, _event()))
     torch.cuda.synchronize()
-    ms = start.elapsed_time(stop) / steps
+    ms = sum(a.elapsed_time(b) for a, b in ts) / steps
     return {"ms_per_step": round(ms, 4), "tokens_per_s": round(T / (ms / 1e3), 1)}
 
 
@@ -342,30 +434,133 @@ def _event():
     return e
 
 
+def cpu_model():
+    """The host CPU's model name and logical CPU count (/proc/cpuinfo)."""
+    try:
+        names = [l.split(":", 1)[1].strip() for l in open("/proc/cpuinfo") if l.startswith("model name")]
+        return (names[0] if names else "unknown"), len(names)
+    except OSError:  # pragma: no cover
+        return "unknown", os.cpu_count()
+
+
 def cpu_baseline(cfg, sample_tokens):
     """The CPU oracle, as it stands, on the first `sample_tokens` tokens of the
-    same workload (all experts' weights, full forward + backward)."""
-    import numpy as np  # noqa: F401
+    same workload: routing, dispatch, every expert's SwiGLU FFN forward and
+    backward (expert by expert over all experts' weights), combine, and the
+    router backward, in fp64."""
     import moe_synth as S
     import oracle
     sub = cfg.replace(T=sample_tokens)
     x = S.x(cfg)[:sample_tokens]
     dy = S.dy(cfg)[:sample_tokens]
-    w1, w2 = S.all_expert_weights(cfg, threads=16)
-    inp = dict(x=x, wr=S.w_router(cfg), bias=S.router_bias(cfg), w1=w1, w2=w2, dy=dy)
+    inp = dict(x=x, wr=S.w_router(cfg), bias=S.router_bias(cfg), dy=dy,
+               w1=lambda e: S.expert_w1(cfg, e), w2=lambda e: S.expert_w2(cfg, e))
     if cfg.shared:
         inp.update(sw1=S.shared_w1(cfg), sw2=S.shared_w2(cfg))
     t0 = time.perf_counter()
-    oracle.layer(sub, inp)
+    oracle.layer_stream(sub, inp)
     dt = time.perf_counter() - t0
+    threads = os.environ.get("OMP_NUM_THREADS")
     try:
         from threadpoolctl import threadpool_info
-        cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [int(threads or 1)])
     except Exception:  # pragma: no cover
-        cores = os.cpu_count()
-    return {"value": sample_tokens / dt, "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
-            "sample": f"first {sample_tokens} of {cfg.T} tokens of {cfg.name}, full layer fwd+bwd "
-                      f"in fp64 over all {cfg.E} experts' weights; {dt:.1f} s"}
+        cores = int(threads or os.cpu_count())
+    model, logical = cpu_model()
+    return {"value": round(sample_tokens / dt, 3), "unit": "tokens/s", "cores": int(cores),
+            "kind": "oracle", "cpu": model, "host_logical_cpus": logical,
+            "sample": f"first {sample_tokens} of {cfg.T} tokens of {cfg.name}: the full layer forward "
+                      f"+ backward in fp64 (numpy/OpenBLAS and the C spec with OpenMP), every routed "
+                      f"expert's weights quantised and streamed; {dt:.1f} s"}
+
+
+def run_config(cfg, args, dev, flush, copy_gbps):
+    """Warm-up, then `steps` timed steps, each after a cache flush; returns
+    the workload's figures (times from events on the library's stream)."""
+    import torch
+    layer, x, dy = make_layer(cfg, dev, args.recompute)
+    for _ in range(args.warmup):
+        timed_step(layer, x, dy, [])
+    torch.cuda.synchronize()
+    steps = []
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        flush()
+        marks = []
+        timed_step(layer, x, dy, marks)
+        steps.append(marks)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    step_ms = sorted(m[0][1].elapsed_time(m[-1][1]) for m in steps)
+    ms = sum(step_ms) / len(step_ms)
+    per = {}
+    for marks in steps:
+        for (_, a), (name, b) in zip(marks[:-1], marks[1:]):
+            per.setdefault(name, []).append(a.elapsed_time(b))
+    per_ms = {n: sum(v) / len(v) for n, v in per.items()}
+    work = stage_work(cfg)
+    dt = "fp8" if cfg.weight in ("fp8", "mxfp8") else cfg.act
+    stages = {}
+    for n, t in per_ms.items():
+        b, fl = work[n]
+        stages[n] = {"ms": round(t, 4), "GBps": round(b / t / 1e6, 1),
+                     "TFLOPs": round(fl / t / 1e9, 1) if fl else 0.0}
+    dom = max(per_ms, key=per_ms.get)
+    b, fl = work[dom]
+    # the binding roofline of the dominant call: its flops at the matrix
+    # cores' peak or its algorithmic bytes at the HBM peak, whichever takes
+    # longer (the expert FFN of 256-expert layers streams more weight bytes
+    # than it has flops to hide them behind)
+    mfma_bound = fl and fl / (MFMA_PEAK_TFLOPS[dt] * 1e12) >= b / (HBM_PEAK_GBPS * 1e9)
+    if "ffn" in dom:
+        traffic = measured_traffic(cfg.name, dom)
+        traffic = None if traffic is None else round(traffic)
+        kname = f"moe_{dom.replace('shared_', 'grouped_')} ({dom})"
+    else:
+        traffic, kname = None, dom
+    if mfma_bound:
+        ach = fl / per_ms[dom] / 1e9
+        roof = {"kernel": kname, "bound": "mfma", "achieved": round(ach, 1), "peak": MFMA_PEAK_TFLOPS[dt],
+                "unit": "TFLOP/s", "frac": round(ach / MFMA_PEAK_TFLOPS[dt], 4), "traffic": traffic,
+                "algorithmic_flops": fl, "ms": round(per_ms[dom], 4)}
+    else:
+        ach = b / per_ms[dom] / 1e6
+        roof = {"kernel": kname, "bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBPS,
+                "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBPS, 4), "traffic": traffic,
+                "algorithmic_bytes": round(b), "ms": round(per_ms[dom], 4)}
+    ffn_f = sum(work[n][1] for n in per_ms if "ffn" in n)
+    ffn_t = sum(per_ms[n] for n in per_ms if "ffn" in n)
+    hbm = {}
+    for n in ("dispatch", "combine", "combine_bwd", "dispatch_bwd"):
+        gbps = work[n][0] / per_ms[n] / 1e6
+        hbm[n] = {"GBps": round(gbps, 1), "frac_of_8TBps": round(gbps / HBM_PEAK_GBPS, 4),
+                  "frac_of_copy": round(gbps / copy_gbps, 4)}
+    dc = (work["dispatch"][0] + work["combine"][0]) / (per_ms["dispatch"] + per_ms["combine"]) / 1e6
+    out = {
+        "workload": f"{cfg.name}: MoE layer fwd+bwd, T={cfg.T} d={cfg.d} E={cfg.E}"
+                    f"{'+1 shared' if cfg.shared else ''} top-{cfg.k} {cfg.score}"
+                    f"{' renorm' if cfg.renorm else ''}, SwiGLU d_ff={cfg.f}, {cfg.weight}"
+                    f"{f', aux loss {cfg.aux_coeff:g}' if cfg.aux_coeff else ''}",
+        "tokens_per_s": round(cfg.T / (ms / 1e3), 1),
+        "ms_per_step": round(ms, 4),
+        "ms_per_step_median": round(step_ms[len(step_ms) // 2], 4),
+        "ms_per_step_min": round(step_ms[0], 4),
+        "dtype": dt,
+        "dispatch_combine_GBps": round(dc, 1),
+        "dispatch_combine_frac_of_8TBps": round(dc / HBM_PEAK_GBPS, 4),
+        "dispatch_combine_frac_of_copy": round(dc / copy_gbps, 4),
+        "hbm_stages": hbm,
+        "grouped_gemm_mfma_pct": round(100 * ffn_f / ffn_t / 1e9 / MFMA_PEAK_TFLOPS[dt], 2),
+        "stages": stages,
+        "roofline": roof,
+        "wall_s": round(wall, 3),
+    }
+    if args.graph:
+        out["graph"] = graph_replay(layer, x, dy, args.warmup, args.steps, cfg.T, flush)
+    del layer, x, dy
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return out
 
 
 def vendor_gemm(name):
@@ -420,7 +615,9 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--config", default="mixtral_bf16")
+    ap.add_argument("--config", default="all",
+                    help="one workload (see moe_synth), or all: the headline workload first, then "
+                         "the others in the same line")
     ap.add_argument("--aux-coeff", type=float, default=0.0,
                     help="load-balancing auxiliary loss coefficient (0.01 in the Megatron recipe; "
                          "0: off, as in the workloads' definitions)")
@@ -429,7 +626,7 @@ def main():
                          "GU only (act), nothing (full)")
     ap.add_argument("--graph", action="store_true",
                     help="also capture the step into one HIP graph and time its replays")
-    ap.add_argument("--cpu-sample", type=int, default=4096,
+    ap.add_argument("--cpu-sample", type=int, default=CPU_SAMPLE_TOKENS,
                     help="tokens of the workload timed on the CPU oracle (0: skip)")
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run a plain 1 GiB device copy (counter calibration)")
@@ -484,101 +681,60 @@ def main():
 
     import torch
     import moe_synth as S
-    cfg = S.BY_NAME[args.config]
-    if args.aux_coeff:
-        cfg = cfg.replace(aux_coeff=args.aux_coeff)
+    if args.config == "all":
+        order = [HEADLINE] + [n for n in CONTEXT_CONFIGS]
+    else:
+        order = [args.config]
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    layer, x, dy = make_layer(cfg, dev, args.recompute)
-
-    for _ in range(args.warmup):
-        timed_step(layer, x, dy, [])
-    torch.cuda.synchronize()
-
-    steps = []
-    t0 = time.perf_counter()
-    start = _event()
-    for _ in range(args.steps):
-        marks = []
-        timed_step(layer, x, dy, marks)
-        steps.append(marks)
-    stop = _event()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    ms = start.elapsed_time(stop) / args.steps
-
-    # each step from its first to its last event: median and minimum
-    step_ms = sorted(m[0][1].elapsed_time(m[-1][1]) for m in steps)
-    per = {}
-    for marks in steps:
-        for (_, a), (name, b) in zip(marks[:-1], marks[1:]):
-            per.setdefault(name, []).append(a.elapsed_time(b))
-    per_ms = {n: sum(v) / len(v) for n, v in per.items()}
-    work = stage_work(cfg)
-    dt = "fp8" if cfg.weight in ("fp8", "mxfp8") else cfg.act
-    stages = {}
-    for n, t in per_ms.items():
-        b, fl = work[n]
-        stages[n] = {"ms": round(t, 4), "GBps": round(b / t / 1e6, 1),
-                     "TFLOPs": round(fl / t / 1e9, 1) if fl else 0.0}
-    dom = max(per_ms, key=per_ms.get)
-    b, fl = work[dom]
-    # the binding roofline of the dominant call: its flops at the matrix
-    # cores' peak or its algorithmic bytes at the HBM peak, whichever takes
-    # longer (the expert FFN of 256-expert layers streams more weight bytes
-    # than it has flops to hide them behind)
-    mfma_bound = fl and fl / (MFMA_PEAK_TFLOPS[dt] * 1e12) >= b / (HBM_PEAK_GBPS * 1e9)
-    if "ffn" in dom:
-        traffic = measured_traffic(cfg.name, dom)
-        traffic = None if traffic is None else round(traffic)
-        kname = f"moe_{dom.replace('shared_', 'grouped_')} ({dom})"
-    else:
-        traffic, kname = None, dom
-    if mfma_bound:
-        ach = fl / per_ms[dom] / 1e9
-        roof = {"kernel": kname, "bound": "mfma", "achieved": round(ach, 1), "peak": MFMA_PEAK_TFLOPS[dt],
-                "unit": "TFLOP/s", "frac": round(ach / MFMA_PEAK_TFLOPS[dt], 4), "traffic": traffic}
-    else:
-        ach = b / per_ms[dom] / 1e6
-        roof = {"kernel": kname, "bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBPS,
-                "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBPS, 4), "traffic": traffic,
-                "algorithmic_bytes": round(b)}
-
-    ffn_f = sum(work[n][1] for n in per_ms if "ffn" in n)
-    ffn_t = sum(per_ms[n] for n in per_ms if "ffn" in n)
-    dc_b = work["dispatch"][0] + work["combine"][0]
-    dc_t = per_ms["dispatch"] + per_ms["combine"]
+    flush = CacheFlush(dev)
+    copy_gbps = copy_peak(dev, flush)
+    results = {}
+    for name in order:
+        cfg = S.BY_NAME[name]
+        if args.aux_coeff:
+            cfg = cfg.replace(aux_coeff=args.aux_coeff)
+        print(f"[bench] {name}", file=sys.stderr, flush=True)
+        results[name] = run_config(cfg, args, dev, flush, copy_gbps)
+    head = results[order[0]]
+    cfg = S.BY_NAME[order[0]]
     out = {
         "metric": "MoE layer tokens/s; dispatch/combine HBM GB/s; grouped-GEMM MFMA % of peak",
-        "value": round(cfg.T / (ms / 1e3), 1),
+        "value": head["tokens_per_s"],
         "unit": "tokens/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(ms, 4),
-        "ms_per_step_median": round(step_ms[len(step_ms) // 2], 4),
-        "ms_per_step_min": round(step_ms[0], 4),
+        "ms_per_step": head["ms_per_step"],
+        "ms_per_step_median": head["ms_per_step_median"],
+        "ms_per_step_min": head["ms_per_step_min"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": dt,
+        "dtype": head["dtype"],
         "data": "synthetic (seeded normal inputs and random-init weights of the layer's shape)",
-        "config": {"workload": f"{cfg.name}: MoE layer fwd+bwd, T={cfg.T} d={cfg.d} E={cfg.E}"
-                               f"{'+1 shared' if cfg.shared else ''} top-{cfg.k} {cfg.score}"
-                               f"{' renorm' if cfg.renorm else ''}, SwiGLU d_ff={cfg.f}"
-                               f"{f', aux loss {cfg.aux_coeff:g}' if cfg.aux_coeff else ''}",
-                   "tokens": cfg.T, "hidden": cfg.d, "experts": cfg.E, "top_k": cfg.k,
-                   "ffn_hidden": cfg.f, "parallelism": "none (one GPU)"},
-        "dispatch_combine_GBps": round(dc_b / dc_t / 1e6, 1),
-        "grouped_gemm_mfma_pct": round(100 * ffn_f / ffn_t / 1e9 / MFMA_PEAK_TFLOPS[dt], 2),
-        "stages": stages,
-        "roofline": roof,
-        "wall_s": round(wall, 3),
+        "config": {"workload": head["workload"], "tokens": cfg.T, "hidden": cfg.d, "experts": cfg.E,
+                   "shared_experts": cfg.shared, "top_k": cfg.k, "ffn_hidden": cfg.f,
+                   "parallelism": "none (one GPU)",
+                   "timing": "HIP events around each step on the library's stream; 1 GiB written "
+                             "and 1 GiB read before every timed step, outside the events"},
+        "copy_peak_GBps": round(copy_gbps, 1),
+        "dispatch_combine_GBps": head["dispatch_combine_GBps"],
+        "dispatch_combine_frac_of_8TBps": head["dispatch_combine_frac_of_8TBps"],
+        "dispatch_combine_frac_of_copy": head["dispatch_combine_frac_of_copy"],
+        "hbm_stages": head["hbm_stages"],
+        "grouped_gemm_mfma_pct": head["grouped_gemm_mfma_pct"],
+        "stages": head["stages"],
+        "roofline": head["roofline"],
+        "wall_s": head["wall_s"],
     }
     if args.recompute != "none":
         out["config"]["recompute"] = args.recompute
-    if args.graph:
-        out["graph"] = graph_replay(layer, x, dy, args.warmup, args.steps, cfg.T)
+    if "graph" in head:
+        out["graph"] = head["graph"]
+    if len(order) > 1:
+        out["configs"] = {n: {k: v for k, v in r.items() if k != "stages"} | {"stages": r["stages"]}
+                          for n, r in results.items() if n != order[0]}
     if args.cpu_sample > 0:
         out["cpu_baseline"] = cpu_baseline(cfg, args.cpu_sample)
     print(json.dumps(out))

@@ -31,6 +31,14 @@
  *    device-to-host copy, no host read of counts or offsets.
  *  - All argument checks run on the host before any launch; on failure a
  *    negative MOE_ERR_* code is returned and nothing is enqueued.
+ *  - Sizes (MOE_ERR_INVALID_ARG otherwise): d and f are multiples of 128,
+ *    for every dtype: the expert GEMMs tile the hidden and expert dimensions
+ *    in blocks of 128 and the contraction in whole K steps, with no partial
+ *    block (a finer multiple, such as 8 for 16-byte rows, is not taken).
+ *    One expert's W1 ([2f, d] in the weight dtype) stays below 4 GiB, since
+ *    the GEMMs address operands with 32-bit offsets from a per-step base;
+ *    an [A, max(d, 2f)] tensor holds at most 2^38 elements (more than one
+ *    GPU's memory), which also keeps every grid below 2^28 workgroups.
  *  - num_tokens == 0 is valid. Buffers with T or A rows may then be NULL
  *    and are not touched; outputs whose size does not depend on T get their
  *    exact values, by a fill kernel: zero counts and offsets (moe_dispatch),

@@ -282,11 +282,17 @@ __device__ __forceinline__ void store_transposed(const u32x4* r, T* dst, int c0,
 
 // Raw buffer descriptors (gfx9 family: stride 0, 32-bit untyped data). A
 // load whose byte offset lies at or past `bytes` returns zeros, which masks
-// rows past the end of a group without branches.
+// rows past the end of a group without branches. The range field is 32 bits:
+// a longer remaining range is clamped to 2^32 - 1, which masks nothing that
+// a load of the step can reach (every offset a step uses is a 32-bit offset
+// from the step's own base, and the host rejects shapes whose per-step
+// offsets could pass 4 GiB).
 typedef __amdgpu_buffer_rsrc_t rsrc_t;
+__device__ __forceinline__ uint32_t rsrc_range(int64_t bytes) {
+  return bytes <= 0 ? 0u : (bytes >= int64_t(0xffffffff) ? 0xffffffffu : uint32_t(bytes));
+}
 __device__ __forceinline__ rsrc_t make_rsrc(const void* base, int64_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0,
-                                           int(uint32_t(bytes > 0 ? bytes : 0)), 0x00020000);
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, int(rsrc_range(bytes)), 0x00020000);
 }
 // One wave instruction of DMA: every lane's 16 bytes at byte offset voff of
 // the buffer described by rsrc go to LDS at dst + 16 * lane (dst is
@@ -297,7 +303,7 @@ __device__ __forceinline__ rsrc_t make_rsrc(const void* base, int64_t bytes) {
 // loop therefore waits for its DMA explicitly (vmcnt) before each barrier.
 __device__ __forceinline__ u32x4 rsrc_words(const void* base, int64_t bytes) {
   const uint64_t a = reinterpret_cast<uint64_t>(base);
-  return u32x4{uint32_t(a), uint32_t(a >> 32) & 0xffffu, uint32_t(bytes > 0 ? bytes : 0), 0x00020000u};
+  return u32x4{uint32_t(a), uint32_t(a >> 32) & 0xffffu, rsrc_range(bytes), 0x00020000u};
 }
 __device__ __forceinline__ void dma16(u32x4 rsrc, void* dst, uint32_t voff) {
   const uint32_t lds = uint32_t(reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) char*)dst));

@@ -29,6 +29,26 @@ int weight_kind(const moe_config* c) {
   }
 }
 
+// Limits of the kernels' addressing, checked in 64-bit arithmetic:
+//  - the grouped GEMMs address operands through buffer descriptors with
+//    32-bit offsets from a per-K-step base; the largest such offset is a
+//    row of one expert's weight matrix away from its start, so one expert's
+//    W1 ([2f, d]) must stay below 4 GiB;
+//  - tile counts (grid sizes) of every GEMM stay within 2^30 workgroups;
+//  - no [A, max(d, 2f)] activation tensor exceeds 2^38 elements (more than
+//    one GPU's memory holds), which keeps the element-wise grids in range.
+int check_sizes(const moe_config* c) {
+  const int64_t T = c->num_tokens, d = c->hidden, E = c->num_experts, k = c->top_k, f = c->ffn_hidden;
+  const int64_t wb = c->weight_dtype == MOE_DTYPE_F32 ? 4 : (c->weight_dtype == MOE_DTYPE_BF16 ? 2 : 1);
+  if (2 * f * d * wb > int64_t(0xffffffff)) return MOE_ERR_INVALID_ARG;
+  const int64_t A = T * k, wide = d > 2 * f ? d : 2 * f;
+  if (A * wide > (int64_t(1) << 38)) return MOE_ERR_INVALID_ARG;
+  const int64_t row_tiles = (A + E * 127) / 128;  // the smallest row tile
+  if (row_tiles * (wide / 128) > (int64_t(1) << 30)) return MOE_ERR_INVALID_ARG;
+  if (E * (2 * f / 128) * (d / 128) > (int64_t(1) << 30)) return MOE_ERR_INVALID_ARG;
+  return MOE_OK;
+}
+
 // Validates the configuration; returns MOE_OK or an error code.
 int check_cfg(const moe_config* c) {
   if (!c) return MOE_ERR_INVALID_ARG;
@@ -67,7 +87,7 @@ int check_cfg(const moe_config* c) {
   } else if (c->weight_dtype != c->act_dtype) {
     return MOE_ERR_UNSUPPORTED_DTYPE;
   }
-  return MOE_OK;
+  return check_sizes(c);
 }
 
 #define MOE_CHECK(expr)          \

@@ -280,6 +280,17 @@ def fp8_roundtrip_rows(a, block: int = 128) -> np.ndarray:
     return dequant_blocks(q, s, 1, block)
 
 
+def fp8_roundtrip_tokens(a, block: int = 128) -> np.ndarray:
+    """Quantise one expert's rows [M, C] (from fp32) in blocks of `block`
+    consecutive rows x 1 column and dequantise (fp64): the operands of a
+    weight-gradient product, whose contraction runs over the expert's rows.
+    The blocks start at the expert's first row; the last one holds the
+    M mod block remaining rows, which is what zero-padding it to a whole
+    block would give (zeros change neither the amax nor the kept codes)."""
+    q, s = quant_blocks(np.asarray(a, dtype=np.float32), block, 1)
+    return dequant_blocks(q, s, block, 1)
+
+
 # ------------------------------------------------------------ MXFP8
 
 MX_BLOCK = 32
@@ -363,7 +374,7 @@ def ffn_fwd(X, W1, W2, identity: bool = False, h_fp8: bool = False, h_quant=None
 
 
 def ffn_bwd(X, W1, W2, GU, H, dO, identity: bool = False, dgrad_fp8: bool = False,
-            dgrad_quant=None, W1d=None, W2d=None):
+            dgrad_quant=None, W1d=None, W2d=None, wgrad_quant=None):
     """Backward of ffn_fwd for one expert's rows (fp64).
       dH  = dO W2                    dW2 = dO^T H
       dG  = dH * U * s(G) * (1 + G (1 - s(G)))   (silu'(G) = s + G s (1 - s))
@@ -377,6 +388,11 @@ def ffn_bwd(X, W1, W2, GU, H, dO, identity: bool = False, dgrad_fp8: bool = Fals
     quantise-dequantise of the gradient operands (MXFP8: 1 x 32 blocks), and
     W1d / W2d replace W1 / W2 in the two data-gradient products (MXFP8
     weights quantised in 32 x 1 blocks along those products' contraction).
+    wgrad_quant, when given, is applied to every operand of the two weight-
+    gradient products (dO and H for dW2, [dG dU] and X for dW1) before they
+    are contracted over the expert's rows (FP8 layers: 128-row x 1 blocks,
+    fp8_roundtrip_tokens); without it they take the unquantised gradients
+    and the forward's (dequantised) X and H.
     Returns dX, dW1, dW2, dGU."""
     dO = np.asarray(dO, dtype=np.float64)
     if identity:
@@ -392,14 +408,15 @@ def ffn_bwd(X, W1, W2, GU, H, dO, identity: bool = False, dgrad_fp8: bool = Fals
     W2d = W2 if W2d is None else np.asarray(W2d, dtype=np.float64)
     dOq = dgrad_quant(dO.astype(np.float32)) if dgrad_quant else dO
     dH = dOq @ W2d
-    dW2 = dO.T @ H
+    wq = wgrad_quant if wgrad_quant is not None else (lambda a: a)
+    dW2 = wq(dO).T @ wq(H)
     s = sigmoid64(G)
     dG = dH * U * s * (1.0 + G * (1.0 - s))
     dU = dH * G * s
     dGU = np.concatenate([dG, dU], axis=1)
     dGUq = dgrad_quant(dGU.astype(np.float32)) if dgrad_quant else dGU
     dX = dGUq @ W1d
-    dW1 = dGU.T @ X
+    dW1 = wq(dGU).T @ wq(X)
     return dX, dW1, dW2, dGU
 
 
@@ -528,44 +545,71 @@ def aux_loss_dlogits(logits, idx, E: int, coeff: float, d_aux: float = 1.0) -> n
 
 # -------------------------------------------------------- the whole layer
 
-def layer(cfg, inp: dict, identity: bool = False) -> dict:
-    """Forward and backward of one MoE layer on the CPU, every tensor.
+# FP8 layers: whether the weight-gradient operands are quantised in 128-row x 1
+# blocks (fp8_roundtrip_tokens) or taken unquantised (the forward's
+# dequantised X and H, the bf16 gradients)
+FP8_WGRAD_TOKEN_BLOCKS = False
 
-    inp: x [T,d], wr [E,d], bias [E] or None, w1 [E,2f,d], w2 [E,d,f],
-    sw1/sw2 (shared expert, when cfg.shared), dy [T,d]; torch or numpy.
+
+def _expert_weight(w, e):
+    """Expert e's weight from a stacked [E, ...] array/tensor or a callable."""
+    return w(e) if callable(w) else w[e]
+
+
+def layer_stream(cfg, inp: dict, identity: bool = False, on_expert=None,
+                 fp8_wgrad: Optional[bool] = None) -> dict:
+    """Forward and backward of one MoE layer on the CPU, one expert at a
+    time, so that no tensor with an expert dimension is ever held whole.
+
+    inp: x [T,d], wr [E,d], bias [E] or None, dy [T,d], w1 and w2 (a stacked
+    [E,2f,d] / [E,d,f] array or tensor, or a callable e -> that expert's
+    weight), sw1/sw2 (shared expert, when cfg.shared); torch or numpy.
     For fp8 weights the oracle quantises the bf16 masters itself in
-    128 x 128 blocks and the dispatched rows per 1 x 128 block. For mxfp8
-    every operand of the six expert products is quantised in blocks of 32
-    along that product's contraction dimension with E8M0 scales: x, H, dO
-    and [dG dU] in 1 x 32 row blocks; W1 and W2 in row blocks for the
-    forward and in 32 x 1 column blocks for the data gradients; the weight
-    gradients take the dequantised x and H and the unquantised gradients.
+    128 x 128 blocks and the dispatched rows per 1 x 128 block; H, dO and
+    [dG dU] are quantised per 1 x 128 before the product that contracts them
+    along their rows (ffn_fwd, ffn_bwd); with fp8_wgrad (default:
+    FP8_WGRAD_TOKEN_BLOCKS) the four operands of the weight-gradient products are
+    quantised in 128-row x 1 blocks inside each expert's rows
+    (fp8_roundtrip_tokens). For mxfp8 every operand of the six expert
+    products is quantised in blocks of 32 along that product's contraction
+    dimension with E8M0 scales: x, H, dO and [dG dU] in 1 x 32 row blocks;
+    W1 and W2 in row blocks for the forward and in 32 x 1 column blocks for
+    the data gradients; the weight gradients take the dequantised x and H and
+    the unquantised gradients.
+
+    on_expert(e, r0, r1, t), when given, is called for every expert in order
+    with its rows [r0, r1) of the dispatched order and t = dict(out_perm,
+    act_gu, act_h, d_out_perm, dx_perm (those rows), dw1, dw2, w_q (the
+    quantised weights, FP8 layers)), or t = None for an expert with no rows
+    (its weight gradients are zero). The returned dict holds every tensor
+    without an expert dimension.
     """
     E, k, f = cfg.E, cfg.k, cfg.f
     mx = cfg.weight == "mxfp8"
     fp8 = cfg.weight == "fp8"
+    if fp8_wgrad is None:
+        fp8_wgrad = fp8 and FP8_WGRAD_TOKEN_BLOCKS
     qb = cfg.quant_block
     h_quant = mx_roundtrip_rows if mx else (fp8_roundtrip_rows if fp8 else None)
+    w_quant = fp8_roundtrip_tokens if (fp8 and fp8_wgrad) else None
     out = {}
     L, idx, g = route(cfg, inp["x"], inp["wr"], inp.get("bias"))
     out.update(logits=L, idx=idx, gates=g)
     counts, offsets, rmap, ptok = dispatch_index(idx, E)
     out.update(counts=counts, offsets=offsets, row_id_map=rmap, perm_token=ptok)
+    T, d = cfg.T, cfg.d
     x32 = as_f32(inp["x"])
+    # the dispatched rows' values (dequantised for FP8 layers), per token
     if mx:
         xq, xs = quant_mx_rows(x32)
         out.update(xq=xq, x_scale=xs)
-        Xdq = dequant_mx_rows(xq, xs)
-        Xp = permute(Xdq, rmap)
-        out.update(xq_perm=permute(xq, rmap), x_scale_perm=permute(xs, rmap))
+        Xt = dequant_mx_rows(xq, xs)
     elif fp8:
         xq, xs = quant_blocks(x32, 1, qb)
         out.update(xq=xq, x_scale=xs)
-        Xp = permute(dequant_blocks(xq, xs, 1, qb), rmap)
-        out.update(xq_perm=permute(xq, rmap), x_scale_perm=permute(xs, rmap))
+        Xt = dequant_blocks(xq, xs, 1, qb)
     else:
-        Xp = permute(x32.astype(np.float64), rmap)
-        out["x_perm"] = permute(x32, rmap)
+        Xt = x32.astype(np.float64)
 
     def expert_weights(w1, w2):
         w1 = as_f32(w1)
@@ -583,61 +627,52 @@ def layer(cfg, inp: dict, identity: bool = False) -> dict:
         return (dequant_blocks(q1, s1, qb, qb), dequant_blocks(q2, s2, qb, qb),
                 (q1, s1, q2, s2))
 
-    A = cfg.T * k
-    d = cfg.d
-    O = np.zeros((A, d))
-    GU = np.zeros((A, 2 * f))
-    H = np.zeros((A, f))
-    W = []
-    for e in range(E):
-        W1, W2, q = expert_weights(inp["w1"][e], inp["w2"][e])
-        W.append((W1, W2, q))
-        r0, r1 = offsets[e], offsets[e + 1]
-        if r1 > r0:
-            gu, h, o = ffn_fwd(Xp[r0:r1], W1, W2, identity, h_quant=h_quant)
-            O[r0:r1] = o
-            if not identity:
-                GU[r0:r1] = gu
-                H[r0:r1] = h
-    out.update(out_perm=O, act_gu=GU, act_h=H)
-    if fp8 or mx:
-        out["w_q"] = [w[2] for w in W]
-    O_sh = None
-    if cfg.shared:
-        SW1, SW2, sq = expert_weights(inp["sw1"], inp["sw2"])
-        Xs = Xdq if mx else (dequant_blocks(xq, xs, 1, qb) if fp8 else x32.astype(np.float64))
-        sgu, sh, O_sh = ffn_fwd(Xs, SW1, SW2, identity, h_quant=h_quant)
-        out.update(shared_out=O_sh, shared_gu=sgu, shared_h=sh)
-    y = combine(O, rmap, g, O_sh)
-    out["y"] = y
-
-    # backward
     dy = as_f64(inp["dy"])
-    dO, dgate = combine_bwd(dy, O, rmap, g)
-    out.update(d_out_perm=dO, d_gate=dgate)
-    dXp = np.zeros((A, d))
-    dW1 = np.zeros((E, 2 * f, d))
-    dW2 = np.zeros((E, d, f))
+    # gate and slot of every dispatched row
+    gate_row = np.empty(T * k)
+    slot_row = np.empty(T * k, dtype=np.int64)
+    gate_row[rmap.reshape(-1)] = np.asarray(g, np.float64).reshape(-1)
+    slot_row[rmap.reshape(-1)] = np.tile(np.arange(k), T)
+    y = np.zeros((T, d))
+    dgate = np.zeros((T, k))
+    dx = np.zeros((T, d))
     for e in range(E):
-        r0, r1 = offsets[e], offsets[e + 1]
-        if r1 > r0:
-            W1, W2, wq = W[e]
-            dx_e, dw1, dw2, _ = ffn_bwd(Xp[r0:r1], W1, W2, GU[r0:r1], H[r0:r1],
-                                        dO[r0:r1], identity, dgrad_quant=h_quant,
-                                        W1d=wq["W1d"] if mx else None,
-                                        W2d=wq["W2d"] if mx else None)
-            dXp[r0:r1] = dx_e
-            if not identity:
-                dW1[e] = dw1
-                dW2[e] = dw2
-    out.update(dx_perm=dXp, dw1=dW1, dw2=dW2)
-    dx_sh = None
+        r0, r1 = int(offsets[e]), int(offsets[e + 1])
+        if r1 == r0:
+            if on_expert:
+                on_expert(e, r0, r1, None)
+            continue
+        toks = ptok[r0:r1]          # distinct tokens: one row per token and expert
+        Xe = Xt[toks]
+        if identity:
+            W1 = W2 = wq = None
+        else:
+            W1, W2, wq = expert_weights(_expert_weight(inp["w1"], e), _expert_weight(inp["w2"], e))
+        gu, h, o = ffn_fwd(Xe, W1, W2, identity, h_quant=h_quant)
+        ge = gate_row[r0:r1, None]
+        y[toks] += ge * o                                      # combine
+        dgate[toks, slot_row[r0:r1]] = np.einsum("rd,rd->r", dy[toks], o)
+        dOe = ge * dy[toks]                                    # combine backward
+        dxe, dw1, dw2, _ = ffn_bwd(Xe, W1, W2, gu, h, dOe, identity, dgrad_quant=h_quant,
+                                   W1d=wq["W1d"] if mx else None, W2d=wq["W2d"] if mx else None,
+                                   wgrad_quant=w_quant)
+        dx[toks] += dxe                                        # dispatch backward
+        if on_expert:
+            on_expert(e, r0, r1, dict(out_perm=o, act_gu=gu, act_h=h, d_out_perm=dOe, dx_perm=dxe,
+                                      dw1=dw1, dw2=dw2, w_q=wq))
     if cfg.shared:
-        dx_sh, sdw1, sdw2, _ = ffn_bwd(Xs, SW1, SW2, sgu, sh, dy, identity, dgrad_quant=h_quant,
+        SW1, SW2, sq = (None, None, None) if identity else expert_weights(inp["sw1"], inp["sw2"])
+        sgu, sh, O_sh = ffn_fwd(Xt, SW1, SW2, identity, h_quant=h_quant)
+        out.update(shared_out=O_sh, shared_gu=sgu, shared_h=sh)
+        y += O_sh
+        dx_sh, sdw1, sdw2, _ = ffn_bwd(Xt, SW1, SW2, sgu, sh, dy, identity, dgrad_quant=h_quant,
                                        W1d=sq["W1d"] if mx else None,
-                                       W2d=sq["W2d"] if mx else None)
+                                       W2d=sq["W2d"] if mx else None, wgrad_quant=w_quant)
         out.update(shared_dx=dx_sh, shared_dw1=sdw1, shared_dw2=sdw2)
-    dx = dispatch_bwd(dXp, rmap, dx_sh)
+        if fp8 or mx:
+            out["shared_w_q"] = sq
+        dx += dx_sh
+    out.update(y=y, d_gate=dgate)
     dL = route_bwd_logits(dgate, idx, L, cfg.score, cfg.renorm, cfg.gate_scale)
     if cfg.aux_coeff:
         # the auxiliary loss enters the step's total loss with weight 1
@@ -645,6 +680,43 @@ def layer(cfg, inp: dict, identity: bool = False) -> dict:
         dL = dL + aux_loss_dlogits(L, idx, E, cfg.aux_coeff, 1.0)
     dWr, dx_r = route_bwd(dL, inp["x"], inp["wr"])
     out.update(d_logits=dL, dw_router=dWr, dx=dx + dx_r, dx_router=dx_r)
+    return out
+
+
+def layer(cfg, inp: dict, identity: bool = False, fp8_wgrad: Optional[bool] = None) -> dict:
+    """Forward and backward of one MoE layer on the CPU, every tensor
+    (layer_stream, with the per-expert tensors gathered): x_perm (or the FP8
+    codes and scales xq_perm, x_scale_perm), out_perm, act_gu, act_h,
+    d_out_perm, dx_perm [A, ...] in dispatched order; dw1 [E,2f,d], dw2
+    [E,d,f]; w_q, each expert's quantised weights (FP8 layers); and every
+    tensor layer_stream returns. For small layers (it holds everything)."""
+    E, f, d, A = cfg.E, cfg.f, cfg.d, cfg.T * cfg.k
+    full = dict(out_perm=np.zeros((A, d)), act_gu=np.zeros((A, 2 * f)), act_h=np.zeros((A, f)),
+                d_out_perm=np.zeros((A, d)), dx_perm=np.zeros((A, d)),
+                dw1=np.zeros((E, 2 * f, d)), dw2=np.zeros((E, d, f)))
+    w_q = [None] * E
+
+    def keep(e, r0, r1, t):
+        if t is None:
+            return
+        for n in ("out_perm", "d_out_perm", "dx_perm"):
+            full[n][r0:r1] = t[n]
+        if not identity:
+            for n in ("act_gu", "act_h"):
+                full[n][r0:r1] = t[n]
+            full["dw1"][e] = t["dw1"]
+            full["dw2"][e] = t["dw2"]
+        w_q[e] = t["w_q"]
+
+    out = layer_stream(cfg, inp, identity, on_expert=keep, fp8_wgrad=fp8_wgrad)
+    rmap = out["row_id_map"]
+    if "xq" in out:
+        out.update(xq_perm=permute(out["xq"], rmap), x_scale_perm=permute(out["x_scale"], rmap))
+    else:
+        out["x_perm"] = permute(as_f32(inp["x"]), rmap)
+    out.update(full)
+    if cfg.weight in ("fp8", "mxfp8"):
+        out["w_q"] = w_q
     return out
 
 
@@ -657,45 +729,3 @@ def rel_l2(a, b) -> float:
     if nb == 0.0:
         return 0.0 if na == 0.0 else float("inf")
     return float(na / nb)
-
-
-def ffn_wgrad_columns(X, W1, W2, dO, cols, h_fp8: bool = False, quant=None, W2d=None):
-    """Selected slices of one expert's weight gradients, over all its rows:
-    for each hidden feature n in `cols`, rows n (gate) and f+n (up) of dW1
-    and column n of dW2 — the same formulas as ffn_bwd evaluated only where
-    asked (fp64). FP8 layers (h_fp8: 1 x 128 blocks; or quant, the
-    quantise-dequantise of the layer's format) quantise H in the forward and
-    dO before the dH product, which reads W2d (the weights of the data
-    gradients; W2 by default), as ffn_fwd and ffn_bwd do. Returns (dW1_rows
-    [2*len(cols), d] ordered gate rows then up rows, dW2_cols [d, len(cols)])."""
-    X = np.asarray(X, dtype=np.float64)
-    W1 = np.asarray(W1, dtype=np.float64)
-    W2 = np.asarray(W2, dtype=np.float64)
-    W2d = W2 if W2d is None else np.asarray(W2d, dtype=np.float64)
-    dO = np.asarray(dO, dtype=np.float64)
-    if h_fp8 and quant is None:
-        quant = fp8_roundtrip_rows
-    f = W2.shape[1]
-    cols = np.asarray(cols, dtype=np.int64)
-    G = X @ W1[cols].T                     # [M, c]
-    U = X @ W1[f + cols].T
-    dOq = quant(dO.astype(np.float32)) if quant else dO
-    dH = dOq @ W2d[:, cols]                # [M, c]
-    s = sigmoid64(G)
-    H = G * s * U
-    if quant:  # the forward's H is quantised in blocks of the full row
-        H = ffn_fwd(X, W1, W2, h_quant=quant)[1][:, cols]
-    dG = dH * U * s * (1.0 + G * (1.0 - s))
-    dU = dH * G * s
-    dW1_rows = np.concatenate([dG.T @ X, dU.T @ X], axis=0)
-    dW2_cols = dO.T @ H
-    return dW1_rows, dW2_cols
-
-
-def ffn_dx_rows(X, W1, W2, dO, fp8: bool = False, quant=None, W1d=None, W2d=None):
-    """dX for the given rows of one expert (fp64), as in ffn_bwd (FP8: fp8
-    for 1 x 128 blocks, or quant and the data-gradient weights W1d, W2d)."""
-    if fp8 and quant is None:
-        quant = fp8_roundtrip_rows
-    GU, H, _ = ffn_fwd(X, W1, W2, h_quant=quant)
-    return ffn_bwd(X, W1, W2, GU, H, dO, dgrad_quant=quant, W1d=W1d, W2d=W2d)[0]

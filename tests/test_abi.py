@@ -72,6 +72,31 @@ def test_config_validation(M):
     assert L.moe_workspace_size(ctypes.byref(_cfg(M, k=9)), 1) == 0
 
 
+def test_size_limits(M):
+    """Shapes whose GEMM operands or grids the kernels cannot address are
+    refused before any launch: one expert's W1 of 4 GiB or more (32-bit
+    buffer offsets from a per-step base), more than 2^38 elements in an
+    [A, max(d, 2f)] tensor, more than 2^30 GEMM tiles; and d or f that are
+    not multiples of 128, with bf16 and fp32 as with FP8 (the GEMM tiles)."""
+    # (valid shapes are seen through moe_workspace_size, which launches
+    # nothing: it returns 0 for a refused configuration)
+    ws = lambda **kw: M.lib().moe_workspace_size(ctypes.byref(_cfg(M, **kw)), 3)
+    # W1 = [2f, d]: 2 * 2^15 * 2^15 * 2 bytes = 4 GiB in bf16 (refused),
+    # 2 GiB in fp8 (taken), 4 GiB in fp32 at f = 2^14 (refused)
+    assert _route(M, _cfg(M, d=1 << 15, f=1 << 15)) == -1 and ws(d=1 << 15, f=1 << 15) == 0
+    assert ws(d=1 << 15, f=1 << 15, weight="fp8") > 0
+    assert ws(d=1 << 15, f=(1 << 15) - 128) > 0
+    assert _route(M, _cfg(M, d=1 << 15, f=1 << 14, act="f32", weight="f32")) == -1
+    assert ws(d=1 << 15, f=(1 << 14) - 128, act="f32", weight="f32") > 0
+    # A * max(d, 2f) > 2^38 elements: T = 2^26 tokens, k = 16, d = 2^13
+    assert _route(M, _cfg(M, T=1 << 26, E=16, k=16, d=1 << 13, f=128)) == -1
+    assert ws(T=1 << 26, E=16, k=16, d=256, f=128) > 0    # exactly 2^38
+    # (the tile-count limits follow from these two: under 4 GiB per W1 and
+    # 2^38 elements, no GEMM has more than 2^28 tiles)
+    for d, f, act in ((1000, 256, "bf16"), (256, 1000, "bf16"), (136, 256, "f32"), (256, 264, "f32")):
+        assert _route(M, _cfg(M, d=d, f=f, act=act, weight=act)) == -1, (d, f, act)
+
+
 def test_empty_batch_enqueues_nothing(M):
     """T = 0: the calls whose outputs all have T rows return at once and
     accept NULL buffers (an empty tensor has no storage). The calls that

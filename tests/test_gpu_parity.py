@@ -4,9 +4,9 @@ Integer and index outputs (logits under the fixed fp32 order, top-k indices,
 counts, offsets, row map, token permutation, dispatched rows) are compared bit
 for bit; floating-point outputs by relative L2 error against the fp64 oracle
 with the tolerance of their precision: 1e-5 (fp32), 2e-2 (bf16), 6e-2 (fp8).
-Small layers are compared on every element; full-size layers on every
-routing/dispatch element, the whole forward output, and sampled gradients
-that the oracle evaluates one slice at a time.
+Small layers and full-size layers are compared on every element; at full
+size the oracle runs expert by expert and the comparison accumulates each
+tensor's error piece by piece.
 """
 import os
 import sys
@@ -327,6 +327,74 @@ def test_fp8_dispatch_bit_exact():
     assert np.array_equal(_np(out["xs"]), oracle.permute(xs, rmap))
 
 
+def _route_sigmoid_gates(x, bias=None):
+    """moe_route with 16 experts, top-16, sigmoid scores, no renormalisation
+    and gate scale 1, so that every gate is the sigmoid of one logit: x
+    [T, 128] f32 on the device, w_router the identity on the first 16 hidden
+    columns. Returns (logits, idx, gates) on the device."""
+    from mixture_experts_layer_gather_amd import make_config, moe_route
+    T = x.shape[0]
+    c = make_config(T=T, d=128, E=16, k=16, f=128, score="sigmoid", renorm=False, gate_scale=1.0,
+                    act="f32", weight="f32")
+    wr = torch.zeros(16, 128, dtype=torch.float32, device=DEV)
+    wr[:, :16] = torch.eye(16, device=DEV)
+    logits = torch.empty(T, 16, dtype=torch.float32, device=DEV)
+    idx = torch.empty(T, 16, dtype=torch.int32, device=DEV)
+    gate = torch.empty(T, 16, dtype=torch.float32, device=DEV)
+    moe_route(c, x, wr, bias, logits, idx, gate)
+    return logits, idx, gate
+
+
+def test_sigmoid_spec_every_fp32_input():
+    """The GPU's sigmoid score (1 / (1 + exp_spec(-L)) with an IEEE divide),
+    which decides the group choice of DeepSeek-style routing, against the
+    oracle's sigmoid_spec bit for bit over every fp32 bit pattern. Finite
+    values go in as logits through the identity router (the fp32 FMA
+    recurrence then returns each value itself; -0 becomes +0, whose sigmoid
+    is the same); infinities and NaNs, for which the recurrence's x * 0
+    terms would not vanish, go in as the expert bias of an all-zero token."""
+    T = 1 << 22                        # tokens per launch, 16 values each
+    per = 16 * T
+    zero_tail = torch.zeros(T, 112, dtype=torch.float32, device=DEV)
+    nfin = 0
+    for lo in range(0, 1 << 32, per):
+        bits = np.arange(lo, lo + per, dtype=np.uint64).astype(np.uint32)
+        v = bits.view(np.float32).reshape(T, 16)
+        finite = np.isfinite(v)
+        if not finite.all():
+            v = np.where(finite, v, np.float32(0.0))
+        want = oracle.sigmoid_spec(v)
+        x = torch.cat([torch.from_numpy(v).to(DEV), zero_tail], dim=1)
+        _, idx, gate = _route_sigmoid_gates(x)
+        w = torch.from_numpy(want.view(np.int32)).to(DEV)
+        ok = torch.equal(torch.gather(w, 1, idx.long()), gate.view(torch.int32))
+        if not ok:
+            got = gate.view(torch.int32).cpu().numpy()
+            exp_ = np.take_along_axis(want.view(np.int32), idx.long().cpu().numpy(), axis=1)
+            t, j = np.argwhere(got != exp_)[0]
+            e = int(idx[t, j])
+            raise AssertionError(f"sigmoid of {v[t, e]!r} (bits {int(v[t, e:e+1].view(np.uint32)[0]):#x}): "
+                                 f"GPU {got[t, j]:#x}, oracle {exp_[t, j]:#x}")
+        nfin += int(finite.sum())
+        if lo % (1 << 30) == 0:
+            _say(f"[sigmoid] {lo:#x}: ok")
+    assert nfin == (1 << 32) - (1 << 24)          # every finite fp32
+    # the 2^24 non-finite patterns: +-inf and a spread of NaN payloads
+    specials = np.array([0x7F800000, 0xFF800000, 0x7FC00000, 0xFFC00000, 0x7F800001, 0xFF800001,
+                         0x7FFFFFFF, 0xFFFFFFFF, 0x7FA00000, 0xFFA00000, 0x7FBFFFFF, 0xFFBFFFFF,
+                         0x7FE00000, 0xFFE00000, 0x7F812345, 0xFF812345], dtype=np.uint32)
+    b = specials.view(np.float32)
+    _, idx, gate = _route_sigmoid_gates(torch.zeros(1, 128, dtype=torch.float32, device=DEV),
+                                        bias=torch.from_numpy(b.copy()).to(DEV))
+    want = oracle.sigmoid_spec(b)
+    got = gate.cpu().numpy()[0]
+    for j, e in enumerate(idx.cpu().numpy()[0]):
+        if np.isnan(want[e]):
+            assert np.isnan(got[j]), hex(specials[e])
+        else:
+            assert got[j].view(np.int32) == want[e].view(np.int32), hex(specials[e])
+
+
 # (T, E): 64 experts per workgroup (>= 512 workgroups) and 32 per workgroup,
 # with ragged token and expert tiles
 ROUTE_TILE_CASES = [(16384, 128), (300, 64), (1000, 96), (8192, 72)]
@@ -397,119 +465,84 @@ def test_dispatch_index_paths(T, E, k, skew):
 
 # ------------------------------------------------------------ full sizes
 
-def _full_size_check(cfg, n_tok=24, n_cols=3):
+class _L2:
+    """Running ||a - b||^2 and ||b||^2 of one tensor, compared piece by piece."""
+
+    def __init__(self):
+        self.num = 0.0
+        self.den = 0.0
+
+    def add(self, got, want):
+        a = np.asarray(got, dtype=np.float64)
+        b = np.asarray(want, dtype=np.float64)
+        self.num += float(np.sum((a - b) ** 2))
+        self.den += float(np.sum(b * b))
+
+    def rel(self):
+        return 0.0 if self.den == 0.0 and self.num == 0.0 else float(np.sqrt(self.num / self.den))
+
+
+OUTPUTS = ("y", "dx", "dw1", "dw2", "dw_router", "d_gate", "out_perm", "dx_perm", "x_perm")
+
+
+def _full_size_check(cfg):
+    """Every element of every output of a full-size layer against the
+    oracle, which runs expert by expert (layer_stream) so that it never holds
+    a whole weight gradient; and a second GPU step, bitwise equal."""
     _say(f"[full] {cfg.name}: generating inputs")
     inp = _inputs(cfg, threads=16)
-    _say(f"[full] {cfg.name}: GPU layer")
+    _say(f"[full] {cfg.name}: GPU layer, two steps")
     layer = _gpu_layer(cfg, inp)
-    _say(f"[full] {cfg.name}: oracle routing")
-    L, idx, g = oracle.route(cfg, inp["x"], inp["wr"], inp.get("bias"))
-    counts, offsets, rmap, ptok = oracle.dispatch_index(idx, cfg.E)
-    ref = dict(logits=L, idx=idx, gates=g, counts=counts, offsets=offsets, row_id_map=rmap,
-               perm_token=ptok)
-    _check_routing_and_dispatch(cfg, layer, ref)
-    # dispatched rows: x_perm == x[perm_token], checked on the device
-    mx = cfg.weight == "mxfp8"
-    if cfg.weight in ("fp8", "mxfp8"):
-        xq, xs = (oracle.quant_mx_rows if mx else lambda a: oracle.quant_blocks(a, 1, 128))(
-            oracle.as_f32(inp["x"]))
-        assert np.array_equal(_np(layer.x_perm), xq[ptok]), "fp8 x_perm codes"
-        assert np.array_equal(_np(layer.x_scale), xs[ptok]), "fp8 x_perm scales"
-    else:
-        x_dev = inp["x"].to(DEV)
-        assert torch.equal(layer.x_perm, x_dev[layer.perm_token.long()]), "x_perm"
+    first = {n: getattr(layer, n).clone() for n in OUTPUTS}
+    if cfg.shared:
+        first.update(s_dw1=layer.s_dw1.clone(), s_dw2=layer.s_dw2.clone())
+    cu = lambda t: t.to(DEV)
+    layer.step(cu(inp["x"]), cu(inp["dy"]))
+    torch.cuda.synchronize()
+    for n, v in first.items():
+        assert torch.equal(v, getattr(layer, n)), f"{n} differs between two runs"
+    del first
     tol = _tol(cfg)
-    # full forward on the oracle, expert by expert (FP8 layers: the oracle's
-    # own quantisation of x per 1 x 128 and of the bf16 master weights per
-    # 128 x 128, dequantised exactly)
-    _say(f"[full] {cfg.name}: oracle forward")
-    fp8 = cfg.weight == "fp8"
-    quant = oracle.mx_roundtrip_rows if mx else (oracle.fp8_roundtrip_rows if fp8 else None)
-    X = oracle.as_f64(inp["x"])
-    if quant:
-        X = quant(oracle.as_f32(inp["x"]))
+    errs = {n: _L2() for n in ("out_perm", "dx_perm", "dw1", "dw2")}
+    empty = []
 
-    def W(w):
-        if mx:
-            return oracle.dequant_mx_rows(*oracle.quant_mx_rows(oracle.as_f32(w)))
-        if not fp8:
-            return oracle.as_f64(w)
-        q, sc = oracle.quant_blocks(oracle.as_f32(w), 128, 128)
-        return oracle.dequant_blocks(q, sc, 128, 128)
-
-    def Wd(w):  # the data-gradient products' weights (MXFP8: 32 x 1 blocks)
-        return oracle.dequant_mx_cols(*oracle.quant_mx_cols(oracle.as_f32(w))) if mx else None
-
-    O = np.zeros((cfg.A, cfg.d))
-    for e in range(cfg.E):
-        r0, r1 = offsets[e], offsets[e + 1]
-        if r1 > r0:
-            O[r0:r1] = oracle.ffn_fwd(X[ptok[r0:r1]], W(inp["w1"][e]), W(inp["w2"][e]), h_quant=quant)[2]
+    def on_expert(e, r0, r1, t):
+        if t is None:
+            empty.append(e)
+            assert not layer.dw1[e].any() and not layer.dw2[e].any(), f"expert {e}: no rows, dW not 0"
+            return
+        errs["dw1"].add(_np(layer.dw1[e]), t["dw1"])
+        errs["dw2"].add(_np(layer.dw2[e]), t["dw2"])
+        errs["out_perm"].add(_np(layer.out_perm[r0:r1]), t["out_perm"])
+        errs["dx_perm"].add(_np(layer.dx_perm[r0:r1]), t["dx_perm"])
         if e % 32 == 31:
-            _say(f"[full] {cfg.name}: oracle forward, {e + 1} experts done")
-    O_sh = None
+            _say(f"[full] {cfg.name}: oracle, {e + 1} experts; dW1 {errs['dw1'].rel():.2e} "
+                 f"dW2 {errs['dw2'].rel():.2e}")
+
+    _say(f"[full] {cfg.name}: oracle, expert by expert")
+    ref = oracle.layer_stream(cfg, inp, on_expert=on_expert)
+    _check_routing_and_dispatch(cfg, layer, ref)
+    ptok = ref["perm_token"]
+    if cfg.weight in ("fp8", "mxfp8"):
+        assert np.array_equal(_np(layer.x_perm), ref["xq"][ptok]), "fp8 x_perm codes"
+        assert np.array_equal(_np(layer.x_scale), ref["x_scale"][ptok]), "fp8 x_perm scales"
+    else:
+        assert torch.equal(layer.x_perm, cu(inp["x"])[layer.perm_token.long()]), "x_perm"
+    pairs = [(n, errs[n].rel()) for n in errs]
+    for n in ("y", "d_gate", "dx", "dw_router"):
+        pairs.append((n, oracle.rel_l2(_np(getattr(layer, n)), ref[n])))
     if cfg.shared:
-        SW1, SW2 = W(inp["sw1"]), W(inp["sw2"])
-        O_sh = oracle.ffn_fwd(X, SW1, SW2, h_quant=quant)[2]
-    y = oracle.combine(O, rmap, g, O_sh)
-    err = oracle.rel_l2(_np(layer.y), y)
-    _say(f"[full] {cfg.name}: y rel L2 {err:.2e}")
-    assert err <= tol, f"y {err}"
-    # backward: d_gate, router gradients in full; dx on sampled tokens;
-    # weight gradients on sampled experts and features
-    dy = oracle.as_f64(inp["dy"])
-    dO, dgate = oracle.combine_bwd(dy, O, rmap, g)
-    assert oracle.rel_l2(_np(layer.d_gate), dgate) <= tol, "d_gate"
-    dL = oracle.route_bwd_logits(dgate, idx, L, cfg.score, cfg.renorm, cfg.gate_scale)
-    dWr, dx_r = oracle.route_bwd(dL, inp["x"], inp["wr"])
-    err = oracle.rel_l2(_np(layer.dw_router), dWr)
-    _say(f"[full] {cfg.name}: dw_router rel L2 {err:.2e}")
-    assert err <= tol, "dw_router"
-    rng = np.random.default_rng(cfg.seed_base)
-    toks = np.sort(rng.choice(cfg.T, n_tok, replace=False))
-    dx_s = dx_r[toks].copy()
-    by_e = {}
-    for ti, t in enumerate(toks):
-        for j in range(cfg.k):
-            by_e.setdefault(int(idx[t, j]), []).append((ti, int(rmap[t, j])))
-    for n_e, (e, lst) in enumerate(by_e.items()):
-        if n_e % 32 == 31:
-            _say(f"[full] {cfg.name}: oracle dx, {n_e + 1} of {len(by_e)} experts")
-        tis = np.array([a for a, _ in lst])
-        rs = np.array([b for _, b in lst])
-        dxe = oracle.ffn_dx_rows(X[toks[tis]], W(inp["w1"][e]), W(inp["w2"][e]), dO[rs], quant=quant,
-                                 W1d=Wd(inp["w1"][e]), W2d=Wd(inp["w2"][e]))
-        np.add.at(dx_s, tis, dxe)
-    if cfg.shared:
-        dx_s += oracle.ffn_dx_rows(X[toks], SW1, SW2, dy[toks], quant=quant, W1d=Wd(inp["sw1"]),
-                                   W2d=Wd(inp["sw2"]))
-    err = oracle.rel_l2(_np(layer.dx[torch.as_tensor(toks)]), dx_s)
-    _say(f"[full] {cfg.name}: dx (sampled) rel L2 {err:.2e}")
-    assert err <= tol, "dx"
-    nonempty = np.nonzero(counts)[0]
-    exps = {int(nonempty[0]), int(np.argmax(counts)), int(rng.choice(nonempty))}
-    for e in sorted(exps):
-        cols = np.sort(rng.choice(cfg.f, n_cols, replace=False))
-        r0, r1 = offsets[e], offsets[e + 1]
-        w1r, w2c = oracle.ffn_wgrad_columns(X[ptok[r0:r1]], W(inp["w1"][e]), W(inp["w2"][e]),
-                                            dO[r0:r1], cols, quant=quant, W2d=Wd(inp["w2"][e]))
-        rows = torch.as_tensor(np.concatenate([cols, cfg.f + cols]))
-        got1 = _np(layer.dw1[e][rows])
-        got2 = _np(layer.dw2[e][:, torch.as_tensor(cols)])
-        e1, e2 = oracle.rel_l2(got1, w1r), oracle.rel_l2(got2, w2c)
-        _say(f"[full] {cfg.name}: expert {e} ({counts[e]} rows) dW1 {e1:.2e} dW2 {e2:.2e}")
-        assert e1 <= tol and e2 <= tol
-    empty = np.nonzero(counts == 0)[0]
-    if empty.size:
-        assert not _np(layer.dw1[int(empty[0])]).any() and not _np(layer.dw2[int(empty[0])]).any()
+        pairs += [("shared_dw1", oracle.rel_l2(_np(layer.s_dw1[0]), ref["shared_dw1"])),
+                  ("shared_dw2", oracle.rel_l2(_np(layer.s_dw2[0]), ref["shared_dw2"]))]
+    _say(f"[full] {cfg.name}: " + ", ".join(f"{n} {v:.2e}" for n, v in pairs)
+         + f"; {len(empty)} empty experts")
+    for n, v in pairs:
+        assert v <= tol, f"{n}: rel L2 {v:.3e} > {tol}"
 
 
 @pytest.mark.parametrize("which", [1, 2, 3, 4, "deepseek_v3_mxfp8"])
 def test_full_size_layer(which):
-    if isinstance(which, int):
-        _full_size_check(S.CONFIGS[which])
-    else:  # MXFP8: the oracle also quantises each sampled expert's weights in columns
-        _full_size_check(S.BY_NAME[which], n_tok=8)
+    _full_size_check(S.CONFIGS[which] if isinstance(which, int) else S.BY_NAME[which])
 
 
 # ------------------------------------------------ load-balancing aux loss

@@ -318,38 +318,66 @@ def test_mxfp8_column_blocks_feed_only_the_data_gradients(monkeypatch):
     assert oracle.rel_l2(out["shared_dx"], 4 * base["shared_dx"]) < 1e-6
 
 
-@pytest.mark.parametrize("which", ["bf16", "fp8", "mxfp8"])
-def test_sampled_gradient_helpers_match_the_full_layer(which):
-    """The slice-by-slice helpers the full-size GPU tests use (dX rows, dW1
-    rows and dW2 columns of one expert) equal the full oracle's tensors."""
-    base = S.mini(S.CONFIGS[4], T=24, d=256, f=256, E=4).replace(num_groups=2, topk_groups=1, k=2)
-    cfg = {"bf16": base.replace(weight="bf16"), "fp8": base,
-           "mxfp8": base.replace(weight="mxfp8", quant_block=32)}[which]
+# ------------------------- FP8 weight gradients on 128-row x 1 blocks
+
+def test_fp8_token_blocks_are_row_blocks_of_the_transpose():
+    """128-row x 1 blocks from the first row (ragged tail kept short) are the
+    1 x 128 row blocks of the transpose, and zero-padding the tail to a whole
+    block changes no kept value."""
+    rng = np.random.default_rng(21)
+    a = (rng.normal(size=(300, 40)) * np.exp(rng.normal(size=(1, 40)) * 3)).astype(np.float32)
+    a[128:256, 7] = 0.0                                  # an all-zero block
+    got = oracle.fp8_roundtrip_tokens(a)
+    assert np.array_equal(got, oracle.fp8_roundtrip_rows(np.ascontiguousarray(a.T)).T)
+    padded = np.concatenate([a, np.zeros((84, 40), np.float32)])
+    assert np.array_equal(oracle.fp8_roundtrip_tokens(padded)[:300], got)
+    assert not got[128:256, 7].any()
+    # each block's largest magnitude takes the largest code, 448 x its
+    # block's scale (amax / 448 in fp32): the block boundaries are the ones
+    # the amax came from
+    for b0, b1 in ((0, 128), (128, 256), (256, 300)):
+        blk = np.abs(a[b0:b1])
+        i = blk.argmax(axis=0)
+        c = np.arange(40)
+        amax = blk[i, c]
+        scale = np.where(amax == 0, np.float32(1), amax / np.float32(448)).astype(np.float32)
+        want = np.where(amax == 0, 0.0, 448.0 * scale.astype(np.float64))
+        assert np.array_equal(np.abs(got[b0:b1][i, c]), want)
+    # relative error of an E4M3 rounding: at most 2^-4 of the block's amax
+    amax = np.stack([np.abs(a[b0:b1]).max(0) for b0, b1 in ((0, 128), (128, 256), (256, 300))])
+    bound = np.repeat(amax, [128, 128, 44], axis=0) * 2.0 ** -4
+    assert np.all(np.abs(got - a) <= bound)
+
+
+def test_fp8_wgrad_token_blocks_feed_only_the_weight_gradients(monkeypatch):
+    """With the 128-row quantiser replaced by an exact doubling, the FP8
+    layer's dW1 and dW2 (both operands marked) become 4x those of the
+    unquantised-gradient reading and nothing else moves: the token blocks
+    serve exactly the four operands of the two weight-gradient products."""
+    cfg = S.mini(S.CONFIGS[4], T=40, d=256, f=256, E=8).replace(num_groups=4, topk_groups=2, k=4)
     inp = _inputs(cfg)
-    out = oracle.layer(cfg, inp)
-    fp8, mx = which == "fp8", which == "mxfp8"
-    x32 = oracle.as_f32(inp["x"])
-    X = (oracle.mx_roundtrip_rows(x32) if mx else
-         oracle.fp8_roundtrip_rows(x32) if fp8 else x32.astype(np.float64))
-    quant = oracle.mx_roundtrip_rows if mx else (oracle.fp8_roundtrip_rows if fp8 else None)
-    ptok, offs = out["perm_token"], out["offsets"]
-    e = int(np.argmax(out["counts"]))
-    r0, r1 = offs[e], offs[e + 1]
-    if mx:
-        w1, w2 = oracle.as_f32(inp["w1"][e]), oracle.as_f32(inp["w2"][e])
-        W1, W2 = oracle.dequant_mx_rows(*oracle.quant_mx_rows(w1)), oracle.dequant_mx_rows(*oracle.quant_mx_rows(w2))
-        W1d, W2d = oracle.dequant_mx_cols(*oracle.quant_mx_cols(w1)), oracle.dequant_mx_cols(*oracle.quant_mx_cols(w2))
-    elif fp8:
-        W1 = oracle.dequant_blocks(*oracle.quant_blocks(oracle.as_f32(inp["w1"][e]), 128, 128), 128, 128)
-        W2 = oracle.dequant_blocks(*oracle.quant_blocks(oracle.as_f32(inp["w2"][e]), 128, 128), 128, 128)
-        W1d, W2d = None, None
-    else:
-        W1, W2, W1d, W2d = oracle.as_f64(inp["w1"][e]), oracle.as_f64(inp["w2"][e]), None, None
-    dO = out["d_out_perm"][r0:r1]
-    dx = oracle.ffn_dx_rows(X[ptok[r0:r1]], W1, W2, dO, quant=quant, W1d=W1d, W2d=W2d)
-    assert np.allclose(dx, out["dx_perm"][r0:r1], rtol=1e-10, atol=1e-14)
-    cols = np.array([0, 5, 77, 255])
-    w1r, w2c = oracle.ffn_wgrad_columns(X[ptok[r0:r1]], W1, W2, dO, cols, quant=quant, W2d=W2d)
-    f = cfg.f
-    assert np.allclose(w1r, out["dw1"][e][np.concatenate([cols, f + cols])], rtol=1e-10, atol=1e-14)
-    assert np.allclose(w2c, out["dw2"][e][:, cols], rtol=1e-10, atol=1e-14)
+    base = oracle.layer(cfg, inp, fp8_wgrad=False)
+    monkeypatch.setattr(oracle, "fp8_roundtrip_tokens", lambda a: 2.0 * np.asarray(a, np.float64))
+    out = oracle.layer(cfg, inp, fp8_wgrad=True)
+    for n in ("y", "dx", "dx_perm", "d_gate", "dw_router", "shared_dx"):
+        assert np.array_equal(out[n], base[n]), n
+    for n in ("dw1", "dw2", "shared_dw1", "shared_dw2"):
+        assert oracle.rel_l2(out[n], 4.0 * base[n]) < 1e-14, n
+    # and with the identity in its place both readings coincide (up to the
+    # fp32 rounding the quantiser's input takes)
+    monkeypatch.setattr(oracle, "fp8_roundtrip_tokens",
+                        lambda a: np.asarray(a, np.float32).astype(np.float64))
+    out = oracle.layer(cfg, inp, fp8_wgrad=True)
+    for n in ("dw1", "dw2", "shared_dw1", "shared_dw2"):
+        assert oracle.rel_l2(out[n], base[n]) < 1e-7, n
+
+
+def test_fp8_wgrad_token_blocks_close_to_unquantised_gradients():
+    cfg = S.mini(S.CONFIGS[4], T=300, d=256, f=256, E=4).replace(num_groups=2, topk_groups=1, k=2)
+    inp = _inputs(cfg)
+    a = oracle.layer(cfg, inp, fp8_wgrad=False)
+    b = oracle.layer(cfg, inp, fp8_wgrad=True)
+    assert np.array_equal(a["y"], b["y"]) and np.array_equal(a["dx"], b["dx"])
+    for n in ("dw1", "dw2", "shared_dw1", "shared_dw2"):
+        err = oracle.rel_l2(b[n], a[n])
+        assert 1e-3 < err < 0.06, (n, err)
