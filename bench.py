@@ -35,7 +35,7 @@ HEADLINE = "deepseek_v3_fp8"
 CONTEXT_CONFIGS = ("tiny_fp32", "mixtral_bf16", "deepseek_v3_bf16", "qwen3_skew_bf16",
                    "deepseek_v3_mxfp8")
 # tokens of the headline workload the CPU oracle runs (a bounded sample)
-CPU_SAMPLE_TOKENS = 256
+CPU_SAMPLE_TOKENS = 8
 PROFILES = os.path.join(ROOT, "profiles")
 
 # Which library call launches a kernel, from its (demangled) name: the GEMM
@@ -344,11 +344,11 @@ def stage_work(c):
     return w
 
 
-def make_layer(cfg, device, recompute="none"):
+def make_layer(cfg, device, recompute="none", gemm_tile="auto"):
     import torch
     import moe_synth as S
     from mixture_experts_layer_gather_amd import MoELayer
-    layer = MoELayer(**cfg.describe(), recompute=recompute, device=device)
+    layer = MoELayer(**cfg.describe(), recompute=recompute, gemm_tile=gemm_tile, device=device)
     w1, w2 = S.all_expert_weights(cfg, device=device, threads=16)
     bias = S.router_bias(cfg)
     sw1 = S.shared_w1(cfg).to(device) if cfg.shared else None
@@ -478,7 +478,7 @@ def run_config(cfg, args, dev, flush, copy_gbps):
     """Warm-up, then `steps` timed steps, each after a cache flush; returns
     the workload's figures (times from events on the library's stream)."""
     import torch
-    layer, x, dy = make_layer(cfg, dev, args.recompute)
+    layer, x, dy = make_layer(cfg, dev, args.recompute, args.gemm_tile)
     for _ in range(args.warmup):
         timed_step(layer, x, dy, [])
     torch.cuda.synchronize()
@@ -624,6 +624,8 @@ def main():
     ap.add_argument("--recompute", choices=["none", "act", "full"], default="none",
                     help="activations the expert FFN keeps for the backward: GU and H (none), "
                          "GU only (act), nothing (full)")
+    ap.add_argument("--gemm-tile", choices=["auto", "small", "big"], default="auto",
+                    help="force the expert GEMMs' output tile (tuning; default: chosen per GEMM)")
     ap.add_argument("--graph", action="store_true",
                     help="also capture the step into one HIP graph and time its replays")
     ap.add_argument("--cpu-sample", type=int, default=CPU_SAMPLE_TOKENS,
@@ -730,6 +732,8 @@ def main():
     }
     if args.recompute != "none":
         out["config"]["recompute"] = args.recompute
+    if args.gemm_tile != "auto":
+        out["config"]["gemm_tile"] = args.gemm_tile
     if "graph" in head:
         out["graph"] = head["graph"]
     if len(order) > 1:

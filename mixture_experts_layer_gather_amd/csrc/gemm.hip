@@ -155,6 +155,11 @@ struct GemmArgs {
   const float* b_scale;      // [G, R/128, C/128] of B's storage [G, R, C]
   int64_t b_scale_gstride;   // (R/128)*(C/128)
   int b_scale_ld;            // C/128
+  // FP8 weight gradients: operands quantised in 128-row x 1 blocks inside
+  // each group's rows; a_scale [NB, M] and b_scale [NB, N] (row lengths
+  // a_scale_ld = M, b_scale_ld = N) hold one scale per block and column, and
+  // kblk[g] is the first block of group g (kblk[G] = NB)
+  const int32_t* kblk;
   int ksuper;                // tiles per XCD super-block (set by run_gemm)
 };
 
@@ -356,7 +361,7 @@ struct OperandPlan {
   static_assert(!DMA || NB * 1024 * NW == ROWS * BK * int(sizeof(T)), "DMA blocks per wave");
   static_assert(DMA || (NT >= 1 && NT * 4 * VEC * NTH == ROWS * BK), "tile/threads");
   static_assert(LM != LM_TDMA || (sizeof(T) == 2 && ROWS * 2 >= 256 && 1024 % (ROWS * 2) == 0) ||
-                    (sizeof(T) == 1 && ROWS == 128),
+                    (sizeof(T) == 1 && (ROWS == 128 || ROWS == 256)),
                 "transposed tiles: bf16 rows of 256 or 512 bytes (at least 16 chunks for the swizzle), "
                 "FP8 rows of 128 bytes");
   uint32_t voff[DMA ? NB : 4 * NT];  // byte offsets from the step's base
@@ -368,6 +373,15 @@ __device__ __forceinline__ int tr_swz(int kr) { return (2 * (kr & 3)) ^ (8 * ((k
 // FP8 K-rows of 8 chunks: K-rows 0, 2, 4, 6, 16, 18, 20, 22 (and the odd ones,
 // which sit in the other half of the banks) get chunk masks 0 .. 7
 __device__ __forceinline__ int tr8_swz(int kr) { return ((kr >> 1) & 3) | ((kr >> 2) & 4); }
+// FP8 K-rows of 16 chunks (256-byte rows: each K-row covers every bank): the
+// 16 K-rows two 16-lane groups read together (K-rows j and 16 + j, j < 8,
+// plus a common offset of 8 or 64) get 16 distinct chunk masks
+__device__ __forceinline__ int tr8w_swz(int kr) { return (kr & 7) | ((kr >> 1) & 8); }
+template <int ROWS>
+__device__ __forceinline__ int tr8_swz_rows(int kr) {
+  if constexpr (ROWS == 256) return tr8w_swz(kr);
+  return tr8_swz(kr);
+}
 
 // 8 consecutive values: fp32 from LDS; bf16 / fp32 to and from global memory
 __device__ __forceinline__ void lds_read8(const float* p, float* v) {
@@ -435,6 +449,8 @@ void gemm_kernel(GemmArgs g) {
   using TO = typename OutOf<T>::type;
   constexpr bool FP8 = sizeof(T) == 1;
   constexpr bool MX = std::is_same<T, mx8_t>::value;
+  // FP8 weight gradient: scales per (128-row block, column) of both operands
+  constexpr bool TOKSCALE = FP8 && !MX && MODE == G_KSPLIT;
   using ST = std::conditional_t<MX, StageMx<BM, BN, BK, WM * WN * 64>, Stage<T, BM, BN, BK, WM * WN * 64, FP8>>;
   constexpr int VEC = 16 / sizeof(T);
   constexpr int WTM = BM / WM, WTN = BN / WN;
@@ -444,8 +460,9 @@ void gemm_kernel(GemmArgs g) {
   using PB = OperandPlan<T, BLM, BN, BK, NTH>;
   static_assert(WM * WN == 4 || WM * WN == 8, "four or eight waves");
   static_assert(EPI != EPI_SWIGLU || FN % 2 == 0, "SwiGLU pairs column fragments");
-  static_assert(!FP8 || (MODE == G_ROWS && A_KMAJ && BK == 128 && BN <= 128 && BM <= 256),
-                "FP8: row-grouped GEMMs, one 128-deep scale block per K step");
+  static_assert(!FP8 || (MODE == G_ROWS && A_KMAJ && BK == 128 && BN <= 256 && BM <= 256) ||
+                    (TOKSCALE && !A_KMAJ && !B_KMAJ && BK == 128 && BM + BN <= WM * WN * 64),
+                "FP8: row-grouped GEMMs, or weight gradients, one 128-deep scale block per K step");
 
   static_assert(NS >= 2 && NS <= 4, "LDS stages");
   static_assert(sizeof(ST) % 16 == 0, "stage alignment");
@@ -540,7 +557,7 @@ void gemm_kernel(GemmArgs g) {
     constexpr int EPC = 16 / int(ES);  // elements per 16-byte chunk
     const int CPR = ROWS / EPC, RPB = 1024 / (ROWS * int(ES));
     const int kr = b * RPB + lane / CPR;
-    const int lc = (lane % CPR) ^ (ES == 1 ? tr8_swz(kr) : tr_swz(kr));
+    const int lc = (lane % CPR) ^ (ES == 1 ? (ROWS == 256 ? tr8w_swz(kr) : tr8_swz(kr)) : tr_swz(kr));
     return uint32_t((int64_t(kr) * ld + col0 + lc * EPC) * ES);
   };
   if constexpr (ALM == LM_KDMA) {
@@ -600,21 +617,38 @@ void gemm_kernel(GemmArgs g) {
   // the row's four E8M0 bytes of the step (a_scale_ld = K / 128 words).
   const char* sa_base = nullptr;
   int64_t sa_end = 0;
-  if constexpr (FP8) {
+  if constexpr (FP8 && !TOKSCALE) {
     sa_base = reinterpret_cast<const char*>(g.a_scale + int64_t(row0) * g.a_scale_ld);
     sa_end = int64_t(mrows) * g.a_scale_ld * 4;
+  }
+  // weight gradients: thread tid < BM stages the scale of A column m0 + tid
+  // (an output row), the next BN threads those of B columns n0 + ...; K step s
+  // is block kb0 + s of the scale arrays
+  const float* ts_col = nullptr;
+  int64_t ts_ld = 0;
+  int kb0 = 0;
+  if constexpr (TOKSCALE) {
+    kb0 = g.kblk[grp];
+    if (tid < BM) {
+      ts_col = g.a_scale + m0 + tid;
+      ts_ld = g.a_scale_ld;
+    } else if (tid < BM + BN) {
+      ts_col = g.b_scale + n0 + (tid - BM);
+      ts_ld = g.b_scale_ld;
+    }
   }
   // FP8: column-block scale rows of B; SwiGLU tiles span a gate block and an
   // up block of W1
   const float* __restrict__ sb_base = nullptr;
   int sb_blk0 = 0, sb_blk1 = 0;
-  if constexpr (FP8 && !MX) {
+  if constexpr (FP8 && !MX && !TOKSCALE) {
     sb_base = g.b_scale + int64_t(grp) * g.b_scale_gstride;
     if (EPI == EPI_SWIGLU) {
       sb_blk0 = (nt * (BN / 2)) / 128;
       sb_blk1 = (g.f + nt * (BN / 2)) / 128;
     } else {
-      sb_blk0 = sb_blk1 = n0 / 128;
+      // a wave's WTN (<= 128) columns lie in one 128-column block
+      sb_blk0 = sb_blk1 = (n0 + wn * WTN) / 128;
     }
   }
 
@@ -675,7 +709,9 @@ void gemm_kernel(GemmArgs g) {
 #pragma unroll
       for (int i = 0; i < 4 * PB::NT; ++i) rb[i] = __builtin_amdgcn_raw_buffer_load_b128(br, pb.voff[i], 0, 0);
     }
-    if constexpr (FP8) {
+    if constexpr (TOKSCALE) {
+      rs = (live && ts_col) ? ts_col[int64_t(kb0 + s) * ts_ld] : 0.0f;
+    } else if constexpr (FP8) {
       const rsrc_t sr = make_rsrc(sa_base, live ? sa_end : 0);
       rs = __builtin_bit_cast(
           float, __builtin_amdgcn_raw_buffer_load_b32(sr, uint32_t((tid * g.a_scale_ld + s * (BK / 128)) * 4), 0, 0));
@@ -742,7 +778,8 @@ void gemm_kernel(GemmArgs g) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int kr = 16 * (lane / 16) + 8 * (r & 1) + 64 * (r >> 1) + j;
-        const char* p = reinterpret_cast<const char*>(tile) + kr * ROWS + (((col / 16) ^ tr8_swz(kr)) * 16) + col % 16;
+        const char* p = reinterpret_cast<const char*>(tile) + kr * ROWS +
+                        (((col / 16) ^ (ROWS == 256 ? tr8w_swz(kr) : tr8_swz(kr))) * 16) + col % 16;
         const i32x2 v = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
             (__attribute__((address_space(3))) i32x2*)(void*)p);
         w[2 * r] = v[0];
@@ -773,7 +810,7 @@ void gemm_kernel(GemmArgs g) {
   // one K step (K block s) on stage st
   auto compute = [&](const ST& st, int s) {
     float sb0 = 0.0f, sb1 = 0.0f;
-    if constexpr (FP8 && !MX) {
+    if constexpr (FP8 && !MX && !TOKSCALE) {
       const int kb = min(s, nk - 1);  // BK == 128: one scale block per step
       if (B_KMAJ) {
         sb0 = sb_base[int64_t(sb_blk0) * g.b_scale_ld + kb];
@@ -809,8 +846,12 @@ void gemm_kernel(GemmArgs g) {
       // ahead of the FN MFMAs (into temporaries) and their scaled adds
       static_assert(BK == MF::MK, "one MFMA K block per step");
       typename MF::frag bfr[FN], acur, anxt;
+      float sbv[FN];  // weight gradients: the scale of each lane's column
 #pragma unroll
-      for (int j = 0; j < FN; ++j) bfr[j] = load_b(st, j, 0);
+      for (int j = 0; j < FN; ++j) {
+        bfr[j] = load_b(st, j, 0);
+        if constexpr (TOKSCALE) sbv[j] = st.SA[BM + wn * WTN + j * 16 + lane % 16];
+      }
       acur = load_a(st, 0, 0);
       __builtin_amdgcn_sched_group_barrier(0x100, FN + 1, 0);
       static_for<FM>([&](auto ic) {
@@ -823,7 +864,7 @@ void gemm_kernel(GemmArgs g) {
         for (int j = 0; j < FN; ++j) dd[j] = MF::mma(acur, bfr[j], f32x4_t{0.0f, 0.0f, 0.0f, 0.0f});
 #pragma unroll
         for (int j = 0; j < FN; ++j) {
-          const float sbj = (EPI == EPI_SWIGLU && j >= FN / 2) ? sb1 : sb0;
+          const float sbj = TOKSCALE ? sbv[j] : ((EPI == EPI_SWIGLU && j >= FN / 2) ? sb1 : sb0);
 #pragma unroll
           for (int r = 0; r < 4; ++r) acc[i][j][r] = __builtin_fmaf(dd[j][r], sa[r] * sbj, acc[i][j][r]);
         }
@@ -1186,6 +1227,135 @@ static void dequant_mx_rows(const uint8_t* q, const uint8_t* e8m0, int64_t rows,
 }
 
 // ---------------------------------------------------------------------------
+// FP8 weight-gradient operands: E4M3 in blocks of 128 consecutive rows x 1
+// column inside each expert's rows (the contraction of dW = P^T Q runs over
+// the expert's rows), one fp32 scale amax / 448 per block and column. Block
+// b of the concatenated block list is block b - kblk[e] of expert e, where
+// kblk[e] = sum of ceil(rows / 128) over the experts before e.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(1024) void kblock_offsets_kernel(const int32_t* __restrict__ offsets,
+                                                              int32_t* __restrict__ kblk, int G) {
+  __shared__ int s_wave[16];
+  const int g = threadIdx.x;
+  const int c = g < G ? (offsets[g + 1] - offsets[g] + 127) / 128 : 0;
+  int v = c;
+  const int lane = lane_id();
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int u = __shfl_up(v, o, kWave);
+    if (lane >= o) v += u;
+  }
+  if (lane == 63) s_wave[g / kWave] = v;
+  __syncthreads();
+  int before = 0;
+  for (int w = 0; w < g / kWave; ++w) before += s_wave[w];
+  if (g < G) kblk[g + 1] = before + v;
+  if (g == 0) kblk[0] = 0;
+}
+
+// One workgroup per (block, 256 columns): thread (cg, rg) holds columns
+// 8 cg .. 8 cg + 7 of rows rg, rg + 8, ..., rg + 120 of the block in
+// registers; the column maxima meet in LDS. Sources: bf16 rows (SRC_FP8 =
+// false) or E4M3 codes with fp32 scales per 1 x 128 block of a row, taken as
+// float(code) * scale in fp32.
+template <bool SRC_FP8>
+__global__ __launch_bounds__(256) void quant_tokens_kernel(const void* __restrict__ src,
+                                                           const float* __restrict__ src_scale,
+                                                           const int32_t* __restrict__ offsets,
+                                                           const int32_t* __restrict__ kblk, int G,
+                                                           int64_t C, fp8_t* __restrict__ q,
+                                                           float* __restrict__ scale) {
+  __shared__ float s_max[8][257];
+  const int b = blockIdx.x;
+  if (b >= kblk[G]) return;
+  // the expert owning block b: the last e with kblk[e] <= b
+  int lo = 0, hi = G - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) / 2;
+    if (kblk[mid] <= b) lo = mid;
+    else hi = mid - 1;
+  }
+  const int64_t r0 = int64_t(offsets[lo]) + int64_t(b - kblk[lo]) * 128;
+  const int nrows = min(int64_t(128), int64_t(offsets[lo + 1]) - r0);
+  const int cg = threadIdx.x % 32, rg = threadIdx.x / 32;
+  const int64_t c0 = int64_t(blockIdx.y) * 256 + cg * 8;
+  const bool col_ok = c0 < C;
+  float v[16][8];
+  float m[8];
+#pragma unroll
+  for (int c = 0; c < 8; ++c) m[c] = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int rr = rg + 8 * i;
+    if (col_ok && rr < nrows) {
+      const int64_t off = (r0 + rr) * C + c0;
+      if constexpr (SRC_FP8) {
+        const u32x2 w = *reinterpret_cast<const u32x2*>(static_cast<const fp8_t*>(src) + off);
+        const float sc = src_scale[(r0 + rr) * (C / 128) + c0 / 128];
+        const float f8[8] = {__builtin_amdgcn_cvt_f32_fp8(w[0], 0), __builtin_amdgcn_cvt_f32_fp8(w[0], 1),
+                             __builtin_amdgcn_cvt_f32_fp8(w[0], 2), __builtin_amdgcn_cvt_f32_fp8(w[0], 3),
+                             __builtin_amdgcn_cvt_f32_fp8(w[1], 0), __builtin_amdgcn_cvt_f32_fp8(w[1], 1),
+                             __builtin_amdgcn_cvt_f32_fp8(w[1], 2), __builtin_amdgcn_cvt_f32_fp8(w[1], 3)};
+#pragma unroll
+        for (int c = 0; c < 8; ++c) v[i][c] = f8[c] * sc;
+      } else {
+        Vec16<bf16_t>::load(static_cast<const bf16_t*>(src) + off, v[i]);
+      }
+    } else {
+#pragma unroll
+      for (int c = 0; c < 8; ++c) v[i][c] = 0.0f;
+    }
+#pragma unroll
+    for (int c = 0; c < 8; ++c) m[c] = fmaxf(m[c], fabsf(v[i][c]));
+  }
+#pragma unroll
+  for (int c = 0; c < 8; ++c) s_max[rg][cg * 8 + c] = m[c];
+  __syncthreads();
+  float sc[8];
+#pragma unroll
+  for (int c = 0; c < 8; ++c) {
+    float a = 0.0f;
+#pragma unroll
+    for (int r = 0; r < 8; ++r) a = fmaxf(a, s_max[r][cg * 8 + c]);
+    sc[c] = (a == 0.0f) ? 1.0f : a / 448.0f;
+  }
+  if (!col_ok) return;
+  if (rg == 0) {
+    float* sp = scale + int64_t(b) * C + c0;
+    *reinterpret_cast<float4*>(sp) = float4{sc[0], sc[1], sc[2], sc[3]};
+    *reinterpret_cast<float4*>(sp + 4) = float4{sc[4], sc[5], sc[6], sc[7]};
+  }
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int rr = rg + 8 * i;
+    if (rr < nrows) {
+      uint32_t w0 = 0, w1 = 0;
+      w0 = __builtin_amdgcn_cvt_pk_fp8_f32(v[i][0] / sc[0], v[i][1] / sc[1], w0, false);
+      w0 = __builtin_amdgcn_cvt_pk_fp8_f32(v[i][2] / sc[2], v[i][3] / sc[3], w0, true);
+      w1 = __builtin_amdgcn_cvt_pk_fp8_f32(v[i][4] / sc[4], v[i][5] / sc[5], w1, false);
+      w1 = __builtin_amdgcn_cvt_pk_fp8_f32(v[i][6] / sc[6], v[i][7] / sc[7], w1, true);
+      *reinterpret_cast<u32x2*>(q + (r0 + rr) * C + c0) = u32x2{w0, w1};
+    }
+  }
+}
+
+static int64_t token_blocks_bound(int64_t A, int64_t G) { return (A + G * 127) / 128; }
+
+// src [A, C] (bf16, or E4M3 codes with [A, C/128] fp32 row-block scales)
+// -> q [A, C] E4M3 and scale [token_blocks_bound(A, G), C] (rows past the
+// actual block count are not written)
+static void quant_tokens(const void* src, const float* src_scale, const int32_t* offsets,
+                         const int32_t* kblk, int64_t G, int64_t A, int64_t C, fp8_t* q, float* scale,
+                         hipStream_t st) {
+  const dim3 grid(unsigned(token_blocks_bound(A, G)), unsigned((C + 255) / 256));
+  if (grid.x == 0) return;
+  if (src_scale)
+    quant_tokens_kernel<true><<<grid, 256, 0, st>>>(src, src_scale, offsets, kblk, int(G), C, q, scale);
+  else
+    quant_tokens_kernel<false><<<grid, 256, 0, st>>>(src, nullptr, offsets, kblk, int(G), C, q, scale);
+}
+
+// ---------------------------------------------------------------------------
 // Tile configurations: BM x BN output tile, BK deep, WM x WN waves, NS LDS
 // stages.
 //   Small: 128 x 128, 4 waves of 64 x 64, 2 stages of 32 KB (every dtype;
@@ -1209,6 +1379,9 @@ template <> struct SmallCfg<float> : Cfg<float, 128, 128, 32, 2, 2, 2> {};
 template <> struct SmallCfg<fp8_t> : Cfg<fp8_t, 128, 128, 128, 2, 2, 2> {};
 template <> struct SmallCfg<mx8_t> : Cfg<mx8_t, 128, 128, 128, 2, 2, 2> {};
 typedef Cfg<bf16_t, 256, 256, 64, 2, 4, 2> BigCfg;
+// FP8 / MXFP8 256 x 256 tile: 8 waves of 128 x 64, BK 128, two 64 KB stages
+// (one workgroup per CU), the byte layout of the bf16 Big tile
+template <typename T> using BigCfg8 = Cfg<T, 256, 256, 128, 2, 4, 2>;
 typedef Cfg<bf16_t, 128, 256, 32, 2, 2, 3> WgradCfg;
 
 static int rows_tile_bound(int64_t A, int64_t G, int BM) {
@@ -1238,6 +1411,9 @@ static bool big_rows(int tile, int64_t A, int64_t E, int64_t n_dim) {
   if (tile == 2) return true;
   return A >= 512 * E && int64_t(rows_tile_bound(A, E, 256)) * (n_dim / 256) >= 4 * 256;
 }
+// FP8 row-grouped GEMMs: the 256 x 256 tile only when forced (MOE_TILE_BIG)
+// and the width allows.
+static bool big8(int tile, int64_t n_dim) { return tile == 2 && n_dim % 256 == 0; }
 // Weight gradients tile the (M, N) = weight shape of every expert, whatever
 // its rows: the big tile whenever the weight shape allows.
 static bool big_wgrad(int tile, int64_t d, int64_t f) { return tile != 1 && d % 256 == 0 && f % 256 == 0; }
@@ -1277,14 +1453,19 @@ struct FfnWs {
   size_t d_out_s = 0;
   size_t d_gu_q = 0;   // bwd fp8: dGU codes [A, 2f] + scales [A, 2f/128]
   size_t d_gu_s = 0;
-  size_t x_deq = 0;    // bwd fp8: dequantised X [A, d] bf16
-  size_t h_deq = 0;    // bwd fp8: dequantised H [A, f] bf16
+  size_t x_deq = 0;    // bwd mxfp8: dequantised X [A, d] bf16
+  size_t h_deq = 0;    // bwd mxfp8: dequantised H [A, f] bf16
+  // bwd fp8: weight-gradient operands in 128-row x 1 blocks: block offsets
+  // [E+1], codes [A, C] and scales [NB, C] of dO, H, dGU and X
+  size_t kblk = 0;
+  size_t t_do = 0, t_do_s = 0, t_h = 0, t_h_s = 0, t_gu = 0, t_gu_s = 0, t_x = 0, t_x_s = 0;
   size_t total = 0;
 };
 
 static size_t al(size_t v) { return (v + 255) & ~size_t(255); }
 
-static FfnWs ffn_ws(int64_t A, int64_t d, int64_t f, int act_bytes, bool fp8, bool bwd, int rc) {
+static FfnWs ffn_ws(int64_t A, int64_t d, int64_t f, int64_t E, int act_bytes, int wt, bool bwd, int rc) {
+  const bool fp8 = wt >= 2;
   FfnWs w;
   size_t o = 0;
   // H, when it is not kept between the calls, lives in the workspace: the
@@ -1302,16 +1483,30 @@ static FfnWs ffn_ws(int64_t A, int64_t d, int64_t f, int act_bytes, bool fp8, bo
       w.d_out_s = o; o += al(size_t(A) * (d / 128) * 4);
       w.d_gu_q = o; o += al(size_t(A) * 2 * f);
       w.d_gu_s = o; o += al(size_t(A) * (2 * f / 128) * 4);
-      w.x_deq = o; o += al(size_t(A) * d * 2);
-      w.h_deq = o; o += al(size_t(A) * f * 2);
+      if (wt == 3) {
+        w.x_deq = o; o += al(size_t(A) * d * 2);
+        w.h_deq = o; o += al(size_t(A) * f * 2);
+      } else {
+        const size_t nb = size_t(token_blocks_bound(A, E));
+        w.kblk = o; o += al(size_t(E + 1) * 4);
+        w.t_do = o; o += al(size_t(A) * d);
+        w.t_do_s = o; o += al(nb * d * 4);
+        w.t_h = o; o += al(size_t(A) * f);
+        w.t_h_s = o; o += al(nb * f * 4);
+        w.t_gu = o; o += al(size_t(A) * 2 * f);
+        w.t_gu_s = o; o += al(nb * 2 * f * 4);
+        w.t_x = o; o += al(size_t(A) * d);
+        w.t_x_s = o; o += al(nb * d * 4);
+      }
     }
   }
   w.total = o;
   return w;
 }
 
-size_t ffn_ws_bytes(int64_t A, int64_t d, int64_t f, int act_bytes, bool fp8, bool bwd, int recompute) {
-  return ffn_ws(A, d, f, act_bytes, fp8, bwd, recompute).total;
+size_t ffn_ws_bytes(int64_t A, int64_t d, int64_t f, int64_t E, int act_bytes, int wt, bool bwd,
+                    int recompute) {
+  return ffn_ws(A, d, f, E, act_bytes, wt, bwd, recompute).total;
 }
 
 static char* at(void* base, size_t off) { return static_cast<char*>(base) + off; }
@@ -1345,9 +1540,9 @@ static void gemm2_fwd(const FfnLaunch& a, const void* h, hipStream_t st) {
 
 // FP8 GEMM1 (+ SwiGLU) into h16 (bf16), then H -> E4M3 per 1 x 128 block
 // (the second GEMM's A operand, and the weight gradient's after dequantising)
+template <typename C>
 static void gemm1_fwd_fp8(const FfnLaunch& a, void* gu, bf16_t* h16, uint8_t* hq, float* hs,
                           hipStream_t st) {
-  typedef SmallCfg<fp8_t> C;
   GemmArgs g1{};
   g1.A = a.x_perm; g1.lda = a.d;
   g1.a_scale = a.x_scale; g1.a_scale_ld = int(a.d / 128);
@@ -1361,8 +1556,8 @@ static void gemm1_fwd_fp8(const FfnLaunch& a, void* gu, bf16_t* h16, uint8_t* hq
   launch_quant_rows(h16, true, a.A, a.f, hq, hs, st);
 }
 
+template <typename C>
 static void gemm2_fwd_fp8(const FfnLaunch& a, const uint8_t* hq, const float* hs, hipStream_t st) {
-  typedef SmallCfg<fp8_t> C;
   GemmArgs g2{};
   g2.A = hq; g2.lda = a.f;
   g2.a_scale = hs; g2.a_scale_ld = int(a.f / 128);
@@ -1379,8 +1574,8 @@ static void gemm2_fwd_fp8(const FfnLaunch& a, const uint8_t* hq, const float* hs
 // words); B scales in bytes: rows of K / 32 for K-major weights (the forward's
 // row-quantised W1, W2), rows of N per 32-deep K block for K-strided weights
 // (the data gradients' column-quantised W2, W1).
+template <typename C>
 static void gemm1_fwd_mx(const FfnLaunch& a, void* gu, bf16_t* h16, uint8_t* hq, uint8_t* hs, hipStream_t st) {
-  typedef SmallCfg<mx8_t> C;
   GemmArgs g1{};
   g1.A = a.x_perm; g1.lda = a.d;
   g1.a_scale = a.x_scale; g1.a_scale_ld = int(a.d / 128);
@@ -1394,8 +1589,8 @@ static void gemm1_fwd_mx(const FfnLaunch& a, void* gu, bf16_t* h16, uint8_t* hq,
   launch_quant_mx_rows(h16, true, a.A, a.f, hq, hs, st);
 }
 
+template <typename C>
 static void gemm2_fwd_mx(const FfnLaunch& a, const uint8_t* hq, const uint8_t* hs, hipStream_t st) {
-  typedef SmallCfg<mx8_t> C;
   GemmArgs g2{};
   g2.A = hq; g2.lda = a.f;
   g2.a_scale = reinterpret_cast<const float*>(hs); g2.a_scale_ld = int(a.f / 128);
@@ -1411,9 +1606,10 @@ static void gemm2_fwd_mx(const FfnLaunch& a, const uint8_t* hq, const uint8_t* h
 // The first half of the forward: GU (into gu unless null) and H (+ scales).
 static void ffn_fwd_gu_h(const FfnLaunch& a, void* gu, void* h, float* hs, bf16_t* h16, hipStream_t st) {
   if (a.wt == 3) {
-    gemm1_fwd_mx(a, gu, h16, static_cast<uint8_t*>(h), reinterpret_cast<uint8_t*>(hs), st);
+    gemm1_fwd_mx<SmallCfg<mx8_t>>(a, gu, h16, static_cast<uint8_t*>(h), reinterpret_cast<uint8_t*>(hs), st);
   } else if (a.wt == 2) {
-    gemm1_fwd_fp8(a, gu, h16, static_cast<uint8_t*>(h), hs, st);
+    if (big8(a.tile, 2 * a.f)) gemm1_fwd_fp8<BigCfg8<fp8_t>>(a, gu, h16, static_cast<uint8_t*>(h), hs, st);
+    else gemm1_fwd_fp8<SmallCfg<fp8_t>>(a, gu, h16, static_cast<uint8_t*>(h), hs, st);
   } else if (a.wt == 1) {
     if (big_rows(a.tile, a.A, a.E, 2 * a.f)) gemm1_fwd<BigCfg>(a, gu, h, st);
     else gemm1_fwd<SmallCfg<bf16_t>>(a, gu, h, st);
@@ -1444,6 +1640,33 @@ static void wgrad_t(const void* d_out, const void* act_h, const void* d_gu, cons
   g4.M = int(2 * f); g4.N = int(d);
   g4.tiles_m = int(2 * f / C::BM); g4.tiles_n = int(d / C::BN);
   run_gemm<C, TW, false, false, G_KSPLIT, EPI_STORE>(g4, int(E) * g4.tiles_m * g4.tiles_n, st);
+}
+
+// FP8 weight gradients: dW2 = dO^T H and dW1 = dGU^T X with every operand
+// in 128-row x 1 blocks (codes [A, C], scales [NB, C], kblk the first block
+// of each expert); bf16 results.
+static void wgrad_fp8(const fp8_t* dq, const float* ds, const fp8_t* hq, const float* hs, const fp8_t* gq,
+                      const float* gs, const fp8_t* xq, const float* xs, const int32_t* kblk, void* dw1,
+                      void* dw2, const int32_t* offsets, int64_t d, int64_t f, int64_t E, hipStream_t st) {
+  typedef SmallCfg<fp8_t> C;
+  GemmArgs g3{};
+  g3.A = dq; g3.lda = d; g3.a_scale = ds; g3.a_scale_ld = int(d);
+  g3.B = hq; g3.ldb = f; g3.b_scale = hs; g3.b_scale_ld = int(f);
+  g3.kblk = kblk;
+  g3.C = dw2; g3.ldc = f; g3.c_gstride = d * f;
+  g3.offsets = offsets; g3.G = int(E);
+  g3.M = int(d); g3.N = int(f);
+  g3.tiles_m = int(d / C::BM); g3.tiles_n = int(f / C::BN);
+  run_gemm<C, bf16_t, false, false, G_KSPLIT, EPI_STORE>(g3, int(E) * g3.tiles_m * g3.tiles_n, st);
+  GemmArgs g4{};
+  g4.A = gq; g4.lda = 2 * f; g4.a_scale = gs; g4.a_scale_ld = int(2 * f);
+  g4.B = xq; g4.ldb = d; g4.b_scale = xs; g4.b_scale_ld = int(d);
+  g4.kblk = kblk;
+  g4.C = dw1; g4.ldc = d; g4.c_gstride = 2 * f * d;
+  g4.offsets = offsets; g4.G = int(E);
+  g4.M = int(2 * f); g4.N = int(d);
+  g4.tiles_m = int(2 * f / C::BM); g4.tiles_n = int(d / C::BN);
+  run_gemm<C, bf16_t, false, false, G_KSPLIT, EPI_STORE>(g4, int(E) * g4.tiles_m * g4.tiles_n, st);
 }
 
 template <typename TC16>
@@ -1487,7 +1710,7 @@ static void dx_bwd(const FfnBwdLaunch& a, const void* d_gu, hipStream_t st) {
 // buffer the dH GEMM's epilogue rebuilds H into from the saved GU.
 template <typename T>
 static void ffn_bwd_t(const FfnBwdLaunch& a, void* h_out, hipStream_t st) {
-  const FfnWs w = ffn_ws(a.A, a.d, a.f, int(sizeof(T)), false, true, a.recompute);
+  const FfnWs w = ffn_ws(a.A, a.d, a.f, a.E, int(sizeof(T)), a.wt, true, a.recompute);
   void* d_gu = at(a.ws, w.d_gu);
   if constexpr (sizeof(T) == 2) {
     if (big_rows(a.tile, a.A, a.E, a.f)) dh_bwd<BigCfg>(a, d_gu, h_out, st);
@@ -1512,30 +1735,12 @@ static void ffn_bwd_t(const FfnBwdLaunch& a, void* h_out, hipStream_t st) {
 // MXFP8 (MXF): the same structure with 1 x 32 E8M0 blocks for the gradient
 // operands and, for the weights, the column-quantised copies (32 x 1 blocks
 // along these products' contraction dims) that the caller passes as w1, w2.
-template <bool MXF>
-static void ffn_bwd_fp8(const FfnBwdLaunch& a, bf16_t* h16, hipStream_t st) {
-  typedef SmallCfg<std::conditional_t<MXF, mx8_t, fp8_t>> C;
-  auto quant = [&](const void* src, int64_t rows, int64_t cols, uint8_t* q, float* sc) {
-    if constexpr (MXF) launch_quant_mx_rows(src, true, rows, cols, q, reinterpret_cast<uint8_t*>(sc), st);
-    else launch_quant_rows(src, true, rows, cols, q, sc, st);
-  };
-  auto dequant = [&](const void* q, const float* sc, int64_t rows, int64_t cols, bf16_t* dst) {
-    if constexpr (MXF)
-      dequant_mx_rows(static_cast<const uint8_t*>(q), reinterpret_cast<const uint8_t*>(sc), rows, cols, dst, st);
-    else
-      dequant_rows(static_cast<const uint8_t*>(q), sc, rows, cols, dst, st);
-  };
-  const FfnWs w = ffn_ws(a.A, a.d, a.f, 2, true, true, a.recompute);
-  bf16_t* d_gu = reinterpret_cast<bf16_t*>(at(a.ws, w.d_gu));
-  uint8_t* dq = reinterpret_cast<uint8_t*>(at(a.ws, w.d_out_q));
-  float* ds = reinterpret_cast<float*>(at(a.ws, w.d_out_s));
-  uint8_t* gq = reinterpret_cast<uint8_t*>(at(a.ws, w.d_gu_q));
-  float* gs = reinterpret_cast<float*>(at(a.ws, w.d_gu_s));
-  bf16_t* xd = reinterpret_cast<bf16_t*>(at(a.ws, w.x_deq));
-  bf16_t* hd = reinterpret_cast<bf16_t*>(at(a.ws, w.h_deq));
-  const int mt_bound = rows_tile_bound(a.A, a.E, C::BM);
-  quant(a.d_out, a.A, a.d, dq, ds);
-  // dH = Q(dO) W2 (+ SwiGLU backward from the saved bf16 GU)
+// FP8 / MXFP8 data gradients: dH = Q(dO) W2 (+ SwiGLU backward from the
+// saved bf16 GU; H rebuilt into h16 unless null) and dX = Q(dGU) W1, on
+// tile configuration C.
+template <bool MXF, typename C>
+static void dh_fp8(const FfnBwdLaunch& a, const uint8_t* dq, const float* ds, bf16_t* d_gu, bf16_t* h16,
+                   hipStream_t st) {
   GemmArgs g1{};
   g1.A = dq; g1.lda = a.d;
   g1.a_scale = ds; g1.a_scale_ld = int(a.d / 128);
@@ -1548,10 +1753,10 @@ static void ffn_bwd_fp8(const FfnBwdLaunch& a, bf16_t* h16, hipStream_t st) {
   g1.N = int(a.f); g1.K = int(a.d); g1.f = int(a.f);
   g1.aux0 = const_cast<void*>(a.act_gu); g1.aux1 = h16;
   g1.tiles_n = int(a.f / C::BN);
-  run_gemm<C, bf16_t, true, false, G_ROWS, EPI_DSWIGLU>(g1, mt_bound * g1.tiles_n, st);
-  if (h16) quant(h16, a.A, a.f, static_cast<uint8_t*>(const_cast<void*>(a.act_h)), const_cast<float*>(a.h_scale));
-  // dX = Q(dGU) W1
-  quant(d_gu, a.A, 2 * a.f, gq, gs);
+  run_gemm<C, bf16_t, true, false, G_ROWS, EPI_DSWIGLU>(g1, rows_tile_bound(a.A, a.E, C::BM) * g1.tiles_n, st);
+}
+template <bool MXF, typename C>
+static void dx_fp8(const FfnBwdLaunch& a, const uint8_t* gq, const float* gs, hipStream_t st) {
   GemmArgs g2{};
   g2.A = gq; g2.lda = 2 * a.f;
   g2.a_scale = gs; g2.a_scale_ld = int(2 * a.f / 128);
@@ -1563,11 +1768,67 @@ static void ffn_bwd_fp8(const FfnBwdLaunch& a, bf16_t* h16, hipStream_t st) {
   g2.offsets = a.offsets; g2.G = int(a.E);
   g2.N = int(a.d); g2.K = int(2 * a.f);
   g2.tiles_n = int(a.d / C::BN);
-  run_gemm<C, bf16_t, true, false, G_ROWS, EPI_STORE>(g2, mt_bound * g2.tiles_n, st);
-  // weight gradients in bf16 on dequantised X and H
-  dequant(a.x_perm, a.x_scale, a.A, a.d, xd);
-  dequant(a.act_h, a.h_scale, a.A, a.f, hd);
-  wgrad_any<bf16_t>(a.tile, a.d_out, hd, d_gu, xd, a.dw1, a.dw2, a.offsets, a.d, a.f, a.E, st);
+  run_gemm<C, bf16_t, true, false, G_ROWS, EPI_STORE>(g2, rows_tile_bound(a.A, a.E, C::BM) * g2.tiles_n, st);
+}
+
+template <bool MXF>
+static void ffn_bwd_fp8(const FfnBwdLaunch& a, bf16_t* h16, hipStream_t st) {
+  typedef std::conditional_t<MXF, mx8_t, fp8_t> T8;
+  auto quant = [&](const void* src, int64_t rows, int64_t cols, uint8_t* q, float* sc) {
+    if constexpr (MXF) launch_quant_mx_rows(src, true, rows, cols, q, reinterpret_cast<uint8_t*>(sc), st);
+    else launch_quant_rows(src, true, rows, cols, q, sc, st);
+  };
+  auto dequant = [&](const void* q, const float* sc, int64_t rows, int64_t cols, bf16_t* dst) {
+    if constexpr (MXF)
+      dequant_mx_rows(static_cast<const uint8_t*>(q), reinterpret_cast<const uint8_t*>(sc), rows, cols, dst, st);
+    else
+      dequant_rows(static_cast<const uint8_t*>(q), sc, rows, cols, dst, st);
+  };
+  const FfnWs w = ffn_ws(a.A, a.d, a.f, a.E, 2, a.wt, true, a.recompute);
+  bf16_t* d_gu = reinterpret_cast<bf16_t*>(at(a.ws, w.d_gu));
+  uint8_t* dq = reinterpret_cast<uint8_t*>(at(a.ws, w.d_out_q));
+  float* ds = reinterpret_cast<float*>(at(a.ws, w.d_out_s));
+  uint8_t* gq = reinterpret_cast<uint8_t*>(at(a.ws, w.d_gu_q));
+  float* gs = reinterpret_cast<float*>(at(a.ws, w.d_gu_s));
+  bf16_t* xd = reinterpret_cast<bf16_t*>(at(a.ws, w.x_deq));
+  bf16_t* hd = reinterpret_cast<bf16_t*>(at(a.ws, w.h_deq));
+  quant(a.d_out, a.A, a.d, dq, ds);
+  // dH = Q(dO) W2 (+ SwiGLU backward from the saved bf16 GU)
+  // (the MXFP8 instance keeps the 128 x 128 tile: its per-lane scale words
+  // do not fit the 256 x 256 tile's registers)
+  if constexpr (!MXF) {
+    if (big8(a.tile, a.f)) dh_fp8<MXF, BigCfg8<T8>>(a, dq, ds, d_gu, h16, st);
+    else dh_fp8<MXF, SmallCfg<T8>>(a, dq, ds, d_gu, h16, st);
+  } else {
+    dh_fp8<MXF, SmallCfg<T8>>(a, dq, ds, d_gu, h16, st);
+  }
+  if (h16) quant(h16, a.A, a.f, static_cast<uint8_t*>(const_cast<void*>(a.act_h)), const_cast<float*>(a.h_scale));
+  // dX = Q(dGU) W1
+  quant(d_gu, a.A, 2 * a.f, gq, gs);
+  if constexpr (!MXF) {
+    if (big8(a.tile, a.d)) dx_fp8<MXF, BigCfg8<T8>>(a, gq, gs, st);
+    else dx_fp8<MXF, SmallCfg<T8>>(a, gq, gs, st);
+  } else {
+    dx_fp8<MXF, SmallCfg<T8>>(a, gq, gs, st);
+  }
+  if constexpr (MXF) {
+    // weight gradients in bf16 on dequantised X and H
+    dequant(a.x_perm, a.x_scale, a.A, a.d, xd);
+    dequant(a.act_h, a.h_scale, a.A, a.f, hd);
+    wgrad_any<bf16_t>(a.tile, a.d_out, hd, d_gu, xd, a.dw1, a.dw2, a.offsets, a.d, a.f, a.E, st);
+  } else {
+    // weight gradients in FP8: the four operands in 128-row x 1 blocks
+    int32_t* kblk = reinterpret_cast<int32_t*>(at(a.ws, w.kblk));
+    auto tq = [&](size_t o) { return reinterpret_cast<fp8_t*>(at(a.ws, o)); };
+    auto ts = [&](size_t o) { return reinterpret_cast<float*>(at(a.ws, o)); };
+    kblock_offsets_kernel<<<1, 1024, 0, st>>>(a.offsets, kblk, int(a.E));
+    quant_tokens(a.d_out, nullptr, a.offsets, kblk, a.E, a.A, a.d, tq(w.t_do), ts(w.t_do_s), st);
+    quant_tokens(a.act_h, a.h_scale, a.offsets, kblk, a.E, a.A, a.f, tq(w.t_h), ts(w.t_h_s), st);
+    quant_tokens(d_gu, nullptr, a.offsets, kblk, a.E, a.A, 2 * a.f, tq(w.t_gu), ts(w.t_gu_s), st);
+    quant_tokens(a.x_perm, a.x_scale, a.offsets, kblk, a.E, a.A, a.d, tq(w.t_x), ts(w.t_x_s), st);
+    wgrad_fp8(tq(w.t_do), ts(w.t_do_s), tq(w.t_h), ts(w.t_h_s), tq(w.t_gu), ts(w.t_gu_s), tq(w.t_x),
+              ts(w.t_x_s), kblk, a.dw1, a.dw2, a.offsets, a.d, a.f, a.E, st);
+  }
 }
 
 void launch_grouped_ffn(const FfnLaunch& a, hipStream_t st) {
@@ -1575,7 +1836,7 @@ void launch_grouped_ffn(const FfnLaunch& a, hipStream_t st) {
     copy_bytes(a.x_perm, a.out_perm, a.A * a.d * (a.act == 1 ? 2 : 4), st);
     return;
   }
-  const FfnWs w = ffn_ws(a.A, a.d, a.f, a.act == 1 ? 2 : 4, a.wt >= 2, false, a.recompute);
+  const FfnWs w = ffn_ws(a.A, a.d, a.f, a.E, a.act == 1 ? 2 : 4, a.wt, false, a.recompute);
   // what the backward will not find saved goes to the workspace (H) or is
   // not stored at all (GU)
   void* gu = a.recompute == 2 ? nullptr : a.act_gu;
@@ -1584,9 +1845,10 @@ void launch_grouped_ffn(const FfnLaunch& a, hipStream_t st) {
   bf16_t* h16 = reinterpret_cast<bf16_t*>(at(a.ws, w.h_bf16));
   ffn_fwd_gu_h(a, gu, h, hs, h16, st);
   if (a.wt == 3) {
-    gemm2_fwd_mx(a, static_cast<const uint8_t*>(h), reinterpret_cast<const uint8_t*>(hs), st);
+    gemm2_fwd_mx<SmallCfg<mx8_t>>(a, static_cast<const uint8_t*>(h), reinterpret_cast<const uint8_t*>(hs), st);
   } else if (a.wt == 2) {
-    gemm2_fwd_fp8(a, static_cast<const uint8_t*>(h), hs, st);
+    if (big8(a.tile, a.d)) gemm2_fwd_fp8<BigCfg8<fp8_t>>(a, static_cast<const uint8_t*>(h), hs, st);
+    else gemm2_fwd_fp8<SmallCfg<fp8_t>>(a, static_cast<const uint8_t*>(h), hs, st);
   } else if (a.wt == 1) {
     if (big_rows(a.tile, a.A, a.E, a.d)) gemm2_fwd<BigCfg>(a, h, st);
     else gemm2_fwd<SmallCfg<bf16_t>>(a, h, st);
@@ -1605,7 +1867,7 @@ void launch_grouped_ffn_bwd(const FfnBwdLaunch& a, hipStream_t st) {
     return;
   }
   const bool fp8 = a.wt >= 2;
-  const FfnWs w = ffn_ws(a.A, a.d, a.f, es, fp8, true, a.recompute);
+  const FfnWs w = ffn_ws(a.A, a.d, a.f, a.E, es, a.wt, true, a.recompute);
   FfnBwdLaunch b = a;
   void* h_out = nullptr;  // activation recompute: H rebuilt by the dH epilogue
   if (a.recompute) {

@@ -126,8 +126,10 @@ struct FfnLaunch {
   int recompute;  // 0 keep GU and H, 1 keep GU only, 2 keep neither
 };
 void launch_grouped_ffn(const FfnLaunch& a, hipStream_t st);
-// Workspace bytes of the grouped FFN forward (bwd = false) or backward.
-size_t ffn_ws_bytes(int64_t A, int64_t d, int64_t f, int act_bytes, bool fp8, bool bwd, int recompute);
+// Workspace bytes of the grouped FFN forward (bwd = false) or backward; wt as
+// in FfnLaunch.
+size_t ffn_ws_bytes(int64_t A, int64_t d, int64_t f, int64_t E, int act_bytes, int wt, bool bwd,
+                    int recompute);
 // FP8 E4M3 quantisation of rows in 1 x 128 blocks (cols a multiple of 128).
 void launch_quant_rows(const void* src, bool src_bf16, int64_t rows, int64_t cols, uint8_t* q,
                        float* scale, hipStream_t st);

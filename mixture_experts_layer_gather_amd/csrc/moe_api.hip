@@ -146,11 +146,11 @@ size_t moe_workspace_size(const moe_config* cfg, int op) {
   switch (op) {
     case MOE_OP_DISPATCH: return T ? round_up(size_t(dispatch_chunks(T)) * size_t(E) * 4) : 0;
     case MOE_OP_GROUPED_FFN:
-      return round_up(moe::ffn_ws_bytes(T * k, cfg->hidden, f, int(act_bytes(cfg->act_dtype)),
-                                        is_fp8(cfg), false, cfg->recompute));
+      return round_up(moe::ffn_ws_bytes(T * k, cfg->hidden, f, E, int(act_bytes(cfg->act_dtype)),
+                                        weight_kind(cfg), false, cfg->recompute));
     case MOE_OP_GROUPED_FFN_BWD:
-      return round_up(moe::ffn_ws_bytes(T * k, cfg->hidden, f, int(act_bytes(cfg->act_dtype)),
-                                        is_fp8(cfg), true, cfg->recompute));
+      return round_up(moe::ffn_ws_bytes(T * k, cfg->hidden, f, E, int(act_bytes(cfg->act_dtype)),
+                                        weight_kind(cfg), true, cfg->recompute));
     case MOE_OP_ROUTE_BWD: {
       const int Z = moe::route_bwd_zsplit(T, cfg->hidden, E);
       const size_t parts = Z > 1 ? size_t(Z) * size_t(E) * size_t(cfg->hidden) * 4 : 0;

@@ -548,7 +548,7 @@ def aux_loss_dlogits(logits, idx, E: int, coeff: float, d_aux: float = 1.0) -> n
 # FP8 layers: whether the weight-gradient operands are quantised in 128-row x 1
 # blocks (fp8_roundtrip_tokens) or taken unquantised (the forward's
 # dequantised X and H, the bf16 gradients)
-FP8_WGRAD_TOKEN_BLOCKS = False
+FP8_WGRAD_TOKEN_BLOCKS = True
 
 
 def _expert_weight(w, e):

@@ -283,6 +283,7 @@ void orc_e4m3_encode_array(const float *v, uint8_t *out, int64_t n)
 
 void orc_e4m3_decode_array(const uint8_t *c, float *out, int64_t n)
 {
+#pragma omp parallel for schedule(static)
     for (int64_t i = 0; i < n; ++i) out[i] = orc_e4m3_decode(c[i]);
 }
 

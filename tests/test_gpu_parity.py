@@ -130,6 +130,10 @@ SMALL = {
     # and ragged groups smaller than a tile
     "qwen_skew_mini_big": S.mini(S.CONFIGS[3], T=700, d=256, f=128, E=16).replace(k=4, seed_base=34),
     "deepseek_fp8_mini": S.mini(S.CONFIGS[4], T=400, d=384, f=256, E=32).replace(k=6),
+    # FP8 with the 256 x 256 tile forced on all four row-grouped products
+    # (d and 2f multiples of 256), ragged experts of 0 to a few hundred rows
+    "deepseek_fp8_mini_big": S.mini(S.CONFIGS[4], T=600, d=512, f=256, E=16).replace(
+        k=4, num_groups=4, topk_groups=2, seed_base=35),
     # the other group rule (a group's best score instead of its best two)
     # and sigmoid gates without renormalisation
     "deepseek_mini_gmax": S.mini(S.CONFIGS[2], T=300, d=256, f=256, E=32).replace(
@@ -150,7 +154,7 @@ SMALL = {
 }
 
 
-FORCED_TILE = {"mixtral_mini_bigtile": "big", "qwen_skew_mini_big": "big"}
+FORCED_TILE = {"mixtral_mini_bigtile": "big", "qwen_skew_mini_big": "big", "deepseek_fp8_mini_big": "big"}
 
 
 @pytest.mark.parametrize("name", list(SMALL))
