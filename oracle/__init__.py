@@ -87,6 +87,7 @@ def lib():
         L.orc_mx_scale_exp.restype = ctypes.c_int
         L.orc_mx_scale_exp.argtypes = [ctypes.c_float]
         L.orc_quant_mx_rows.argtypes = [i64, i64, P, P, P]
+        L.orc_quant_mx_cols.argtypes = [i64, i64, P, P, P]
         _lib = L
     return _lib
 
@@ -312,9 +313,17 @@ def quant_mx_rows(src):
 
 def quant_mx_cols(src):
     """MXFP8 in 32 x 1 blocks (32 consecutive rows of one column), for an
-    operand contracted over its rows: (q uint8 [R,C], e8m0 uint8 [R/32, C])."""
-    qt, et = quant_mx_rows(np.ascontiguousarray(as_f32(src).T))
-    return np.ascontiguousarray(qt.T), np.ascontiguousarray(et.T)
+    operand contracted over its rows: (q uint8 [R,C], e8m0 uint8 [R/32, C]),
+    the row rule applied to the transpose (spec.c: orc_quant_mx_cols walks
+    the columns in place)."""
+    s = as_f32(src)
+    R, C = s.shape
+    if R % MX_BLOCK:
+        raise ValueError("MXFP8 column blocks need a multiple of 32 rows")
+    q = np.empty((R, C), dtype=np.uint8)
+    e = np.empty((R // MX_BLOCK, C), dtype=np.uint8)
+    lib().orc_quant_mx_cols(R, C, _ptr(s), _ptr(q), _ptr(e))
+    return q, e
 
 
 def mx_scale(e8m0) -> np.ndarray:

@@ -355,3 +355,25 @@ void orc_quant_mx_rows(int64_t R, int64_t C, const float *src, uint8_t *q, uint8
         }
     }
 }
+
+/* The same MXFP8 rule in 32 x 1 blocks: src [R,C] fp32, R a multiple of 32,
+ * each block 32 consecutive rows of one column (the row rule applied to the
+ * transpose): q [R,C] E4M3 codes, e8m0 [R/32, C]. */
+void orc_quant_mx_cols(int64_t R, int64_t C, const float *src, uint8_t *q, uint8_t *e8m0)
+{
+    int64_t nb = R / 32;
+#pragma omp parallel for schedule(static)
+    for (int64_t b = 0; b < nb; ++b) {
+        for (int64_t c = 0; c < C; ++c) {
+            float amax = 0.0f;
+            for (int i = 0; i < 32; ++i) {
+                float a = fabsf(src[(b * 32 + i) * C + c]);
+                if (a > amax) amax = a;
+            }
+            int x = orc_mx_scale_exp(amax);
+            e8m0[b * C + c] = (uint8_t)(x + 127);
+            for (int i = 0; i < 32; ++i)
+                q[(b * 32 + i) * C + c] = orc_e4m3_encode(ldexpf(src[(b * 32 + i) * C + c], -x));
+        }
+    }
+}

@@ -367,3 +367,15 @@ def test_mx_properties_and_roundtrip():
     assert np.array_equal(qc, q[:, :64].T) and np.array_equal(ec, e[:, :2].T)
     with pytest.raises(ValueError):
         oracle.quant_mx_rows(np.zeros((2, 48), F32))
+
+
+def test_mx_cols_are_the_rows_of_the_transpose():
+    """The column-block MXFP8 quantiser equals the row-block one applied to
+    the transpose, codes and scales, over magnitudes across the fp32 range."""
+    rng = np.random.default_rng(13)
+    a = (rng.normal(size=(96, 70)) * np.exp(rng.normal(size=(1, 70)) * 15)).astype(np.float32)
+    a[:32, 3] = 0.0
+    a[40, 5] = -3.0e-41
+    q, e = oracle.quant_mx_cols(a)
+    qt, et = oracle.quant_mx_rows(np.ascontiguousarray(a.T))
+    assert np.array_equal(q, qt.T) and np.array_equal(e, et.T)
