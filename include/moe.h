@@ -46,7 +46,9 @@
  *    auxiliary loss. Every other call enqueues nothing.
  *  - Outputs are overwritten unless marked "+=". For the same inputs every
  *    output is bitwise identical from run to run (no floating-point atomics).
- *  - The library keeps no global state; calls are thread-safe.
+ *  - The library keeps no global state, except the per-device scratch array
+ *    of moe_dispatch_scratch; calls are thread-safe (that one excepted for
+ *    overlapping calls on one GPU).
  *
  * Notation: T tokens, d hidden, E experts, k top-k, f expert hidden size,
  * A = T*k dispatched rows. "act" is cfg->act_dtype (f32 or bf16),
@@ -183,6 +185,28 @@ int moe_dispatch(const moe_config *cfg, const void *x, const int32_t *topk_idx,
                  int32_t *counts, int32_t *offsets, int32_t *row_id_map,
                  int32_t *perm_token, void *x_perm, void *x_scale, void *ws,
                  size_t ws_bytes, void *stream);
+
+/* moe_dispatch for callers that cannot allocate device memory: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.
+ * Same arguments, results and errors as moe_dispatch, without ws/ws_bytes:
+ * the workspace is a device array inside the library, one per GPU, of
+ * MOE_DISPATCH_SCRATCH_BYTES (8 MiB), held until the process ends. The call
+ * allocates nothing (no hipMalloc, hipFree or allocating library routine);
+ * its first call on a device looks the array's address up there
+ * (hipGetSymbolAddress; MOE_ERR_HIP if that fails), with the device of
+ * `stream` current. Every call on a GPU shares that GPU's array: calls that
+ * may overlap on one GPU (different streams, or host threads, without
+ * ordering between them) race and must not be made; calls on one stream
+ * are ordered and safe. Nothing in the array needs clearing (each call
+ * overwrites every entry it reads).
+ * Errors: as moe_dispatch; MOE_ERR_WORKSPACE when the configuration needs
+ * more than MOE_DISPATCH_SCRATCH_BYTES (moe_workspace_size(cfg,
+ * MOE_OP_DISPATCH) = ceil(T / 256) * E * 4 bytes, rounded up to 256: e.g.
+ * T up to 524288 tokens with E = 1024, up to 2^22 with E = 128). */
+#define MOE_DISPATCH_SCRATCH_BYTES (8u << 20)
+int moe_dispatch_scratch(const moe_config *cfg, const void *x, const int32_t *topk_idx,
+                         int32_t *counts, int32_t *offsets, int32_t *row_id_map,
+                         int32_t *perm_token, void *x_perm, void *x_scale, void *stream);
 
 /* Grouped SwiGLU expert FFN forward over expert-contiguous rows (Megatron
  * Core MoE summary, section 2.4: many expert GEMMs in one kernel). For each

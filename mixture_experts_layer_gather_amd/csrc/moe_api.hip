@@ -5,8 +5,13 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <atomic>
+
 #include "../../include/moe.h"
 #include "launch.hpp"
+
+// The device array behind moe_dispatch_scratch (see scratch_ptr below).
+static __device__ __align__(256) uint8_t scratch[MOE_DISPATCH_SCRATCH_BYTES];
 
 namespace {
 
@@ -124,6 +129,73 @@ size_t aux_bwd_bytes(const moe_config* c) {
   return c->aux_coeff != 0.0f ? aux_part_bytes(c) + round_up(size_t(c->num_experts) * 4) : 0;
 }
 
+// Workspace of moe_dispatch_scratch, for callers that cannot allocate: one
+// array per device (each GPU the library runs on holds its own copy until
+// the process ends), shared by every call on that device. Host code never
+// passes its name to a kernel (on the host it is only a stand-in for the
+// symbol): the device address comes from hipGetSymbolAddress, once per
+// device, with that device current, and is kept in g_scratch. The dispatch
+// kernels overwrite every entry they read (per-chunk counts, then bases), so
+// nothing needs clearing between calls.
+constexpr size_t kDispatchScratchBytes = size_t(MOE_DISPATCH_SCRATCH_BYTES);
+constexpr int kMaxDevices = 64;
+std::atomic<void*> g_scratch[kMaxDevices];
+
+int scratch_ptr(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return MOE_ERR_HIP;
+  void* p = g_scratch[dev].load(std::memory_order_acquire);
+  if (!p) {
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return MOE_ERR_HIP;
+    g_scratch[dev].store(p, std::memory_order_release);
+  }
+  *out = p;
+  return MOE_OK;
+}
+
+// moe_dispatch, with its workspace either the caller's (ws, ws_bytes) or,
+// with from_scratch, the device array `scratch` (taken after every argument
+// check, so that a refused call touches no device state).
+int dispatch_call(const moe_config* cfg, const void* x, const int32_t* topk_idx, int32_t* counts,
+                  int32_t* offsets, int32_t* row_id_map, int32_t* perm_token, void* x_perm,
+                  void* x_scale, void* ws, size_t ws_bytes, void* stream, bool from_scratch) {
+  MOE_CHECK(check_cfg(cfg));
+  const bool fp8 = is_fp8(cfg);
+  if (from_scratch && moe_workspace_size(cfg, MOE_OP_DISPATCH) > kDispatchScratchBytes)
+    return MOE_ERR_WORKSPACE;
+  if (cfg->num_tokens == 0) {  // an empty batch: every expert has no rows
+    MOE_CHECK(need(counts)); MOE_CHECK(need(offsets)); MOE_CHECK(align_all(counts, offsets));
+    const hipStream_t st = static_cast<hipStream_t>(stream);
+    moe::launch_zero(counts, cfg->num_experts * 4, st);
+    moe::launch_zero(offsets, (cfg->num_experts + 1) * 4, st);
+    return launched();
+  }
+  MOE_CHECK(need(x)); MOE_CHECK(need(topk_idx)); MOE_CHECK(need(counts)); MOE_CHECK(need(offsets));
+  MOE_CHECK(need(row_id_map)); MOE_CHECK(need(perm_token)); MOE_CHECK(need(x_perm));
+  if (fp8) MOE_CHECK(need(x_scale));
+  MOE_CHECK(align(x)); MOE_CHECK(align(topk_idx)); MOE_CHECK(align(counts)); MOE_CHECK(align(offsets));
+  MOE_CHECK(align(row_id_map)); MOE_CHECK(align(perm_token)); MOE_CHECK(align(x_perm));
+  MOE_CHECK(align(x_scale)); MOE_CHECK(align(ws));
+  const size_t need_ws = moe_workspace_size(cfg, MOE_OP_DISPATCH);
+  if (from_scratch) {
+    if (need_ws > kDispatchScratchBytes) return MOE_ERR_WORKSPACE;
+    MOE_CHECK(scratch_ptr(&ws));
+    ws_bytes = kDispatchScratchBytes;
+  }
+  if (!ws || ws_bytes < need_ws) return MOE_ERR_WORKSPACE;
+  moe::DispatchLaunch a{};
+  a.x = x; a.idx = topk_idx; a.counts = counts; a.offsets = offsets; a.row_id_map = row_id_map;
+  a.perm_token = perm_token; a.x_perm = x_perm; a.x_scale = static_cast<float*>(x_scale);
+  a.chunk_base = static_cast<int32_t*>(ws);
+  a.T = cfg->num_tokens; a.d = cfg->hidden; a.E = cfg->num_experts; a.k = cfg->top_k;
+  a.act = cfg->act_dtype == MOE_DTYPE_BF16 ? 1 : 0;
+  a.fp8 = fp8;
+  a.mx = cfg->weight_dtype == MOE_DTYPE_MXFP8;
+  a.qblock = cfg->quant_block;
+  moe::launch_dispatch(a, static_cast<hipStream_t>(stream));
+  return launched();
+}
+
 }  // namespace
 
 extern "C" {
@@ -187,33 +259,15 @@ int moe_route(const moe_config* cfg, const void* x, const float* w_router, const
 int moe_dispatch(const moe_config* cfg, const void* x, const int32_t* topk_idx, int32_t* counts,
                  int32_t* offsets, int32_t* row_id_map, int32_t* perm_token, void* x_perm,
                  void* x_scale, void* ws, size_t ws_bytes, void* stream) {
-  MOE_CHECK(check_cfg(cfg));
-  const bool fp8 = is_fp8(cfg);
-  if (cfg->num_tokens == 0) {  // an empty batch: every expert has no rows
-    MOE_CHECK(need(counts)); MOE_CHECK(need(offsets)); MOE_CHECK(align_all(counts, offsets));
-    const hipStream_t st = static_cast<hipStream_t>(stream);
-    moe::launch_zero(counts, cfg->num_experts * 4, st);
-    moe::launch_zero(offsets, (cfg->num_experts + 1) * 4, st);
-    return launched();
-  }
-  MOE_CHECK(need(x)); MOE_CHECK(need(topk_idx)); MOE_CHECK(need(counts)); MOE_CHECK(need(offsets));
-  MOE_CHECK(need(row_id_map)); MOE_CHECK(need(perm_token)); MOE_CHECK(need(x_perm));
-  if (fp8) MOE_CHECK(need(x_scale));
-  MOE_CHECK(align(x)); MOE_CHECK(align(topk_idx)); MOE_CHECK(align(counts)); MOE_CHECK(align(offsets));
-  MOE_CHECK(align(row_id_map)); MOE_CHECK(align(perm_token)); MOE_CHECK(align(x_perm));
-  MOE_CHECK(align(x_scale)); MOE_CHECK(align(ws));
-  if (!ws || ws_bytes < moe_workspace_size(cfg, MOE_OP_DISPATCH)) return MOE_ERR_WORKSPACE;
-  moe::DispatchLaunch a{};
-  a.x = x; a.idx = topk_idx; a.counts = counts; a.offsets = offsets; a.row_id_map = row_id_map;
-  a.perm_token = perm_token; a.x_perm = x_perm; a.x_scale = static_cast<float*>(x_scale);
-  a.chunk_base = static_cast<int32_t*>(ws);
-  a.T = cfg->num_tokens; a.d = cfg->hidden; a.E = cfg->num_experts; a.k = cfg->top_k;
-  a.act = cfg->act_dtype == MOE_DTYPE_BF16 ? 1 : 0;
-  a.fp8 = fp8;
-  a.mx = cfg->weight_dtype == MOE_DTYPE_MXFP8;
-  a.qblock = cfg->quant_block;
-  moe::launch_dispatch(a, static_cast<hipStream_t>(stream));
-  return launched();
+  return dispatch_call(cfg, x, topk_idx, counts, offsets, row_id_map, perm_token, x_perm, x_scale, ws,
+                       ws_bytes, stream, false);
+}
+
+int moe_dispatch_scratch(const moe_config* cfg, const void* x, const int32_t* topk_idx, int32_t* counts,
+                         int32_t* offsets, int32_t* row_id_map, int32_t* perm_token, void* x_perm,
+                         void* x_scale, void* stream) {
+  return dispatch_call(cfg, x, topk_idx, counts, offsets, row_id_map, perm_token, x_perm, x_scale,
+                       nullptr, 0, stream, true);
 }
 
 int moe_grouped_ffn(const moe_config* cfg, const void* x_perm, const void* x_scale,

@@ -27,7 +27,7 @@ def _declared():
 
 def test_exports_every_declared_symbol(M):
     names = _declared()
-    assert len(names) == 13, names
+    assert len(names) == 14, names
     L = M.lib()
     for n in names:
         assert hasattr(L, n), n
@@ -95,6 +95,19 @@ def test_size_limits(M):
     # 2^38 elements, no GEMM has more than 2^28 tiles)
     for d, f, act in ((1000, 256, "bf16"), (256, 1000, "bf16"), (136, 256, "f32"), (256, 264, "f32")):
         assert _route(M, _cfg(M, d=d, f=f, act=act, weight=act)) == -1, (d, f, act)
+
+
+def test_dispatch_scratch_refusals(M):
+    """The allocation-free dispatch refuses, before any device call, a
+    configuration whose workspace exceeds its device array, and the argument
+    errors of moe_dispatch."""
+    L = M.lib()
+    N = None
+    big = _cfg(M, T=1 << 21, E=1024, d=128)        # 8192 chunks x 1024 experts x 4 B = 32 MiB
+    assert L.moe_workspace_size(ctypes.byref(big), 1) > (8 << 20)
+    assert L.moe_dispatch_scratch(ctypes.byref(big), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, N, N) == -4
+    assert L.moe_dispatch_scratch(ctypes.byref(_cfg(M, k=9)), *([FAKE] * 7), N, N) == -1
+    assert L.moe_dispatch_scratch(ctypes.byref(_cfg(M, T=0)), N, N, N, FAKE, N, N, N, N, N) == -1
 
 
 def test_empty_batch_enqueues_nothing(M):
