@@ -317,6 +317,15 @@ __device__ __forceinline__ void dma16(u32x4 rsrc, void* dst, uint32_t voff) {
                : "v"(voff), "s"(lds), "s"(rsrc)
                : "memory", "m0");
 }
+// The same with 4 bytes per lane (lane l's dword to LDS at dst + 4 * l): a
+// gather of one value per row, such as FP8 row scales.
+__device__ __forceinline__ void dma4(u32x4 rsrc, void* dst, uint32_t voff) {
+  const uint32_t lds = uint32_t(reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) char*)dst));
+  asm volatile("s_mov_b32 m0, %1\n\tbuffer_load_dword %0, %2, 0 offen lds"
+               :
+               : "v"(voff), "s"(lds), "s"(rsrc)
+               : "memory", "m0");
+}
 // s_waitcnt vmcnt(0) (expcnt and lgkmcnt left at their maxima)
 __device__ __forceinline__ void wait_vm0() { __builtin_amdgcn_s_waitcnt(0x0f70); }
 
@@ -394,6 +403,14 @@ template <typename T> __device__ __forceinline__ void store8(T* p, const float* 
   } else {
     Vec16<float>::store(p, v);
     Vec16<float>::store(p + 4, v + 4);
+  }
+}
+template <typename T> __device__ __forceinline__ void store8_stream(T* p, const float* v) {
+  if constexpr (sizeof(T) == 2) {
+    st_stream(p, Vec16<bf16_t>::pack(v));
+  } else {
+    st_stream(p, Vec16<float>::pack(v));
+    st_stream(p + 4, Vec16<float>::pack(v + 4));
   }
 }
 // Rounds 8 values to the storage type T and back (the values as saved).
@@ -711,6 +728,11 @@ void gemm_kernel(GemmArgs g) {
     }
     if constexpr (TOKSCALE) {
       rs = (live && ts_col) ? ts_col[int64_t(kb0 + s) * ts_ld] : 0.0f;
+    } else if constexpr (FP8 && !MX && NS > 2) {
+      // deep pipelines: the row scales land in LDS by DMA like the tiles;
+      // wave w gathers rows 64 w .. 64 w + 63 (rows past the group read 0)
+      dma4(rsrc_words(sa_base, live ? sa_end : 0), &st.SA[wave * 64],
+           uint32_t(((wave * 64 + lane) * g.a_scale_ld + s) * 4));
     } else if constexpr (FP8) {
       const rsrc_t sr = make_rsrc(sa_base, live ? sa_end : 0);
       rs = __builtin_bit_cast(
@@ -939,8 +961,10 @@ void gemm_kernel(GemmArgs g) {
       }
     }
   } else {
-    static_assert(PA::DMA && PB::DMA && !FP8, "deep pipelines take DMA operands only");
-    constexpr int NDMA = PA::NB + PB::NB;  // DMA instructions per wave and step
+    static_assert(PA::DMA && PB::DMA && (!FP8 || (!MX && !TOKSCALE && NTH / 64 * 64 >= BM)),
+                  "deep pipelines take DMA operands (and FP8 row scales) only");
+    // DMA instructions per wave and step (FP8: one more, the row scales)
+    constexpr int NDMA = PA::NB + PB::NB + (FP8 ? 1 : 0);
     constexpr int LEFT = NDMA * (NS - 2);  // may stay in flight at a step's end
     static_assert(LEFT < 64, "vmcnt range");
     constexpr int WAIT = (LEFT & 15) | ((LEFT >> 4) << 14) | (7 << 4) | (15 << 8);
@@ -1019,7 +1043,11 @@ void gemm_kernel(GemmArgs g) {
           const int col = n0 + wn * WTN + c8 * 8;
           float v[8];
           lds_read8(&stg[rr * EP + c8 * 8], v);
-          if constexpr (EPI == EPI_STORE) {
+          if constexpr (EPI == EPI_STORE && MODE == G_KSPLIT) {
+            // weight gradients: written once, never read by this kernel;
+            // streaming stores keep them from displacing the operands in L2
+            store8_stream<TC>(Cb + row * g.ldc + col, v);
+          } else if constexpr (EPI == EPI_STORE) {
             store8<TC>(Cb + row * g.ldc + col, v);
           } else {  // EPI_DSWIGLU: v = dH; C = dGU [rows, 2f]
             const TO* GU = reinterpret_cast<const TO*>(g.aux0);
@@ -1253,19 +1281,24 @@ __global__ __launch_bounds__(1024) void kblock_offsets_kernel(const int32_t* __r
   if (g == 0) kblk[0] = 0;
 }
 
-// One workgroup per (block, 256 columns): thread (cg, rg) holds columns
-// 8 cg .. 8 cg + 7 of rows rg, rg + 8, ..., rg + 120 of the block in
+// One workgroup per (block, 128 columns): thread (cg, rg) holds columns
+// 8 cg .. 8 cg + 7 of rows rg, rg + 16, ..., rg + 112 of the block in
 // registers; the column maxima meet in LDS. Sources: bf16 rows (SRC_FP8 =
 // false) or E4M3 codes with fp32 scales per 1 x 128 block of a row, taken as
-// float(code) * scale in fp32.
-template <bool SRC_FP8>
+// float(code) * scale in fp32. ROWQ (bf16 sources): the same read also
+// quantises each row's 128 columns as one 1 x 128 block (the data-gradient
+// products' operand), into rq / rs [A, C/128]: the tile's 16 threads of one
+// row reduce its amax with lane shuffles (they share a wave).
+template <bool SRC_FP8, bool ROWQ>
 __global__ __launch_bounds__(256) void quant_tokens_kernel(const void* __restrict__ src,
                                                            const float* __restrict__ src_scale,
                                                            const int32_t* __restrict__ offsets,
                                                            const int32_t* __restrict__ kblk, int G,
                                                            int64_t C, fp8_t* __restrict__ q,
-                                                           float* __restrict__ scale) {
-  __shared__ float s_max[8][257];
+                                                           float* __restrict__ scale, fp8_t* __restrict__ rq,
+                                                           float* __restrict__ rs) {
+  static_assert(!(SRC_FP8 && ROWQ), "row blocks are taken from bf16 sources");
+  __shared__ float s_max[16][129];
   const int b = blockIdx.x;
   if (b >= kblk[G]) return;
   // the expert owning block b: the last e with kblk[e] <= b
@@ -1276,18 +1309,17 @@ __global__ __launch_bounds__(256) void quant_tokens_kernel(const void* __restric
     else hi = mid - 1;
   }
   const int64_t r0 = int64_t(offsets[lo]) + int64_t(b - kblk[lo]) * 128;
-  const int nrows = min(int64_t(128), int64_t(offsets[lo + 1]) - r0);
-  const int cg = threadIdx.x % 32, rg = threadIdx.x / 32;
-  const int64_t c0 = int64_t(blockIdx.y) * 256 + cg * 8;
-  const bool col_ok = c0 < C;
-  float v[16][8];
+  const int nrows = int(min(int64_t(128), int64_t(offsets[lo + 1]) - r0));
+  const int cg = threadIdx.x % 16, rg = threadIdx.x / 16;
+  const int64_t c0 = int64_t(blockIdx.y) * 128 + cg * 8;  // C is a multiple of 128
+  float v[8][8];
   float m[8];
 #pragma unroll
   for (int c = 0; c < 8; ++c) m[c] = 0.0f;
 #pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    const int rr = rg + 8 * i;
-    if (col_ok && rr < nrows) {
+  for (int i = 0; i < 8; ++i) {
+    const int rr = rg + 16 * i;
+    if (rr < nrows) {
       const int64_t off = (r0 + rr) * C + c0;
       if constexpr (SRC_FP8) {
         const u32x2 w = *reinterpret_cast<const u32x2*>(static_cast<const fp8_t*>(src) + off);
@@ -1310,24 +1342,45 @@ __global__ __launch_bounds__(256) void quant_tokens_kernel(const void* __restric
   }
 #pragma unroll
   for (int c = 0; c < 8; ++c) s_max[rg][cg * 8 + c] = m[c];
+  if constexpr (ROWQ) {
+    // 1 x 128 row blocks: amax over the row's 16 threads (lanes 16 j .. 16 j + 15)
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int rr = rg + 16 * i;
+      float a = 0.0f;
+#pragma unroll
+      for (int c = 0; c < 8; ++c) a = fmaxf(a, fabsf(v[i][c]));
+#pragma unroll
+      for (int o = 8; o >= 1; o >>= 1) a = fmaxf(a, __shfl_xor(a, o, kWave));
+      const float sr = (a == 0.0f) ? 1.0f : a / 448.0f;
+      if (rr < nrows) {
+        uint32_t w0 = 0, w1 = 0;
+        w0 = __builtin_amdgcn_cvt_pk_fp8_f32(v[i][0] / sr, v[i][1] / sr, w0, false);
+        w0 = __builtin_amdgcn_cvt_pk_fp8_f32(v[i][2] / sr, v[i][3] / sr, w0, true);
+        w1 = __builtin_amdgcn_cvt_pk_fp8_f32(v[i][4] / sr, v[i][5] / sr, w1, false);
+        w1 = __builtin_amdgcn_cvt_pk_fp8_f32(v[i][6] / sr, v[i][7] / sr, w1, true);
+        *reinterpret_cast<u32x2*>(rq + (r0 + rr) * C + c0) = u32x2{w0, w1};
+        if (cg == 0) rs[(r0 + rr) * (C / 128) + c0 / 128] = sr;
+      }
+    }
+  }
   __syncthreads();
   float sc[8];
 #pragma unroll
   for (int c = 0; c < 8; ++c) {
     float a = 0.0f;
 #pragma unroll
-    for (int r = 0; r < 8; ++r) a = fmaxf(a, s_max[r][cg * 8 + c]);
+    for (int r = 0; r < 16; ++r) a = fmaxf(a, s_max[r][cg * 8 + c]);
     sc[c] = (a == 0.0f) ? 1.0f : a / 448.0f;
   }
-  if (!col_ok) return;
   if (rg == 0) {
     float* sp = scale + int64_t(b) * C + c0;
     *reinterpret_cast<float4*>(sp) = float4{sc[0], sc[1], sc[2], sc[3]};
     *reinterpret_cast<float4*>(sp + 4) = float4{sc[4], sc[5], sc[6], sc[7]};
   }
 #pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    const int rr = rg + 8 * i;
+  for (int i = 0; i < 8; ++i) {
+    const int rr = rg + 16 * i;
     if (rr < nrows) {
       uint32_t w0 = 0, w1 = 0;
       w0 = __builtin_amdgcn_cvt_pk_fp8_f32(v[i][0] / sc[0], v[i][1] / sc[1], w0, false);
@@ -1343,16 +1396,22 @@ static int64_t token_blocks_bound(int64_t A, int64_t G) { return (A + G * 127) /
 
 // src [A, C] (bf16, or E4M3 codes with [A, C/128] fp32 row-block scales)
 // -> q [A, C] E4M3 and scale [token_blocks_bound(A, G), C] (rows past the
-// actual block count are not written)
+// actual block count are not written); with rq (bf16 sources) also the
+// 1 x 128 row blocks rq [A, C], rs [A, C/128] from the same read
 static void quant_tokens(const void* src, const float* src_scale, const int32_t* offsets,
                          const int32_t* kblk, int64_t G, int64_t A, int64_t C, fp8_t* q, float* scale,
-                         hipStream_t st) {
-  const dim3 grid(unsigned(token_blocks_bound(A, G)), unsigned((C + 255) / 256));
+                         hipStream_t st, fp8_t* rq = nullptr, float* rs = nullptr) {
+  const dim3 grid(unsigned(token_blocks_bound(A, G)), unsigned(C / 128));
   if (grid.x == 0) return;
   if (src_scale)
-    quant_tokens_kernel<true><<<grid, 256, 0, st>>>(src, src_scale, offsets, kblk, int(G), C, q, scale);
+    quant_tokens_kernel<true, false><<<grid, 256, 0, st>>>(src, src_scale, offsets, kblk, int(G), C, q, scale,
+                                                          nullptr, nullptr);
+  else if (rq)
+    quant_tokens_kernel<false, true><<<grid, 256, 0, st>>>(src, nullptr, offsets, kblk, int(G), C, q, scale, rq,
+                                                          rs);
   else
-    quant_tokens_kernel<false><<<grid, 256, 0, st>>>(src, nullptr, offsets, kblk, int(G), C, q, scale);
+    quant_tokens_kernel<false, false><<<grid, 256, 0, st>>>(src, nullptr, offsets, kblk, int(G), C, q, scale,
+                                                           nullptr, nullptr);
 }
 
 // ---------------------------------------------------------------------------
@@ -1382,6 +1441,8 @@ typedef Cfg<bf16_t, 256, 256, 64, 2, 4, 2> BigCfg;
 // FP8 / MXFP8 256 x 256 tile: 8 waves of 128 x 64, BK 128, two 64 KB stages
 // (one workgroup per CU), the byte layout of the bf16 Big tile
 template <typename T> using BigCfg8 = Cfg<T, 256, 256, 128, 2, 4, 2>;
+// FP8 weight gradients: 128 x 128, 4 waves of 64 x 64, BK 128, two stages
+typedef Cfg<fp8_t, 128, 128, 128, 2, 2, 2> WgradCfg8;
 typedef Cfg<bf16_t, 128, 256, 32, 2, 2, 3> WgradCfg;
 
 static int rows_tile_bound(int64_t A, int64_t G, int BM) {
@@ -1648,7 +1709,7 @@ static void wgrad_t(const void* d_out, const void* act_h, const void* d_gu, cons
 static void wgrad_fp8(const fp8_t* dq, const float* ds, const fp8_t* hq, const float* hs, const fp8_t* gq,
                       const float* gs, const fp8_t* xq, const float* xs, const int32_t* kblk, void* dw1,
                       void* dw2, const int32_t* offsets, int64_t d, int64_t f, int64_t E, hipStream_t st) {
-  typedef SmallCfg<fp8_t> C;
+  typedef WgradCfg8 C;
   GemmArgs g3{};
   g3.A = dq; g3.lda = d; g3.a_scale = ds; g3.a_scale_ld = int(d);
   g3.B = hq; g3.ldb = f; g3.b_scale = hs; g3.b_scale_ld = int(f);
@@ -1792,7 +1853,16 @@ static void ffn_bwd_fp8(const FfnBwdLaunch& a, bf16_t* h16, hipStream_t st) {
   float* gs = reinterpret_cast<float*>(at(a.ws, w.d_gu_s));
   bf16_t* xd = reinterpret_cast<bf16_t*>(at(a.ws, w.x_deq));
   bf16_t* hd = reinterpret_cast<bf16_t*>(at(a.ws, w.h_deq));
-  quant(a.d_out, a.A, a.d, dq, ds);
+  int32_t* kblk = reinterpret_cast<int32_t*>(at(a.ws, w.kblk));
+  auto tq = [&](size_t o) { return reinterpret_cast<fp8_t*>(at(a.ws, o)); };
+  auto ts = [&](size_t o) { return reinterpret_cast<float*>(at(a.ws, o)); };
+  if constexpr (MXF) {
+    quant(a.d_out, a.A, a.d, dq, ds);
+  } else {
+    // dO read once: its 1 x 128 row blocks (dH) and 128-row blocks (dW2)
+    kblock_offsets_kernel<<<1, 1024, 0, st>>>(a.offsets, kblk, int(a.E));
+    quant_tokens(a.d_out, nullptr, a.offsets, kblk, a.E, a.A, a.d, tq(w.t_do), ts(w.t_do_s), st, dq, ds);
+  }
   // dH = Q(dO) W2 (+ SwiGLU backward from the saved bf16 GU)
   // (the MXFP8 instance keeps the 128 x 128 tile: its per-lane scale words
   // do not fit the 256 x 256 tile's registers)
@@ -1804,7 +1874,8 @@ static void ffn_bwd_fp8(const FfnBwdLaunch& a, bf16_t* h16, hipStream_t st) {
   }
   if (h16) quant(h16, a.A, a.f, static_cast<uint8_t*>(const_cast<void*>(a.act_h)), const_cast<float*>(a.h_scale));
   // dX = Q(dGU) W1
-  quant(d_gu, a.A, 2 * a.f, gq, gs);
+  if constexpr (MXF) quant(d_gu, a.A, 2 * a.f, gq, gs);
+  else quant_tokens(d_gu, nullptr, a.offsets, kblk, a.E, a.A, 2 * a.f, tq(w.t_gu), ts(w.t_gu_s), st, gq, gs);
   if constexpr (!MXF) {
     if (big8(a.tile, a.d)) dx_fp8<MXF, BigCfg8<T8>>(a, gq, gs, st);
     else dx_fp8<MXF, SmallCfg<T8>>(a, gq, gs, st);
@@ -1817,14 +1888,9 @@ static void ffn_bwd_fp8(const FfnBwdLaunch& a, bf16_t* h16, hipStream_t st) {
     dequant(a.act_h, a.h_scale, a.A, a.f, hd);
     wgrad_any<bf16_t>(a.tile, a.d_out, hd, d_gu, xd, a.dw1, a.dw2, a.offsets, a.d, a.f, a.E, st);
   } else {
-    // weight gradients in FP8: the four operands in 128-row x 1 blocks
-    int32_t* kblk = reinterpret_cast<int32_t*>(at(a.ws, w.kblk));
-    auto tq = [&](size_t o) { return reinterpret_cast<fp8_t*>(at(a.ws, o)); };
-    auto ts = [&](size_t o) { return reinterpret_cast<float*>(at(a.ws, o)); };
-    kblock_offsets_kernel<<<1, 1024, 0, st>>>(a.offsets, kblk, int(a.E));
-    quant_tokens(a.d_out, nullptr, a.offsets, kblk, a.E, a.A, a.d, tq(w.t_do), ts(w.t_do_s), st);
+    // weight gradients in FP8: the four operands in 128-row x 1 blocks (dO
+    // and dGU were quantised so with their row blocks)
     quant_tokens(a.act_h, a.h_scale, a.offsets, kblk, a.E, a.A, a.f, tq(w.t_h), ts(w.t_h_s), st);
-    quant_tokens(d_gu, nullptr, a.offsets, kblk, a.E, a.A, 2 * a.f, tq(w.t_gu), ts(w.t_gu_s), st);
     quant_tokens(a.x_perm, a.x_scale, a.offsets, kblk, a.E, a.A, a.d, tq(w.t_x), ts(w.t_x_s), st);
     wgrad_fp8(tq(w.t_do), ts(w.t_do_s), tq(w.t_h), ts(w.t_h_s), tq(w.t_gu), ts(w.t_gu_s), tq(w.t_x),
               ts(w.t_x_s), kblk, a.dw1, a.dw2, a.offsets, a.d, a.f, a.E, st);
