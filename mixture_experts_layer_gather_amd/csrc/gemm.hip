@@ -638,19 +638,21 @@ void gemm_kernel(GemmArgs g) {
     sa_base = reinterpret_cast<const char*>(g.a_scale + int64_t(row0) * g.a_scale_ld);
     sa_end = int64_t(mrows) * g.a_scale_ld * 4;
   }
-  // weight gradients: thread tid < BM stages the scale of A column m0 + tid
-  // (an output row), the next BN threads those of B columns n0 + ...; K step s
-  // is block kb0 + s of the scale arrays
-  const float* ts_col = nullptr;
-  int64_t ts_ld = 0;
+  // weight gradients: K step s is block kb0 + s of the scale arrays; its
+  // scales land in LDS by DMA, 64 consecutive ones per wave: the A scales of
+  // output rows m0 .. m0 + BM (waves below BM / 64), then the B scales of
+  // columns n0 .. n0 + BN
+  static_assert(!TOKSCALE || (BM % 64 == 0 && BN % 64 == 0 && BM + BN == NTH), "one scale run per wave");
   int kb0 = 0;
+  const float* ts_run = nullptr;
+  int64_t ts_ld = 0;
   if constexpr (TOKSCALE) {
     kb0 = g.kblk[grp];
-    if (tid < BM) {
-      ts_col = g.a_scale + m0 + tid;
+    if (wave * 64 < BM) {
+      ts_run = g.a_scale + m0 + wave * 64;
       ts_ld = g.a_scale_ld;
-    } else if (tid < BM + BN) {
-      ts_col = g.b_scale + n0 + (tid - BM);
+    } else {
+      ts_run = g.b_scale + n0 + (wave * 64 - BM);
       ts_ld = g.b_scale_ld;
     }
   }
@@ -727,7 +729,8 @@ void gemm_kernel(GemmArgs g) {
       for (int i = 0; i < 4 * PB::NT; ++i) rb[i] = __builtin_amdgcn_raw_buffer_load_b128(br, pb.voff[i], 0, 0);
     }
     if constexpr (TOKSCALE) {
-      rs = (live && ts_col) ? ts_col[int64_t(kb0 + s) * ts_ld] : 0.0f;
+      dma4(rsrc_words(ts_run + (live ? int64_t(kb0 + s) * ts_ld : 0), live ? 256 : 0), &st.SA[wave * 64],
+           uint32_t(lane * 4));
     } else if constexpr (FP8 && !MX && NS > 2) {
       // deep pipelines: the row scales land in LDS by DMA like the tiles;
       // wave w gathers rows 64 w .. 64 w + 63 (rows past the group read 0)
@@ -768,7 +771,7 @@ void gemm_kernel(GemmArgs g) {
     if constexpr (MX) {
       st.SA[tid] = __builtin_bit_cast(uint32_t, rs);
       if (tid < BN) st.SB[tid] = rsb;
-    } else if constexpr (FP8) {
+    } else if constexpr (FP8 && !TOKSCALE) {
       st.SA[tid] = rs;
     }
   };
@@ -938,7 +941,35 @@ void gemm_kernel(GemmArgs g) {
   // NS > 2 stages (DMA operands only): the loads of step s + NS - 1 are
   // issued at step s, and the barrier that ends step s waits only for step
   // s + 1 to land, so NS - 1 steps of loads are in flight.
-  if constexpr (NS == 2) {
+  if constexpr (TOKSCALE) {
+    // FP8 weight gradients: a few K steps per tile, so the loads of steps 0
+    // and 1 go out together; later steps are issued into a stage as soon as
+    // every wave is done with it, one step ahead (all DMA: NDMA instructions
+    // per wave and step, tiles and scales)
+    static_assert(NS == 2, "two stages");
+    constexpr int NDMA = PA::NB + PB::NB + 1;
+    constexpr int WAIT1 = (NDMA & 15) | ((NDMA >> 4) << 14) | (7 << 4) | (15 << 8);
+    if (nk > 0) {
+      issue(st0, 0);
+      issue(st1, 1);
+      __builtin_amdgcn_s_waitcnt(WAIT1);  // step 0 landed, step 1 may be in flight
+      __syncthreads();
+      for (int s = 0; s < nk; s += 2) {
+        compute(st0, s);
+        __syncthreads();
+        issue(st0, s + 2);
+        __builtin_amdgcn_s_waitcnt(WAIT1);  // step s + 1 landed
+        __syncthreads();
+        if (s + 1 < nk) compute(st1, s + 1);
+        __syncthreads();
+        issue(st1, s + 3);
+        __builtin_amdgcn_s_waitcnt(WAIT1);  // step s + 2 landed
+        __syncthreads();
+      }
+      wait_vm0();  // the last prefetches (zeros) before the epilogue reuses the LDS
+      __syncthreads();
+    }
+  } else if constexpr (NS == 2) {
     if (nk > 0) {
       const int nk2 = (nk + 1) & ~1;
       issue(st0, 0);
@@ -1706,10 +1737,15 @@ static void wgrad_t(const void* d_out, const void* act_h, const void* d_gu, cons
 // FP8 weight gradients: dW2 = dO^T H and dW1 = dGU^T X with every operand
 // in 128-row x 1 blocks (codes [A, C], scales [NB, C], kblk the first block
 // of each expert); bf16 results.
-static void wgrad_fp8(const fp8_t* dq, const float* ds, const fp8_t* hq, const float* hs, const fp8_t* gq,
-                      const float* gs, const fp8_t* xq, const float* xs, const int32_t* kblk, void* dw1,
-                      void* dw2, const int32_t* offsets, int64_t d, int64_t f, int64_t E, hipStream_t st) {
+static void wgrad_fp8(int tile, const fp8_t* dq, const float* ds, const fp8_t* hq, const float* hs,
+                      const fp8_t* gq, const float* gs, const fp8_t* xq, const float* xs, const int32_t* kblk,
+                      void* dw1, void* dw2, const int32_t* offsets, int64_t d, int64_t f, int64_t E,
+                      hipStream_t st) {
   typedef WgradCfg8 C;
+  (void)tile;
+  auto run = [&](GemmArgs& gg) {
+    run_gemm<C, bf16_t, false, false, G_KSPLIT, EPI_STORE>(gg, int(E) * gg.tiles_m * gg.tiles_n, st);
+  };
   GemmArgs g3{};
   g3.A = dq; g3.lda = d; g3.a_scale = ds; g3.a_scale_ld = int(d);
   g3.B = hq; g3.ldb = f; g3.b_scale = hs; g3.b_scale_ld = int(f);
@@ -1718,7 +1754,7 @@ static void wgrad_fp8(const fp8_t* dq, const float* ds, const fp8_t* hq, const f
   g3.offsets = offsets; g3.G = int(E);
   g3.M = int(d); g3.N = int(f);
   g3.tiles_m = int(d / C::BM); g3.tiles_n = int(f / C::BN);
-  run_gemm<C, bf16_t, false, false, G_KSPLIT, EPI_STORE>(g3, int(E) * g3.tiles_m * g3.tiles_n, st);
+  run(g3);
   GemmArgs g4{};
   g4.A = gq; g4.lda = 2 * f; g4.a_scale = gs; g4.a_scale_ld = int(2 * f);
   g4.B = xq; g4.ldb = d; g4.b_scale = xs; g4.b_scale_ld = int(d);
@@ -1727,7 +1763,7 @@ static void wgrad_fp8(const fp8_t* dq, const float* ds, const fp8_t* hq, const f
   g4.offsets = offsets; g4.G = int(E);
   g4.M = int(2 * f); g4.N = int(d);
   g4.tiles_m = int(2 * f / C::BM); g4.tiles_n = int(d / C::BN);
-  run_gemm<C, bf16_t, false, false, G_KSPLIT, EPI_STORE>(g4, int(E) * g4.tiles_m * g4.tiles_n, st);
+  run(g4);
 }
 
 template <typename TC16>
@@ -1892,7 +1928,7 @@ static void ffn_bwd_fp8(const FfnBwdLaunch& a, bf16_t* h16, hipStream_t st) {
     // and dGU were quantised so with their row blocks)
     quant_tokens(a.act_h, a.h_scale, a.offsets, kblk, a.E, a.A, a.f, tq(w.t_h), ts(w.t_h_s), st);
     quant_tokens(a.x_perm, a.x_scale, a.offsets, kblk, a.E, a.A, a.d, tq(w.t_x), ts(w.t_x_s), st);
-    wgrad_fp8(tq(w.t_do), ts(w.t_do_s), tq(w.t_h), ts(w.t_h_s), tq(w.t_gu), ts(w.t_gu_s), tq(w.t_x),
+    wgrad_fp8(a.tile, tq(w.t_do), ts(w.t_do_s), tq(w.t_h), ts(w.t_h_s), tq(w.t_gu), ts(w.t_gu_s), tq(w.t_x),
               ts(w.t_x_s), kblk, a.dw1, a.dw2, a.offsets, a.d, a.f, a.E, st);
   }
 }
