@@ -658,17 +658,23 @@ void gemm_kernel(GemmArgs g) {
   }
   // FP8: column-block scale rows of B; SwiGLU tiles span a gate block and an
   // up block of W1
+  // They travel one step ahead with the row scales, into SA[BM + q] (q < NQB):
+  // lane q of each wave past the A rows fetches block q's scale of the step
+  // (SwiGLU: q = 0 gate, 1 up; otherwise column block n0 / 128 + q). Read at
+  // the step itself, a global load would make the wait for it also wait for
+  // the next step's prefetch (loads complete in issue order).
+  constexpr int NQB = (FP8 && !MX && !TOKSCALE) ? (EPI == EPI_SWIGLU ? 2 : (BN + 127) / 128) : 0;
+  static_assert(NQB <= 2 && (NQB == 0 || NTH >= BM + 64), "a wave past the A rows fetches the B scales");
   const float* __restrict__ sb_base = nullptr;
-  int sb_blk0 = 0, sb_blk1 = 0;
-  if constexpr (FP8 && !MX && !TOKSCALE) {
+  int64_t sb_end = 0;
+  uint32_t sb_off = 0, sb_step = 0;  // byte offset of this lane's scale at step 0, and per step
+  if constexpr (NQB > 0) {
     sb_base = g.b_scale + int64_t(grp) * g.b_scale_gstride;
-    if (EPI == EPI_SWIGLU) {
-      sb_blk0 = (nt * (BN / 2)) / 128;
-      sb_blk1 = (g.f + nt * (BN / 2)) / 128;
-    } else {
-      // a wave's WTN (<= 128) columns lie in one 128-column block
-      sb_blk0 = sb_blk1 = (n0 + wn * WTN) / 128;
-    }
+    sb_end = g.b_scale_gstride * 4;
+    const int q = min(lane, NQB - 1);
+    const int blk = (EPI == EPI_SWIGLU) ? ((q == 0 ? 0 : g.f) + nt * (BN / 2)) / 128 : n0 / 128 + q;
+    sb_off = uint32_t((B_KMAJ ? blk * g.b_scale_ld : blk) * 4);
+    sb_step = uint32_t((B_KMAJ ? 1 : g.b_scale_ld) * 4);
   }
 
   // MXFP8: E8M0 bytes of B (b_scale bytes; group stride b_scale_gstride
@@ -732,14 +738,23 @@ void gemm_kernel(GemmArgs g) {
       dma4(rsrc_words(ts_run + (live ? int64_t(kb0 + s) * ts_ld : 0), live ? 256 : 0), &st.SA[wave * 64],
            uint32_t(lane * 4));
     } else if constexpr (FP8 && !MX && NS > 2) {
-      // deep pipelines: the row scales land in LDS by DMA like the tiles;
-      // wave w gathers rows 64 w .. 64 w + 63 (rows past the group read 0)
-      dma4(rsrc_words(sa_base, live ? sa_end : 0), &st.SA[wave * 64],
-           uint32_t(((wave * 64 + lane) * g.a_scale_ld + s) * 4));
+      // deep pipelines: the scales land in LDS by DMA like the tiles; wave
+      // w < BM / 64 gathers rows 64 w .. 64 w + 63 (rows past the group read
+      // 0), the waves past them the B scales
+      if (wave < BM / 64)
+        dma4(rsrc_words(sa_base, live ? sa_end : 0), &st.SA[wave * 64],
+             uint32_t(((wave * 64 + lane) * g.a_scale_ld + s) * 4));
+      else
+        dma4(rsrc_words(sb_base, live ? sb_end : 0), &st.SA[wave * 64], sb_off + uint32_t(s) * sb_step);
     } else if constexpr (FP8) {
-      const rsrc_t sr = make_rsrc(sa_base, live ? sa_end : 0);
-      rs = __builtin_bit_cast(
-          float, __builtin_amdgcn_raw_buffer_load_b32(sr, uint32_t((tid * g.a_scale_ld + s * (BK / 128)) * 4), 0, 0));
+      if (wave < BM / 64) {
+        const rsrc_t sr = make_rsrc(sa_base, live ? sa_end : 0);
+        rs = __builtin_bit_cast(
+            float, __builtin_amdgcn_raw_buffer_load_b32(sr, uint32_t((tid * g.a_scale_ld + s * (BK / 128)) * 4), 0, 0));
+      } else {
+        const rsrc_t sr = make_rsrc(sb_base, live ? sb_end : 0);
+        rs = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(sr, sb_off + uint32_t(s) * sb_step, 0, 0));
+      }
     }
     if constexpr (MX) {
       if (tid < BN) {
@@ -835,14 +850,11 @@ void gemm_kernel(GemmArgs g) {
   // one K step (K block s) on stage st
   auto compute = [&](const ST& st, int s) {
     float sb0 = 0.0f, sb1 = 0.0f;
-    if constexpr (FP8 && !MX && !TOKSCALE) {
-      const int kb = min(s, nk - 1);  // BK == 128: one scale block per step
-      if (B_KMAJ) {
-        sb0 = sb_base[int64_t(sb_blk0) * g.b_scale_ld + kb];
-        sb1 = sb_base[int64_t(sb_blk1) * g.b_scale_ld + kb];
-      } else {
-        sb0 = sb1 = sb_base[int64_t(kb) * g.b_scale_ld + sb_blk0];
-      }
+    if constexpr (NQB > 0) {
+      // BK == 128: one scale block per step (a wave's WTN <= 128 columns
+      // lie in one 128-column block)
+      sb0 = st.SA[BM + (EPI == EPI_SWIGLU ? 0 : (wn * WTN) / 128)];
+      sb1 = st.SA[BM + (EPI == EPI_SWIGLU ? 1 : (wn * WTN) / 128)];
     }
     if constexpr (MX) {
       // one 128-deep block per step; the matrix core applies the E8M0 byte
