@@ -160,6 +160,7 @@ struct GemmArgs {
   // a_scale_ld = M, b_scale_ld = N) hold one scale per block and column, and
   // kblk[g] is the first block of group g (kblk[G] = NB)
   const int32_t* kblk;
+  int tpw;                   // FP8 weight gradients: column tiles per workgroup
   int ksuper;                // tiles per XCD super-block (set by run_gemm)
 };
 
@@ -328,6 +329,8 @@ __device__ __forceinline__ void dma4(u32x4 rsrc, void* dst, uint32_t voff) {
 }
 // s_waitcnt vmcnt(0) (expcnt and lgkmcnt left at their maxima)
 __device__ __forceinline__ void wait_vm0() { __builtin_amdgcn_s_waitcnt(0x0f70); }
+// the s_waitcnt immediate for vmcnt(n), n < 64
+constexpr int vm_wait(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
 
 // Operand tiles in LDS, by layout mode:
 //   LM_KDMA  K-major source, DMA straight from global memory into ROWS rows of
@@ -512,6 +515,21 @@ void gemm_kernel(GemmArgs g) {
     mrows = min(BM, g.offsets[grp + 1] - row0);
     kbase = 0;
     kcount = g.K;
+  } else if constexpr (TOKSCALE) {
+    // a run of up to tpw consecutive column tiles of one (group, row block);
+    // row blocks fastest, so that a super-block of workgroups shares its
+    // B column panel
+    const int nch = (g.tiles_n + g.tpw - 1) / g.tpw;
+    const int per = g.tiles_m * nch;
+    grp = tile / per;
+    if (grp >= g.G) return;  // padding of the grid
+    const int rem = tile % per;
+    mt = rem % g.tiles_m;
+    nt = (rem / g.tiles_m) * g.tpw;
+    row0 = 0;
+    mrows = BM;
+    kbase = g.offsets[grp];
+    kcount = g.offsets[grp + 1] - kbase;
   } else {
     const int per = g.tiles_m * g.tiles_n;
     grp = tile / per;
@@ -954,33 +972,97 @@ void gemm_kernel(GemmArgs g) {
   // issued at step s, and the barrier that ends step s waits only for step
   // s + 1 to land, so NS - 1 steps of loads are in flight.
   if constexpr (TOKSCALE) {
-    // FP8 weight gradients: a few K steps per tile, so the loads of steps 0
-    // and 1 go out together; later steps are issued into a stage as soon as
-    // every wave is done with it, one step ahead (all DMA: NDMA instructions
-    // per wave and step, tiles and scales)
-    static_assert(NS == 2, "two stages");
+    // FP8 weight gradients. The workgroup runs ntl column tiles of one
+    // (group, row block), nk K steps each (a few: the group's rows), as one
+    // sequence of Q = ntl * nk steps over the two stages: the loads of step
+    // q + 2 go out as soon as every wave is done with step q's stage, across
+    // tile boundaries, so that the next tile's loads are in flight while a
+    // tile's last step runs and its results are stored. All loads are DMA
+    // (NDMA instructions per wave and step: tiles and scales); a tile's
+    // results go through a staging region of their own, after the next
+    // loads have been issued. Loads and stores complete in issue order, so
+    // the wait for a step's loads counts the stores issued after them.
+    static_assert(NS == 2 && EPI == EPI_STORE && sizeof(TC) == 2, "two stages, plain bf16 stores");
     constexpr int NDMA = PA::NB + PB::NB + 1;
-    constexpr int WAIT1 = (NDMA & 15) | ((NDMA >> 4) << 14) | (7 << 4) | (15 << 8);
-    if (nk > 0) {
-      issue(st0, 0);
-      issue(st1, 1);
-      __builtin_amdgcn_s_waitcnt(WAIT1);  // step 0 landed, step 1 may be in flight
-      __syncthreads();
-      for (int s = 0; s < nk; s += 2) {
-        compute(st0, s);
-        __syncthreads();
-        issue(st0, s + 2);
-        __builtin_amdgcn_s_waitcnt(WAIT1);  // step s + 1 landed
-        __syncthreads();
-        if (s + 1 < nk) compute(st1, s + 1);
-        __syncthreads();
-        issue(st1, s + 3);
-        __builtin_amdgcn_s_waitcnt(WAIT1);  // step s + 2 landed
-        __syncthreads();
+    constexpr int EPB = WTN + 8;  // bf16 per staged row (16-byte pad: no bank conflicts)
+    constexpr int UPR = WTN / 8;  // 8-column units per staged row
+    static_assert(16 * UPR % 64 == 0, "whole store rounds per lane");
+    constexpr int EPT = FM * (16 * UPR / 64);  // store instructions per lane and tile
+    static_assert(NDMA + 2 * EPT < 64, "vmcnt range");
+    __shared__ __attribute__((aligned(16))) bf16_t stg_all[NTH / 64 * 16 * EPB];
+    const int ntl = min(g.tpw, g.tiles_n - nt);
+    const int Q = ntl * nk;
+    auto issue_t = [&](ST& st, int q) {
+      const int j = q / nk, s = q - j * nk;
+      const int64_t jb = int64_t(j) * BN * ES;  // column tile j of the run
+      const u32x4 ar = rsrc_words(a_base + int64_t(s) * a_step, a_end - int64_t(s) * a_step);
+#pragma unroll
+      for (int b = 0; b < PA::NB; ++b) dma16(ar, &st.A[(b * PA::NW + wave) * (1024 / ES)], pa.voff[b]);
+      const u32x4 br = rsrc_words(b_base + int64_t(s) * b_step + jb, b_end - int64_t(s) * b_step - jb);
+#pragma unroll
+      for (int b = 0; b < PB::NB; ++b) dma16(br, &st.B[(b * PB::NW + wave) * (1024 / ES)], pb.voff[b]);
+      const int64_t so = int64_t(kb0 + s) * ts_ld + (wave * 64 < BM ? 0 : int64_t(j) * BN);
+      dma4(rsrc_words(ts_run + so, 256), &st.SA[wave * 64], uint32_t(lane * 4));
+    };
+    TC* Cb = reinterpret_cast<TC*>(g.C) + int64_t(grp) * g.c_gstride;
+    // A lane holds rows 4 (lane / 16) + r, column lane % 16 of each 16 x 16
+    // block. Each wave rounds a 16-row block to bf16 into its own staging
+    // region and reads it back as 8 consecutive columns per lane, for
+    // 16-byte stores; a wave's LDS accesses complete in order, so it needs
+    // no barrier. Every lane takes part in every access (no lane-dependent
+    // branches around them).
+    auto store_tile = [&](int j) {
+      bf16_t* stg = stg_all + wave * 16 * EPB;
+      const int n0j = n0 + j * BN;
+#pragma unroll
+      for (int i = 0; i < FM; ++i) {
+#pragma unroll
+        for (int jj = 0; jj < FN; ++jj)
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            stg[(4 * (lane / 16) + r) * EPB + jj * 16 + lane % 16] = f32_to_bf16(acc[i][jj][r]);
+#pragma unroll
+        for (int t = 0; t < 16 * UPR / 64; ++t) {
+          const int u = lane + 64 * t;
+          const int rr = u / UPR, c8 = u % UPR;
+          const uint4 w = *reinterpret_cast<const uint4*>(&stg[rr * EPB + c8 * 8]);
+          const int64_t row = m0 + wm * WTM + i * 16 + rr;
+          // written once, never read here: streaming stores keep them from
+          // displacing the operands in L2
+          st_stream(Cb + row * g.ldc + n0j + wn * WTN + c8 * 8, w);
+        }
+#pragma unroll
+        for (int jj = 0; jj < FN; ++jj) acc[i][jj] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
       }
-      wait_vm0();  // the last prefetches (zeros) before the epilogue reuses the LDS
-      __syncthreads();
+    };
+    if (Q == 0) {  // no rows: zero gradients
+      for (int j = 0; j < ntl; ++j) store_tile(j);
+      return;
     }
+    issue_t(st0, 0);
+    if (Q > 1) issue_t(st1, 1);
+    for (int q = 0; q < Q; ++q) {
+      ST& cur = (q & 1) ? st1 : st0;
+      // issued after step q's loads: the stores of the tile step q - 2 ended
+      // (if it ended one), step q + 1's loads (if any) and the stores of the
+      // tile step q - 1 ended
+      const int nst = int(q >= 2 && (q - 1) % nk == 0) + int(q >= 1 && q % nk == 0);
+      if (q + 1 < Q) {
+        if (nst == 0) __builtin_amdgcn_s_waitcnt(vm_wait(NDMA));
+        else if (nst == 1) __builtin_amdgcn_s_waitcnt(vm_wait(NDMA + EPT));
+        else __builtin_amdgcn_s_waitcnt(vm_wait(NDMA + 2 * EPT));
+      } else {
+        if (nst == 0) wait_vm0();
+        else if (nst == 1) __builtin_amdgcn_s_waitcnt(vm_wait(EPT));
+        else __builtin_amdgcn_s_waitcnt(vm_wait(2 * EPT));
+      }
+      __syncthreads();
+      compute(cur, 0);
+      __syncthreads();
+      if (q + 2 < Q) issue_t(cur, q + 2);
+      if ((q + 1) % nk == 0) store_tile(q / nk);
+    }
+    return;
   } else if constexpr (NS == 2) {
     if (nk > 0) {
       const int nk2 = (nk + 1) & ~1;
@@ -1484,8 +1566,10 @@ typedef Cfg<bf16_t, 256, 256, 64, 2, 4, 2> BigCfg;
 // FP8 / MXFP8 256 x 256 tile: 8 waves of 128 x 64, BK 128, two 64 KB stages
 // (one workgroup per CU), the byte layout of the bf16 Big tile
 template <typename T> using BigCfg8 = Cfg<T, 256, 256, 128, 2, 4, 2>;
-// FP8 weight gradients: 128 x 128, 4 waves of 64 x 64, BK 128, two stages
+// FP8 weight gradients: 128 x 128, 4 waves of 64 x 64, BK 128, two stages;
+// a workgroup runs up to kWgradRun column tiles of one row block
 typedef Cfg<fp8_t, 128, 128, 128, 2, 2, 2> WgradCfg8;
+constexpr int kWgradRun = 8;
 typedef Cfg<bf16_t, 128, 256, 32, 2, 2, 3> WgradCfg;
 
 static int rows_tile_bound(int64_t A, int64_t G, int BM) {
@@ -1496,7 +1580,7 @@ static int rows_tile_bound(int64_t A, int64_t G, int BM) {
 template <typename C, typename TC, bool AK, bool BKm, int MODE, int EPI>
 static void run_gemm(GemmArgs g, int tiles, hipStream_t st) {
   if (tiles <= 0) return;
-  if (MODE == G_KSPLIT) g.ksuper = super_wgrad(g.tiles_m * g.tiles_n);
+  if (MODE == G_KSPLIT) g.ksuper = super_wgrad(g.tiles_m * (g.tpw > 0 ? (g.tiles_n + g.tpw - 1) / g.tpw : g.tiles_n));
   else g.ksuper = super_rows(tiles / (g.G > 0 ? g.G : 1), C::BM);
   gemm_kernel<typename C::type, TC, AK, BKm, MODE, EPI, C::BM, C::BN, C::BK, C::WM, C::WN, C::NS>
       <<<padded_grid(tiles, g.ksuper), C::WM * C::WN * 64, 0, st>>>(g);
@@ -1756,7 +1840,11 @@ static void wgrad_fp8(int tile, const fp8_t* dq, const float* ds, const fp8_t* h
   typedef WgradCfg8 C;
   (void)tile;
   auto run = [&](GemmArgs& gg) {
-    run_gemm<C, bf16_t, false, false, G_KSPLIT, EPI_STORE>(gg, int(E) * gg.tiles_m * gg.tiles_n, st);
+    // runs of column tiles while the grid keeps at least 8 workgroups per CU
+    const int64_t tiles = E * gg.tiles_m * gg.tiles_n;
+    gg.tpw = int(std::max<int64_t>(1, std::min<int64_t>(kWgradRun, tiles / 2048)));
+    run_gemm<C, bf16_t, false, false, G_KSPLIT, EPI_STORE>(
+        gg, int(E) * gg.tiles_m * ((gg.tiles_n + gg.tpw - 1) / gg.tpw), st);
   };
   GemmArgs g3{};
   g3.A = dq; g3.lda = d; g3.a_scale = ds; g3.a_scale_ld = int(d);
