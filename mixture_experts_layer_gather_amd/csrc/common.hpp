@@ -26,6 +26,55 @@ __device__ __forceinline__ bf16_t f32_to_bf16(float f) {
   return __builtin_bit_cast(bf16_t, b);
 }
 
+// E4M3 encoding of block-scaled values: codes of the quotients v / s,
+// rounded to nearest even by v_cvt_pk_fp8_f32, 8 values to two words.
+// Each quotient is v·r corrected once by its residual v − s·(v·r), which one
+// FMA gives exactly, with r the correctly rounded 1/s: that is the correctly
+// rounded quotient wherever it is a normal number (Markstein's theorem), and
+// where it underflows a value with the same E4M3 code (±0, v's sign). So the
+// codes are those of the exact division, at a multiply and two FMAs per value
+// instead of a division (checked against the division's codes for every fp32
+// v with |v| <= 448 s, for scales across the fp32 range; the test
+// fp8_quotient_check.c repeats it for six). Scales outside [2^-125, 2^125],
+// where r or the residual leaves the normal range, divide outright.
+__device__ __forceinline__ bool fp8_fast_scale(float s) { return s >= 0x1p-125f && s <= 0x1p125f; }
+__device__ __forceinline__ float fp8_quot(float v, float s, float r) {
+  const float y = v * r;
+  return __builtin_copysignf(__builtin_fmaf(__builtin_fmaf(-s, y, v), r, y), v);
+}
+__device__ __forceinline__ u32x2 fp8_pack8(const float* q) {
+  uint32_t lo = 0, hi = 0;
+  lo = __builtin_amdgcn_cvt_pk_fp8_f32(q[0], q[1], lo, false);
+  lo = __builtin_amdgcn_cvt_pk_fp8_f32(q[2], q[3], lo, true);
+  hi = __builtin_amdgcn_cvt_pk_fp8_f32(q[4], q[5], hi, false);
+  hi = __builtin_amdgcn_cvt_pk_fp8_f32(q[6], q[7], hi, true);
+  return u32x2{lo, hi};
+}
+// one scale s for the 8 values (r = 1/s, fast = fp8_fast_scale(s))
+__device__ __forceinline__ u32x2 fp8_encode8(const float* v, float s, float r, bool fast) {
+  float q[8];
+  if (fast) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) q[e] = fp8_quot(v[e], s, r);
+  } else {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) q[e] = v[e] / s;
+  }
+  return fp8_pack8(q);
+}
+// a scale per value (fast: every s[e] passes fp8_fast_scale)
+__device__ __forceinline__ u32x2 fp8_encode8(const float* v, const float* s, const float* r, bool fast) {
+  float q[8];
+  if (fast) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) q[e] = fp8_quot(v[e], s[e], r[e]);
+  } else {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) q[e] = v[e] / s[e];
+  }
+  return fp8_pack8(q);
+}
+
 // MXFP8 shared exponent of a block of 32 elements with largest magnitude
 // amax (>= 0): the smallest x in [-127, 127] with amax * 2^-x <= 448, 0 for
 // amax = 0. With amax = 1.m * 2^(E-127): x = E - 134 when the mantissa

@@ -245,11 +245,8 @@ __global__ __launch_bounds__(256) void dispatch_gather_fp8_kernel(
     for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(v[i]));
     for (int o = 8; o >= 1; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o, kWave));
     const float scale = (amax == 0.0f) ? 1.0f : amax / 448.0f;
-    uint32_t lo = 0, hi = 0;
-    lo = __builtin_amdgcn_cvt_pk_fp8_f32(v[0] / scale, v[1] / scale, lo, false);
-    lo = __builtin_amdgcn_cvt_pk_fp8_f32(v[2] / scale, v[3] / scale, lo, true);
-    hi = __builtin_amdgcn_cvt_pk_fp8_f32(v[4] / scale, v[5] / scale, hi, false);
-    hi = __builtin_amdgcn_cvt_pk_fp8_f32(v[6] / scale, v[7] / scale, hi, true);
+    const u32x2 w = fp8_encode8(v, scale, 1.0f / scale, fp8_fast_scale(scale));
+    const uint32_t lo = w[0], hi = w[1];
     if (ok) {
       const int blk = ch / 16;
       _Pragma("unroll") for (int j = 0; j < 16; ++j) if (j < k) {
@@ -540,14 +537,12 @@ __global__ __launch_bounds__(256) void quant_tiles128_kernel(const T* __restrict
   amax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
   const float s = (amax == 0.0f) ? 1.0f : amax / 448.0f;
   if (threadIdx.x == 0) scale[I * nbc + J] = s;
+  const float r = 1.0f / s;
+  const bool fast = fp8_fast_scale(s);
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
-    uint32_t lo = 0, hi = 0;
-    lo = __builtin_amdgcn_cvt_pk_fp8_f32(v[i][0] / s, v[i][1] / s, lo, false);
-    lo = __builtin_amdgcn_cvt_pk_fp8_f32(v[i][2] / s, v[i][3] / s, lo, true);
-    hi = __builtin_amdgcn_cvt_pk_fp8_f32(v[i][4] / s, v[i][5] / s, hi, false);
-    hi = __builtin_amdgcn_cvt_pk_fp8_f32(v[i][6] / s, v[i][7] / s, hi, true);
-    *reinterpret_cast<uint2*>(dst + base + int64_t(16 * i) * cols) = make_uint2(lo, hi);
+    const u32x2 w = fp8_encode8(v[i], s, r, fast);
+    *reinterpret_cast<uint2*>(dst + base + int64_t(16 * i) * cols) = make_uint2(w[0], w[1]);
   }
 }
 

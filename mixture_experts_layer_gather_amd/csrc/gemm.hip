@@ -1225,13 +1225,9 @@ __global__ __launch_bounds__(256) void quant_rows_kernel(const TS* __restrict__ 
   for (int i = 0; i < V; ++i) amax = fmaxf(amax, fabsf(v[i]));
   for (int o = 8; o >= 1; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o, kWave));
   const float s = (amax == 0.0f) ? 1.0f : amax / 448.0f;
-  uint32_t lo = 0, hi = 0;
-  lo = __builtin_amdgcn_cvt_pk_fp8_f32(v[0] / s, v[1] / s, lo, false);
-  lo = __builtin_amdgcn_cvt_pk_fp8_f32(v[2] / s, v[3] / s, lo, true);
-  hi = __builtin_amdgcn_cvt_pk_fp8_f32(v[4] / s, v[5] / s, hi, false);
-  hi = __builtin_amdgcn_cvt_pk_fp8_f32(v[6] / s, v[7] / s, hi, true);
+  const u32x2 w = fp8_encode8(v, s, 1.0f / s, fp8_fast_scale(s));
   if (ok) {
-    *reinterpret_cast<u32x2*>(q + ch * V) = u32x2{lo, hi};
+    *reinterpret_cast<u32x2*>(q + ch * V) = w;
     if ((ch & 15) == 0) scale[ch / 16] = s;  // rows are whole 128-blocks
   }
 }
@@ -1479,24 +1475,22 @@ __global__ __launch_bounds__(256) void quant_tokens_kernel(const void* __restric
       for (int o = 8; o >= 1; o >>= 1) a = fmaxf(a, __shfl_xor(a, o, kWave));
       const float sr = (a == 0.0f) ? 1.0f : a / 448.0f;
       if (rr < nrows) {
-        uint32_t w0 = 0, w1 = 0;
-        w0 = __builtin_amdgcn_cvt_pk_fp8_f32(v[i][0] / sr, v[i][1] / sr, w0, false);
-        w0 = __builtin_amdgcn_cvt_pk_fp8_f32(v[i][2] / sr, v[i][3] / sr, w0, true);
-        w1 = __builtin_amdgcn_cvt_pk_fp8_f32(v[i][4] / sr, v[i][5] / sr, w1, false);
-        w1 = __builtin_amdgcn_cvt_pk_fp8_f32(v[i][6] / sr, v[i][7] / sr, w1, true);
-        *reinterpret_cast<u32x2*>(rq + (r0 + rr) * C + c0) = u32x2{w0, w1};
+        *reinterpret_cast<u32x2*>(rq + (r0 + rr) * C + c0) = fp8_encode8(v[i], sr, 1.0f / sr, fp8_fast_scale(sr));
         if (cg == 0) rs[(r0 + rr) * (C / 128) + c0 / 128] = sr;
       }
     }
   }
   __syncthreads();
-  float sc[8];
+  float sc[8], rc[8];
+  bool fast = true;
 #pragma unroll
   for (int c = 0; c < 8; ++c) {
     float a = 0.0f;
 #pragma unroll
     for (int r = 0; r < 16; ++r) a = fmaxf(a, s_max[r][cg * 8 + c]);
     sc[c] = (a == 0.0f) ? 1.0f : a / 448.0f;
+    rc[c] = 1.0f / sc[c];
+    fast = fast && fp8_fast_scale(sc[c]);
   }
   if (rg == 0) {
     float* sp = scale + int64_t(b) * C + c0;
@@ -1506,14 +1500,7 @@ __global__ __launch_bounds__(256) void quant_tokens_kernel(const void* __restric
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     const int rr = rg + 16 * i;
-    if (rr < nrows) {
-      uint32_t w0 = 0, w1 = 0;
-      w0 = __builtin_amdgcn_cvt_pk_fp8_f32(v[i][0] / sc[0], v[i][1] / sc[1], w0, false);
-      w0 = __builtin_amdgcn_cvt_pk_fp8_f32(v[i][2] / sc[2], v[i][3] / sc[3], w0, true);
-      w1 = __builtin_amdgcn_cvt_pk_fp8_f32(v[i][4] / sc[4], v[i][5] / sc[5], w1, false);
-      w1 = __builtin_amdgcn_cvt_pk_fp8_f32(v[i][6] / sc[6], v[i][7] / sc[7], w1, true);
-      *reinterpret_cast<u32x2*>(q + (r0 + rr) * C + c0) = u32x2{w0, w1};
-    }
+    if (rr < nrows) *reinterpret_cast<u32x2*>(q + (r0 + rr) * C + c0) = fp8_encode8(v[i], sc, rc, fast);
   }
 }
 
