@@ -460,6 +460,16 @@ struct alignas(16) StageMx {
   uint32_t SB[BN];
 };
 
+// The weight-gradient instances that run persistent runs of column tiles:
+// FP8 operands (token-block scales), bf16 results. (bf16 operands on the
+// 128 x 128 tile were measured the same way and lost to the 128 x 256
+// three-stage tile on every bf16 layer but one product: Qwen3-style dW1
+// 0.95 -> 2.17 ms, Mixtral-style 2.15 -> 2.55 ms.)
+template <typename T, typename TC, int MODE, int EPI, int NS>
+constexpr bool persistent_wgrad() {
+  return MODE == G_KSPLIT && EPI == EPI_STORE && NS == 2 && sizeof(TC) == 2 && std::is_same<T, fp8_t>::value;
+}
+
 template <typename T, typename TC, bool A_KMAJ, bool B_KMAJ, int MODE, int EPI, int BM, int BN,
           int BK, int WM, int WN, int NS>
 __global__ __launch_bounds__(WM * WN * 64) __attribute__((amdgpu_waves_per_eu(2)))
@@ -478,6 +488,9 @@ void gemm_kernel(GemmArgs g) {
   constexpr int ALM = layout_mode<T, A_KMAJ>(), BLM = layout_mode<T, B_KMAJ>();
   using PA = OperandPlan<T, ALM, BM, BK, NTH>;
   using PB = OperandPlan<T, BLM, BN, BK, NTH>;
+  // weight gradients as runs of column tiles per workgroup (FP8)
+  constexpr bool PERSIST = persistent_wgrad<T, TC, MODE, EPI, NS>();
+  static_assert(!PERSIST || (PA::DMA && PB::DMA), "persistent weight gradients load by DMA");
   static_assert(WM * WN == 4 || WM * WN == 8, "four or eight waves");
   static_assert(EPI != EPI_SWIGLU || FN % 2 == 0, "SwiGLU pairs column fragments");
   static_assert(!FP8 || (MODE == G_ROWS && A_KMAJ && BK == 128 && BN <= 256 && BM <= 256) ||
@@ -515,17 +528,18 @@ void gemm_kernel(GemmArgs g) {
     mrows = min(BM, g.offsets[grp + 1] - row0);
     kbase = 0;
     kcount = g.K;
-  } else if constexpr (TOKSCALE) {
+  } else if constexpr (PERSIST) {
     // a run of up to tpw consecutive column tiles of one (group, row block);
     // row blocks fastest, so that a super-block of workgroups shares its
     // B column panel
-    const int nch = (g.tiles_n + g.tpw - 1) / g.tpw;
+    const int tpw = max(g.tpw, 1);
+    const int nch = (g.tiles_n + tpw - 1) / tpw;
     const int per = g.tiles_m * nch;
     grp = tile / per;
     if (grp >= g.G) return;  // padding of the grid
     const int rem = tile % per;
     mt = rem % g.tiles_m;
-    nt = (rem / g.tiles_m) * g.tpw;
+    nt = (rem / g.tiles_m) * tpw;
     row0 = 0;
     mrows = BM;
     kbase = g.offsets[grp];
@@ -971,26 +985,26 @@ void gemm_kernel(GemmArgs g) {
   // NS > 2 stages (DMA operands only): the loads of step s + NS - 1 are
   // issued at step s, and the barrier that ends step s waits only for step
   // s + 1 to land, so NS - 1 steps of loads are in flight.
-  if constexpr (TOKSCALE) {
-    // FP8 weight gradients. The workgroup runs ntl column tiles of one
+  if constexpr (PERSIST) {
+    // Weight gradients. The workgroup runs ntl column tiles of one
     // (group, row block), nk K steps each (a few: the group's rows), as one
     // sequence of Q = ntl * nk steps over the two stages: the loads of step
     // q + 2 go out as soon as every wave is done with step q's stage, across
     // tile boundaries, so that the next tile's loads are in flight while a
     // tile's last step runs and its results are stored. All loads are DMA
-    // (NDMA instructions per wave and step: tiles and scales); a tile's
+    // (NDMA instructions per wave and step: tiles, and FP8 scales); a tile's
     // results go through a staging region of their own, after the next
     // loads have been issued. Loads and stores complete in issue order, so
     // the wait for a step's loads counts the stores issued after them.
     static_assert(NS == 2 && EPI == EPI_STORE && sizeof(TC) == 2, "two stages, plain bf16 stores");
-    constexpr int NDMA = PA::NB + PB::NB + 1;
+    constexpr int NDMA = PA::NB + PB::NB + (TOKSCALE ? 1 : 0);
     constexpr int EPB = WTN + 8;  // bf16 per staged row (16-byte pad: no bank conflicts)
     constexpr int UPR = WTN / 8;  // 8-column units per staged row
     static_assert(16 * UPR % 64 == 0, "whole store rounds per lane");
     constexpr int EPT = FM * (16 * UPR / 64);  // store instructions per lane and tile
     static_assert(NDMA + 2 * EPT < 64, "vmcnt range");
     __shared__ __attribute__((aligned(16))) bf16_t stg_all[NTH / 64 * 16 * EPB];
-    const int ntl = min(g.tpw, g.tiles_n - nt);
+    const int ntl = min(max(g.tpw, 1), g.tiles_n - nt);
     const int Q = ntl * nk;
     auto issue_t = [&](ST& st, int q) {
       const int j = q / nk, s = q - j * nk;
@@ -1001,8 +1015,10 @@ void gemm_kernel(GemmArgs g) {
       const u32x4 br = rsrc_words(b_base + int64_t(s) * b_step + jb, b_end - int64_t(s) * b_step - jb);
 #pragma unroll
       for (int b = 0; b < PB::NB; ++b) dma16(br, &st.B[(b * PB::NW + wave) * (1024 / ES)], pb.voff[b]);
-      const int64_t so = int64_t(kb0 + s) * ts_ld + (wave * 64 < BM ? 0 : int64_t(j) * BN);
-      dma4(rsrc_words(ts_run + so, 256), &st.SA[wave * 64], uint32_t(lane * 4));
+      if constexpr (TOKSCALE) {
+        const int64_t so = int64_t(kb0 + s) * ts_ld + (wave * 64 < BM ? 0 : int64_t(j) * BN);
+        dma4(rsrc_words(ts_run + so, 256), &st.SA[wave * 64], uint32_t(lane * 4));
+      }
     };
     TC* Cb = reinterpret_cast<TC*>(g.C) + int64_t(grp) * g.c_gstride;
     // A lane holds rows 4 (lane / 16) + r, column lane % 16 of each 16 x 16
@@ -1797,6 +1813,14 @@ static void ffn_fwd_gu_h(const FfnLaunch& a, void* gu, void* h, float* hs, bf16_
 template <typename C, typename TW>
 static void wgrad_t(const void* d_out, const void* act_h, const void* d_gu, const void* x, void* dw1,
                     void* dw2, const int32_t* offsets, int64_t d, int64_t f, int64_t E, hipStream_t st) {
+  constexpr bool persist = persistent_wgrad<typename C::type, TW, G_KSPLIT, EPI_STORE, C::NS>();
+  // persistent instances: runs of column tiles while the grid keeps at least
+  // 8 workgroups per CU
+  auto grid = [&](GemmArgs& gg) {
+    if (!persist) return int(E) * gg.tiles_m * gg.tiles_n;
+    gg.tpw = int(std::max<int64_t>(1, std::min<int64_t>(kWgradRun, E * gg.tiles_m * gg.tiles_n / 2048)));
+    return int(E) * gg.tiles_m * ((gg.tiles_n + gg.tpw - 1) / gg.tpw);
+  };
   // dW2 = dO^T H   [d, f]
   GemmArgs g3{};
   g3.A = d_out; g3.lda = d;
@@ -1805,7 +1829,8 @@ static void wgrad_t(const void* d_out, const void* act_h, const void* d_gu, cons
   g3.offsets = offsets; g3.G = int(E);
   g3.M = int(d); g3.N = int(f);
   g3.tiles_m = int(d / C::BM); g3.tiles_n = int(f / C::BN);
-  run_gemm<C, TW, false, false, G_KSPLIT, EPI_STORE>(g3, int(E) * g3.tiles_m * g3.tiles_n, st);
+  const int n3 = grid(g3);  // sets g3.tpw before the copy run_gemm takes
+  run_gemm<C, TW, false, false, G_KSPLIT, EPI_STORE>(g3, n3, st);
   // dW1 = dGU^T X   [2f, d]
   GemmArgs g4{};
   g4.A = d_gu; g4.lda = 2 * f;
@@ -1814,7 +1839,8 @@ static void wgrad_t(const void* d_out, const void* act_h, const void* d_gu, cons
   g4.offsets = offsets; g4.G = int(E);
   g4.M = int(2 * f); g4.N = int(d);
   g4.tiles_m = int(2 * f / C::BM); g4.tiles_n = int(d / C::BN);
-  run_gemm<C, TW, false, false, G_KSPLIT, EPI_STORE>(g4, int(E) * g4.tiles_m * g4.tiles_n, st);
+  const int n4 = grid(g4);
+  run_gemm<C, TW, false, false, G_KSPLIT, EPI_STORE>(g4, n4, st);
 }
 
 // FP8 weight gradients: dW2 = dO^T H and dW1 = dGU^T X with every operand
