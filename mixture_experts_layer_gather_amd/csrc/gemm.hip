@@ -766,10 +766,8 @@ void gemm_kernel(GemmArgs g) {
 #pragma unroll
       for (int i = 0; i < 4 * PB::NT; ++i) rb[i] = __builtin_amdgcn_raw_buffer_load_b128(br, pb.voff[i], 0, 0);
     }
-    if constexpr (TOKSCALE) {
-      dma4(rsrc_words(ts_run + (live ? int64_t(kb0 + s) * ts_ld : 0), live ? 256 : 0), &st.SA[wave * 64],
-           uint32_t(lane * 4));
-    } else if constexpr (FP8 && !MX && NS > 2) {
+    // (the FP8 weight gradients issue through their own loop's issue_t)
+    if constexpr (FP8 && !MX && !TOKSCALE && NS > 2) {
       // deep pipelines: the scales land in LDS by DMA like the tiles; wave
       // w < BM / 64 gathers rows 64 w .. 64 w + 63 (rows past the group read
       // 0), the waves past them the B scales
@@ -778,7 +776,7 @@ void gemm_kernel(GemmArgs g) {
              uint32_t(((wave * 64 + lane) * g.a_scale_ld + s) * 4));
       else
         dma4(rsrc_words(sb_base, live ? sb_end : 0), &st.SA[wave * 64], sb_off + uint32_t(s) * sb_step);
-    } else if constexpr (FP8) {
+    } else if constexpr (FP8 && !TOKSCALE) {
       if (wave < BM / 64) {
         const rsrc_t sr = make_rsrc(sa_base, live ? sa_end : 0);
         rs = __builtin_bit_cast(

@@ -134,6 +134,14 @@ SMALL = {
     # (d and 2f multiples of 256), ragged experts of 0 to a few hundred rows
     "deepseek_fp8_mini_big": S.mini(S.CONFIGS[4], T=600, d=512, f=256, E=16).replace(
         k=4, num_groups=4, topk_groups=2, seed_base=35),
+    # FP8 weight gradients in runs of two column tiles per workgroup (64
+    # experts x 8 x 9 tiles of dW1), the last run of each row block one tile
+    # short. Even routing: experts of one 128-row block, so each tile's only
+    # K step ends it and two tiles' stores sit between a load and its wait;
+    # skewed routing: experts of one block, of several, and with no rows
+    "deepseek_fp8_runs": S.mini(S.CONFIGS[4], T=1024, d=1152, f=512, E=64).replace(k=4, seed_base=36),
+    "deepseek_fp8_runs_skew": S.mini(S.CONFIGS[4], T=1024, d=1152, f=512, E=64).replace(
+        k=4, bias="zipf", seed_base=37),
     # the other group rule (a group's best score instead of its best two)
     # and sigmoid gates without renormalisation
     "deepseek_mini_gmax": S.mini(S.CONFIGS[2], T=300, d=256, f=256, E=32).replace(
