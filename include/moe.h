@@ -271,6 +271,17 @@ int moe_combine_bwd(const moe_config *cfg, const void *dy, const void *out_perm,
  * out: dx_perm [A,d] act; dw1 [E,2f,d], dw2 [E,d,f] in the parameter dtype
  * (f32 when wt is f32, else bf16), overwritten; an expert with no rows gets
  * exact zeros.
+ * Low precision (the Megatron Core MoE summary trains in FP8, Resumo tecnico
+ * section 2.2; the block rules are the library's reading): with
+ * MOE_DTYPE_FP8_E4M3 all four products take E4M3 operands with fp32 scales
+ * amax/448. The data-gradient products quantise dO and [dG dU] in 1 x 128
+ * blocks along d and 2f and use the forward's 128 x 128 weight blocks. The
+ * weight-gradient products quantise dO, H, [dG dU] and X in 128-row x 1
+ * blocks inside each expert's rows (the first block starts at the expert's
+ * first row, the last holds the rest), one scale per block and column; H and
+ * X enter as their dequantised forward values. With MOE_DTYPE_MXFP8 the
+ * data-gradient operands take 1 x 32 E8M0 blocks and the weight gradients run
+ * in bf16 on the dequantised X and H.
  * Recompute (Megatron Core MoE summary, section 2.2: activations that take
  * memory but are cheap to compute are recomputed in the backward instead of
  * stored):
