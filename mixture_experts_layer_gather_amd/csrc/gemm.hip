@@ -1054,26 +1054,18 @@ void gemm_kernel(GemmArgs g) {
       return;
     }
     issue_t(st0, 0);
-    if (Q > 1) issue_t(st1, 1);
     for (int q = 0; q < Q; ++q) {
       ST& cur = (q & 1) ? st1 : st0;
-      // issued after step q's loads: the stores of the tile step q - 2 ended
-      // (if it ended one), step q + 1's loads (if any) and the stores of the
-      // tile step q - 1 ended
-      const int nst = int(q >= 2 && (q - 1) % nk == 0) + int(q >= 1 && q % nk == 0);
-      if (q + 1 < Q) {
-        if (nst == 0) __builtin_amdgcn_s_waitcnt(vm_wait(NDMA));
-        else if (nst == 1) __builtin_amdgcn_s_waitcnt(vm_wait(NDMA + EPT));
-        else __builtin_amdgcn_s_waitcnt(vm_wait(NDMA + 2 * EPT));
-      } else {
-        if (nst == 0) wait_vm0();
-        else if (nst == 1) __builtin_amdgcn_s_waitcnt(vm_wait(EPT));
-        else __builtin_amdgcn_s_waitcnt(vm_wait(2 * EPT));
-      }
+      ST& nxt = (q & 1) ? st0 : st1;
+      // issued after step q's loads: the stores of the tile step q - 1 ended
+      // (if it ended one)
+      if (q >= 1 && q % nk == 0) __builtin_amdgcn_s_waitcnt(vm_wait(EPT));
+      else wait_vm0();
+      // every wave's loads of step q landed, and every wave is done with
+      // step q - 1's stage
       __syncthreads();
+      if (q + 1 < Q) issue_t(nxt, q + 1);
       compute(cur, 0);
-      __syncthreads();
-      if (q + 2 < Q) issue_t(cur, q + 2);
       if ((q + 1) % nk == 0) store_tile(q / nk);
     }
     return;
