@@ -1431,12 +1431,17 @@ __global__ __launch_bounds__(1024) void kblock_offsets_kernel(const int32_t* __r
 
 // One workgroup per (block, 128 columns): thread (cg, rg) holds columns
 // 8 cg .. 8 cg + 7 of rows rg, rg + 16, ..., rg + 112 of the block in
-// registers; the column maxima meet in LDS. Sources: bf16 rows (SRC_FP8 =
-// false) or E4M3 codes with fp32 scales per 1 x 128 block of a row, taken as
-// float(code) * scale in fp32. ROWQ (bf16 sources): the same read also
-// quantises each row's 128 columns as one 1 x 128 block (the data-gradient
-// products' operand), into rq / rs [A, C/128]: the tile's 16 threads of one
-// row reduce its amax with lane shuffles (they share a wave).
+// registers; the column maxima meet in LDS, where 128 threads turn them into
+// the column scales and their reciprocals once (a division each), for every
+// thread to read. Sources: bf16 rows (SRC_FP8 = false) or E4M3 codes with
+// fp32 scales per 1 x 128 block of a row, taken as float(code) * scale in
+// fp32. ROWQ (bf16 sources): the same read also quantises each row's 128
+// columns as one 1 x 128 block (the data-gradient products' operand), into
+// rq / rs [A, C/128]. The 16 threads holding rows rg + 16 i (one 16-lane
+// group of a wave) reduce their 8 row maxima by a transposing butterfly:
+// each exchange step halves the rows a lane keeps, so after four steps lane
+// cg holds the whole maximum of row cg / 2, divides once, and the row scales
+// go back to the group by lane broadcasts.
 template <bool SRC_FP8, bool ROWQ>
 __global__ __launch_bounds__(256) void quant_tokens_kernel(const void* __restrict__ src,
                                                            const float* __restrict__ src_scale,
@@ -1447,6 +1452,8 @@ __global__ __launch_bounds__(256) void quant_tokens_kernel(const void* __restric
                                                            float* __restrict__ rs) {
   static_assert(!(SRC_FP8 && ROWQ), "row blocks are taken from bf16 sources");
   __shared__ float s_max[16][129];
+  __shared__ float s_sc[128], s_rc[128];
+  __shared__ int s_fast[128];
   const int b = blockIdx.x;
   if (b >= kblk[G]) return;
   // the expert owning block b: the last e with kblk[e] <= b
@@ -1491,33 +1498,58 @@ __global__ __launch_bounds__(256) void quant_tokens_kernel(const void* __restric
 #pragma unroll
   for (int c = 0; c < 8; ++c) s_max[rg][cg * 8 + c] = m[c];
   if constexpr (ROWQ) {
-    // 1 x 128 row blocks: amax over the row's 16 threads (lanes 16 j .. 16 j + 15)
+    // 1 x 128 row blocks: this lane's part of the 8 row maxima
+    float x[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      x[i] = 0.0f;
+#pragma unroll
+      for (int c = 0; c < 8; ++c) x[i] = fmaxf(x[i], fabsf(v[i][c]));
+    }
+    // transposing butterfly over the 16 lanes of the row group: at the step
+    // over lane bit h, a lane keeps the half of its rows selected by that
+    // bit and takes its partner's values for them
+    const int b3 = (cg >> 3) & 1, b2 = (cg >> 2) & 1, b1 = (cg >> 1) & 1;
+    float y[4], z[2];
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      y[j] = fmaxf(b3 ? x[j + 4] : x[j], __shfl_xor(b3 ? x[j] : x[j + 4], 8, kWave));
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+      z[j] = fmaxf(b2 ? y[j + 2] : y[j], __shfl_xor(b2 ? y[j] : y[j + 2], 4, kWave));
+    float a = fmaxf(b1 ? z[1] : z[0], __shfl_xor(b1 ? z[0] : z[1], 2, kWave));
+    a = fmaxf(a, __shfl_xor(a, 1, kWave));  // the maximum of row 4 b3 + 2 b2 + b1 = cg / 2
+    const float sr_own = (a == 0.0f) ? 1.0f : a / 448.0f;
+    const float rr_own = 1.0f / sr_own;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       const int rr = rg + 16 * i;
-      float a = 0.0f;
-#pragma unroll
-      for (int c = 0; c < 8; ++c) a = fmaxf(a, fabsf(v[i][c]));
-#pragma unroll
-      for (int o = 8; o >= 1; o >>= 1) a = fmaxf(a, __shfl_xor(a, o, kWave));
-      const float sr = (a == 0.0f) ? 1.0f : a / 448.0f;
+      const float sr = __shfl(sr_own, 2 * i, 16), rsr = __shfl(rr_own, 2 * i, 16);
       if (rr < nrows) {
-        *reinterpret_cast<u32x2*>(rq + (r0 + rr) * C + c0) = fp8_encode8(v[i], sr, 1.0f / sr, fp8_fast_scale(sr));
+        *reinterpret_cast<u32x2*>(rq + (r0 + rr) * C + c0) = fp8_encode8(v[i], sr, rsr, fp8_fast_scale(sr));
         if (cg == 0) rs[(r0 + rr) * (C / 128) + c0 / 128] = sr;
       }
     }
+  }
+  __syncthreads();
+  if (threadIdx.x < 128) {  // waves 0 and 1: one column each
+    const int col = threadIdx.x;
+    float a = 0.0f;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) a = fmaxf(a, s_max[r][col]);
+    const float scol = (a == 0.0f) ? 1.0f : a / 448.0f;
+    s_sc[col] = scol;
+    s_rc[col] = 1.0f / scol;
+    s_fast[col] = fp8_fast_scale(scol) ? 1 : 0;
   }
   __syncthreads();
   float sc[8], rc[8];
   bool fast = true;
 #pragma unroll
   for (int c = 0; c < 8; ++c) {
-    float a = 0.0f;
-#pragma unroll
-    for (int r = 0; r < 16; ++r) a = fmaxf(a, s_max[r][cg * 8 + c]);
-    sc[c] = (a == 0.0f) ? 1.0f : a / 448.0f;
-    rc[c] = 1.0f / sc[c];
-    fast = fast && fp8_fast_scale(sc[c]);
+    sc[c] = s_sc[cg * 8 + c];
+    rc[c] = s_rc[cg * 8 + c];
+    fast = fast && s_fast[cg * 8 + c] != 0;
   }
   if (rg == 0) {
     float* sp = scale + int64_t(b) * C + c0;
