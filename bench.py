@@ -565,8 +565,10 @@ def run_config(cfg, args, dev, flush, copy_gbps):
 
 def vendor_gemm(name):
     """Context for the grouped GEMM's roofline: the vendor library's dense
-    GEMM (torch.matmul, hipBLASLt) on the same per-expert shapes, one call per
-    expert with the mean rows per expert, bf16 in and out, no epilogue work;
+    GEMM (torch.matmul, or torch._scaled_mm for the FP8 layers; hipBLASLt) on
+    the same per-expert shapes, one call per expert with the mean rows per
+    expert, no epilogue work; the first product over all rows against one
+    expert's weights (the same flops without streaming 256 weight matrices);
     and a large square GEMM as the library's best case on this GPU."""
     import torch
     import moe_synth as S
@@ -590,23 +592,69 @@ def vendor_gemm(name):
              ("wgrad dW1", "X_e^T @ dGU_e", lambda: [rows(x, e).t() @ rows(gu, e) for e in range(E)], f1),
              ("wgrad dW2", "H_e^T @ dY_e", lambda: [rows(h, e).t() @ rows(dy, e) for e in range(E)], f2)]
     sq = rnd(8192, 8192)
+    cases.append(("gemm1 dense", "X @ W1_0^T (all rows, one weight)", lambda: x @ w1[0].t(), f1))
     cases.append(("square", "8192 x 8192 x 8192", lambda: sq @ sq, 2.0 * 8192 ** 3))
-    print(f"# torch.matmul (hipBLASLt) on the GEMM shapes of {name}\n")
-    print(f"{E} experts x {R} rows (mean rows per expert), d={d}, f={f}; bf16; "
-          f"one call per expert; peak 2500 TFLOP/s.\n")
+    peak = 2500
+    lib = "torch.matmul (hipBLASLt)"
+    dtype_note = "bf16"
+    if cfg.weight in ("fp8", "mxfp8"):
+        # the same products in E4M3 through torch._scaled_mm with one fp32
+        # scale per tensor (no block scales: the library's plain FP8 GEMM),
+        # bf16 out; the second operand column-major as the call requires,
+        # transposed copies made once before timing
+        f8 = torch.float8_e4m3fn
+        one = torch.ones((), dtype=torch.float32, device=dev)
+        q = lambda t: t.to(f8)
+        xq, dyq, hq, guq = q(x), q(dy), q(h), q(gu)
+        w1q, w2q = q(w1), q(w2)
+        w1t = w1q.transpose(1, 2).contiguous()  # [E, d, 2f]
+        w2t = w2q.transpose(1, 2).contiguous()  # [E, f, d]
+        xT = [rows(xq, e).t().contiguous() for e in range(E)]
+        hT = [rows(hq, e).t().contiguous() for e in range(E)]
+        guT = [rows(guq, e).t().contiguous() for e in range(E)]
+        dyT = [rows(dyq, e).t().contiguous() for e in range(E)]
+        mm = lambda a, b_cm: torch._scaled_mm(a, b_cm, scale_a=one, scale_b=one, out_dtype=bf)
+        sq8, sq8t = q(sq), q(sq).t().contiguous()
+        w1q0 = w1q[0].t()
+        cases = [("gemm1", "X_e @ W1_e^T", lambda: [mm(rows(xq, e), w1q[e].t()) for e in range(E)], f1),
+                 ("gemm2", "H_e @ W2_e^T", lambda: [mm(rows(hq, e), w2q[e].t()) for e in range(E)], f2),
+                 ("dh", "dY_e @ W2_e", lambda: [mm(rows(dyq, e), w2t[e].t()) for e in range(E)], f2),
+                 ("dx", "dGU_e @ W1_e", lambda: [mm(rows(guq, e), w1t[e].t()) for e in range(E)], f1),
+                 ("wgrad dW1", "X_e^T @ dGU_e", lambda: [mm(xT[e], guT[e].t()) for e in range(E)], f1),
+                 ("wgrad dW2", "H_e^T @ dY_e", lambda: [mm(hT[e], dyT[e].t()) for e in range(E)], f2),
+                 ("gemm1 dense", "X @ W1_0^T (all rows, one weight)", lambda: mm(xq, w1q0), f1),
+                 ("square", "8192 x 8192 x 8192", lambda: mm(sq8, sq8t.t()), 2.0 * 8192 ** 3)]
+        peak = 5000
+        lib = "torch._scaled_mm (hipBLASLt)"
+        dtype_note = "E4M3 in with one fp32 scale per tensor, bf16 out"
+    print(f"# {lib} on the GEMM shapes of {name}\n")
+    print(f"{E} experts x {R} rows (mean rows per expert), d={d}, f={f}; {dtype_note}; "
+          f"one call per expert; peak {peak} TFLOP/s.\n")
+    print("Each case's calls are captured once into a HIP graph and the graph is replayed, so host launch "
+          "overhead is not timed (eager replays where capture fails).\n")
     print("| role | product | ms | TFLOP/s | % of peak |\n|---|---|---:|---:|---:|")
     for role, what, fn, flops in cases:
         for _ in range(3):
             fn()
         torch.cuda.synchronize()
+        run = fn
+        try:
+            graph = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(graph):
+                fn()
+            run = graph.replay
+            run()
+        except RuntimeError:
+            run = fn
+        torch.cuda.synchronize()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record()
         for _ in range(10):
-            fn()
+            run()
         e1.record()
         torch.cuda.synchronize()
         ms = e0.elapsed_time(e1) / 10
-        print(f"| {role} | {what} | {ms:.3f} | {flops / ms / 1e9:.0f} | {flops / ms / 1e9 / 25:.1f} |",
+        print(f"| {role} | {what} | {ms:.3f} | {flops / ms / 1e9:.0f} | {flops / ms / 1e9 / peak * 100:.1f} |",
               flush=True)
 
 
