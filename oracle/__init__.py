@@ -346,6 +346,22 @@ def mx_roundtrip_rows(a) -> np.ndarray:
     return dequant_mx_rows(*quant_mx_rows(np.asarray(a, dtype=np.float32)))
 
 
+def mx_roundtrip_tokens(a) -> np.ndarray:
+    """Quantise one expert's rows [M, C] (from fp32) in MX blocks of 32
+    consecutive rows x 1 column (E8M0 scales) and dequantise (fp64): the
+    operands of an MXFP8 weight-gradient product, whose contraction runs
+    over the expert's rows. The blocks start at the expert's first row; the
+    last one holds the M mod 32 remaining rows, quantised as the block
+    zero-padded to 32 rows (zeros change neither its amax nor its kept
+    codes)."""
+    a = np.asarray(a, dtype=np.float32)
+    M = a.shape[0]
+    pad = (-M) % MX_BLOCK
+    if pad:
+        a = np.concatenate([a, np.zeros((pad, a.shape[1]), np.float32)])
+    return dequant_mx_cols(*quant_mx_cols(a))[:M]
+
+
 # ------------------------------------------------------------ expert FFN
 
 def silu(z):
@@ -554,10 +570,13 @@ def aux_loss_dlogits(logits, idx, E: int, coeff: float, d_aux: float = 1.0) -> n
 
 # -------------------------------------------------------- the whole layer
 
-# FP8 layers: whether the weight-gradient operands are quantised in 128-row x 1
-# blocks (fp8_roundtrip_tokens) or taken unquantised (the forward's
-# dequantised X and H, the bf16 gradients)
+# 8-bit layers: whether the weight-gradient operands are quantised in token
+# blocks inside each expert's rows (FP8: 128-row x 1 blocks with fp32 scales,
+# fp8_roundtrip_tokens; MXFP8: 32-row x 1 blocks with E8M0 scales,
+# mx_roundtrip_tokens) or taken unquantised (the forward's dequantised X and
+# H, the bf16 gradients)
 FP8_WGRAD_TOKEN_BLOCKS = True
+MXFP8_WGRAD_TOKEN_BLOCKS = False
 
 
 def _expert_weight(w, e):
@@ -577,14 +596,17 @@ def layer_stream(cfg, inp: dict, identity: bool = False, on_expert=None,
     128 x 128 blocks and the dispatched rows per 1 x 128 block; H, dO and
     [dG dU] are quantised per 1 x 128 before the product that contracts them
     along their rows (ffn_fwd, ffn_bwd); with fp8_wgrad (default:
-    FP8_WGRAD_TOKEN_BLOCKS) the four operands of the weight-gradient products are
+    FP8_WGRAD_TOKEN_BLOCKS, MXFP8_WGRAD_TOKEN_BLOCKS) the four operands of the weight-gradient products are
     quantised in 128-row x 1 blocks inside each expert's rows
     (fp8_roundtrip_tokens). For mxfp8 every operand of the six expert
     products is quantised in blocks of 32 along that product's contraction
-    dimension with E8M0 scales: x, H, dO and [dG dU] in 1 x 32 row blocks;
-    W1 and W2 in row blocks for the forward and in 32 x 1 column blocks for
-    the data gradients; the weight gradients take the dequantised x and H and
-    the unquantised gradients.
+    dimension with E8M0 scales: x, H, dO and [dG dU] in 1 x 32 row blocks
+    for the forward and data-gradient products; W1 and W2 in row blocks for
+    the forward and in 32 x 1 column blocks for the data gradients; with
+    fp8_wgrad the four operands of the weight-gradient products (the
+    dequantised x and H, the unquantised dO and [dG dU]) in 32-row x 1
+    blocks inside each expert's rows (mx_roundtrip_tokens); without it the
+    weight gradients take those four unquantised.
 
     on_expert(e, r0, r1, t), when given, is called for every expert in order
     with its rows [r0, r1) of the dispatched order and t = dict(out_perm,
@@ -597,10 +619,14 @@ def layer_stream(cfg, inp: dict, identity: bool = False, on_expert=None,
     mx = cfg.weight == "mxfp8"
     fp8 = cfg.weight == "fp8"
     if fp8_wgrad is None:
-        fp8_wgrad = fp8 and FP8_WGRAD_TOKEN_BLOCKS
+        fp8_wgrad = (fp8 and FP8_WGRAD_TOKEN_BLOCKS) or (mx and MXFP8_WGRAD_TOKEN_BLOCKS)
     qb = cfg.quant_block
     h_quant = mx_roundtrip_rows if mx else (fp8_roundtrip_rows if fp8 else None)
-    w_quant = fp8_roundtrip_tokens if (fp8 and fp8_wgrad) else None
+    w_quant = None
+    if fp8_wgrad and fp8:
+        w_quant = fp8_roundtrip_tokens
+    elif fp8_wgrad and mx:
+        w_quant = mx_roundtrip_tokens
     out = {}
     L, idx, g = route(cfg, inp["x"], inp["wr"], inp.get("bias"))
     out.update(logits=L, idx=idx, gates=g)

@@ -19,7 +19,13 @@ and both against the unquantised bf16 layer (bf16 weights and inputs taken
 exactly, no quantisation anywhere), for context. Prints one JSON line with
 the relative L2 errors over all experts (the shared expert included).
 
-    python -m oracle.fp8_wgrad_budget [--experts N]
+With --mx the same comparison on the MXFP8 variant of that layer: every
+operand of the forward and data-gradient products in 1 x 32 (activations,
+gradients, forward weights) or 32 x 1 (data-gradient weights) E8M0 blocks,
+and the token-block reading quantising the four weight-gradient operands in
+32-row x 1 E8M0 blocks inside each expert's rows.
+
+    python -m oracle.fp8_wgrad_budget [--experts N] [--mx]
 """
 from __future__ import annotations
 
@@ -43,14 +49,15 @@ def _deq_w(w):
     return oracle.dequant_blocks(q, s, 128, 128)
 
 
-def measure(n_experts=None, log=print):
-    cfg = S.BY_NAME["deepseek_v3_fp8"]
+def measure(n_experts=None, log=print, mx=False):
+    cfg = S.BY_NAME["deepseek_v3_mxfp8" if mx else "deepseek_v3_fp8"]
     x = S.x(cfg)
     dy = oracle.as_f64(S.dy(cfg))
     L, idx, g = oracle.route(cfg, x, S.w_router(cfg))
     counts, offsets, rmap, ptok = oracle.dispatch_index(idx, cfg.E)
     x32 = oracle.as_f32(x)
-    Xq = oracle.fp8_roundtrip_rows(x32)          # dispatched rows, dequantised
+    # dispatched rows, dequantised
+    Xq = oracle.mx_roundtrip_rows(x32) if mx else oracle.fp8_roundtrip_rows(x32)
     X16 = x32.astype(np.float64)                 # the bf16 layer's rows
     # dO of the FP8 layer and of the bf16 layer: gate * dy for every routed row
     gate_of_row = np.empty(cfg.A)
@@ -61,11 +68,22 @@ def measure(n_experts=None, log=print):
     t0 = time.time()
 
     def one(Xe, X16e, dOe, w1, w2):
-        W1, W2 = _deq_w(w1), _deq_w(w2)
-        GU, H, _ = oracle.ffn_fwd(Xe, W1, W2, h_fp8=True)
-        _, dw1_a, dw2_a, _ = oracle.ffn_bwd(Xe, W1, W2, GU, H, dOe, dgrad_fp8=True)
-        _, dw1_b, dw2_b, _ = oracle.ffn_bwd(Xe, W1, W2, GU, H, dOe, dgrad_fp8=True,
-                                            wgrad_quant=oracle.fp8_roundtrip_tokens)
+        if mx:
+            w1f, w2f = oracle.as_f32(w1), oracle.as_f32(w2)
+            W1 = oracle.dequant_mx_rows(*oracle.quant_mx_rows(w1f))
+            W2 = oracle.dequant_mx_rows(*oracle.quant_mx_rows(w2f))
+            kw = dict(dgrad_quant=oracle.mx_roundtrip_rows,
+                      W1d=oracle.dequant_mx_cols(*oracle.quant_mx_cols(w1f)),
+                      W2d=oracle.dequant_mx_cols(*oracle.quant_mx_cols(w2f)))
+            GU, H, _ = oracle.ffn_fwd(Xe, W1, W2, h_quant=oracle.mx_roundtrip_rows)
+            tq = oracle.mx_roundtrip_tokens
+        else:
+            W1, W2 = _deq_w(w1), _deq_w(w2)
+            kw = dict(dgrad_fp8=True)
+            GU, H, _ = oracle.ffn_fwd(Xe, W1, W2, h_fp8=True)
+            tq = oracle.fp8_roundtrip_tokens
+        _, dw1_a, dw2_a, _ = oracle.ffn_bwd(Xe, W1, W2, GU, H, dOe, **kw)
+        _, dw1_b, dw2_b, _ = oracle.ffn_bwd(Xe, W1, W2, GU, H, dOe, wgrad_quant=tq, **kw)
         R1, R2 = oracle.as_f64(w1), oracle.as_f64(w2)
         GUr, Hr, _ = oracle.ffn_fwd(X16e, R1, R2)
         _, dw1_r, dw2_r, _ = oracle.ffn_bwd(X16e, R1, R2, GUr, Hr, dOe)
@@ -89,7 +107,7 @@ def measure(n_experts=None, log=print):
             one(Xq[rows], X16[rows], gate_of_row[r0:r1, None] * dy[rows],
                 S.expert_w1(cfg, e), S.expert_w2(cfg, e))
         if e % 16 == 15:
-            log(f"[fp8 wgrad] {e + 1} experts, {time.time() - t0:.0f} s")
+            log(f"[{'mxfp8' if mx else 'fp8'} wgrad] {e + 1} experts, {time.time() - t0:.0f} s")
     one(Xq, X16, dy, S.shared_w1(cfg), S.shared_w2(cfg))   # shared expert: gate 1, every token
     r = lambda a, b: float(np.sqrt(acc[a] / acc[b]))
     return {"workload": cfg.name, "experts": E, "shared": 1,
@@ -105,5 +123,6 @@ def measure(n_experts=None, log=print):
 if __name__ == "__main__":
     ap = argparse.ArgumentParser()
     ap.add_argument("--experts", type=int, default=None, help="first N routed experts only")
+    ap.add_argument("--mx", action="store_true", help="the MXFP8 variant of the layer")
     a = ap.parse_args()
-    print(json.dumps(measure(a.experts, log=lambda m: print(m, file=sys.stderr, flush=True))))
+    print(json.dumps(measure(a.experts, log=lambda m: print(m, file=sys.stderr, flush=True), mx=a.mx)))

@@ -309,6 +309,8 @@ def test_mxfp8_column_blocks_feed_only_the_data_gradients(monkeypatch):
     monkeypatch.setattr(oracle, "dequant_mx_rows", lambda q, e: q.astype(np.float64))
     monkeypatch.setattr(oracle, "mx_roundtrip_rows", lambda a: np.asarray(a, np.float32).astype(np.float64))
     monkeypatch.setattr(oracle, "dequant_mx_cols", lambda q, e: q.astype(np.float64))
+    # the weight-gradient token blocks are column blocks too: held fixed here
+    monkeypatch.setattr(oracle, "mx_roundtrip_tokens", lambda a: np.asarray(a, np.float32).astype(np.float64))
     base = oracle.layer(cfg, inp)
     monkeypatch.setattr(oracle, "dequant_mx_cols", lambda q, e: 2.0 * q.astype(np.float64))
     out = oracle.layer(cfg, inp)
@@ -374,6 +376,81 @@ def test_fp8_wgrad_token_blocks_feed_only_the_weight_gradients(monkeypatch):
 
 def test_fp8_wgrad_token_blocks_close_to_unquantised_gradients():
     cfg = S.mini(S.CONFIGS[4], T=300, d=256, f=256, E=4).replace(num_groups=2, topk_groups=1, k=2)
+    inp = _inputs(cfg)
+    a = oracle.layer(cfg, inp, fp8_wgrad=False)
+    b = oracle.layer(cfg, inp, fp8_wgrad=True)
+    assert np.array_equal(a["y"], b["y"]) and np.array_equal(a["dx"], b["dx"])
+    for n in ("dw1", "dw2", "shared_dw1", "shared_dw2"):
+        err = oracle.rel_l2(b[n], a[n])
+        assert 1e-3 < err < 0.06, (n, err)
+
+
+# ------------------------- MXFP8 weight gradients on 32-row x 1 blocks
+
+def _mx_exp_brute(amax):
+    """Smallest integer x in [-127, 127] with amax * 2^-x <= 448, by search."""
+    if amax == 0:
+        return 0
+    for x in range(-127, 128):
+        if float(amax) * 2.0 ** -x <= 448.0:
+            return x
+    raise AssertionError
+
+
+def test_mx_token_blocks_follow_the_expert_rows():
+    """32-row x 1 blocks from the first row, ragged tail kept short: they are
+    the 1 x 32 row blocks of the zero-padded transpose, padding changes no
+    kept value, and each block's largest magnitude picks the block's
+    power-of-two scale (brute-force exponent search) and lands in
+    [224, 448] x that scale: the block boundaries are the ones the scales
+    came from."""
+    rng = np.random.default_rng(31)
+    M, C = 75, 40
+    a = (rng.normal(size=(M, C)) * np.exp(rng.normal(size=(1, C)) * 3)).astype(np.float32)
+    a[32:64, 7] = 0.0                                    # an all-zero block
+    a[40, 9] = 1e4                                       # one large element
+    got = oracle.mx_roundtrip_tokens(a)
+    assert got.shape == (M, C)
+    pad = np.concatenate([a, np.zeros((96 - M, C), np.float32)])
+    assert np.array_equal(got, oracle.mx_roundtrip_rows(np.ascontiguousarray(pad.T)).T[:M])
+    assert np.array_equal(oracle.mx_roundtrip_tokens(pad)[:M], got)
+    assert not got[32:64, 7].any()
+    for b0, b1 in ((0, 32), (32, 64), (64, M)):
+        for c in range(C):
+            blk = a[b0:b1, c]
+            x = _mx_exp_brute(np.max(np.abs(blk)))
+            scaled = np.abs(got[b0:b1, c]) * 2.0 ** -x
+            assert np.all(scaled <= 448.0)
+            if blk.any():
+                assert 224.0 <= scaled.max(), (b0, c)
+    # the large element sets its own block's scale only
+    assert np.abs(got[32:64, 9]).max() >= 224.0 * 2.0 ** _mx_exp_brute(1e4)
+    assert np.abs(got[0:32, 9]).max() < 2.0 ** _mx_exp_brute(1e4)
+
+
+def test_mx_wgrad_token_blocks_feed_only_the_weight_gradients(monkeypatch):
+    """With the 32-row quantiser replaced by an exact doubling, the MXFP8
+    layer's dW1 and dW2 (both operands marked) become 4x those of the
+    unquantised-gradient reading and nothing else moves; with the identity
+    in its place both readings coincide."""
+    cfg = _mx_mini().replace(T=40)
+    inp = _inputs(cfg)
+    base = oracle.layer(cfg, inp, fp8_wgrad=False)
+    monkeypatch.setattr(oracle, "mx_roundtrip_tokens", lambda a: 2.0 * np.asarray(a, np.float64))
+    out = oracle.layer(cfg, inp, fp8_wgrad=True)
+    for n in ("y", "dx", "dx_perm", "d_gate", "dw_router", "shared_dx"):
+        assert np.array_equal(out[n], base[n]), n
+    for n in ("dw1", "dw2", "shared_dw1", "shared_dw2"):
+        assert oracle.rel_l2(out[n], 4.0 * base[n]) < 1e-14, n
+    monkeypatch.setattr(oracle, "mx_roundtrip_tokens",
+                        lambda a: np.asarray(a, np.float32).astype(np.float64))
+    out = oracle.layer(cfg, inp, fp8_wgrad=True)
+    for n in ("dw1", "dw2", "shared_dw1", "shared_dw2"):
+        assert oracle.rel_l2(out[n], base[n]) < 1e-7, n
+
+
+def test_mx_wgrad_token_blocks_close_to_unquantised_gradients():
+    cfg = _mx_mini().replace(T=300, E=4, num_groups=2, topk_groups=1, k=2)
     inp = _inputs(cfg)
     a = oracle.layer(cfg, inp, fp8_wgrad=False)
     b = oracle.layer(cfg, inp, fp8_wgrad=True)
