@@ -280,8 +280,10 @@ int moe_combine_bwd(const moe_config *cfg, const void *dy, const void *out_perm,
  * blocks inside each expert's rows (the first block starts at the expert's
  * first row, the last holds the rest), one scale per block and column; H and
  * X enter as their dequantised forward values. With MOE_DTYPE_MXFP8 the
- * data-gradient operands take 1 x 32 E8M0 blocks and the weight gradients run
- * in bf16 on the dequantised X and H.
+ * data-gradient operands take 1 x 32 E8M0 blocks, and the weight-gradient
+ * operands 32-row x 1 E8M0 blocks inside each expert's rows (the same
+ * blocking as the FP8 rule, 32 rows deep, scales applied by the matrix
+ * core).
  * Recompute (Megatron Core MoE summary, section 2.2: activations that take
  * memory but are cheap to compute are recomputed in the backward instead of
  * stored):

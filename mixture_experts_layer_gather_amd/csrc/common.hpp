@@ -98,6 +98,15 @@ __device__ __forceinline__ u32x2 mx_codes8(const float* v, int x) {
   hi = __builtin_amdgcn_cvt_pk_fp8_f32(ldexpf(v[6], -x), ldexpf(v[7], -x), hi, true);
   return u32x2{lo, hi};
 }
+// The same with one exponent per value.
+__device__ __forceinline__ u32x2 mx_codes8(const float* v, const int* x) {
+  uint32_t lo = 0, hi = 0;
+  lo = __builtin_amdgcn_cvt_pk_fp8_f32(ldexpf(v[0], -x[0]), ldexpf(v[1], -x[1]), lo, false);
+  lo = __builtin_amdgcn_cvt_pk_fp8_f32(ldexpf(v[2], -x[2]), ldexpf(v[3], -x[3]), lo, true);
+  hi = __builtin_amdgcn_cvt_pk_fp8_f32(ldexpf(v[4], -x[4]), ldexpf(v[5], -x[5]), hi, false);
+  hi = __builtin_amdgcn_cvt_pk_fp8_f32(ldexpf(v[6], -x[6]), ldexpf(v[7], -x[7]), hi, true);
+  return u32x2{lo, hi};
+}
 
 // Load/store one element of an activation tensor stored as f32 or bf16.
 template <typename T> struct Elem;

@@ -461,13 +461,14 @@ struct alignas(16) StageMx {
 };
 
 // The weight-gradient instances that run persistent runs of column tiles:
-// FP8 operands (token-block scales), bf16 results. (bf16 operands on the
+// FP8 or MXFP8 operands (token-block scales), bf16 results. (bf16 operands on the
 // 128 x 128 tile were measured the same way and lost to the 128 x 256
 // three-stage tile on every bf16 layer but one product: Qwen3-style dW1
 // 0.95 -> 2.17 ms, Mixtral-style 2.15 -> 2.55 ms.)
 template <typename T, typename TC, int MODE, int EPI, int NS>
 constexpr bool persistent_wgrad() {
-  return MODE == G_KSPLIT && EPI == EPI_STORE && NS == 2 && sizeof(TC) == 2 && std::is_same<T, fp8_t>::value;
+  return MODE == G_KSPLIT && EPI == EPI_STORE && NS == 2 && sizeof(TC) == 2 &&
+         (std::is_same<T, fp8_t>::value || std::is_same<T, mx8_t>::value);
 }
 
 template <typename T, typename TC, bool A_KMAJ, bool B_KMAJ, int MODE, int EPI, int BM, int BN,
@@ -479,8 +480,13 @@ void gemm_kernel(GemmArgs g) {
   using TO = typename OutOf<T>::type;
   constexpr bool FP8 = sizeof(T) == 1;
   constexpr bool MX = std::is_same<T, mx8_t>::value;
-  // FP8 weight gradient: scales per (128-row block, column) of both operands
+  // 8-bit weight gradients: a scale per (128-row block, column) of both
+  // operands, staged per K step with the tiles (TOKW): FP8 fp32 scales,
+  // applied by VALU FMAs (TOKSCALE), or MXFP8 words of the block's four
+  // 32-row E8M0 bytes, applied by the matrix core (TOKMX)
   constexpr bool TOKSCALE = FP8 && !MX && MODE == G_KSPLIT;
+  constexpr bool TOKMX = MX && MODE == G_KSPLIT;
+  constexpr bool TOKW = TOKSCALE || TOKMX;
   using ST = std::conditional_t<MX, StageMx<BM, BN, BK, WM * WN * 64>, Stage<T, BM, BN, BK, WM * WN * 64, FP8>>;
   constexpr int VEC = 16 / sizeof(T);
   constexpr int WTM = BM / WM, WTN = BN / WN;
@@ -488,13 +494,13 @@ void gemm_kernel(GemmArgs g) {
   constexpr int ALM = layout_mode<T, A_KMAJ>(), BLM = layout_mode<T, B_KMAJ>();
   using PA = OperandPlan<T, ALM, BM, BK, NTH>;
   using PB = OperandPlan<T, BLM, BN, BK, NTH>;
-  // weight gradients as runs of column tiles per workgroup (FP8)
+  // weight gradients as runs of column tiles per workgroup (8-bit operands)
   constexpr bool PERSIST = persistent_wgrad<T, TC, MODE, EPI, NS>();
   static_assert(!PERSIST || (PA::DMA && PB::DMA), "persistent weight gradients load by DMA");
   static_assert(WM * WN == 4 || WM * WN == 8, "four or eight waves");
   static_assert(EPI != EPI_SWIGLU || FN % 2 == 0, "SwiGLU pairs column fragments");
   static_assert(!FP8 || (MODE == G_ROWS && A_KMAJ && BK == 128 && BN <= 256 && BM <= 256) ||
-                    (TOKSCALE && !A_KMAJ && !B_KMAJ && BK == 128 && BM + BN <= WM * WN * 64),
+                    (TOKW && PERSIST && !A_KMAJ && !B_KMAJ && BK == 128 && BM + BN <= WM * WN * 64),
                 "FP8: row-grouped GEMMs, or weight gradients, one 128-deep scale block per K step");
 
   static_assert(NS >= 2 && NS <= 4, "LDS stages");
@@ -666,7 +672,7 @@ void gemm_kernel(GemmArgs g) {
   // the row's four E8M0 bytes of the step (a_scale_ld = K / 128 words).
   const char* sa_base = nullptr;
   int64_t sa_end = 0;
-  if constexpr (FP8 && !TOKSCALE) {
+  if constexpr (FP8 && !TOKW) {
     sa_base = reinterpret_cast<const char*>(g.a_scale + int64_t(row0) * g.a_scale_ld);
     sa_end = int64_t(mrows) * g.a_scale_ld * 4;
   }
@@ -674,11 +680,11 @@ void gemm_kernel(GemmArgs g) {
   // scales land in LDS by DMA, 64 consecutive ones per wave: the A scales of
   // output rows m0 .. m0 + BM (waves below BM / 64), then the B scales of
   // columns n0 .. n0 + BN
-  static_assert(!TOKSCALE || (BM % 64 == 0 && BN % 64 == 0 && BM + BN == NTH), "one scale run per wave");
+  static_assert(!TOKW || (BM % 64 == 0 && BN % 64 == 0 && BM + BN == NTH), "one scale run per wave");
   int kb0 = 0;
   const float* ts_run = nullptr;
   int64_t ts_ld = 0;
-  if constexpr (TOKSCALE) {
+  if constexpr (TOKW) {
     kb0 = g.kblk[grp];
     if (wave * 64 < BM) {
       ts_run = g.a_scale + m0 + wave * 64;
@@ -717,7 +723,7 @@ void gemm_kernel(GemmArgs g) {
   const char* mb_base = nullptr;
   int64_t mb_end = 0;
   int mb_row = 0;  // K-major: byte offset of column tid's scale row
-  if constexpr (MX) {
+  if constexpr (MX && !TOKMX) {
     mb_base = reinterpret_cast<const char*>(g.b_scale) + int64_t(grp) * g.b_scale_gstride;
     mb_end = B_KMAJ ? int64_t(g.N) * g.b_scale_ld : int64_t(g.K / 32) * g.b_scale_ld;
     if constexpr (B_KMAJ) {
@@ -738,7 +744,7 @@ void gemm_kernel(GemmArgs g) {
   const char* sc_base = nullptr;
   int64_t sc_end = 0;
   uint32_t sc_off = 0, sc_inc = 0;
-  if constexpr (FP8 && !TOKSCALE) {
+  if constexpr (FP8 && !TOKW) {
     const bool arow = wave < BM / 64;
     sc_base = arow ? sa_base : reinterpret_cast<const char*>(sb_base);
     sc_end = arow ? sa_end : sb_end;
@@ -788,11 +794,11 @@ void gemm_kernel(GemmArgs g) {
       // w < BM / 64 gathers rows 64 w .. 64 w + 63 (rows past the group read
       // 0), the waves past them the B scales
       dma4(rsrc_words(sc_base, live ? sc_end : 0), &st.SA[wave * 64], sc_off + uint32_t(s) * sc_inc);
-    } else if constexpr (FP8 && !TOKSCALE) {
+    } else if constexpr (FP8 && !TOKW) {
       const rsrc_t sr = make_rsrc(sc_base, live ? sc_end : 0);
       rs = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(sr, sc_off + uint32_t(s) * sc_inc, 0, 0));
     }
-    if constexpr (MX) {
+    if constexpr (MX && !TOKMX) {
       // threads tid < BN (whole waves) fetch a column's word; the others
       // read an empty range (zeros): no branch, as for the FP8 scales
       const rsrc_t sr = make_rsrc(mb_base, (live && wave < BN / 64) ? mb_end : 0);
@@ -819,10 +825,10 @@ void gemm_kernel(GemmArgs g) {
 #pragma unroll
       for (int i = 0; i < PB::NT; ++i) store_transposed<T, BK>(&rb[4 * i], st.B, pb.lrow[i], pb.lk[i]);
     }
-    if constexpr (MX) {
+    if constexpr (MX && !TOKMX) {
       st.SA[tid] = __builtin_bit_cast(uint32_t, rs);
       st.SB[tid] = rsb;  // entries past BN: zeros, unused
-    } else if constexpr (FP8 && !TOKSCALE) {
+    } else if constexpr (FP8 && !TOKW) {
       st.SA[tid] = rs;
     }
   };
@@ -913,7 +919,9 @@ void gemm_kernel(GemmArgs g) {
 #pragma unroll
       for (int j = 0; j < FN; ++j) {
         bfr[j] = load_b(st, j, 0);
-        sbj[j] = int((st.SB[wn * WTN + j * 16 + lane % 16] >> sh) & 0xffu);
+        // (weight gradients: the B words follow the A rows' in SA)
+        const uint32_t wj = TOKMX ? st.SA[BM + wn * WTN + j * 16 + lane % 16] : st.SB[wn * WTN + j * 16 + lane % 16];
+        sbj[j] = int((wj >> sh) & 0xffu);
       }
       acur = load_a(st, 0, 0);
       static_for<FM>([&](auto ic) {
@@ -1011,7 +1019,7 @@ void gemm_kernel(GemmArgs g) {
     // loads have been issued. Loads and stores complete in issue order, so
     // the wait for a step's loads counts the stores issued after them.
     static_assert(NS == 2 && EPI == EPI_STORE && sizeof(TC) == 2, "two stages, plain bf16 stores");
-    constexpr int NDMA = PA::NB + PB::NB + (TOKSCALE ? 1 : 0);
+    constexpr int NDMA = PA::NB + PB::NB + (TOKW ? 1 : 0);
     constexpr int EPB = WTN + 8;  // bf16 per staged row (16-byte pad: no bank conflicts)
     constexpr int UPR = WTN / 8;  // 8-column units per staged row
     static_assert(16 * UPR % 64 == 0, "whole store rounds per lane");
@@ -1029,7 +1037,7 @@ void gemm_kernel(GemmArgs g) {
       const u32x4 br = rsrc_words(b_base + int64_t(s) * b_step + jb, b_end - int64_t(s) * b_step - jb);
 #pragma unroll
       for (int b = 0; b < PB::NB; ++b) dma16(br, &st.B[(b * PB::NW + wave) * (1024 / ES)], pb.voff[b]);
-      if constexpr (TOKSCALE) {
+      if constexpr (TOKW) {
         const int64_t so = int64_t(kb0 + s) * ts_ld + (wave * 64 < BM ? 0 : int64_t(j) * BN);
         dma4(rsrc_words(ts_run + so, 256), &st.SA[wave * 64], uint32_t(lane * 4));
       }
@@ -1565,6 +1573,111 @@ __global__ __launch_bounds__(256) void quant_tokens_kernel(const void* __restric
 
 static int64_t token_blocks_bound(int64_t A, int64_t G) { return (A + G * 127) / 128; }
 
+// MXFP8 weight-gradient operands: E4M3 in blocks of 32 consecutive rows x 1
+// column inside each expert's rows, one E8M0 byte per block (the MXFP8 rule
+// of the row quantiser). The four blocks of a 128-row block and column share
+// one word, byte q for rows 32 q .. 32 q + 31 of the 128-row block: the
+// per-K-step scale word of the weight-gradient GEMM. Rows past the expert's
+// end count as zeros (their blocks take byte 127). Block b of the
+// concatenated 128-row block list is block b - kblk[e] of expert e. One
+// workgroup per (128-row block, 128 columns), thread (cg, rg) holding
+// columns 8 cg .. 8 cg + 7 of rows rg, rg + 16, ..., rg + 112 (rows rg + 16 i
+// lie in 32-row block i / 2); the block maxima meet in LDS. Sources: bf16
+// rows, or E4M3 codes with one E8M0 byte per 1 x 32 block of a row, taken as
+// code x 2^(byte - 127) in fp32.
+template <bool SRC_MX>
+__global__ __launch_bounds__(256) void quant_tokens_mx_kernel(const void* __restrict__ src,
+                                                              const uint8_t* __restrict__ src_e8m0,
+                                                              const int32_t* __restrict__ offsets,
+                                                              const int32_t* __restrict__ kblk, int G, int64_t C,
+                                                              fp8_t* __restrict__ q, uint32_t* __restrict__ words) {
+  __shared__ __attribute__((aligned(16))) float s_max[16][4][132];  // 16-byte rows: float4 stores
+  __shared__ int s_x[4][128];
+  const int b = blockIdx.x;
+  if (b >= kblk[G]) return;
+  int lo = 0, hi = G - 1;  // the expert owning block b: the last e with kblk[e] <= b
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) / 2;
+    if (kblk[mid] <= b) lo = mid;
+    else hi = mid - 1;
+  }
+  const int64_t r0 = int64_t(offsets[lo]) + int64_t(b - kblk[lo]) * 128;
+  const int nrows = int(min(int64_t(128), int64_t(offsets[lo + 1]) - r0));
+  const int cg = threadIdx.x % 16, rg = threadIdx.x / 16;
+  const int64_t c0 = int64_t(blockIdx.y) * 128 + cg * 8;  // C is a multiple of 128
+  float v[8][8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int rr = rg + 16 * i;
+    if (rr < nrows) {
+      const int64_t off = (r0 + rr) * C + c0;
+      if constexpr (SRC_MX) {
+        const u32x2 w = *reinterpret_cast<const u32x2*>(static_cast<const fp8_t*>(src) + off);
+        const int x = int(src_e8m0[(r0 + rr) * (C / 32) + c0 / 32]) - 127;
+        const float f8[8] = {__builtin_amdgcn_cvt_f32_fp8(w[0], 0), __builtin_amdgcn_cvt_f32_fp8(w[0], 1),
+                             __builtin_amdgcn_cvt_f32_fp8(w[0], 2), __builtin_amdgcn_cvt_f32_fp8(w[0], 3),
+                             __builtin_amdgcn_cvt_f32_fp8(w[1], 0), __builtin_amdgcn_cvt_f32_fp8(w[1], 1),
+                             __builtin_amdgcn_cvt_f32_fp8(w[1], 2), __builtin_amdgcn_cvt_f32_fp8(w[1], 3)};
+#pragma unroll
+        for (int c = 0; c < 8; ++c) v[i][c] = ldexpf(f8[c], x);
+      } else {
+        Vec16<bf16_t>::load(static_cast<const bf16_t*>(src) + off, v[i]);
+      }
+    } else {
+#pragma unroll
+      for (int c = 0; c < 8; ++c) v[i][c] = 0.0f;
+    }
+  }
+#pragma unroll
+  for (int qb = 0; qb < 4; ++qb) {
+    float m[8];
+#pragma unroll
+    for (int c = 0; c < 8; ++c) m[c] = fmaxf(fabsf(v[2 * qb][c]), fabsf(v[2 * qb + 1][c]));
+    *reinterpret_cast<float4*>(&s_max[rg][qb][cg * 8]) = float4{m[0], m[1], m[2], m[3]};
+    *reinterpret_cast<float4*>(&s_max[rg][qb][cg * 8 + 4]) = float4{m[4], m[5], m[6], m[7]};
+  }
+  __syncthreads();
+  {  // 512 (32-row block, column) pairs, two per thread
+    const int col = threadIdx.x % 128, q0 = (threadIdx.x / 128) * 2;
+#pragma unroll
+    for (int qb = q0; qb < q0 + 2; ++qb) {
+      float a = 0.0f;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) a = fmaxf(a, s_max[r][qb][col]);
+      s_x[qb][col] = mx_scale_exp(a);
+    }
+  }
+  __syncthreads();
+  if (threadIdx.x < 128) {
+    const int col = threadIdx.x;
+    uint32_t w = 0;
+#pragma unroll
+    for (int qb = 0; qb < 4; ++qb) w |= uint32_t(s_x[qb][col] + 127) << (8 * qb);
+    words[int64_t(b) * C + int64_t(blockIdx.y) * 128 + col] = w;
+  }
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int rr = rg + 16 * i;
+    int x[8];
+#pragma unroll
+    for (int c = 0; c < 8; ++c) x[c] = s_x[i / 2][cg * 8 + c];
+    if (rr < nrows) *reinterpret_cast<u32x2*>(q + (r0 + rr) * C + c0) = mx_codes8(v[i], x);
+  }
+}
+
+// src [A, C] (bf16, or E4M3 codes with [A, C/32] E8M0 row-block bytes) ->
+// q [A, C] E4M3 and words [token_blocks_bound(A, G), C] (rows past the
+// actual block count are not written)
+static void quant_tokens_mx(const void* src, const uint8_t* src_e8m0, const int32_t* offsets, const int32_t* kblk,
+                            int64_t G, int64_t A, int64_t C, fp8_t* q, uint32_t* words, hipStream_t st) {
+  const dim3 grid(unsigned(token_blocks_bound(A, G)), unsigned(C / 128));
+  if (grid.x == 0) return;
+  if (src_e8m0)
+    quant_tokens_mx_kernel<true><<<grid, 256, 0, st>>>(src, src_e8m0, offsets, kblk, int(G), C, q, words);
+  else
+    quant_tokens_mx_kernel<false><<<grid, 256, 0, st>>>(src, nullptr, offsets, kblk, int(G), C, q, words);
+}
+
 // src [A, C] (bf16, or E4M3 codes with [A, C/128] fp32 row-block scales)
 // -> q [A, C] E4M3 and scale [token_blocks_bound(A, G), C] (rows past the
 // actual block count are not written); with rq (bf16 sources) also the
@@ -1615,6 +1728,7 @@ template <typename T> using BigCfg8 = Cfg<T, 256, 256, 128, 2, 4, 2>;
 // FP8 weight gradients: 128 x 128, 4 waves of 64 x 64, BK 128, two stages;
 // a workgroup runs up to kWgradRun column tiles of one row block
 typedef Cfg<fp8_t, 128, 128, 128, 2, 2, 2> WgradCfg8;
+typedef Cfg<mx8_t, 128, 128, 128, 2, 2, 2> WgradCfgMx8;
 constexpr int kWgradRun = 8;
 typedef Cfg<bf16_t, 128, 256, 32, 2, 2, 3> WgradCfg;
 
@@ -1687,10 +1801,8 @@ struct FfnWs {
   size_t d_out_s = 0;
   size_t d_gu_q = 0;   // bwd fp8: dGU codes [A, 2f] + scales [A, 2f/128]
   size_t d_gu_s = 0;
-  size_t x_deq = 0;    // bwd mxfp8: dequantised X [A, d] bf16
-  size_t h_deq = 0;    // bwd mxfp8: dequantised H [A, f] bf16
-  // bwd fp8: weight-gradient operands in 128-row x 1 blocks: block offsets
-  // [E+1], codes [A, C] and scales [NB, C] of dO, H, dGU and X
+  // bwd fp8 and mxfp8: weight-gradient operands in token blocks: 128-row
+  // block offsets [E+1], codes [A, C] and scales [NB, C] of dO, H, dGU and X
   size_t kblk = 0;
   size_t t_do = 0, t_do_s = 0, t_h = 0, t_h_s = 0, t_gu = 0, t_gu_s = 0, t_x = 0, t_x_s = 0;
   size_t total = 0;
@@ -1717,10 +1829,9 @@ static FfnWs ffn_ws(int64_t A, int64_t d, int64_t f, int64_t E, int act_bytes, i
       w.d_out_s = o; o += al(size_t(A) * (d / 128) * 4);
       w.d_gu_q = o; o += al(size_t(A) * 2 * f);
       w.d_gu_s = o; o += al(size_t(A) * (2 * f / 128) * 4);
-      if (wt == 3) {
-        w.x_deq = o; o += al(size_t(A) * d * 2);
-        w.h_deq = o; o += al(size_t(A) * f * 2);
-      } else {
+      {
+        // (MXFP8: the scale arrays hold one word of four E8M0 bytes per
+        // 128-row block and column, the size of the FP8 fp32 scales)
         const size_t nb = size_t(token_blocks_bound(A, E));
         w.kblk = o; o += al(size_t(E + 1) * 4);
         w.t_do = o; o += al(size_t(A) * d);
@@ -1886,15 +1997,16 @@ static void wgrad_t(const void* d_out, const void* act_h, const void* d_gu, cons
   run_gemm<C, TW, false, false, G_KSPLIT, EPI_STORE>(g4, n4, st);
 }
 
-// FP8 weight gradients: dW2 = dO^T H and dW1 = dGU^T X with every operand
-// in 128-row x 1 blocks (codes [A, C], scales [NB, C], kblk the first block
-// of each expert); bf16 results.
-static void wgrad_fp8(int tile, const fp8_t* dq, const float* ds, const fp8_t* hq, const float* hs,
-                      const fp8_t* gq, const float* gs, const fp8_t* xq, const float* xs, const int32_t* kblk,
-                      void* dw1, void* dw2, const int32_t* offsets, int64_t d, int64_t f, int64_t E,
-                      hipStream_t st) {
-  typedef WgradCfg8 C;
-  (void)tile;
+// 8-bit weight gradients: dW2 = dO^T H and dW1 = dGU^T X with every operand
+// in token blocks (codes [A, C], scales [NB, C] per 128-row block and
+// column: FP8 fp32 scales of 128-row x 1 blocks, or MXFP8 words of four
+// 32-row E8M0 bytes; kblk the first block of each expert); bf16 results.
+template <bool MXF>
+static void wgrad_8bit(const fp8_t* dq, const void* ds, const fp8_t* hq, const void* hs, const fp8_t* gq,
+                       const void* gs, const fp8_t* xq, const void* xs, const int32_t* kblk, void* dw1, void* dw2,
+                       const int32_t* offsets, int64_t d, int64_t f, int64_t E, hipStream_t st) {
+  typedef std::conditional_t<MXF, WgradCfgMx8, WgradCfg8> C;
+  auto sc = [](const void* p) { return static_cast<const float*>(p); };
   auto run = [&](GemmArgs& gg) {
     // runs of column tiles while the grid keeps at least 8 workgroups per CU
     const int64_t tiles = E * gg.tiles_m * gg.tiles_n;
@@ -1903,8 +2015,8 @@ static void wgrad_fp8(int tile, const fp8_t* dq, const float* ds, const fp8_t* h
         gg, int(E) * gg.tiles_m * ((gg.tiles_n + gg.tpw - 1) / gg.tpw), st);
   };
   GemmArgs g3{};
-  g3.A = dq; g3.lda = d; g3.a_scale = ds; g3.a_scale_ld = int(d);
-  g3.B = hq; g3.ldb = f; g3.b_scale = hs; g3.b_scale_ld = int(f);
+  g3.A = dq; g3.lda = d; g3.a_scale = sc(ds); g3.a_scale_ld = int(d);
+  g3.B = hq; g3.ldb = f; g3.b_scale = sc(hs); g3.b_scale_ld = int(f);
   g3.kblk = kblk;
   g3.C = dw2; g3.ldc = f; g3.c_gstride = d * f;
   g3.offsets = offsets; g3.G = int(E);
@@ -1912,8 +2024,8 @@ static void wgrad_fp8(int tile, const fp8_t* dq, const float* ds, const fp8_t* h
   g3.tiles_m = int(d / C::BM); g3.tiles_n = int(f / C::BN);
   run(g3);
   GemmArgs g4{};
-  g4.A = gq; g4.lda = 2 * f; g4.a_scale = gs; g4.a_scale_ld = int(2 * f);
-  g4.B = xq; g4.ldb = d; g4.b_scale = xs; g4.b_scale_ld = int(d);
+  g4.A = gq; g4.lda = 2 * f; g4.a_scale = sc(gs); g4.a_scale_ld = int(2 * f);
+  g4.B = xq; g4.ldb = d; g4.b_scale = sc(xs); g4.b_scale_ld = int(d);
   g4.kblk = kblk;
   g4.C = dw1; g4.ldc = d; g4.c_gstride = 2 * f * d;
   g4.offsets = offsets; g4.G = int(E);
@@ -2031,25 +2143,21 @@ static void ffn_bwd_fp8(const FfnBwdLaunch& a, bf16_t* h16, hipStream_t st) {
     if constexpr (MXF) launch_quant_mx_rows(src, true, rows, cols, q, reinterpret_cast<uint8_t*>(sc), st);
     else launch_quant_rows(src, true, rows, cols, q, sc, st);
   };
-  auto dequant = [&](const void* q, const float* sc, int64_t rows, int64_t cols, bf16_t* dst) {
-    if constexpr (MXF)
-      dequant_mx_rows(static_cast<const uint8_t*>(q), reinterpret_cast<const uint8_t*>(sc), rows, cols, dst, st);
-    else
-      dequant_rows(static_cast<const uint8_t*>(q), sc, rows, cols, dst, st);
-  };
   const FfnWs w = ffn_ws(a.A, a.d, a.f, a.E, 2, a.wt, true, a.recompute);
   bf16_t* d_gu = reinterpret_cast<bf16_t*>(at(a.ws, w.d_gu));
   uint8_t* dq = reinterpret_cast<uint8_t*>(at(a.ws, w.d_out_q));
   float* ds = reinterpret_cast<float*>(at(a.ws, w.d_out_s));
   uint8_t* gq = reinterpret_cast<uint8_t*>(at(a.ws, w.d_gu_q));
   float* gs = reinterpret_cast<float*>(at(a.ws, w.d_gu_s));
-  bf16_t* xd = reinterpret_cast<bf16_t*>(at(a.ws, w.x_deq));
-  bf16_t* hd = reinterpret_cast<bf16_t*>(at(a.ws, w.h_deq));
   int32_t* kblk = reinterpret_cast<int32_t*>(at(a.ws, w.kblk));
   auto tq = [&](size_t o) { return reinterpret_cast<fp8_t*>(at(a.ws, o)); };
   auto ts = [&](size_t o) { return reinterpret_cast<float*>(at(a.ws, o)); };
+  auto tw = [&](size_t o) { return reinterpret_cast<uint32_t*>(at(a.ws, o)); };
   if constexpr (MXF) {
+    // dO: 1 x 32 row blocks (dH) and 32-row blocks (dW2)
+    kblock_offsets_kernel<<<1, 1024, 0, st>>>(a.offsets, kblk, int(a.E));
     quant(a.d_out, a.A, a.d, dq, ds);
+    quant_tokens_mx(a.d_out, nullptr, a.offsets, kblk, a.E, a.A, a.d, tq(w.t_do), tw(w.t_do_s), st);
   } else {
     // dO read once: its 1 x 128 row blocks (dH) and 128-row blocks (dW2)
     kblock_offsets_kernel<<<1, 1024, 0, st>>>(a.offsets, kblk, int(a.E));
@@ -2066,8 +2174,12 @@ static void ffn_bwd_fp8(const FfnBwdLaunch& a, bf16_t* h16, hipStream_t st) {
   }
   if (h16) quant(h16, a.A, a.f, static_cast<uint8_t*>(const_cast<void*>(a.act_h)), const_cast<float*>(a.h_scale));
   // dX = Q(dGU) W1
-  if constexpr (MXF) quant(d_gu, a.A, 2 * a.f, gq, gs);
-  else quant_tokens(d_gu, nullptr, a.offsets, kblk, a.E, a.A, 2 * a.f, tq(w.t_gu), ts(w.t_gu_s), st, gq, gs);
+  if constexpr (MXF) {
+    quant(d_gu, a.A, 2 * a.f, gq, gs);
+    quant_tokens_mx(d_gu, nullptr, a.offsets, kblk, a.E, a.A, 2 * a.f, tq(w.t_gu), tw(w.t_gu_s), st);
+  } else {
+    quant_tokens(d_gu, nullptr, a.offsets, kblk, a.E, a.A, 2 * a.f, tq(w.t_gu), ts(w.t_gu_s), st, gq, gs);
+  }
   if constexpr (!MXF) {
     if (big8(a.tile, a.d)) dx_fp8<MXF, BigCfg8<T8>>(a, gq, gs, st);
     else dx_fp8<MXF, SmallCfg<T8>>(a, gq, gs, st);
@@ -2075,18 +2187,20 @@ static void ffn_bwd_fp8(const FfnBwdLaunch& a, bf16_t* h16, hipStream_t st) {
     dx_fp8<MXF, SmallCfg<T8>>(a, gq, gs, st);
   }
   if constexpr (MXF) {
-    // weight gradients in bf16 on dequantised X and H
-    dequant(a.x_perm, a.x_scale, a.A, a.d, xd);
-    dequant(a.act_h, a.h_scale, a.A, a.f, hd);
-    wgrad_any<bf16_t>(a.tile, a.d_out, hd, d_gu, xd, a.dw1, a.dw2, a.offsets, a.d, a.f, a.E, st);
+    // weight gradients in MXFP8: the four operands in 32-row x 1 blocks,
+    // H and X from their forward codes
+    const uint8_t* hs8 = reinterpret_cast<const uint8_t*>(a.h_scale);
+    const uint8_t* xs8 = reinterpret_cast<const uint8_t*>(a.x_scale);
+    quant_tokens_mx(a.act_h, hs8, a.offsets, kblk, a.E, a.A, a.f, tq(w.t_h), tw(w.t_h_s), st);
+    quant_tokens_mx(a.x_perm, xs8, a.offsets, kblk, a.E, a.A, a.d, tq(w.t_x), tw(w.t_x_s), st);
   } else {
     // weight gradients in FP8: the four operands in 128-row x 1 blocks (dO
     // and dGU were quantised so with their row blocks)
     quant_tokens(a.act_h, a.h_scale, a.offsets, kblk, a.E, a.A, a.f, tq(w.t_h), ts(w.t_h_s), st);
     quant_tokens(a.x_perm, a.x_scale, a.offsets, kblk, a.E, a.A, a.d, tq(w.t_x), ts(w.t_x_s), st);
-    wgrad_fp8(a.tile, tq(w.t_do), ts(w.t_do_s), tq(w.t_h), ts(w.t_h_s), tq(w.t_gu), ts(w.t_gu_s), tq(w.t_x),
-              ts(w.t_x_s), kblk, a.dw1, a.dw2, a.offsets, a.d, a.f, a.E, st);
   }
+  wgrad_8bit<MXF>(tq(w.t_do), at(a.ws, w.t_do_s), tq(w.t_h), at(a.ws, w.t_h_s), tq(w.t_gu), at(a.ws, w.t_gu_s),
+                  tq(w.t_x), at(a.ws, w.t_x_s), kblk, a.dw1, a.dw2, a.offsets, a.d, a.f, a.E, st);
 }
 
 void launch_grouped_ffn(const FfnLaunch& a, hipStream_t st) {

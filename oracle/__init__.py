@@ -576,7 +576,7 @@ def aux_loss_dlogits(logits, idx, E: int, coeff: float, d_aux: float = 1.0) -> n
 # mx_roundtrip_tokens) or taken unquantised (the forward's dequantised X and
 # H, the bf16 gradients)
 FP8_WGRAD_TOKEN_BLOCKS = True
-MXFP8_WGRAD_TOKEN_BLOCKS = False
+MXFP8_WGRAD_TOKEN_BLOCKS = True
 
 
 def _expert_weight(w, e):

@@ -249,19 +249,19 @@ def test_mxfp8_config_and_quantiser_arguments(M):
     # the backward holds the column-quantised weights only: no GEMM1 rerun
     assert _route(M, _cfg(M, weight="mxfp8", quant_block=32, recompute="full")) == -2
     assert _route(M, _cfg(M, weight="mxfp8", quant_block=32, recompute="act", T=0)) == 0
-    # E8M0 scales take as many bytes as the fp32 1 x 128 scales: same forward
-    # workspace; the backward's differs (FP8 keeps its weight-gradient operands
-    # in 128-row blocks: codes [A, C] and scales [NB, C] for dO, H, dGU and X,
-    # NB = (A + 127 E) / 128; MXFP8 keeps X and H dequantised to bf16)
+    # E8M0 scales take as many bytes as the fp32 1 x 128 scales, and both
+    # 8-bit layers keep their weight-gradient operands in token blocks (codes
+    # [A, C] and [NB, C] scales: FP8 fp32 per 128-row block, MXFP8 one word of
+    # four 32-row E8M0 bytes per 128-row block; NB = (A + 127 E) / 128): the
+    # same workspace for every call
     A, E, d, f = 4000, 16, 512, 384
     cm = _cfg(M, T=1000, E=E, k=4, f=f, d=d, weight="mxfp8", quant_block=32)
     cf = _cfg(M, T=1000, E=E, k=4, f=f, d=d, weight="fp8")
-    for op in (1, 2):
+    for op in (1, 2, 3):
         assert L.moe_workspace_size(ctypes.byref(cm), op) == L.moe_workspace_size(ctypes.byref(cf), op)
     nb = (A + 127 * E) // 128
     tok = A * (2 * d + 3 * f) + 4 * nb * (2 * d + 3 * f)
-    assert L.moe_workspace_size(ctypes.byref(cf), 3) - L.moe_workspace_size(ctypes.byref(cm), 3) >= \
-        tok - A * (d + f) * 2 - 10 * 256
+    assert L.moe_workspace_size(ctypes.byref(cm), 3) >= tok
     q = L.moe_quantize_mxfp8
     assert q(FAKE, 7, 32, 32, 0, FAKE, FAKE, None) == -2          # dtype
     assert q(FAKE, 1, 32, 48, 0, FAKE, FAKE, None) == -1          # cols % 32 (rows mode)

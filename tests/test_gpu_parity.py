@@ -153,6 +153,13 @@ SMALL = {
     "max_experts_topk": S.mini(S.CONFIGS[1], T=200, d=128, f=128, E=1024).replace(k=16, seed_base=63),
     # MXFP8: 1 x 32 / 32 x 1 blocks with E8M0 scales on the matrix cores
     "deepseek_mxfp8_mini": S.mini(S.BY_NAME["deepseek_v3_mxfp8"], T=400, d=384, f=256, E=32).replace(k=6),
+    # MXFP8 weight gradients (32-row E8M0 token blocks) in runs of two column
+    # tiles, as for FP8 above: even routing, and skewed routing with empty
+    # experts and experts whose last 128-row block ends inside a 32-row block
+    "deepseek_mxfp8_runs": S.mini(S.BY_NAME["deepseek_v3_mxfp8"], T=1024, d=1152, f=512, E=64).replace(
+        k=4, seed_base=38),
+    "deepseek_mxfp8_runs_skew": S.mini(S.BY_NAME["deepseek_v3_mxfp8"], T=1024, d=1152, f=512, E=64).replace(
+        k=4, bias="zipf", seed_base=39),
     # the load-balancing auxiliary loss on (coefficient 0.01): its value and
     # its share of the router gradient
     "mixtral_mini_aux": S.mini(S.CONFIGS[1], T=1000, d=256, f=384).replace(aux_coeff=0.01),
