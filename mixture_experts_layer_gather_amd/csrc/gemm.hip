@@ -1237,7 +1237,7 @@ void gemm_kernel(GemmArgs g) {
 }
 
 // ---------------------------------------------------------------------------
-// FP8 row quantisation (1 x 128 blocks) and dequantisation, 16 lanes per block
+// FP8 row quantisation (1 x 128 blocks), 16 lanes per block
 // ---------------------------------------------------------------------------
 template <typename TS>
 __global__ __launch_bounds__(256) void quant_rows_kernel(const TS* __restrict__ src, fp8_t* __restrict__ q,
@@ -1267,22 +1267,6 @@ __global__ __launch_bounds__(256) void quant_rows_kernel(const TS* __restrict__ 
   }
 }
 
-__global__ __launch_bounds__(256) void dequant_rows_kernel(const fp8_t* __restrict__ q,
-                                                           const float* __restrict__ scale,
-                                                           bf16_t* __restrict__ dst, int64_t nchunks) {
-  const int64_t ch = blockIdx.x * int64_t(256) + threadIdx.x;
-  if (ch >= nchunks) return;
-  const u32x2 c = *reinterpret_cast<const u32x2*>(q + ch * 8);
-  const float s = scale[ch / 16];
-  float v[8] = {__builtin_amdgcn_cvt_f32_fp8(c[0], 0), __builtin_amdgcn_cvt_f32_fp8(c[0], 1),
-                __builtin_amdgcn_cvt_f32_fp8(c[0], 2), __builtin_amdgcn_cvt_f32_fp8(c[0], 3),
-                __builtin_amdgcn_cvt_f32_fp8(c[1], 0), __builtin_amdgcn_cvt_f32_fp8(c[1], 1),
-                __builtin_amdgcn_cvt_f32_fp8(c[1], 2), __builtin_amdgcn_cvt_f32_fp8(c[1], 3)};
-#pragma unroll
-  for (int i = 0; i < 8; ++i) v[i] *= s;
-  Vec16<bf16_t>::store(dst + ch * 8, v);
-}
-
 void launch_quant_rows(const void* src, bool src_bf16, int64_t rows, int64_t cols, uint8_t* q, float* scale,
                        hipStream_t st) {
   const int64_t nchunks = rows * cols / 8;
@@ -1292,13 +1276,6 @@ void launch_quant_rows(const void* src, bool src_bf16, int64_t rows, int64_t col
     quant_rows_kernel<bf16_t><<<grid, 256, 0, st>>>(reinterpret_cast<const bf16_t*>(src), q, scale, nchunks);
   else
     quant_rows_kernel<float><<<grid, 256, 0, st>>>(reinterpret_cast<const float*>(src), q, scale, nchunks);
-}
-
-static void dequant_rows(const uint8_t* q, const float* scale, int64_t rows, int64_t cols, bf16_t* dst,
-                         hipStream_t st) {
-  const int64_t nchunks = rows * cols / 8;
-  const int64_t grid = (nchunks + 255) / 256;
-  if (grid > 0) dequant_rows_kernel<<<grid, 256, 0, st>>>(q, scale, dst, nchunks);
 }
 
 // ---------------------------------------------------------------------------
@@ -1365,22 +1342,6 @@ __global__ __launch_bounds__(256) void quant_mx_cols_kernel(const TS* __restrict
   e8m0[br * C + c] = uint8_t(x + 127);
 }
 
-__global__ __launch_bounds__(256) void dequant_mx_rows_kernel(const fp8_t* __restrict__ q,
-                                                              const uint8_t* __restrict__ e8m0,
-                                                              bf16_t* __restrict__ dst, int64_t nchunks) {
-  const int64_t ch = blockIdx.x * int64_t(256) + threadIdx.x;
-  if (ch >= nchunks) return;
-  const u32x2 c = *reinterpret_cast<const u32x2*>(q + ch * 8);
-  const int x = int(e8m0[ch / 4]) - 127;
-  float v[8] = {__builtin_amdgcn_cvt_f32_fp8(c[0], 0), __builtin_amdgcn_cvt_f32_fp8(c[0], 1),
-                __builtin_amdgcn_cvt_f32_fp8(c[0], 2), __builtin_amdgcn_cvt_f32_fp8(c[0], 3),
-                __builtin_amdgcn_cvt_f32_fp8(c[1], 0), __builtin_amdgcn_cvt_f32_fp8(c[1], 1),
-                __builtin_amdgcn_cvt_f32_fp8(c[1], 2), __builtin_amdgcn_cvt_f32_fp8(c[1], 3)};
-#pragma unroll
-  for (int i = 0; i < 8; ++i) v[i] = ldexpf(v[i], x);
-  Vec16<bf16_t>::store(dst + ch * 8, v);
-}
-
 void launch_quant_mx_rows(const void* src, bool src_bf16, int64_t rows, int64_t cols, uint8_t* q,
                           uint8_t* e8m0, hipStream_t st) {
   const int64_t nchunks = rows * cols / 8;
@@ -1401,13 +1362,6 @@ void launch_quant_mx_cols(const void* src, bool src_bf16, int64_t rows, int64_t 
     quant_mx_cols_kernel<bf16_t><<<grid, 256, 0, st>>>(reinterpret_cast<const bf16_t*>(src), q, e8m0, cols, cb);
   else
     quant_mx_cols_kernel<float><<<grid, 256, 0, st>>>(reinterpret_cast<const float*>(src), q, e8m0, cols, cb);
-}
-
-static void dequant_mx_rows(const uint8_t* q, const uint8_t* e8m0, int64_t rows, int64_t cols, bf16_t* dst,
-                            hipStream_t st) {
-  const int64_t nchunks = rows * cols / 8;
-  const int64_t grid = (nchunks + 255) / 256;
-  if (grid > 0) dequant_mx_rows_kernel<<<grid, 256, 0, st>>>(q, e8m0, dst, nchunks);
 }
 
 // ---------------------------------------------------------------------------
@@ -1884,7 +1838,8 @@ static void gemm2_fwd(const FfnLaunch& a, const void* h, hipStream_t st) {
 }
 
 // FP8 GEMM1 (+ SwiGLU) into h16 (bf16), then H -> E4M3 per 1 x 128 block
-// (the second GEMM's A operand, and the weight gradient's after dequantising)
+// (the second GEMM's A operand; the weight gradient requantises it in token
+// blocks)
 template <typename C>
 static void gemm1_fwd_fp8(const FfnLaunch& a, void* gu, bf16_t* h16, uint8_t* hq, float* hs,
                           hipStream_t st) {
@@ -2091,15 +2046,16 @@ static void ffn_bwd_t(const FfnBwdLaunch& a, void* h_out, hipStream_t st) {
   }
 }
 
-// FP8 backward: the data-gradient GEMMs run in FP8 with their gradient
-// operand quantised per 1 x 128 block along the contraction dim and the
-// forward's 128 x 128 weight blocks; the weight gradients run in bf16 on the
-// dequantised forward operands (X, H) and the bf16 gradients. With h16 set
+// 8-bit backward: the data-gradient GEMMs run with their gradient operand
+// quantised in row blocks along the contraction dim (FP8: 1 x 128 with fp32
+// scales and the forward's 128 x 128 weight blocks; MXFP8 (MXF): 1 x 32 E8M0
+// blocks and the column-quantised weight copies, 32 x 1 blocks along these
+// products' contraction dims, that the caller passes as w1, w2). The weight
+// gradients take all four operands in token blocks inside each expert's rows
+// (FP8: 128-row x 1 with fp32 scales; MXFP8: 32-row x 1 E8M0 blocks, four to
+// a scale word), X and H requantised from their forward codes. With h16 set
 // (activation recompute) the dH epilogue rebuilds H in bf16 from the saved
 // GU and it is quantised as in the forward into a.act_h / a.h_scale.
-// MXFP8 (MXF): the same structure with 1 x 32 E8M0 blocks for the gradient
-// operands and, for the weights, the column-quantised copies (32 x 1 blocks
-// along these products' contraction dims) that the caller passes as w1, w2.
 // FP8 / MXFP8 data gradients: dH = Q(dO) W2 (+ SwiGLU backward from the
 // saved bf16 GU; H rebuilt into h16 unless null) and dX = Q(dGU) W1, on
 // tile configuration C.
