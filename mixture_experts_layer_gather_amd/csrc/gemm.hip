@@ -461,14 +461,14 @@ struct alignas(16) StageMx {
 };
 
 // The weight-gradient instances that run persistent runs of column tiles:
-// FP8 or MXFP8 operands (token-block scales), bf16 results. (bf16 operands on the
-// 128 x 128 tile were measured the same way and lost to the 128 x 256
-// three-stage tile on every bf16 layer but one product: Qwen3-style dW1
-// 0.95 -> 2.17 ms, Mixtral-style 2.15 -> 2.55 ms.)
+// FP8 or MXFP8 operands (token-block scales), or bf16 operands on the
+// two-stage 128 x 128 tile; bf16 results. (The host takes the bf16 one only
+// for experts of a few hundred rows: with long K the 128 x 256 three-stage
+// tile wins, Qwen3-style dW1 0.95 vs 2.17 ms, Mixtral-style 2.15 vs 2.55 ms.)
 template <typename T, typename TC, int MODE, int EPI, int NS>
 constexpr bool persistent_wgrad() {
   return MODE == G_KSPLIT && EPI == EPI_STORE && NS == 2 && sizeof(TC) == 2 &&
-         (std::is_same<T, fp8_t>::value || std::is_same<T, mx8_t>::value);
+         (std::is_same<T, fp8_t>::value || std::is_same<T, mx8_t>::value || std::is_same<T, bf16_t>::value);
 }
 
 template <typename T, typename TC, bool A_KMAJ, bool B_KMAJ, int MODE, int EPI, int BM, int BN,
@@ -1989,10 +1989,17 @@ static void wgrad_8bit(const fp8_t* dq, const void* ds, const fp8_t* hq, const v
   run(g4);
 }
 
+// bf16 weight gradients: experts of a few hundred rows (a few K steps per
+// tile, so each tile is mostly its result stores) take the persistent
+// column-tile runs of the 128 x 128 tile, whose next tile's loads overlap a
+// tile's stores; longer experts the 128 x 256 three-stage tile.
+static bool persist_wgrad_bf16(int tile, int64_t A, int64_t E) { return tile != 2 && A <= 256 * E; }
+
 template <typename TC16>
 static void wgrad_any(int tile, const void* d_out, const void* act_h, const void* d_gu, const void* x, void* dw1,
-                      void* dw2, const int32_t* offsets, int64_t d, int64_t f, int64_t E, hipStream_t st) {
-  if (big_wgrad(tile, d, f))
+                      void* dw2, const int32_t* offsets, int64_t A, int64_t d, int64_t f, int64_t E,
+                      hipStream_t st) {
+  if (!persist_wgrad_bf16(tile, A, E) && big_wgrad(tile, d, f))
     wgrad_t<WgradCfg, TC16>(d_out, act_h, d_gu, x, dw1, dw2, offsets, d, f, E, st);
   else
     wgrad_t<SmallCfg<bf16_t>, TC16>(d_out, act_h, d_gu, x, dw1, dw2, offsets, d, f, E, st);
@@ -2037,7 +2044,7 @@ static void ffn_bwd_t(const FfnBwdLaunch& a, void* h_out, hipStream_t st) {
     else dh_bwd<SmallCfg<bf16_t>>(a, d_gu, h_out, st);
     if (big_rows(a.tile, a.A, a.E, a.d)) dx_bwd<BigCfg>(a, d_gu, st);
     else dx_bwd<SmallCfg<bf16_t>>(a, d_gu, st);
-    wgrad_any<bf16_t>(a.tile, a.d_out, a.act_h, d_gu, a.x_perm, a.dw1, a.dw2, a.offsets, a.d, a.f, a.E, st);
+    wgrad_any<bf16_t>(a.tile, a.d_out, a.act_h, d_gu, a.x_perm, a.dw1, a.dw2, a.offsets, a.A, a.d, a.f, a.E, st);
   } else {
     dh_bwd<SmallCfg<float>>(a, d_gu, h_out, st);
     dx_bwd<SmallCfg<float>>(a, d_gu, st);

@@ -142,6 +142,12 @@ SMALL = {
     "deepseek_fp8_runs": S.mini(S.CONFIGS[4], T=1024, d=1152, f=512, E=64).replace(k=4, seed_base=36),
     "deepseek_fp8_runs_skew": S.mini(S.CONFIGS[4], T=1024, d=1152, f=512, E=64).replace(
         k=4, bias="zipf", seed_base=37),
+    # bf16 weight gradients of short experts (persistent runs of two
+    # 128 x 128 column tiles, the last run of each row block one tile short):
+    # even routing, and skewed routing with empty and multi-block experts
+    "deepseek_bf16_runs": S.mini(S.CONFIGS[2], T=1024, d=1152, f=512, E=64).replace(k=4, seed_base=44),
+    "deepseek_bf16_runs_skew": S.mini(S.CONFIGS[2], T=1024, d=1152, f=512, E=64).replace(
+        k=4, bias="zipf", seed_base=45),
     # the other group rule (a group's best score instead of its best two)
     # and sigmoid gates without renormalisation
     "deepseek_mini_gmax": S.mini(S.CONFIGS[2], T=300, d=256, f=256, E=32).replace(
