@@ -536,16 +536,18 @@ void gemm_kernel(GemmArgs g) {
     kcount = g.K;
   } else if constexpr (PERSIST) {
     // a run of up to tpw consecutive column tiles of one (group, row block);
-    // row blocks fastest, so that a super-block of workgroups shares its
-    // B column panel
+    // runs fastest, so that the workgroups running at once write
+    // neighbouring runs of the same rows: the write front covers whole rows
+    // instead of 256-byte pieces of many rows (row blocks fastest measured
+    // 6 % slower on dW1, FP8 and bf16)
     const int tpw = max(g.tpw, 1);
     const int nch = (g.tiles_n + tpw - 1) / tpw;
     const int per = g.tiles_m * nch;
     grp = tile / per;
     if (grp >= g.G) return;  // padding of the grid
     const int rem = tile % per;
-    mt = rem % g.tiles_m;
-    nt = (rem / g.tiles_m) * tpw;
+    nt = (rem % nch) * tpw;
+    mt = rem / nch;
     row0 = 0;
     mrows = BM;
     kbase = g.offsets[grp];
