@@ -1540,13 +1540,19 @@ static int64_t token_blocks_bound(int64_t A, int64_t G) { return (A + G * 127) /
 // columns 8 cg .. 8 cg + 7 of rows rg, rg + 16, ..., rg + 112 (rows rg + 16 i
 // lie in 32-row block i / 2); the block maxima meet in LDS. Sources: bf16
 // rows, or E4M3 codes with one E8M0 byte per 1 x 32 block of a row, taken as
-// code x 2^(byte - 127) in fp32.
-template <bool SRC_MX>
+// code x 2^(byte - 127) in fp32. ROWQ (bf16 sources): the same read also
+// quantises each row in 1 x 32 blocks (the data-gradient products'
+// operand, exactly as the row quantiser does), into rq [A, C] and re8m0
+// [A, C/32]: the four threads of a block (lanes 4 j .. 4 j + 3 of a 16-lane
+// group) reduce its amax with lane shuffles.
+template <bool SRC_MX, bool ROWQ>
 __global__ __launch_bounds__(256) void quant_tokens_mx_kernel(const void* __restrict__ src,
                                                               const uint8_t* __restrict__ src_e8m0,
                                                               const int32_t* __restrict__ offsets,
                                                               const int32_t* __restrict__ kblk, int G, int64_t C,
-                                                              fp8_t* __restrict__ q, uint32_t* __restrict__ words) {
+                                                              fp8_t* __restrict__ q, uint32_t* __restrict__ words,
+                                                              fp8_t* __restrict__ rq, uint8_t* __restrict__ re8m0) {
+  static_assert(!(SRC_MX && ROWQ), "row blocks are taken from bf16 sources");
   __shared__ __attribute__((aligned(16))) float s_max[16][4][132];  // 16-byte rows: float4 stores
   __shared__ int s_x[4][128];
   const int b = blockIdx.x;
@@ -1582,6 +1588,22 @@ __global__ __launch_bounds__(256) void quant_tokens_mx_kernel(const void* __rest
     } else {
 #pragma unroll
       for (int c = 0; c < 8; ++c) v[i][c] = 0.0f;
+    }
+  }
+  if constexpr (ROWQ) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int rr = rg + 16 * i;
+      float a = 0.0f;
+#pragma unroll
+      for (int c = 0; c < 8; ++c) a = fmaxf(a, fabsf(v[i][c]));
+      a = fmaxf(a, __shfl_xor(a, 1, kWave));
+      a = fmaxf(a, __shfl_xor(a, 2, kWave));
+      const int x = mx_scale_exp(a);
+      if (rr < nrows) {
+        *reinterpret_cast<u32x2*>(rq + (r0 + rr) * C + c0) = mx_codes8(v[i], x);
+        if ((cg & 3) == 0) re8m0[(r0 + rr) * (C / 32) + c0 / 32] = uint8_t(x + 127);
+      }
     }
   }
 #pragma unroll
@@ -1623,15 +1645,22 @@ __global__ __launch_bounds__(256) void quant_tokens_mx_kernel(const void* __rest
 
 // src [A, C] (bf16, or E4M3 codes with [A, C/32] E8M0 row-block bytes) ->
 // q [A, C] E4M3 and words [token_blocks_bound(A, G), C] (rows past the
-// actual block count are not written)
+// actual block count are not written); with rq (bf16 sources) also the
+// 1 x 32 row blocks rq [A, C], re8m0 [A, C/32] from the same read
 static void quant_tokens_mx(const void* src, const uint8_t* src_e8m0, const int32_t* offsets, const int32_t* kblk,
-                            int64_t G, int64_t A, int64_t C, fp8_t* q, uint32_t* words, hipStream_t st) {
+                            int64_t G, int64_t A, int64_t C, fp8_t* q, uint32_t* words, hipStream_t st,
+                            fp8_t* rq = nullptr, uint8_t* re8m0 = nullptr) {
   const dim3 grid(unsigned(token_blocks_bound(A, G)), unsigned(C / 128));
   if (grid.x == 0) return;
   if (src_e8m0)
-    quant_tokens_mx_kernel<true><<<grid, 256, 0, st>>>(src, src_e8m0, offsets, kblk, int(G), C, q, words);
+    quant_tokens_mx_kernel<true, false><<<grid, 256, 0, st>>>(src, src_e8m0, offsets, kblk, int(G), C, q, words,
+                                                             nullptr, nullptr);
+  else if (rq)
+    quant_tokens_mx_kernel<false, true><<<grid, 256, 0, st>>>(src, nullptr, offsets, kblk, int(G), C, q, words, rq,
+                                                             re8m0);
   else
-    quant_tokens_mx_kernel<false><<<grid, 256, 0, st>>>(src, nullptr, offsets, kblk, int(G), C, q, words);
+    quant_tokens_mx_kernel<false, false><<<grid, 256, 0, st>>>(src, nullptr, offsets, kblk, int(G), C, q, words,
+                                                              nullptr, nullptr);
 }
 
 // src [A, C] (bf16, or E4M3 codes with [A, C/128] fp32 row-block scales)
@@ -2119,10 +2148,10 @@ static void ffn_bwd_fp8(const FfnBwdLaunch& a, bf16_t* h16, hipStream_t st) {
   auto ts = [&](size_t o) { return reinterpret_cast<float*>(at(a.ws, o)); };
   auto tw = [&](size_t o) { return reinterpret_cast<uint32_t*>(at(a.ws, o)); };
   if constexpr (MXF) {
-    // dO: 1 x 32 row blocks (dH) and 32-row blocks (dW2)
+    // dO read once: its 1 x 32 row blocks (dH) and 32-row blocks (dW2)
     kblock_offsets_kernel<<<1, 1024, 0, st>>>(a.offsets, kblk, int(a.E));
-    quant(a.d_out, a.A, a.d, dq, ds);
-    quant_tokens_mx(a.d_out, nullptr, a.offsets, kblk, a.E, a.A, a.d, tq(w.t_do), tw(w.t_do_s), st);
+    quant_tokens_mx(a.d_out, nullptr, a.offsets, kblk, a.E, a.A, a.d, tq(w.t_do), tw(w.t_do_s), st, dq,
+                    reinterpret_cast<uint8_t*>(ds));
   } else {
     // dO read once: its 1 x 128 row blocks (dH) and 128-row blocks (dW2)
     kblock_offsets_kernel<<<1, 1024, 0, st>>>(a.offsets, kblk, int(a.E));
@@ -2140,8 +2169,8 @@ static void ffn_bwd_fp8(const FfnBwdLaunch& a, bf16_t* h16, hipStream_t st) {
   if (h16) quant(h16, a.A, a.f, static_cast<uint8_t*>(const_cast<void*>(a.act_h)), const_cast<float*>(a.h_scale));
   // dX = Q(dGU) W1
   if constexpr (MXF) {
-    quant(d_gu, a.A, 2 * a.f, gq, gs);
-    quant_tokens_mx(d_gu, nullptr, a.offsets, kblk, a.E, a.A, 2 * a.f, tq(w.t_gu), tw(w.t_gu_s), st);
+    quant_tokens_mx(d_gu, nullptr, a.offsets, kblk, a.E, a.A, 2 * a.f, tq(w.t_gu), tw(w.t_gu_s), st, gq,
+                    reinterpret_cast<uint8_t*>(gs));
   } else {
     quant_tokens(d_gu, nullptr, a.offsets, kblk, a.E, a.A, 2 * a.f, tq(w.t_gu), ts(w.t_gu_s), st, gq, gs);
   }
