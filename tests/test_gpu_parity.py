@@ -24,8 +24,26 @@ TOL = {"f32": 1e-5, "bf16": 2e-2, "fp8": 6e-2}
 DEV = "cuda"
 
 
+_CAPMAN = None
+
+
+@pytest.fixture(autouse=True)
+def _progress_to_terminal(request):
+    """Lets _say reach the terminal while pytest captures output: the full-
+    size tests run their CPU oracle for minutes, and a run that prints
+    nothing for that long looks hung."""
+    global _CAPMAN
+    _CAPMAN = request.config.pluginmanager.getplugin("capturemanager")
+    yield
+    _CAPMAN = None
+
+
 def _say(msg):
-    print(msg, flush=True)
+    if _CAPMAN is not None:
+        with _CAPMAN.global_and_fixture_disabled():
+            print(msg, flush=True)
+    else:
+        print(msg, flush=True)
     sys.stdout.flush()
 
 
