@@ -1397,24 +1397,21 @@ __global__ __launch_bounds__(1024) void kblock_offsets_kernel(const int32_t* __r
 // 8 cg .. 8 cg + 7 of rows rg, rg + 16, ..., rg + 112 of the block in
 // registers; the column maxima meet in LDS, where 128 threads turn them into
 // the column scales and their reciprocals once (a division each), for every
-// thread to read. Sources: bf16 rows (SRC_FP8 = false) or E4M3 codes with
-// fp32 scales per 1 x 128 block of a row, taken as float(code) * scale in
-// fp32. ROWQ (bf16 sources): the same read also quantises each row's 128
-// columns as one 1 x 128 block (the data-gradient products' operand), into
-// rq / rs [A, C/128]. The 16 threads holding rows rg + 16 i (one 16-lane
+// thread to read. Sources: bf16 rows (E4M3 sources take
+// quant_tokens_f8src_kernel). ROWQ: the same read also quantises each row's
+// 128 columns as one 1 x 128 block (the data-gradient products' operand),
+// into rq / rs [A, C/128]. The 16 threads holding rows rg + 16 i (one 16-lane
 // group of a wave) reduce their 8 row maxima by a transposing butterfly:
 // each exchange step halves the rows a lane keeps, so after four steps lane
 // cg holds the whole maximum of row cg / 2, divides once, and the row scales
 // go back to the group by lane broadcasts.
-template <bool SRC_FP8, bool ROWQ>
-__global__ __launch_bounds__(256) void quant_tokens_kernel(const void* __restrict__ src,
-                                                           const float* __restrict__ src_scale,
+template <bool ROWQ>
+__global__ __launch_bounds__(256) void quant_tokens_kernel(const bf16_t* __restrict__ src,
                                                            const int32_t* __restrict__ offsets,
                                                            const int32_t* __restrict__ kblk, int G,
                                                            int64_t C, fp8_t* __restrict__ q,
                                                            float* __restrict__ scale, fp8_t* __restrict__ rq,
                                                            float* __restrict__ rs) {
-  static_assert(!(SRC_FP8 && ROWQ), "row blocks are taken from bf16 sources");
   __shared__ float s_max[16][129];
   __shared__ float s_sc[128], s_rc[128];
   __shared__ int s_fast[128];
@@ -1439,19 +1436,7 @@ __global__ __launch_bounds__(256) void quant_tokens_kernel(const void* __restric
   for (int i = 0; i < 8; ++i) {
     const int rr = rg + 16 * i;
     if (rr < nrows) {
-      const int64_t off = (r0 + rr) * C + c0;
-      if constexpr (SRC_FP8) {
-        const u32x2 w = *reinterpret_cast<const u32x2*>(static_cast<const fp8_t*>(src) + off);
-        const float sc = src_scale[(r0 + rr) * (C / 128) + c0 / 128];
-        const float f8[8] = {__builtin_amdgcn_cvt_f32_fp8(w[0], 0), __builtin_amdgcn_cvt_f32_fp8(w[0], 1),
-                             __builtin_amdgcn_cvt_f32_fp8(w[0], 2), __builtin_amdgcn_cvt_f32_fp8(w[0], 3),
-                             __builtin_amdgcn_cvt_f32_fp8(w[1], 0), __builtin_amdgcn_cvt_f32_fp8(w[1], 1),
-                             __builtin_amdgcn_cvt_f32_fp8(w[1], 2), __builtin_amdgcn_cvt_f32_fp8(w[1], 3)};
-#pragma unroll
-        for (int c = 0; c < 8; ++c) v[i][c] = f8[c] * sc;
-      } else {
-        Vec16<bf16_t>::load(static_cast<const bf16_t*>(src) + off, v[i]);
-      }
+      Vec16<bf16_t>::load(src + (r0 + rr) * C + c0, v[i]);
     } else {
 #pragma unroll
       for (int c = 0; c < 8; ++c) v[i][c] = 0.0f;
@@ -1524,6 +1509,89 @@ __global__ __launch_bounds__(256) void quant_tokens_kernel(const void* __restric
   for (int i = 0; i < 8; ++i) {
     const int rr = rg + 16 * i;
     if (rr < nrows) *reinterpret_cast<u32x2*>(q + (r0 + rr) * C + c0) = fp8_encode8(v[i], sc, rc, fast);
+  }
+}
+
+// The same blocks from E4M3 sources (X and H, with fp32 scales per 1 x 128
+// block of a row), with 16-byte accesses: thread (cg, rg) holds columns
+// 16 cg .. 16 cg + 15 of rows rg, rg + 32, rg + 64, rg + 96 of the block;
+// the column maxima meet in LDS, where 128 threads turn them into the scales
+// and reciprocals. The arithmetic is quant_tokens_kernel's.
+__global__ __launch_bounds__(256) void quant_tokens_f8src_kernel(const fp8_t* __restrict__ src,
+                                                                 const float* __restrict__ src_scale,
+                                                                 const int32_t* __restrict__ offsets,
+                                                                 const int32_t* __restrict__ kblk, int G, int64_t C,
+                                                                 fp8_t* __restrict__ q, float* __restrict__ scale) {
+  __shared__ __attribute__((aligned(16))) float s_max[32][132];  // 16-byte rows: float4 stores
+  __shared__ __attribute__((aligned(16))) float s_sc[128];
+  __shared__ __attribute__((aligned(16))) float s_rc[128];
+  __shared__ int s_fast[128];
+  const int b = blockIdx.x;
+  if (b >= kblk[G]) return;
+  int lo = 0, hi = G - 1;  // the expert owning block b: the last e with kblk[e] <= b
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) / 2;
+    if (kblk[mid] <= b) lo = mid;
+    else hi = mid - 1;
+  }
+  const int64_t r0 = int64_t(offsets[lo]) + int64_t(b - kblk[lo]) * 128;
+  const int nrows = int(min(int64_t(128), int64_t(offsets[lo + 1]) - r0));
+  const int cg = threadIdx.x % 8, rg = threadIdx.x / 8;
+  const int64_t c0 = int64_t(blockIdx.y) * 128 + cg * 16;  // C is a multiple of 128
+  float v[4][16];
+  float m[16];
+#pragma unroll
+  for (int c = 0; c < 16; ++c) m[c] = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int rr = rg + 32 * i;
+    if (rr < nrows) {
+      const u32x4 w = *reinterpret_cast<const u32x4*>(src + (r0 + rr) * C + c0);
+      const float sc = src_scale[(r0 + rr) * (C / 128) + blockIdx.y];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        v[i][4 * k] = __builtin_amdgcn_cvt_f32_fp8(w[k], 0) * sc;
+        v[i][4 * k + 1] = __builtin_amdgcn_cvt_f32_fp8(w[k], 1) * sc;
+        v[i][4 * k + 2] = __builtin_amdgcn_cvt_f32_fp8(w[k], 2) * sc;
+        v[i][4 * k + 3] = __builtin_amdgcn_cvt_f32_fp8(w[k], 3) * sc;
+      }
+    } else {
+#pragma unroll
+      for (int c = 0; c < 16; ++c) v[i][c] = 0.0f;
+    }
+#pragma unroll
+    for (int c = 0; c < 16; ++c) m[c] = fmaxf(m[c], fabsf(v[i][c]));
+  }
+#pragma unroll
+  for (int c = 0; c < 16; c += 4)
+    *reinterpret_cast<float4*>(&s_max[rg][cg * 16 + c]) = float4{m[c], m[c + 1], m[c + 2], m[c + 3]};
+  __syncthreads();
+  if (threadIdx.x < 128) {  // waves 0 and 1: one column each
+    const int col = threadIdx.x;
+    float a = 0.0f;
+#pragma unroll
+    for (int r = 0; r < 32; ++r) a = fmaxf(a, s_max[r][col]);
+    const float scol = (a == 0.0f) ? 1.0f : a / 448.0f;
+    s_sc[col] = scol;
+    s_rc[col] = 1.0f / scol;
+    s_fast[col] = fp8_fast_scale(scol) ? 1 : 0;
+    scale[int64_t(b) * C + int64_t(blockIdx.y) * 128 + col] = scol;
+  }
+  __syncthreads();
+  float sc[16], rc[16];
+  bool fast = true;
+#pragma unroll
+  for (int c = 0; c < 16; ++c) {
+    sc[c] = s_sc[cg * 16 + c];
+    rc[c] = s_rc[cg * 16 + c];
+    fast = fast && s_fast[cg * 16 + c] != 0;
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int rr = rg + 32 * i;
+    const u32x2 lo8 = fp8_encode8(v[i], sc, rc, fast);
+    const u32x2 hi8 = fp8_encode8(v[i] + 8, sc + 8, rc + 8, fast);
+    if (rr < nrows) *reinterpret_cast<u32x4*>(q + (r0 + rr) * C + c0) = u32x4{lo8[0], lo8[1], hi8[0], hi8[1]};
   }
 }
 
@@ -1673,14 +1741,14 @@ static void quant_tokens(const void* src, const float* src_scale, const int32_t*
   const dim3 grid(unsigned(token_blocks_bound(A, G)), unsigned(C / 128));
   if (grid.x == 0) return;
   if (src_scale)
-    quant_tokens_kernel<true, false><<<grid, 256, 0, st>>>(src, src_scale, offsets, kblk, int(G), C, q, scale,
-                                                          nullptr, nullptr);
+    quant_tokens_f8src_kernel<<<grid, 256, 0, st>>>(static_cast<const fp8_t*>(src), src_scale, offsets, kblk,
+                                                    int(G), C, q, scale);
   else if (rq)
-    quant_tokens_kernel<false, true><<<grid, 256, 0, st>>>(src, nullptr, offsets, kblk, int(G), C, q, scale, rq,
-                                                          rs);
+    quant_tokens_kernel<true><<<grid, 256, 0, st>>>(static_cast<const bf16_t*>(src), offsets, kblk, int(G), C, q,
+                                                    scale, rq, rs);
   else
-    quant_tokens_kernel<false, false><<<grid, 256, 0, st>>>(src, nullptr, offsets, kblk, int(G), C, q, scale,
-                                                           nullptr, nullptr);
+    quant_tokens_kernel<false><<<grid, 256, 0, st>>>(static_cast<const bf16_t*>(src), offsets, kblk, int(G), C, q,
+                                                     scale, nullptr, nullptr);
 }
 
 // ---------------------------------------------------------------------------
