@@ -166,6 +166,15 @@ SMALL = {
     "deepseek_bf16_runs": S.mini(S.CONFIGS[2], T=1024, d=1152, f=512, E=64).replace(k=4, seed_base=44),
     "deepseek_bf16_runs_skew": S.mini(S.CONFIGS[2], T=1024, d=1152, f=512, E=64).replace(
         k=4, bias="zipf", seed_base=45),
+    # 8-bit layers whose experts average 256 rows (more than 128, at most
+    # 320): the 160 x 128 tile; even and skewed routing (experts of one to
+    # several row tiles, empty experts), FP8 and MXFP8
+    "deepseek_fp8_mid": S.mini(S.CONFIGS[4], T=1024, d=384, f=256, E=16).replace(
+        k=4, num_groups=4, topk_groups=2, seed_base=46),
+    "deepseek_fp8_mid_skew": S.mini(S.CONFIGS[4], T=1024, d=384, f=256, E=16).replace(
+        k=4, num_groups=4, topk_groups=2, bias="zipf", seed_base=47),
+    "deepseek_mxfp8_mid": S.mini(S.BY_NAME["deepseek_v3_mxfp8"], T=1024, d=384, f=256, E=16).replace(
+        k=4, num_groups=4, topk_groups=2, seed_base=48),
     # the other group rule (a group's best score instead of its best two)
     # and sigmoid gates without renormalisation
     "deepseek_mini_gmax": S.mini(S.CONFIGS[2], T=300, d=256, f=256, E=32).replace(
