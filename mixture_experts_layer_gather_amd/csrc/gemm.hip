@@ -1782,6 +1782,8 @@ template <> struct SmallCfg<mx8_t> : Cfg<mx8_t, 128, 128, 128, 2, 2, 2> {};
 // tiles cover up to 320 rows where the 128-row tile needs three, the last
 // often a few rows that still stream the whole weight panel
 template <typename T> using MidCfg8 = Cfg<T, 160, 128, 128, 2, 2, 2>;
+// bf16 160 x 128 tile (BK 64, two 36 KB stages), for the same experts
+typedef Cfg<bf16_t, 160, 128, 64, 2, 2, 2> MidCfg16;
 typedef Cfg<bf16_t, 256, 256, 64, 2, 4, 2> BigCfg;
 // FP8 / MXFP8 256 x 256 tile: 8 waves of 128 x 64, BK 128, two 64 KB stages
 // (one workgroup per CU), the byte layout of the bf16 Big tile
@@ -1823,11 +1825,13 @@ static bool big_rows(int tile, int64_t A, int64_t E, int64_t n_dim) {
 // FP8 row-grouped GEMMs: the 256 x 256 tile only when forced (MOE_TILE_BIG)
 // and the width allows.
 static bool big8(int tile, int64_t n_dim) { return tile == 2 && n_dim % 256 == 0; }
-// ... the 160-row tile when experts average more than 128 and at most 320
-// rows (measured on the FP8 DeepSeek-V3-style layer, 256 rows per expert:
-// GEMM1 3.39 -> 3.26 ms, GEMM2 1.97 -> 1.87, dH 1.87 -> 1.76, dX 3.48 ->
-// 3.29; a dense group of 8,192 rows lost 8 % on GEMM1 with it)
-static bool mid8(int tile, int64_t A, int64_t E) { return tile == 0 && A > 128 * E && A <= 320 * E; }
+// The 160-row tile (FP8, MXFP8 and bf16 row-grouped GEMMs) when experts
+// average 120 to 320 rows: one row tile for experts of up to 160 rows, two
+// up to 320, where the 128-row tile often needs one more for a few rows
+// (measured on the FP8 DeepSeek-V3-style layer, 256 rows per expert:
+// GEMM1 3.34 -> 3.13 ms, GEMM2 1.95 -> 1.79, dH 1.86 -> 1.73, dX 3.40 ->
+// 3.22; a dense group of 8,192 rows lost 8 % on GEMM1 with it)
+static bool mid8(int tile, int64_t A, int64_t E) { return tile == 0 && A >= 120 * E && A <= 320 * E; }
 // Weight gradients tile the (M, N) = weight shape of every expert, whatever
 // its rows: the big tile whenever the weight shape allows.
 static bool big_wgrad(int tile, int64_t d, int64_t f) { return tile != 1 && d % 256 == 0 && f % 256 == 0; }
@@ -2028,6 +2032,7 @@ static void ffn_fwd_gu_h(const FfnLaunch& a, void* gu, void* h, float* hs, bf16_
     else gemm1_fwd_fp8<SmallCfg<fp8_t>>(a, gu, h16, static_cast<uint8_t*>(h), hs, st);
   } else if (a.wt == 1) {
     if (big_rows(a.tile, a.A, a.E, 2 * a.f)) gemm1_fwd<BigCfg>(a, gu, h, st);
+    else if (mid8(a.tile, a.A, a.E)) gemm1_fwd<MidCfg16>(a, gu, h, st);
     else gemm1_fwd<SmallCfg<bf16_t>>(a, gu, h, st);
   } else {
     gemm1_fwd<SmallCfg<float>>(a, gu, h, st);
@@ -2157,8 +2162,10 @@ static void ffn_bwd_t(const FfnBwdLaunch& a, void* h_out, hipStream_t st) {
   void* d_gu = at(a.ws, w.d_gu);
   if constexpr (sizeof(T) == 2) {
     if (big_rows(a.tile, a.A, a.E, a.f)) dh_bwd<BigCfg>(a, d_gu, h_out, st);
+    else if (mid8(a.tile, a.A, a.E)) dh_bwd<MidCfg16>(a, d_gu, h_out, st);
     else dh_bwd<SmallCfg<bf16_t>>(a, d_gu, h_out, st);
     if (big_rows(a.tile, a.A, a.E, a.d)) dx_bwd<BigCfg>(a, d_gu, st);
+    else if (mid8(a.tile, a.A, a.E)) dx_bwd<MidCfg16>(a, d_gu, st);
     else dx_bwd<SmallCfg<bf16_t>>(a, d_gu, st);
     wgrad_any<bf16_t>(a.tile, a.d_out, a.act_h, d_gu, a.x_perm, a.dw1, a.dw2, a.offsets, a.A, a.d, a.f, a.E, st);
   } else {
@@ -2310,6 +2317,7 @@ void launch_grouped_ffn(const FfnLaunch& a, hipStream_t st) {
     else gemm2_fwd_fp8<SmallCfg<fp8_t>>(a, static_cast<const uint8_t*>(h), hs, st);
   } else if (a.wt == 1) {
     if (big_rows(a.tile, a.A, a.E, a.d)) gemm2_fwd<BigCfg>(a, h, st);
+    else if (mid8(a.tile, a.A, a.E)) gemm2_fwd<MidCfg16>(a, h, st);
     else gemm2_fwd<SmallCfg<bf16_t>>(a, h, st);
   } else {
     gemm2_fwd<SmallCfg<float>>(a, h, st);
