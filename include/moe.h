@@ -186,6 +186,29 @@ int moe_dispatch(const moe_config *cfg, const void *x, const int32_t *topk_idx,
                  int32_t *perm_token, void *x_perm, void *x_scale, void *ws,
                  size_t ws_bytes, void *stream);
 
+/* Route and dispatch in one call, with the dispatch histogram fused into the
+ * top-k selection (Megatron Core MoE summary, section 2.4: routing and
+ * permutation in fused kernels). Arguments, results and errors are those of
+ * moe_route followed by moe_dispatch on the same x and topk_idx, and every
+ * output is bit-identical to theirs. The difference is where the per-chunk
+ * expert histogram comes from: with E >= 128 the selection kernel counts
+ * each token's k experts into it as it picks them (integer atomics, whose
+ * order does not change the counts; the logits kernel clears it first), so
+ * the dispatch skips its own counting pass over topk_idx; with fewer
+ * experts that pass runs, as it is faster there (the atomics of few
+ * experts queue on a few cache lines). For routing replay (top-k indices
+ * from elsewhere) call moe_dispatch.
+ * Workspace: moe_workspace_size(cfg, MOE_OP_DISPATCH) bytes, as moe_dispatch;
+ * its contents are overwritten. Every argument is checked before anything is
+ * enqueued, so a refused call leaves every buffer untouched. T = 0: counts
+ * and offsets are zeroed, nothing else is touched. */
+int moe_route_dispatch(const moe_config *cfg, const void *x, const float *w_router,
+                       const float *expert_bias, float *logits, int32_t *topk_idx,
+                       float *topk_gate, uint8_t *routing_map, int32_t *counts,
+                       int32_t *offsets, int32_t *row_id_map, int32_t *perm_token,
+                       void *x_perm, void *x_scale, void *ws, size_t ws_bytes,
+                       void *stream);
+
 /* moe_dispatch for callers that cannot allocate device memory: code under
  * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.
  * Same arguments, results and errors as moe_dispatch, without ws/ws_bytes:

@@ -23,7 +23,7 @@ SCORE = {"softmax": 0, "sigmoid": 1}
 GROUP_SCORE = {"top2_sum": 0, "max": 1}
 OP_ROUTE, OP_DISPATCH, OP_GROUPED_FFN, OP_GROUPED_FFN_BWD, OP_ROUTE_BWD, OP_AUX_LOSS = range(6)
 
-EXPORTS = ["moe_workspace_size", "moe_route", "moe_dispatch", "moe_dispatch_scratch",
+EXPORTS = ["moe_workspace_size", "moe_route", "moe_dispatch", "moe_route_dispatch", "moe_dispatch_scratch",
            "moe_grouped_ffn", "moe_combine",
            "moe_combine_bwd", "moe_grouped_ffn_bwd", "moe_dispatch_bwd", "moe_route_bwd",
            "moe_route_aux_loss",
@@ -90,6 +90,7 @@ def lib():
             "moe_workspace_size": (sz, [C, ctypes.c_int]),
             "moe_route": (ctypes.c_int, [C, P, P, P, P, P, P, P, P, sz, P]),
             "moe_dispatch": (ctypes.c_int, [C, P, P, P, P, P, P, P, P, P, sz, P]),
+            "moe_route_dispatch": (ctypes.c_int, [C] + [P] * 14 + [sz, P]),
             "moe_dispatch_scratch": (ctypes.c_int, [C, P, P, P, P, P, P, P, P, P]),
             "moe_grouped_ffn": (ctypes.c_int, [C, P, P, P, P, P, P, P, P, P, P, P, P, sz, P]),
             "moe_combine": (ctypes.c_int, [C, P, P, P, P, P, P]),
@@ -151,6 +152,15 @@ def moe_dispatch(cfg, x, topk_idx, counts, offsets, row_id_map, perm_token, x_pe
                                               _p(offsets), _p(row_id_map), _p(perm_token),
                                               _p(x_perm), _p(x_scale), _p(ws), _nbytes(ws),
                                               _stream(stream)))
+
+
+def moe_route_dispatch(cfg, x, w_router, expert_bias, logits, topk_idx, topk_gate, routing_map,
+                       counts, offsets, row_id_map, perm_token, x_perm, x_scale=None, ws=None,
+                       stream=None):
+    _check("moe_route_dispatch", lib().moe_route_dispatch(
+        ctypes.byref(cfg), _p(x), _p(w_router), _p(expert_bias), _p(logits), _p(topk_idx),
+        _p(topk_gate), _p(routing_map), _p(counts), _p(offsets), _p(row_id_map), _p(perm_token),
+        _p(x_perm), _p(x_scale), _p(ws), _nbytes(ws), _stream(stream)))
 
 
 def moe_dispatch_scratch(cfg, x, topk_idx, counts, offsets, row_id_map, perm_token, x_perm,

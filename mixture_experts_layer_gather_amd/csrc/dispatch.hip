@@ -17,8 +17,6 @@
 
 namespace moe {
 
-constexpr int kChunkTok = 256;  // tokens per dispatch chunk (one per thread)
-
 int64_t dispatch_chunks(int64_t T) { return (T + kChunkTok - 1) / kChunkTok; }
 
 // --- 1. per-chunk expert histogram --------------------------------------
@@ -301,7 +299,8 @@ static int tokens_per_block(int64_t d, int vec) {
 void launch_dispatch(const DispatchLaunch& a, hipStream_t st) {
   const int T = int(a.T), E = int(a.E), k = int(a.k);
   const int nchunks = int(dispatch_chunks(a.T));
-  dispatch_count_kernel<<<nchunks, 256, sizeof(int32_t) * E, st>>>(a.idx, a.chunk_base, T, E, k);
+  if (!a.counted)
+    dispatch_count_kernel<<<nchunks, 256, sizeof(int32_t) * E, st>>>(a.idx, a.chunk_base, T, E, k);
   const size_t bits_lds = sizeof(uint32_t) * E * (kChunkTok / 32);
   if (nchunks <= kScanInPosChunks) {
     dispatch_pos_kernel<true><<<nchunks, 256, bits_lds + sizeof(int32_t) * E, st>>>(

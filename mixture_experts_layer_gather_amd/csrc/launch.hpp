@@ -7,6 +7,10 @@
 
 namespace moe {
 
+// Tokens per dispatch chunk: the dispatch ranks tokens inside chunks of this
+// many and keeps one expert histogram per chunk ([nchunks, E] i32).
+constexpr int kChunkTok = 256;
+
 struct RouteLaunch {
   const void* x;
   const float* w_router;
@@ -20,6 +24,10 @@ struct RouteLaunch {
   float gate_scale;
   int num_groups, topk_groups, group_score;
   bool act_bf16;
+  // fused route and dispatch: when set, the per-chunk expert histogram
+  // [ceil(T / kChunkTok), E] i32 of the selection (cleared by the logits
+  // kernel, counted by the selection kernel); nullptr otherwise
+  int32_t* chunk_cnt;
 };
 void launch_route_fwd(const RouteLaunch& r, hipStream_t st);
 
@@ -72,6 +80,7 @@ struct DispatchLaunch {
   void* x_perm;
   float* x_scale;        // fp8 only (mx: E8M0 bytes [T*k, d/32])
   int32_t* chunk_base;   // workspace [nchunks, E]
+  bool counted;          // chunk_base already holds the per-chunk expert counts (fused route)
   int64_t T, d, E, k;
   int act;               // 0 f32, 1 bf16
   bool fp8;

@@ -379,12 +379,23 @@ static void launch_rgemm(VArgs a, hipStream_t st, int zsplit = 1) {
 // ---------------------------------------------------------------------------
 constexpr int kLgTM = 64, kLgKC = 32, kLgP = kLgKC + 4;
 
+// Clears n ints of p (nothing when p is null), spread over the whole grid:
+// the logits kernels clear the fused route-and-dispatch histogram this way,
+// so that the selection kernel, next on the stream, can count into it.
+__device__ __forceinline__ void clear_grid_part(int32_t* p, int64_t n) {
+  if (!p) return;
+  const int64_t nb = int64_t(gridDim.x) * gridDim.y;
+  const int64_t b = int64_t(blockIdx.y) * gridDim.x + blockIdx.x;
+  for (int64_t i = b * 256 + threadIdx.x; i < n; i += nb * 256) p[i] = 0;
+}
+
 // TN = 64 experts per block, or 32 when 64 would leave fewer than two blocks
 // per CU (then a thread holds 4 x 2 recurrences)
 template <typename TX, int TN>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void logits_kernel(const TX* __restrict__ x, const float* __restrict__ w,
                                                      const float* __restrict__ bias, float* __restrict__ out,
-                                                     int T, int E, int d) {
+                                                     int T, int E, int d, int32_t* clr, int64_t nclr) {
+  clear_grid_part(clr, nclr);
   constexpr int FN = TN / 16;                  // expert columns per thread
   constexpr int WL = TN * kLgKC / 4 / 256;     // w loads per thread
   __shared__ __attribute__((aligned(16))) float As[2][kLgTM * kLgP];
@@ -504,7 +515,8 @@ constexpr int kSeKC = 256, kSeP = kSeKC + 4;
 template <typename TX, int EP>
 __global__ __launch_bounds__(256) void logits_small_e_kernel(const TX* __restrict__ x, const float* __restrict__ w,
                                                              const float* __restrict__ bias, float* __restrict__ out,
-                                                             int T, int E, int d) {
+                                                             int T, int E, int d, int32_t* clr, int64_t nclr) {
+  clear_grid_part(clr, nclr);
   constexpr int TPB = 256 / EP;  // tokens per block
   __shared__ __attribute__((aligned(16))) float Xs[2][TPB * kSeP];
   __shared__ __attribute__((aligned(16))) float Ws[2][EP * kSeP];
@@ -588,10 +600,14 @@ template <typename TX>
 static void launch_logits_small_e(const RouteLaunch& r, hipStream_t st) {
   const TX* x = reinterpret_cast<const TX*>(r.x);
   const int T = int(r.T), E = int(r.E), d = int(r.d);
+  const int64_t nclr = r.chunk_cnt ? (r.T + kChunkTok - 1) / kChunkTok * r.E : 0;
   auto grid = [&](int ep) { return dim3(unsigned((T + 256 / ep - 1) / (256 / ep))); };
-  if (E <= 8) logits_small_e_kernel<TX, 8><<<grid(8), 256, 0, st>>>(x, r.w_router, r.bias, r.logits, T, E, d);
-  else if (E <= 16) logits_small_e_kernel<TX, 16><<<grid(16), 256, 0, st>>>(x, r.w_router, r.bias, r.logits, T, E, d);
-  else logits_small_e_kernel<TX, 32><<<grid(32), 256, 0, st>>>(x, r.w_router, r.bias, r.logits, T, E, d);
+  if (E <= 8)
+    logits_small_e_kernel<TX, 8><<<grid(8), 256, 0, st>>>(x, r.w_router, r.bias, r.logits, T, E, d, r.chunk_cnt, nclr);
+  else if (E <= 16)
+    logits_small_e_kernel<TX, 16><<<grid(16), 256, 0, st>>>(x, r.w_router, r.bias, r.logits, T, E, d, r.chunk_cnt, nclr);
+  else
+    logits_small_e_kernel<TX, 32><<<grid(32), 256, 0, st>>>(x, r.w_router, r.bias, r.logits, T, E, d, r.chunk_cnt, nclr);
 }
 
 // Token-chunk count of the router weight gradient: enough workgroups to
@@ -650,6 +666,7 @@ struct SelArgs {
   int32_t* idx;
   float* gate;
   uint8_t* rmap;
+  int32_t* chunk_cnt;  // or null: the per-chunk expert histogram of the fused route and dispatch
 };
 
 template <int NPL>
@@ -781,6 +798,16 @@ __global__ __launch_bounds__(256) void select_kernel(SelArgs s) {
       s.idx[int64_t(t) * s.k + j] = sel_e[j];
       s.gate[int64_t(t) * s.k + j] = g[j];
     }
+  if (s.chunk_cnt) {
+    // the dispatch histogram, fused into the selection: lane j < k adds the
+    // token's j-th expert to its chunk's count (integer atomics: the result
+    // does not depend on their order; the logits kernel cleared the counts)
+    int mine_e = 0;
+#pragma unroll
+    for (int j = 0; j < kMaxK; ++j)
+      if (lane == j) mine_e = sel_e[j];
+    if (lane < s.k) atomicAdd(&s.chunk_cnt[int64_t(t / kChunkTok) * s.E + mine_e], 1);
+  }
   if (s.rmap) {
 #pragma unroll
     for (int p = 0; p < NPL; ++p) {
@@ -1117,12 +1144,15 @@ static void route_fwd_t(const RouteLaunch& r, hipStream_t st) {
   if (r.E >= 32) {
     const unsigned gy = unsigned((r.T + kLgTM - 1) / kLgTM);
     const int64_t blocks64 = int64_t((r.E + 63) / 64) * gy;
+    const int64_t nclr = r.chunk_cnt ? (r.T + kChunkTok - 1) / kChunkTok * r.E : 0;
     if (blocks64 >= 512)
       logits_kernel<TX, 64><<<dim3(unsigned((r.E + 63) / 64), gy), 256, 0, st>>>(
-          reinterpret_cast<const TX*>(r.x), r.w_router, r.bias, r.logits, int(r.T), int(r.E), int(r.d));
+          reinterpret_cast<const TX*>(r.x), r.w_router, r.bias, r.logits, int(r.T), int(r.E), int(r.d),
+          r.chunk_cnt, nclr);
     else
       logits_kernel<TX, 32><<<dim3(unsigned((r.E + 31) / 32), gy), 256, 0, st>>>(
-          reinterpret_cast<const TX*>(r.x), r.w_router, r.bias, r.logits, int(r.T), int(r.E), int(r.d));
+          reinterpret_cast<const TX*>(r.x), r.w_router, r.bias, r.logits, int(r.T), int(r.E), int(r.d),
+          r.chunk_cnt, nclr);
   } else {
     launch_logits_small_e<TX>(r, st);
   }
@@ -1131,7 +1161,7 @@ static void route_fwd_t(const RouteLaunch& r, hipStream_t st) {
   s.logits = r.logits; s.T = int(r.T); s.E = int(r.E); s.k = int(r.k);
   s.score_fn = r.score_fn; s.renorm = r.renorm; s.gate_scale = r.gate_scale;
   s.num_groups = r.num_groups; s.topk_groups = r.topk_groups; s.group_score = r.group_score;
-  s.idx = r.idx; s.gate = r.gate; s.rmap = r.rmap;
+  s.idx = r.idx; s.gate = r.gate; s.rmap = r.rmap; s.chunk_cnt = r.chunk_cnt;
   const dim3 grid((r.T + 3) / 4);
   if (r.E <= 64) select_kernel<1><<<grid, 256, 0, st>>>(s);
   else if (r.E <= 128) select_kernel<2><<<grid, 256, 0, st>>>(s);

@@ -27,7 +27,7 @@ def _declared():
 
 def test_exports_every_declared_symbol(M):
     names = _declared()
-    assert len(names) == 14, names
+    assert len(names) == 15, names
     L = M.lib()
     for n in names:
         assert hasattr(L, n), n
@@ -108,6 +108,27 @@ def test_dispatch_scratch_refusals(M):
     assert L.moe_dispatch_scratch(ctypes.byref(big), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, N, N) == -4
     assert L.moe_dispatch_scratch(ctypes.byref(_cfg(M, k=9)), *([FAKE] * 7), N, N) == -1
     assert L.moe_dispatch_scratch(ctypes.byref(_cfg(M, T=0)), N, N, N, FAKE, N, N, N, N, N) == -1
+
+
+def test_route_dispatch_refusals(M):
+    """The fused route and dispatch checks the arguments of both calls before
+    it enqueues either: a bad dispatch argument leaves the routing outputs
+    untouched too."""
+    L = M.lib()
+    N = None
+    c = _cfg(M)
+    need = L.moe_workspace_size(ctypes.byref(c), 1)
+
+    def rd(cfg, x=FAKE, w=FAKE, x_scale=None, ws=FAKE, nbytes=need, counts=FAKE):
+        return L.moe_route_dispatch(ctypes.byref(cfg), x, w, N, FAKE, FAKE, FAKE, N, counts, FAKE,
+                                    FAKE, FAKE, FAKE, x_scale, ws, nbytes, N)
+    assert rd(c, ws=None, nbytes=0) == -4          # dispatch workspace missing
+    assert rd(c, nbytes=need - 1) == -4            # ... or short
+    assert rd(c, w=None) == -1                     # route argument
+    assert rd(c, x=FAKE + 4) == -3                 # alignment
+    assert rd(_cfg(M, weight="fp8")) == -1         # fp8 needs the scale output
+    assert rd(_cfg(M, k=9)) == -1                  # configuration
+    assert rd(_cfg(M, T=0), x=None, w=None, ws=None, nbytes=0, counts=None) == -1  # zeros to write
 
 
 def test_empty_batch_enqueues_nothing(M):

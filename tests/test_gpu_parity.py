@@ -515,6 +515,82 @@ def test_dispatch_index_paths(T, E, k, skew):
     assert np.array_equal(got, oracle.permute(x.view(torch.int16).numpy(), rmap))
 
 
+# (name, base layer, T, d, E, k): the fused route and dispatch, its histogram
+# counted by the selection (E >= 128: up to the 1024-expert, top-16 limit)
+# and by the dispatch's own pass (fewer experts); both logits kernel
+# families (E <= 32, and 32 / 64 experts per workgroup), up to 32 chunks of
+# 256 tokens (bases derived in the positions kernel) and beyond (separate
+# scan), ragged last chunks, group-limited sigmoid routing, and the FP8 and
+# MXFP8 gathers
+ROUTE_DISPATCH_CASES = [("qwen3_skew_bf16", 3000, 256, 8, 2), ("qwen3_skew_bf16", 8192, 256, 72, 4),
+                        ("qwen3_skew_bf16", 16384, 256, 128, 8), ("qwen3_skew_bf16", 2000, 128, 1024, 16),
+                        ("deepseek_v3_bf16", 1000, 256, 256, 8), ("deepseek_v3_bf16", 9000, 256, 128, 8),
+                        ("deepseek_v3_fp8", 300, 512, 256, 4), ("deepseek_v3_mxfp8", 777, 256, 128, 8),
+                        ("deepseek_v3_mxfp8", 500, 256, 64, 8), ("tiny_fp32", 257, 128, 5, 5)]
+
+
+@pytest.mark.parametrize("name,T,d,E,k", ROUTE_DISPATCH_CASES)
+def test_route_dispatch_fused(name, T, d, E, k):
+    """moe_route_dispatch (the dispatch histogram counted by the top-k
+    selection) against the oracle's router and dispatch, every output bit
+    for bit (gates to 1e-6); run twice on one workspace, so the second call
+    must clear the counts the first left there."""
+    from mixture_experts_layer_gather_amd import make_config, moe_route_dispatch, workspace_size
+    cfg = S.mini(S.BY_NAME[name], T=T, d=d, f=128, E=E).replace(k=k)
+    _say(f"[route+dispatch] {name} T={T} d={d} E={E} k={k}")
+    x, wr = S.x(cfg), S.w_router(cfg)
+    bias = S.router_bias(cfg)
+    L, idx, gates = oracle.route(cfg, x, wr, bias)
+    counts, offsets, rmap, ptok = oracle.dispatch_index(idx, E)
+    c = make_config(**cfg.describe())
+    A = T * k
+    fp8, mx = cfg.weight == "fp8", cfg.weight == "mxfp8"
+    xs32 = oracle.as_f32(x)
+    if fp8:
+        xq, xsc = oracle.quant_blocks(xs32, 1, 128)
+    elif mx:
+        xq, xsc = oracle.quant_mx_rows(xs32)
+    out = dict(logits=torch.empty(T, E, dtype=torch.float32, device=DEV),
+               idx=torch.empty(T, k, dtype=torch.int32, device=DEV),
+               gate=torch.empty(T, k, dtype=torch.float32, device=DEV),
+               rmapu8=torch.empty(T, E, dtype=torch.uint8, device=DEV),
+               counts=torch.empty(E, dtype=torch.int32, device=DEV),
+               offsets=torch.empty(E + 1, dtype=torch.int32, device=DEV),
+               rmap=torch.empty(T, k, dtype=torch.int32, device=DEV),
+               ptok=torch.empty(A, dtype=torch.int32, device=DEV))
+    if fp8 or mx:
+        out["xp"] = torch.empty(A, d, dtype=torch.uint8, device=DEV)
+        out["xs"] = (torch.empty(A, d // 128, dtype=torch.float32, device=DEV) if fp8
+                     else torch.empty(A, d // 32, dtype=torch.uint8, device=DEV))
+    else:
+        out["xp"] = torch.empty(A, d, dtype=x.dtype, device=DEV)
+        out["xs"] = None
+    ws = torch.empty(workspace_size(c, 1), dtype=torch.uint8, device=DEV)
+    xd, wd = x.to(DEV), wr.to(DEV)
+    bd = None if bias is None else bias.to(DEV)
+    for rep in range(2):
+        moe_route_dispatch(c, xd, wd, bd, out["logits"], out["idx"], out["gate"], out["rmapu8"],
+                           out["counts"], out["offsets"], out["rmap"], out["ptok"], out["xp"], out["xs"], ws)
+        torch.cuda.synchronize()
+        assert np.array_equal(_np(out["logits"]), L), rep
+        assert np.array_equal(_np(out["idx"]), idx), rep
+        assert oracle.rel_l2(_np(out["gate"]), gates) <= 1e-6, rep
+        want_map = np.zeros((T, E), dtype=np.uint8)
+        np.put_along_axis(want_map, idx.astype(np.int64), 1, axis=1)
+        assert np.array_equal(_np(out["rmapu8"]), want_map), rep
+        assert np.array_equal(_np(out["counts"]), counts), rep
+        assert np.array_equal(_np(out["offsets"]), offsets), rep
+        assert np.array_equal(_np(out["rmap"]), rmap), rep
+        assert np.array_equal(_np(out["ptok"]), ptok), rep
+        if fp8 or mx:
+            assert np.array_equal(_np(out["xp"]), oracle.permute(xq, rmap)), rep
+            assert np.array_equal(_np(out["xs"]), oracle.permute(xsc, rmap)), rep
+        else:
+            isz = torch.int16 if x.dtype == torch.bfloat16 else torch.int32
+            got = out["xp"].view(isz).cpu().numpy()
+            assert np.array_equal(got, oracle.permute(x.view(isz).numpy(), rmap)), rep
+
+
 # ------------------------------------------------------------ full sizes
 
 class _L2:
