@@ -526,7 +526,8 @@ ROUTE_DISPATCH_CASES = [("qwen3_skew_bf16", 3000, 256, 8, 2), ("qwen3_skew_bf16"
                         ("qwen3_skew_bf16", 16384, 256, 128, 8), ("qwen3_skew_bf16", 2000, 128, 1024, 16),
                         ("deepseek_v3_bf16", 1000, 256, 256, 8), ("deepseek_v3_bf16", 9000, 256, 128, 8),
                         ("deepseek_v3_fp8", 300, 512, 256, 4), ("deepseek_v3_mxfp8", 777, 256, 128, 8),
-                        ("deepseek_v3_mxfp8", 500, 256, 64, 8), ("tiny_fp32", 257, 128, 5, 5)]
+                        ("deepseek_v3_mxfp8", 500, 256, 64, 8), ("tiny_fp32", 257, 128, 5, 5),
+                        ("deepseek_v3_fp8", 8192, 7168, 256, 8)]  # the full FP8 DeepSeek-style layer
 
 
 @pytest.mark.parametrize("name,T,d,E,k", ROUTE_DISPATCH_CASES)
