@@ -592,6 +592,77 @@ def test_route_dispatch_fused(name, T, d, E, k):
             assert np.array_equal(got, oracle.permute(x.view(isz).numpy(), rmap)), rep
 
 
+def test_route_dispatch_graph_replay():
+    """moe_route_dispatch captured into a HIP graph (the histogram is cleared
+    by a kernel, so the graph holds no memset): every replay, after its
+    outputs were scribbled over, equals the eager call bit for bit, also
+    after an input that routes differently is copied into the captured
+    buffer."""
+    from mixture_experts_layer_gather_amd import make_config, moe_route_dispatch, workspace_size
+    cfg = S.mini(S.BY_NAME["deepseek_v3_fp8"], T=1500, d=256, f=128, E=128).replace(k=8)
+    _say("[route+dispatch graph] deepseek_v3_fp8 T=1500 d=256 E=128 k=8")
+    c = make_config(**cfg.describe())
+    T, d, E, k, A = cfg.T, cfg.d, cfg.E, cfg.k, cfg.T * cfg.k
+    wr = S.w_router(cfg).to(DEV)
+    bias = S.router_bias(cfg)
+    bias = None if bias is None else bias.to(DEV)
+    x = S.x(cfg).to(DEV)
+    x2 = S.x(cfg.replace(seed_base=cfg.seed_base + 101)).to(DEV)
+    names = ("logits", "idx", "gate", "counts", "offsets", "rmap", "ptok", "xp", "xs")
+    out = dict(logits=torch.empty(T, E, dtype=torch.float32, device=DEV),
+               idx=torch.empty(T, k, dtype=torch.int32, device=DEV),
+               gate=torch.empty(T, k, dtype=torch.float32, device=DEV),
+               counts=torch.empty(E, dtype=torch.int32, device=DEV),
+               offsets=torch.empty(E + 1, dtype=torch.int32, device=DEV),
+               rmap=torch.empty(T, k, dtype=torch.int32, device=DEV),
+               ptok=torch.empty(A, dtype=torch.int32, device=DEV),
+               xp=torch.empty(A, d, dtype=torch.uint8, device=DEV),
+               xs=torch.empty(A, d // 128, dtype=torch.float32, device=DEV))
+    ws = torch.empty(workspace_size(c, 1), dtype=torch.uint8, device=DEV)
+    xin = x.clone()  # the captured input buffer
+
+    def call():
+        moe_route_dispatch(c, xin, wr, bias, out["logits"], out["idx"], out["gate"], None, out["counts"],
+                           out["offsets"], out["rmap"], out["ptok"], out["xp"], out["xs"], ws)
+
+    def snapshot():
+        torch.cuda.synchronize()
+        return {n: out[n].clone() for n in names}
+
+    def scribble():
+        for n in names:
+            out[n].view(torch.uint8).fill_(0xAB)
+        ws.fill_(0x5A)
+
+    call()
+    eager1 = snapshot()
+    xin.copy_(x2)
+    call()
+    eager2 = snapshot()
+    assert not torch.equal(eager1["counts"], eager2["counts"]), "the second input should route differently"
+    xin.copy_(x)
+    g = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        call()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g):
+        call()
+    torch.cuda.synchronize()
+    for want, tag in ((eager1, "first input"), (eager2, "second input")):
+        if tag == "second input":
+            xin.copy_(x2)
+        for rep in range(3):
+            scribble()
+            torch.cuda.synchronize()
+            g.replay()
+            got = snapshot()
+            for n in names:
+                assert torch.equal(got[n].view(torch.uint8), want[n].view(torch.uint8)), f"{tag} replay {rep}: {n}"
+
+
 # ------------------------------------------------------------ full sizes
 
 class _L2:
