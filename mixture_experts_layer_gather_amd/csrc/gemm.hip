@@ -1431,21 +1431,26 @@ __global__ __launch_bounds__(256) void quant_tokens_kernel(const bf16_t* __restr
   const int nrows = int(min(int64_t(128), int64_t(offsets[lo + 1]) - r0));
   const int cg = threadIdx.x % 16, rg = threadIdx.x / 16;
   const int64_t c0 = int64_t(blockIdx.y) * 128 + cg * 8;  // C is a multiple of 128
+  // All 8 row loads go out together: a row past the block reads the
+  // block's last row (nrows >= 1, so in bounds) and is zeroed after. (Under
+  // a per-row branch each load waited for its data before the next one.)
+  uint4 raw[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+    raw[i] = *reinterpret_cast<const uint4*>(src + (r0 + min(rg + 16 * i, nrows - 1)) * C + c0);
   float v[8][8];
   float m[8];
 #pragma unroll
   for (int c = 0; c < 8; ++c) m[c] = 0.0f;
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
-    const int rr = rg + 16 * i;
-    if (rr < nrows) {
-      Vec16<bf16_t>::load(src + (r0 + rr) * C + c0, v[i]);
-    } else {
+    Vec16<bf16_t>::unpack(raw[i], v[i]);
+    const bool in = rg + 16 * i < nrows;
 #pragma unroll
-      for (int c = 0; c < 8; ++c) v[i][c] = 0.0f;
+    for (int c = 0; c < 8; ++c) {
+      v[i][c] = in ? v[i][c] : 0.0f;
+      m[c] = fmaxf(m[c], fabsf(v[i][c]));
     }
-#pragma unroll
-    for (int c = 0; c < 8; ++c) m[c] = fmaxf(m[c], fabsf(v[i][c]));
   }
 #pragma unroll
   for (int c = 0; c < 8; ++c) s_max[rg][cg * 8 + c] = m[c];
@@ -1541,29 +1546,37 @@ __global__ __launch_bounds__(256) void quant_tokens_f8src_kernel(const fp8_t* __
   const int nrows = int(min(int64_t(128), int64_t(offsets[lo + 1]) - r0));
   const int cg = threadIdx.x % 8, rg = threadIdx.x / 8;
   const int64_t c0 = int64_t(blockIdx.y) * 128 + cg * 16;  // C is a multiple of 128
+  // all 4 row loads (codes and scale) go out together: a row past the
+  // block reads the block's last row (in bounds) and is zeroed after
+  u32x4 raw[4];
+  float rsc[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int64_t r = r0 + min(rg + 32 * i, nrows - 1);
+    raw[i] = *reinterpret_cast<const u32x4*>(src + r * C + c0);
+    rsc[i] = src_scale[r * (C / 128) + blockIdx.y];
+  }
   float v[4][16];
   float m[16];
 #pragma unroll
   for (int c = 0; c < 16; ++c) m[c] = 0.0f;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const int rr = rg + 32 * i;
-    if (rr < nrows) {
-      const u32x4 w = *reinterpret_cast<const u32x4*>(src + (r0 + rr) * C + c0);
-      const float sc = src_scale[(r0 + rr) * (C / 128) + blockIdx.y];
+    const bool in = rg + 32 * i < nrows;
+    const u32x4 w = raw[i];
+    const float sc = rsc[i];
 #pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        v[i][4 * k] = __builtin_amdgcn_cvt_f32_fp8(w[k], 0) * sc;
-        v[i][4 * k + 1] = __builtin_amdgcn_cvt_f32_fp8(w[k], 1) * sc;
-        v[i][4 * k + 2] = __builtin_amdgcn_cvt_f32_fp8(w[k], 2) * sc;
-        v[i][4 * k + 3] = __builtin_amdgcn_cvt_f32_fp8(w[k], 3) * sc;
-      }
-    } else {
-#pragma unroll
-      for (int c = 0; c < 16; ++c) v[i][c] = 0.0f;
+    for (int k = 0; k < 4; ++k) {
+      v[i][4 * k] = __builtin_amdgcn_cvt_f32_fp8(w[k], 0) * sc;
+      v[i][4 * k + 1] = __builtin_amdgcn_cvt_f32_fp8(w[k], 1) * sc;
+      v[i][4 * k + 2] = __builtin_amdgcn_cvt_f32_fp8(w[k], 2) * sc;
+      v[i][4 * k + 3] = __builtin_amdgcn_cvt_f32_fp8(w[k], 3) * sc;
     }
 #pragma unroll
-    for (int c = 0; c < 16; ++c) m[c] = fmaxf(m[c], fabsf(v[i][c]));
+    for (int c = 0; c < 16; ++c) {
+      v[i][c] = in ? v[i][c] : 0.0f;
+      m[c] = fmaxf(m[c], fabsf(v[i][c]));
+    }
   }
 #pragma unroll
   for (int c = 0; c < 16; c += 4)
@@ -1638,27 +1651,43 @@ __global__ __launch_bounds__(256) void quant_tokens_mx_kernel(const void* __rest
   const int nrows = int(min(int64_t(128), int64_t(offsets[lo + 1]) - r0));
   const int cg = threadIdx.x % 16, rg = threadIdx.x / 16;
   const int64_t c0 = int64_t(blockIdx.y) * 128 + cg * 8;  // C is a multiple of 128
+  // All 8 row loads go out together: a row past the block reads the
+  // block's last row (nrows >= 1, so in bounds) and is zeroed after. (Under
+  // a per-row branch each load waited for its data before the next one.)
   float v[8][8];
+  if constexpr (SRC_MX) {
+    u32x2 raw[8];
+    int rx[8];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int rr = rg + 16 * i;
-    if (rr < nrows) {
-      const int64_t off = (r0 + rr) * C + c0;
-      if constexpr (SRC_MX) {
-        const u32x2 w = *reinterpret_cast<const u32x2*>(static_cast<const fp8_t*>(src) + off);
-        const int x = int(src_e8m0[(r0 + rr) * (C / 32) + c0 / 32]) - 127;
-        const float f8[8] = {__builtin_amdgcn_cvt_f32_fp8(w[0], 0), __builtin_amdgcn_cvt_f32_fp8(w[0], 1),
-                             __builtin_amdgcn_cvt_f32_fp8(w[0], 2), __builtin_amdgcn_cvt_f32_fp8(w[0], 3),
-                             __builtin_amdgcn_cvt_f32_fp8(w[1], 0), __builtin_amdgcn_cvt_f32_fp8(w[1], 1),
-                             __builtin_amdgcn_cvt_f32_fp8(w[1], 2), __builtin_amdgcn_cvt_f32_fp8(w[1], 3)};
+    for (int i = 0; i < 8; ++i) {
+      const int64_t r = r0 + min(rg + 16 * i, nrows - 1);
+      raw[i] = *reinterpret_cast<const u32x2*>(static_cast<const fp8_t*>(src) + r * C + c0);
+      rx[i] = int(src_e8m0[r * (C / 32) + c0 / 32]);
+    }
 #pragma unroll
-        for (int c = 0; c < 8; ++c) v[i][c] = ldexpf(f8[c], x);
-      } else {
-        Vec16<bf16_t>::load(static_cast<const bf16_t*>(src) + off, v[i]);
-      }
-    } else {
+    for (int i = 0; i < 8; ++i) {
+      const u32x2 w = raw[i];
+      const int x = rx[i] - 127;
+      const float f8[8] = {__builtin_amdgcn_cvt_f32_fp8(w[0], 0), __builtin_amdgcn_cvt_f32_fp8(w[0], 1),
+                           __builtin_amdgcn_cvt_f32_fp8(w[0], 2), __builtin_amdgcn_cvt_f32_fp8(w[0], 3),
+                           __builtin_amdgcn_cvt_f32_fp8(w[1], 0), __builtin_amdgcn_cvt_f32_fp8(w[1], 1),
+                           __builtin_amdgcn_cvt_f32_fp8(w[1], 2), __builtin_amdgcn_cvt_f32_fp8(w[1], 3)};
+      const bool in = rg + 16 * i < nrows;
 #pragma unroll
-      for (int c = 0; c < 8; ++c) v[i][c] = 0.0f;
+      for (int c = 0; c < 8; ++c) v[i][c] = in ? ldexpf(f8[c], x) : 0.0f;
+    }
+  } else {
+    uint4 raw[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      raw[i] = *reinterpret_cast<const uint4*>(static_cast<const bf16_t*>(src) +
+                                               (r0 + min(rg + 16 * i, nrows - 1)) * C + c0);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      Vec16<bf16_t>::unpack(raw[i], v[i]);
+      const bool in = rg + 16 * i < nrows;
+#pragma unroll
+      for (int c = 0; c < 8; ++c) v[i][c] = in ? v[i][c] : 0.0f;
     }
   }
   if constexpr (ROWQ) {
