@@ -421,36 +421,36 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void l
     wk[q] = (idx % (kLgKC / 4)) * 4;
   }
   const int nch = d / kLgKC;
-  float xv[XL][XV];
+  // A chunk's loads go out with no branch around them and stay raw until
+  // the next chunk has been computed: rows past T (experts past E) read
+  // the last one, in bounds, and are zeroed when stored to LDS. (Converted
+  // under a bounds branch, each load was waited for as soon as issued.)
+  uint4 xraw[XL];
   float4 wv[WL];
   auto gload = [&](int c) {
     const int k0 = c * kLgKC;
 #pragma unroll
-    for (int q = 0; q < XL; ++q) {
-      const int t = t0 + xrow[q];
-      if (t < T) {
-        Vec16<TX>::load(x + int64_t(t) * d + k0 + xk[q], xv[q]);
-      } else {
+    for (int q = 0; q < XL; ++q)
+      xraw[q] = *reinterpret_cast<const uint4*>(x + int64_t(min(t0 + xrow[q], T - 1)) * d + k0 + xk[q]);
 #pragma unroll
-        for (int v = 0; v < XV; ++v) xv[q][v] = 0.0f;
-      }
-    }
-#pragma unroll
-    for (int q = 0; q < WL; ++q) {
-      const int e = e0 + wrow[q];
-      wv[q] = e < E ? *reinterpret_cast<const float4*>(w + int64_t(e) * d + k0 + wk[q])
-                    : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
-    }
+    for (int q = 0; q < WL; ++q)
+      wv[q] = *reinterpret_cast<const float4*>(w + int64_t(min(e0 + wrow[q], E - 1)) * d + k0 + wk[q]);
   };
   auto lstore = [&](int buf) {
 #pragma unroll
-    for (int q = 0; q < XL; ++q)
+    for (int q = 0; q < XL; ++q) {
+      float xv[XV];
+      Vec16<TX>::unpack(xraw[q], xv);
+      const bool in = t0 + xrow[q] < T;
 #pragma unroll
       for (int v = 0; v < XV; v += 4)
         *reinterpret_cast<float4*>(&As[buf][xrow[q] * kLgP + xk[q] + v]) =
-            make_float4(xv[q][v], xv[q][v + 1], xv[q][v + 2], xv[q][v + 3]);
+            in ? make_float4(xv[v], xv[v + 1], xv[v + 2], xv[v + 3]) : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+    }
 #pragma unroll
-    for (int q = 0; q < WL; ++q) *reinterpret_cast<float4*>(&Bs[buf][wrow[q] * kLgP + wk[q]]) = wv[q];
+    for (int q = 0; q < WL; ++q)
+      *reinterpret_cast<float4*>(&Bs[buf][wrow[q] * kLgP + wk[q]]) =
+          e0 + wrow[q] < E ? wv[q] : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
   };
   float acc[4][FN];
 #pragma unroll
@@ -529,41 +529,44 @@ __global__ __launch_bounds__(256) void logits_small_e_kernel(const TX* __restric
   constexpr int WU = EP * kSeKC / 4;     // 16-byte units of the w chunk
   constexpr int XL = (XU + 255) / 256, WL = (WU + 255) / 256;
   const int nch = (d + kSeKC - 1) / kSeKC;
-  float xv[XL][XV];
+  static_assert(XU % 256 == 0 && WU % 256 == 0, "whole load rounds");
+  // A chunk's loads go out with no branch around them and stay raw until
+  // the next chunk has been computed: a unit past T, E or d reads the last
+  // row / chunk in bounds and is zeroed when stored to LDS. (Converted
+  // under a bounds branch, each load was waited for as soon as issued.)
+  uint4 xraw[XL];
   float4 wv[WL];
+  bool xin[XL], win[WL];
   auto gload = [&](int c) {
     const int k0 = c * kSeKC;
 #pragma unroll
     for (int q = 0; q < XL; ++q) {
       const int u = tid + 256 * q, r = u / (kSeKC / XV), kk = (u % (kSeKC / XV)) * XV;
-      if (u < XU && t0 + r < T && k0 + kk < d) {
-        Vec16<TX>::load(x + int64_t(t0 + r) * d + k0 + kk, xv[q]);
-      } else {
-#pragma unroll
-        for (int v = 0; v < XV; ++v) xv[q][v] = 0.0f;
-      }
+      xin[q] = t0 + r < T && k0 + kk < d;
+      xraw[q] = *reinterpret_cast<const uint4*>(x + int64_t(min(t0 + r, T - 1)) * d + min(k0 + kk, d - XV));
     }
 #pragma unroll
     for (int q = 0; q < WL; ++q) {
       const int u = tid + 256 * q, r = u / (kSeKC / 4), kk = (u % (kSeKC / 4)) * 4;
-      wv[q] = (u < WU && r < E && k0 + kk < d) ? *reinterpret_cast<const float4*>(w + int64_t(r) * d + k0 + kk)
-                                               : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+      win[q] = r < E && k0 + kk < d;
+      wv[q] = *reinterpret_cast<const float4*>(w + int64_t(min(r, E - 1)) * d + min(k0 + kk, d - 4));
     }
   };
   auto lstore = [&](int buf) {
 #pragma unroll
     for (int q = 0; q < XL; ++q) {
       const int u = tid + 256 * q, r = u / (kSeKC / XV), kk = (u % (kSeKC / XV)) * XV;
-      if (u < XU)
+      float xv[XV];
+      Vec16<TX>::unpack(xraw[q], xv);
 #pragma unroll
-        for (int v = 0; v < XV; v += 4)
-          *reinterpret_cast<float4*>(&Xs[buf][r * kSeP + kk + v]) =
-              make_float4(xv[q][v], xv[q][v + 1], xv[q][v + 2], xv[q][v + 3]);
+      for (int v = 0; v < XV; v += 4)
+        *reinterpret_cast<float4*>(&Xs[buf][r * kSeP + kk + v]) =
+            xin[q] ? make_float4(xv[v], xv[v + 1], xv[v + 2], xv[v + 3]) : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
     }
 #pragma unroll
     for (int q = 0; q < WL; ++q) {
       const int u = tid + 256 * q, r = u / (kSeKC / 4), kk = (u % (kSeKC / 4)) * 4;
-      if (u < WU) *reinterpret_cast<float4*>(&Ws[buf][r * kSeP + kk]) = wv[q];
+      *reinterpret_cast<float4*>(&Ws[buf][r * kSeP + kk]) = win[q] ? wv[q] : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
     }
   };
   float acc = 0.0f;
