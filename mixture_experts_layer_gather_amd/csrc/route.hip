@@ -486,6 +486,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void l
     __syncthreads();
   }
   compute((nch - 1) & 1);
+  float bv[FN];  // this lane's experts' biases, loaded together
+#pragma unroll
+  for (int j = 0; j < FN; ++j) bv[j] = bias ? bias[min(e0 + tn + 16 * j, E - 1)] : 0.0f;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int t = t0 + tm + 16 * i;
@@ -495,7 +498,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void l
       const int e = e0 + tn + 16 * j;
       if (e >= E) continue;
       float v = acc[i][j];
-      if (bias) v = v + bias[e];
+      if (bias) v = v + bv[j];
       out[int64_t(t) * E + e] = v;
     }
   }
@@ -682,16 +685,15 @@ __global__ __launch_bounds__(256) void select_kernel(SelArgs s) {
 
   uint64_t key[NPL];
   float Lv[NPL];
+  // every load of the row at once (a lane past E reads the last logit, in
+  // bounds, and drops it): under a bounds branch each was waited for alone
+#pragma unroll
+  for (int p = 0; p < NPL; ++p) Lv[p] = Lrow[min(lane + kWave * p, s.E - 1)];
 #pragma unroll
   for (int p = 0; p < NPL; ++p) {
     const int e = lane + kWave * p;
-    if (e < s.E) {
-      Lv[p] = Lrow[e];
-      key[p] = make_key(Lv[p], e);
-    } else {
-      Lv[p] = 0.0f;
-      key[p] = 0;
-    }
+    Lv[p] = e < s.E ? Lv[p] : 0.0f;
+    key[p] = e < s.E ? make_key(Lv[p], e) : 0;
   }
   // global best logit (softmax normaliser), before any group masking
   uint64_t gbest = 0;
@@ -850,17 +852,22 @@ __global__ __launch_bounds__(256) void dlogits_kernel(DLArgs a) {
   for (int p = 0; p < NPL; ++p) dl[p] = 0.0f;
   int e_j[kMaxK];
   float L_j[kMaxK], dg_j[kMaxK];
+  // all k slots' loads in two rounds (indices and gate gradients, then the
+  // selected logits); slots past k read slot k - 1, in bounds, and are
+  // dropped. Under a per-slot branch each load was waited for alone.
 #pragma unroll
   for (int j = 0; j < kMaxK; ++j) {
-    if (j < a.k) {
-      e_j[j] = a.idx[int64_t(t) * a.k + j];
-      L_j[j] = Lrow[e_j[j]];
-      dg_j[j] = a.dgate[int64_t(t) * a.k + j];
-    } else {
-      e_j[j] = -1;
-      L_j[j] = 0.0f;
-      dg_j[j] = 0.0f;
-    }
+    const int64_t o = int64_t(t) * a.k + min(j, a.k - 1);
+    e_j[j] = a.idx[o];
+    dg_j[j] = a.dgate[o];
+  }
+#pragma unroll
+  for (int j = 0; j < kMaxK; ++j) L_j[j] = Lrow[e_j[j]];
+#pragma unroll
+  for (int j = 0; j < kMaxK; ++j) {
+    e_j[j] = j < a.k ? e_j[j] : -1;
+    L_j[j] = j < a.k ? L_j[j] : 0.0f;
+    dg_j[j] = j < a.k ? dg_j[j] : 0.0f;
   }
   const float c = a.gate_scale;
   float sel_grad[kMaxK];  // dL for each selected slot (sparse rules)
