@@ -135,6 +135,25 @@ __global__ __launch_bounds__(256) void rgemm_kernel(VArgs a) {
   };
   float ra[NA][4], rb[NB][VB];
   auto gload = [&](int k0) {
+    // a chunk inside M, N and the K range (uniform over the workgroup):
+    // every load unconditional, so they all go out together; under the
+    // per-load bounds branches below each one was waited for alone
+    if (a_vec && m0 + BM <= a.M && n0 + BN <= a.N && k0 + BK <= ke) {
+#pragma unroll
+      for (int i = 0; i < NA; ++i) {
+        int m, kk;
+        a_pos(i, m, kk);
+        const float4 v = *reinterpret_cast<const float4*>(A_MK ? A + int64_t(m0 + m) * a.lda + k0 + kk
+                                                                : A + int64_t(k0 + kk) * a.lda + m0 + m);
+        ra[i][0] = v.x; ra[i][1] = v.y; ra[i][2] = v.z; ra[i][3] = v.w;
+      }
+#pragma unroll
+      for (int i = 0; i < NB; ++i) {
+        const int q = (tid + 256 * i) * VB;
+        Vec16<TB>::load(reinterpret_cast<const TB*>(a.B) + int64_t(k0 + q / BN) * a.ldb + n0 + q % BN, rb[i]);
+      }
+      return;
+    }
 #pragma unroll
     for (int i = 0; i < NA; ++i) {
       int m, kk;
@@ -262,6 +281,25 @@ __global__ __launch_bounds__(256) void rgemm_bf16_kernel(VArgs a) {
   };
   float ra[NA][4], rb[NB][VB];
   auto gload = [&](int k0) {
+    // a chunk inside M, N and the K range (uniform over the workgroup):
+    // every load unconditional, so they all go out together; under the
+    // per-load bounds branches below each one was waited for alone
+    if (a_vec && m0 + BM <= a.M && n0 + BN <= a.N && k0 + BK <= ke) {
+#pragma unroll
+      for (int i = 0; i < NA; ++i) {
+        int m, kk;
+        a_pos(i, m, kk);
+        const float4 v = *reinterpret_cast<const float4*>(A_MK ? A + int64_t(m0 + m) * a.lda + k0 + kk
+                                                                : A + int64_t(k0 + kk) * a.lda + m0 + m);
+        ra[i][0] = v.x; ra[i][1] = v.y; ra[i][2] = v.z; ra[i][3] = v.w;
+      }
+#pragma unroll
+      for (int i = 0; i < NB; ++i) {
+        const int q = (tid + 256 * i) * VB;
+        Vec16<TB>::load(reinterpret_cast<const TB*>(a.B) + int64_t(k0 + q / BN) * a.ldb + n0 + q % BN, rb[i]);
+      }
+      return;
+    }
 #pragma unroll
     for (int i = 0; i < NA; ++i) {
       int m, kk;
