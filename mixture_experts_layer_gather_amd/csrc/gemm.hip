@@ -207,14 +207,16 @@ __device__ void find_group(const int32_t* __restrict__ offsets, int G, int tiles
   const int tid = threadIdx.x;
   constexpr int PER = 1024 / NTH;  // groups per thread (G <= 1024)
   int cnt[PER], local = 0;
+  // the PER + 1 offsets go out together (a group past G reads offsets[G],
+  // in bounds, and counts nothing); under a per-group branch each load was
+  // waited for alone
+  int off[PER + 1];
+#pragma unroll
+  for (int i = 0; i <= PER; ++i) off[i] = offsets[min(tid * PER + i, G)];
 #pragma unroll
   for (int i = 0; i < PER; ++i) {
     const int g = tid * PER + i;
-    int c = 0;
-    if (g < G) {
-      const int m = offsets[g + 1] - offsets[g];
-      c = (m + BM - 1) / BM;
-    }
+    const int c = g < G ? (off[i + 1] - off[i] + BM - 1) / BM : 0;
     cnt[i] = c;
     local += c;
   }
