@@ -135,55 +135,55 @@ def _compare_small(cfg, identity=False, inp=None, gemm_tile="auto"):
 # ------------------------------------------------------------ small layers
 
 SMALL = {
-    "tiny_fp32": S.CONFIGS[0],
-    "mixtral_mini": S.mini(S.CONFIGS[1], T=1000, d=256, f=384),
+    "tiny_fp32": S.BY_NAME["tiny_fp32"],
+    "mixtral_mini": S.mini(S.BY_NAME["mixtral_bf16"], T=1000, d=256, f=384),
     # >= 512 rows per expert and 256-multiple widths, run with the 256 x 256
     # tile forced on every GEMM (too few tiles for the shape-based choice)
-    "mixtral_mini_bigtile": S.mini(S.CONFIGS[1], T=2304, d=512, f=512, seed_base=33),
-    "mixtral_mini_f32": S.mini(S.CONFIGS[1], T=333, d=128, f=256).replace(act="f32", weight="f32"),
-    "deepseek_mini": S.mini(S.CONFIGS[2], T=300, d=256, f=256, E=32).replace(k=6),
-    "qwen_skew_mini": S.mini(S.CONFIGS[3], T=700, d=256, f=128, E=16).replace(k=4),
+    "mixtral_mini_bigtile": S.mini(S.BY_NAME["mixtral_bf16"], T=2304, d=512, f=512, seed_base=33),
+    "mixtral_mini_f32": S.mini(S.BY_NAME["mixtral_bf16"], T=333, d=128, f=256).replace(act="f32", weight="f32"),
+    "deepseek_mini": S.mini(S.BY_NAME["deepseek_v3_bf16"], T=300, d=256, f=256, E=32).replace(k=6),
+    "qwen_skew_mini": S.mini(S.BY_NAME["qwen3_skew_bf16"], T=700, d=256, f=128, E=16).replace(k=4),
     # 256 x 256 tiles forced where the widths allow (GEMM1, GEMM2 and dX; f =
     # 128 keeps dH and the weight gradients on 128 x 128): mixed tile sizes
     # and ragged groups smaller than a tile
-    "qwen_skew_mini_big": S.mini(S.CONFIGS[3], T=700, d=256, f=128, E=16).replace(k=4, seed_base=34),
-    "deepseek_fp8_mini": S.mini(S.CONFIGS[4], T=400, d=384, f=256, E=32).replace(k=6),
+    "qwen_skew_mini_big": S.mini(S.BY_NAME["qwen3_skew_bf16"], T=700, d=256, f=128, E=16).replace(k=4, seed_base=34),
+    "deepseek_fp8_mini": S.mini(S.BY_NAME["deepseek_v3_fp8"], T=400, d=384, f=256, E=32).replace(k=6),
     # FP8 with the 256 x 256 tile forced on all four row-grouped products
     # (d and 2f multiples of 256), ragged experts of 0 to a few hundred rows
-    "deepseek_fp8_mini_big": S.mini(S.CONFIGS[4], T=600, d=512, f=256, E=16).replace(
+    "deepseek_fp8_mini_big": S.mini(S.BY_NAME["deepseek_v3_fp8"], T=600, d=512, f=256, E=16).replace(
         k=4, num_groups=4, topk_groups=2, seed_base=35),
     # FP8 weight gradients in runs of two column tiles per workgroup (64
     # experts x 8 x 9 tiles of dW1), the last run of each row block one tile
     # short. Even routing: experts of one 128-row block, so each tile's only
     # K step ends it and two tiles' stores sit between a load and its wait;
     # skewed routing: experts of one block, of several, and with no rows
-    "deepseek_fp8_runs": S.mini(S.CONFIGS[4], T=1024, d=1152, f=512, E=64).replace(k=4, seed_base=36),
-    "deepseek_fp8_runs_skew": S.mini(S.CONFIGS[4], T=1024, d=1152, f=512, E=64).replace(
+    "deepseek_fp8_runs": S.mini(S.BY_NAME["deepseek_v3_fp8"], T=1024, d=1152, f=512, E=64).replace(k=4, seed_base=36),
+    "deepseek_fp8_runs_skew": S.mini(S.BY_NAME["deepseek_v3_fp8"], T=1024, d=1152, f=512, E=64).replace(
         k=4, bias="zipf", seed_base=37),
     # bf16 weight gradients of short experts (persistent runs of two
     # 128 x 128 column tiles, the last run of each row block one tile short):
     # even routing, and skewed routing with empty and multi-block experts
-    "deepseek_bf16_runs": S.mini(S.CONFIGS[2], T=1024, d=1152, f=512, E=64).replace(k=4, seed_base=44),
-    "deepseek_bf16_runs_skew": S.mini(S.CONFIGS[2], T=1024, d=1152, f=512, E=64).replace(
+    "deepseek_bf16_runs": S.mini(S.BY_NAME["deepseek_v3_bf16"], T=1024, d=1152, f=512, E=64).replace(k=4, seed_base=44),
+    "deepseek_bf16_runs_skew": S.mini(S.BY_NAME["deepseek_v3_bf16"], T=1024, d=1152, f=512, E=64).replace(
         k=4, bias="zipf", seed_base=45),
     # 8-bit layers whose experts average 256 rows (more than 128, at most
     # 320): the 160 x 128 tile; even and skewed routing (experts of one to
     # several row tiles, empty experts), FP8 and MXFP8
-    "deepseek_fp8_mid": S.mini(S.CONFIGS[4], T=1024, d=384, f=256, E=16).replace(
+    "deepseek_fp8_mid": S.mini(S.BY_NAME["deepseek_v3_fp8"], T=1024, d=384, f=256, E=16).replace(
         k=4, num_groups=4, topk_groups=2, seed_base=46),
-    "deepseek_fp8_mid_skew": S.mini(S.CONFIGS[4], T=1024, d=384, f=256, E=16).replace(
+    "deepseek_fp8_mid_skew": S.mini(S.BY_NAME["deepseek_v3_fp8"], T=1024, d=384, f=256, E=16).replace(
         k=4, num_groups=4, topk_groups=2, bias="zipf", seed_base=47),
     "deepseek_mxfp8_mid": S.mini(S.BY_NAME["deepseek_v3_mxfp8"], T=1024, d=384, f=256, E=16).replace(
         k=4, num_groups=4, topk_groups=2, seed_base=48),
     # the other group rule (a group's best score instead of its best two)
     # and sigmoid gates without renormalisation
-    "deepseek_mini_gmax": S.mini(S.CONFIGS[2], T=300, d=256, f=256, E=32).replace(
+    "deepseek_mini_gmax": S.mini(S.BY_NAME["deepseek_v3_bf16"], T=300, d=256, f=256, E=32).replace(
         k=6, group_score="max", seed_base=61),
-    "deepseek_mini_norenorm": S.mini(S.CONFIGS[2], T=300, d=256, f=256, E=32).replace(
+    "deepseek_mini_norenorm": S.mini(S.BY_NAME["deepseek_v3_bf16"], T=300, d=256, f=256, E=32).replace(
         k=6, renorm=False, gate_scale=1.0, seed_base=62),
     # the largest expert count and top-k the library takes (E = 1024,
     # k = 16): most experts get 0 to 3 rows
-    "max_experts_topk": S.mini(S.CONFIGS[1], T=200, d=128, f=128, E=1024).replace(k=16, seed_base=63),
+    "max_experts_topk": S.mini(S.BY_NAME["mixtral_bf16"], T=200, d=128, f=128, E=1024).replace(k=16, seed_base=63),
     # MXFP8: 1 x 32 / 32 x 1 blocks with E8M0 scales on the matrix cores
     "deepseek_mxfp8_mini": S.mini(S.BY_NAME["deepseek_v3_mxfp8"], T=400, d=384, f=256, E=32).replace(k=6),
     # MXFP8 weight gradients (32-row E8M0 token blocks) in runs of two column
@@ -195,9 +195,9 @@ SMALL = {
         k=4, bias="zipf", seed_base=39),
     # the load-balancing auxiliary loss on (coefficient 0.01): its value and
     # its share of the router gradient
-    "mixtral_mini_aux": S.mini(S.CONFIGS[1], T=1000, d=256, f=384).replace(aux_coeff=0.01),
-    "tiny_fp32_aux": S.CONFIGS[0].replace(aux_coeff=0.01),
-    "deepseek_mini_aux": S.mini(S.CONFIGS[2], T=300, d=256, f=256, E=32).replace(
+    "mixtral_mini_aux": S.mini(S.BY_NAME["mixtral_bf16"], T=1000, d=256, f=384).replace(aux_coeff=0.01),
+    "tiny_fp32_aux": S.BY_NAME["tiny_fp32"].replace(aux_coeff=0.01),
+    "deepseek_mini_aux": S.mini(S.BY_NAME["deepseek_v3_bf16"], T=300, d=256, f=256, E=32).replace(
         k=6, aux_coeff=0.01),
 }
 
@@ -225,7 +225,7 @@ def test_identity_experts(name):
 
 
 def test_edge_shapes():
-    base = S.mini(S.CONFIGS[1], T=1, d=128, f=128, E=8)
+    base = S.mini(S.BY_NAME["mixtral_bf16"], T=1, d=128, f=128, E=8)
     for cfg in [base,                                    # a single token
                 base.replace(T=37, k=4, E=4, seed_base=40),    # k = E
                 base.replace(T=50, k=1, E=1, seed_base=41),    # one expert
@@ -261,7 +261,7 @@ def test_empty_batch(name):
 
 
 def test_all_equal_logits_pick_lowest_indices():
-    cfg = S.mini(S.CONFIGS[1], T=100, d=128, f=128, E=8).replace(k=3)
+    cfg = S.mini(S.BY_NAME["mixtral_bf16"], T=100, d=128, f=128, E=8).replace(k=3)
     inp = _inputs(cfg)
     inp["wr"] = torch.zeros_like(inp["wr"])
     layer, ref = _compare_small(cfg, inp=inp)
@@ -356,7 +356,7 @@ def test_mxfp8_quantiser_bit_exact():
 
 def test_fp8_dispatch_bit_exact():
     from mixture_experts_layer_gather_amd import make_config, moe_dispatch, workspace_size
-    cfg = S.mini(S.CONFIGS[4], T=300, d=512, f=256, E=32).replace(k=4)
+    cfg = S.mini(S.BY_NAME["deepseek_v3_fp8"], T=300, d=512, f=256, E=32).replace(k=4)
     x = S.x(cfg)
     L, idx, _ = oracle.route(cfg, x, S.w_router(cfg))
     counts, offsets, rmap, ptok = oracle.dispatch_index(idx, cfg.E)
@@ -455,7 +455,7 @@ ROUTE_TILE_CASES = [(16384, 128), (300, 64), (1000, 96), (8192, 72)]
 @pytest.mark.parametrize("T,E", ROUTE_TILE_CASES)
 def test_route_logits_tilings(T, E):
     from mixture_experts_layer_gather_amd import make_config, moe_route, workspace_size
-    cfg = S.mini(S.CONFIGS[3], T=T, d=256, f=128, E=E).replace(k=4)
+    cfg = S.mini(S.BY_NAME["qwen3_skew_bf16"], T=T, d=256, f=128, E=E).replace(k=4)
     _say(f"[route tiles] T={T} E={E}")
     x, wr = S.x(cfg), S.w_router(cfg)
     bias = S.router_bias(cfg)
@@ -740,9 +740,10 @@ def _full_size_check(cfg):
         assert v <= tol, f"{n}: rel L2 {v:.3e} > {tol}"
 
 
-@pytest.mark.parametrize("which", [1, 2, 3, 4, "deepseek_v3_mxfp8"])
+@pytest.mark.parametrize("which", ["mixtral_bf16", "deepseek_v3_bf16", "qwen3_skew_bf16", "deepseek_v3_fp8",
+                                   "deepseek_v3_mxfp8"])
 def test_full_size_layer(which):
-    _full_size_check(S.CONFIGS[which] if isinstance(which, int) else S.BY_NAME[which])
+    _full_size_check(S.BY_NAME[which])
 
 
 # ------------------------------------------------ load-balancing aux loss

@@ -72,8 +72,8 @@ def test_ffn_matches_torch_dense_swiglu():
 
 
 def test_identity_experts_return_gate_sum_times_x():
-    for base, shared_add in [(S.CONFIGS[0], 0.0), (S.mini(S.CONFIGS[2], 40, 64, 32, E=32), 1.0),
-                             (S.mini(S.CONFIGS[3], 40, 64, 32, E=16), 0.0)]:
+    for base, shared_add in [(S.BY_NAME["tiny_fp32"], 0.0), (S.mini(S.BY_NAME["deepseek_v3_bf16"], 40, 64, 32, E=32), 1.0),
+                             (S.mini(S.BY_NAME["qwen3_skew_bf16"], 40, 64, 32, E=16), 0.0)]:
         inp = _inputs(base)
         out = oracle.layer(base, inp, identity=True)
         x = oracle.as_f64(inp["x"])
@@ -125,12 +125,12 @@ def _torch_layer(cfg, inp, idx, L32):
     return leaves, y, loss
 
 
-@pytest.mark.parametrize("which", [0, 2, 3])
+@pytest.mark.parametrize("which", ["tiny_fp32", "deepseek_v3_bf16", "qwen3_skew_bf16"])
 def test_layer_matches_torch_autograd_fp64(which):
-    cfg = S.CONFIGS[which]
-    if which:
-        cfg = S.mini(cfg, T=24, d=32, f=24, E=16 if which == 2 else 8)
-        if which == 2:
+    cfg = S.BY_NAME[which]
+    if which != "tiny_fp32":
+        cfg = S.mini(cfg, T=24, d=32, f=24, E=16 if which == "deepseek_v3_bf16" else 8)
+        if which == "deepseek_v3_bf16":
             cfg = cfg.replace(num_groups=4, topk_groups=2, k=3)
         else:
             cfg = cfg.replace(k=3)
@@ -153,7 +153,7 @@ def test_layer_matches_torch_autograd_fp64(which):
 def test_layer_gradients_central_differences():
     """Central differences of <y, dy> in fp64 with routing frozen; the
     selection margin is checked to exceed the perturbation's effect."""
-    cfg = S.mini(S.CONFIGS[0], T=12, d=16, f=12, E=4)
+    cfg = S.mini(S.BY_NAME["tiny_fp32"], T=12, d=16, f=12, E=4)
     inp = _inputs(cfg)
     out = oracle.layer(cfg, inp)
     L = out["logits"].astype(np.float64)
@@ -196,7 +196,7 @@ def test_layer_gradients_central_differences():
 def test_fp8_layer_consistency():
     """fp8 weights: the oracle's own quantisation of the bf16 masters is used
     consistently and stays close to the unquantised layer."""
-    cfg = S.mini(S.CONFIGS[4], T=16, d=256, f=256, E=16).replace(num_groups=4, topk_groups=2, k=4)
+    cfg = S.mini(S.BY_NAME["deepseek_v3_fp8"], T=16, d=256, f=256, E=16).replace(num_groups=4, topk_groups=2, k=4)
     inp = _inputs(cfg)
     out = oracle.layer(cfg, inp)
     ref = oracle.layer(cfg.replace(weight="bf16"), inp)
@@ -356,7 +356,7 @@ def test_fp8_wgrad_token_blocks_feed_only_the_weight_gradients(monkeypatch):
     layer's dW1 and dW2 (both operands marked) become 4x those of the
     unquantised-gradient reading and nothing else moves: the token blocks
     serve exactly the four operands of the two weight-gradient products."""
-    cfg = S.mini(S.CONFIGS[4], T=40, d=256, f=256, E=8).replace(num_groups=4, topk_groups=2, k=4)
+    cfg = S.mini(S.BY_NAME["deepseek_v3_fp8"], T=40, d=256, f=256, E=8).replace(num_groups=4, topk_groups=2, k=4)
     inp = _inputs(cfg)
     base = oracle.layer(cfg, inp, fp8_wgrad=False)
     monkeypatch.setattr(oracle, "fp8_roundtrip_tokens", lambda a: 2.0 * np.asarray(a, np.float64))
@@ -375,7 +375,7 @@ def test_fp8_wgrad_token_blocks_feed_only_the_weight_gradients(monkeypatch):
 
 
 def test_fp8_wgrad_token_blocks_close_to_unquantised_gradients():
-    cfg = S.mini(S.CONFIGS[4], T=300, d=256, f=256, E=4).replace(num_groups=2, topk_groups=1, k=2)
+    cfg = S.mini(S.BY_NAME["deepseek_v3_fp8"], T=300, d=256, f=256, E=4).replace(num_groups=2, topk_groups=1, k=2)
     inp = _inputs(cfg)
     a = oracle.layer(cfg, inp, fp8_wgrad=False)
     b = oracle.layer(cfg, inp, fp8_wgrad=True)

@@ -37,8 +37,8 @@ def _call(fn, cfg, x, idx, o, ws=None):
     torch.cuda.synchronize()
 
 
-CASES = [S.mini(S.CONFIGS[3], T=3000, d=256, f=128, E=64).replace(k=4),      # bf16, 12 chunks
-         S.mini(S.CONFIGS[4], T=700, d=256, f=128, E=32).replace(k=6)]        # fp8, smaller
+CASES = [S.mini(S.BY_NAME["qwen3_skew_bf16"], T=3000, d=256, f=128, E=64).replace(k=4),      # bf16, 12 chunks
+         S.mini(S.BY_NAME["deepseek_v3_fp8"], T=700, d=256, f=128, E=32).replace(k=6)]        # fp8, smaller
 
 
 def test_dispatch_scratch_matches_dispatch():
